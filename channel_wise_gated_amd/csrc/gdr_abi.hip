@@ -1,0 +1,145 @@
+// gdr_abi.hip -- the extern "C" entry points of libgdr.so (declared in
+// include/gdr.h): host-side validation, workspace carving and launches.
+// Validation is pure host code and returns before any HIP call.
+#include <stdint.h>
+
+#include "gdr_launch.h"
+
+
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_dtype(int d) { return d == GDR_BF16 || d == GDR_F32; }
+
+bool valid_mode(int m) { return m >= GDR_GATE_PER_CHANNEL && m <= GDR_GATE_ZEROS; }
+
+bool needs_ptr(int m) { return m == GDR_GATE_PER_CHANNEL || m == GDR_GATE_PER_TOKEN; }
+
+// Checks shared by both calls; `tokens` = T for chunk_fwd, 1 for decode.
+gdr_status check_common(const gdr_desc *d, long long tokens) {
+  if (!d) return GDR_ERR_INVALID_ARG;
+  if (d->B < 0 || d->H < 0 || tokens < 0) return GDR_ERR_INVALID_ARG;
+  if (d->dk <= 0 || d->dv <= 0) return GDR_ERR_INVALID_ARG;
+  if (!valid_dtype(d->in_dtype) || !valid_dtype(d->out_dtype)) return GDR_ERR_INVALID_ARG;
+  if (!valid_mode(d->alpha_mode) || !valid_mode(d->b_mode) || !valid_mode(d->w_mode))
+    return GDR_ERR_INVALID_ARG;
+  if (d->alpha_mode == GDR_GATE_ZEROS) return GDR_ERR_INVALID_ARG;  // log alpha = -inf
+  if (d->normalize_qk != 0 && d->normalize_qk != 1) return GDR_ERR_INVALID_ARG;
+  if (!(d->scale == d->scale) || d->scale > 3.0e38f || d->scale < -3.0e38f) return GDR_ERR_INVALID_ARG;
+  // element counts must stay addressable
+  const long long elems = (long long)d->B * d->H * tokens * (d->dk > d->dv ? d->dk : d->dv);
+  if (d->B > 0 && d->H > 0 && tokens > 0 && elems / d->B / d->H / tokens <= 0) return GDR_ERR_INVALID_ARG;
+  if (elems > (1LL << 40)) return GDR_ERR_INVALID_ARG;
+  if (d->dk != d->dv) return GDR_ERR_UNSUPPORTED;
+  if (d->dk != 64 && d->dk != 128) return GDR_ERR_UNSUPPORTED;
+  return GDR_OK;
+}
+
+gdr_status check_inputs(const gdr_desc *d, const void *q, const void *k, const void *v,
+                        const float *la, const void *b, const void *w, const float *gamma,
+                        const void *z, const void *o) {
+  if (!q || !k || !v || !o) return GDR_ERR_INVALID_ARG;
+  if (needs_ptr(d->alpha_mode) && !la) return GDR_ERR_INVALID_ARG;
+  if (needs_ptr(d->b_mode) && !b) return GDR_ERR_INVALID_ARG;
+  if (needs_ptr(d->w_mode) && !w) return GDR_ERR_INVALID_ARG;
+  const void *ptrs[] = {q, k, v, o, needs_ptr(d->alpha_mode) ? la : nullptr,
+                        needs_ptr(d->b_mode) ? b : nullptr, needs_ptr(d->w_mode) ? w : nullptr,
+                        gamma, z};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return GDR_ERR_INVALID_ARG;
+  return GDR_OK;
+}
+
+gdr_status chunk_plan(const gdr_desc *d, size_t *ws) {
+  gdr_status s = check_common(d, d ? d->T : 0);
+  if (s != GDR_OK) return s;
+  if (d->chunk != 64 && d->chunk != 128) return GDR_ERR_INVALID_ARG;
+  if (d->T % d->chunk != 0) return GDR_ERR_INVALID_ARG;
+  const int ns = d->in_dtype == GDR_BF16 ? 2 : 3;
+  if (!gdr::chunk_intra_fits(d->chunk, d->dk, ns)) return GDR_ERR_UNSUPPORTED;
+  *ws = gdr::chunk_workspace_bytes(d->B, d->H, d->T, d->chunk, d->dk, ns);
+  return GDR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdr_status gdr_chunk_fwd_workspace_size(const gdr_desc *desc, size_t *bytes) {
+  if (!bytes) return GDR_ERR_INVALID_ARG;
+  size_t ws = 0;
+  gdr_status s = chunk_plan(desc, &ws);
+  if (s == GDR_OK) *bytes = ws;
+  return s;
+}
+
+gdr_status gdr_chunk_fwd(const gdr_desc *desc, const void *q, const void *k, const void *v,
+                         const float *log_alpha, const void *b, const void *w, const float *gamma,
+                         const void *z, const float *S0, void *o, float *S_T, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+  size_t need = 0;
+  gdr_status s = chunk_plan(desc, &need);
+  if (s != GDR_OK) return s;
+  const gdr_desc &d = *desc;
+  if ((size_t)d.B * d.H == 0) return GDR_OK;
+  if (d.T > 0) {
+    s = check_inputs(desc, q, k, v, log_alpha, b, w, gamma, z, o);
+    if (s != GDR_OK) return s;
+  }
+  if ((S0 && !aligned16(S0)) || (S_T && !aligned16(S_T))) return GDR_ERR_INVALID_ARG;
+  if (need > 0 && (!workspace || workspace_bytes < need)) return GDR_ERR_WORKSPACE;
+  if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u)) return GDR_ERR_WORKSPACE;
+
+  const int ns = d.in_dtype == GDR_BF16 ? 2 : 3;
+  const size_t nch = (size_t)d.B * d.H * (d.T / d.chunk);
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  unsigned char *ws = static_cast<unsigned char *>(workspace);
+  gdr::ChunkArgs a;
+  a.q = q; a.k = k; a.v = v; a.b = b; a.w = w; a.z = z;
+  a.log_alpha = log_alpha; a.gamma = gamma; a.S0 = S0;
+  a.o = o; a.S_T = S_T;
+  a.Qp = reinterpret_cast<uint16_t *>(ws);
+  ws += al(nch * ns * (size_t)d.chunk * d.dk * 2);
+  a.Mm = reinterpret_cast<uint16_t *>(ws);
+  ws += al(nch * ns * (size_t)d.dk * d.dk * 2);
+  a.Ob = reinterpret_cast<float *>(ws);
+  ws += al(nch * (size_t)d.chunk * d.dk * 4);
+  a.Nn = reinterpret_cast<float *>(ws);
+  a.B = d.B; a.H = d.H; a.T = d.T;
+  a.alpha_mode = d.alpha_mode; a.b_mode = d.b_mode; a.w_mode = d.w_mode;
+  a.normalize_qk = d.normalize_qk; a.scale = d.scale;
+  hipError_t e = gdr::launch_chunk(d, a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
+
+gdr_status gdr_decode_step(const gdr_desc *desc, float *S, const void *q, const void *k,
+                           const void *v, const float *log_alpha, const void *b, const void *w,
+                           const float *gamma, const void *z, void *o, void *stream) {
+  gdr_status s = check_common(desc, 1);
+  if (s != GDR_OK) return s;
+  const gdr_desc &d = *desc;
+  if ((size_t)d.B * d.H == 0) return GDR_OK;
+  if (!S || !aligned16(S)) return GDR_ERR_INVALID_ARG;
+  s = check_inputs(desc, q, k, v, log_alpha, b, w, gamma, z, o);
+  if (s != GDR_OK) return s;
+  hipError_t e = gdr::launch_decode(d, S, q, k, v, log_alpha, b, w, gamma, z, o,
+                                    static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
+
+const char *gdr_status_string(gdr_status status) {
+  switch (status) {
+    case GDR_OK: return "GDR_OK";
+    case GDR_ERR_INVALID_ARG: return "GDR_ERR_INVALID_ARG: invalid argument";
+    case GDR_ERR_UNSUPPORTED: return "GDR_ERR_UNSUPPORTED: configuration not supported";
+    case GDR_ERR_WORKSPACE: return "GDR_ERR_WORKSPACE: workspace missing, misaligned or too small";
+    case GDR_ERR_HIP: return "GDR_ERR_HIP: a HIP launch or runtime call failed";
+    default: return "unknown gdr_status";
+  }
+}
+
+int gdr_version(void) { return 100; }
+
+}  // extern "C"

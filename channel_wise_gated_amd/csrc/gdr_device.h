@@ -1,0 +1,167 @@
+// gdr_device.h -- device helpers shared by the gfx950 kernels of libgdr.
+//
+// bf16 storage, fp32 arithmetic, hi/lo bf16 operand splits for the matrix
+// cores, and the two MFMA shapes the kernels use.
+//
+// MFMA lane layouts (wave64, verified on gfx950 by an in-bounds probe):
+//   v_mfma_f32_16x16x32_bf16   A (16 x 32): lane l holds row l%16, k = 8*(l/16) + e, e < 8
+//                              B (32 x 16): lane l holds col l%16, k = 8*(l/16) + e
+//                              D (16 x 16): lane l holds col l%16, rows 4*(l/16) + r, r < 4
+//   v_mfma_f32_16x16x16_bf16   same with k = 4*(l/16) + e, e < 4
+// The contraction index k may be permuted freely as long as A and B use the
+// same permutation; the kernels use that to feed accumulator tiles (rows
+// 4*(l/16)+r) straight back in as operands: within a 32-wide k-step that
+// covers 16-row tiles m0 and m0+1, lane group g = l/16 and element e stand for
+// row 16*(m0 + e/4) + 4*g + e%4 ("tile-pair order").
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/gdr.h"
+
+namespace gdr {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- bf16 <-> f32
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
+  return __uint_as_float(((uint32_t)h) << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+  __bf16 b = (__bf16)x;  // round to nearest even (v_cvt_pk_bf16_f32)
+  return __builtin_bit_cast(uint16_t, b);
+}
+__device__ __forceinline__ float round_bf16(float x) {
+  return bf16_bits_to_f32(f32_to_bf16_bits(x));
+}
+
+// Load one element of a tensor stored as bf16 or f32.
+template <bool BF16>
+__device__ __forceinline__ float ld1(const void *p, size_t i) {
+  if constexpr (BF16)
+    return bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(p)[i]);
+  else
+    return reinterpret_cast<const float *>(p)[i];
+}
+
+// Load 4 consecutive elements (i multiple of 4; 8- or 16-byte aligned).
+template <bool BF16>
+__device__ __forceinline__ void ld4(const void *p, size_t i, float out[4]) {
+  if constexpr (BF16) {
+    uint2 u = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(p) + i);
+    out[0] = __uint_as_float(u.x << 16);
+    out[1] = __uint_as_float(u.x & 0xffff0000u);
+    out[2] = __uint_as_float(u.y << 16);
+    out[3] = __uint_as_float(u.y & 0xffff0000u);
+  } else {
+    float4 f = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(p) + i);
+    out[0] = f.x; out[1] = f.y; out[2] = f.z; out[3] = f.w;
+  }
+}
+
+// Load 8 consecutive elements (i multiple of 8).
+template <bool BF16>
+__device__ __forceinline__ void ld8(const void *p, size_t i, float out[8]) {
+  if constexpr (BF16) {
+    uint4 u = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(p) + i);
+    out[0] = __uint_as_float(u.x << 16); out[1] = __uint_as_float(u.x & 0xffff0000u);
+    out[2] = __uint_as_float(u.y << 16); out[3] = __uint_as_float(u.y & 0xffff0000u);
+    out[4] = __uint_as_float(u.z << 16); out[5] = __uint_as_float(u.z & 0xffff0000u);
+    out[6] = __uint_as_float(u.w << 16); out[7] = __uint_as_float(u.w & 0xffff0000u);
+  } else {
+    const float4 *f = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(p) + i);
+    float4 a = f[0], b = f[1];
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void st1(void *p, size_t i, float x) {
+  if constexpr (BF16)
+    reinterpret_cast<uint16_t *>(p)[i] = f32_to_bf16_bits(x);
+  else
+    reinterpret_cast<float *>(p)[i] = x;
+}
+
+// ---------------------------------------------------------------- math
+__device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
+__device__ __forceinline__ float two_sigmoid(float x) { return 2.0f / (1.0f + __expf(-x)); }
+
+// ---------------------------------------------------------------- hi/lo splits
+// x ~= sum_{p < NS} plane_p(x), each plane a bf16.  NS = 2 keeps ~16 mantissa
+// bits, NS = 3 ~24 (fp32).
+template <int NS>
+__device__ __forceinline__ void split(float x, uint16_t out[NS]) {
+  float r = x;
+#pragma unroll
+  for (int p = 0; p < NS; ++p) {
+    uint16_t h = f32_to_bf16_bits(r);
+    out[p] = h;
+    r = r - bf16_bits_to_f32(h);
+  }
+}
+
+// Eight fp32 values -> NS packed bf16x8 fragments.
+template <int NS>
+__device__ __forceinline__ void split8(const float x[8], bf16x8 out[NS]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    uint16_t h[NS];
+    split<NS>(x[e], h);
+#pragma unroll
+    for (int p = 0; p < NS; ++p) out[p][e] = __builtin_bit_cast(__bf16, h[p]);
+  }
+}
+
+// ---------------------------------------------------------------- MFMA
+__device__ __forceinline__ f32x4 mfma32(const bf16x8 &a, const bf16x8 &b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Split product: sum over plane pairs (pa, pb) with pa + pb < NS.
+template <int NS>
+__device__ __forceinline__ f32x4 mfma32_split(const bf16x8 a[NS], const bf16x8 b[NS], f32x4 c) {
+  // small terms first
+#pragma unroll
+  for (int s = NS - 1; s >= 0; --s)
+#pragma unroll
+    for (int pa = 0; pa <= s; ++pa) c = mfma32(a[pa], b[s - pa], c);
+  return c;
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// ---------------------------------------------------------------- gates
+// Value of a gate for element (token row `row`, channel `c`) of a tensor with
+// d channels, given its mode.  `row` indexes [B*H*T] (or [B*H] for decode).
+template <bool BF16>
+__device__ __forceinline__ float gate_at(const void *p, int mode, size_t row, int c, int d) {
+  switch (mode) {
+    case GDR_GATE_PER_CHANNEL: return ld1<BF16>(p, row * (size_t)d + c);
+    case GDR_GATE_PER_TOKEN: return ld1<BF16>(p, row);
+    case GDR_GATE_ONES: return 1.0f;
+    default: return 0.0f;
+  }
+}
+
+__device__ __forceinline__ float log_alpha_at(const float *p, int mode, size_t row, int c, int d) {
+  switch (mode) {
+    case GDR_GATE_PER_CHANNEL: return p[row * (size_t)d + c];
+    case GDR_GATE_PER_TOKEN: return p[row];
+    default: return 0.0f;
+  }
+}
+
+// ---------------------------------------------------------------- reductions
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, kWave);
+  return x;
+}
+
+}  // namespace gdr

@@ -1,0 +1,210 @@
+"""Thin ctypes binding of libgdr.so (C ABI in include/gdr.h).
+
+Argument marshalling only: every step of the recurrence runs in the HIP
+kernels of libgdr.so.  PyTorch provides device memory and the stream.  There
+is no fallback: if the library is missing or cannot be loaded, every call
+raises.
+
+Entry points (same names as the C ABI):
+  gdr_chunk_fwd_workspace_size(desc) -> bytes
+  gdr_chunk_fwd(q, k, v, log_alpha, b, w, gamma=None, z=None, S0=None, ...)
+      -> (o, S_T)
+  gdr_decode_step(S, q, k, v, log_alpha, b, w, gamma=None, z=None, ...) -> o
+  gdr_status_string(code) -> str
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdr.so")
+
+GDR_OK, GDR_ERR_INVALID_ARG, GDR_ERR_UNSUPPORTED, GDR_ERR_WORKSPACE, GDR_ERR_HIP = range(5)
+GDR_BF16, GDR_F32 = 0, 1
+PER_CHANNEL, PER_TOKEN, ONES, ZEROS = 0, 1, 2, 3
+SYMBOLS = ("gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_decode_step",
+           "gdr_status_string", "gdr_version")
+
+
+class GdrDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("H", ctypes.c_int), ("T", ctypes.c_int),
+                ("dk", ctypes.c_int), ("dv", ctypes.c_int), ("chunk", ctypes.c_int),
+                ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
+                ("normalize_qk", ctypes.c_int), ("scale", ctypes.c_float),
+                ("alpha_mode", ctypes.c_int), ("b_mode", ctypes.c_int),
+                ("w_mode", ctypes.c_int)]
+
+
+class GdrError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {gdr_status_string(code)}")
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libgdr.so; raise (never fall back) if it is not there."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m channel_wise_gated_amd.build` "
+            "(or __graft_entry__.build()); there is no non-HIP fallback")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    dp = ctypes.POINTER(GdrDesc)
+    lib.gdr_chunk_fwd_workspace_size.restype = ctypes.c_int
+    lib.gdr_chunk_fwd_workspace_size.argtypes = [dp, ctypes.POINTER(sz)]
+    lib.gdr_chunk_fwd.restype = ctypes.c_int
+    lib.gdr_chunk_fwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gdr_decode_step.restype = ctypes.c_int
+    lib.gdr_decode_step.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.gdr_status_string.restype = ctypes.c_char_p
+    lib.gdr_status_string.argtypes = [ctypes.c_int]
+    lib.gdr_version.restype = ctypes.c_int
+    lib.gdr_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def gdr_status_string(code: int) -> str:
+    return load().gdr_status_string(int(code)).decode()
+
+
+def make_desc(B, H, T, dk, dv, chunk=64, in_dtype=GDR_BF16, out_dtype=GDR_F32,
+              normalize_qk=1, scale=1.0, alpha_mode=PER_CHANNEL, b_mode=PER_CHANNEL,
+              w_mode=PER_CHANNEL) -> GdrDesc:
+    return GdrDesc(int(B), int(H), int(T), int(dk), int(dv), int(chunk), int(in_dtype),
+                   int(out_dtype), int(normalize_qk), float(scale), int(alpha_mode),
+                   int(b_mode), int(w_mode))
+
+
+def gdr_chunk_fwd_workspace_size(desc: GdrDesc) -> int:
+    n = ctypes.c_size_t(0)
+    rc = load().gdr_chunk_fwd_workspace_size(ctypes.byref(desc), ctypes.byref(n))
+    if rc != GDR_OK:
+        raise GdrError(rc, "gdr_chunk_fwd_workspace_size")
+    return int(n.value)
+
+
+# ----------------------------------------------------------------- marshalling
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return GDR_BF16
+    if t.dtype == torch.float32:
+        return GDR_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _gate(g, full_ndim: int, name: str):
+    """(mode, tensor-or-None) from a gate argument: tensor with the full rank
+    (per channel), one dim less (per token), or the scalar 1 / 0 / None."""
+    if g is None:
+        return ONES, None
+    if isinstance(g, (int, float)):
+        if g == 1:
+            return ONES, None
+        if g == 0:
+            return ZEROS, None
+        raise ValueError(f"{name}: scalar gates must be 0 or 1")
+    if g.dim() == full_ndim:
+        return PER_CHANNEL, g
+    if g.dim() == full_ndim - 1:
+        return PER_TOKEN, g
+    raise ValueError(f"{name}: rank {g.dim()} does not fit")
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(int(stream.cuda_stream))
+
+
+def _contig(t):
+    if t is None or isinstance(t, (int, float)):
+        return t
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t
+
+
+def gdr_chunk_fwd(q, k, v, log_alpha, b, w, gamma=None, z=None, S0=None, *, chunk=64,
+                  out_dtype=torch.float32, normalize_qk=True, scale=1.0, o=None, S_T=None,
+                  workspace=None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Chunkwise forward over whole sequences; see gdr_chunk_fwd in gdr.h.
+
+    q, k: [B,H,T,dk]; v: [B,H,T,dv] (bf16 or fp32, same dtype); log_alpha: fp32
+    [B,H,T,dk] or [B,H,T] or 0; b, w: per channel, per token or the scalars
+    1 / 0; gamma [H,dk] fp32; z [B,H,T,dk]; S0 [B,H,dk,dv] fp32.
+    Returns (o [B,H,T,dv] out_dtype, S_T [B,H,dk,dv] fp32).
+    """
+    lib = load()
+    q, k, v, z, gamma, S0 = map(_contig, (q, k, v, z, gamma, S0))
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    if isinstance(log_alpha, (int, float)):
+        if log_alpha != 0:
+            raise ValueError("scalar log_alpha must be 0")
+        amode, la = ONES, None
+    else:
+        amode, la = _gate(_contig(log_alpha), 4, "log_alpha")
+    bmode, bt = _gate(_contig(b), 4, "b")
+    wmode, wt = _gate(_contig(w), 4, "w")
+    od = GDR_BF16 if out_dtype == torch.bfloat16 else GDR_F32
+    desc = make_desc(B, H, T, dk, dv, chunk, _dtype_code(q), od, int(bool(normalize_qk)),
+                     scale, amode, bmode, wmode)
+    if o is None:
+        o = torch.empty((B, H, T, dv), dtype=out_dtype, device=q.device)
+    if S_T is None:
+        S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    need = gdr_chunk_fwd_workspace_size(desc)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    rc = lib.gdr_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(la), _ptr(bt),
+                           _ptr(wt), _ptr(gamma), _ptr(z), _ptr(S0), _ptr(o), _ptr(S_T),
+                           _ptr(workspace), workspace.numel(), _stream(stream))
+    if rc != GDR_OK:
+        raise GdrError(rc, "gdr_chunk_fwd")
+    return o, S_T
+
+
+def gdr_decode_step(S, q, k, v, log_alpha, b, w, gamma=None, z=None, *, out_dtype=torch.float32,
+                    normalize_qk=True, scale=1.0, o=None, stream=None) -> torch.Tensor:
+    """One decode step; S [B,H,dk,dv] fp32 is updated in place; returns o [B,H,dv].
+
+    q, k, z: [B,H,dk]; v: [B,H,dv]; log_alpha [B,H,dk] / [B,H] / 0; b, w per
+    channel [B,H,d], per token [B,H] or the scalars 1 / 0.
+    """
+    lib = load()
+    S, q, k, v, z, gamma = map(_contig, (S, q, k, v, z, gamma))
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    if isinstance(log_alpha, (int, float)):
+        if log_alpha != 0:
+            raise ValueError("scalar log_alpha must be 0")
+        amode, la = ONES, None
+    else:
+        amode, la = _gate(_contig(log_alpha), 3, "log_alpha")
+    bmode, bt = _gate(_contig(b), 3, "b")
+    wmode, wt = _gate(_contig(w), 3, "w")
+    od = GDR_BF16 if out_dtype == torch.bfloat16 else GDR_F32
+    desc = make_desc(B, H, 1, dk, dv, 64, _dtype_code(q), od, int(bool(normalize_qk)), scale,
+                     amode, bmode, wmode)
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=out_dtype, device=q.device)
+    rc = lib.gdr_decode_step(ctypes.byref(desc), _ptr(S), _ptr(q), _ptr(k), _ptr(v), _ptr(la),
+                             _ptr(bt), _ptr(wt), _ptr(gamma), _ptr(z), _ptr(o), _stream(stream))
+    if rc != GDR_OK:
+        raise GdrError(rc, "gdr_decode_step")
+    return o

@@ -1,0 +1,156 @@
+/*
+ * gdr.h -- C ABI of libgdr.so: the channel-wise gated delta rule on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operation (Muir reading notes, arXiv:2611.08376, section 2.1 "GDN-2 state
+ * update and Muir read-out"; pre-pass from the "Kimi3 = GPT2 x 22580" blog,
+ * section 3 "DeltaNet", forward()).  For every independent stream (b, h) the
+ * state S in R^{dk x dv} (fp32, rows = key channels) evolves token by token:
+ *
+ *   qh  = SiLU(q_t) / max(|SiLU(q_t)|_2, 1e-12)      (skipped if !normalize_qk)
+ *   kn  = SiLU(k_t) / max(|SiLU(k_t)|_2, 1e-12)      (skipped if !normalize_qk)
+ *   qt  = scale * gamma (.) 2 sigmoid(z_t) (.) qh     read-out gain on the query
+ *   S_hat = Diag(alpha_t) S_{t-1},  alpha_t = exp(log_alpha_t) in (0, 1]
+ *   u   = w_t (.) v_t - (b_t (.) kn) S_hat            erase key b (.) k, write w (.) v
+ *   S_t = S_hat + kn^T u
+ *   o_t = qt S_t                                       read after the write
+ *
+ * With b = w = beta this is Kimi Delta Attention, with a scalar alpha Gated
+ * DeltaNet, with alpha = 1 DeltaNet, with b = 0 gated linear attention.  The
+ * notes drop the display equation of the update; the form above is the one
+ * under which their chunk system T Z = [V_hat, K_hat decayed],
+ * T = I + L_strict (section 2.4, "Boundary-Pivoted Chunkwise Kernel") holds.
+ *
+ * Calls
+ *   gdr_chunk_fwd     whole sequences [B, H, T] at once, chunkwise (prefill /
+ *                     training forward); S0 -> S_T
+ *   gdr_decode_step   one token per (sequence, head); state updated in place
+ *
+ * Conventions common to every call
+ *   - Tensors are device pointers owned by the caller, contiguous, row-major,
+ *     head-major:  q, k, z, log_alpha, b (per channel): [B, H, T, dk];
+ *     v, w (per channel), o: [B, H, T, dv]; per-token gates: [B, H, T];
+ *     gamma: [H, dk]; states: [B, H, dk, dv] fp32.  For decode T = 1.
+ *   - Every pointer that is read must be 16-byte aligned.
+ *   - q, k, v, b, w, z share the storage dtype desc->in_dtype; log_alpha,
+ *     gamma and states are always fp32; o has desc->out_dtype.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; 0 = the null
+ *     stream).  The library never synchronises and allocates no device
+ *     memory; chunk_fwd takes its scratch from a caller workspace whose size
+ *     gdr_chunk_fwd_workspace_size() reports.
+ *   - Arguments are validated on the host before anything is launched; a
+ *     failed validation returns its status and has no side effect.  A launch
+ *     failure returns GDR_ERR_HIP.  No C++ exception crosses this ABI.
+ *   - Inputs must not alias outputs, except S_T == S0 in gdr_chunk_fwd and
+ *     the in-place state of gdr_decode_step.
+ *   - Preconditions not checked on the hot path: log_alpha finite and in
+ *     [-30, 0]; b, w, z, gamma finite.  A NaN in one (b, h) stream stays in
+ *     that stream.
+ *   - fp32 inputs (in_dtype = GDR_F32) select the fp32-accurate arithmetic
+ *     (three-term bf16 splits on the matrix cores, relative error ~1e-6);
+ *     bf16 inputs select two-term splits (~1e-5).  State, log-decay and all
+ *     accumulation are fp32 in both.
+ *   - The library keeps no mutable global state: concurrent calls from
+ *     several threads or streams are safe.
+ */
+#ifndef GDR_H
+#define GDR_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gdr_status {
+  GDR_OK = 0,
+  GDR_ERR_INVALID_ARG = 1, /* null / misaligned pointer, bad size or enum      */
+  GDR_ERR_UNSUPPORTED = 2, /* valid but not implemented (e.g. dk not 64/128)   */
+  GDR_ERR_WORKSPACE = 3,   /* workspace pointer null or smaller than required */
+  GDR_ERR_HIP = 4          /* a HIP launch or runtime call failed              */
+} gdr_status;
+
+typedef enum gdr_dtype { GDR_BF16 = 0, GDR_F32 = 1 } gdr_dtype;
+
+/* How a gate argument is given. */
+typedef enum gdr_gate_mode {
+  GDR_GATE_PER_CHANNEL = 0, /* full tensor [B, H, T, d]                          */
+  GDR_GATE_PER_TOKEN = 1,   /* scalar per token [B, H, T], broadcast over d      */
+  GDR_GATE_ONES = 2,        /* pointer ignored; value 1 (for alpha: log_alpha 0) */
+  GDR_GATE_ZEROS = 3        /* pointer ignored; value 0 (b only: linear attention) */
+} gdr_gate_mode;
+
+typedef struct gdr_desc {
+  int B;                    /* batch (decode: number of sequences)            */
+  int H;                    /* heads                                           */
+  int T;                    /* tokens per sequence (ignored by decode, = 1)    */
+  int dk;                   /* key channels: 64 or 128                         */
+  int dv;                   /* value channels: must equal dk                   */
+  int chunk;                /* chunk size of gdr_chunk_fwd: 64 or 128; T % chunk == 0 */
+  gdr_dtype in_dtype;       /* storage of q, k, v, b, w, z                     */
+  gdr_dtype out_dtype;      /* storage of o                                    */
+  int normalize_qk;         /* 1: SiLU + L2 pre-pass on q, k; 0: used as given */
+  float scale;              /* query scale (1.0: no 1/sqrt(d))                 */
+  gdr_gate_mode alpha_mode; /* PER_CHANNEL, PER_TOKEN or ONES                  */
+  gdr_gate_mode b_mode;     /* PER_CHANNEL, PER_TOKEN, ONES or ZEROS           */
+  gdr_gate_mode w_mode;     /* PER_CHANNEL, PER_TOKEN or ONES                  */
+} gdr_desc;
+
+/*
+ * Bytes of device workspace gdr_chunk_fwd needs for `desc` (validated as for
+ * gdr_chunk_fwd).  Written to *bytes on success.
+ */
+gdr_status gdr_chunk_fwd_workspace_size(const gdr_desc *desc, size_t *bytes);
+
+/*
+ * Chunkwise forward of whole sequences (Muir notes section 2.4; the blog's
+ * section 4 chunk form): per chunk of `desc->chunk` tokens, an intra-chunk
+ * kernel builds the decayed key Gram matrix and read-out scores with
+ * boundary pivots (every decay factor exp(Lambda_t - Lambda_s) is formed from
+ * exponents <= 0), solves the unit-lower-triangular system T Z = [V_hat,
+ * K_hat e^Lambda], and reduces the chunk to an affine map of the state; a
+ * scan kernel then carries S in fp32 across chunks and writes o.
+ *
+ *   q, k      [B,H,T,dk] in_dtype        v     [B,H,T,dv] in_dtype
+ *   log_alpha per alpha_mode, fp32       b, w  per b_mode / w_mode, in_dtype
+ *   gamma     [H,dk] fp32 or NULL (= 1)  z     [B,H,T,dk] in_dtype or NULL (2 sigma = 1)
+ *   S0        [B,H,dk,dv] fp32 or NULL (= 0)
+ *   o         [B,H,T,dv] out_dtype (written)
+ *   S_T       [B,H,dk,dv] fp32 or NULL (written; may alias S0)
+ *   workspace >= gdr_chunk_fwd_workspace_size() bytes, 256-byte aligned,
+ *             contents undefined on entry and on return.
+ */
+gdr_status gdr_chunk_fwd(const gdr_desc *desc, const void *q, const void *k,
+                         const void *v, const float *log_alpha, const void *b,
+                         const void *w, const float *gamma, const void *z,
+                         const float *S0, void *o, float *S_T, void *workspace,
+                         size_t workspace_bytes, void *stream);
+
+/*
+ * One decode step for B sequences x H heads (the blog's section 3 forward()
+ * with a one-token x and `cache` = S): reads S once, forms
+ * u = v_hat - k_hat (Diag(alpha) S), writes S <- Diag(alpha) S + kn^T u in
+ * place and o = qt S.  desc->T and desc->chunk are ignored.
+ *
+ *   S         [B,H,dk,dv] fp32, updated in place
+ *   q, k, z   [B,H,dk] in_dtype (z may be NULL)    v [B,H,dv] in_dtype
+ *   log_alpha [B,H,dk] or [B,H] fp32 per alpha_mode
+ *   b, w      [B,H,d] or [B,H] per mode             gamma [H,dk] fp32 or NULL
+ *   o         [B,H,dv] out_dtype (written)
+ */
+gdr_status gdr_decode_step(const gdr_desc *desc, float *S, const void *q,
+                           const void *k, const void *v, const float *log_alpha,
+                           const void *b, const void *w, const float *gamma,
+                           const void *z, void *o, void *stream);
+
+/* Static, human-readable name of a status code. */
+const char *gdr_status_string(gdr_status status);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int gdr_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDR_H */

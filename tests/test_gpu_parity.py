@@ -1,0 +1,333 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Bars (element-wise relative L2 over the whole tensor, outputs and final states
+both compared): <= 2e-3 for bf16 inputs, <= 1e-5 for fp32 inputs.  Small cases
+run the oracle on everything; the workloads at their full sizes run the GPU on
+everything, in the launch configuration the benchmark times, and the oracle on
+sampled (batch, head) streams.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from channel_wise_gated_amd import gdr
+from channel_wise_gated_amd.inputs import WORKLOADS, make_inputs
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TOL_BF16 = 2e-3
+TOL_F32 = 1e-5
+
+
+def rel(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def tol_for(x):
+    return TOL_BF16 if x["q"].dtype == torch.bfloat16 else TOL_F32
+
+
+def dev(x):
+    return {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+
+
+def gpu_chunk(x, chunk, **kw):
+    d = dev(x)
+    o, sT = gdr.gdr_chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"],
+                              gamma=d["gamma"], z=d["z"], S0=d["S0"], chunk=chunk, **kw)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), sT.cpu().numpy()
+
+
+def oracle_run(x, **kw):
+    return oracle.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"],
+                          gamma=x["gamma"], z=x["z"], S0=x["S0"], **kw)
+
+
+def sample_streams(x, pairs):
+    """Inputs of the chosen (b, h) streams as a [1, n, ...] problem."""
+    out = {}
+    for key, val in x.items():
+        if not isinstance(val, torch.Tensor):
+            out[key] = val
+        elif key == "gamma":
+            out[key] = torch.stack([val[h] for _, h in pairs])
+        else:
+            out[key] = torch.stack([val[b, h] for b, h in pairs])[None]
+    return out
+
+
+def check(name, got, ref, tol):
+    e = rel(got, ref)
+    print(f"{name}: rel L2 {e:.3e} (tol {tol:.0e})", flush=True)
+    assert np.all(np.isfinite(got)), name
+    assert e <= tol, (name, e)
+    return e
+
+
+# ----------------------------------------------------------------------------
+# chunkwise forward, small sizes: oracle on everything
+# ----------------------------------------------------------------------------
+
+def test_chunk_tiny_fp32_full_config():
+    wl = WORKLOADS["tiny"]
+    x = make_inputs(wl)
+    o, sT = gpu_chunk(x, wl.chunk)
+    ro, rs = oracle_run(x)
+    check("tiny o", o, ro, TOL_F32)
+    check("tiny S_T", sT, rs, TOL_F32)
+
+
+@pytest.mark.parametrize("name,chunk,T", [
+    ("kda", 64, 512), ("gdn2", 64, 512), ("gdn2", 128, 512), ("stress", 64, 1024),
+    ("stress", 128, 1024), ("tiny", 64, 192)])
+def test_chunk_small_cases(name, chunk, T):
+    wl = WORKLOADS[name].with_sizes(B=2 if name != "tiny" else 1, H=3, T=T)
+    x = make_inputs(wl)
+    o, sT = gpu_chunk(x, chunk)
+    ro, rs = oracle_run(x)
+    check(f"{name} C{chunk} o", o, ro, tol_for(x))
+    check(f"{name} C{chunk} S_T", sT, rs, tol_for(x))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d,chunk", [(64, 64), (64, 128), (128, 64)])
+def test_chunk_dims_and_dtypes(dtype, d, chunk):
+    wl = WORKLOADS["gdn2"].with_sizes(B=1, H=2, T=256, dk=d, dv=d, dtype=dtype)
+    x = make_inputs(wl)
+    o, sT = gpu_chunk(x, chunk)
+    ro, rs = oracle_run(x)
+    check(f"{dtype} d{d} C{chunk} o", o, ro, tol_for(x))
+    check(f"{dtype} d{d} C{chunk} S_T", sT, rs, tol_for(x))
+
+
+# ----------------------------------------------------------------------------
+# the workloads at full size: GPU on everything, oracle on sampled streams
+# ----------------------------------------------------------------------------
+
+FULL = [("kda", 64, [(0, 0), (1, 7), (2, 11), (3, 15)]),
+        ("gdn2", 64, [(0, 3), (1, 12)]),
+        ("stress", 64, [(0, 0), (0, 9)]),
+        ("stress", 128, [(0, 5), (0, 14)])]
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,chunk,pairs", FULL)
+def test_chunk_full_size_sampled(name, chunk, pairs):
+    wl = WORKLOADS[name]
+    print(f"full-size {name} B{wl.B} H{wl.H} T{wl.T} C{chunk}", flush=True)
+    x = make_inputs(wl)
+    o, sT = gpu_chunk(x, chunk)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(sT))
+    xs = sample_streams(x, pairs)
+    ro, rs = oracle_run(xs)
+    got_o = np.stack([o[b, h] for b, h in pairs])[None]
+    got_s = np.stack([sT[b, h] for b, h in pairs])[None]
+    check(f"{name} C{chunk} o sampled", got_o, ro, TOL_BF16)
+    check(f"{name} C{chunk} S_T sampled", got_s, rs, TOL_BF16)
+
+
+# ----------------------------------------------------------------------------
+# decode
+# ----------------------------------------------------------------------------
+
+def decode_inputs(wl, step):
+    x = make_inputs(wl, step=step)
+    sq = {}
+    for key in ("q", "k", "v", "log_alpha", "z"):
+        sq[key] = None if x[key] is None else x[key][:, :, 0]
+    for key in ("b", "w"):
+        val = x[key]
+        sq[key] = val[:, :, 0] if val.dim() == 4 else val[:, :, 0]
+    sq["gamma"] = x["gamma"]
+    sq["S0"] = x["S0"]
+    return sq
+
+
+def gpu_decode(S, x, **kw):
+    d = dev(x)
+    return gdr.gdr_decode_step(S, d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"],
+                               gamma=d["gamma"], z=d["z"], **kw)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("gates", ["gdn2", "kda"])
+def test_decode_small_many_steps(d, dtype, gates):
+    wl = WORKLOADS["decode"].with_sizes(B=3, H=2, dk=d, dv=d, dtype=dtype, gates=gates)
+    x0 = decode_inputs(wl, 0)
+    S = x0["S0"].clone().to(DEV)
+    Sref = x0["S0"].double().numpy()
+    outs, refs = [], []
+    for step in range(12):
+        x = decode_inputs(wl, step)
+        o = gpu_decode(S, x)
+        ro, Sref = oracle.decode_step(Sref, x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"],
+                                      gamma=x["gamma"], z=x["z"])
+        outs.append(o.float().cpu().numpy())
+        refs.append(ro)
+    torch.cuda.synchronize()
+    tol = TOL_BF16 if dtype == "bf16" else TOL_F32
+    check(f"decode d{d} {dtype} {gates} o", np.stack(outs), np.stack(refs), tol)
+    check(f"decode d{d} {dtype} {gates} S", S.cpu().numpy(), Sref, tol)
+
+
+@pytest.mark.timeout(1200)
+def test_decode_full_config_1024_steps():
+    """256 sequences x 16 heads, 1024 consecutive steps, one launch per step;
+    the oracle follows 24 sampled streams through all steps."""
+    wl = WORKLOADS["decode"]
+    pairs = [(b, h) for b in (0, 37, 101, 200, 255, 128) for h in (0, 5, 10, 15)]
+    bi = torch.tensor([p[0] for p in pairs])
+    hi = torch.tensor([p[1] for p in pairs])
+    x0 = decode_inputs(wl, 0)
+    S = x0["S0"].clone().to(DEV)
+    Sref = x0["S0"][bi, hi][None].double().numpy()
+    gam = x0["gamma"][hi]
+    o_err_num = o_err_den = 0.0
+    checkpoints = {}
+    for step in range(wl.steps):
+        x = decode_inputs(wl, step)
+        o = gpu_decode(S, x)
+        xs = {k: (None if v is None else v[bi, hi][None]) for k, v in x.items()
+              if k not in ("gamma", "S0")}
+        ro, Sref = oracle.decode_step(Sref, xs["q"], xs["k"], xs["v"], xs["log_alpha"], xs["b"],
+                                      xs["w"], gamma=gam, z=xs["z"], threads=8)
+        got = o[bi.to(DEV), hi.to(DEV)].float().cpu().numpy()
+        o_err_num += float(np.sum((got - ro[0]) ** 2))
+        o_err_den += float(np.sum(ro[0] ** 2))
+        if step in (0, 511, wl.steps - 1):
+            checkpoints[step] = (S[bi.to(DEV), hi.to(DEV)].cpu().numpy(), Sref[0].copy())
+        if step % 128 == 0:
+            print(f"decode step {step}", flush=True)
+    assert np.all(np.isfinite(S.cpu().numpy()))
+    e = (o_err_num / o_err_den) ** 0.5
+    print(f"decode 1024 steps o rel L2 {e:.3e}", flush=True)
+    assert e <= TOL_BF16
+    for step, (got, ref) in checkpoints.items():
+        check(f"decode S after step {step + 1}", got, ref, TOL_BF16)
+
+
+def test_decode_equals_chunk():
+    """Running the decode step T times equals one chunkwise call."""
+    wl = WORKLOADS["gdn2"].with_sizes(B=1, H=2, T=128)
+    x = make_inputs(wl)
+    o_chunk, s_chunk = gpu_chunk(x, 64)
+    S = x["S0"].clone().to(DEV)
+    outs = []
+    for t in range(wl.T):
+        xt = {k: (v[:, :, t] if isinstance(v, torch.Tensor) and k not in ("gamma", "S0") else v)
+              for k, v in x.items()}
+        outs.append(gpu_decode(S, xt).float().cpu().numpy())
+    torch.cuda.synchronize()
+    o_dec = np.stack(outs, axis=2)
+    ro, rs = oracle_run(x)
+    check("decode-as-prefill o", o_dec, ro, TOL_BF16)
+    check("chunk o", o_chunk, ro, TOL_BF16)
+    check("decode-as-prefill S", S.cpu().numpy(), rs, TOL_BF16)
+    check("decode vs chunk S", S.cpu().numpy(), s_chunk, 2 * TOL_BF16)
+
+
+# ----------------------------------------------------------------------------
+# edge cases and degenerate gates
+# ----------------------------------------------------------------------------
+
+def test_zero_length_sequence_copies_state():
+    wl = WORKLOADS["gdn2"].with_sizes(B=2, H=3, T=64)
+    x = dev(make_inputs(wl))
+    q = x["q"][:, :, :0].contiguous()
+    o, sT = gdr.gdr_chunk_fwd(q, q, q, x["log_alpha"][:, :, :0].contiguous(),
+                              x["b"][:, :, :0].contiguous(), x["w"][:, :, :0].contiguous(),
+                              gamma=x["gamma"], z=q, S0=x["S0"])
+    torch.cuda.synchronize()
+    assert o.numel() == 0
+    assert torch.equal(sT, x["S0"])
+    _, sT0 = gdr.gdr_chunk_fwd(q, q, q, x["log_alpha"][:, :, :0].contiguous(),
+                               x["b"][:, :, :0].contiguous(), x["w"][:, :, :0].contiguous())
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(sT0).item() == 0
+
+
+@pytest.mark.parametrize("chunk", [64, 128])
+def test_alpha_zero_and_extreme_decay_runs(chunk):
+    """log alpha = -30 (alpha ~ 0: memory cleared) at single tokens, and long
+    runs of it that force the exact-exponential path of diagonal blocks."""
+    wl = WORKLOADS["gdn2"].with_sizes(B=1, H=2, T=256)
+    x = make_inputs(wl)
+    la = x["log_alpha"].clone()
+    la[:, 0, 37] = -30.0
+    la[:, 1, 100:140] = -30.0      # a run wider than a 16-token block
+    la[:, 1, 200:203, :64] = -30.0
+    x["log_alpha"] = la
+    o, sT = gpu_chunk(x, chunk)
+    ro, rs = oracle_run(x)
+    check(f"alpha->0 C{chunk} o", o, ro, TOL_BF16)
+    check(f"alpha->0 C{chunk} S_T", sT, rs, TOL_BF16)
+
+
+def test_gate_modes_and_options():
+    wl = WORKLOADS["gdn2"].with_sizes(B=1, H=2, T=128)
+    x = make_inputs(wl)
+    cases = {
+        "linear-attention (b=0, alpha=1, w=1)": dict(log_alpha=0, b=0, w=1),
+        "per-token alpha and gates": dict(log_alpha=x["log_alpha"][..., 0].contiguous(),
+                                          b=x["b"][..., 0].contiguous(), w=x["w"][..., 0].contiguous()),
+        "DeltaNet (alpha=1, b=w=1)": dict(log_alpha=0, b=1, w=1),
+    }
+    for label, over in cases.items():
+        y = dict(x)
+        y.update(over)
+        o, sT = gpu_chunk(y, 64)
+        ro, rs = oracle_run(y)
+        check(label + " o", o, ro, TOL_BF16)
+        check(label + " S_T", sT, rs, TOL_BF16)
+    # no pre-pass normalisation, a query scale and a bf16 output
+    y = dict(x)
+    kn = torch.nn.functional.normalize(x["k"].float(), dim=-1).to(torch.bfloat16)
+    y["k"] = kn
+    d = dev(y)
+    o, sT = gdr.gdr_chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"],
+                              gamma=d["gamma"], z=d["z"], S0=d["S0"], normalize_qk=False,
+                              scale=0.125, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ro, rs = oracle_run(y, normalize_qk=False, scale=0.125)
+    # bf16 storage of o alone costs ~1.7e-3 relative L2; the state stays fp32
+    check("raw qk, scale, bf16 o", o.float().cpu().numpy(), ro, 3e-3)
+    check("raw qk, scale S_T", sT.cpu().numpy(), rs, TOL_BF16)
+
+
+def test_zero_keys_and_state_aliasing():
+    wl = WORKLOADS["gdn2"].with_sizes(B=1, H=2, T=128)
+    x = make_inputs(wl)
+    k = x["k"].clone()
+    k[:, :, 10] = 0.0          # SiLU(0) = 0: unit-norm floor gives a zero key
+    k[:, :, 77:80] = 0.0
+    x["k"] = k
+    ro, rs = oracle_run(x)
+    d = dev(x)
+    S = d["S0"].clone()
+    o, sT = gdr.gdr_chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"],
+                              gamma=d["gamma"], z=d["z"], S0=S, S_T=S)   # S_T aliases S0
+    torch.cuda.synchronize()
+    assert sT.data_ptr() == S.data_ptr()
+    check("zero keys o", o.cpu().numpy(), ro, TOL_BF16)
+    check("zero keys, aliased S", S.cpu().numpy(), rs, TOL_BF16)
+
+
+def test_nan_stays_in_its_stream_and_runs_are_deterministic():
+    wl = WORKLOADS["gdn2"].with_sizes(B=2, H=3, T=256)
+    x = make_inputs(wl)
+    o1, s1 = gpu_chunk(x, 64)
+    o2, s2 = gpu_chunk(x, 64)
+    assert np.array_equal(o1, o2) and np.array_equal(s1, s2)
+    v = x["v"].clone()
+    v[1, 2, 70, 5] = float("nan")
+    x["v"] = v
+    o3, s3 = gpu_chunk(x, 64)
+    assert np.isnan(o3[1, 2]).any()
+    mask = np.ones(o3.shape[:2], dtype=bool)
+    mask[1, 2] = False
+    assert np.array_equal(o3[mask], o1[mask]) and np.array_equal(s3[mask], s1[mask])
