@@ -1,0 +1,235 @@
+#!/usr/bin/env python3
+"""Benchmark of the channel-wise gated delta rule on one MI355X.
+
+A step is one chunkwise forward (both kernels) over the long-context stress
+workload: B1 H16 T32768 dk=dv=128, bf16 inputs, fp32 output and state, chunk
+128 (default) -- inputs resident in HBM before the timed region.  The decode
+step (256 sequences x 16 heads, fp32 128 x 128 states, 1024 consecutive
+steps) is timed in the same run and reported beside it.
+
+Prints one JSON line.  Per-kernel durations come from HIP events recorded on
+the stream the kernels run on; the roofline object describes the kernel with
+the largest share of the step.  The fp64 CPU oracle is timed on a bounded
+sample of the same workload (rank 0, N = 1 only) as `cpu_baseline`.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--chunk 64|128]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
+METRIC = "tokens/s + % bf16 MFMA peak, chunk fwd T=32K H=16 d=128; decode HBM GB/s"
+PMC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def flops_per_token_head(C, dk, dv):
+    """Algorithmic flops of the chunk path per (token, head): the three
+    state products (Y S, Qt S, K'^T U: 2 C dk dv each per chunk) plus the
+    intra-chunk work (Gram and scores C^2 dk each, triangular solve with
+    dk + dv right-hand sides C^2 (dk + dv), A U C^2 dv), triangles counted
+    once, divided by C."""
+    return 6 * dk * dv + C * (3 * dk + 2 * dv)
+
+
+def chunk_bytes_per_token_head(dk, dv, in_bytes=2, out_bytes=4, gain=True):
+    """HBM bytes that must move per (token, head): q, k, v, b, w (+ z) in the
+    input dtype, fp32 log-decay, o in the output dtype."""
+    n_in = 5 + (1 if gain else 0)
+    return n_in * dk * in_bytes - (dk - dv) * 2 * in_bytes + 4 * dk + out_bytes * dv
+
+
+def sources_digest():
+    h = hashlib.sha256()
+    for name in ("gdr_chunk.hip", "gdr_decode.hip", "gdr_device.h"):
+        with open(os.path.join(ROOT, "channel_wise_gated_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def timed_chunk(call, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in ev:
+        e[0].record()
+        call.intra()
+        e[1].record()
+        call.scan()
+        e[2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    intra = sorted(e[0].elapsed_time(e[1]) for e in ev)
+    scan = sorted(e[1].elapsed_time(e[2]) for e in ev)
+    return wall, intra, scan
+
+
+def timed_decode(wl, steps, warmup):
+    import ctypes
+
+    import torch
+
+    from channel_wise_gated_amd import gdr
+    from channel_wise_gated_amd.inputs import make_inputs_device
+    lib = gdr.load()
+    x = make_inputs_device(wl, "cuda", steps=steps)
+    S = x["S0"].clone()
+    o = torch.empty((wl.B, wl.H, wl.dv), dtype=torch.float32, device="cuda")
+    desc = gdr.make_desc(wl.B, wl.H, 1, wl.dk, wl.dv, 64, gdr.GDR_BF16, gdr.GDR_F32)
+    stream = ctypes.c_void_p(int(torch.cuda.current_stream().cuda_stream))
+    # marshal every step's arguments before timing
+    args = []
+    for s in range(steps):
+        p = [ctypes.c_void_p(x[n][s].data_ptr()) for n in ("q", "k", "v", "log_alpha", "b", "w")]
+        args.append((ctypes.byref(desc), ctypes.c_void_p(S.data_ptr()), *p,
+                     ctypes.c_void_p(x["gamma"].data_ptr()), ctypes.c_void_p(x["z"][s].data_ptr()),
+                     ctypes.c_void_p(o.data_ptr()), stream))
+    for s in range(warmup):
+        if lib.gdr_decode_step(*args[s % steps]) != 0:
+            raise RuntimeError("gdr_decode_step failed")
+    S.copy_(x["S0"])
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    t0 = time.perf_counter()
+    ev[0].record()
+    for s in range(steps):
+        lib.gdr_decode_step(*args[s])
+        ev[s + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = sorted(ev[s].elapsed_time(ev[s + 1]) for s in range(steps))
+    del x
+    return wall, per
+
+
+def cpu_baseline(x, target_s=12.0):
+    """The fp64 oracle, as it stands, on the first Ts tokens of every head."""
+    import oracle
+    import numpy as np
+
+    def sample(Ts):
+        return {k: (v[:, :, :Ts].cpu() if (v is not None and v.dim() == 4 and k != "S0")
+                    else (v.cpu() if v is not None else None)) for k, v in x.items()}
+
+    H = x["q"].shape[1]
+    threads = oracle.default_threads(H * x["q"].shape[0])
+    probe = 512
+    s = sample(probe)
+    t0 = time.perf_counter()
+    oracle.forward(s["q"], s["k"], s["v"], s["log_alpha"], s["b"], s["w"], gamma=s["gamma"],
+                   z=s["z"], S0=s["S0"], threads=threads)
+    rate = probe / (time.perf_counter() - t0)
+    T = x["q"].shape[2]
+    Ts = int(min(T, max(probe, (rate * target_s) // 64 * 64)))
+    s = sample(Ts)
+    t0 = time.perf_counter()
+    oracle.forward(s["q"], s["k"], s["v"], s["log_alpha"], s["b"], s["w"], gamma=s["gamma"],
+                   z=s["z"], S0=s["S0"], threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": round(Ts * x["q"].shape[0] / dt, 1), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"first {Ts} of {T} tokens, all {H} heads, fp64 token recurrence"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--chunk", type=int, default=128, choices=(64, 128))
+    ap.add_argument("--decode-steps", type=int, default=1024)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} requested, but this build runs on exactly one GPU "
+              "(the recurrence shards over (batch, head) streams with no communication; no "
+              "multi-GPU path is built). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from channel_wise_gated_amd import gdr
+    from channel_wise_gated_amd.inputs import WORKLOADS, make_inputs_device
+
+    torch.cuda.set_device(0)
+    gdr.load()
+    wl = WORKLOADS["stress"]
+    C = args.chunk
+    x = make_inputs_device(wl, "cuda")
+    call = gdr.ChunkCall(x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"], x["gamma"],
+                         x["z"], x["S0"], chunk=C)
+    wall, intra, scan = timed_chunk(call, args.steps, args.warmup)
+    ms_step = 1e3 * wall / args.steps
+    med = lambda a: a[len(a) // 2]
+    intra_ms, scan_ms = med(intra), med(scan)
+    BH = wl.B * wl.H
+    toks = wl.B * wl.T
+    tok_s = toks / (ms_step / 1e3)
+    fl = flops_per_token_head(C, wl.dk, wl.dv) * BH * wl.T
+    tflops = fl / (ms_step / 1e3) / 1e12
+    byt = chunk_bytes_per_token_head(wl.dk, wl.dv) * BH * wl.T + 2 * BH * wl.dk * wl.dv * 4
+    gbs = byt / (ms_step / 1e3) / 1e9
+
+    # roofline of the kernel with the largest share of the step
+    in_bytes = (chunk_bytes_per_token_head(wl.dk, wl.dv) - 4 * wl.dv) * BH * wl.T
+    out_bytes = 4 * wl.dv * BH * wl.T + 2 * BH * wl.dk * wl.dv * 4
+    if intra_ms >= scan_ms:
+        kname, kms, kbytes = "chunk_intra_kernel", intra_ms, in_bytes
+    else:
+        kname, kms, kbytes = "chunk_scan_kernel", scan_ms, out_bytes
+    achieved = kbytes / (kms / 1e3) / 1e9
+    traffic = None
+    if os.path.exists(PMC_FILE):
+        with open(PMC_FILE) as f:
+            pmc = json.load(f)
+        ent = pmc.get(f"{kname}_C{C}")
+        if ent and pmc.get("sources") == sources_digest():
+            traffic = ent.get("bytes_per_launch")
+    roof = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "algorithmic_bytes_per_launch": kbytes, "avg_ms": round(sum(intra if kname.endswith(
+                "intra_kernel") else scan) / args.steps, 4)}
+
+    # decode
+    dwl = WORKLOADS["decode"]
+    dsteps = args.decode_steps
+    dwall, dper = timed_decode(dwl, dsteps, warmup=min(16, dsteps))
+    dbytes = dwl.B * dwl.H * (2 * dwl.dk * dwl.dv * 4 + 6 * dwl.dk * 2 + 4 * dwl.dk + 4 * dwl.dv)
+    d_us = 1e3 * sum(dper) / dsteps
+    d_gbs = dbytes / (d_us / 1e6) / 1e9
+
+    line = {
+        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"stress B{wl.B} H{wl.H} T{wl.T} dk{wl.dk} dv{wl.dv} chunk{C}",
+                   "inputs": "bf16 q,k,v,b,w,z; fp32 log-decay, gain, state and o",
+                   "arith": "bf16 hi/lo-split MFMA, fp32 accumulate and state"},
+        "tflops_algorithmic": round(tflops, 2), "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+        "hbm_gbs_algorithmic": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "kernels_ms": {"chunk_intra_kernel": round(intra_ms, 4), "chunk_scan_kernel": round(scan_ms, 4)},
+        "roofline": roof,
+        "decode": {"workload": f"decode {dwl.B} seq x H{dwl.H}, fp32 state {dwl.dk}x{dwl.dv}, "
+                               f"{dsteps} steps", "us_per_step": round(d_us, 2),
+                   "gbs": round(d_gbs, 1), "hbm_frac": round(d_gbs / HBM_PEAK_GBS, 4),
+                   "bytes_per_step": dbytes, "wall_s": round(dwall, 3)},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(x)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -63,31 +63,23 @@ gdr_status chunk_plan(const gdr_desc *d, size_t *ws) {
   return GDR_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-gdr_status gdr_chunk_fwd_workspace_size(const gdr_desc *desc, size_t *bytes) {
-  if (!bytes) return GDR_ERR_INVALID_ARG;
-  size_t ws = 0;
-  gdr_status s = chunk_plan(desc, &ws);
-  if (s == GDR_OK) *bytes = ws;
-  return s;
-}
-
-gdr_status gdr_chunk_fwd(const gdr_desc *desc, const void *q, const void *k, const void *v,
-                         const float *log_alpha, const void *b, const void *w, const float *gamma,
-                         const void *z, const float *S0, void *o, float *S_T, void *workspace,
-                         size_t workspace_bytes, void *stream) {
+// Validation and launch shared by the whole call (phases = 3), the
+// intra-chunk phase (1: reads the token inputs, writes the workspace) and the
+// scan phase (2: reads the workspace and S0, writes o and S_T).
+gdr_status chunk_call(const gdr_desc *desc, const void *q, const void *k, const void *v,
+                      const float *log_alpha, const void *b, const void *w, const float *gamma,
+                      const void *z, const float *S0, void *o, float *S_T, void *workspace,
+                      size_t workspace_bytes, void *stream, int phases) {
   size_t need = 0;
   gdr_status s = chunk_plan(desc, &need);
   if (s != GDR_OK) return s;
   const gdr_desc &d = *desc;
   if ((size_t)d.B * d.H == 0) return GDR_OK;
-  if (d.T > 0) {
-    s = check_inputs(desc, q, k, v, log_alpha, b, w, gamma, z, o);
+  if (d.T > 0 && (phases & 1)) {
+    s = check_inputs(desc, q, k, v, log_alpha, b, w, gamma, z, (phases & 2) ? o : q);
     if (s != GDR_OK) return s;
   }
+  if (d.T > 0 && (phases & 2) && (!o || !aligned16(o))) return GDR_ERR_INVALID_ARG;
   if ((S0 && !aligned16(S0)) || (S_T && !aligned16(S_T))) return GDR_ERR_INVALID_ARG;
   if (need > 0 && (!workspace || workspace_bytes < need)) return GDR_ERR_WORKSPACE;
   if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u)) return GDR_ERR_WORKSPACE;
@@ -110,8 +102,42 @@ gdr_status gdr_chunk_fwd(const gdr_desc *desc, const void *q, const void *k, con
   a.B = d.B; a.H = d.H; a.T = d.T;
   a.alpha_mode = d.alpha_mode; a.b_mode = d.b_mode; a.w_mode = d.w_mode;
   a.normalize_qk = d.normalize_qk; a.scale = d.scale;
-  hipError_t e = gdr::launch_chunk(d, a, static_cast<hipStream_t>(stream));
+  hipError_t e = gdr::launch_chunk(d, a, phases, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdr_status gdr_chunk_fwd_workspace_size(const gdr_desc *desc, size_t *bytes) {
+  if (!bytes) return GDR_ERR_INVALID_ARG;
+  size_t ws = 0;
+  gdr_status s = chunk_plan(desc, &ws);
+  if (s == GDR_OK) *bytes = ws;
+  return s;
+}
+
+gdr_status gdr_chunk_fwd(const gdr_desc *desc, const void *q, const void *k, const void *v,
+                         const float *log_alpha, const void *b, const void *w, const float *gamma,
+                         const void *z, const float *S0, void *o, float *S_T, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+  return chunk_call(desc, q, k, v, log_alpha, b, w, gamma, z, S0, o, S_T, workspace,
+                    workspace_bytes, stream, 3);
+}
+
+gdr_status gdr_chunk_fwd_intra(const gdr_desc *desc, const void *q, const void *k, const void *v,
+                               const float *log_alpha, const void *b, const void *w,
+                               const float *gamma, const void *z, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+  return chunk_call(desc, q, k, v, log_alpha, b, w, gamma, z, nullptr, nullptr, nullptr, workspace,
+                    workspace_bytes, stream, 1);
+}
+
+gdr_status gdr_chunk_fwd_scan(const gdr_desc *desc, const float *S0, void *o, float *S_T,
+                              const void *workspace, size_t workspace_bytes, void *stream) {
+  return chunk_call(desc, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                    S0, o, S_T, const_cast<void *>(workspace), workspace_bytes, stream, 2);
 }
 
 gdr_status gdr_decode_step(const gdr_desc *desc, float *S, const void *q, const void *k,

@@ -99,38 +99,52 @@ __device__ __forceinline__ void load_frag(const uint16_t *base, size_t plane_str
 
 template <int C, int D, int NS>
 struct IntraLds {
-  static constexpr int NB = C / 16, NKC = C / 32;
-  static constexpr int LAM_LD = D + 4;     // padded rows: conflict-free 16-byte reads
-  static constexpr int TILE_LD = 20;
+  static constexpr int NB = C / 16, NKC = C / 32, NKD = D / 32;
+  static constexpr int TILE_LD = 20;       // padded 16 x 16 fp32 tiles
   static constexpr int TILE_SZ = 16 * TILE_LD;
   static constexpr int NTILES = NB * (NB + 1) / 2;
   static constexpr int FRAG = 64 * 8;      // bf16 per fragment plane
   static constexpr int STAGE = NKC * 2 * NS * FRAG;
-  static constexpr size_t bytes = sizeof(float) * ((size_t)C * LAM_LD + 2 * C + NTILES * TILE_SZ) +
-                                  sizeof(uint16_t) * 2 * STAGE + sizeof(int) * NB;
+  // float offsets
+  static constexpr int KCF = 0;                        // [NB][NKD][64][8]  kn * Cf
+  static constexpr int CUM = KCF + C * D;              // [NB + 1][D]      block-start log decay
+  static constexpr int NRM = CUM + (NB + 1) * D;       // [2][C]           inverse norms of q, k
+  static constexpr int LT = NRM + 2 * C;               // [NTILES][TILE_SZ] L, then T^-1
+  static constexpr int STG = LT + NTILES * TILE_SZ;    // R and Z staging (bf16)
+  static constexpr size_t bytes = sizeof(float) * (size_t)STG + sizeof(uint16_t) * 2 * STAGE +
+                                  sizeof(int) * NB;
+  static constexpr int WAVES = NB > D / 16 ? NB : D / 16;
 };
 
+// Channel held by (lane group g, k-step ks, element e) in tile-pair order.
+__device__ __forceinline__ int tp_chan(int ks, int g, int e) { return 32 * ks + 16 * (e >> 2) + 4 * g + (e & 3); }
+
 // ============================================================================
-// Kernel 1: one workgroup (8 waves) per (stream, chunk).
+// Kernel 1: one workgroup per (stream, chunk); wave i owns token block i
+// (16 tokens) and channel tile i.  Per-token values live in the registers of
+// the owning wave in "row-operand" layout: lane (t = l%16, g = l/16) holds
+// channels tp_chan(ks, g, e) of token t.
 // ============================================================================
 template <int C, int D, int NS, bool BF>
 __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
   using Lds = IntraLds<C, D, NS>;
   constexpr int NB = C / 16, NKC = C / 32, NKD = D / 32, NMT = D / 16;
-  constexpr int LAM_LD = Lds::LAM_LD, TILE_LD = Lds::TILE_LD, TILE_SZ = Lds::TILE_SZ;
-  constexpr int FRAG = Lds::FRAG;
-  static_assert(NB <= 8 && NMT <= 8, "one wave per block row and per channel tile");
+  constexpr int TILE_LD = Lds::TILE_LD, TILE_SZ = Lds::TILE_SZ, FRAG = Lds::FRAG;
+  static_assert(NB <= 8 && NMT <= 8, "one wave per token block and per channel tile");
 
   extern __shared__ __align__(16) unsigned char smem[];
-  float *lam = reinterpret_cast<float *>(smem);
-  float *inq = lam + C * LAM_LD;
+  float *sm = reinterpret_cast<float *>(smem);
+  float *kcf = sm + Lds::KCF;
+  float *cum = sm + Lds::CUM;
+  float *inq = sm + Lds::NRM;
   float *ink = inq + C;
-  float *Lt = ink + C;
-  uint16_t *rst = reinterpret_cast<uint16_t *>(Lt + Lds::NTILES * TILE_SZ);
+  float *Lt = sm + Lds::LT;
+  uint16_t *rst = reinterpret_cast<uint16_t *>(sm + Lds::STG);
   uint16_t *zst = rst + Lds::STAGE;
   int *dflag = reinterpret_cast<int *>(zst + Lds::STAGE);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int l16 = lane & 15, g = lane >> 4;
   const int NC = a.T / C;
   const size_t ch = blockIdx.x;
@@ -138,126 +152,153 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
   const int h = (int)(bh % a.H);
   const size_t row0 = bh * (size_t)a.T + (size_t)(ch % NC) * C;  // first token row
   const bool norm = a.normalize_qk != 0;
+  const bool rowwave = wave < NB;
+  const int i = wave;                       // token block of this wave
+  const int t = 16 * i + l16;               // token of this lane (row-operand layout)
+  const size_t rowt = row0 + t;
 
-  // -------------------------------------------------- A1: inverse norms
-  for (int t = wave; t < C; t += 8) {
+  // ----------------------------------------------------------- A: pre-pass
+  // QRp / KRp: NS bf16 planes of qt * R and k_hat * R, R = exp(P_t), P the
+  // inclusive log-decay prefix inside the block (<= 0).
+  bf16x8 QRp[NKD][NS], KRp[NKD][NS];
+  if (rowwave) {
+    float qv[NKD][8], kv[NKD][8], zv[NKD][8], bv[NKD][8], lv[NKD][8], gm[NKD][8];
+#pragma unroll
+    for (int ks = 0; ks < NKD; ++ks)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int c0 = 32 * ks + 16 * hh + 4 * g;
+        ld4<BF>(a.q, rowt * D + c0, &qv[ks][4 * hh]);
+        ld4<BF>(a.k, rowt * D + c0, &kv[ks][4 * hh]);
+        if (a.z) ld4<BF>(a.z, rowt * D + c0, &zv[ks][4 * hh]);
+        gate4<BF>(a.b, a.b_mode, rowt, c0, D, &bv[ks][4 * hh]);
+        log_alpha4(a.log_alpha, a.alpha_mode, rowt, c0, D, &lv[ks][4 * hh]);
+        if (a.gamma) {
+          float4 f = *reinterpret_cast<const float4 *>(a.gamma + (size_t)h * D + c0);
+          gm[ks][4 * hh] = f.x; gm[ks][4 * hh + 1] = f.y; gm[ks][4 * hh + 2] = f.z; gm[ks][4 * hh + 3] = f.w;
+        }
+      }
     float sq = 0.f, sk = 0.f;
-    for (int c = lane; c < D; c += 64) {
-      float qv = ld1<BF>(a.q, (row0 + t) * D + c), kv = ld1<BF>(a.k, (row0 + t) * D + c);
-      if (norm) { qv = silu(qv); kv = silu(kv); }
-      sq += qv * qv;
-      sk += kv * kv;
-    }
-    sq = wave_sum(sq);
-    sk = wave_sum(sk);
-    if (lane == 0) {
-      inq[t] = norm ? 1.f / fmaxf(sqrtf(sq), 1e-12f) : 1.f;
-      ink[t] = norm ? 1.f / fmaxf(sqrtf(sk), 1e-12f) : 1.f;
-    }
-  }
-  // -------------------------------------------------- A2: Lambda (prefix over tokens)
-  {
-    constexpr int P = 512 / D, TP = C / P;
-    const int c = tid % D, part = tid / D;
-    float *tot = Lt;  // scratch, Lt is not live yet
-    float run = 0.f;
-    for (int u = 0; u < TP; ++u) {
-      const int t = part * TP + u;
-      run += log_alpha_at(a.log_alpha, a.alpha_mode, row0 + t, c, D);
-      lam[t * LAM_LD + c] = run;
-    }
-    tot[part * D + c] = run;
-    __syncthreads();
-    float off = 0.f;
-    for (int p2 = 0; p2 < part; ++p2) off += tot[p2 * D + c];
-    if (part)
-      for (int u = 0; u < TP; ++u) lam[(part * TP + u) * LAM_LD + c] += off;
-  }
-  __syncthreads();
-  // diagonal-block decay ranges
-  if (wave < NB) {
-    const int i = wave;
-    float m = 0.f;
-    for (int c = lane; c < D; c += 64) {
-      const float ref = i ? lam[(16 * i - 1) * LAM_LD + c] : 0.f;
-      m = fmaxf(m, ref - lam[(16 * i + 15) * LAM_LD + c]);
+#pragma unroll
+    for (int ks = 0; ks < NKD; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (norm) { qv[ks][e] = silu(qv[ks][e]); kv[ks][e] = silu(kv[ks][e]); }
+        sq += qv[ks][e] * qv[ks][e];
+        sk += kv[ks][e] * kv[ks][e];
+      }
+    sq += __shfl_xor(sq, 16, kWave); sq += __shfl_xor(sq, 32, kWave);
+    sk += __shfl_xor(sk, 16, kWave); sk += __shfl_xor(sk, 32, kWave);
+    const float nq = norm ? inv_norm(sq) : 1.f, nk = norm ? inv_norm(sk) : 1.f;
+    if (g == 0) { inq[t] = nq; ink[t] = nk; }
+    // inclusive prefix of log alpha over the 16 tokens of the block
+#pragma unroll
+    for (int ks = 0; ks < NKD; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float x = lv[ks][e];
+#pragma unroll
+        for (int dd = 1; dd < 16; dd <<= 1) {
+          const float y = __shfl_up(x, dd, 16);
+          if (l16 >= dd) x += y;
+        }
+        lv[ks][e] = x;
+      }
+    float range = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < NKD; ++ks) {
+      float QR[8], KR[8], KC[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float P = lv[ks][e];
+        const float tot = __shfl(P, 15, 16);     // block total, same for all 16 tokens
+        range = fmaxf(range, -tot);
+        if (l16 == 15) cum[(i + 1) * D + tp_chan(ks, g, e)] = tot;
+        const float R = __expf(P), Cf = __expf(tot - P);
+        const float dy = a.z ? two_sigmoid(zv[ks][e]) : 1.f;
+        const float gg = a.gamma ? gm[ks][e] : 1.f;
+        const float qt = a.scale * gg * dy * qv[ks][e] * nq;
+        const float kn = kv[ks][e] * nk;
+        QR[e] = qt * R;
+        KR[e] = bv[ks][e] * kn * R;
+        KC[e] = kn * Cf;
+      }
+      split8<NS>(QR, QRp[ks]);
+      split8<NS>(KR, KRp[ks]);
+      float4 *dst = reinterpret_cast<float4 *>(kcf + ((i * NKD + ks) * 64 + lane) * 8);
+      dst[0] = make_float4(KC[0], KC[1], KC[2], KC[3]);
+      dst[1] = make_float4(KC[4], KC[5], KC[6], KC[7]);
     }
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
-    if (lane == 0) dflag[i] = m > kMaxDiagRange;
+    for (int off = 32; off > 0; off >>= 1) range = fmaxf(range, __shfl_xor(range, off, kWave));
+    if (lane == 0) dflag[i] = range > kMaxDiagRange;
+  }
+  __syncthreads();
+  // cumulative block-start log decay: cum[m][c] = sum_{m' < m} total_{m'}[c]
+  if (tid < D) {
+    float s = 0.f;
+    cum[tid] = 0.f;
+    for (int m = 1; m <= NB; ++m) {
+      s += cum[m * D + tid];
+      cum[m * D + tid] = s;
+    }
   }
   __syncthreads();
 
-  // per-channel gain pieces: qt_c = scale * gamma_c * 2 sigma(z_c) * q_c * inq
-  auto qtilde = [&](size_t row, int t, int c, float qraw, float zraw) {
-    float qn = (norm ? silu(qraw) : qraw) * inq[t];
-    float gm = a.gamma ? a.gamma[(size_t)h * D + c] : 1.f;
-    float dy = a.z ? two_sigmoid(zraw) : 1.f;
-    return a.scale * gm * dy * qn;
+  // per-lane factor vectors for this wave's channels (row-operand layout)
+  auto cum8 = [&](int m, int ks, float out[8]) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      float4 f = *reinterpret_cast<const float4 *>(cum + m * D + 32 * ks + 16 * hh + 4 * g);
+      out[4 * hh] = f.x; out[4 * hh + 1] = f.y; out[4 * hh + 2] = f.z; out[4 * hh + 3] = f.w;
+    }
   };
 
-  // -------------------------------------------------- B: L and A tiles
-  // Wave i owns token block i.  Products are computed transposed
-  // (rows = s, cols = t) so that the accumulator lane <-> t.
+  // ----------------------------------------------------------- B: L and A tiles
+  // Tiles are computed transposed (rows s, cols t) so that the accumulator
+  // lane <-> t:  L^T[s][t] = sum_c (kn_s Cf_s D_ij)_c (k_hat_t R_t)_c with
+  // Cf_s = exp(Lambda_end(j) - Lambda_s), R_t = exp(Lambda_t - Lambda_start(i))
+  // and D_ij = exp(Lambda_start(i) - Lambda_end(j)); the product is
+  // exp(Lambda_t - Lambda_s).  For j < i every factor is in (0, 1].
   bf16x8 afr[NKC][NS];  // A-fragments of A (row block i), tile-pair order over s
 #pragma unroll
-  for (int ks = 0; ks < NKC; ++ks)
+  for (int kk = 0; kk < NKC; ++kk)
 #pragma unroll
     for (int p = 0; p < NS; ++p)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) afr[ks][p][e] = (__bf16)0.f;
+      for (int e = 0; e < 8; ++e) afr[kk][p][e] = (__bf16)0.f;
 
-  if (wave < NB) {
-    const int i = wave;
-    const int t = 16 * i + l16;
-    const size_t rowt = row0 + t;
-    const float *lref = lam + (16 * i - 1) * LAM_LD;  // valid for i > 0
-    bf16x8 qr[NKD][NS], kr[NKD][NS];                 // Qt R_i and K_hat R_i, lane <-> t
-#pragma unroll
-    for (int ks = 0; ks < NKD; ++ks) {
-      const int c0 = 32 * ks + 8 * g;
-      float qv[8], kv[8], zv[8], xq[8], xk[8];
-      ld8<BF>(a.q, rowt * D + c0, qv);
-      ld8<BF>(a.k, rowt * D + c0, kv);
-      if (a.z) ld8<BF>(a.z, rowt * D + c0, zv);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int c = c0 + e;
-        const float f = __expf(lam[t * LAM_LD + c] - (i ? lref[c] : 0.f));
-        const float kn = (norm ? silu(kv[e]) : kv[e]) * ink[t];
-        const float bb = gate_at<BF>(a.b, a.b_mode, rowt, c, D);
-        xq[e] = qtilde(rowt, t, c, qv[e], a.z ? zv[e] : 0.f) * f;
-        xk[e] = bb * kn * f;
-      }
-      split8<NS>(xq, qr[ks]);
-      split8<NS>(xk, kr[ks]);
-    }
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      if (j > i) continue;
-      const int s = 16 * j + l16;
-      const size_t rows = row0 + s;
+  if (rowwave) {
+#pragma unroll 1
+    for (int j = 0; j <= i; ++j) {
       f32x4 accL = zero4(), accA = zero4();
 #pragma unroll
       for (int ks = 0; ks < NKD; ++ks) {
-        const int c0 = 32 * ks + 8 * g;
-        float kv[8], x[8];
-        ld8<BF>(a.k, rows * D + c0, kv);
+        float x[8];
+        const float4 *src = reinterpret_cast<const float4 *>(kcf + ((j * NKD + ks) * 64 + lane) * 8);
+        float4 f0 = src[0], f1 = src[1];
+        x[0] = f0.x; x[1] = f0.y; x[2] = f0.z; x[3] = f0.w;
+        x[4] = f1.x; x[5] = f1.y; x[6] = f1.z; x[7] = f1.w;
+        {
+          // D_ij = exp(cum_i - cum_{j+1}): <= 1 for j < i (clamped against
+          // rounding); for j = i it is exp(-total_i) >= 1, bounded by the
+          // block's decay range (wide ranges take the exact path below).
+          float ci[8], cj[8];
+          cum8(i, ks, ci);
+          cum8(j + 1, ks, cj);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int c = c0 + e;
-          const float kn = (norm ? silu(kv[e]) : kv[e]) * ink[s];
-          x[e] = kn * __expf((i ? lref[c] : 0.f) - lam[s * LAM_LD + c]);
+          for (int e = 0; e < 8; ++e) x[e] *= __expf(j < i ? fminf(ci[e] - cj[e], 0.f) : ci[e] - cj[e]);
         }
         bf16x8 kc[NS];
         split8<NS>(x, kc);
-        accL = mfma32_split<NS>(kc, kr[ks], accL);
-        accA = mfma32_split<NS>(kc, qr[ks], accA);
+        accL = mfma32_split<NS>(kc, KRp[ks], accL);
+        accA = mfma32_split<NS>(kc, QRp[ks], accA);
       }
       // lane (col t, group g) holds rows s = 16j + 4g + r
       if (j == i) {
         if (dflag[i]) {
-          // exact pairwise exponentials for a block whose decay range is too wide
+          // a block whose decay range is too wide for one pivot: exact
+          // pairwise exponentials exp(sum_{x=s+1}^{t} log alpha_x)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int s2 = 16 * j + 4 * g + r;
@@ -265,12 +306,17 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
             if (s2 <= t) {
               const size_t r2 = row0 + s2;
               for (int c = 0; c < D; ++c) {
-                const float pi = __expf(lam[t * LAM_LD + c] - lam[s2 * LAM_LD + c]);
-                const float kns = (norm ? silu(ld1<BF>(a.k, r2 * D + c)) : ld1<BF>(a.k, r2 * D + c)) * ink[s2];
-                const float knt = (norm ? silu(ld1<BF>(a.k, rowt * D + c)) : ld1<BF>(a.k, rowt * D + c)) * ink[t];
+                float dec = 0.f;
+                for (int xx = s2 + 1; xx <= t; ++xx) dec += log_alpha_at(a.log_alpha, a.alpha_mode, row0 + xx, c, D);
+                const float pi = __expf(dec);
+                const float kraw_s = ld1<BF>(a.k, r2 * D + c), kraw_t = ld1<BF>(a.k, rowt * D + c);
+                const float kns = (norm ? silu(kraw_s) : kraw_s) * ink[s2];
+                const float knt = (norm ? silu(kraw_t) : kraw_t) * ink[t];
                 const float bb = gate_at<BF>(a.b, a.b_mode, rowt, c, D);
-                const float qt = qtilde(rowt, t, c, ld1<BF>(a.q, rowt * D + c),
-                                        a.z ? ld1<BF>(a.z, rowt * D + c) : 0.f);
+                const float qraw = ld1<BF>(a.q, rowt * D + c);
+                const float dy = a.z ? two_sigmoid(ld1<BF>(a.z, rowt * D + c)) : 1.f;
+                const float gg = a.gamma ? a.gamma[(size_t)h * D + c] : 1.f;
+                const float qt = a.scale * gg * dy * (norm ? silu(qraw) : qraw) * inq[t];
                 lsum += bb * knt * pi * kns;
                 asum += qt * pi * kns;
               }
@@ -286,17 +332,22 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
           if (s2 > t) accA[r] = 0.f;
         }
       }
-      // L[t][s] -> LDS tile (i, j), row t, columns 4g..4g+3
       *reinterpret_cast<float4 *>(Lt + tidx(i, j) * TILE_SZ + l16 * TILE_LD + 4 * g) =
           make_float4(accL[0], accL[1], accL[2], accL[3]);
-      // A -> fragment ks = j/2, elements 4*(j%2) + r
+      uint16_t hp[4][NS];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        uint16_t hp[NS];
-        split<NS>(accA[r], hp);
+      for (int r = 0; r < 4; ++r) split<NS>(accA[r], hp[r]);
+      // afr[j/2] elements 4*(j%2) + r  (j is uniform: compares, no dynamic indexing)
 #pragma unroll
-        for (int p = 0; p < NS; ++p) afr[j / 2][p][4 * (j % 2) + r] = __builtin_bit_cast(__bf16, hp[p]);
-      }
+      for (int kk = 0; kk < NKC; ++kk)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+          if (j == 2 * kk + hf) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+              for (int p = 0; p < NS; ++p) afr[kk][p][4 * hf + r] = __builtin_bit_cast(__bf16, hp[r][p]);
+          }
     }
   }
   __syncthreads();
@@ -359,8 +410,7 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
   // -------------------------------------------------- D: Z = T^-1 R and the chunk map
   // T^-1 A-fragments for row block i (lane <-> t), tile-pair order over s.
   bf16x8 tif[NKC][NS];
-  if (wave < NB) {
-    const int i = wave;
+  if (rowwave) {
 #pragma unroll
     for (int ks = 0; ks < NKC; ++ks) {
       float x[8];
@@ -373,21 +423,24 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
       split8<NS>(x, tif[ks]);
     }
   }
-  // K'^T fragments for channel tile m (lane <-> c), tile-pair order over s.
+  // K'^T fragments for channel tile m = wave (lane <-> c), tile-pair order
+  // over s: K'[s][c] = kn_s,c Cf_s,c exp(cum_NB - cum_{blk(s)+1}).
   bf16x8 kpf[NKC][NS];
   float gdiag = 0.f;
   if (wave < NMT) {
     const int c = 16 * wave + l16;
-    const float lamC = lam[(C - 1) * LAM_LD + c];
-    gdiag = __expf(lamC);
+    const int ksc = c / 32, cw = c % 32;
+    const int ec = 4 * (cw / 16) + (cw % 4), gc = (cw % 16) / 4;
+    const float cend = cum[NB * D + c];
+    gdiag = __expf(cend);
 #pragma unroll
     for (int ks = 0; ks < NKC; ++ks) {
       float x[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int s = 32 * ks + 16 * (e / 4) + 4 * g + (e % 4);
-        const float kv = ld1<BF>(a.k, (row0 + s) * D + c);
-        x[e] = (norm ? silu(kv) : kv) * ink[s] * __expf(lamC - lam[s * LAM_LD + c]);
+        const int blk = 2 * ks + e / 4, ts = 4 * g + (e % 4);
+        const float kc = kcf[((blk * NKD + ksc) * 64 + ts + 16 * gc) * 8 + ec];
+        x[e] = kc * __expf(fminf(cend - cum[(blk + 1) * D + c], 0.f));
       }
       split8<NS>(x, kpf[ks]);
     }
@@ -399,35 +452,60 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
   float *Ob = a.Ob + ch * (size_t)C * D;
   float *Nn = a.Nn + ch * (size_t)D * D;
 
+#pragma unroll 1
   for (int cp = 0; cp < 2 * D / 32; ++cp) {
     const bool vhalf = cp < D / 32;
-    // D1: stage R[:, 32cp .. 32cp+32) as B-fragments (lane <-> column)
-    for (int item = tid; item < (C / 4) * 32; item += 512) {
-      const int jl = item % 32, s0 = 4 * (item / 32);
-      const int jcol = 32 * cp + jl;
-      float val[4];
+    const int kq = vhalf ? 0 : cp - D / 32;  // channel k-step of the K_hat / Q' half
+    bf16x8 QRs[NS], KRs[NS];                 // QRp[kq], KRp[kq] selected without dynamic indexing
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int s = s0 + r;
-        const size_t rs = row0 + s;
-        if (vhalf) {
-          val[r] = gate_at<BF>(a.w, a.w_mode, rs, jcol, D) * ld1<BF>(a.v, rs * D + jcol);
-        } else {
-          const int c = jcol - D;
-          const float kv = ld1<BF>(a.k, rs * D + c);
-          val[r] = gate_at<BF>(a.b, a.b_mode, rs, c, D) * (norm ? silu(kv) : kv) * ink[s] *
-                   __expf(lam[s * LAM_LD + c]);
+    for (int p = 0; p < NS; ++p) { QRs[p] = QRp[0][p]; KRs[p] = KRp[0][p]; }
+#pragma unroll
+    for (int kk = 1; kk < NKD; ++kk)
+      if (kq == kk) {
+#pragma unroll
+        for (int p = 0; p < NS; ++p) { QRs[p] = QRp[kk][p]; KRs[p] = KRp[kk][p]; }
+      }
+    // D1: the owner wave of each token block writes its 16 rows of
+    // R[:, 32cp .. 32cp+32) into the B-fragment staging (lane <-> column,
+    // tile-pair order over tokens).
+    if (rowwave) {
+      float val[8];
+      if (vhalf) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int c0 = 32 * cp + 16 * hh + 4 * g;
+          float vv[4], ww[4];
+          ld4<BF>(a.v, rowt * D + c0, vv);
+          gate4<BF>(a.w, a.w_mode, rowt, c0, D, ww);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) val[4 * hh + r] = ww[r] * vv[r];
+        }
+      } else {
+        const int ks = cp - D / 32;
+        float ci[8];
+        cum8(i, ks, ci);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float kr = 0.f;
+#pragma unroll
+          for (int p = 0; p < NS; ++p) kr += (float)KRs[p][e];
+          val[e] = kr * __expf(ci[e]);  // k_hat e^Lambda = (k_hat R) e^{cum_i}
         }
       }
-      const int ks = s0 / 32, w32 = s0 % 32;
-      const int ehi = w32 / 16, gq = (w32 % 16) / 4;
-      const int ln = (jl % 16) + 16 * gq;
-      store4_planes<NS>(rst + ((ks * 2 + jl / 16) * NS) * FRAG + ln * 8 + 4 * ehi, FRAG, val);
+      // value e sits in column 16*(e/4) + 4g + e%4 and row t = 16i + l16
+      const int ksr = i / 2, el = 4 * (i % 2) + (l16 % 4), lg = l16 / 4;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        uint16_t hp[NS];
+        split<NS>(val[e], hp);
+        const int ln = 4 * g + (e % 4) + 16 * lg;
+#pragma unroll
+        for (int p = 0; p < NS; ++p) rst[((ksr * 2 + e / 4) * NS + p) * FRAG + ln * 8 + el] = hp[p];
+      }
     }
     __syncthreads();
     // D2: Z rows of block i (wave i), two column tiles
-    if (wave < NB) {
-      const int i = wave;
+    if (rowwave) {
 #pragma unroll
       for (int ctl = 0; ctl < 2; ++ctl) {
         f32x4 zacc = zero4();
@@ -459,8 +537,7 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
           *reinterpret_cast<f32x4 *>(Nn + ((size_t)(wave * NMT + jt) * 64 + lane) * 4) = acc;
         }
       }
-      if (wave < NB) {  // O_bar = A U_bar
-        const int i = wave;
+      if (rowwave) {  // O_bar = A U_bar
 #pragma unroll
         for (int ctl = 0; ctl < 2; ++ctl) {
           f32x4 acc = zero4();
@@ -497,10 +574,9 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
         }
         store8_planes<NS>(Mm + ((size_t)(wave * NKD + ksy) * 64 + lane) * 8, (size_t)D * D, mv);
       }
-      if (wave < NB) {  // Q' = Qt e^Lambda - A Y, as (A Y)^T = Y^T A^T
-        const int i = wave;
-        const int t = 16 * i + l16;
-        const size_t rowt = row0 + t;
+      if (rowwave) {  // Q' = Qt e^Lambda - A Y, as (A Y)^T = Y^T A^T
+        float ci[8];
+        cum8(i, ksy, ci);
         float qv8[8];
 #pragma unroll
         for (int ctl = 0; ctl < 2; ++ctl) {
@@ -512,15 +588,13 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
             load_frag<NS>(zst + ((ks * 2 + ctl) * NS) * FRAG + lane * 8, FRAG, zb);
             acc = mfma32_split<NS>(zb, afr[ks], acc);
           }
-          const int c0 = 32 * ksy + 16 * ctl + 4 * g;
-          float qr4[4], zr4[4] = {0.f, 0.f, 0.f, 0.f};
-          ld4<BF>(a.q, rowt * D + c0, qr4);
-          if (a.z) ld4<BF>(a.z, rowt * D + c0, zr4);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int c = c0 + r;
-            const float qe = qtilde(rowt, t, c, qr4[r], zr4[r]) * __expf(lam[t * LAM_LD + c]);
-            qv8[4 * ctl + r] = qe - acc[r];
+            const int e = 4 * ctl + r;  // channel tp_chan(ksy, g, e)
+            float qr = 0.f;
+#pragma unroll
+            for (int p = 0; p < NS; ++p) qr += (float)QRs[p][e];
+            qv8[e] = qr * __expf(ci[e]) - acc[r];
           }
         }
         store8_planes<NS>(Qp + ((size_t)(i * NKD + ksy) * 64 + lane) * 8, (size_t)C * D, qv8);
@@ -531,14 +605,22 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
 }
 
 // ============================================================================
-// Kernel 2: one workgroup (4 waves) per (stream, 16-column value slice).
-// The fp32 state slice lives in the accumulator tiles of the waves; its NS
-// bf16 planes are shared through LDS as B-fragments every chunk.
+// Kernel 2: one workgroup per (stream, 16-column value slice); wave w owns
+// output row tile w (w < C/16) and state row tile w (w < D/16).  The fp32
+// state slice lives in the accumulator tiles of the waves; its NS bf16 planes
+// are shared through LDS as B-fragments every chunk.  The fragments of chunk
+// c+1 are loaded while chunk c is computed (two register buffers).
 // ============================================================================
+template <int C, int D, int NS>
+struct ScanBuf {
+  bf16x8 q[D / 32][NS];  // A-fragments of Q' (output row tile)
+  bf16x8 m[D / 32][NS];  // A-fragments of M (state row tile)
+  f32x4 ob, nn;          // accumulator tiles of O_bar and N
+};
+
 template <int C, int D, int NS, bool OB16>
-__global__ void __launch_bounds__(256) chunk_scan_kernel(ChunkArgs a) {
+__global__ void __launch_bounds__(512) chunk_scan_kernel(ChunkArgs a) {
   constexpr int NRT = C / 16, NMT = D / 16, NKD = D / 32, NSL = D / 16;
-  constexpr int RPW = (NRT + 3) / 4, MPW = (NMT + 3) / 4;
   constexpr int FRAG = 64 * 8;
   __shared__ __align__(16) uint16_t sfr[NKD * NS * FRAG];
 
@@ -549,92 +631,87 @@ __global__ void __launch_bounds__(256) chunk_scan_kernel(ChunkArgs a) {
   const size_t bh = (size_t)grp * 8 + rem % 8;
   if (bh >= (size_t)a.B * a.H) return;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
   const int NC = a.T / C;
   const int col = 16 * slice + l16;
+  const bool orow = wave < NRT, srow = wave < NMT;
 
-  f32x4 S[MPW];
+  f32x4 S = zero4();
+  if (srow && a.S0) {
 #pragma unroll
-  for (int u = 0; u < MPW; ++u) {
-    const int mt = wave + 4 * u;
-    S[u] = zero4();
-    if (mt < NMT && a.S0) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) S[u][r] = a.S0[(bh * D + 16 * mt + 4 * g + r) * D + col];
-    }
+    for (int r = 0; r < 4; ++r) S[r] = a.S0[(bh * D + 16 * wave + 4 * g + r) * D + col];
   }
   auto publish = [&]() {
-#pragma unroll
-    for (int u = 0; u < MPW; ++u) {
-      const int mt = wave + 4 * u;
-      if (mt < NMT) {
-        float x[4] = {S[u][0], S[u][1], S[u][2], S[u][3]};
-        store4_planes<NS>(sfr + ((mt / 2) * NS) * FRAG + lane * 8 + 4 * (mt % 2), FRAG, x);
-      }
+    if (srow) {
+      float x[4] = {S[0], S[1], S[2], S[3]};
+      store4_planes<NS>(sfr + ((wave / 2) * NS) * FRAG + lane * 8 + 4 * (wave % 2), FRAG, x);
     }
   };
-  publish();
-  __syncthreads();
-
-  for (int c = 0; c < NC; ++c) {
+  // Loads are issued by every wave without a branch (waves without an output
+  // or state tile fetch a clamped, valid tile and discard it): conditional
+  // loads would make the wait-count pass wait for the prefetch as well.
+  const int rt_ld = wave < NRT ? wave : NRT - 1, mt_ld = wave < NMT ? wave : NMT - 1;
+  // per-lane 32-bit offsets (elements) added to uniform per-chunk bases
+  const uint32_t off_q = (uint32_t)((rt_ld * NKD * 64 + lane) * 8);
+  const uint32_t off_m = (uint32_t)((mt_ld * NKD * 64 + lane) * 8);
+  const uint32_t off_ob = (uint32_t)(((rt_ld * NMT + slice) * 64 + lane) * 4);
+  const uint32_t off_nn = (uint32_t)(((mt_ld * NMT + slice) * 64 + lane) * 4);
+  auto load = [&](int c, ScanBuf<C, D, NS> &bf) {
     const size_t ch = bh * NC + c;
     const uint16_t *Qp = a.Qp + ch * NS * (size_t)C * D;
     const uint16_t *Mm = a.Mm + ch * NS * (size_t)D * D;
     const float *Ob = a.Ob + ch * (size_t)C * D;
     const float *Nn = a.Nn + ch * (size_t)D * D;
+    bf.ob = *reinterpret_cast<const f32x4 *>(Ob + off_ob);
+    bf.nn = *reinterpret_cast<const f32x4 *>(Nn + off_nn);
+#pragma unroll
+    for (int ks = 0; ks < NKD; ++ks)
+#pragma unroll
+      for (int p = 0; p < NS; ++p) {
+        bf.q[ks][p] = *reinterpret_cast<const bf16x8 *>(Qp + (size_t)p * C * D + off_q + ks * 512);
+        bf.m[ks][p] = *reinterpret_cast<const bf16x8 *>(Mm + (size_t)p * D * D + off_m + ks * 512);
+      }
+  };
+  auto step = [&](int c, const ScanBuf<C, D, NS> &cur) {
     bf16x8 sf[NKD][NS];
 #pragma unroll
     for (int ks = 0; ks < NKD; ++ks) load_frag<NS>(sfr + (ks * NS) * FRAG + lane * 8, FRAG, sf[ks]);
-    // outputs
+    if (orow) {
+      f32x4 acc = cur.ob;
 #pragma unroll
-    for (int u = 0; u < RPW; ++u) {
-      const int rt = wave + 4 * u;
-      if (rt < NRT) {
-        f32x4 acc = *reinterpret_cast<const f32x4 *>(Ob + ((size_t)(rt * NMT + slice) * 64 + lane) * 4);
+      for (int ks = 0; ks < NKD; ++ks) acc = mfma32_split<NS>(cur.q[ks], sf[ks], acc);
+      const size_t orow0 = bh * (size_t)a.T + (size_t)c * C + 16 * wave + 4 * g;
 #pragma unroll
-        for (int ks = 0; ks < NKD; ++ks) {
-          bf16x8 qa[NS];
-          load_frag<NS>(Qp + ((size_t)(rt * NKD + ks) * 64 + lane) * 8, (size_t)C * D, qa);
-          acc = mfma32_split<NS>(qa, sf[ks], acc);
-        }
-        const size_t orow = bh * (size_t)a.T + (size_t)c * C + 16 * rt + 4 * g;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) st1<OB16>(a.o, (orow + r) * D + col, acc[r]);
-      }
+      for (int r = 0; r < 4; ++r) st1<OB16>(a.o, (orow0 + r) * D + col, acc[r]);
     }
-    // next state
-    f32x4 Sn[MPW];
+    f32x4 Sn = S;
+    if (srow) {
+      Sn = cur.nn;
 #pragma unroll
-    for (int u = 0; u < MPW; ++u) {
-      const int mt = wave + 4 * u;
-      Sn[u] = zero4();
-      if (mt < NMT) {
-        f32x4 acc = *reinterpret_cast<const f32x4 *>(Nn + ((size_t)(mt * NMT + slice) * 64 + lane) * 4);
-#pragma unroll
-        for (int ks = 0; ks < NKD; ++ks) {
-          bf16x8 ma[NS];
-          load_frag<NS>(Mm + ((size_t)(mt * NKD + ks) * 64 + lane) * 8, (size_t)D * D, ma);
-          acc = mfma32_split<NS>(ma, sf[ks], acc);
-        }
-        Sn[u] = acc;
-      }
+      for (int ks = 0; ks < NKD; ++ks) Sn = mfma32_split<NS>(cur.m[ks], sf[ks], Sn);
     }
     __syncthreads();
-#pragma unroll
-    for (int u = 0; u < MPW; ++u) S[u] = Sn[u];
+    S = Sn;
     publish();
     __syncthreads();
+  };
+
+  publish();
+  __syncthreads();
+  ScanBuf<C, D, NS> b0, b1;
+  if (NC > 0) load(0, b0);
+  for (int c = 0; c < NC; c += 2) {
+    if (c + 1 < NC) load(c + 1, b1);
+    step(c, b0);
+    if (c + 1 >= NC) break;
+    if (c + 2 < NC) load(c + 2, b0);
+    step(c + 1, b1);
   }
-  if (a.S_T) {
+  if (a.S_T && srow) {
 #pragma unroll
-    for (int u = 0; u < MPW; ++u) {
-      const int mt = wave + 4 * u;
-      if (mt < NMT) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) a.S_T[(bh * D + 16 * mt + 4 * g + r) * D + col] = S[u][r];
-      }
-    }
+    for (int r = 0; r < 4; ++r) a.S_T[(bh * D + 16 * wave + 4 * g + r) * D + col] = S[r];
   }
 }
 
@@ -658,7 +735,7 @@ bool chunk_intra_fits(int C, int D, int NS) {
 }
 
 template <int C, int D, int NS, bool BF, bool OB16>
-static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st) {
+static hipError_t launch_chunk_t(const ChunkArgs &a, int phases, hipStream_t st) {
   using Lds = IntraLds<C, D, NS>;
   static_assert(Lds::bytes <= 160 * 1024 || NS == 3, "intra-chunk LDS budget");
   if constexpr (Lds::bytes <= 160 * 1024) {
@@ -671,25 +748,27 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st) {
     if (attr_err != hipSuccess) return attr_err;
     const size_t nbh = (size_t)a.B * a.H;
     const size_t nch = nbh * (size_t)(a.T / C);
-    if (nch > 0) {
-      hipLaunchKernelGGL((chunk_intra_kernel<C, D, NS, BF>), dim3((unsigned)nch), dim3(512), Lds::bytes, st, a);
+    if (nch > 0 && (phases & 1)) {
+      hipLaunchKernelGGL((chunk_intra_kernel<C, D, NS, BF>), dim3((unsigned)nch), dim3(64 * Lds::WAVES), Lds::bytes, st, a);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
+    if (!(phases & 2)) return hipSuccess;
     constexpr int NSL = D / 16;
     const size_t nblk = ((nbh + 7) / 8) * 8 * NSL;
-    hipLaunchKernelGGL((chunk_scan_kernel<C, D, NS, OB16>), dim3((unsigned)nblk), dim3(256), 0, st, a);
+    constexpr int NSW = (C / 16 > D / 16 ? C / 16 : D / 16);
+    hipLaunchKernelGGL((chunk_scan_kernel<C, D, NS, OB16>), dim3((unsigned)nblk), dim3(64 * NSW), 0, st, a);
     return hipGetLastError();
   } else {
     return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_chunk(const gdr_desc &d, const ChunkArgs &a, hipStream_t st) {
+hipError_t launch_chunk(const gdr_desc &d, const ChunkArgs &a, int phases, hipStream_t st) {
   const bool ib = d.in_dtype == GDR_BF16, ob = d.out_dtype == GDR_BF16;
 #define GDR_CH(CC, DD, IB, OBB)                                                            \
   if (d.chunk == CC && d.dk == DD && ib == IB && ob == OBB)                                \
-    return launch_chunk_t<CC, DD, (IB ? 2 : 3), IB, OBB>(a, st);
+    return launch_chunk_t<CC, DD, (IB ? 2 : 3), IB, OBB>(a, phases, st);
   GDR_CH(64, 64, true, false) GDR_CH(64, 64, true, true) GDR_CH(64, 64, false, false)
   GDR_CH(64, 64, false, true) GDR_CH(64, 128, true, false) GDR_CH(64, 128, true, true)
   GDR_CH(64, 128, false, false) GDR_CH(64, 128, false, true) GDR_CH(128, 64, true, false)

@@ -75,8 +75,8 @@ __global__ void __launch_bounds__(256) decode_kernel(
       float sq = 0.f, sk = 0.f;
 #pragma unroll
       for (int w = 0; w < (D + kWave - 1) / kWave; ++w) { sq += s_red[0][w]; sk += s_red[1][w]; }
-      nq = 1.f / fmaxf(sqrtf(sq), 1e-12f);
-      nk = 1.f / fmaxf(sqrtf(sk), 1e-12f);
+      nq = inv_norm(sq);
+      nk = inv_norm(sk);
     }
     float g = gamma ? gamma[(size_t)h * D + tid] : 1.f;
     float dyn = z ? two_sigmoid(ld1<IN_BF16>(z, bh * D + tid)) : 1.f;

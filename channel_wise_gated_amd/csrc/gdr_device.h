@@ -89,8 +89,13 @@ __device__ __forceinline__ void st1(void *p, size_t i, float x) {
 }
 
 // ---------------------------------------------------------------- math
-__device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
-__device__ __forceinline__ float two_sigmoid(float x) { return 2.0f / (1.0f + __expf(-x)); }
+// Hardware reciprocal (v_rcp_f32, 1 ulp) instead of an IEEE division.
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+// x * sigmoid(x); e^-x = inf for very negative x gives rcp(inf) = 0 and -0.
+__device__ __forceinline__ float silu(float x) { return x * fast_rcp(1.0f + __expf(-x)); }
+__device__ __forceinline__ float two_sigmoid(float x) { return 2.0f * fast_rcp(1.0f + __expf(-x)); }
+// 1 / max(|x|_2, 1e-12) from a sum of squares (the l2 normalisation floor).
+__device__ __forceinline__ float inv_norm(float sumsq) { return fast_rcp(fmaxf(sqrtf(sumsq), 1e-12f)); }
 
 // ---------------------------------------------------------------- hi/lo splits
 // x ~= sum_{p < NS} plane_p(x), each plane a bf16.  NS = 2 keeps ~16 mantissa
@@ -146,6 +151,27 @@ __device__ __forceinline__ float gate_at(const void *p, int mode, size_t row, in
     case GDR_GATE_PER_TOKEN: return ld1<BF16>(p, row);
     case GDR_GATE_ONES: return 1.0f;
     default: return 0.0f;
+  }
+}
+
+// Four consecutive channels c0..c0+3 of a gate (c0 multiple of 4).
+template <bool BF16>
+__device__ __forceinline__ void gate4(const void *p, int mode, size_t row, int c0, int d, float out[4]) {
+  if (mode == GDR_GATE_PER_CHANNEL) {
+    ld4<BF16>(p, row * (size_t)d + c0, out);
+  } else {
+    const float v = mode == GDR_GATE_PER_TOKEN ? ld1<BF16>(p, row) : (mode == GDR_GATE_ONES ? 1.0f : 0.0f);
+    out[0] = out[1] = out[2] = out[3] = v;
+  }
+}
+
+__device__ __forceinline__ void log_alpha4(const float *p, int mode, size_t row, int c0, int d, float out[4]) {
+  if (mode == GDR_GATE_PER_CHANNEL) {
+    float4 f = *reinterpret_cast<const float4 *>(p + row * (size_t)d + c0);
+    out[0] = f.x; out[1] = f.y; out[2] = f.z; out[3] = f.w;
+  } else {
+    const float v = mode == GDR_GATE_PER_TOKEN ? p[row] : 0.0f;
+    out[0] = out[1] = out[2] = out[3] = v;
   }
 }
 

@@ -24,7 +24,8 @@ struct ChunkArgs {
 hipError_t launch_decode(const gdr_desc &d, float *S, const void *q, const void *k, const void *v,
                          const float *la, const void *b, const void *w, const float *gamma,
                          const void *z, void *o, hipStream_t st);
-hipError_t launch_chunk(const gdr_desc &d, const ChunkArgs &a, hipStream_t st);
+// phases: bit 0 = intra-chunk kernel, bit 1 = scan kernel
+hipError_t launch_chunk(const gdr_desc &d, const ChunkArgs &a, int phases, hipStream_t st);
 size_t chunk_workspace_bytes(int B, int H, int T, int C, int D, int NS);
 bool chunk_intra_fits(int C, int D, int NS);
 

@@ -26,8 +26,8 @@ LIB_PATH = os.path.join(_HERE, "libgdr.so")
 GDR_OK, GDR_ERR_INVALID_ARG, GDR_ERR_UNSUPPORTED, GDR_ERR_WORKSPACE, GDR_ERR_HIP = range(5)
 GDR_BF16, GDR_F32 = 0, 1
 PER_CHANNEL, PER_TOKEN, ONES, ZEROS = 0, 1, 2, 3
-SYMBOLS = ("gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_decode_step",
-           "gdr_status_string", "gdr_version")
+SYMBOLS = ("gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_chunk_fwd_intra",
+           "gdr_chunk_fwd_scan", "gdr_decode_step", "gdr_status_string", "gdr_version")
 
 
 class GdrDesc(ctypes.Structure):
@@ -64,6 +64,10 @@ def load() -> ctypes.CDLL:
     lib.gdr_chunk_fwd_workspace_size.argtypes = [dp, ctypes.POINTER(sz)]
     lib.gdr_chunk_fwd.restype = ctypes.c_int
     lib.gdr_chunk_fwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gdr_chunk_fwd_intra.restype = ctypes.c_int
+    lib.gdr_chunk_fwd_intra.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gdr_chunk_fwd_scan.restype = ctypes.c_int
+    lib.gdr_chunk_fwd_scan.argtypes = [dp, vp, vp, vp, vp, sz, vp]
     lib.gdr_decode_step.restype = ctypes.c_int
     lib.gdr_decode_step.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.gdr_status_string.restype = ctypes.c_char_p
@@ -139,6 +143,67 @@ def _contig(t):
     return t
 
 
+class ChunkCall:
+    """Marshalled arguments of one chunkwise forward (pointers, descriptor,
+    outputs and workspace), so that the call -- or either of its two phases --
+    can be issued repeatedly without re-marshalling."""
+
+    def __init__(self, q, k, v, log_alpha, b, w, gamma=None, z=None, S0=None, *, chunk=64,
+                 out_dtype=torch.float32, normalize_qk=True, scale=1.0, o=None, S_T=None,
+                 workspace=None):
+        q, k, v, z, gamma, S0 = map(_contig, (q, k, v, z, gamma, S0))
+        B, H, T, dk = q.shape
+        dv = v.shape[-1]
+        if isinstance(log_alpha, (int, float)):
+            if log_alpha != 0:
+                raise ValueError("scalar log_alpha must be 0")
+            amode, la = ONES, None
+        else:
+            amode, la = _gate(_contig(log_alpha), 4, "log_alpha")
+        bmode, bt = _gate(_contig(b), 4, "b")
+        wmode, wt = _gate(_contig(w), 4, "w")
+        od = GDR_BF16 if out_dtype == torch.bfloat16 else GDR_F32
+        self.desc = make_desc(B, H, T, dk, dv, chunk, _dtype_code(q), od, int(bool(normalize_qk)),
+                              scale, amode, bmode, wmode)
+        if o is None:
+            o = torch.empty((B, H, T, dv), dtype=out_dtype, device=q.device)
+        if S_T is None:
+            S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+        need = gdr_chunk_fwd_workspace_size(self.desc)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        self.o, self.S_T, self.workspace = o, S_T, workspace
+        self._keep = (q, k, v, la, bt, wt, gamma, z, S0)   # keep the inputs alive
+        self.ptrs = [_ptr(t) for t in self._keep]
+        self.out_ptrs = (_ptr(S0), _ptr(o), _ptr(S_T))
+        self.ws = (_ptr(workspace), workspace.numel())
+
+    def __call__(self, stream=None):
+        """gdr_chunk_fwd: both phases."""
+        S0p, op, sTp = self.out_ptrs
+        rc = load().gdr_chunk_fwd(ctypes.byref(self.desc), *self.ptrs[:8], S0p, op, sTp,
+                                  *self.ws, _stream(stream))
+        if rc != GDR_OK:
+            raise GdrError(rc, "gdr_chunk_fwd")
+        return self.o, self.S_T
+
+    def intra(self, stream=None):
+        """gdr_chunk_fwd_intra: token inputs -> per-chunk maps in the workspace."""
+        rc = load().gdr_chunk_fwd_intra(ctypes.byref(self.desc), *self.ptrs[:8], *self.ws,
+                                        _stream(stream))
+        if rc != GDR_OK:
+            raise GdrError(rc, "gdr_chunk_fwd_intra")
+
+    def scan(self, stream=None):
+        """gdr_chunk_fwd_scan: workspace and S0 -> o and S_T."""
+        S0p, op, sTp = self.out_ptrs
+        rc = load().gdr_chunk_fwd_scan(ctypes.byref(self.desc), S0p, op, sTp, *self.ws,
+                                       _stream(stream))
+        if rc != GDR_OK:
+            raise GdrError(rc, "gdr_chunk_fwd_scan")
+        return self.o, self.S_T
+
+
 def gdr_chunk_fwd(q, k, v, log_alpha, b, w, gamma=None, z=None, S0=None, *, chunk=64,
                   out_dtype=torch.float32, normalize_qk=True, scale=1.0, o=None, S_T=None,
                   workspace=None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
@@ -149,34 +214,10 @@ def gdr_chunk_fwd(q, k, v, log_alpha, b, w, gamma=None, z=None, S0=None, *, chun
     1 / 0; gamma [H,dk] fp32; z [B,H,T,dk]; S0 [B,H,dk,dv] fp32.
     Returns (o [B,H,T,dv] out_dtype, S_T [B,H,dk,dv] fp32).
     """
-    lib = load()
-    q, k, v, z, gamma, S0 = map(_contig, (q, k, v, z, gamma, S0))
-    B, H, T, dk = q.shape
-    dv = v.shape[-1]
-    if isinstance(log_alpha, (int, float)):
-        if log_alpha != 0:
-            raise ValueError("scalar log_alpha must be 0")
-        amode, la = ONES, None
-    else:
-        amode, la = _gate(_contig(log_alpha), 4, "log_alpha")
-    bmode, bt = _gate(_contig(b), 4, "b")
-    wmode, wt = _gate(_contig(w), 4, "w")
-    od = GDR_BF16 if out_dtype == torch.bfloat16 else GDR_F32
-    desc = make_desc(B, H, T, dk, dv, chunk, _dtype_code(q), od, int(bool(normalize_qk)),
-                     scale, amode, bmode, wmode)
-    if o is None:
-        o = torch.empty((B, H, T, dv), dtype=out_dtype, device=q.device)
-    if S_T is None:
-        S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
-    need = gdr_chunk_fwd_workspace_size(desc)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    rc = lib.gdr_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(la), _ptr(bt),
-                           _ptr(wt), _ptr(gamma), _ptr(z), _ptr(S0), _ptr(o), _ptr(S_T),
-                           _ptr(workspace), workspace.numel(), _stream(stream))
-    if rc != GDR_OK:
-        raise GdrError(rc, "gdr_chunk_fwd")
-    return o, S_T
+    load()
+    call = ChunkCall(q, k, v, log_alpha, b, w, gamma, z, S0, chunk=chunk, out_dtype=out_dtype,
+                     normalize_qk=normalize_qk, scale=scale, o=o, S_T=S_T, workspace=workspace)
+    return call(stream)
 
 
 def gdr_decode_step(S, q, k, v, log_alpha, b, w, gamma=None, z=None, *, out_dtype=torch.float32,

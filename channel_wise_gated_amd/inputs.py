@@ -178,3 +178,50 @@ def key_participation_ratio(k_unit: np.ndarray) -> float:
     """Mean of (sum k^2)^2 / sum k^4 over tokens: effective number of key channels."""
     k2 = np.asarray(k_unit, dtype=np.float64) ** 2
     return float(np.mean(k2.sum(-1) ** 2 / np.maximum((k2 ** 2).sum(-1), 1e-300)))
+
+
+def make_inputs_device(wl: Workload, device: str, seed: int = 0, steps: int = 0) -> dict:
+    """The same recipe as ``make_inputs``, drawn with torch's generator on
+    ``device`` (fast, for benchmarks; the values differ from ``make_inputs``).
+
+    With ``steps`` > 0 every per-token tensor gets a leading step dimension
+    (decode: [steps, B, H, d]); gamma and S0 stay static.
+    """
+    gen = torch.Generator(device=device)
+    gen.manual_seed(1000003 * wl.seed + seed)
+    B, H, T, dk, dv = wl.B, wl.H, wl.T, wl.dk, wl.dv
+    lead = (steps,) if steps else ()
+    tok = lead + (B, H) + ((T,) if not steps else ())
+    f32 = dict(device=device, dtype=torch.float32)
+    sdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+
+    def normal(*shape):
+        return torch.randn(shape, generator=gen, **f32)
+
+    def uniform(lo, hi, *shape):
+        return lo + (hi - lo) * torch.rand(shape, generator=gen, **f32)
+
+    out = {"q": normal(*tok, dk).to(sdt)}
+    kraw = normal(*tok, dk)
+    if wl.sparse_keys:
+        order = torch.rand(tok + (dk,), generator=gen, **f32).argsort(dim=-1)
+        kraw = kraw + 3.0 * (order < 6).float()
+    out["k"] = kraw.to(sdt)
+    out["v"] = normal(*tok, dv).to(sdt)
+    if wl.alpha == "softplus":
+        out["log_alpha"] = -0.1 * torch.nn.functional.softplus(normal(*tok, dk))
+    else:
+        split = torch.rand((H, dk), generator=gen, **f32).argsort(dim=1) < dk // 2
+        split = split.view((1,) * len(lead) + (1, H) + ((1,) if not steps else ()) + (dk,))
+        om = torch.where(split, uniform(1e-4, 1e-3, *tok, dk), uniform(0.1, 0.5, *tok, dk))
+        out["log_alpha"] = torch.log1p(-om)
+    if wl.gates == "kda":
+        out["b"] = torch.sigmoid(normal(*tok)).to(sdt)
+        out["w"] = out["b"]
+    else:
+        out["b"] = (2.0 * torch.sigmoid(normal(*tok, dk))).to(sdt)
+        out["w"] = torch.sigmoid(normal(*tok, dv)).to(sdt)
+    out["gamma"] = (1.0 + 0.1 * normal(H, dk)) if wl.gain else None
+    out["z"] = normal(*tok, dk).to(sdt) if wl.gain else None
+    out["S0"] = (0.02 * normal(B, H, dk, dv)) if wl.s0 else None
+    return out

@@ -127,6 +127,30 @@ gdr_status gdr_chunk_fwd(const gdr_desc *desc, const void *q, const void *k,
                          size_t workspace_bytes, void *stream);
 
 /*
+ * The two phases of gdr_chunk_fwd as separate calls, for callers that overlap
+ * the fully parallel phase of one batch with the serial scan of another on a
+ * second stream, or that time the phases.  gdr_chunk_fwd(...) is exactly
+ * gdr_chunk_fwd_intra(...) followed by gdr_chunk_fwd_scan(...) on the same
+ * stream with the same descriptor and workspace.
+ *
+ * gdr_chunk_fwd_intra: reads the token inputs (arguments as gdr_chunk_fwd)
+ *   and writes, per chunk, the chunk's affine state map into the workspace:
+ *   Q' = Qt e^Lambda - A Y, O_bar = A U_bar, M = Diag(e^Lambda_C) - K'^T Y,
+ *   N = K'^T U_bar (Muir notes section 2.4: the chunk system solved once per
+ *   chunk, outputs and next state by matrix products).
+ * gdr_chunk_fwd_scan: reads that workspace and S0, carries the fp32 state
+ *   through the chunks (O = Q' S + O_bar, S <- M S + N) and writes o and S_T.
+ *   The workspace must hold the intra phase's results for the same inputs.
+ */
+gdr_status gdr_chunk_fwd_intra(const gdr_desc *desc, const void *q, const void *k,
+                               const void *v, const float *log_alpha, const void *b,
+                               const void *w, const float *gamma, const void *z,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+gdr_status gdr_chunk_fwd_scan(const gdr_desc *desc, const float *S0, void *o, float *S_T,
+                              const void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * One decode step for B sequences x H heads (the blog's section 3 forward()
  * with a one-token x and `cache` = S): reads S once, forms
  * u = v_hat - k_hat (Diag(alpha) S), writes S <- Diag(alpha) S + kn^T u in

@@ -72,7 +72,7 @@ def check(name, got, ref, tol):
 # chunkwise forward, small sizes: oracle on everything
 # ----------------------------------------------------------------------------
 
-def test_chunk_tiny_fp32_full_config():
+def test_chunk_tiny_fp32_config():
     wl = WORKLOADS["tiny"]
     x = make_inputs(wl)
     o, sT = gpu_chunk(x, wl.chunk)
