@@ -99,6 +99,8 @@ gdr_status chunk_call(const gdr_desc *desc, const void *q, const void *k, const 
   a.Ob = reinterpret_cast<float *>(ws);
   ws += al(nch * (size_t)d.chunk * d.dk * 4);
   a.Nn = reinterpret_cast<float *>(ws);
+  ws += al(nch * (size_t)d.dk * d.dk * 4);
+  a.Sc = reinterpret_cast<uint16_t *>(ws);
   a.B = d.B; a.H = d.H; a.T = d.T;
   a.alpha_mode = d.alpha_mode; a.b_mode = d.b_mode; a.w_mode = d.w_mode;
   a.normalize_qk = d.normalize_qk; a.scale = d.scale;

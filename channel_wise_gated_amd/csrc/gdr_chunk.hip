@@ -12,8 +12,10 @@
 //   O   = (Qt e^Lambda - A Y) S + A U_bar      =: Q' S + O_bar
 //   S' = (Diag(e^Lambda_C) - K'^T Y) S + K'^T U_bar =: M S + N,  K' = kn e^{Lambda_C - Lambda}
 // Kernel 1 ("intra", fully parallel over chunks) reduces every chunk to its
-// affine map (Q', O_bar, M, N); kernel 2 ("scan") carries S in fp32 through
-// the chunks of one stream, split over value-column slices, and writes o.
+// affine map (Q', O_bar, M, N); kernel 2 ("chain") carries S in fp32 through
+// the chunks of one stream, split over value-column slices, and records each
+// chunk-start state; kernel 3 ("output", parallel over chunks) forms
+// O = Q' S_c + O_bar.
 //
 // Decay factors never divide by a decay prefix: every exponent is <= 0.  The
 // chunk is cut into 16-token blocks; for a pair of blocks (i > j) the pivot is
@@ -34,6 +36,7 @@
 //   Mm : NS planes x [D/16][D/32][64][8]   bf16        A-fragments of M
 //   Ob : [C/16][D/16][64][4] fp32                      accumulator tiles of O_bar
 //   Nn : [D/16][D/16][64][4] fp32                      accumulator tiles of N
+//   Sc : [D/16 slices][D/32][NS][64][8] bf16            B-fragments of S_c
 // The contraction index of Q' and M (a state row) is in tile-pair order, the
 // order in which the scan kernel's accumulator tiles of S hold it.
 #include <mutex>
@@ -353,56 +356,101 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
   __syncthreads();
 
   // -------------------------------------------------- C1: leaf inverses
-  if (wave < NB && lane < 16) {
-    float *Tii = Lt + tidx(wave, wave) * TILE_SZ;
-    const int cc = lane;
-    float x[16];
+  // (I + N)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8) for the strictly lower
+  // 16 x 16 diagonal block N (nilpotent: N^16 = 0), on 16x16x16 MFMA.  All
+  // factors are polynomials in N and commute, so every product takes a matrix
+  // read from LDS (row layout) as the A operand and the running accumulator
+  // (whose layout is the B layout) as the B operand.
+  if (rowwave) {
+    float *Tii = Lt + tidx(i, i) * TILE_SZ;
+    float *scr = reinterpret_cast<float *>(rst) + i * TILE_SZ;  // staging is free here
+    auto rowA = [&](const float *T, float av[4]) {
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      float acc = (t == cc) ? 1.f : 0.f;
+      for (int e = 0; e < 4; ++e) av[e] = T[l16 * TILE_LD + 4 * g + e];
+    };
+    auto put = [&](float *T, const f32x4 &x) {
 #pragma unroll
-      for (int s = 0; s < t; ++s)
-        if (s >= cc) acc -= Tii[t * TILE_LD + s] * x[s];
-      x[t] = (t < cc) ? 0.f : acc;
-    }
-    __builtin_amdgcn_wave_barrier();
+      for (int r = 0; r < 4; ++r) T[(4 * g + r) * TILE_LD + l16] = x[r];
+    };
+    float an[4], bn[4], av[4], bv[4];
+    rowA(Tii, an);
 #pragma unroll
-    for (int t = 0; t < 16; ++t) Tii[t * TILE_LD + cc] = x[t];
+    for (int e = 0; e < 4; ++e) bn[e] = Tii[(4 * g + e) * TILE_LD + l16];
+    f32x4 Nacc;                                  // N in accumulator layout
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Nacc[r] = bn[r];
+    const f32x4 N2 = mfma16_split<NS>(an, bn, zero4());
+    put(scr, N2);
+    // P = (I - N)(I + N^2) = I - N + N^2 - N N^2
+#pragma unroll
+    for (int e = 0; e < 4; ++e) bv[e] = N2[e];
+    f32x4 P = mfma16_split<NS>(an, bv, zero4());
+#pragma unroll
+    for (int r = 0; r < 4; ++r) P[r] = ((4 * g + r) == l16 ? 1.f : 0.f) - Nacc[r] + N2[r] - P[r];
+    // N^4 = N^2 N^2 -> Tii (N itself is no longer needed)
+    rowA(scr, av);
+    const f32x4 N4 = mfma16_split<NS>(av, bv, zero4());
+    put(Tii, N4);
+    // Q = P (I + N^4) = P + N^4 P
+    rowA(Tii, av);
+    float bp[4] = {P[0], P[1], P[2], P[3]};
+    f32x4 Q = mfma16_split<NS>(av, bp, P);
+    // N^8 = N^4 N^4 -> scr
+    float b4[4] = {N4[0], N4[1], N4[2], N4[3]};
+    const f32x4 N8 = mfma16_split<NS>(av, b4, zero4());
+    put(scr, N8);
+    // X = Q (I + N^8) = Q + N^8 Q -> Tii
+    rowA(scr, av);
+    float bq[4] = {Q[0], Q[1], Q[2], Q[3]};
+    const f32x4 X = mfma16_split<NS>(av, bq, Q);
+    put(Tii, X);
   }
   __syncthreads();
 
   // -------------------------------------------------- C2: blocked forward substitution
-  // X[i][q] = -X[i][i] sum_{j=q}^{i-1} L[i][j] X[j][q]; wave q owns column block q.
-  for (int i = 1; i < NB; ++i) {
-    const int qb = wave;
-    f32x4 res = zero4();
-    if (qb < i) {
-      f32x4 W = zero4();
-      for (int j = qb; j < i; ++j) {
-        const float *Lij = Lt + tidx(i, j) * TILE_SZ;
-        const float *Xjq = Lt + tidx(j, qb) * TILE_SZ;
-        float av[4], bv[4];
+  // X[i][q] = -X[i][i] sum_{j=q}^{i-1} L[i][j] X[j][q].  Wave q owns column
+  // block q and keeps X[j][q] in accumulator layout -- the B-operand layout of
+  // the 16x16x16 product -- so the waves need no barrier until the write-back.
+  {
+    f32x4 Xc[NB];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          av[e] = Lij[l16 * TILE_LD + 4 * g + e];
-          bv[e] = Xjq[(4 * g + e) * TILE_LD + l16];
+    for (int j = 0; j < NB; ++j) Xc[j] = zero4();
+    const int q = wave;
+    if (rowwave) {
+#pragma unroll
+      for (int jj = 0; jj < NB; ++jj)
+        if (jj == q) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) Xc[jj][r] = Lt[tidx(jj, jj) * TILE_SZ + (4 * g + r) * TILE_LD + l16];
         }
-        W = mfma16_split<NS>(av, bv, W);
-      }
-      const float *Xii = Lt + tidx(i, i) * TILE_SZ;
-      float av[4], bv[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        av[e] = Xii[l16 * TILE_LD + 4 * g + e];
-        bv[e] = W[e];
+      for (int ii = 1; ii < NB; ++ii) {
+        if (ii <= q) continue;
+        f32x4 W = zero4();
+#pragma unroll
+        for (int j = 0; j < NB - 1; ++j) {
+          if (j < q || j >= ii) continue;
+          float av[4], bv[4] = {Xc[j][0], Xc[j][1], Xc[j][2], Xc[j][3]};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) av[e] = Lt[tidx(ii, j) * TILE_SZ + l16 * TILE_LD + 4 * g + e];
+          W = mfma16_split<NS>(av, bv, W);
+        }
+        float av[4], bw[4] = {W[0], W[1], W[2], W[3]};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) av[e] = Lt[tidx(ii, ii) * TILE_SZ + l16 * TILE_LD + 4 * g + e];
+        const f32x4 Xn = mfma16_split<NS>(av, bw, zero4());
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Xc[ii][r] = -Xn[r];
       }
-      res = mfma16_split<NS>(av, bv, zero4());
     }
-    __syncthreads();
-    if (qb < i) {
-      float *Xiq = Lt + tidx(i, qb) * TILE_SZ;
+    __syncthreads();  // every L tile has been read before X overwrites it
+    if (rowwave) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Xiq[(4 * g + r) * TILE_LD + l16] = -res[r];
+      for (int ii = 1; ii < NB; ++ii) {
+        if (ii <= q) continue;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Lt[tidx(ii, q) * TILE_SZ + (4 * g + r) * TILE_LD + l16] = Xc[ii][r];
+      }
     }
     __syncthreads();
   }
@@ -605,24 +653,25 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
 }
 
 // ============================================================================
-// Kernel 2: one workgroup per (stream, 16-column value slice); wave w owns
-// output row tile w (w < C/16) and state row tile w (w < D/16).  The fp32
-// state slice lives in the accumulator tiles of the waves; its NS bf16 planes
-// are shared through LDS as B-fragments every chunk.  The fragments of chunk
-// c+1 are loaded while chunk c is computed (two register buffers).
+// Kernel 2 (chain): one workgroup per (stream, 16-column value slice); wave w
+// owns state row tile w.  Per chunk: S <- M S + N, with the fp32 slice in the
+// accumulator tiles and its NS bf16 planes shared through LDS as
+// B-fragments.  Those planes -- the chunk-start state S_c -- are also written
+// to the workspace for the output kernel.  M and N of chunks c+1 and c+2 are
+// in flight while chunk c is computed (three register buffers); every wave
+// issues its loads without a branch, so that the wait counts stay exact.
 // ============================================================================
-template <int C, int D, int NS>
-struct ScanBuf {
-  bf16x8 q[D / 32][NS];  // A-fragments of Q' (output row tile)
+template <int D, int NS>
+struct ChainBuf {
   bf16x8 m[D / 32][NS];  // A-fragments of M (state row tile)
-  f32x4 ob, nn;          // accumulator tiles of O_bar and N
+  f32x4 nn;              // accumulator tile of N
 };
 
-template <int C, int D, int NS, bool OB16>
-__global__ void __launch_bounds__(512) chunk_scan_kernel(ChunkArgs a) {
-  constexpr int NRT = C / 16, NMT = D / 16, NKD = D / 32, NSL = D / 16;
-  constexpr int FRAG = 64 * 8;
-  __shared__ __align__(16) uint16_t sfr[NKD * NS * FRAG];
+template <int C, int D, int NS>
+__global__ void __launch_bounds__(64 * (D / 16)) chunk_chain_kernel(ChunkArgs a) {
+  constexpr int NMT = D / 16, NKD = D / 32, NSL = D / 16;
+  constexpr int FRAG = 64 * 8, NFR = NKD * NS;
+  __shared__ __align__(16) uint16_t sfr[NFR * FRAG];
 
   // all slices of one stream on the same XCD (workgroups go round-robin over 8)
   const int id = blockIdx.x;
@@ -636,62 +685,41 @@ __global__ void __launch_bounds__(512) chunk_scan_kernel(ChunkArgs a) {
   const int l16 = lane & 15, g = lane >> 4;
   const int NC = a.T / C;
   const int col = 16 * slice + l16;
-  const bool orow = wave < NRT, srow = wave < NMT;
 
   f32x4 S = zero4();
-  if (srow && a.S0) {
+  if (a.S0) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) S[r] = a.S0[(bh * D + 16 * wave + 4 * g + r) * D + col];
   }
   auto publish = [&]() {
-    if (srow) {
-      float x[4] = {S[0], S[1], S[2], S[3]};
-      store4_planes<NS>(sfr + ((wave / 2) * NS) * FRAG + lane * 8 + 4 * (wave % 2), FRAG, x);
-    }
+    float x[4] = {S[0], S[1], S[2], S[3]};
+    store4_planes<NS>(sfr + ((wave / 2) * NS) * FRAG + lane * 8 + 4 * (wave % 2), FRAG, x);
   };
-  // Loads are issued by every wave without a branch (waves without an output
-  // or state tile fetch a clamped, valid tile and discard it): conditional
-  // loads would make the wait-count pass wait for the prefetch as well.
-  const int rt_ld = wave < NRT ? wave : NRT - 1, mt_ld = wave < NMT ? wave : NMT - 1;
-  // per-lane 32-bit offsets (elements) added to uniform per-chunk bases
-  const uint32_t off_q = (uint32_t)((rt_ld * NKD * 64 + lane) * 8);
-  const uint32_t off_m = (uint32_t)((mt_ld * NKD * 64 + lane) * 8);
-  const uint32_t off_ob = (uint32_t)(((rt_ld * NMT + slice) * 64 + lane) * 4);
-  const uint32_t off_nn = (uint32_t)(((mt_ld * NMT + slice) * 64 + lane) * 4);
-  auto load = [&](int c, ScanBuf<C, D, NS> &bf) {
+  const uint32_t off_m = (uint32_t)((wave * NKD * 64 + lane) * 8);
+  const uint32_t off_nn = (uint32_t)(((wave * NMT + slice) * 64 + lane) * 4);
+  auto load = [&](int c, ChainBuf<D, NS> &bf) {
+    c = c < NC ? c : NC - 1;  // clamped instead of skipped: no conditional load
     const size_t ch = bh * NC + c;
-    const uint16_t *Qp = a.Qp + ch * NS * (size_t)C * D;
     const uint16_t *Mm = a.Mm + ch * NS * (size_t)D * D;
-    const float *Ob = a.Ob + ch * (size_t)C * D;
-    const float *Nn = a.Nn + ch * (size_t)D * D;
-    bf.ob = *reinterpret_cast<const f32x4 *>(Ob + off_ob);
-    bf.nn = *reinterpret_cast<const f32x4 *>(Nn + off_nn);
+    bf.nn = *reinterpret_cast<const f32x4 *>(a.Nn + ch * (size_t)D * D + off_nn);
 #pragma unroll
     for (int ks = 0; ks < NKD; ++ks)
 #pragma unroll
-      for (int p = 0; p < NS; ++p) {
-        bf.q[ks][p] = *reinterpret_cast<const bf16x8 *>(Qp + (size_t)p * C * D + off_q + ks * 512);
+      for (int p = 0; p < NS; ++p)
         bf.m[ks][p] = *reinterpret_cast<const bf16x8 *>(Mm + (size_t)p * D * D + off_m + ks * 512);
-      }
   };
-  auto step = [&](int c, const ScanBuf<C, D, NS> &cur) {
+  auto step = [&](int c, const ChainBuf<D, NS> &cur) {
+    // chunk-start state planes -> workspace (fragment f = ks * NS + p)
+    uint16_t *Sc = a.Sc + (bh * NC + c) * (size_t)NS * D * D + (size_t)slice * NFR * FRAG;
+    for (int f = wave; f < NFR; f += NMT)
+      *reinterpret_cast<bf16x8 *>(Sc + f * FRAG + lane * 8) =
+          *reinterpret_cast<const bf16x8 *>(sfr + f * FRAG + lane * 8);
     bf16x8 sf[NKD][NS];
 #pragma unroll
     for (int ks = 0; ks < NKD; ++ks) load_frag<NS>(sfr + (ks * NS) * FRAG + lane * 8, FRAG, sf[ks]);
-    if (orow) {
-      f32x4 acc = cur.ob;
+    f32x4 Sn = cur.nn;
 #pragma unroll
-      for (int ks = 0; ks < NKD; ++ks) acc = mfma32_split<NS>(cur.q[ks], sf[ks], acc);
-      const size_t orow0 = bh * (size_t)a.T + (size_t)c * C + 16 * wave + 4 * g;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) st1<OB16>(a.o, (orow0 + r) * D + col, acc[r]);
-    }
-    f32x4 Sn = S;
-    if (srow) {
-      Sn = cur.nn;
-#pragma unroll
-      for (int ks = 0; ks < NKD; ++ks) Sn = mfma32_split<NS>(cur.m[ks], sf[ks], Sn);
-    }
+    for (int ks = 0; ks < NKD; ++ks) Sn = mfma32_split<NS>(cur.m[ks], sf[ks], Sn);
     __syncthreads();
     S = Sn;
     publish();
@@ -700,18 +728,73 @@ __global__ void __launch_bounds__(512) chunk_scan_kernel(ChunkArgs a) {
 
   publish();
   __syncthreads();
-  ScanBuf<C, D, NS> b0, b1;
-  if (NC > 0) load(0, b0);
-  for (int c = 0; c < NC; c += 2) {
-    if (c + 1 < NC) load(c + 1, b1);
-    step(c, b0);
-    if (c + 1 >= NC) break;
-    if (c + 2 < NC) load(c + 2, b0);
-    step(c + 1, b1);
+  if (NC > 0) {
+    ChainBuf<D, NS> b0, b1, b2;
+    load(0, b0);
+    load(1, b1);
+    for (int c = 0; c < NC; c += 3) {
+      load(c + 2, b2);
+      step(c, b0);
+      if (c + 1 >= NC) break;
+      load(c + 3, b0);
+      step(c + 1, b1);
+      if (c + 2 >= NC) break;
+      load(c + 4, b1);
+      step(c + 2, b2);
+    }
   }
-  if (a.S_T && srow) {
+  if (a.S_T) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) a.S_T[(bh * D + 16 * wave + 4 * g + r) * D + col] = S[r];
+  }
+}
+
+// ============================================================================
+// Kernel 3 (output): one workgroup per (stream, chunk); wave w owns output row
+// tile w and sweeps the value slices: O = Q' S_c + O_bar.  S_c (all slices,
+// NS bf16 planes in B-fragment layout) is staged in LDS once.
+// ============================================================================
+template <int C, int D, int NS, bool OB16>
+__global__ void __launch_bounds__(64 * (C / 16)) chunk_out_kernel(ChunkArgs a) {
+  constexpr int NRT = C / 16, NMT = D / 16, NKD = D / 32, NSL = D / 16;
+  constexpr int FRAG = 64 * 8, NFR = NKD * NS;
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint16_t *sc = reinterpret_cast<uint16_t *>(smem);  // [NSL][NFR][FRAG]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, g = lane >> 4;
+  const int NC = a.T / C;
+  const size_t ch = blockIdx.x;
+  const size_t bh = ch / NC;
+  const int c = (int)(ch % NC);
+
+  const uint16_t *Scg = a.Sc + ch * (size_t)NS * D * D;
+  constexpr int NV = NSL * NFR * FRAG / 8;  // 16-byte vectors
+  for (int v = tid; v < NV; v += 64 * NRT)
+    *reinterpret_cast<uint4 *>(sc + v * 8) = *reinterpret_cast<const uint4 *>(Scg + v * 8);
+  const uint16_t *Qp = a.Qp + ch * NS * (size_t)C * D;
+  bf16x8 qf[NKD][NS];
+#pragma unroll
+  for (int ks = 0; ks < NKD; ++ks)
+#pragma unroll
+    for (int p = 0; p < NS; ++p)
+      qf[ks][p] = *reinterpret_cast<const bf16x8 *>(Qp + (size_t)p * C * D + ((wave * NKD + ks) * 64 + lane) * 8);
+  const float *Ob = a.Ob + ch * (size_t)C * D;
+  __syncthreads();
+  const size_t orow0 = bh * (size_t)a.T + (size_t)c * C + 16 * wave + 4 * g;
+#pragma unroll 1
+  for (int jt = 0; jt < NSL; ++jt) {
+    f32x4 acc = *reinterpret_cast<const f32x4 *>(Ob + ((size_t)(wave * NMT + jt) * 64 + lane) * 4);
+#pragma unroll
+    for (int ks = 0; ks < NKD; ++ks) {
+      bf16x8 sf[NS];
+      load_frag<NS>(sc + (jt * NFR + ks * NS) * FRAG + lane * 8, FRAG, sf);
+      acc = mfma32_split<NS>(qf[ks], sf, acc);
+    }
+    const int col = 16 * jt + l16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) st1<OB16>(a.o, (orow0 + r) * D + col, acc[r]);
   }
 }
 
@@ -722,7 +805,7 @@ size_t chunk_workspace_bytes(int B, int H, int T, int C, int D, int NS) {
   const size_t nch = (size_t)B * H * (T / C);
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   return al(nch * NS * (size_t)C * D * 2) + al(nch * NS * (size_t)D * D * 2) +
-         al(nch * (size_t)C * D * 4) + al(nch * (size_t)D * D * 4);
+         al(nch * (size_t)C * D * 4) + al(nch * (size_t)D * D * 4) + al(nch * NS * (size_t)D * D * 2);
 }
 
 bool chunk_intra_fits(int C, int D, int NS) {
@@ -756,8 +839,18 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, int phases, hipStream_t st)
     if (!(phases & 2)) return hipSuccess;
     constexpr int NSL = D / 16;
     const size_t nblk = ((nbh + 7) / 8) * 8 * NSL;
-    constexpr int NSW = (C / 16 > D / 16 ? C / 16 : D / 16);
-    hipLaunchKernelGGL((chunk_scan_kernel<C, D, NS, OB16>), dim3((unsigned)nblk), dim3(64 * NSW), 0, st, a);
+    hipLaunchKernelGGL((chunk_chain_kernel<C, D, NS>), dim3((unsigned)nblk), dim3(64 * (D / 16)), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || nch == 0) return e;
+    constexpr size_t out_lds = (size_t)NSL * (D / 32) * NS * 512 * 2;
+    static std::once_flag once2;
+    static hipError_t attr2 = hipSuccess;
+    std::call_once(once2, [] {
+      attr2 = hipFuncSetAttribute(reinterpret_cast<const void *>(&chunk_out_kernel<C, D, NS, OB16>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)out_lds);
+    });
+    if (attr2 != hipSuccess) return attr2;
+    hipLaunchKernelGGL((chunk_out_kernel<C, D, NS, OB16>), dim3((unsigned)nch), dim3(64 * (C / 16)), out_lds, st, a);
     return hipGetLastError();
   } else {
     return hipErrorInvalidValue;

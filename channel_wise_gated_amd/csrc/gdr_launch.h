@@ -17,6 +17,7 @@ struct ChunkArgs {
   float *S_T;
   uint16_t *Qp, *Mm;  // workspace: A-fragment planes of Q' and M
   float *Ob, *Nn;     // workspace: accumulator tiles of O_bar and N
+  uint16_t *Sc;       // workspace: chunk-start states as B-fragment planes
   int B, H, T, alpha_mode, b_mode, w_mode, normalize_qk;
   float scale;
 };

@@ -73,8 +73,9 @@ def test_workspace_query_sizes():
     rc, n = ws(gdr.make_desc(**GOOD))
     assert rc == gdr.GDR_OK
     nch = 2 * 4 * (256 // 64)
-    # Q', M as two bf16 planes, O_bar and N in fp32
-    assert n == nch * (2 * 64 * 128 * 2 + 2 * 128 * 128 * 2 + 64 * 128 * 4 + 128 * 128 * 4)
+    # Q', M and the chunk-start states as two bf16 planes, O_bar and N in fp32
+    assert n == nch * (2 * 64 * 128 * 2 + 2 * 128 * 128 * 2 + 64 * 128 * 4 + 128 * 128 * 4 +
+                       2 * 128 * 128 * 2)
     rc, n0 = ws(gdr.make_desc(**dict(GOOD, T=0)))
     assert rc == gdr.GDR_OK and n0 == 0
     # fp32 mode needs three planes; C = D = 128 does not fit the LDS budget
