@@ -40,6 +40,7 @@
 // The contraction index of Q' and M (a state row) is in tile-pair order, the
 // order in which the scan kernel's accumulator tiles of S hold it.
 #include <mutex>
+#include <type_traits>
 
 #include "gdr_device.h"
 #include "gdr_launch.h"
@@ -110,10 +111,15 @@ struct IntraLds {
   static constexpr int STAGE = NKC * 2 * NS * FRAG;
   // float offsets
   static constexpr int KCF = 0;                        // [NB][NKD][64][8]  kn * Cf
-  static constexpr int CUM = KCF + C * D;              // [NB + 1][D]      block-start log decay
+  static constexpr int LT = KCF + C * D;               // [NTILES][TILE_SZ] L, then T^-1
+  static constexpr int CUM = LT + NTILES * TILE_SZ;    // [NB + 1][D]      block-start log decay
   static constexpr int NRM = CUM + (NB + 1) * D;       // [2][C]           inverse norms of q, k
-  static constexpr int LT = NRM + 2 * C;               // [NTILES][TILE_SZ] L, then T^-1
-  static constexpr int STG = LT + NTILES * TILE_SZ;    // R and Z staging (bf16)
+  static constexpr int STG = NRM + 2 * C;              // R and Z staging (bf16)
+  // In the last phase the KCF region is dead; if it is large enough it holds
+  // the QR / KR planes of every token block, which frees those registers for
+  // the column-pair loop (LT still holds T^-1 then).
+  static constexpr int STASH_BYTES = NB * 2 * NKD * NS * FRAG * 2;
+  static constexpr bool STASH = STASH_BYTES <= C * D * 4;
   static constexpr size_t bytes = sizeof(float) * (size_t)STG + sizeof(uint16_t) * 2 * STAGE +
                                   sizeof(int) * NB;
   static constexpr int WAVES = NB > D / 16 ? NB : D / 16;
@@ -165,7 +171,10 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
   // inclusive log-decay prefix inside the block (<= 0).
   bf16x8 QRp[NKD][NS], KRp[NKD][NS];
   if (rowwave) {
-    float qv[NKD][8], kv[NKD][8], zv[NKD][8], bv[NKD][8], lv[NKD][8], gm[NKD][8];
+    float qv[NKD][8], kv[NKD][8], lv[NKD][8];
+    using Raw = typename std::conditional<BF, uint2, float4>::type;  // 4 raw values
+    Raw zr[NKD][2], br[NKD][2];
+    const bool bchan = a.b_mode == GDR_GATE_PER_CHANNEL;
 #pragma unroll
     for (int ks = 0; ks < NKD; ++ks)
 #pragma unroll
@@ -173,14 +182,21 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
         const int c0 = 32 * ks + 16 * hh + 4 * g;
         ld4<BF>(a.q, rowt * D + c0, &qv[ks][4 * hh]);
         ld4<BF>(a.k, rowt * D + c0, &kv[ks][4 * hh]);
-        if (a.z) ld4<BF>(a.z, rowt * D + c0, &zv[ks][4 * hh]);
-        gate4<BF>(a.b, a.b_mode, rowt, c0, D, &bv[ks][4 * hh]);
+        if (a.z) zr[ks][hh] = *reinterpret_cast<const Raw *>(reinterpret_cast<const char *>(a.z) +
+                                                             (rowt * D + c0) * (BF ? 2 : 4));
+        if (bchan) br[ks][hh] = *reinterpret_cast<const Raw *>(reinterpret_cast<const char *>(a.b) +
+                                                              (rowt * D + c0) * (BF ? 2 : 4));
         log_alpha4(a.log_alpha, a.alpha_mode, rowt, c0, D, &lv[ks][4 * hh]);
-        if (a.gamma) {
-          float4 f = *reinterpret_cast<const float4 *>(a.gamma + (size_t)h * D + c0);
-          gm[ks][4 * hh] = f.x; gm[ks][4 * hh + 1] = f.y; gm[ks][4 * hh + 2] = f.z; gm[ks][4 * hh + 3] = f.w;
-        }
       }
+    const float bscal = bchan ? 0.f : gate_at<BF>(a.b, a.b_mode, rowt, 0, D);
+    auto raw_at = [](const Raw &r, int e) -> float {
+      if constexpr (BF) {
+        const uint32_t w = (e < 2) ? r.x : r.y;
+        return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+      } else {
+        return e == 0 ? r.x : (e == 1 ? r.y : (e == 2 ? r.z : r.w));
+      }
+    };
     float sq = 0.f, sk = 0.f;
 #pragma unroll
     for (int ks = 0; ks < NKD; ++ks)
@@ -218,12 +234,13 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
         range = fmaxf(range, -tot);
         if (l16 == 15) cum[(i + 1) * D + tp_chan(ks, g, e)] = tot;
         const float R = __expf(P), Cf = __expf(tot - P);
-        const float dy = a.z ? two_sigmoid(zv[ks][e]) : 1.f;
-        const float gg = a.gamma ? gm[ks][e] : 1.f;
+        const float dy = a.z ? two_sigmoid(raw_at(zr[ks][e / 4], e % 4)) : 1.f;
+        const float gg = a.gamma ? a.gamma[(size_t)h * D + tp_chan(ks, g, e)] : 1.f;
+        const float bb = bchan ? raw_at(br[ks][e / 4], e % 4) : bscal;
         const float qt = a.scale * gg * dy * qv[ks][e] * nq;
         const float kn = kv[ks][e] * nk;
         QR[e] = qt * R;
-        KR[e] = bv[ks][e] * kn * R;
+        KR[e] = bb * kn * R;
         KC[e] = kn * Cf;
       }
       split8<NS>(QR, QRp[ks]);
@@ -494,6 +511,20 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
     }
   }
 
+  uint16_t *stash = reinterpret_cast<uint16_t *>(sm + Lds::KCF);
+  if constexpr (Lds::STASH) {
+    __syncthreads();  // every wave has read kcf
+    if (rowwave) {
+#pragma unroll
+      for (int ks = 0; ks < NKD; ++ks)
+#pragma unroll
+        for (int p = 0; p < NS; ++p) {
+          *reinterpret_cast<bf16x8 *>(stash + (((i * 2 + 0) * NKD + ks) * NS + p) * FRAG + lane * 8) = QRp[ks][p];
+          *reinterpret_cast<bf16x8 *>(stash + (((i * 2 + 1) * NKD + ks) * NS + p) * FRAG + lane * 8) = KRp[ks][p];
+        }
+    }
+  }
+
   const size_t chq = ch * NS;
   uint16_t *Qp = a.Qp + chq * (size_t)C * D;
   uint16_t *Mm = a.Mm + chq * (size_t)D * D;
@@ -504,15 +535,25 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
   for (int cp = 0; cp < 2 * D / 32; ++cp) {
     const bool vhalf = cp < D / 32;
     const int kq = vhalf ? 0 : cp - D / 32;  // channel k-step of the K_hat / Q' half
-    bf16x8 QRs[NS], KRs[NS];                 // QRp[kq], KRp[kq] selected without dynamic indexing
+    bf16x8 QRs[NS], KRs[NS];  // QRp[kq], KRp[kq]: from the LDS stash, or selected without dynamic indexing
+    if constexpr (Lds::STASH) {
+      if (rowwave && !vhalf) {
 #pragma unroll
-    for (int p = 0; p < NS; ++p) { QRs[p] = QRp[0][p]; KRs[p] = KRp[0][p]; }
-#pragma unroll
-    for (int kk = 1; kk < NKD; ++kk)
-      if (kq == kk) {
-#pragma unroll
-        for (int p = 0; p < NS; ++p) { QRs[p] = QRp[kk][p]; KRs[p] = KRp[kk][p]; }
+        for (int p = 0; p < NS; ++p) {
+          QRs[p] = *reinterpret_cast<const bf16x8 *>(stash + (((i * 2 + 0) * NKD + kq) * NS + p) * FRAG + lane * 8);
+          KRs[p] = *reinterpret_cast<const bf16x8 *>(stash + (((i * 2 + 1) * NKD + kq) * NS + p) * FRAG + lane * 8);
+        }
       }
+    } else {
+#pragma unroll
+      for (int p = 0; p < NS; ++p) { QRs[p] = QRp[0][p]; KRs[p] = KRp[0][p]; }
+#pragma unroll
+      for (int kk = 1; kk < NKD; ++kk)
+        if (kq == kk) {
+#pragma unroll
+          for (int p = 0; p < NS; ++p) { QRs[p] = QRp[kk][p]; KRs[p] = KRp[kk][p]; }
+        }
+    }
     // D1: the owner wave of each token block writes its 16 rows of
     // R[:, 32cp .. 32cp+32) into the B-fragment staging (lane <-> column,
     // tile-pair order over tokens).
@@ -717,9 +758,16 @@ __global__ void __launch_bounds__(64 * (D / 16)) chunk_chain_kernel(ChunkArgs a)
     bf16x8 sf[NKD][NS];
 #pragma unroll
     for (int ks = 0; ks < NKD; ++ks) load_frag<NS>(sfr + (ks * NS) * FRAG + lane * 8, FRAG, sf[ks]);
-    f32x4 Sn = cur.nn;
+    __builtin_amdgcn_sched_barrier(0);  // all fragment reads in flight before the products
+    // two independent accumulation chains (even / odd k-steps)
+    f32x4 Sn = cur.nn, Sn2 = zero4();
 #pragma unroll
-    for (int ks = 0; ks < NKD; ++ks) Sn = mfma32_split<NS>(cur.m[ks], sf[ks], Sn);
+    for (int ks = 0; ks < NKD; ++ks) {
+      if (ks % 2 == 0) Sn = mfma32_split<NS>(cur.m[ks], sf[ks], Sn);
+      else Sn2 = mfma32_split<NS>(cur.m[ks], sf[ks], Sn2);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Sn[r] += Sn2[r];
     __syncthreads();
     S = Sn;
     publish();
