@@ -148,7 +148,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--chunk", type=int, default=128, choices=(64, 128))
-    ap.add_argument("--decode-steps", type=int, default=1024)
+    ap.add_argument("--decode-steps", type=int, default=1024, help="0 skips the decode leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -204,10 +204,11 @@ def main():
     # decode
     dwl = WORKLOADS["decode"]
     dsteps = args.decode_steps
-    dwall, dper = timed_decode(dwl, dsteps, warmup=min(16, dsteps))
-    dbytes = dwl.B * dwl.H * (2 * dwl.dk * dwl.dv * 4 + 6 * dwl.dk * 2 + 4 * dwl.dk + 4 * dwl.dv)
-    d_us = 1e3 * sum(dper) / dsteps
-    d_gbs = dbytes / (d_us / 1e6) / 1e9
+    if dsteps > 0:
+        dwall, dper = timed_decode(dwl, dsteps, warmup=min(16, dsteps))
+        dbytes = dwl.B * dwl.H * (2 * dwl.dk * dwl.dv * 4 + 6 * dwl.dk * 2 + 4 * dwl.dk + 4 * dwl.dv)
+        d_us = 1e3 * sum(dper) / dsteps
+        d_gbs = dbytes / (d_us / 1e6) / 1e9
 
     line = {
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -221,11 +222,12 @@ def main():
         "hbm_gbs_algorithmic": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "kernels_ms": {"chunk_intra_kernel": round(intra_ms, 4), "chunk_scan_kernel": round(scan_ms, 4)},
         "roofline": roof,
-        "decode": {"workload": f"decode {dwl.B} seq x H{dwl.H}, fp32 state {dwl.dk}x{dwl.dv}, "
-                               f"{dsteps} steps", "us_per_step": round(d_us, 2),
-                   "gbs": round(d_gbs, 1), "hbm_frac": round(d_gbs / HBM_PEAK_GBS, 4),
-                   "bytes_per_step": dbytes, "wall_s": round(dwall, 3)},
     }
+    if dsteps > 0:
+        line["decode"] = {"workload": f"decode {dwl.B} seq x H{dwl.H}, fp32 state {dwl.dk}x{dwl.dv}, "
+                                      f"{dsteps} steps", "us_per_step": round(d_us, 2),
+                          "gbs": round(d_gbs, 1), "hbm_frac": round(d_gbs / HBM_PEAK_GBS, 4),
+                          "bytes_per_step": dbytes, "wall_s": round(dwall, 3)}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(x)
     print(json.dumps(line), flush=True)

@@ -265,6 +265,31 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
   }
   __syncthreads();
 
+  // pair decay factors D_ij[c] = exp(cum_i - cum_{j+1}) for j <= i, one
+  // exponential per (pair, channel), kept in the (still unused) staging area
+  float *dtab = reinterpret_cast<float *>(rst);
+  static_assert(Lds::NTILES * D * 4 <= 2 * Lds::STAGE * 2, "pair decay table fits the staging area");
+  {
+    // thread <-> channel c; the pairs are dealt out over the P groups of D
+    // threads (a group is whole waves, so the pair test is a scalar branch)
+    constexpr int P = 64 * Lds::WAVES / D;
+    static_assert(D % 64 == 0 && (64 * Lds::WAVES) % D == 0, "whole waves per channel group");
+    const int c = tid % D, part = wave / (D / 64);
+    float cm[NB + 1];
+#pragma unroll
+    for (int m = 0; m <= NB; ++m) cm[m] = cum[m * D + c];
+#pragma unroll
+    for (int ii = 0; ii < NB; ++ii)
+#pragma unroll
+      for (int jj = 0; jj <= ii; ++jj) {
+        const int pr = tidx(ii, jj);
+        if (pr % P != part) continue;
+        const float dd = cm[ii] - cm[jj + 1];
+        dtab[pr * D + c] = __expf(jj < ii ? fminf(dd, 0.f) : dd);
+      }
+  }
+  __syncthreads();
+
   // per-lane factor vectors for this wave's channels (row-operand layout)
   auto cum8 = [&](int m, int ks, float out[8]) {
 #pragma unroll
@@ -303,11 +328,10 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
           // D_ij = exp(cum_i - cum_{j+1}): <= 1 for j < i (clamped against
           // rounding); for j = i it is exp(-total_i) >= 1, bounded by the
           // block's decay range (wide ranges take the exact path below).
-          float ci[8], cj[8];
-          cum8(i, ks, ci);
-          cum8(j + 1, ks, cj);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] *= __expf(j < i ? fminf(ci[e] - cj[e], 0.f) : ci[e] - cj[e]);
+          const float4 *dp = reinterpret_cast<const float4 *>(dtab + tidx(i, j) * D + 32 * ks + 4 * g);
+          const float4 d0 = dp[0], d1 = dp[4];  // channels tp_chan(ks, g, 0..3) and (.., 4..7)
+          x[0] *= d0.x; x[1] *= d0.y; x[2] *= d0.z; x[3] *= d0.w;
+          x[4] *= d1.x; x[5] *= d1.y; x[6] *= d1.z; x[7] *= d1.w;
         }
         bf16x8 kc[NS];
         split8<NS>(x, kc);
@@ -581,15 +605,32 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
           val[e] = kr * __expf(ci[e]);  // k_hat e^Lambda = (k_hat R) e^{cum_i}
         }
       }
-      // value e sits in column 16*(e/4) + 4g + e%4 and row t = 16i + l16
-      const int ksr = i / 2, el = 4 * (i % 2) + (l16 % 4), lg = l16 / 4;
+      // Value e sits in column 16*(e/4) + 4g + e%4 and token t = 16i + l16.
+      // The B-fragment wants, per column, the 4 tokens of a lane quad as 4
+      // consecutive bf16: transpose 4 x 4 inside each quad (DPP), then every
+      // lane writes 8 contiguous bytes per plane (no bank conflicts).
+      const int r = l16 & 3, q4 = l16 >> 2;
+      const bool b0 = (r & 1) != 0, b1 = (r & 2) != 0;
+      const int ksr = i / 2;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint16_t hp[NS];
-        split<NS>(val[e], hp);
-        const int ln = 4 * g + (e % 4) + 16 * lg;
-#pragma unroll
-        for (int p = 0; p < NS; ++p) rst[((ksr * 2 + e / 4) * NS + p) * FRAG + ln * 8 + el] = hp[p];
+      for (int hf = 0; hf < 2; ++hf) {
+        // 4 x 4 transpose over (lane r of the quad, element k): swap the
+        // off-diagonal 2 x 2 blocks across lanes r ^ 2, then the off-diagonal
+        // elements of each 2 x 2 block across lanes r ^ 1 (selects on lane
+        // bits, no lane-dependent indexing).
+        const float *w = &val[4 * hf];
+        const float s0 = b1 ? w[0] : w[2], s1 = b1 ? w[1] : w[3];
+        const float t0 = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s0), 0x4E, 0xF, 0xF, false));
+        const float t1 = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s1), 0x4E, 0xF, 0xF, false));
+        const float n0 = b1 ? t0 : w[0], n1 = b1 ? t1 : w[1];
+        const float n2 = b1 ? w[2] : t0, n3 = b1 ? w[3] : t1;
+        const float u0 = b0 ? n0 : n1, u1 = b0 ? n2 : n3;
+        const float v0 = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(u0), 0xB1, 0xF, 0xF, false));
+        const float v1 = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(u1), 0xB1, 0xF, 0xF, false));
+        // column 16hf + 4g + r, tokens 4q + 0..3
+        const float tok[4] = {b0 ? v0 : n0, b0 ? n1 : v0, b0 ? v1 : n2, b0 ? n3 : v1};
+        const int ln = 4 * g + r + 16 * q4;
+        store4_planes<NS>(rst + ((ksr * 2 + hf) * NS) * FRAG + ln * 8 + 4 * (i % 2), FRAG, tok);
       }
     }
     __syncthreads();
