@@ -115,11 +115,8 @@ struct IntraLds {
   static constexpr int CUM = LT + NTILES * TILE_SZ;    // [NB + 1][D]      block-start log decay
   static constexpr int NRM = CUM + (NB + 1) * D;       // [2][C]           inverse norms of q, k
   static constexpr int STG = NRM + 2 * C;              // R and Z staging (bf16)
-  // In the last phase the KCF region is dead; if it is large enough it holds
-  // the QR / KR planes of every token block, which frees those registers for
-  // the column-pair loop (LT still holds T^-1 then).
-  static constexpr int STASH_BYTES = NB * 2 * NKD * NS * FRAG * 2;
-  static constexpr bool STASH = STASH_BYTES <= C * D * 4;
+  // In the last phase the KCF region is dead and holds v_hat = w * v (fp32,
+  // same layout), loaded during the pre-pass.
   static constexpr size_t bytes = sizeof(float) * (size_t)STG + sizeof(uint16_t) * 2 * STAGE +
                                   sizeof(int) * NB;
   static constexpr int WAVES = NB > D / 16 ? NB : D / 16;
@@ -170,11 +167,15 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
   // QRp / KRp: NS bf16 planes of qt * R and k_hat * R, R = exp(P_t), P the
   // inclusive log-decay prefix inside the block (<= 0).
   bf16x8 QRp[NKD][NS], KRp[NKD][NS];
+  Raw4<BF> vraw[NKD][2];    // v of this lane's token and channels
+  Raw4<BF> wraw[NKD][2];    // w of the same (gate_load groups)
+  const void *any = a.q;    // a valid 16-byte-aligned address for unused gate loads
   if (rowwave) {
     float qv[NKD][8], kv[NKD][8], lv[NKD][8];
-    using Raw = typename std::conditional<BF, uint2, float4>::type;  // 4 raw values
-    Raw zr[NKD][2], br[NKD][2];
-    const bool bchan = a.b_mode == GDR_GATE_PER_CHANNEL;
+    Raw4<BF> zg[NKD][2], bg[NKD][2];
+    Raw4<false> lg[NKD][2], gm[NKD][2];
+    const int zmode = a.z ? GDR_GATE_PER_CHANNEL : GDR_GATE_ONES;
+    const int gmode = a.gamma ? GDR_GATE_PER_CHANNEL : GDR_GATE_ONES;
 #pragma unroll
     for (int ks = 0; ks < NKD; ++ks)
 #pragma unroll
@@ -182,21 +183,16 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
         const int c0 = 32 * ks + 16 * hh + 4 * g;
         ld4<BF>(a.q, rowt * D + c0, &qv[ks][4 * hh]);
         ld4<BF>(a.k, rowt * D + c0, &kv[ks][4 * hh]);
-        if (a.z) zr[ks][hh] = *reinterpret_cast<const Raw *>(reinterpret_cast<const char *>(a.z) +
-                                                             (rowt * D + c0) * (BF ? 2 : 4));
-        if (bchan) br[ks][hh] = *reinterpret_cast<const Raw *>(reinterpret_cast<const char *>(a.b) +
-                                                              (rowt * D + c0) * (BF ? 2 : 4));
-        log_alpha4(a.log_alpha, a.alpha_mode, rowt, c0, D, &lv[ks][4 * hh]);
+        zg[ks][hh] = gate_load<BF>(a.z, zmode, rowt, c0, D, any);
+        bg[ks][hh] = gate_load<BF>(a.b, a.b_mode, rowt, c0, D, any);
+        lg[ks][hh] = gate_load<false>(a.log_alpha, a.alpha_mode, rowt, c0, D, any);
+        gm[ks][hh] = gate_load<false>(a.gamma, gmode, (size_t)h, c0, D, any);
       }
-    const float bscal = bchan ? 0.f : gate_at<BF>(a.b, a.b_mode, rowt, 0, D);
-    auto raw_at = [](const Raw &r, int e) -> float {
-      if constexpr (BF) {
-        const uint32_t w = (e < 2) ? r.x : r.y;
-        return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
-      } else {
-        return e == 0 ? r.x : (e == 1 ? r.y : (e == 2 ? r.z : r.w));
-      }
-    };
+    const float bconst = gate_const(a.b_mode);
+#pragma unroll
+    for (int ks = 0; ks < NKD; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) lv[ks][e] = gate_elem<false>(lg[ks][e / 4], e % 4, a.alpha_mode, rowt, 0.f);
     float sq = 0.f, sk = 0.f;
 #pragma unroll
     for (int ks = 0; ks < NKD; ++ks)
@@ -234,9 +230,9 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
         range = fmaxf(range, -tot);
         if (l16 == 15) cum[(i + 1) * D + tp_chan(ks, g, e)] = tot;
         const float R = __expf(P), Cf = __expf(tot - P);
-        const float dy = a.z ? two_sigmoid(raw_at(zr[ks][e / 4], e % 4)) : 1.f;
-        const float gg = a.gamma ? a.gamma[(size_t)h * D + tp_chan(ks, g, e)] : 1.f;
-        const float bb = bchan ? raw_at(br[ks][e / 4], e % 4) : bscal;
+        const float dy = a.z ? two_sigmoid(raw_elem<BF>(zg[ks][e / 4], e % 4)) : 1.f;
+        const float gg = a.gamma ? raw_elem<false>(gm[ks][e / 4], e % 4) : 1.f;
+        const float bb = gate_elem<BF>(bg[ks][e / 4], e % 4, a.b_mode, rowt, bconst);
         const float qt = a.scale * gg * dy * qv[ks][e] * nq;
         const float kn = kv[ks][e] * nk;
         QR[e] = qt * R;
@@ -396,6 +392,20 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
   }
   __syncthreads();
 
+  // v and w of this lane's token and channels, only needed in the last phase:
+  // issued here so that their latency hides behind the triangular inverse
+  if (rowwave) {
+#pragma unroll
+    for (int ks = 0; ks < NKD; ++ks)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int c0 = 32 * ks + 16 * hh + 4 * g;
+        vraw[ks][hh] = *reinterpret_cast<const Raw4<BF> *>(reinterpret_cast<const char *>(a.v) +
+                                                          (rowt * D + c0) * (BF ? 2 : 4));
+        wraw[ks][hh] = gate_load<BF>(a.w, a.w_mode, rowt, c0, D, any);
+      }
+  }
+
   // -------------------------------------------------- C1: leaf inverses
   // (I + N)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8) for the strictly lower
   // 16 x 16 diagonal block N (nilpotent: N^16 = 0), on 16x16x16 MFMA.  All
@@ -535,17 +545,21 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
     }
   }
 
-  uint16_t *stash = reinterpret_cast<uint16_t *>(sm + Lds::KCF);
-  if constexpr (Lds::STASH) {
-    __syncthreads();  // every wave has read kcf
-    if (rowwave) {
+  // every wave has read kcf: the region now takes v_hat = w * v (fp32, kcf
+  // layout), read back by the same wave in the first half of the loop below
+  __syncthreads();
+  float *vhat = sm + Lds::KCF;
+  if (rowwave) {
+    const float wconst = gate_const(a.w_mode);
 #pragma unroll
-      for (int ks = 0; ks < NKD; ++ks)
+    for (int ks = 0; ks < NKD; ++ks) {
+      float x[8];
 #pragma unroll
-        for (int p = 0; p < NS; ++p) {
-          *reinterpret_cast<bf16x8 *>(stash + (((i * 2 + 0) * NKD + ks) * NS + p) * FRAG + lane * 8) = QRp[ks][p];
-          *reinterpret_cast<bf16x8 *>(stash + (((i * 2 + 1) * NKD + ks) * NS + p) * FRAG + lane * 8) = KRp[ks][p];
-        }
+      for (int e = 0; e < 8; ++e)
+        x[e] = raw_elem<BF>(vraw[ks][e / 4], e % 4) * gate_elem<BF>(wraw[ks][e / 4], e % 4, a.w_mode, rowt, wconst);
+      float4 *dst = reinterpret_cast<float4 *>(vhat + ((i * NKD + ks) * 64 + lane) * 8);
+      dst[0] = make_float4(x[0], x[1], x[2], x[3]);
+      dst[1] = make_float4(x[4], x[5], x[6], x[7]);
     }
   }
 
@@ -559,40 +573,25 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
   for (int cp = 0; cp < 2 * D / 32; ++cp) {
     const bool vhalf = cp < D / 32;
     const int kq = vhalf ? 0 : cp - D / 32;  // channel k-step of the K_hat / Q' half
-    bf16x8 QRs[NS], KRs[NS];  // QRp[kq], KRp[kq]: from the LDS stash, or selected without dynamic indexing
-    if constexpr (Lds::STASH) {
-      if (rowwave && !vhalf) {
+    bf16x8 QRs[NS], KRs[NS];  // QRp[kq], KRp[kq], selected without dynamic indexing
 #pragma unroll
-        for (int p = 0; p < NS; ++p) {
-          QRs[p] = *reinterpret_cast<const bf16x8 *>(stash + (((i * 2 + 0) * NKD + kq) * NS + p) * FRAG + lane * 8);
-          KRs[p] = *reinterpret_cast<const bf16x8 *>(stash + (((i * 2 + 1) * NKD + kq) * NS + p) * FRAG + lane * 8);
-        }
+    for (int p = 0; p < NS; ++p) { QRs[p] = QRp[0][p]; KRs[p] = KRp[0][p]; }
+#pragma unroll
+    for (int kk = 1; kk < NKD; ++kk)
+      if (kq == kk) {
+#pragma unroll
+        for (int p = 0; p < NS; ++p) { QRs[p] = QRp[kk][p]; KRs[p] = KRp[kk][p]; }
       }
-    } else {
-#pragma unroll
-      for (int p = 0; p < NS; ++p) { QRs[p] = QRp[0][p]; KRs[p] = KRp[0][p]; }
-#pragma unroll
-      for (int kk = 1; kk < NKD; ++kk)
-        if (kq == kk) {
-#pragma unroll
-          for (int p = 0; p < NS; ++p) { QRs[p] = QRp[kk][p]; KRs[p] = KRp[kk][p]; }
-        }
-    }
     // D1: the owner wave of each token block writes its 16 rows of
     // R[:, 32cp .. 32cp+32) into the B-fragment staging (lane <-> column,
     // tile-pair order over tokens).
     if (rowwave) {
       float val[8];
       if (vhalf) {
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int c0 = 32 * cp + 16 * hh + 4 * g;
-          float vv[4], ww[4];
-          ld4<BF>(a.v, rowt * D + c0, vv);
-          gate4<BF>(a.w, a.w_mode, rowt, c0, D, ww);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) val[4 * hh + r] = ww[r] * vv[r];
-        }
+        const float4 *src = reinterpret_cast<const float4 *>(vhat + ((i * NKD + cp) * 64 + lane) * 8);
+        const float4 f0 = src[0], f1 = src[1];
+        val[0] = f0.x; val[1] = f0.y; val[2] = f0.z; val[3] = f0.w;
+        val[4] = f1.x; val[5] = f1.y; val[6] = f1.z; val[7] = f1.w;
       } else {
         const int ks = cp - D / 32;
         float ci[8];

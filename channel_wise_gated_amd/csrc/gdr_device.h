@@ -17,6 +17,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "../../include/gdr.h"
 
 namespace gdr {
@@ -182,6 +184,64 @@ __device__ __forceinline__ float log_alpha_at(const float *p, int mode, size_t r
     default: return 0.0f;
   }
 }
+
+// ---------------------------------------------------------------- branch-free gate loads
+// Four raw storage elements (bf16 or fp32).
+template <bool BF>
+using Raw4 = typename std::conditional<BF, uint2, float4>::type;
+
+// Element e (0..3, known at compile time) of a raw group.
+template <bool BF>
+__device__ __forceinline__ float raw_elem(const Raw4<BF> &r, int e) {
+  if constexpr (BF) {
+    const uint32_t w = (e < 2) ? r.x : r.y;
+    return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+  } else {
+    return e == 0 ? r.x : (e == 1 ? r.y : (e == 2 ? r.z : r.w));
+  }
+}
+
+// Element (idx & 3) for an index that differs between lanes: two selects on
+// its bits (no lane-dependent indexing, no branch).
+template <bool BF>
+__device__ __forceinline__ float raw_pick(const Raw4<BF> &r, int idx) {
+  // bit masks rather than selects: a select between two elements of one vector
+  // would be folded into a dynamic element index
+  const uint32_t m1 = 0u - (uint32_t)(idx & 1), m2 = 0u - (uint32_t)((idx >> 1) & 1);
+  if constexpr (BF) {
+    const uint32_t w = r.x ^ ((r.x ^ r.y) & m2);
+    return __uint_as_float((w << (16 & ~m1)) & 0xffff0000u);
+  } else {
+    const uint32_t x = __float_as_uint(r.x), y = __float_as_uint(r.y);
+    const uint32_t z = __float_as_uint(r.z), w = __float_as_uint(r.w);
+    const uint32_t lo = x ^ ((x ^ y) & m1), hi = z ^ ((z ^ w) & m1);
+    return __uint_as_float(lo ^ ((lo ^ hi) & m2));
+  }
+}
+
+// Four gate values (channels c0..c0+3 of token row `row`) fetched with one
+// unconditional load whatever the gate mode -- a load under a branch makes
+// the compiler wait for every load in flight where the paths join:
+//   per channel  p[row * d + c0 .. c0 + 3]
+//   per token    the aligned group of four token values that holds p[row]
+//                (per-token tensors hold B*H*T values, a multiple of 4)
+//   constant     `any`, a valid 16-byte-aligned address; the value is unused.
+template <bool BF>
+__device__ __forceinline__ Raw4<BF> gate_load(const void *p, int mode, size_t row, int c0, int d, const void *any) {
+  const bool chan = mode == GDR_GATE_PER_CHANNEL, tok = mode == GDR_GATE_PER_TOKEN;
+  const char *base = reinterpret_cast<const char *>((chan || tok) ? p : any);
+  const size_t off = chan ? row * (size_t)d + c0 : (tok ? (row & ~(size_t)3) : 0);
+  return *reinterpret_cast<const Raw4<BF> *>(base + off * (BF ? 2 : 4));
+}
+// Value of element e of a group from gate_load; `cval` is the value of a constant mode.
+template <bool BF>
+__device__ __forceinline__ float gate_elem(const Raw4<BF> &raw, int e, int mode, size_t row, float cval) {
+  return mode == GDR_GATE_PER_CHANNEL ? raw_elem<BF>(raw, e)
+                                      : (mode == GDR_GATE_PER_TOKEN ? raw_pick<BF>(raw, (int)(row & 3)) : cval);
+}
+
+// Value of the constant gate modes: ONES -> 1 (for log alpha: 0), ZEROS -> 0.
+__device__ __forceinline__ float gate_const(int mode) { return mode == GDR_GATE_ONES ? 1.0f : 0.0f; }
 
 // ---------------------------------------------------------------- reductions
 __device__ __forceinline__ float wave_sum(float x) {
