@@ -48,7 +48,28 @@ __global__ void __launch_bounds__(256) decode_kernel(
   const int cg = tid % CG, rg = tid / CG;
   float *Sb = S + bh * (size_t)D * D;
 
-  // 1. issue the state loads
+  // 1. the token's inputs first, then the state: waiting for the former
+  // leaves the state loads in flight.  Every thread loads channel tid % D
+  // (threads beyond D duplicate), and each load is unconditional -- gates of
+  // a constant mode read a dummy valid address -- so that no branch forces a
+  // wait for every load in flight.
+  const int c = tid % D;
+  const size_t ix = bh * D + c;
+  const void *any = q;
+  const bool a_ld = alpha_mode == GDR_GATE_PER_CHANNEL || alpha_mode == GDR_GATE_PER_TOKEN;
+  const bool b_ld = b_mode == GDR_GATE_PER_CHANNEL || b_mode == GDR_GATE_PER_TOKEN;
+  const bool w_ld = w_mode == GDR_GATE_PER_CHANNEL || w_mode == GDR_GATE_PER_TOKEN;
+  float qv = ld1<IN_BF16>(q, ix);
+  float kv = ld1<IN_BF16>(k, ix);
+  const float vv = ld1<IN_BF16>(v, ix);
+  const float zr = ld1<IN_BF16>(z ? z : any, z ? ix : 0);
+  const float gr = ld1<false>(gamma ? gamma : any, gamma ? (size_t)h * D + c : 0);
+  const float lr = ld1<false>(a_ld ? log_alpha : any,
+                              alpha_mode == GDR_GATE_PER_CHANNEL ? ix : (alpha_mode == GDR_GATE_PER_TOKEN ? bh : 0));
+  const float br = ld1<IN_BF16>(b_ld ? bgate : any,
+                                b_mode == GDR_GATE_PER_CHANNEL ? ix : (b_mode == GDR_GATE_PER_TOKEN ? bh : 0));
+  const float wr = ld1<IN_BF16>(w_ld ? wgate : any,
+                                w_mode == GDR_GATE_PER_CHANNEL ? ix : (w_mode == GDR_GATE_PER_TOKEN ? bh : 0));
   float4 sreg[RPT];
 #pragma unroll
   for (int r = 0; r < RPT; ++r)
@@ -56,14 +77,8 @@ __global__ void __launch_bounds__(256) decode_kernel(
 
   // 2. pre-pass: thread i < D owns channel i
   const int lane = tid % kWave, wave = tid / kWave;
-  float qs = 0.f, ks = 0.f, qv = 0.f, kv = 0.f;
-  if (tid < D) {
-    qv = ld1<IN_BF16>(q, bh * D + tid);
-    kv = ld1<IN_BF16>(k, bh * D + tid);
-    if (normalize_qk) { qv = silu(qv); kv = silu(kv); }
-    qs = qv * qv;
-    ks = kv * kv;
-  }
+  if (normalize_qk) { qv = silu(qv); kv = silu(kv); }
+  float qs = tid < D ? qv * qv : 0.f, ks = tid < D ? kv * kv : 0.f;
   qs = wave_sum(qs);
   ks = wave_sum(ks);
   if (lane == 0) { s_red[0][wave] = qs; s_red[1][wave] = ks; }
@@ -78,18 +93,18 @@ __global__ void __launch_bounds__(256) decode_kernel(
       nq = inv_norm(sq);
       nk = inv_norm(sk);
     }
-    float g = gamma ? gamma[(size_t)h * D + tid] : 1.f;
-    float dyn = z ? two_sigmoid(ld1<IN_BF16>(z, bh * D + tid)) : 1.f;
-    float qt = scale * g * dyn * qv * nq;
-    float kn = kv * nk;
-    float a = __expf(log_alpha_at(log_alpha, alpha_mode, bh, tid, D));
-    float bb = gate_at<IN_BF16>(bgate, b_mode, bh, tid, D);
-    float ww = gate_at<IN_BF16>(wgate, w_mode, bh, tid, D);
+    const float g = gamma ? gr : 1.f;
+    const float dyn = z ? two_sigmoid(zr) : 1.f;
+    const float qt = scale * g * dyn * qv * nq;
+    const float kn = kv * nk;
+    const float a = __expf(a_ld ? lr : 0.f);
+    const float bb = b_ld ? br : gate_const(b_mode);
+    const float ww = w_ld ? wr : gate_const(w_mode);
     s_qa[tid] = qt * a;
     s_ka[tid] = bb * kn * a;
     s_a[tid] = a;
     s_kn[tid] = kn;
-    s_vh[tid] = ww * ld1<IN_BF16>(v, bh * D + tid);
+    s_vh[tid] = ww * vv;
     qkd = qt * kn;
   }
   qkd = wave_sum(qkd);
