@@ -738,8 +738,9 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
 // owns state row tile w.  Per chunk: S <- M S + N, with the fp32 slice in the
 // accumulator tiles and its NS bf16 planes shared through LDS as
 // B-fragments.  Those planes -- the chunk-start state S_c -- are also written
-// to the workspace for the output kernel.  M and N of chunks c+1 and c+2 are
-// in flight while chunk c is computed (three register buffers); every wave
+// to the workspace for the output kernel.  M and N of chunks c+1 .. c+3 are
+// in flight while chunk c is computed (four register buffers; three, holding
+// c+1 and c+2, in fp32 mode); every wave
 // issues its loads without a branch, so that the wait counts stay exact.
 // ============================================================================
 template <int D, int NS>
@@ -752,7 +753,9 @@ template <int C, int D, int NS>
 __global__ void __launch_bounds__(64 * (D / 16)) chunk_chain_kernel(ChunkArgs a) {
   constexpr int NMT = D / 16, NKD = D / 32, NSL = D / 16;
   constexpr int FRAG = 64 * 8, NFR = NKD * NS;
-  __shared__ __align__(16) uint16_t sfr[NFR * FRAG];
+  // S_c planes, double-buffered by chunk parity: step c reads buffer c & 1 and
+  // writes buffer (c + 1) & 1, so one barrier per step suffices
+  __shared__ __align__(16) uint16_t sfr2[2][NFR * FRAG];
 
   // all slices of one stream on the same XCD (workgroups go round-robin over 8)
   const int id = blockIdx.x;
@@ -772,63 +775,98 @@ __global__ void __launch_bounds__(64 * (D / 16)) chunk_chain_kernel(ChunkArgs a)
 #pragma unroll
     for (int r = 0; r < 4; ++r) S[r] = a.S0[(bh * D + 16 * wave + 4 * g + r) * D + col];
   }
-  auto publish = [&]() {
+  auto publish = [&](uint16_t *sfr) {
     float x[4] = {S[0], S[1], S[2], S[3]};
     store4_planes<NS>(sfr + ((wave / 2) * NS) * FRAG + lane * 8 + 4 * (wave % 2), FRAG, x);
   };
   const uint32_t off_m = (uint32_t)((wave * NKD * 64 + lane) * 8);
   const uint32_t off_nn = (uint32_t)(((wave * NMT + slice) * 64 + lane) * 4);
+  // buffer loads: the chunk base goes in scalar registers and the lane
+  // offsets never change, so no address register is rewritten while a load
+  // into another buffer is still in flight (that would cost a wait)
+  // buffer loads: the chunk base goes in scalar registers and the lane
+  // offsets never change, so no address register is rewritten while a load
+  // into another buffer is still in flight (that would cost a wait)
   auto load = [&](int c, ChainBuf<D, NS> &bf) {
     c = c < NC ? c : NC - 1;  // clamped instead of skipped: no conditional load
     const size_t ch = bh * NC + c;
-    const uint16_t *Mm = a.Mm + ch * NS * (size_t)D * D;
-    bf.nn = *reinterpret_cast<const f32x4 *>(a.Nn + ch * (size_t)D * D + off_nn);
+    const auto rm = buffer_rsrc(a.Mm + ch * NS * (size_t)D * D, (uint32_t)(NS * D * D * 2));
+    const auto rn = buffer_rsrc(a.Nn + ch * (size_t)D * D, (uint32_t)(D * D * 4));
+    bf.nn = buffer_load16<f32x4>(rn, 4 * off_nn);
 #pragma unroll
     for (int ks = 0; ks < NKD; ++ks)
 #pragma unroll
-      for (int p = 0; p < NS; ++p)
-        bf.m[ks][p] = *reinterpret_cast<const bf16x8 *>(Mm + (size_t)p * D * D + off_m + ks * 512);
+      for (int p = 0; p < NS; ++p) bf.m[ks][p] = buffer_load16<bf16x8>(rm, 2 * (p * D * D + off_m + ks * 512));
   };
-  auto step = [&](int c, const ChainBuf<D, NS> &cur) {
+  // step c with the state planes in LDS buffer `par`
+  auto step = [&](int c, const ChainBuf<D, NS> &cur, int par) {
+    const uint16_t *sfr = sfr2[par];
     // chunk-start state planes -> workspace (fragment f = ks * NS + p)
     uint16_t *Sc = a.Sc + (bh * NC + c) * (size_t)NS * D * D + (size_t)slice * NFR * FRAG;
-    for (int f = wave; f < NFR; f += NMT)
-      *reinterpret_cast<bf16x8 *>(Sc + f * FRAG + lane * 8) =
-          *reinterpret_cast<const bf16x8 *>(sfr + f * FRAG + lane * 8);
+    if constexpr (NFR == NMT) {  // one fragment per wave, no branch (keeps the wait counts exact)
+      *reinterpret_cast<bf16x8 *>(Sc + wave * FRAG + lane * 8) =
+          *reinterpret_cast<const bf16x8 *>(sfr + wave * FRAG + lane * 8);
+    } else {
+      for (int f = wave; f < NFR; f += NMT)
+        *reinterpret_cast<bf16x8 *>(Sc + f * FRAG + lane * 8) =
+            *reinterpret_cast<const bf16x8 *>(sfr + f * FRAG + lane * 8);
+    }
     bf16x8 sf[NKD][NS];
 #pragma unroll
     for (int ks = 0; ks < NKD; ++ks) load_frag<NS>(sfr + (ks * NS) * FRAG + lane * 8, FRAG, sf[ks]);
     __builtin_amdgcn_sched_barrier(0);  // all fragment reads in flight before the products
-    // two independent accumulation chains (even / odd k-steps)
-    f32x4 Sn = cur.nn, Sn2 = zero4();
+    // independent accumulation chains over the k-steps (one per k-step; two
+    // in fp32 mode, where registers are short)
+    constexpr int NACC = NS == 3 ? 2 : NKD;
+    f32x4 acc[NACC];
 #pragma unroll
-    for (int ks = 0; ks < NKD; ++ks) {
-      if (ks % 2 == 0) Sn = mfma32_split<NS>(cur.m[ks], sf[ks], Sn);
-      else Sn2 = mfma32_split<NS>(cur.m[ks], sf[ks], Sn2);
-    }
+    for (int ks = 0; ks < NACC; ++ks) acc[ks] = ks == 0 ? cur.nn : zero4();
 #pragma unroll
-    for (int r = 0; r < 4; ++r) Sn[r] += Sn2[r];
-    __syncthreads();
-    S = Sn;
-    publish();
+    for (int ks = 0; ks < NKD; ++ks) acc[ks % NACC] = mfma32_split<NS>(cur.m[ks], sf[ks], acc[ks % NACC]);
+#pragma unroll
+    for (int ks = 1; ks < NACC; ++ks)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[0][r] += acc[ks][r];
+    S = acc[0];
+    publish(sfr2[par ^ 1]);
     __syncthreads();
   };
 
-  publish();
+  publish(sfr2[0]);
   __syncthreads();
-  if (NC > 0) {
+  if (NC <= 0) {
+    // no chunk: S_T = S0 below
+  } else if constexpr (NS == 3) {  // fp32 mode: wider buffers, three of them
     ChainBuf<D, NS> b0, b1, b2;
     load(0, b0);
     load(1, b1);
     for (int c = 0; c < NC; c += 3) {
       load(c + 2, b2);
-      step(c, b0);
+      step(c, b0, c & 1);
       if (c + 1 >= NC) break;
       load(c + 3, b0);
-      step(c + 1, b1);
+      step(c + 1, b1, (c + 1) & 1);
       if (c + 2 >= NC) break;
       load(c + 4, b1);
-      step(c + 2, b2);
+      step(c + 2, b2, c & 1);
+    }
+  } else {
+    ChainBuf<D, NS> b0, b1, b2, b3;
+    load(0, b0);
+    load(1, b1);
+    load(2, b2);
+    for (int c = 0; c < NC; c += 4) {
+      load(c + 3, b3);
+      step(c, b0, 0);
+      if (c + 1 >= NC) break;
+      load(c + 4, b0);
+      step(c + 1, b1, 1);
+      if (c + 2 >= NC) break;
+      load(c + 5, b1);
+      step(c + 2, b2, 0);
+      if (c + 3 >= NC) break;
+      load(c + 6, b2);
+      step(c + 3, b3, 1);
     }
   }
   if (a.S_T) {

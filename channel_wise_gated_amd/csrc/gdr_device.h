@@ -243,6 +243,20 @@ __device__ __forceinline__ float gate_elem(const Raw4<BF> &raw, int e, int mode,
 // Value of the constant gate modes: ONES -> 1 (for log alpha: 0), ZEROS -> 0.
 __device__ __forceinline__ float gate_const(int mode) { return mode == GDR_GATE_ONES ? 1.0f : 0.0f; }
 
+// ---------------------------------------------------------------- buffer loads
+// A raw buffer resource over [base, base + bytes) (gfx9 word 3: 32-bit data
+// format).  Loads through it take the base from scalar registers and a
+// 32-bit lane offset; offsets outside the range read zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+template <typename T>
+__device__ __forceinline__ T buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  static_assert(sizeof(T) == 16, "16-byte loads");
+  return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
+}
+
 // ---------------------------------------------------------------- reductions
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
