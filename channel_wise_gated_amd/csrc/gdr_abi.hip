@@ -56,7 +56,6 @@ gdr_status chunk_plan(const gdr_desc *d, size_t *ws) {
   gdr_status s = check_common(d, d ? d->T : 0);
   if (s != GDR_OK) return s;
   if (d->chunk != 64 && d->chunk != 128) return GDR_ERR_INVALID_ARG;
-  if (d->T % d->chunk != 0) return GDR_ERR_INVALID_ARG;
   const int ns = d->in_dtype == GDR_BF16 ? 2 : 3;
   if (!gdr::chunk_intra_fits(d->chunk, d->dk, ns)) return GDR_ERR_UNSUPPORTED;
   *ws = gdr::chunk_workspace_bytes(d->B, d->H, d->T, d->chunk, d->dk, ns);
@@ -85,7 +84,7 @@ gdr_status chunk_call(const gdr_desc *desc, const void *q, const void *k, const 
   if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u)) return GDR_ERR_WORKSPACE;
 
   const int ns = d.in_dtype == GDR_BF16 ? 2 : 3;
-  const size_t nch = (size_t)d.B * d.H * (d.T / d.chunk);
+  const size_t nch = (size_t)d.B * d.H * ((d.T + d.chunk - 1) / d.chunk);  // last chunk may be short
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   unsigned char *ws = static_cast<unsigned char *>(workspace);
   gdr::ChunkArgs a;

@@ -152,30 +152,36 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int l16 = lane & 15, g = lane >> 4;
-  const int NC = a.T / C;
+  const int NC = (a.T + C - 1) / C;
   const size_t ch = blockIdx.x;
   const size_t bh = ch / NC;
   const int h = (int)(bh % a.H);
   const size_t row0 = bh * (size_t)a.T + (size_t)(ch % NC) * C;  // first token row
+  // The last chunk of a sequence may be short: its tokens from `tvalid` on
+  // are padding, read at the last real row and turned into identity steps
+  // (log alpha = 0, no erase, no write); their outputs are never stored.
+  const int tvalid = min(C, a.T - (int)(ch % NC) * C);
   const bool norm = a.normalize_qk != 0;
   const bool rowwave = wave < NB;
   const int i = wave;                       // token block of this wave
   const int t = 16 * i + l16;               // token of this lane (row-operand layout)
-  const size_t rowt = row0 + t;
+  const bool tok_ok = t < tvalid;
+  const size_t rowt = row0 + min(t, tvalid - 1);  // row the lane's inputs are read from
+  auto rowc = [&](int tt) { return row0 + min(tt, tvalid - 1); };
 
   // ----------------------------------------------------------- A: pre-pass
   // QRp / KRp: NS bf16 planes of qt * R and k_hat * R, R = exp(P_t), P the
   // inclusive log-decay prefix inside the block (<= 0).
   bf16x8 QRp[NKD][NS], KRp[NKD][NS];
   Raw4<BF> vraw[NKD][2];    // v of this lane's token and channels
-  Raw4<BF> wraw[NKD][2];    // w of the same (gate_load groups)
-  const void *any = a.q;    // a valid 16-byte-aligned address for unused gate loads
+  Gate4<BF> wraw[NKD][2];   // w of the same
+  const void *any = a.q;    // a valid 16-byte-aligned address for unused loads
   if (rowwave) {
     float qv[NKD][8], kv[NKD][8], lv[NKD][8];
-    Raw4<BF> zg[NKD][2], bg[NKD][2];
-    Raw4<false> lg[NKD][2], gm[NKD][2];
-    const int zmode = a.z ? GDR_GATE_PER_CHANNEL : GDR_GATE_ONES;
-    const int gmode = a.gamma ? GDR_GATE_PER_CHANNEL : GDR_GATE_ONES;
+    Raw4<BF> zg[NKD][2];
+    Raw4<false> gm[NKD][2];
+    Gate4<BF> bg[NKD][2];
+    Gate4<false> lg[NKD][2];
 #pragma unroll
     for (int ks = 0; ks < NKD; ++ks)
 #pragma unroll
@@ -183,16 +189,19 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
         const int c0 = 32 * ks + 16 * hh + 4 * g;
         ld4<BF>(a.q, rowt * D + c0, &qv[ks][4 * hh]);
         ld4<BF>(a.k, rowt * D + c0, &kv[ks][4 * hh]);
-        zg[ks][hh] = gate_load<BF>(a.z, zmode, rowt, c0, D, any);
+        // optional tensors: the pointer is selected, the load is unconditional
+        zg[ks][hh] = *reinterpret_cast<const Raw4<BF> *>(
+            a.z ? reinterpret_cast<const char *>(a.z) + (rowt * D + c0) * (BF ? 2 : 4) : reinterpret_cast<const char *>(any));
+        gm[ks][hh] = *reinterpret_cast<const Raw4<false> *>(
+            a.gamma ? reinterpret_cast<const char *>(a.gamma + (size_t)h * D + c0) : reinterpret_cast<const char *>(any));
         bg[ks][hh] = gate_load<BF>(a.b, a.b_mode, rowt, c0, D, any);
         lg[ks][hh] = gate_load<false>(a.log_alpha, a.alpha_mode, rowt, c0, D, any);
-        gm[ks][hh] = gate_load<false>(a.gamma, gmode, (size_t)h, c0, D, any);
       }
-    const float bconst = gate_const(a.b_mode);
+    const float bconst = tok_ok ? gate_const(a.b_mode) : 0.f;
 #pragma unroll
     for (int ks = 0; ks < NKD; ++ks)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) lv[ks][e] = gate_elem<false>(lg[ks][e / 4], e % 4, a.alpha_mode, rowt, 0.f);
+      for (int e = 0; e < 8; ++e) lv[ks][e] = tok_ok ? gate_elem<false>(lg[ks][e / 4], e % 4, a.alpha_mode, 0.f) : 0.f;
     float sq = 0.f, sk = 0.f;
 #pragma unroll
     for (int ks = 0; ks < NKD; ++ks)
@@ -232,7 +241,7 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
         const float R = __expf(P), Cf = __expf(tot - P);
         const float dy = a.z ? two_sigmoid(raw_elem<BF>(zg[ks][e / 4], e % 4)) : 1.f;
         const float gg = a.gamma ? raw_elem<false>(gm[ks][e / 4], e % 4) : 1.f;
-        const float bb = gate_elem<BF>(bg[ks][e / 4], e % 4, a.b_mode, rowt, bconst);
+        const float bb = tok_ok ? gate_elem<BF>(bg[ks][e / 4], e % 4, a.b_mode, bconst) : 0.f;
         const float qt = a.scale * gg * dy * qv[ks][e] * nq;
         const float kn = kv[ks][e] * nk;
         QR[e] = qt * R;
@@ -344,15 +353,16 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
             const int s2 = 16 * j + 4 * g + r;
             float lsum = 0.f, asum = 0.f;
             if (s2 <= t) {
-              const size_t r2 = row0 + s2;
+              const size_t r2 = rowc(s2);
               for (int c = 0; c < D; ++c) {
                 float dec = 0.f;
-                for (int xx = s2 + 1; xx <= t; ++xx) dec += log_alpha_at(a.log_alpha, a.alpha_mode, row0 + xx, c, D);
+                for (int xx = s2 + 1; xx <= t; ++xx)
+                  if (xx < tvalid) dec += log_alpha_at(a.log_alpha, a.alpha_mode, row0 + xx, c, D);
                 const float pi = __expf(dec);
                 const float kraw_s = ld1<BF>(a.k, r2 * D + c), kraw_t = ld1<BF>(a.k, rowt * D + c);
                 const float kns = (norm ? silu(kraw_s) : kraw_s) * ink[s2];
                 const float knt = (norm ? silu(kraw_t) : kraw_t) * ink[t];
-                const float bb = gate_at<BF>(a.b, a.b_mode, rowt, c, D);
+                const float bb = tok_ok ? gate_at<BF>(a.b, a.b_mode, rowt, c, D) : 0.f;
                 const float qraw = ld1<BF>(a.q, rowt * D + c);
                 const float dy = a.z ? two_sigmoid(ld1<BF>(a.z, rowt * D + c)) : 1.f;
                 const float gg = a.gamma ? a.gamma[(size_t)h * D + c] : 1.f;
@@ -402,7 +412,7 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
         const int c0 = 32 * ks + 16 * hh + 4 * g;
         vraw[ks][hh] = *reinterpret_cast<const Raw4<BF> *>(reinterpret_cast<const char *>(a.v) +
                                                           (rowt * D + c0) * (BF ? 2 : 4));
-        wraw[ks][hh] = gate_load<BF>(a.w, a.w_mode, rowt, c0, D, any);
+        wraw[ks][hh] = gate_load<BF>(a.w, a.w_mode, rowt, c0, D, any);  // padding: zeroed at use
       }
   }
 
@@ -551,12 +561,13 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
   float *vhat = sm + Lds::KCF;
   if (rowwave) {
     const float wconst = gate_const(a.w_mode);
+    const float wmask = tok_ok ? 1.f : 0.f;  // padding tokens write nothing
 #pragma unroll
     for (int ks = 0; ks < NKD; ++ks) {
       float x[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        x[e] = raw_elem<BF>(vraw[ks][e / 4], e % 4) * gate_elem<BF>(wraw[ks][e / 4], e % 4, a.w_mode, rowt, wconst);
+        x[e] = raw_elem<BF>(vraw[ks][e / 4], e % 4) * (wmask * gate_elem<BF>(wraw[ks][e / 4], e % 4, a.w_mode, wconst));
       float4 *dst = reinterpret_cast<float4 *>(vhat + ((i * NKD + ks) * 64 + lane) * 8);
       dst[0] = make_float4(x[0], x[1], x[2], x[3]);
       dst[1] = make_float4(x[4], x[5], x[6], x[7]);
@@ -767,7 +778,7 @@ __global__ void __launch_bounds__(64 * (D / 16)) chunk_chain_kernel(ChunkArgs a)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
-  const int NC = a.T / C;
+  const int NC = (a.T + C - 1) / C;  // the last chunk may be short
   const int col = 16 * slice + l16;
 
   f32x4 S = zero4();
@@ -890,7 +901,7 @@ __global__ void __launch_bounds__(64 * (C / 16)) chunk_out_kernel(ChunkArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
-  const int NC = a.T / C;
+  const int NC = (a.T + C - 1) / C;  // the last chunk may be short
   const size_t ch = blockIdx.x;
   const size_t bh = ch / NC;
   const int c = (int)(ch % NC);
@@ -908,7 +919,8 @@ __global__ void __launch_bounds__(64 * (C / 16)) chunk_out_kernel(ChunkArgs a) {
       qf[ks][p] = *reinterpret_cast<const bf16x8 *>(Qp + (size_t)p * C * D + ((wave * NKD + ks) * 64 + lane) * 8);
   const float *Ob = a.Ob + ch * (size_t)C * D;
   __syncthreads();
-  const size_t orow0 = bh * (size_t)a.T + (size_t)c * C + 16 * wave + 4 * g;
+  const int tok0 = c * C + 16 * wave + 4 * g;  // token index (within the sequence) of acc[0]
+  const size_t orow0 = bh * (size_t)a.T + tok0;
 #pragma unroll 1
   for (int jt = 0; jt < NSL; ++jt) {
     f32x4 acc = *reinterpret_cast<const f32x4 *>(Ob + ((size_t)(wave * NMT + jt) * 64 + lane) * 4);
@@ -920,7 +932,8 @@ __global__ void __launch_bounds__(64 * (C / 16)) chunk_out_kernel(ChunkArgs a) {
     }
     const int col = 16 * jt + l16;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) st1<OB16>(a.o, (orow0 + r) * D + col, acc[r]);
+    for (int r = 0; r < 4; ++r)
+      if (tok0 + r < a.T) st1<OB16>(a.o, (orow0 + r) * D + col, acc[r]);  // no padding rows
   }
 }
 
@@ -928,7 +941,7 @@ __global__ void __launch_bounds__(64 * (C / 16)) chunk_out_kernel(ChunkArgs a) {
 // host side
 // ============================================================================
 size_t chunk_workspace_bytes(int B, int H, int T, int C, int D, int NS) {
-  const size_t nch = (size_t)B * H * (T / C);
+  const size_t nch = (size_t)B * H * ((T + C - 1) / C);
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   return al(nch * NS * (size_t)C * D * 2) + al(nch * NS * (size_t)D * D * 2) +
          al(nch * (size_t)C * D * 4) + al(nch * (size_t)D * D * 4) + al(nch * NS * (size_t)D * D * 2);
@@ -956,7 +969,7 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, int phases, hipStream_t st)
     });
     if (attr_err != hipSuccess) return attr_err;
     const size_t nbh = (size_t)a.B * a.H;
-    const size_t nch = nbh * (size_t)(a.T / C);
+    const size_t nch = nbh * (size_t)((a.T + C - 1) / C);
     if (nch > 0 && (phases & 1)) {
       hipLaunchKernelGGL((chunk_intra_kernel<C, D, NS, BF>), dim3((unsigned)nch), dim3(64 * Lds::WAVES), Lds::bytes, st, a);
       hipError_t e = hipGetLastError();

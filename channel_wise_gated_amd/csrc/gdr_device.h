@@ -201,43 +201,33 @@ __device__ __forceinline__ float raw_elem(const Raw4<BF> &r, int e) {
   }
 }
 
-// Element (idx & 3) for an index that differs between lanes: two selects on
-// its bits (no lane-dependent indexing, no branch).
-template <bool BF>
-__device__ __forceinline__ float raw_pick(const Raw4<BF> &r, int idx) {
-  // bit masks rather than selects: a select between two elements of one vector
-  // would be folded into a dynamic element index
-  const uint32_t m1 = 0u - (uint32_t)(idx & 1), m2 = 0u - (uint32_t)((idx >> 1) & 1);
-  if constexpr (BF) {
-    const uint32_t w = r.x ^ ((r.x ^ r.y) & m2);
-    return __uint_as_float((w << (16 & ~m1)) & 0xffff0000u);
-  } else {
-    const uint32_t x = __float_as_uint(r.x), y = __float_as_uint(r.y);
-    const uint32_t z = __float_as_uint(r.z), w = __float_as_uint(r.w);
-    const uint32_t lo = x ^ ((x ^ y) & m1), hi = z ^ ((z ^ w) & m1);
-    return __uint_as_float(lo ^ ((lo ^ hi) & m2));
-  }
-}
-
-// Four gate values (channels c0..c0+3 of token row `row`) fetched with one
-// unconditional load whatever the gate mode -- a load under a branch makes
-// the compiler wait for every load in flight where the paths join:
+// Four gate values (channels c0..c0+3 of token row `row`) fetched without a
+// branch whatever the gate mode -- a load under a branch makes the compiler
+// wait for every load in flight where the paths join.  Two loads are always
+// issued: the group of four channel values and the single token value; the
+// one the mode does not use reads `any`, a valid 16-byte-aligned address.
 //   per channel  p[row * d + c0 .. c0 + 3]
-//   per token    the aligned group of four token values that holds p[row]
-//                (per-token tensors hold B*H*T values, a multiple of 4)
-//   constant     `any`, a valid 16-byte-aligned address; the value is unused.
+//   per token    p[row]
+//   constant     neither (the value is a constant)
 template <bool BF>
-__device__ __forceinline__ Raw4<BF> gate_load(const void *p, int mode, size_t row, int c0, int d, const void *any) {
-  const bool chan = mode == GDR_GATE_PER_CHANNEL, tok = mode == GDR_GATE_PER_TOKEN;
-  const char *base = reinterpret_cast<const char *>((chan || tok) ? p : any);
-  const size_t off = chan ? row * (size_t)d + c0 : (tok ? (row & ~(size_t)3) : 0);
-  return *reinterpret_cast<const Raw4<BF> *>(base + off * (BF ? 2 : 4));
+struct Gate4 {
+  Raw4<BF> grp;
+  float tok;
+};
+template <bool BF>
+__device__ __forceinline__ Gate4<BF> gate_load(const void *p, int mode, size_t row, int c0, int d, const void *any) {
+  const bool chan = mode == GDR_GATE_PER_CHANNEL, tokm = mode == GDR_GATE_PER_TOKEN;
+  const char *gb = reinterpret_cast<const char *>(chan ? p : any);
+  const char *tb = reinterpret_cast<const char *>(tokm ? p : any);
+  Gate4<BF> g;
+  g.grp = *reinterpret_cast<const Raw4<BF> *>(gb + (chan ? row * (size_t)d + c0 : 0) * (BF ? 2 : 4));
+  g.tok = ld1<BF>(tb, tokm ? row : 0);
+  return g;
 }
-// Value of element e of a group from gate_load; `cval` is the value of a constant mode.
+// Value of element e of a gate_load result; `cval` is the value of a constant mode.
 template <bool BF>
-__device__ __forceinline__ float gate_elem(const Raw4<BF> &raw, int e, int mode, size_t row, float cval) {
-  return mode == GDR_GATE_PER_CHANNEL ? raw_elem<BF>(raw, e)
-                                      : (mode == GDR_GATE_PER_TOKEN ? raw_pick<BF>(raw, (int)(row & 3)) : cval);
+__device__ __forceinline__ float gate_elem(const Gate4<BF> &g, int e, int mode, float cval) {
+  return mode == GDR_GATE_PER_CHANNEL ? raw_elem<BF>(g.grp, e) : (mode == GDR_GATE_PER_TOKEN ? g.tok : cval);
 }
 
 // Value of the constant gate modes: ONES -> 1 (for log alpha: 0), ZEROS -> 0.

@@ -86,7 +86,8 @@ typedef struct gdr_desc {
   int T;                    /* tokens per sequence (ignored by decode, = 1)    */
   int dk;                   /* key channels: 64 or 128                         */
   int dv;                   /* value channels: must equal dk                   */
-  int chunk;                /* chunk size of gdr_chunk_fwd: 64 or 128; T % chunk == 0 */
+  int chunk;                /* chunk size of gdr_chunk_fwd: 64 or 128 (any T;  */
+                            /* the last chunk of a sequence may be short)      */
   gdr_dtype in_dtype;       /* storage of q, k, v, b, w, z                     */
   gdr_dtype out_dtype;      /* storage of o                                    */
   int normalize_qk;         /* 1: SiLU + L2 pre-pass on q, k; 0: used as given */

@@ -51,7 +51,6 @@ GOOD = dict(B=2, H=4, T=256, dk=128, dv=128, chunk=64)
     ("dk", 0, gdr.GDR_ERR_INVALID_ARG),
     ("dv", 64, gdr.GDR_ERR_UNSUPPORTED),          # dk != dv
     ("chunk", 32, gdr.GDR_ERR_INVALID_ARG),
-    ("T", 100, gdr.GDR_ERR_INVALID_ARG),           # T % chunk != 0
     ("T", -64, gdr.GDR_ERR_INVALID_ARG),
     ("B", -1, gdr.GDR_ERR_INVALID_ARG),
     ("in_dtype", 7, gdr.GDR_ERR_INVALID_ARG),
@@ -78,6 +77,9 @@ def test_workspace_query_sizes():
                        2 * 128 * 128 * 2)
     rc, n0 = ws(gdr.make_desc(**dict(GOOD, T=0)))
     assert rc == gdr.GDR_OK and n0 == 0
+    # a ragged length takes one (short) chunk more
+    rc, nr = ws(gdr.make_desc(**dict(GOOD, T=257)))
+    assert rc == gdr.GDR_OK and nr == n * (256 // 64 + 1) // (256 // 64)
     # fp32 mode needs three planes; C = D = 128 does not fit the LDS budget
     assert ws(gdr.make_desc(**dict(GOOD, chunk=128, in_dtype=gdr.GDR_F32)))[0] == gdr.GDR_ERR_UNSUPPORTED
     assert ws(gdr.make_desc(**dict(GOOD, chunk=128)))[0] == gdr.GDR_OK

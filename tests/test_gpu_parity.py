@@ -105,8 +105,85 @@ def test_chunk_dims_and_dtypes(dtype, d, chunk):
 
 
 # ----------------------------------------------------------------------------
+# ragged sequence lengths: T not a multiple of the chunk (short last chunk)
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,chunk,T", [
+    ("gdn2", 64, 1), ("gdn2", 64, 37), ("gdn2", 128, 100), ("gdn2", 128, 129),
+    ("kda", 64, 203), ("stress", 128, 333), ("tiny", 64, 70)])
+def test_chunk_ragged_tail(name, chunk, T):
+    wl = WORKLOADS[name].with_sizes(B=2, H=2, T=T)
+    x = make_inputs(wl)
+    o, sT = gpu_chunk(x, chunk)
+    ro, rs = oracle_run(x)
+    check(f"{name} T{T} C{chunk} o", o, ro, tol_for(x))
+    check(f"{name} T{T} C{chunk} S_T", sT, rs, tol_for(x))
+
+
+def test_ragged_tail_leaves_neighbours_untouched():
+    """The padding rows of a short last chunk are never stored: o is written
+    exactly over [B,H,T] (a guard region around it keeps its fill value)."""
+    wl = WORKLOADS["gdn2"].with_sizes(B=2, H=2, T=77)
+    x = dev(make_inputs(wl))
+    B, H, T, dv = 2, 2, 77, wl.dv
+    big = torch.full((B * H * T * dv + 4096,), 12345.0, device=DEV)
+    o = big[2048:2048 + B * H * T * dv].view(B, H, T, dv)
+    call = gdr.ChunkCall(x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"], x["gamma"],
+                         x["z"], x["S0"], chunk=64, o=o)
+    call()
+    torch.cuda.synchronize()
+    assert bool((big[:2048] == 12345.0).all()) and bool((big[-2048:] == 12345.0).all())
+    ro, _ = oracle_run({k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in x.items()})
+    check("guarded o", o.cpu().numpy(), ro, TOL_BF16)
+
+
+def test_prefill_then_decode_handoff():
+    """A chunkwise prefill of a ragged length followed by decode steps from
+    its final state equals the recurrence over the whole sequence."""
+    wl = WORKLOADS["gdn2"].with_sizes(B=2, H=2, T=150)
+    x = make_inputs(wl)
+    Tp = 141
+    pre = {k: (v[:, :, :Tp].contiguous() if isinstance(v, torch.Tensor) and k not in ("gamma", "S0")
+               else v) for k, v in x.items()}
+    o_pre, S = gpu_chunk(pre, 64)
+    S = torch.from_numpy(S).to(DEV)
+    outs = [o_pre]
+    for tt in range(Tp, wl.T):
+        xt = {k: (v[:, :, tt] if isinstance(v, torch.Tensor) and k not in ("gamma", "S0") else v)
+              for k, v in x.items()}
+        outs.append(gpu_decode(S, xt).float().cpu().numpy()[:, :, None])
+    torch.cuda.synchronize()
+    ro, rs = oracle_run(x)
+    check("prefill+decode o", np.concatenate(outs, axis=2), ro, TOL_BF16)
+    check("prefill+decode S", S.cpu().numpy(), rs, TOL_BF16)
+
+
+# ----------------------------------------------------------------------------
 # the workloads at full size: GPU on everything, oracle on sampled streams
 # ----------------------------------------------------------------------------
+
+FULL_RAGGED = [("stress", 128, 32768 - 45, [(0, 2), (0, 13)])]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,chunk,T,pairs", FULL_RAGGED)
+def test_chunk_full_size_ragged_sampled(name, chunk, T, pairs):
+    """The long-context workload with a length that is not a multiple of the
+    chunk, in the benchmark's launch configuration, sampled streams."""
+    wl = WORKLOADS[name].with_sizes(T=T)
+    print(f"full-size ragged {name} B{wl.B} H{wl.H} T{wl.T} C{chunk}", flush=True)
+    xd = make_inputs_device(wl, DEV, seed=13)
+    o, sT = gdr.gdr_chunk_fwd(xd["q"], xd["k"], xd["v"], xd["log_alpha"], xd["b"], xd["w"],
+                              gamma=xd["gamma"], z=xd["z"], S0=xd["S0"], chunk=chunk)
+    torch.cuda.synchronize()
+    bi = torch.tensor([b for b, _ in pairs], device=DEV)
+    hi = torch.tensor([h for _, h in pairs], device=DEV)
+    xs = {key: (None if val is None else (val[hi].cpu() if key == "gamma" else val[bi, hi][None].cpu()))
+          for key, val in xd.items()}
+    ro, rs = oracle_run(xs)
+    check(f"{name} T{T} C{chunk} o sampled", o[bi, hi][None].float().cpu().numpy(), ro, TOL_BF16)
+    check(f"{name} T{T} C{chunk} S_T sampled", sT[bi, hi][None].cpu().numpy(), rs, TOL_BF16)
+
 
 FULL = [("kda", 64, [(0, 0), (1, 7), (2, 11), (3, 15)]),
         ("gdn2", 64, [(0, 3), (1, 12)]),
