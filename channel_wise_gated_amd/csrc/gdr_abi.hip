@@ -52,28 +52,32 @@ gdr_status check_inputs(const gdr_desc *d, const void *q, const void *k, const v
   return GDR_OK;
 }
 
-gdr_status chunk_plan(const gdr_desc *d, size_t *ws) {
+// nseq = 0: B sequences of T tokens; nseq > 0: a packed batch (B = 1).
+gdr_status chunk_plan(const gdr_desc *d, int nseq, size_t *ws) {
   gdr_status s = check_common(d, d ? d->T : 0);
   if (s != GDR_OK) return s;
   if (d->chunk != 64 && d->chunk != 128) return GDR_ERR_INVALID_ARG;
+  if (nseq < 0 || (nseq > 0 && d->B != 1)) return GDR_ERR_INVALID_ARG;
   const int ns = d->in_dtype == GDR_BF16 ? 2 : 3;
   if (!gdr::chunk_intra_fits(d->chunk, d->dk, ns)) return GDR_ERR_UNSUPPORTED;
-  *ws = gdr::chunk_workspace_bytes(d->B, d->H, d->T, d->chunk, d->dk, ns);
+  *ws = gdr::chunk_workspace(nullptr, nullptr, d->B, d->H, d->T, d->chunk, d->dk, ns, nseq);
   return GDR_OK;
 }
 
 // Validation and launch shared by the whole call (phases = 3), the
 // intra-chunk phase (1: reads the token inputs, writes the workspace) and the
 // scan phase (2: reads the workspace and S0, writes o and S_T).
-gdr_status chunk_call(const gdr_desc *desc, const void *q, const void *k, const void *v,
-                      const float *log_alpha, const void *b, const void *w, const float *gamma,
-                      const void *z, const float *S0, void *o, float *S_T, void *workspace,
-                      size_t workspace_bytes, void *stream, int phases) {
+gdr_status chunk_call(const gdr_desc *desc, int nseq, const int *cu, const void *q, const void *k,
+                      const void *v, const float *log_alpha, const void *b, const void *w,
+                      const float *gamma, const void *z, const float *S0, void *o, float *S_T,
+                      void *workspace, size_t workspace_bytes, void *stream, int phases) {
   size_t need = 0;
-  gdr_status s = chunk_plan(desc, &need);
+  gdr_status s = chunk_plan(desc, nseq, &need);
   if (s != GDR_OK) return s;
   const gdr_desc &d = *desc;
-  if ((size_t)d.B * d.H == 0) return GDR_OK;
+  const long long streams = nseq > 0 ? (long long)nseq * d.H : (long long)d.B * d.H;
+  if (streams == 0) return GDR_OK;
+  if (nseq > 0 && (!cu || (reinterpret_cast<uintptr_t>(cu) & 3u))) return GDR_ERR_INVALID_ARG;
   if (d.T > 0 && (phases & 1)) {
     s = check_inputs(desc, q, k, v, log_alpha, b, w, gamma, z, (phases & 2) ? o : q);
     if (s != GDR_OK) return s;
@@ -84,25 +88,18 @@ gdr_status chunk_call(const gdr_desc *desc, const void *q, const void *k, const 
   if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u)) return GDR_ERR_WORKSPACE;
 
   const int ns = d.in_dtype == GDR_BF16 ? 2 : 3;
-  const size_t nch = (size_t)d.B * d.H * ((d.T + d.chunk - 1) / d.chunk);  // last chunk may be short
-  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  unsigned char *ws = static_cast<unsigned char *>(workspace);
   gdr::ChunkArgs a;
   a.q = q; a.k = k; a.v = v; a.b = b; a.w = w; a.z = z;
   a.log_alpha = log_alpha; a.gamma = gamma; a.S0 = S0;
   a.o = o; a.S_T = S_T;
-  a.Qp = reinterpret_cast<uint16_t *>(ws);
-  ws += al(nch * ns * (size_t)d.chunk * d.dk * 2);
-  a.Mm = reinterpret_cast<uint16_t *>(ws);
-  ws += al(nch * ns * (size_t)d.dk * d.dk * 2);
-  a.Ob = reinterpret_cast<float *>(ws);
-  ws += al(nch * (size_t)d.chunk * d.dk * 4);
-  a.Nn = reinterpret_cast<float *>(ws);
-  ws += al(nch * (size_t)d.dk * d.dk * 4);
-  a.Sc = reinterpret_cast<uint16_t *>(ws);
-  a.B = d.B; a.H = d.H; a.T = d.T;
+  a.Qp = a.Mm = a.Sc = nullptr; a.Ob = a.Nn = nullptr;
+  gdr::chunk_workspace(&a, workspace, d.B, d.H, d.T, d.chunk, d.dk, ns, nseq);
+  a.B = nseq > 0 ? nseq : d.B; a.H = d.H; a.T = d.T;
   a.alpha_mode = d.alpha_mode; a.b_mode = d.b_mode; a.w_mode = d.w_mode;
   a.normalize_qk = d.normalize_qk; a.scale = d.scale;
+  a.cu = nseq > 0 ? cu : nullptr;
+  a.nseq = nseq;
+  if (nseq == 0) { a.ctab = nullptr; a.coff = nullptr; a.ctab_len = 0; }
   hipError_t e = gdr::launch_chunk(d, a, phases, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }
@@ -114,7 +111,7 @@ extern "C" {
 gdr_status gdr_chunk_fwd_workspace_size(const gdr_desc *desc, size_t *bytes) {
   if (!bytes) return GDR_ERR_INVALID_ARG;
   size_t ws = 0;
-  gdr_status s = chunk_plan(desc, &ws);
+  gdr_status s = chunk_plan(desc, 0, &ws);
   if (s == GDR_OK) *bytes = ws;
   return s;
 }
@@ -123,7 +120,7 @@ gdr_status gdr_chunk_fwd(const gdr_desc *desc, const void *q, const void *k, con
                          const float *log_alpha, const void *b, const void *w, const float *gamma,
                          const void *z, const float *S0, void *o, float *S_T, void *workspace,
                          size_t workspace_bytes, void *stream) {
-  return chunk_call(desc, q, k, v, log_alpha, b, w, gamma, z, S0, o, S_T, workspace,
+  return chunk_call(desc, 0, nullptr, q, k, v, log_alpha, b, w, gamma, z, S0, o, S_T, workspace,
                     workspace_bytes, stream, 3);
 }
 
@@ -131,14 +128,32 @@ gdr_status gdr_chunk_fwd_intra(const gdr_desc *desc, const void *q, const void *
                                const float *log_alpha, const void *b, const void *w,
                                const float *gamma, const void *z, void *workspace,
                                size_t workspace_bytes, void *stream) {
-  return chunk_call(desc, q, k, v, log_alpha, b, w, gamma, z, nullptr, nullptr, nullptr, workspace,
-                    workspace_bytes, stream, 1);
+  return chunk_call(desc, 0, nullptr, q, k, v, log_alpha, b, w, gamma, z, nullptr, nullptr, nullptr,
+                    workspace, workspace_bytes, stream, 1);
 }
 
 gdr_status gdr_chunk_fwd_scan(const gdr_desc *desc, const float *S0, void *o, float *S_T,
                               const void *workspace, size_t workspace_bytes, void *stream) {
-  return chunk_call(desc, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
-                    S0, o, S_T, const_cast<void *>(workspace), workspace_bytes, stream, 2);
+  return chunk_call(desc, 0, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                    nullptr, S0, o, S_T, const_cast<void *>(workspace), workspace_bytes, stream, 2);
+}
+
+gdr_status gdr_chunk_fwd_varlen_workspace_size(const gdr_desc *desc, int n_seqs, size_t *bytes) {
+  if (!bytes || n_seqs < 1) return GDR_ERR_INVALID_ARG;
+  size_t ws = 0;
+  gdr_status s = chunk_plan(desc, n_seqs, &ws);
+  if (s == GDR_OK) *bytes = ws;
+  return s;
+}
+
+gdr_status gdr_chunk_fwd_varlen(const gdr_desc *desc, int n_seqs, const int *cu_seqlens,
+                                const void *q, const void *k, const void *v,
+                                const float *log_alpha, const void *b, const void *w,
+                                const float *gamma, const void *z, const float *S0, void *o,
+                                float *S_T, void *workspace, size_t workspace_bytes, void *stream) {
+  if (n_seqs < 1) return GDR_ERR_INVALID_ARG;
+  return chunk_call(desc, n_seqs, cu_seqlens, q, k, v, log_alpha, b, w, gamma, z, S0, o, S_T,
+                    workspace, workspace_bytes, stream, 3);
 }
 
 gdr_status gdr_decode_step(const gdr_desc *desc, float *S, const void *q, const void *k,

@@ -152,15 +152,25 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int l16 = lane & 15, g = lane >> 4;
-  const int NC = (a.T + C - 1) / C;
-  const size_t ch = blockIdx.x;
-  const size_t bh = ch / NC;
-  const int h = (int)(bh % a.H);
-  const size_t row0 = bh * (size_t)a.T + (size_t)(ch % NC) * C;  // first token row
+  const size_t ch = blockIdx.x;  // chunk slot in the workspace
+  int h, tvalid;
+  size_t row0;  // first token row
+  if (a.ctab) {  // packed batch: slot = entry * H + head
+    const int4 e = a.ctab[ch / a.H];
+    if (e.x < 0) return;  // past the last chunk (the grid is an upper bound)
+    h = (int)(ch % a.H);
+    row0 = (size_t)h * a.T + e.z;
+    tvalid = e.w;
+  } else {
+    const int NC = (a.T + C - 1) / C;
+    const size_t bh = ch / NC;
+    h = (int)(bh % a.H);
+    row0 = bh * (size_t)a.T + (size_t)(ch % NC) * C;
+    tvalid = min(C, a.T - (int)(ch % NC) * C);
+  }
   // The last chunk of a sequence may be short: its tokens from `tvalid` on
   // are padding, read at the last real row and turned into identity steps
   // (log alpha = 0, no erase, no write); their outputs are never stored.
-  const int tvalid = min(C, a.T - (int)(ch % NC) * C);
   const bool norm = a.normalize_qk != 0;
   const bool rowwave = wave < NB;
   const int i = wave;                       // token block of this wave
@@ -778,7 +788,20 @@ __global__ void __launch_bounds__(64 * (D / 16)) chunk_chain_kernel(ChunkArgs a)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
-  const int NC = (a.T + C - 1) / C;  // the last chunk may be short
+  // chunks of this stream and their workspace slots
+  int NC;
+  size_t slot0, slot_step;
+  if (a.ctab) {  // packed batch: stream = sequence * H + head, slot = entry * H + head
+    const int n = (int)(bh / a.H);
+    NC = (max(a.cu[n + 1] - a.cu[n], 0) + C - 1) / C;
+    slot0 = (size_t)a.coff[n] * a.H + bh % a.H;
+    slot_step = a.H;
+  } else {
+    NC = (a.T + C - 1) / C;  // the last chunk may be short
+    slot0 = bh * NC;
+    slot_step = 1;
+  }
+  auto slot = [&](int c) { return slot0 + (size_t)c * slot_step; };
   const int col = 16 * slice + l16;
 
   f32x4 S = zero4();
@@ -800,7 +823,7 @@ __global__ void __launch_bounds__(64 * (D / 16)) chunk_chain_kernel(ChunkArgs a)
   // into another buffer is still in flight (that would cost a wait)
   auto load = [&](int c, ChainBuf<D, NS> &bf) {
     c = c < NC ? c : NC - 1;  // clamped instead of skipped: no conditional load
-    const size_t ch = bh * NC + c;
+    const size_t ch = slot(c);
     const auto rm = buffer_rsrc(a.Mm + ch * NS * (size_t)D * D, (uint32_t)(NS * D * D * 2));
     const auto rn = buffer_rsrc(a.Nn + ch * (size_t)D * D, (uint32_t)(D * D * 4));
     bf.nn = buffer_load16<f32x4>(rn, 4 * off_nn);
@@ -813,7 +836,7 @@ __global__ void __launch_bounds__(64 * (D / 16)) chunk_chain_kernel(ChunkArgs a)
   auto step = [&](int c, const ChainBuf<D, NS> &cur, int par) {
     const uint16_t *sfr = sfr2[par];
     // chunk-start state planes -> workspace (fragment f = ks * NS + p)
-    uint16_t *Sc = a.Sc + (bh * NC + c) * (size_t)NS * D * D + (size_t)slice * NFR * FRAG;
+    uint16_t *Sc = a.Sc + slot(c) * (size_t)NS * D * D + (size_t)slice * NFR * FRAG;
     if constexpr (NFR == NMT) {  // one fragment per wave, no branch (keeps the wait counts exact)
       *reinterpret_cast<bf16x8 *>(Sc + wave * FRAG + lane * 8) =
           *reinterpret_cast<const bf16x8 *>(sfr + wave * FRAG + lane * 8);
@@ -901,10 +924,20 @@ __global__ void __launch_bounds__(64 * (C / 16)) chunk_out_kernel(ChunkArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
-  const int NC = (a.T + C - 1) / C;  // the last chunk may be short
-  const size_t ch = blockIdx.x;
-  const size_t bh = ch / NC;
-  const int c = (int)(ch % NC);
+  const size_t ch = blockIdx.x;  // chunk slot (layout as in the intra-chunk kernel)
+  size_t rbase;                   // first token row of the chunk
+  int tvalid;
+  if (a.ctab) {
+    const int4 e = a.ctab[ch / a.H];
+    if (e.x < 0) return;
+    rbase = (ch % a.H) * (size_t)a.T + e.z;
+    tvalid = e.w;
+  } else {
+    const int NC = (a.T + C - 1) / C;  // the last chunk may be short
+    const int c = (int)(ch % NC);
+    rbase = (ch / NC) * (size_t)a.T + (size_t)c * C;
+    tvalid = min(C, a.T - c * C);
+  }
 
   const uint16_t *Scg = a.Sc + ch * (size_t)NS * D * D;
   constexpr int NV = NSL * NFR * FRAG / 8;  // 16-byte vectors
@@ -919,8 +952,8 @@ __global__ void __launch_bounds__(64 * (C / 16)) chunk_out_kernel(ChunkArgs a) {
       qf[ks][p] = *reinterpret_cast<const bf16x8 *>(Qp + (size_t)p * C * D + ((wave * NKD + ks) * 64 + lane) * 8);
   const float *Ob = a.Ob + ch * (size_t)C * D;
   __syncthreads();
-  const int tok0 = c * C + 16 * wave + 4 * g;  // token index (within the sequence) of acc[0]
-  const size_t orow0 = bh * (size_t)a.T + tok0;
+  const int tok0 = 16 * wave + 4 * g;  // token of acc[0] within the chunk
+  const size_t orow0 = rbase + tok0;
 #pragma unroll 1
   for (int jt = 0; jt < NSL; ++jt) {
     f32x4 acc = *reinterpret_cast<const f32x4 *>(Ob + ((size_t)(wave * NMT + jt) * 64 + lane) * 4);
@@ -933,18 +966,80 @@ __global__ void __launch_bounds__(64 * (C / 16)) chunk_out_kernel(ChunkArgs a) {
     const int col = 16 * jt + l16;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      if (tok0 + r < a.T) st1<OB16>(a.o, (orow0 + r) * D + col, acc[r]);  // no padding rows
+      if (tok0 + r < tvalid) st1<OB16>(a.o, (orow0 + r) * D + col, acc[r]);  // no padding rows
   }
+}
+
+// ============================================================================
+// Packed batches: the per-head chunk list.  One workgroup scans the chunk
+// counts ceil(len_n / C) of the sequences (1024 at a time), writes the
+// offsets coff[0..nseq] and, per sequence, its entries {n, c, first packed
+// row, valid tokens}; entries past the last chunk get sequence -1.
+// ============================================================================
+template <int C>
+__global__ void __launch_bounds__(1024) chunk_table_kernel(ChunkArgs a) {
+  __shared__ int wsum[16];
+  __shared__ int carry;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) carry = 0;
+  __syncthreads();
+  for (int base = 0; base <= a.nseq; base += 1024) {
+    const int n = base + tid;
+    int len = 0, cnt = 0;
+    if (n < a.nseq) {
+      len = max(a.cu[n + 1] - a.cu[n], 0);
+      cnt = (len + C - 1) / C;
+    }
+    int x = cnt;  // inclusive scan within the wave
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(x, d, 64);
+      if (lane >= d) x += y;
+    }
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    if (tid == 0) {  // wave totals -> exclusive offsets of the waves
+      int acc = 0;
+      for (int w = 0; w < 16; ++w) { const int t = wsum[w]; wsum[w] = acc; acc += t; }
+    }
+    __syncthreads();
+    const int excl = carry + wsum[wave] + x - cnt;  // chunks before sequence n
+    if (n <= a.nseq) a.coff[n] = excl;
+    if (n < a.nseq) {
+      const int r0 = a.cu[n];
+      for (int c = 0; c < cnt; ++c) a.ctab[excl + c] = make_int4(n, c, r0 + c * C, min(C, len - c * C));
+    }
+    __syncthreads();
+    if (tid == 1023) carry = excl + cnt;  // running total after this block of sequences
+    __syncthreads();
+  }
+  for (int j = carry + tid; j < a.ctab_len; j += 1024) a.ctab[j] = make_int4(-1, 0, 0, 0);
 }
 
 // ============================================================================
 // host side
 // ============================================================================
-size_t chunk_workspace_bytes(int B, int H, int T, int C, int D, int NS) {
-  const size_t nch = (size_t)B * H * ((T + C - 1) / C);
+size_t chunk_workspace(ChunkArgs *a, void *ws, int B, int H, int T, int C, int D, int NS, int nseq) {
+  const size_t per_head = (size_t)((T + C - 1) / C) + (nseq > 0 ? (size_t)nseq : 0);
+  const size_t nch = nseq > 0 ? (size_t)H * per_head : (size_t)B * H * ((T + C - 1) / C);
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  return al(nch * NS * (size_t)C * D * 2) + al(nch * NS * (size_t)D * D * 2) +
-         al(nch * (size_t)C * D * 4) + al(nch * (size_t)D * D * 4) + al(nch * NS * (size_t)D * D * 2);
+  const size_t sz[7] = {nch * NS * (size_t)C * D * 2, nch * NS * (size_t)D * D * 2, nch * (size_t)C * D * 4,
+                        nch * (size_t)D * D * 4, nch * NS * (size_t)D * D * 2,
+                        nseq > 0 ? per_head * sizeof(int4) : 0, nseq > 0 ? ((size_t)nseq + 1) * sizeof(int) : 0};
+  size_t off[7], total = 0;
+  for (int r = 0; r < 7; ++r) { off[r] = total; total += al(sz[r]); }
+  if (ws && a) {
+    unsigned char *base = static_cast<unsigned char *>(ws);
+    a->Qp = reinterpret_cast<uint16_t *>(base + off[0]);
+    a->Mm = reinterpret_cast<uint16_t *>(base + off[1]);
+    a->Ob = reinterpret_cast<float *>(base + off[2]);
+    a->Nn = reinterpret_cast<float *>(base + off[3]);
+    a->Sc = reinterpret_cast<uint16_t *>(base + off[4]);
+    a->ctab = nseq > 0 ? reinterpret_cast<int4 *>(base + off[5]) : nullptr;
+    a->coff = nseq > 0 ? reinterpret_cast<int *>(base + off[6]) : nullptr;
+    a->ctab_len = nseq > 0 ? (int)per_head : 0;
+  }
+  return total;
 }
 
 bool chunk_intra_fits(int C, int D, int NS) {
@@ -969,7 +1064,12 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, int phases, hipStream_t st)
     });
     if (attr_err != hipSuccess) return attr_err;
     const size_t nbh = (size_t)a.B * a.H;
-    const size_t nch = nbh * (size_t)((a.T + C - 1) / C);
+    const size_t nch = a.ctab ? (size_t)a.H * a.ctab_len : nbh * (size_t)((a.T + C - 1) / C);
+    if (a.ctab && (phases & 1)) {
+      hipLaunchKernelGGL((chunk_table_kernel<C>), dim3(1), dim3(1024), 0, st, a);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
     if (nch > 0 && (phases & 1)) {
       hipLaunchKernelGGL((chunk_intra_kernel<C, D, NS, BF>), dim3((unsigned)nch), dim3(64 * Lds::WAVES), Lds::bytes, st, a);
       hipError_t e = hipGetLastError();

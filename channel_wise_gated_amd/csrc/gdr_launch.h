@@ -20,6 +20,15 @@ struct ChunkArgs {
   uint16_t *Sc;       // workspace: chunk-start states as B-fragment planes
   int B, H, T, alpha_mode, b_mode, w_mode, normalize_qk;
   float scale;
+  // Packed variable-length batch (all null / 0 otherwise): B = 1, T = total
+  // tokens, sequence n holds packed rows cu[n] .. cu[n+1]-1.  Chunk slot
+  // g = j * H + h holds chunk j of the per-head chunk list ctab (entries
+  // {sequence, chunk of the sequence, first packed row, valid tokens}, or
+  // sequence -1 past the end); coff[n] is the first entry of sequence n.
+  const int *cu;
+  int *coff;
+  int4 *ctab;
+  int nseq, ctab_len;
 };
 
 hipError_t launch_decode(const gdr_desc &d, float *S, const void *q, const void *k, const void *v,
@@ -27,7 +36,12 @@ hipError_t launch_decode(const gdr_desc &d, float *S, const void *q, const void 
                          const void *z, void *o, hipStream_t st);
 // phases: bit 0 = intra-chunk kernel, bit 1 = scan kernel
 hipError_t launch_chunk(const gdr_desc &d, const ChunkArgs &a, int phases, hipStream_t st);
-size_t chunk_workspace_bytes(int B, int H, int T, int C, int D, int NS);
+// Workspace of the chunkwise forward: per chunk slot the maps Q', M, O_bar,
+// N and the chunk-start state; for a packed batch (nseq > 0) also the chunk
+// list and sequence offsets.  Slots: B*H*ceil(T/C), or H * (ceil(T/C) + nseq)
+// for a packed batch (each sequence adds at most one short chunk).  Returns
+// the size in bytes; with `ws` set, also points the fields of *a into it.
+size_t chunk_workspace(ChunkArgs *a, void *ws, int B, int H, int T, int C, int D, int NS, int nseq);
 bool chunk_intra_fits(int C, int D, int NS);
 
 }  // namespace gdr

@@ -27,7 +27,8 @@ GDR_OK, GDR_ERR_INVALID_ARG, GDR_ERR_UNSUPPORTED, GDR_ERR_WORKSPACE, GDR_ERR_HIP
 GDR_BF16, GDR_F32 = 0, 1
 PER_CHANNEL, PER_TOKEN, ONES, ZEROS = 0, 1, 2, 3
 SYMBOLS = ("gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_chunk_fwd_intra",
-           "gdr_chunk_fwd_scan", "gdr_decode_step", "gdr_status_string", "gdr_version")
+           "gdr_chunk_fwd_scan", "gdr_chunk_fwd_varlen_workspace_size", "gdr_chunk_fwd_varlen",
+           "gdr_decode_step", "gdr_status_string", "gdr_version")
 
 
 class GdrDesc(ctypes.Structure):
@@ -68,6 +69,11 @@ def load() -> ctypes.CDLL:
     lib.gdr_chunk_fwd_intra.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gdr_chunk_fwd_scan.restype = ctypes.c_int
     lib.gdr_chunk_fwd_scan.argtypes = [dp, vp, vp, vp, vp, sz, vp]
+    lib.gdr_chunk_fwd_varlen_workspace_size.restype = ctypes.c_int
+    lib.gdr_chunk_fwd_varlen_workspace_size.argtypes = [dp, ctypes.c_int, ctypes.POINTER(sz)]
+    lib.gdr_chunk_fwd_varlen.restype = ctypes.c_int
+    lib.gdr_chunk_fwd_varlen.argtypes = [dp, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                         vp, vp, vp, sz, vp]
     lib.gdr_decode_step.restype = ctypes.c_int
     lib.gdr_decode_step.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.gdr_status_string.restype = ctypes.c_char_p
@@ -249,3 +255,56 @@ def gdr_decode_step(S, q, k, v, log_alpha, b, w, gamma=None, z=None, *, out_dtyp
     if rc != GDR_OK:
         raise GdrError(rc, "gdr_decode_step")
     return o
+
+
+def gdr_chunk_fwd_varlen_workspace_size(desc: GdrDesc, n_seqs: int) -> int:
+    n = ctypes.c_size_t(0)
+    rc = load().gdr_chunk_fwd_varlen_workspace_size(ctypes.byref(desc), int(n_seqs), ctypes.byref(n))
+    if rc != GDR_OK:
+        raise GdrError(rc, "gdr_chunk_fwd_varlen_workspace_size")
+    return int(n.value)
+
+
+def gdr_chunk_fwd_varlen(q, k, v, log_alpha, b, w, cu_seqlens, gamma=None, z=None, S0=None, *,
+                         chunk=64, out_dtype=torch.float32, normalize_qk=True, scale=1.0, o=None,
+                         S_T=None, workspace=None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Chunkwise forward of a packed batch of sequences of different lengths;
+    see gdr_chunk_fwd_varlen in gdr.h.
+
+    q, k: [1,H,T,dk], v: [1,H,T,dv], z [1,H,T,dk], gates [1,H,T,d] / [1,H,T] /
+    scalars, all packed along T; cu_seqlens: int32 device tensor [N+1]
+    (cu_seqlens[N] = T); gamma [H,dk]; S0 [N,H,dk,dv] fp32.
+    Returns (o [1,H,T,dv], S_T [N,H,dk,dv]).
+    """
+    lib = load()
+    q, k, v, z, gamma, S0 = map(_contig, (q, k, v, z, gamma, S0))
+    cu = _contig(cu_seqlens)
+    if cu.dtype != torch.int32 or cu.dim() != 1 or not cu.is_cuda:
+        raise ValueError("cu_seqlens must be a 1-d int32 device tensor")
+    n_seqs = cu.numel() - 1
+    Bq, H, T, dk = q.shape
+    dv = v.shape[-1]
+    if isinstance(log_alpha, (int, float)):
+        if log_alpha != 0:
+            raise ValueError("scalar log_alpha must be 0")
+        amode, la = ONES, None
+    else:
+        amode, la = _gate(_contig(log_alpha), 4, "log_alpha")
+    bmode, bt = _gate(_contig(b), 4, "b")
+    wmode, wt = _gate(_contig(w), 4, "w")
+    od = GDR_BF16 if out_dtype == torch.bfloat16 else GDR_F32
+    desc = make_desc(Bq, H, T, dk, dv, chunk, _dtype_code(q), od, int(bool(normalize_qk)), scale,
+                     amode, bmode, wmode)
+    if o is None:
+        o = torch.empty((Bq, H, T, dv), dtype=out_dtype, device=q.device)
+    if S_T is None:
+        S_T = torch.empty((max(n_seqs, 0), H, dk, dv), dtype=torch.float32, device=q.device)
+    need = gdr_chunk_fwd_varlen_workspace_size(desc, n_seqs)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ptrs = [_ptr(t) for t in (q, k, v, la, bt, wt, gamma, z)]
+    rc = lib.gdr_chunk_fwd_varlen(ctypes.byref(desc), n_seqs, _ptr(cu), *ptrs, _ptr(S0), _ptr(o),
+                                  _ptr(S_T), _ptr(workspace), workspace.numel(), _stream(stream))
+    if rc != GDR_OK:
+        raise GdrError(rc, "gdr_chunk_fwd_varlen")
+    return o, S_T

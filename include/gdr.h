@@ -152,6 +152,34 @@ gdr_status gdr_chunk_fwd_scan(const gdr_desc *desc, const float *S0, void *o, fl
                               const void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Chunkwise forward of a packed batch of n_seqs sequences of different
+ * lengths: every sequence and head runs the recurrence of gdr_chunk_fwd from
+ * its own S0 (Muir notes section 2.4 chunk form; the blog's forward(x, cache)
+ * per sequence).  The token axis of every per-token tensor is the
+ * concatenation of the sequences: sequence n holds packed tokens
+ * cu_seqlens[n] .. cu_seqlens[n+1]-1, and its chunks start at its first token.
+ *
+ *   desc->B     must be 1; desc->T = total packed tokens = cu_seqlens[n_seqs]
+ *   cu_seqlens  device int32 [n_seqs + 1]: cu_seqlens[0] = 0, nondecreasing,
+ *               last = desc->T (a precondition, not checked on the device);
+ *               a sequence may be empty
+ *   q, k, v, log_alpha, b, w, z, o   as gdr_chunk_fwd with B = 1 (packed)
+ *   gamma       [H,dk] fp32 or NULL
+ *   S0, S_T     [n_seqs,H,dk,dv] fp32 or NULL; S_T may alias S0
+ *   workspace   >= gdr_chunk_fwd_varlen_workspace_size(desc, n_seqs) bytes,
+ *               256-byte aligned, contents undefined on entry and on return.
+ * Errors as gdr_chunk_fwd; GDR_ERR_INVALID_ARG also for desc->B != 1,
+ * n_seqs < 1, or a null or misaligned cu_seqlens.
+ */
+gdr_status gdr_chunk_fwd_varlen_workspace_size(const gdr_desc *desc, int n_seqs, size_t *bytes);
+
+gdr_status gdr_chunk_fwd_varlen(const gdr_desc *desc, int n_seqs, const int *cu_seqlens,
+                                const void *q, const void *k, const void *v,
+                                const float *log_alpha, const void *b, const void *w,
+                                const float *gamma, const void *z, const float *S0, void *o,
+                                float *S_T, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * One decode step for B sequences x H heads (the blog's section 3 forward()
  * with a one-token x and `cache` = S): reads S once, forms
  * u = v_hat - k_hat (Diag(alpha) S), writes S <- Diag(alpha) S + kn^T u in

@@ -157,3 +157,27 @@ def test_decode_rejects_before_launch():
     bad = gdr.make_desc(B=4, H=2, T=1, dk=80, dv=80)
     assert lib.gdr_decode_step(ctypes.byref(bad), *[c(x) for x in args], None) == gdr.GDR_ERR_UNSUPPORTED
     assert lib.gdr_decode_step(None, *[c(x) for x in args], None) == gdr.GDR_ERR_INVALID_ARG
+
+
+def test_varlen_validation():
+    lib = _lib()
+    d = gdr.make_desc(B=1, H=4, T=300, dk=128, dv=128, chunk=64)
+    n = ctypes.c_size_t(0)
+    assert lib.gdr_chunk_fwd_varlen_workspace_size(ctypes.byref(d), 3, ctypes.byref(n)) == gdr.GDR_OK
+    # per head ceil(300 / 64) + 3 chunk slots, plus the chunk list and offsets
+    per_head = 5 + 3
+    slots = 4 * per_head
+    maps = slots * (2 * 64 * 128 * 2 + 2 * 128 * 128 * 2 + 64 * 128 * 4 + 128 * 128 * 4 + 2 * 128 * 128 * 2)
+    assert n.value == maps + 256 + 256     # 8 x 16-byte entries and 4 offsets, each padded to 256
+    assert lib.gdr_chunk_fwd_varlen_workspace_size(ctypes.byref(d), 0, ctypes.byref(n)) == \
+        gdr.GDR_ERR_INVALID_ARG
+    d2 = gdr.make_desc(B=2, H=4, T=300, dk=128, dv=128, chunk=64)
+    assert lib.gdr_chunk_fwd_varlen_workspace_size(ctypes.byref(d2), 3, ctypes.byref(n)) == \
+        gdr.GDR_ERR_INVALID_ARG
+    c = lambda x: None if x is None else ctypes.c_void_p(x)
+    def call(cu, nseq=3):
+        return lib.gdr_chunk_fwd_varlen(ctypes.byref(d), nseq, c(cu), c(16), c(32), c(48), c(64), c(80),
+                                        c(96), None, None, None, c(112), c(128), c(256), 1 << 30, None)
+    assert call(None) == gdr.GDR_ERR_INVALID_ARG
+    assert call(1026) == gdr.GDR_ERR_INVALID_ARG   # misaligned offsets
+    assert call(1024, nseq=0) == gdr.GDR_ERR_INVALID_ARG

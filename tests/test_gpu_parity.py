@@ -159,6 +159,82 @@ def test_prefill_then_decode_handoff():
 
 
 # ----------------------------------------------------------------------------
+# packed batches of sequences of different lengths
+# ----------------------------------------------------------------------------
+
+def packed_inputs(name, lens, seed_shift=0, **sizes):
+    """A [1,H,T,d] packed batch (T = sum of lens), per-sequence S0 [N,H,dk,dv]
+    and the int32 offsets."""
+    T = int(sum(lens))
+    wl = WORKLOADS[name].with_sizes(B=1, H=2, T=T, seed=WORKLOADS[name].seed + seed_shift, **sizes)
+    x = make_inputs(wl)
+    N = len(lens)
+    S0 = None
+    if wl.s0:
+        S0 = (0.02 * torch.from_numpy(np.random.default_rng(7 + seed_shift).standard_normal(
+            (N, wl.H, wl.dk, wl.dv)))).float()
+    x["S0"] = S0
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    return x, cu
+
+
+def oracle_packed(x, cu):
+    """The oracle run per sequence on the slices of the packed batch."""
+    outs, states = [], []
+    for n in range(len(cu) - 1):
+        a, b = int(cu[n]), int(cu[n + 1])
+        xs = {key: (val[:, :, a:b].contiguous() if isinstance(val, torch.Tensor) and key not in ("gamma", "S0")
+                    else val) for key, val in x.items()}
+        xs["S0"] = None if x["S0"] is None else x["S0"][n:n + 1]
+        ro, rs = oracle_run(xs)
+        outs.append(ro)
+        states.append(rs[0])
+    return np.concatenate(outs, axis=2), np.stack(states)
+
+
+def gpu_packed(x, cu, chunk):
+    d = dev(x)
+    cut = torch.from_numpy(cu).to(DEV)
+    o, sT = gdr.gdr_chunk_fwd_varlen(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], cut,
+                                     gamma=d["gamma"], z=d["z"], S0=d["S0"], chunk=chunk)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), sT.cpu().numpy()
+
+
+@pytest.mark.parametrize("name,chunk", [("gdn2", 64), ("gdn2", 128), ("kda", 64), ("stress", 128),
+                                        ("tiny", 64)])
+def test_varlen_mixed_lengths(name, chunk):
+    lens = [0, 1, 63, 64, 65, 200, 0, 129, 17]
+    x, cu = packed_inputs(name, lens)
+    o, sT = gpu_packed(x, cu, chunk)
+    ro, rs = oracle_packed(x, cu)
+    check(f"varlen {name} C{chunk} o", o, ro, tol_for(x))
+    if x["S0"] is None:
+        rs = np.where(np.array(lens)[:, None, None, None] > 0, rs, 0.0)
+    check(f"varlen {name} C{chunk} S_T", sT, rs, tol_for(x))
+    empty = [n for n, L in enumerate(lens) if L == 0]
+    s0 = np.zeros_like(sT) if x["S0"] is None else x["S0"].numpy()
+    for n in empty:  # an empty sequence hands its S0 through unchanged
+        assert np.array_equal(sT[n], s0[n])
+
+
+def test_varlen_equal_lengths_match_the_batched_call():
+    """N equal lengths packed give bit-identical results to a [N,H,T,d] call."""
+    N, L = 3, 150
+    wl = WORKLOADS["gdn2"].with_sizes(B=N, H=2, T=L)
+    x = make_inputs(wl)
+    ob, sb = gpu_chunk(x, 64)
+    packed = {key: (val.permute(1, 0, 2, *range(3, val.dim())).reshape(1, wl.H, N * L, *val.shape[3:]).contiguous()
+                    if isinstance(val, torch.Tensor) and key not in ("gamma", "S0") else val)
+              for key, val in x.items()}
+    cu = (np.arange(N + 1) * L).astype(np.int32)
+    op, sp = gpu_packed(packed, cu, 64)
+    op = op.reshape(wl.H, N, L, wl.dv).transpose(1, 0, 2, 3)
+    assert np.array_equal(op, ob)
+    assert np.array_equal(sp, sb)
+
+
+# ----------------------------------------------------------------------------
 # the workloads at full size: GPU on everything, oracle on sampled streams
 # ----------------------------------------------------------------------------
 
