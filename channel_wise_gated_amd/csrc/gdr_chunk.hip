@@ -427,54 +427,28 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
   }
 
   // -------------------------------------------------- C1: leaf inverses
-  // (I + N)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8) for the strictly lower
-  // 16 x 16 diagonal block N (nilpotent: N^16 = 0), on 16x16x16 MFMA.  All
-  // factors are polynomials in N and commute, so every product takes a matrix
-  // read from LDS (row layout) as the A operand and the running accumulator
-  // (whose layout is the B layout) as the B operand.
+  // X = (I + N)^-1 for the strictly lower 16 x 16 diagonal block N, by fp32
+  // forward substitution (column-parallel, right-looking): once rows < s are
+  // done, row s of X is final; it is broadcast and every later row t takes
+  // off N[t][s] X[s][:].  Lane (column j = l16, group g) holds rows 4g..4g+3
+  // of X.  Unlike a Neumann-product form (whose powers of N grow
+  // combinatorially and cancel), this keeps the rounding error at the level
+  // of the system's conditioning.
   if (rowwave) {
     float *Tii = Lt + tidx(i, i) * TILE_SZ;
-    float *scr = reinterpret_cast<float *>(rst) + i * TILE_SZ;  // staging is free here
-    auto rowA = [&](const float *T, float av[4]) {
+    float x[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) av[e] = T[l16 * TILE_LD + 4 * g + e];
-    };
-    auto put = [&](float *T, const f32x4 &x) {
+    for (int r = 0; r < 4; ++r) x[r] = (4 * g + r) == l16 ? 1.f : 0.f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) T[(4 * g + r) * TILE_LD + l16] = x[r];
-    };
-    float an[4], bn[4], av[4], bv[4];
-    rowA(Tii, an);
+    for (int s_ = 0; s_ < 16; ++s_) {
+      // X[s][j] from the lane of group s/4 that holds column j
+      const float xs = __shfl(x[s_ % 4], l16 + 16 * (s_ / 4), kWave);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) bn[e] = Tii[(4 * g + e) * TILE_LD + l16];
-    f32x4 Nacc;                                  // N in accumulator layout
+      for (int r = 0; r < 4; ++r) x[r] -= Tii[(4 * g + r) * TILE_LD + s_] * xs;  // N[t][s] = 0 for t <= s
+    }
+    __builtin_amdgcn_wave_barrier();  // every lane has read N before X overwrites it
 #pragma unroll
-    for (int r = 0; r < 4; ++r) Nacc[r] = bn[r];
-    const f32x4 N2 = mfma16_split<NS>(an, bn, zero4());
-    put(scr, N2);
-    // P = (I - N)(I + N^2) = I - N + N^2 - N N^2
-#pragma unroll
-    for (int e = 0; e < 4; ++e) bv[e] = N2[e];
-    f32x4 P = mfma16_split<NS>(an, bv, zero4());
-#pragma unroll
-    for (int r = 0; r < 4; ++r) P[r] = ((4 * g + r) == l16 ? 1.f : 0.f) - Nacc[r] + N2[r] - P[r];
-    // N^4 = N^2 N^2 -> Tii (N itself is no longer needed)
-    rowA(scr, av);
-    const f32x4 N4 = mfma16_split<NS>(av, bv, zero4());
-    put(Tii, N4);
-    // Q = P (I + N^4) = P + N^4 P
-    rowA(Tii, av);
-    float bp[4] = {P[0], P[1], P[2], P[3]};
-    f32x4 Q = mfma16_split<NS>(av, bp, P);
-    // N^8 = N^4 N^4 -> scr
-    float b4[4] = {N4[0], N4[1], N4[2], N4[3]};
-    const f32x4 N8 = mfma16_split<NS>(av, b4, zero4());
-    put(scr, N8);
-    // X = Q (I + N^8) = Q + N^8 Q -> Tii
-    rowA(scr, av);
-    float bq[4] = {Q[0], Q[1], Q[2], Q[3]};
-    const f32x4 X = mfma16_split<NS>(av, bq, Q);
-    put(Tii, X);
+    for (int r = 0; r < 4; ++r) Tii[(4 * g + r) * TILE_LD + l16] = x[r];
   }
   __syncthreads();
 

@@ -438,6 +438,50 @@ def test_alpha_zero_and_extreme_decay_runs(chunk):
     check(f"alpha->0 C{chunk} S_T", sT, rs, TOL_BF16)
 
 
+def adversarial_inputs(wl, start, n, bval=1.99):
+    """One key repeated over n tokens with erase strength bval near 2 and no
+    decay there: the chunk's unit-lower-triangular system becomes badly
+    conditioned (the regime the Muir notes' section 2.4 stability discussion
+    probes adversarially)."""
+    x = make_inputs(wl)
+    k = x["k"].clone()
+    k[:, :, start:start + n] = k[:, :, start:start + 1]
+    b = x["b"].clone()
+    b[:, :, start:start + n] = bval
+    la = x["log_alpha"].clone()
+    la[:, :, start:start + n] = 0.0
+    x.update(k=k, b=b, log_alpha=la)
+    return x
+
+
+def chunk_system_cond(x, bi, hi, t0, C):
+    """cond_2(I + L) of the chunk starting at token t0 (fp64, from the
+    oracle's pre-pass and the decayed Gram of the chunk algebra)."""
+    kn = np.stack([oracle.prepass(x["q"][bi, hi, t], x["k"][bi, hi, t])[1] for t in range(t0, t0 + C)])
+    b = x["b"][bi, hi, t0:t0 + C].double().numpy()
+    lam = np.cumsum(x["log_alpha"][bi, hi, t0:t0 + C].double().numpy(), axis=0)
+    Tm = np.eye(C)
+    for t in range(C):
+        for s_ in range(t):
+            Tm[t, s_] += np.sum(b[t] * kn[t] * np.exp(lam[t] - lam[s_]) * kn[s_])
+    return float(np.linalg.cond(Tm))
+
+
+@pytest.mark.parametrize("chunk,dtype", [(64, "bf16"), (128, "bf16"), (64, "f32")])  # fp32 mode: C = 64
+def test_ill_conditioned_chunk_system(chunk, dtype):
+    wl = WORKLOADS["gdn2"].with_sizes(B=1, H=2, T=256, dtype=dtype)
+    x = adversarial_inputs(wl, chunk, chunk)
+    cond = chunk_system_cond(x, 0, 0, chunk, chunk)
+    assert cond > 1e3, cond
+    o, sT = gpu_chunk(x, chunk)
+    ro, rs = oracle_run(x)
+    print(f"cond(I+L) = {cond:.3e}", flush=True)
+    # the bf16-input bar for both modes: fp32 mode's 1e-5 is stated for
+    # well-conditioned systems (the Muir notes report ~1e-6 there)
+    check(f"ill-conditioned C{chunk} {dtype} o", o, ro, TOL_BF16)
+    check(f"ill-conditioned C{chunk} {dtype} S_T", sT, rs, TOL_BF16)
+
+
 def test_gate_modes_and_options():
     wl = WORKLOADS["gdn2"].with_sizes(B=1, H=2, T=128)
     x = make_inputs(wl)
