@@ -231,11 +231,12 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         float x = lv[ks][e];
-#pragma unroll
-        for (int dd = 1; dd < 16; dd <<= 1) {
-          const float y = __shfl_up(x, dd, 16);
-          if (l16 >= dd) x += y;
-        }
+        // inclusive scan within each row of 16 lanes: DPP row shifts by 1, 2,
+        // 4, 8 (lanes without a source add 0)
+        x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xF, 0xF, false));
+        x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xF, 0xF, false));
+        x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xF, 0xF, false));
+        x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xF, 0xF, false));
         lv[ks][e] = x;
       }
     float range = 0.f;
@@ -245,7 +246,8 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float P = lv[ks][e];
-        const float tot = __shfl(P, 15, 16);     // block total, same for all 16 tokens
+        // block total (lane 15 of the row), broadcast by a bit-mode swizzle: lane -> (lane & 16) | 15
+        const float tot = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(P), 0x1F0));
         range = fmaxf(range, -tot);
         if (l16 == 15) cum[(i + 1) * D + tp_chan(ks, g, e)] = tot;
         const float R = __expf(P), Cf = __expf(tot - P);
