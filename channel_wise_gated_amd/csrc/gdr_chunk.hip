@@ -53,6 +53,14 @@ constexpr float kMaxDiagRange = 40.0f;
 
 __device__ __forceinline__ int tidx(int i, int j) { return i * (i + 1) / 2 + j; }
 
+// Index of the pair (s-tile st, k-step kt >= st / 2) in st-major order: row
+// st' holds NKC - st'/2 pairs, and sum_{st' < st} st'/2 = m (m - 1 + st % 2)
+// with m = st / 2.
+template <int NKC>
+__device__ __forceinline__ constexpr int tf_pair(int st, int kt) {
+  return st * NKC - (st / 2) * (st / 2 - 1 + st % 2) + kt - st / 2;
+}
+
 template <int NS>
 __device__ __forceinline__ f32x4 mfma16_split(const float a[4], const float b[4], f32x4 c) {
   s16x4 ap[NS], bp[NS];
@@ -109,16 +117,21 @@ struct IntraLds {
   static constexpr int NTILES = NB * (NB + 1) / 2;
   static constexpr int FRAG = 64 * 8;      // bf16 per fragment plane
   static constexpr int STAGE = NKC * 2 * NS * FRAG;
+  // (s-tile st, token k-step kt) pairs with kt >= st / 2, in st-major order:
+  // the A-fragments of T^-T that are not identically zero
+  static constexpr int NPAIR = NB * NKC - (NB / 2) * (NB / 2 - 1);
+  static constexpr int TF_HALVES = NPAIR * NS * FRAG / 2;  // in floats
+  static constexpr int LT_SZ = NTILES * TILE_SZ > TF_HALVES ? NTILES * TILE_SZ : TF_HALVES;
+  static constexpr int STG_SZ = NTILES * D > STAGE / 2 ? NTILES * D : STAGE / 2;  // in floats
   // float offsets
   static constexpr int KCF = 0;                        // [NB][NKD][64][8]  kn * Cf
-  static constexpr int LT = KCF + C * D;               // [NTILES][TILE_SZ] L, then T^-1
-  static constexpr int CUM = LT + NTILES * TILE_SZ;    // [NB + 1][D]      block-start log decay
+  static constexpr int LT = KCF + C * D;               // [NTILES][TILE_SZ] L, then T^-1 fragments
+  static constexpr int CUM = LT + LT_SZ;               // [NB + 1][D]      block-start log decay
   static constexpr int NRM = CUM + (NB + 1) * D;       // [2][C]           inverse norms of q, k
-  static constexpr int STG = NRM + 2 * C;              // R and Z staging (bf16)
+  static constexpr int STG = NRM + 2 * C;              // pair decay table, then R staging (bf16)
   // In the last phase the KCF region is dead and holds v_hat = w * v (fp32,
   // same layout), loaded during the pre-pass.
-  static constexpr size_t bytes = sizeof(float) * (size_t)STG + sizeof(uint16_t) * 2 * STAGE +
-                                  sizeof(int) * NB;
+  static constexpr size_t bytes = sizeof(float) * ((size_t)STG + STG_SZ) + sizeof(int) * NB;
   static constexpr int WAVES = NB > D / 16 ? NB : D / 16;
 };
 
@@ -145,9 +158,9 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
   float *inq = sm + Lds::NRM;
   float *ink = inq + C;
   float *Lt = sm + Lds::LT;
+  uint16_t *tf = reinterpret_cast<uint16_t *>(Lt);  // T^-1 fragments, once C2 is done
   uint16_t *rst = reinterpret_cast<uint16_t *>(sm + Lds::STG);
-  uint16_t *zst = rst + Lds::STAGE;
-  int *dflag = reinterpret_cast<int *>(zst + Lds::STAGE);
+  int *dflag = reinterpret_cast<int *>(sm + Lds::STG + Lds::STG_SZ);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
@@ -285,7 +298,6 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
   // pair decay factors D_ij[c] = exp(cum_i - cum_{j+1}) for j <= i, one
   // exponential per (pair, channel), kept in the (still unused) staging area
   float *dtab = reinterpret_cast<float *>(rst);
-  static_assert(Lds::NTILES * D * 4 <= 2 * Lds::STAGE * 2, "pair decay table fits the staging area");
   {
     // thread <-> channel c; the pairs are dealt out over the P groups of D
     // threads (a group is whole waves, so the pair test is a scalar branch)
@@ -490,34 +502,32 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
         for (int r = 0; r < 4; ++r) Xc[ii][r] = -Xn[r];
       }
     }
-    __syncthreads();  // every L tile has been read before X overwrites it
+    __syncthreads();  // every L and X tile has been read before the fragments overwrite them
+    // Column block q of T^-1 leaves as A-fragments of T^-T, pre-split into NS
+    // bf16 planes: for pair (st = q, kt), lane (s = l16, g) holds tokens
+    // t = 16 (2 kt + e/4) + 4g + e%4 -- exactly rows 4g..4g+3 of the tiles
+    // X[2kt][q], X[2kt+1][q] that this lane holds.  The tile above the
+    // diagonal (2kt = q - 1 for odd q) is written as zeros.
     if (rowwave) {
 #pragma unroll
-      for (int ii = 1; ii < NB; ++ii) {
-        if (ii <= q) continue;
+      for (int ii = 0; ii < NB; ++ii) {
+        if (ii < q - q % 2) continue;
+        float x[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) Lt[tidx(ii, q) * TILE_SZ + (4 * g + r) * TILE_LD + l16] = Xc[ii][r];
+        for (int r = 0; r < 4; ++r) x[r] = ii >= q ? Xc[ii][r] : 0.f;
+        store4_planes<NS>(tf + (tf_pair<NKC>(q, ii / 2) * NS) * FRAG + lane * 8 + 4 * (ii % 2), FRAG, x);
       }
     }
     __syncthreads();
   }
 
-  // -------------------------------------------------- D: Z = T^-1 R and the chunk map
-  // T^-1 A-fragments for row block i (lane <-> t), tile-pair order over s.
-  bf16x8 tif[NKC][NS];
-  if (rowwave) {
-#pragma unroll
-    for (int ks = 0; ks < NKC; ++ks) {
-      float x[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int jb = 2 * ks + e / 4;
-        const int sc = 4 * g + (e % 4);
-        x[e] = (jb <= i) ? Lt[tidx(i, jb) * TILE_SZ + l16 * TILE_LD + sc] : 0.f;
-      }
-      split8<NS>(x, tif[ks]);
-    }
-  }
+  // -------------------------------------------------- D: the chunk map
+  // With W = K'^T T^-1 (D x C) and P = A T^-1 (C x C, lower triangular):
+  //   N = W V_hat,  M = Diag(e^Lambda_C) - W K_hat e^Lambda,
+  //   O_bar = P V_hat,  Q' = Qt e^Lambda - P K_hat e^Lambda,
+  // so the column loop multiplies the staged R = [V_hat | K_hat e^Lambda]
+  // directly, with no Z = T^-1 R round trip.  W and P are formed once per
+  // chunk from the T^-1 tiles in LDS.
   // K'^T fragments for channel tile m = wave (lane <-> c), tile-pair order
   // over s: K'[s][c] = kn_s,c Cf_s,c exp(cum_NB - cum_{blk(s)+1}).
   bf16x8 kpf[NKC][NS];
@@ -538,6 +548,37 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
         x[e] = kc * __expf(fminf(cend - cum[(blk + 1) * D + c], 0.f));
       }
       split8<NS>(x, kpf[ks]);
+    }
+  }
+
+  // W^T (rows s, cols c of this channel tile) = T^-T K' and P^T (rows s, cols
+  // t of block i) = T^-T A^T, one s-tile at a time; the accumulators of
+  // s-tiles 2ks, 2ks+1 form the A-fragment of W (lane <-> c) and of P
+  // (lane <-> t) for k-step ks in tile-pair order over s.  P^T is zero for
+  // s-tiles beyond block i, and A^T for token k-steps beyond it.
+  bf16x8 wf[NKC][NS], pf[NKC][NS];
+  {
+    f32x4 accW[2], accP[2];
+#pragma unroll
+    for (int st = 0; st < NB; ++st) {
+      accW[st % 2] = zero4();
+      accP[st % 2] = zero4();
+#pragma unroll
+      for (int kt = st / 2; kt < NKC; ++kt) {
+        bf16x8 ta[NS];
+        load_frag<NS>(tf + (tf_pair<NKC>(st, kt) * NS) * FRAG + lane * 8, FRAG, ta);
+        if (wave < NMT) accW[st % 2] = mfma32_split<NS>(ta, kpf[kt], accW[st % 2]);
+        if (rowwave && st <= i && 2 * kt <= i) accP[st % 2] = mfma32_split<NS>(ta, afr[kt], accP[st % 2]);
+      }
+      if (st % 2 == 1) {
+        const int ks = st / 2;
+        float x[8] = {accW[0][0], accW[0][1], accW[0][2], accW[0][3],
+                      accW[1][0], accW[1][1], accW[1][2], accW[1][3]};
+        split8<NS>(x, wf[ks]);
+        float y[8] = {accP[0][0], accP[0][1], accP[0][2], accP[0][3],
+                      accP[1][0], accP[1][1], accP[1][2], accP[1][3]};
+        split8<NS>(y, pf[ks]);
+      }
     }
   }
 
@@ -630,24 +671,7 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
       }
     }
     __syncthreads();
-    // D2: Z rows of block i (wave i), two column tiles
-    if (rowwave) {
-#pragma unroll
-      for (int ctl = 0; ctl < 2; ++ctl) {
-        f32x4 zacc = zero4();
-#pragma unroll
-        for (int ks = 0; ks < NKC; ++ks) {
-          if (2 * ks > i) continue;
-          bf16x8 rb[NS];
-          load_frag<NS>(rst + ((ks * 2 + ctl) * NS) * FRAG + lane * 8, FRAG, rb);
-          zacc = mfma32_split<NS>(tif[ks], rb, zacc);
-        }
-        float zv[4] = {zacc[0], zacc[1], zacc[2], zacc[3]};
-        store4_planes<NS>(zst + (((i / 2) * 2 + ctl) * NS) * FRAG + lane * 8 + 4 * (i % 2), FRAG, zv);
-      }
-    }
-    __syncthreads();
-    // D3: products with Z
+    // D3: products with R (the chunk map)
     if (vhalf) {
       if (wave < NMT) {  // N = K'^T U_bar
 #pragma unroll
@@ -656,8 +680,8 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
 #pragma unroll
           for (int ks = 0; ks < NKC; ++ks) {
             bf16x8 zb[NS];
-            load_frag<NS>(zst + ((ks * 2 + ctl) * NS) * FRAG + lane * 8, FRAG, zb);
-            acc = mfma32_split<NS>(kpf[ks], zb, acc);
+            load_frag<NS>(rst + ((ks * 2 + ctl) * NS) * FRAG + lane * 8, FRAG, zb);
+            acc = mfma32_split<NS>(wf[ks], zb, acc);
           }
           const int jt = 2 * cp + ctl;
           *reinterpret_cast<f32x4 *>(Nn + ((size_t)(wave * NMT + jt) * 64 + lane) * 4) = acc;
@@ -671,8 +695,8 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
           for (int ks = 0; ks < NKC; ++ks) {
             if (2 * ks > i) continue;
             bf16x8 zb[NS];
-            load_frag<NS>(zst + ((ks * 2 + ctl) * NS) * FRAG + lane * 8, FRAG, zb);
-            acc = mfma32_split<NS>(afr[ks], zb, acc);
+            load_frag<NS>(rst + ((ks * 2 + ctl) * NS) * FRAG + lane * 8, FRAG, zb);
+            acc = mfma32_split<NS>(pf[ks], zb, acc);
           }
           const int jt = 2 * cp + ctl;
           *reinterpret_cast<f32x4 *>(Ob + ((size_t)(i * NMT + jt) * 64 + lane) * 4) = acc;
@@ -689,8 +713,8 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
 #pragma unroll
           for (int ks = 0; ks < NKC; ++ks) {
             bf16x8 zb[NS];
-            load_frag<NS>(zst + ((ks * 2 + ctl) * NS) * FRAG + lane * 8, FRAG, zb);
-            acc = mfma32_split<NS>(zb, kpf[ks], acc);
+            load_frag<NS>(rst + ((ks * 2 + ctl) * NS) * FRAG + lane * 8, FRAG, zb);
+            acc = mfma32_split<NS>(zb, wf[ks], acc);
           }
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
@@ -711,8 +735,8 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
           for (int ks = 0; ks < NKC; ++ks) {
             if (2 * ks > i) continue;
             bf16x8 zb[NS];
-            load_frag<NS>(zst + ((ks * 2 + ctl) * NS) * FRAG + lane * 8, FRAG, zb);
-            acc = mfma32_split<NS>(zb, afr[ks], acc);
+            load_frag<NS>(rst + ((ks * 2 + ctl) * NS) * FRAG + lane * 8, FRAG, zb);
+            acc = mfma32_split<NS>(zb, pf[ks], acc);
           }
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
@@ -1018,11 +1042,14 @@ size_t chunk_workspace(ChunkArgs *a, void *ws, int B, int H, int T, int C, int D
   return total;
 }
 
+// Configurations with an instantiated kernel whose workgroup fits in LDS.
+// C = 128, d = 128 with fp32 inputs (three planes) is not instantiated; the
+// C = 64 kernel serves that input type at d = 128.
 bool chunk_intra_fits(int C, int D, int NS) {
   size_t b = 0;
 #define GDR_FIT(CC, DD, NN) if (C == CC && D == DD && NS == NN) b = IntraLds<CC, DD, NN>::bytes;
   GDR_FIT(64, 64, 2) GDR_FIT(64, 64, 3) GDR_FIT(64, 128, 2) GDR_FIT(64, 128, 3)
-  GDR_FIT(128, 64, 2) GDR_FIT(128, 64, 3) GDR_FIT(128, 128, 2) GDR_FIT(128, 128, 3)
+  GDR_FIT(128, 64, 2) GDR_FIT(128, 64, 3) GDR_FIT(128, 128, 2)
 #undef GDR_FIT
   return b > 0 && b <= 160 * 1024;
 }
