@@ -222,9 +222,7 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
       }
     const float bconst = tok_ok ? gate_const(a.b_mode) : 0.f;
 #pragma unroll
-    for (int ks = 0; ks < NKD; ++ks)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) lv[ks][e] = tok_ok ? gate_elem<false>(lg[ks][e / 4], e % 4, a.alpha_mode, 0.f) : 0.f;
+    for (int ks = 0; ks < NKD; ++ks) gate8<false>(lg[ks], a.alpha_mode, 0.f, tok_ok, lv[ks]);
     float sq = 0.f, sk = 0.f;
 #pragma unroll
     for (int ks = 0; ks < NKD; ++ks)
@@ -255,23 +253,39 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
     float range = 0.f;
 #pragma unroll
     for (int ks = 0; ks < NKD; ++ks) {
-      float QR[8], KR[8], KC[8];
+      // per-channel factors of this k-step: the erase gate, and the read-out
+      // multiplier 2 sigma(z) gamma (optional inputs tested once per k-step)
+      float bbv[8], fq[8];
+      gate8<BF>(bg[ks], a.b_mode, bconst, tok_ok, bbv);
+      if (a.z) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) fq[e] = a.scale * two_sigmoid(raw_elem<BF>(zg[ks][e / 4], e % 4));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) fq[e] = a.scale;
+      }
+      if (a.gamma) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) fq[e] *= raw_elem<false>(gm[ks][e / 4], e % 4);
+      }
+      float QR[8], KR[8], KC[8], tot[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float P = lv[ks][e];
         // block total (lane 15 of the row), broadcast by a bit-mode swizzle: lane -> (lane & 16) | 15
-        const float tot = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(P), 0x1F0));
-        range = fmaxf(range, -tot);
-        if (l16 == 15) cum[(i + 1) * D + tp_chan(ks, g, e)] = tot;
-        const float R = __expf(P), Cf = __expf(tot - P);
-        const float dy = a.z ? two_sigmoid(raw_elem<BF>(zg[ks][e / 4], e % 4)) : 1.f;
-        const float gg = a.gamma ? raw_elem<false>(gm[ks][e / 4], e % 4) : 1.f;
-        const float bb = tok_ok ? gate_elem<BF>(bg[ks][e / 4], e % 4, a.b_mode, bconst) : 0.f;
-        const float qt = a.scale * gg * dy * qv[ks][e] * nq;
+        tot[e] = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(P), 0x1F0));
+        range = fmaxf(range, -tot[e]);
+        const float R = __expf(P), Cf = __expf(tot[e] - P);
+        const float qt = fq[e] * qv[ks][e] * nq;
         const float kn = kv[ks][e] * nk;
         QR[e] = qt * R;
-        KR[e] = bb * kn * R;
+        KR[e] = bbv[e] * kn * R;
         KC[e] = kn * Cf;
+      }
+      if (l16 == 15) {  // channels tp_chan(ks, g, 0..3) and (ks, g, 4..7) are two runs of 4
+        float *cb = cum + (i + 1) * D + 32 * ks + 4 * g;
+        *reinterpret_cast<float4 *>(cb) = make_float4(tot[0], tot[1], tot[2], tot[3]);
+        *reinterpret_cast<float4 *>(cb + 16) = make_float4(tot[4], tot[5], tot[6], tot[7]);
       }
       split8<NS>(QR, QRp[ks]);
       split8<NS>(KR, KRp[ks]);
@@ -588,13 +602,13 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
   float *vhat = sm + Lds::KCF;
   if (rowwave) {
     const float wconst = gate_const(a.w_mode);
-    const float wmask = tok_ok ? 1.f : 0.f;  // padding tokens write nothing
 #pragma unroll
     for (int ks = 0; ks < NKD; ++ks) {
       float x[8];
+      gate8<BF>(wraw[ks], a.w_mode, wconst, true, x);
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        x[e] = raw_elem<BF>(vraw[ks][e / 4], e % 4) * (wmask * gate_elem<BF>(wraw[ks][e / 4], e % 4, a.w_mode, wconst));
+      for (int e = 0; e < 8; ++e)  // padding tokens write nothing
+        x[e] = tok_ok ? raw_elem<BF>(vraw[ks][e / 4], e % 4) * x[e] : 0.f;
       float4 *dst = reinterpret_cast<float4 *>(vhat + ((i * NKD + ks) * 64 + lane) * 8);
       dst[0] = make_float4(x[0], x[1], x[2], x[3]);
       dst[1] = make_float4(x[4], x[5], x[6], x[7]);

@@ -224,10 +224,25 @@ __device__ __forceinline__ Gate4<BF> gate_load(const void *p, int mode, size_t r
   g.tok = ld1<BF>(tb, tokm ? row : 0);
   return g;
 }
-// Value of element e of a gate_load result; `cval` is the value of a constant mode.
+
+// The 8 gate values of a lane's two 4-channel groups, zero where `ok` is
+// false.  The mode is tested once for all 8 (uniform branches around plain
+// moves), and `ok` is applied as a select afterwards, so no lane-divergent
+// region encloses the mode test.
 template <bool BF>
-__device__ __forceinline__ float gate_elem(const Gate4<BF> &g, int e, int mode, float cval) {
-  return mode == GDR_GATE_PER_CHANNEL ? raw_elem<BF>(g.grp, e) : (mode == GDR_GATE_PER_TOKEN ? g.tok : cval);
+__device__ __forceinline__ void gate8(const Gate4<BF> g[2], int mode, float cval, bool ok, float out[8]) {
+  if (mode == GDR_GATE_PER_CHANNEL) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = raw_elem<BF>(g[e / 4].grp, e % 4);
+  } else if (mode == GDR_GATE_PER_TOKEN) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = g[e / 4].tok;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = cval;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) out[e] = ok ? out[e] : 0.f;
 }
 
 // Value of the constant gate modes: ONES -> 1 (for log alpha: 0), ZEROS -> 0.
