@@ -139,8 +139,9 @@ struct IntraLds {
 __device__ __forceinline__ int tp_chan(int ks, int g, int e) { return 32 * ks + 16 * (e >> 2) + 4 * g + (e & 3); }
 
 // ============================================================================
-// Kernel 1: one workgroup per (stream, chunk); wave i owns token block i
-// (16 tokens) and channel tile i.  Per-token values live in the registers of
+// Kernel 1: one workgroup per (stream, chunk); each wave owns one token block
+// i (16 tokens; a permutation of the waves balances the SIMDs) and channel
+// tile m = wave.  Per-token values live in the registers of
 // the owning wave in "row-operand" layout: lane (t = l%16, g = l/16) holds
 // channels tp_chan(ks, g, e) of token t.
 // ============================================================================
@@ -186,7 +187,11 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
   // (log alpha = 0, no erase, no write); their outputs are never stored.
   const bool norm = a.normalize_qk != 0;
   const bool rowwave = wave < NB;
-  const int i = wave;                       // token block of this wave
+  // Token block of this wave.  The triangular phases give block i work in
+  // proportion to i + 1 (or to NB - i); waves w and w + 4 are dealt to one
+  // SIMD, so with 8 blocks wave w >= 4 takes block 11 - w and every SIMD holds
+  // a pair of blocks whose work sums to the same total.
+  const int i = (NB == 8 && wave >= 4) ? (wave ^ 3) : wave;
   const int t = 16 * i + l16;               // token of this lane (row-operand layout)
   const bool tok_ok = t < tvalid;
   const size_t rowt = row0 + min(t, tvalid - 1);  // row the lane's inputs are read from
@@ -481,14 +486,14 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
   __syncthreads();
 
   // -------------------------------------------------- C2: blocked forward substitution
-  // X[i][q] = -X[i][i] sum_{j=q}^{i-1} L[i][j] X[j][q].  Wave q owns column
-  // block q and keeps X[j][q] in accumulator layout -- the B-operand layout of
+  // X[i][q] = -X[i][i] sum_{j=q}^{i-1} L[i][j] X[j][q].  The owner wave of
+  // token block q owns column block q and keeps X[j][q] in accumulator layout -- the B-operand layout of
   // the 16x16x16 product -- so the waves need no barrier until the write-back.
   {
     f32x4 Xc[NB];
 #pragma unroll
     for (int j = 0; j < NB; ++j) Xc[j] = zero4();
-    const int q = wave;
+    const int q = i;  // column block of this wave
     if (rowwave) {
 #pragma unroll
       for (int jj = 0; jj < NB; ++jj)
