@@ -92,13 +92,15 @@ gdr_status chunk_call(const gdr_desc *desc, int nseq, const int *cu, const void 
   a.q = q; a.k = k; a.v = v; a.b = b; a.w = w; a.z = z;
   a.log_alpha = log_alpha; a.gamma = gamma; a.S0 = S0;
   a.o = o; a.S_T = S_T;
-  a.Qp = a.Mm = a.Sc = nullptr; a.Ob = a.Nn = nullptr;
+  a.Qp = a.Mm = a.Sc = nullptr; a.Ob = a.Nn = a.Sst = nullptr;
   gdr::chunk_workspace(&a, workspace, d.B, d.H, d.T, d.chunk, d.dk, ns, nseq);
   a.B = nseq > 0 ? nseq : d.B; a.H = d.H; a.T = d.T;
   a.alpha_mode = d.alpha_mode; a.b_mode = d.b_mode; a.w_mode = d.w_mode;
   a.normalize_qk = d.normalize_qk; a.scale = d.scale;
   a.cu = nseq > 0 ? cu : nullptr;
   a.nseq = nseq;
+  a.c0 = 0;  // the chunk range of each launch is set by launch_chunk
+  a.ncs = 0;
   if (nseq == 0) { a.ctab = nullptr; a.coff = nullptr; a.ctab_len = 0; }
   hipError_t e = gdr::launch_chunk(d, a, phases, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;

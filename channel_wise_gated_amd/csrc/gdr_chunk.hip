@@ -39,6 +39,7 @@
 //   Sc : [D/16 slices][D/32][NS][64][8] bf16            B-fragments of S_c
 // The contraction index of Q' and M (a state row) is in tile-pair order, the
 // order in which the scan kernel's accumulator tiles of S hold it.
+#include <algorithm>
 #include <mutex>
 #include <type_traits>
 
@@ -176,11 +177,11 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
     row0 = (size_t)h * a.T + e.z;
     tvalid = e.w;
   } else {
-    const int NC = (a.T + C - 1) / C;
-    const size_t bh = ch / NC;
+    const size_t bh = ch / a.ncs;
+    const int c = a.c0 + (int)(ch % a.ncs);
     h = (int)(bh % a.H);
-    row0 = bh * (size_t)a.T + (size_t)(ch % NC) * C;
-    tvalid = min(C, a.T - (int)(ch % NC) * C);
+    row0 = bh * (size_t)a.T + (size_t)c * C;
+    tvalid = min(C, a.T - c * C);
   }
   // The last chunk of a sequence may be short: its tokens from `tvalid` on
   // are padding, read at the last real row and turned into identity steps
@@ -816,7 +817,7 @@ __global__ void __launch_bounds__(64 * (D / 16)) chunk_chain_kernel(ChunkArgs a)
     slot0 = (size_t)a.coff[n] * a.H + bh % a.H;
     slot_step = a.H;
   } else {
-    NC = (a.T + C - 1) / C;  // the last chunk may be short
+    NC = a.ncs;  // chunks c0 .. c0 + ncs - 1 (the last chunk of a stream may be short)
     slot0 = bh * NC;
     slot_step = 1;
   }
@@ -952,9 +953,8 @@ __global__ void __launch_bounds__(64 * (C / 16)) chunk_out_kernel(ChunkArgs a) {
     rbase = (ch % a.H) * (size_t)a.T + e.z;
     tvalid = e.w;
   } else {
-    const int NC = (a.T + C - 1) / C;  // the last chunk may be short
-    const int c = (int)(ch % NC);
-    rbase = (ch / NC) * (size_t)a.T + (size_t)c * C;
+    const int c = a.c0 + (int)(ch % a.ncs);  // the last chunk of a stream may be short
+    rbase = (ch / a.ncs) * (size_t)a.T + (size_t)c * C;
     tvalid = min(C, a.T - c * C);
   }
 
@@ -1042,11 +1042,12 @@ size_t chunk_workspace(ChunkArgs *a, void *ws, int B, int H, int T, int C, int D
   const size_t per_head = (size_t)((T + C - 1) / C) + (nseq > 0 ? (size_t)nseq : 0);
   const size_t nch = nseq > 0 ? (size_t)H * per_head : (size_t)B * H * ((T + C - 1) / C);
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  const size_t sz[7] = {nch * NS * (size_t)C * D * 2, nch * NS * (size_t)D * D * 2, nch * (size_t)C * D * 4,
+  const size_t sz[8] = {nch * NS * (size_t)C * D * 2, nch * NS * (size_t)D * D * 2, nch * (size_t)C * D * 4,
                         nch * (size_t)D * D * 4, nch * NS * (size_t)D * D * 2,
-                        nseq > 0 ? per_head * sizeof(int4) : 0, nseq > 0 ? ((size_t)nseq + 1) * sizeof(int) : 0};
-  size_t off[7], total = 0;
-  for (int r = 0; r < 7; ++r) { off[r] = total; total += al(sz[r]); }
+                        nseq > 0 ? per_head * sizeof(int4) : 0, nseq > 0 ? ((size_t)nseq + 1) * sizeof(int) : 0,
+                        nseq > 0 || T == 0 ? 0 : (size_t)B * H * D * D * sizeof(float)};
+  size_t off[8], total = 0;
+  for (int r = 0; r < 8; ++r) { off[r] = total; total += al(sz[r]); }
   if (ws && a) {
     unsigned char *base = static_cast<unsigned char *>(ws);
     a->Qp = reinterpret_cast<uint16_t *>(base + off[0]);
@@ -1057,6 +1058,7 @@ size_t chunk_workspace(ChunkArgs *a, void *ws, int B, int H, int T, int C, int D
     a->ctab = nseq > 0 ? reinterpret_cast<int4 *>(base + off[5]) : nullptr;
     a->coff = nseq > 0 ? reinterpret_cast<int *>(base + off[6]) : nullptr;
     a->ctab_len = nseq > 0 ? (int)per_head : 0;
+    a->Sst = nseq > 0 ? nullptr : reinterpret_cast<float *>(base + off[7]);
   }
   return total;
 }
@@ -1073,6 +1075,48 @@ bool chunk_intra_fits(int C, int D, int NS) {
   return b > 0 && b <= 160 * 1024;
 }
 
+// Chunks per stream in one segment of a whole-call launch.  Each kernel of a
+// segment reads what the previous one wrote to the workspace (Q', M, O_bar, N,
+// S_c: `chunk_bytes` per chunk); a segment of at most kSegmentBytes keeps that
+// traffic inside MI355X's 256 MB last-level cache instead of HBM.  The count
+// is a multiple of 256 / gcd(streams, 256), so that every intra-chunk launch
+// fills whole rounds of the 256 CUs, and at least kMinSegment chunks (launch
+// cost); NC (one segment) when the whole workspace is small enough.
+constexpr size_t kSegmentBytes = (size_t)160 << 20;
+constexpr size_t kMinSegment = 8;
+static int segment_chunks(size_t nbh, int NC, size_t chunk_bytes) {
+  if (nbh == 0 || NC <= 0 || nbh * (size_t)NC * chunk_bytes <= kSegmentBytes) return NC > 0 ? NC : 1;
+  size_t g = 256, x = nbh % 256;
+  while (x) { const size_t t = g % x; g = x; x = t; }  // gcd(256, nbh)
+  const size_t q = 256 / g;
+  size_t seg = kSegmentBytes / (nbh * chunk_bytes);
+  seg -= seg % q;
+  if (seg < kMinSegment) return NC;  // too short to pay for the extra launches
+  return seg >= (size_t)NC ? NC : (int)seg;
+}
+
+// One pass of the kernels over `nch` chunk slots (phases: bit 0 intra-chunk,
+// bit 1 chain + output).
+template <int C, int D, int NS, bool BF, bool OB16>
+static hipError_t launch_chunk_pass(const ChunkArgs &a, size_t nch, int phases, hipStream_t st) {
+  using Lds = IntraLds<C, D, NS>;
+  const size_t nbh = (size_t)a.B * a.H;
+  if (nch > 0 && (phases & 1)) {
+    hipLaunchKernelGGL((chunk_intra_kernel<C, D, NS, BF>), dim3((unsigned)nch), dim3(64 * Lds::WAVES), Lds::bytes, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (!(phases & 2)) return hipSuccess;
+  constexpr int NSL = D / 16;
+  const size_t nblk = ((nbh + 7) / 8) * 8 * NSL;
+  hipLaunchKernelGGL((chunk_chain_kernel<C, D, NS>), dim3((unsigned)nblk), dim3(64 * (D / 16)), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || nch == 0) return e;
+  constexpr size_t out_lds = (size_t)NSL * (D / 32) * NS * 512 * 2;
+  hipLaunchKernelGGL((chunk_out_kernel<C, D, NS, OB16>), dim3((unsigned)nch), dim3(64 * (C / 16)), out_lds, st, a);
+  return hipGetLastError();
+}
+
 template <int C, int D, int NS, bool BF, bool OB16>
 static hipError_t launch_chunk_t(const ChunkArgs &a, int phases, hipStream_t st) {
   using Lds = IntraLds<C, D, NS>;
@@ -1085,34 +1129,42 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, int phases, hipStream_t st)
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lds::bytes);
     });
     if (attr_err != hipSuccess) return attr_err;
-    const size_t nbh = (size_t)a.B * a.H;
-    const size_t nch = a.ctab ? (size_t)a.H * a.ctab_len : nbh * (size_t)((a.T + C - 1) / C);
-    if (a.ctab && (phases & 1)) {
-      hipLaunchKernelGGL((chunk_table_kernel<C>), dim3(1), dim3(1024), 0, st, a);
-      hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
-    if (nch > 0 && (phases & 1)) {
-      hipLaunchKernelGGL((chunk_intra_kernel<C, D, NS, BF>), dim3((unsigned)nch), dim3(64 * Lds::WAVES), Lds::bytes, st, a);
-      hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
-    if (!(phases & 2)) return hipSuccess;
-    constexpr int NSL = D / 16;
-    const size_t nblk = ((nbh + 7) / 8) * 8 * NSL;
-    hipLaunchKernelGGL((chunk_chain_kernel<C, D, NS>), dim3((unsigned)nblk), dim3(64 * (D / 16)), 0, st, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || nch == 0) return e;
-    constexpr size_t out_lds = (size_t)NSL * (D / 32) * NS * 512 * 2;
     static std::once_flag once2;
     static hipError_t attr2 = hipSuccess;
     std::call_once(once2, [] {
+      constexpr size_t out_lds = (size_t)(D / 16) * (D / 32) * NS * 512 * 2;
       attr2 = hipFuncSetAttribute(reinterpret_cast<const void *>(&chunk_out_kernel<C, D, NS, OB16>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)out_lds);
     });
     if (attr2 != hipSuccess) return attr2;
-    hipLaunchKernelGGL((chunk_out_kernel<C, D, NS, OB16>), dim3((unsigned)nch), dim3(64 * (C / 16)), out_lds, st, a);
-    return hipGetLastError();
+    const size_t nbh = (size_t)a.B * a.H;
+    if (a.ctab) {  // packed batch: one pass over the device-built chunk list
+      if (phases & 1) {
+        hipLaunchKernelGGL((chunk_table_kernel<C>), dim3(1), dim3(1024), 0, st, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
+      return launch_chunk_pass<C, D, NS, BF, OB16>(a, (size_t)a.H * a.ctab_len, phases, st);
+    }
+    // Uniform batch: the whole call (phases 3) runs in segments of `seg`
+    // chunks per stream, the state carried between segments in Sst; the
+    // separate intra / scan calls exchange the whole workspace and are not
+    // segmented.
+    const int NC = (a.T + C - 1) / C;
+    constexpr size_t chunk_bytes = (size_t)NS * C * D * 2 + (size_t)NS * D * D * 2 * 2 + (size_t)C * D * 4 +
+                                   (size_t)D * D * 4;
+    const int seg = phases == 3 ? segment_chunks(nbh, NC, chunk_bytes) : NC;
+    const int nseg = NC > 0 ? (NC + seg - 1) / seg : 1;
+    for (int sgi = 0; sgi < nseg; ++sgi) {
+      ChunkArgs sa = a;
+      sa.c0 = sgi * seg;
+      sa.ncs = NC > 0 ? std::min(seg, NC - sa.c0) : 0;
+      if (sgi > 0) sa.S0 = a.Sst;
+      if (sgi + 1 < nseg) sa.S_T = a.Sst;
+      hipError_t e = launch_chunk_pass<C, D, NS, BF, OB16>(sa, nbh * (size_t)sa.ncs, phases, st);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
   } else {
     return hipErrorInvalidValue;
   }

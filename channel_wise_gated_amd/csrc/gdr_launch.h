@@ -29,6 +29,10 @@ struct ChunkArgs {
   int *coff;
   int4 *ctab;
   int nseq, ctab_len;
+  // Uniform batches: this launch covers chunks c0 .. c0 + ncs - 1 of every
+  // stream; stream bh's chunk c sits in slot bh * ncs + (c - c0).
+  int c0, ncs;
+  float *Sst;  // workspace: fp32 states handed from one segment to the next
 };
 
 hipError_t launch_decode(const gdr_desc &d, float *S, const void *q, const void *k, const void *v,
@@ -37,8 +41,9 @@ hipError_t launch_decode(const gdr_desc &d, float *S, const void *q, const void 
 // phases: bit 0 = intra-chunk kernel, bit 1 = scan kernel
 hipError_t launch_chunk(const gdr_desc &d, const ChunkArgs &a, int phases, hipStream_t st);
 // Workspace of the chunkwise forward: per chunk slot the maps Q', M, O_bar,
-// N and the chunk-start state; for a packed batch (nseq > 0) also the chunk
-// list and sequence offsets.  Slots: B*H*ceil(T/C), or H * (ceil(T/C) + nseq)
+// N and the chunk-start state; for a packed batch (nseq > 0) the chunk list
+// and sequence offsets, otherwise (T > 0) the fp32 states [B,H,D,D] handed
+// between segments.  Slots: B*H*ceil(T/C), or H * (ceil(T/C) + nseq)
 // for a packed batch (each sequence adds at most one short chunk).  Returns
 // the size in bytes; with `ws` set, also points the fields of *a into it.
 size_t chunk_workspace(ChunkArgs *a, void *ws, int B, int H, int T, int C, int D, int NS, int nseq);

@@ -108,9 +108,13 @@ gdr_status gdr_chunk_fwd_workspace_size(const gdr_desc *desc, size_t *bytes);
  * section 4 chunk form): per chunk of `desc->chunk` tokens, an intra-chunk
  * kernel builds the decayed key Gram matrix and read-out scores with
  * boundary pivots (every decay factor exp(Lambda_t - Lambda_s) is formed from
- * exponents <= 0), solves the unit-lower-triangular system T Z = [V_hat,
- * K_hat e^Lambda], and reduces the chunk to an affine map of the state; a
- * scan kernel then carries S in fp32 across chunks and writes o.
+ * exponents <= 0), inverts the unit-lower-triangular matrix T of the chunk
+ * system T Z = [V_hat, K_hat e^Lambda], and reduces the chunk to an affine map
+ * of the state; a scan kernel then carries S in fp32 across chunks and writes
+ * o.  A long uniform batch is processed in segments of chunks (the state
+ * handed from one segment to the next in fp32, so the result is the same), so
+ * that the workspace a segment's kernels pass to each other stays in the
+ * GPU's last-level cache.
  *
  *   q, k      [B,H,T,dk] in_dtype        v     [B,H,T,dv] in_dtype
  *   log_alpha per alpha_mode, fp32       b, w  per b_mode / w_mode, in_dtype
@@ -130,9 +134,10 @@ gdr_status gdr_chunk_fwd(const gdr_desc *desc, const void *q, const void *k,
 /*
  * The two phases of gdr_chunk_fwd as separate calls, for callers that overlap
  * the fully parallel phase of one batch with the serial scan of another on a
- * second stream, or that time the phases.  gdr_chunk_fwd(...) is exactly
- * gdr_chunk_fwd_intra(...) followed by gdr_chunk_fwd_scan(...) on the same
- * stream with the same descriptor and workspace.
+ * second stream, or that time the phases.  gdr_chunk_fwd(...) gives exactly
+ * the results of gdr_chunk_fwd_intra(...) followed by gdr_chunk_fwd_scan(...)
+ * on the same stream with the same descriptor and workspace (these two are
+ * not segmented: the workspace holds every chunk between them).
  *
  * gdr_chunk_fwd_intra: reads the token inputs (arguments as gdr_chunk_fwd)
  *   and writes, per chunk, the chunk's affine state map into the workspace:

@@ -73,13 +73,14 @@ def test_workspace_query_sizes():
     assert rc == gdr.GDR_OK
     nch = 2 * 4 * (256 // 64)
     # Q', M and the chunk-start states as two bf16 planes, O_bar and N in fp32
-    assert n == nch * (2 * 64 * 128 * 2 + 2 * 128 * 128 * 2 + 64 * 128 * 4 + 128 * 128 * 4 +
-                       2 * 128 * 128 * 2)
+    per_chunk = 2 * 64 * 128 * 2 + 2 * 128 * 128 * 2 + 64 * 128 * 4 + 128 * 128 * 4 + 2 * 128 * 128 * 2
+    handoff = 2 * 4 * 128 * 128 * 4  # fp32 states carried between segments
+    assert n == nch * per_chunk + handoff
     rc, n0 = ws(gdr.make_desc(**dict(GOOD, T=0)))
     assert rc == gdr.GDR_OK and n0 == 0
-    # a ragged length takes one (short) chunk more
+    # a ragged length takes one (short) chunk more per stream
     rc, nr = ws(gdr.make_desc(**dict(GOOD, T=257)))
-    assert rc == gdr.GDR_OK and nr == n * (256 // 64 + 1) // (256 // 64)
+    assert rc == gdr.GDR_OK and nr == (nch + 2 * 4) * per_chunk + handoff
     # fp32 mode needs three planes; C = D = 128 does not fit the LDS budget
     assert ws(gdr.make_desc(**dict(GOOD, chunk=128, in_dtype=gdr.GDR_F32)))[0] == gdr.GDR_ERR_UNSUPPORTED
     assert ws(gdr.make_desc(**dict(GOOD, chunk=128)))[0] == gdr.GDR_OK

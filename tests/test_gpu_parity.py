@@ -234,6 +234,27 @@ def test_varlen_equal_lengths_match_the_batched_call():
     assert np.array_equal(sp, sb)
 
 
+@pytest.mark.parametrize("chunk", [128, 64])
+def test_segmented_call_matches_the_phase_calls(chunk):
+    """The whole call runs a long uniform batch in segments of chunks (here
+    16 streams x 79 or 157 chunks: three or more segments), handing the fp32
+    state from one segment to the next; the separate intra / scan calls do not
+    segment.  Both must give bit-identical outputs and final states."""
+    wl = WORKLOADS["stress"].with_sizes(T=10000)
+    xd = make_inputs_device(wl, DEV, seed=21)
+    args = (xd["q"], xd["k"], xd["v"], xd["log_alpha"], xd["b"], xd["w"], xd["gamma"], xd["z"], xd["S0"])
+    whole = gdr.ChunkCall(*args, chunk=chunk)
+    phased = gdr.ChunkCall(*args, chunk=chunk)
+    o1, s1 = whole()
+    phased.intra()
+    o2, s2 = phased.scan()
+    torch.cuda.synchronize()
+    print(f"segmented C{chunk}: max |diff| o {float((o1 - o2).abs().max()):.3e} "
+          f"S_T {float((s1 - s2).abs().max()):.3e}", flush=True)
+    assert torch.equal(o1, o2)
+    assert torch.equal(s1, s2)
+
+
 # ----------------------------------------------------------------------------
 # the workloads at full size: GPU on everything, oracle on sampled streams
 # ----------------------------------------------------------------------------
