@@ -1,7 +1,8 @@
 #!/usr/bin/env python3
 """Benchmark of the channel-wise gated delta rule on one MI355X.
 
-A step is one chunkwise forward (both kernels) over the long-context stress
+A step is one chunkwise forward (gdr_chunk_fwd: intra-chunk, chain and
+output kernels, in segments of chunks) over the long-context stress
 workload: B1 H16 T32768 dk=dv=128, bf16 inputs, fp32 output and state, chunk
 128 (default) -- inputs resident in HBM before the timed region.  The decode
 step (256 sequences x 16 heads, fp32 128 x 128 states, 1024 consecutive
@@ -27,13 +28,15 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
 METRIC = "tokens/s + % bf16 MFMA peak, chunk fwd T=32K H=16 d=128; decode HBM GB/s"
-# HBM bytes per dispatch, from two rocprofv3 counter runs (FETCH_SIZE, then
-# WRITE_SIZE) over this benchmark, each scaled by what the same counter reads
-# for a plain 1 GiB device copy (fetch x2.0, write x1.0).  Valid only for the
-# kernel sources they were taken on (digest below); otherwise reported as null.
+# HBM bytes per dispatch of the intra-chunk kernel launched over all 4096
+# chunks (the phase call the roofline times), from two rocprofv3 counter runs
+# (FETCH_SIZE, then WRITE_SIZE) over this benchmark, each scaled by what the
+# same counter reads for a plain 1 GiB device copy (fetch x2.0, write x1.0).
+# Valid only for the kernel sources they were taken on (digest below);
+# otherwise reported as null.
 MEASURED_TRAFFIC = {
-    "sources": "716934a80597fe48",
-    "chunk_intra_kernel_C128": 2149373977,
+    "sources": "7c9315f842434d05",
+    "chunk_intra_kernel_C128": 2149500958,
 }
 
 
@@ -62,13 +65,21 @@ def sources_digest():
 
 
 def timed_chunk(call, steps, warmup):
+    """Wall time of `steps` whole calls (gdr_chunk_fwd, which runs a long
+    batch in segments of chunks), then per-kernel HIP-event times from the
+    same number of phase-call pairs (gdr_chunk_fwd_intra over every chunk in
+    one launch, gdr_chunk_fwd_scan), recorded on the stream the kernels run
+    on."""
     import torch
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     for e in ev:
         e[0].record()
         call.intra()
@@ -76,7 +87,6 @@ def timed_chunk(call, steps, warmup):
         call.scan()
         e[2].record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     intra = sorted(e[0].elapsed_time(e[1]) for e in ev)
     scan = sorted(e[1].elapsed_time(e[2]) for e in ev)
     return wall, intra, scan
@@ -165,7 +175,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--chunk", type=int, default=128, choices=(64, 128))
     ap.add_argument("--decode-steps", type=int, default=1024, help="0 skips the decode leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -239,7 +249,8 @@ def main():
                    "arith": "bf16 hi/lo-split MFMA, fp32 accumulate and state"},
         "tflops_algorithmic": round(tflops, 2), "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4),
         "hbm_gbs_algorithmic": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-        "kernels_ms": {"chunk_intra_kernel": round(intra_ms, 4), "chunk_scan_kernel": round(scan_ms, 4)},
+        "kernels_ms": {"chunk_intra_kernel": round(intra_ms, 4), "chunk_scan_kernel": round(scan_ms, 4),
+                       "from": "phase calls over all chunks in one launch each (median of steps)"},
         "roofline": roof,
     }
     if dsteps > 0:
