@@ -366,22 +366,26 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
 #pragma unroll 1
     for (int j = 0; j <= i; ++j) {
       f32x4 accL = zero4(), accA = zero4();
+      // every LDS operand of the pair is read first, so the reads overlap and
+      // each k-step waits only for its own
+      float4 kf[NKD][2], df[NKD][2];
 #pragma unroll
       for (int ks = 0; ks < NKD; ++ks) {
-        float x[8];
         const float4 *src = reinterpret_cast<const float4 *>(kcf + ((j * NKD + ks) * 64 + lane) * 8);
-        float4 f0 = src[0], f1 = src[1];
-        x[0] = f0.x; x[1] = f0.y; x[2] = f0.z; x[3] = f0.w;
-        x[4] = f1.x; x[5] = f1.y; x[6] = f1.z; x[7] = f1.w;
-        {
-          // D_ij = exp(cum_i - cum_{j+1}): <= 1 for j < i (clamped against
-          // rounding); for j = i it is exp(-total_i) >= 1, bounded by the
-          // block's decay range (wide ranges take the exact path below).
-          const float4 *dp = reinterpret_cast<const float4 *>(dtab + tidx(i, j) * D + 32 * ks + 4 * g);
-          const float4 d0 = dp[0], d1 = dp[4];  // channels tp_chan(ks, g, 0..3) and (.., 4..7)
-          x[0] *= d0.x; x[1] *= d0.y; x[2] *= d0.z; x[3] *= d0.w;
-          x[4] *= d1.x; x[5] *= d1.y; x[6] *= d1.z; x[7] *= d1.w;
-        }
+        kf[ks][0] = src[0];
+        kf[ks][1] = src[1];
+        // D_ij = exp(cum_i - cum_{j+1}): <= 1 for j < i (clamped against
+        // rounding); for j = i it is exp(-total_i) >= 1, bounded by the
+        // block's decay range (wide ranges take the exact path below).
+        const float4 *dp = reinterpret_cast<const float4 *>(dtab + tidx(i, j) * D + 32 * ks + 4 * g);
+        df[ks][0] = dp[0];  // channels tp_chan(ks, g, 0..3)
+        df[ks][1] = dp[4];  // and (ks, g, 4..7)
+      }
+#pragma unroll
+      for (int ks = 0; ks < NKD; ++ks) {
+        const float4 f0 = kf[ks][0], f1 = kf[ks][1], d0 = df[ks][0], d1 = df[ks][1];
+        float x[8] = {f0.x * d0.x, f0.y * d0.y, f0.z * d0.z, f0.w * d0.w,
+                      f1.x * d1.x, f1.y * d1.y, f1.z * d1.z, f1.w * d1.w};
         bf16x8 kc[NS];
         split8<NS>(x, kc);
         accL = mfma32_split<NS>(kc, KRp[ks], accL);
