@@ -146,8 +146,14 @@ __device__ __forceinline__ int tp_chan(int ks, int g, int e) { return 32 * ks + 
 // the owning wave in "row-operand" layout: lane (t = l%16, g = l/16) holds
 // channels tp_chan(ks, g, e) of token t.
 // ============================================================================
-template <int C, int D, int NS, bool BF>
+// SA (scalar decay): log alpha is one value per token (GDN, DeltaNet), given
+// per token or as ONES.  Every decay factor is then a scalar per token or per
+// block pair, which leaves the channel dimension of the Gram products free of
+// per-pair factors: kn * Cf is split into bf16 planes once, in the pre-pass,
+// and the pair factor D_ij scales the accumulated tile.
+template <int C, int D, int NS, bool BF, bool SA>
 __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
+  static_assert(!SA || NS == 2, "the scalar-decay kernel keeps kn * Cf as two bf16 planes in the kn * Cf region");
   using Lds = IntraLds<C, D, NS>;
   constexpr int NB = C / 16, NKC = C / 32, NKD = D / 32, NMT = D / 16;
   constexpr int TILE_LD = Lds::TILE_LD, TILE_SZ = Lds::TILE_SZ, FRAG = Lds::FRAG;
@@ -156,6 +162,7 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   float *sm = reinterpret_cast<float *>(smem);
   float *kcf = sm + Lds::KCF;
+  uint16_t *kcs = reinterpret_cast<uint16_t *>(kcf);  // scalar decay: kn * Cf as bf16 planes
   float *cum = sm + Lds::CUM;
   float *inq = sm + Lds::NRM;
   float *ink = inq + C;
@@ -224,11 +231,20 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
         gm[ks][hh] = *reinterpret_cast<const Raw4<false> *>(
             a.gamma ? reinterpret_cast<const char *>(a.gamma + (size_t)h * D + c0) : reinterpret_cast<const char *>(any));
         bg[ks][hh] = gate_load<BF>(a.b, a.b_mode, rowt, c0, D, any);
-        lg[ks][hh] = gate_load<false>(a.log_alpha, a.alpha_mode, rowt, c0, D, any);
+        if constexpr (!SA) lg[ks][hh] = gate_load<false>(a.log_alpha, a.alpha_mode, rowt, c0, D, any);
       }
+    // scalar decay: one log alpha per token (0 in ONES mode and for padding)
+    float la1 = 0.f;
+    if constexpr (SA) {
+      const bool tokm = a.alpha_mode == GDR_GATE_PER_TOKEN;
+      la1 = ld1<false>(tokm ? reinterpret_cast<const void *>(a.log_alpha) : any, tokm ? rowt : 0);
+      la1 = tokm && tok_ok ? la1 : 0.f;
+    }
     const float bconst = tok_ok ? gate_const(a.b_mode) : 0.f;
+    if constexpr (!SA) {
 #pragma unroll
-    for (int ks = 0; ks < NKD; ++ks) gate8<false>(lg[ks], a.alpha_mode, 0.f, tok_ok, lv[ks]);
+      for (int ks = 0; ks < NKD; ++ks) gate8<false>(lg[ks], a.alpha_mode, 0.f, tok_ok, lv[ks]);
+    }
     float sq = 0.f, sk = 0.f;
 #pragma unroll
     for (int ks = 0; ks < NKD; ++ks)
@@ -242,20 +258,30 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
     sk += __shfl_xor(sk, 16, kWave); sk += __shfl_xor(sk, 32, kWave);
     const float nq = norm ? inv_norm(sq) : 1.f, nk = norm ? inv_norm(sk) : 1.f;
     if (g == 0) { inq[t] = nq; ink[t] = nk; }
-    // inclusive prefix of log alpha over the 16 tokens of the block
+    // inclusive prefix of log alpha over the 16 tokens of the block: a scan
+    // within each row of 16 lanes by DPP row shifts of 1, 2, 4, 8 (lanes
+    // without a source add 0)
+    auto row_scan = [](float x) {
+      x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xF, 0xF, false));
+      x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xF, 0xF, false));
+      x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xF, 0xF, false));
+      x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xF, 0xF, false));
+      return x;
+    };
+    // block total (lane 15 of the row), broadcast by a bit-mode swizzle: lane -> (lane & 16) | 15
+    auto row_total = [](float x) { return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x1F0)); };
+    float P1 = 0.f, tot1 = 0.f, R1 = 1.f, Cf1 = 1.f;  // scalar decay: per token
+    if constexpr (SA) {
+      P1 = row_scan(la1);
+      tot1 = row_total(P1);
+      R1 = __expf(P1);
+      Cf1 = __expf(tot1 - P1);
+    } else {
 #pragma unroll
-    for (int ks = 0; ks < NKD; ++ks)
+      for (int ks = 0; ks < NKD; ++ks)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float x = lv[ks][e];
-        // inclusive scan within each row of 16 lanes: DPP row shifts by 1, 2,
-        // 4, 8 (lanes without a source add 0)
-        x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xF, 0xF, false));
-        x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xF, 0xF, false));
-        x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xF, 0xF, false));
-        x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xF, 0xF, false));
-        lv[ks][e] = x;
-      }
+        for (int e = 0; e < 8; ++e) lv[ks][e] = row_scan(lv[ks][e]);
+    }
     float range = 0.f;
 #pragma unroll
     for (int ks = 0; ks < NKD; ++ks) {
@@ -277,11 +303,18 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
       float QR[8], KR[8], KC[8], tot[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float P = lv[ks][e];
-        // block total (lane 15 of the row), broadcast by a bit-mode swizzle: lane -> (lane & 16) | 15
-        tot[e] = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(P), 0x1F0));
+        float R, Cf;
+        if constexpr (SA) {
+          tot[e] = tot1;
+          R = R1;
+          Cf = Cf1;
+        } else {
+          const float P = lv[ks][e];
+          tot[e] = row_total(P);
+          R = __expf(P);
+          Cf = __expf(tot[e] - P);
+        }
         range = fmaxf(range, -tot[e]);
-        const float R = __expf(P), Cf = __expf(tot[e] - P);
         const float qt = fq[e] * qv[ks][e] * nq;
         const float kn = kv[ks][e] * nk;
         QR[e] = qt * R;
@@ -295,9 +328,17 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
       }
       split8<NS>(QR, QRp[ks]);
       split8<NS>(KR, KRp[ks]);
-      float4 *dst = reinterpret_cast<float4 *>(kcf + ((i * NKD + ks) * 64 + lane) * 8);
-      dst[0] = make_float4(KC[0], KC[1], KC[2], KC[3]);
-      dst[1] = make_float4(KC[4], KC[5], KC[6], KC[7]);
+      if constexpr (SA) {  // A-fragment planes of kn * Cf for the Gram products
+        bf16x8 kp[NS];
+        split8<NS>(KC, kp);
+#pragma unroll
+        for (int p = 0; p < NS; ++p)
+          *reinterpret_cast<bf16x8 *>(kcs + (((i * NKD + ks) * NS + p) * 64 + lane) * 8) = kp[p];
+      } else {
+        float4 *dst = reinterpret_cast<float4 *>(kcf + ((i * NKD + ks) * 64 + lane) * 8);
+        dst[0] = make_float4(KC[0], KC[1], KC[2], KC[3]);
+        dst[1] = make_float4(KC[4], KC[5], KC[6], KC[7]);
+      }
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) range = fmaxf(range, __shfl_xor(range, off, kWave));
@@ -318,7 +359,7 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
   // pair decay factors D_ij[c] = exp(cum_i - cum_{j+1}) for j <= i, one
   // exponential per (pair, channel), kept in the (still unused) staging area
   float *dtab = reinterpret_cast<float *>(rst);
-  {
+  if constexpr (!SA) {  // scalar decay: D_ij is one exponential per pair, formed in B
     // thread <-> channel c; the pairs are dealt out over the P groups of D
     // threads (a group is whole waves, so the pair test is a scalar branch)
     constexpr int P = 64 * Lds::WAVES / D;
@@ -336,8 +377,8 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
         const float dd = cm[ii] - cm[jj + 1];
         dtab[pr * D + c] = __expf(jj < ii ? fminf(dd, 0.f) : dd);
       }
+    __syncthreads();
   }
-  __syncthreads();
 
   // per-lane factor vectors for this wave's channels (row-operand layout)
   auto cum8 = [&](int m, int ks, float out[8]) {
@@ -366,6 +407,22 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
 #pragma unroll 1
     for (int j = 0; j <= i; ++j) {
       f32x4 accL = zero4(), accA = zero4();
+      if constexpr (SA) {
+        // kn * Cf of block j as ready A-fragments; the scalar pair factor
+        // D_ij scales the accumulated tiles
+        bf16x8 kc[NKD][NS];
+#pragma unroll
+        for (int ks = 0; ks < NKD; ++ks) load_frag<NS>(kcs + ((j * NKD + ks) * NS * 64 + lane) * 8, FRAG, kc[ks]);
+#pragma unroll
+        for (int ks = 0; ks < NKD; ++ks) {
+          accL = mfma32_split<NS>(kc[ks], KRp[ks], accL);
+          accA = mfma32_split<NS>(kc[ks], QRp[ks], accA);
+        }
+        const float dd = cum[i * D] - cum[(j + 1) * D];
+        const float dij = __expf(j < i ? fminf(dd, 0.f) : dd);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) { accL[r] *= dij; accA[r] *= dij; }
+      } else {
       // every LDS operand of the pair is read first, so the reads overlap and
       // each k-step waits only for its own
       float4 kf[NKD][2], df[NKD][2];
@@ -390,6 +447,7 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
         split8<NS>(x, kc);
         accL = mfma32_split<NS>(kc, KRp[ks], accL);
         accA = mfma32_split<NS>(kc, QRp[ks], accA);
+      }
       }
       // lane (col t, group g) holds rows s = 16j + 4g + r
       if (j == i) {
@@ -568,7 +626,15 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int blk = 2 * ks + e / 4, ts = 4 * g + (e % 4);
-        const float kc = kcf[((blk * NKD + ksc) * 64 + ts + 16 * gc) * 8 + ec];
+        float kc;
+        if constexpr (SA) {
+          kc = 0.f;
+#pragma unroll
+          for (int p = NS - 1; p >= 0; --p)
+            kc += __builtin_bit_cast(float, (uint32_t)kcs[(((blk * NKD + ksc) * NS + p) * 64 + ts + 16 * gc) * 8 + ec] << 16);
+        } else {
+          kc = kcf[((blk * NKD + ksc) * 64 + ts + 16 * gc) * 8 + ec];
+        }
         x[e] = kc * __expf(fminf(cend - cum[(blk + 1) * D + c], 0.f));
       }
       split8<NS>(x, kpf[ks]);
@@ -1106,7 +1172,12 @@ static hipError_t launch_chunk_pass(const ChunkArgs &a, size_t nch, int phases, 
   using Lds = IntraLds<C, D, NS>;
   const size_t nbh = (size_t)a.B * a.H;
   if (nch > 0 && (phases & 1)) {
-    hipLaunchKernelGGL((chunk_intra_kernel<C, D, NS, BF>), dim3((unsigned)nch), dim3(64 * Lds::WAVES), Lds::bytes, st, a);
+    if (NS == 2 && a.alpha_mode != GDR_GATE_PER_CHANNEL)  // scalar decay
+      hipLaunchKernelGGL((chunk_intra_kernel<C, D, NS, BF, NS == 2>), dim3((unsigned)nch), dim3(64 * Lds::WAVES),
+                         Lds::bytes, st, a);
+    else
+      hipLaunchKernelGGL((chunk_intra_kernel<C, D, NS, BF, false>), dim3((unsigned)nch), dim3(64 * Lds::WAVES),
+                         Lds::bytes, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1129,8 +1200,11 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, int phases, hipStream_t st)
     static std::once_flag once;
     static hipError_t attr_err = hipSuccess;
     std::call_once(once, [] {
-      attr_err = hipFuncSetAttribute(reinterpret_cast<const void *>(&chunk_intra_kernel<C, D, NS, BF>),
+      attr_err = hipFuncSetAttribute(reinterpret_cast<const void *>(&chunk_intra_kernel<C, D, NS, BF, false>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lds::bytes);
+      if (attr_err == hipSuccess && NS == 2)
+        attr_err = hipFuncSetAttribute(reinterpret_cast<const void *>(&chunk_intra_kernel<C, D, NS, BF, NS == 2>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lds::bytes);
     });
     if (attr_err != hipSuccess) return attr_err;
     static std::once_flag once2;

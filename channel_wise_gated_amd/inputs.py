@@ -55,7 +55,7 @@ class Workload:
     chunk: int
     seed: int
     gates: str            # "gdn2" (per-channel b, w), "kda" (per-token beta)
-    alpha: str            # "softplus" or "bimodal"
+    alpha: str            # "softplus", "bimodal" (per channel) or "scalar" (per token)
     sparse_keys: bool
     gain: bool            # gamma and z present
     s0: bool              # nonzero initial state
@@ -76,6 +76,10 @@ WORKLOADS: Dict[str, Workload] = {
                        "bimodal", True, True, True),
     "decode": Workload("decode", 256, 16, 1, 128, 128, "bf16", 64, 4, "gdn2",
                        "softplus", False, True, True, steps=1024),
+    # scalar-gate case (Gated DeltaNet): one decay and one beta per token
+    # (b = w = beta), at the long-context shape
+    "gdn": Workload("gdn", 1, 16, 32768, 128, 128, "bf16", 128, 5, "kda", "scalar",
+                    False, False, True),
 }
 
 
@@ -105,6 +109,9 @@ def _log_alpha(wl: Workload, shape, step: int) -> np.ndarray:
     if wl.alpha == "softplus":
         x = _rng(wl.seed, "log_alpha", step).standard_normal(shape)
         return -0.1 * _softplus(x)
+    if wl.alpha == "scalar":  # one decay per token: [B,H,T]
+        x = _rng(wl.seed, "log_alpha", step).standard_normal(shape[:-1])
+        return -0.1 * _softplus(x)
     if wl.alpha == "bimodal":
         B, H, T, dk = shape
         # one fixed slow/fast split of the key channels per head
@@ -133,7 +140,7 @@ def make_inputs(wl: Workload, step: int = 0, device: Optional[str] = None) -> di
 
     Returns a dict of torch tensors (CPU unless ``device``):
       q, k: [B,H,T,dk]; v: [B,H,T,dv] (storage dtype);
-      log_alpha: [B,H,T,dk] fp32;
+      log_alpha: [B,H,T,dk] fp32 ([B,H,T] for a scalar decay);
       b: [B,H,T,dk] or [B,H,T] (kda: per-token beta); w: [B,H,T,dv] or [B,H,T];
       gamma: [H,dk] fp32 or None; z: [B,H,T,dk] or None; S0: [B,H,dk,dv] fp32
       or None; plus the gate modes "b_mode"/"w_mode" ("channel" or "token").
@@ -210,6 +217,8 @@ def make_inputs_device(wl: Workload, device: str, seed: int = 0, steps: int = 0)
     out["v"] = normal(*tok, dv).to(sdt)
     if wl.alpha == "softplus":
         out["log_alpha"] = -0.1 * torch.nn.functional.softplus(normal(*tok, dk))
+    elif wl.alpha == "scalar":
+        out["log_alpha"] = -0.1 * torch.nn.functional.softplus(normal(*tok))
     else:
         split = torch.rand((H, dk), generator=gen, **f32).argsort(dim=1) < dk // 2
         split = split.view((1,) * len(lead) + (1, H) + ((1,) if not steps else ()) + (dk,))

@@ -285,7 +285,8 @@ def test_chunk_full_size_ragged_sampled(name, chunk, T, pairs):
 FULL = [("kda", 64, [(0, 0), (1, 7), (2, 11), (3, 15)]),
         ("gdn2", 64, [(0, 3), (1, 12)]),
         ("stress", 64, [(0, 0), (0, 9)]),
-        ("stress", 128, [(0, 5), (0, 14)])]
+        ("stress", 128, [(0, 5), (0, 14)]),
+        ("gdn", 128, [(0, 1), (0, 10)])]
 
 
 @pytest.mark.timeout(600)
@@ -457,6 +458,61 @@ def test_alpha_zero_and_extreme_decay_runs(chunk):
     ro, rs = oracle_run(x)
     check(f"alpha->0 C{chunk} o", o, ro, TOL_BF16)
     check(f"alpha->0 C{chunk} S_T", sT, rs, TOL_BF16)
+
+
+# ----------------------------------------------------------------------------
+# scalar decay (one log alpha per token: Gated DeltaNet, DeltaNet) -- bf16
+# inputs take the scalar-decay intra-chunk kernel
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("chunk,d,T,gates,gain", [
+    (64, 128, 300, "kda", False), (128, 128, 300, "kda", False), (64, 64, 257, "gdn2", True),
+    (128, 64, 129, "gdn2", True), (128, 128, 200, "gdn2", True), (64, 128, 64, "kda", True)])
+def test_scalar_decay(chunk, d, T, gates, gain):
+    """Per-token decay with per-token beta (b = w) or per-channel b, w, with
+    and without the read-out gain, ragged lengths included."""
+    wl = WORKLOADS["gdn"].with_sizes(B=2, H=2, T=T, dk=d, dv=d, gates=gates, gain=gain)
+    x = make_inputs(wl)
+    assert x["log_alpha"].dim() == 3
+    o, sT = gpu_chunk(x, chunk)
+    ro, rs = oracle_run(x)
+    check(f"scalar decay C{chunk} d{d} T{T} {gates} o", o, ro, TOL_BF16)
+    check(f"scalar decay C{chunk} d{d} T{T} {gates} S_T", sT, rs, TOL_BF16)
+
+
+@pytest.mark.parametrize("chunk", [64, 128])
+def test_scalar_decay_matches_the_per_channel_kernel(chunk):
+    """The same decay given per token (scalar-decay kernel) and replicated over
+    the channels (general kernel): both against the oracle, and against each
+    other far inside the tolerance."""
+    wl = WORKLOADS["gdn"].with_sizes(B=1, H=3, T=320)
+    x = make_inputs(wl)
+    o1, s1 = gpu_chunk(x, chunk)
+    y = dict(x)
+    y["log_alpha"] = x["log_alpha"][..., None].expand(*x["log_alpha"].shape, wl.dk).contiguous()
+    o2, s2 = gpu_chunk(y, chunk)
+    ro, rs = oracle_run(x)
+    check(f"scalar kernel C{chunk} o", o1, ro, TOL_BF16)
+    check(f"per-channel kernel C{chunk} o", o2, ro, TOL_BF16)
+    check(f"scalar vs per-channel C{chunk} o", o1, o2, 1e-4)
+    check(f"scalar vs per-channel C{chunk} S_T", s1, s2, 1e-4)
+
+
+@pytest.mark.parametrize("chunk", [64, 128])
+def test_scalar_decay_extreme_runs(chunk):
+    """Per-token log alpha = -30 at single tokens and over runs wider than a
+    block (the exact-exponential path of diagonal blocks), and alpha = 1."""
+    wl = WORKLOADS["gdn"].with_sizes(B=1, H=2, T=256)
+    x = make_inputs(wl)
+    la = x["log_alpha"].clone()
+    la[:, 0, 37] = -30.0
+    la[:, 1, 100:140] = -30.0
+    la[:, 0, 150:256] = 0.0
+    x["log_alpha"] = la
+    o, sT = gpu_chunk(x, chunk)
+    ro, rs = oracle_run(x)
+    check(f"scalar alpha->0 C{chunk} o", o, ro, TOL_BF16)
+    check(f"scalar alpha->0 C{chunk} S_T", sT, rs, TOL_BF16)
 
 
 def adversarial_inputs(wl, start, n, bval=1.99):
