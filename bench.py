@@ -6,7 +6,9 @@ output kernels, in segments of chunks) over the long-context stress
 workload: B1 H16 T32768 dk=dv=128, bf16 inputs, fp32 output and state, chunk
 128 (default) -- inputs resident in HBM before the timed region.  The decode
 step (256 sequences x 16 heads, fp32 128 x 128 states, 1024 consecutive
-steps) is timed in the same run and reported beside it.
+steps) and the same long-context shape with scalar gates (one decay and one
+beta per token, Gated DeltaNet) are timed in the same run and reported
+beside it.
 
 Prints one JSON line.  Per-kernel durations come from HIP events recorded on
 the stream the kernels run on; the roofline object describes the kernel with
@@ -178,6 +180,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--chunk", type=int, default=128, choices=(64, 128))
     ap.add_argument("--decode-steps", type=int, default=1024, help="0 skips the decode leg")
+    ap.add_argument("--gdn-steps", type=int, default=20,
+                    help="whole calls of the scalar-gate (Gated DeltaNet) leg; 0 skips it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="also run a plain MIB-MiB copy (reference for HBM byte counters)")
@@ -230,6 +234,23 @@ def main():
             "algorithmic_bytes_per_launch": kbytes, "avg_ms": round(sum(intra if kname.endswith(
                 "intra_kernel") else scan) / args.steps, 4)}
 
+    # scalar-gate leg: the same shape with one decay and one beta per token
+    gsteps = args.gdn_steps
+    if gsteps > 0:
+        gwl = WORKLOADS["gdn"]
+        xg = make_inputs_device(gwl, "cuda")
+        callg = gdr.ChunkCall(xg["q"], xg["k"], xg["v"], xg["log_alpha"], xg["b"], xg["w"], xg["gamma"],
+                              xg["z"], xg["S0"], chunk=C)
+        for _ in range(args.warmup):
+            callg()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(gsteps):
+            callg()
+        torch.cuda.synchronize()
+        g_ms = 1e3 * (time.perf_counter() - t0) / gsteps
+        del callg, xg
+
     # decode
     dwl = WORKLOADS["decode"]
     dsteps = args.decode_steps
@@ -253,6 +274,11 @@ def main():
                        "from": "phase calls over all chunks in one launch each (median of steps)"},
         "roofline": roof,
     }
+    if gsteps > 0:
+        line["gdn"] = {"workload": f"gdn B{gwl.B} H{gwl.H} T{gwl.T} dk{gwl.dk} dv{gwl.dv} chunk{C}, "
+                                   "one decay and one beta per token (b = w)",
+                       "steps": gsteps, "ms_per_step": round(g_ms, 4),
+                       "tokens_s": round(gwl.B * gwl.T / (g_ms / 1e3), 1)}
     if dsteps > 0:
         line["decode"] = {"workload": f"decode {dwl.B} seq x H{dwl.H}, fp32 state {dwl.dk}x{dwl.dv}, "
                                       f"{dsteps} steps", "us_per_step": round(d_us, 2),
