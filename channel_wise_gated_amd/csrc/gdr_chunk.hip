@@ -62,22 +62,37 @@ __device__ __forceinline__ constexpr int tf_pair(int st, int kt) {
   return st * NKC - (st / 2) * (st / 2 - 1 + st % 2) + kt - st / 2;
 }
 
+// Four fp32 values as NS bf16 planes (a 16x16x16 operand fragment).
 template <int NS>
-__device__ __forceinline__ f32x4 mfma16_split(const float a[4], const float b[4], f32x4 c) {
-  s16x4 ap[NS], bp[NS];
+struct Split4 {
+  s16x4 p[NS];
+};
+template <int NS>
+__device__ __forceinline__ Split4<NS> split4(const float x[4]) {
+  Split4<NS> r;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    uint16_t ha[NS], hb[NS];
-    split<NS>(a[e], ha);
-    split<NS>(b[e], hb);
+    uint16_t h[NS];
+    split<NS>(x[e], h);
 #pragma unroll
-    for (int p = 0; p < NS; ++p) { ap[p][e] = (short)ha[p]; bp[p][e] = (short)hb[p]; }
+    for (int p = 0; p < NS; ++p) r.p[p][e] = (short)h[p];
   }
+  return r;
+}
+// Product of pre-split operands, smallest plane products first.
+template <int NS>
+__device__ __forceinline__ f32x4 mfma16_pre(const Split4<NS> &a, const Split4<NS> &b, f32x4 c) {
 #pragma unroll
   for (int s = NS - 1; s >= 0; --s)
 #pragma unroll
     for (int pa = 0; pa <= s; ++pa)
-      c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ap[pa], bp[s - pa], c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.p[pa], b.p[s - pa], c, 0, 0, 0);
+  return c;
+}
+
+template <int NS>
+__device__ __forceinline__ f32x4 mfma16_split(const float a[4], const float b[4], f32x4 c) {
+  return mfma16_pre<NS>(split4<NS>(a), split4<NS>(b), c);
   return c;
 }
 
@@ -158,6 +173,9 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
   constexpr int NB = C / 16, NKC = C / 32, NKD = D / 32, NMT = D / 16;
   constexpr int TILE_LD = Lds::TILE_LD, TILE_SZ = Lds::TILE_SZ, FRAG = Lds::FRAG;
   static_assert(NB <= 8 && NMT <= 8, "one wave per token block and per channel tile");
+  // off-diagonal L tiles are stored as NS bf16 planes of A-fragments when those
+  // fit the fp32 tile slot (NS = 2), else in fp32
+  constexpr bool LPRE = NS * 256 <= 2 * TILE_SZ;
 
   extern __shared__ __align__(16) unsigned char smem[];
   float *sm = reinterpret_cast<float *>(smem);
@@ -488,8 +506,16 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
           if (s2 > t) accA[r] = 0.f;
         }
       }
-      *reinterpret_cast<float4 *>(Lt + tidx(i, j) * TILE_SZ + l16 * TILE_LD + 4 * g) =
-          make_float4(accL[0], accL[1], accL[2], accL[3]);
+      if (j == i || !LPRE) {  // diagonal tile: fp32, row-major [t][s], for the leaf inverse
+        *reinterpret_cast<float4 *>(Lt + tidx(i, j) * TILE_SZ + l16 * TILE_LD + 4 * g) =
+            make_float4(accL[0], accL[1], accL[2], accL[3]);
+      } else {  // off-diagonal: this lane's A-fragment (row t, k = 4g..4g+3) as NS bf16 planes
+        const float lv4[4] = {accL[0], accL[1], accL[2], accL[3]};
+        const Split4<NS> ls = split4<NS>(lv4);
+        uint16_t *lt = reinterpret_cast<uint16_t *>(Lt + tidx(i, j) * TILE_SZ);
+#pragma unroll
+        for (int p = 0; p < NS; ++p) *reinterpret_cast<s16x4 *>(lt + p * 256 + lane * 4) = ls.p[p];
+      }
       uint16_t hp[4][NS];
 #pragma unroll
       for (int r = 0; r < 4; ++r) split<NS>(accA[r], hp[r]);
@@ -554,6 +580,7 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
   // the 16x16x16 product -- so the waves need no barrier until the write-back.
   {
     f32x4 Xc[NB];
+    Split4<NS> Xs[NB];  // the planes of each finished X[j][q]
 #pragma unroll
     for (int j = 0; j < NB; ++j) Xc[j] = zero4();
     const int q = i;  // column block of this wave
@@ -563,6 +590,8 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
         if (jj == q) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) Xc[jj][r] = Lt[tidx(jj, jj) * TILE_SZ + (4 * g + r) * TILE_LD + l16];
+          const float xv[4] = {Xc[jj][0], Xc[jj][1], Xc[jj][2], Xc[jj][3]};
+          Xs[jj] = split4<NS>(xv);
         }
 #pragma unroll
       for (int ii = 1; ii < NB; ++ii) {
@@ -571,10 +600,18 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
 #pragma unroll
         for (int j = 0; j < NB - 1; ++j) {
           if (j < q || j >= ii) continue;
-          float av[4], bv[4] = {Xc[j][0], Xc[j][1], Xc[j][2], Xc[j][3]};
+          Split4<NS> la;  // L[ii][j], pre-split when the planes fit the tile slot
+          if constexpr (LPRE) {
+            const uint16_t *lt = reinterpret_cast<const uint16_t *>(Lt + tidx(ii, j) * TILE_SZ);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) av[e] = Lt[tidx(ii, j) * TILE_SZ + l16 * TILE_LD + 4 * g + e];
-          W = mfma16_split<NS>(av, bv, W);
+            for (int p = 0; p < NS; ++p) la.p[p] = *reinterpret_cast<const s16x4 *>(lt + p * 256 + lane * 4);
+          } else {
+            float av[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) av[e] = Lt[tidx(ii, j) * TILE_SZ + l16 * TILE_LD + 4 * g + e];
+            la = split4<NS>(av);
+          }
+          W = mfma16_pre<NS>(la, Xs[j], W);
         }
         float av[4], bw[4] = {W[0], W[1], W[2], W[3]};
 #pragma unroll
@@ -582,6 +619,8 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
         const f32x4 Xn = mfma16_split<NS>(av, bw, zero4());
 #pragma unroll
         for (int r = 0; r < 4; ++r) Xc[ii][r] = -Xn[r];
+        const float xv[4] = {Xc[ii][0], Xc[ii][1], Xc[ii][2], Xc[ii][3]};
+        Xs[ii] = split4<NS>(xv);
       }
     }
     __syncthreads();  // every L and X tile has been read before the fragments overwrite them
@@ -710,6 +749,14 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
 #pragma unroll
         for (int p = 0; p < NS; ++p) { QRs[p] = QRp[kk][p]; KRs[p] = KRp[kk][p]; }
       }
+    // e^{cum_i} of this lane's channels in the K_hat / Q' half (both D1 and
+    // the Q' products use it)
+    float eci[8];
+    if (rowwave && !vhalf) {
+      cum8(i, kq, eci);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) eci[e] = __expf(eci[e]);
+    }
     // D1: the owner wave of each token block writes its 16 rows of
     // R[:, 32cp .. 32cp+32) into the B-fragment staging (lane <-> column,
     // tile-pair order over tokens).
@@ -721,15 +768,12 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
         val[0] = f0.x; val[1] = f0.y; val[2] = f0.z; val[3] = f0.w;
         val[4] = f1.x; val[5] = f1.y; val[6] = f1.z; val[7] = f1.w;
       } else {
-        const int ks = cp - D / 32;
-        float ci[8];
-        cum8(i, ks, ci);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           float kr = 0.f;
 #pragma unroll
           for (int p = 0; p < NS; ++p) kr += (float)KRs[p][e];
-          val[e] = kr * __expf(ci[e]);  // k_hat e^Lambda = (k_hat R) e^{cum_i}
+          val[e] = kr * eci[e];  // k_hat e^Lambda = (k_hat R) e^{cum_i}
         }
       }
       // Value e sits in column 16*(e/4) + 4g + e%4 and token t = 16i + l16.
@@ -815,8 +859,6 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
         store8_planes<NS>(Mm + ((size_t)(wave * NKD + ksy) * 64 + lane) * 8, (size_t)D * D, mv);
       }
       if (rowwave) {  // Q' = Qt e^Lambda - A Y, as (A Y)^T = Y^T A^T
-        float ci[8];
-        cum8(i, ksy, ci);
         float qv8[8];
 #pragma unroll
         for (int ctl = 0; ctl < 2; ++ctl) {
@@ -834,7 +876,7 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
             float qr = 0.f;
 #pragma unroll
             for (int p = 0; p < NS; ++p) qr += (float)QRs[p][e];
-            qv8[e] = qr * __expf(ci[e]) - acc[r];
+            qv8[e] = qr * eci[e] - acc[r];
           }
         }
         store8_planes<NS>(Qp + ((size_t)(i * NKD + ksy) * 64 + lane) * 8, (size_t)C * D, qv8);
