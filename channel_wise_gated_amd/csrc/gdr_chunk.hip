@@ -736,19 +736,11 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
   float *Ob = a.Ob + ch * (size_t)C * D;
   float *Nn = a.Nn + ch * (size_t)D * D;
 
-#pragma unroll 1
-  for (int cp = 0; cp < 2 * D / 32; ++cp) {
+  // one column pair; QRs, KRs = QRp[kq], KRp[kq] (the K half is unrolled, so
+  // they are indexed at compile time)
+  auto pair_iter = [&](const int cp, const bf16x8 (&QRs)[NS], const bf16x8 (&KRs)[NS]) {
     const bool vhalf = cp < D / 32;
     const int kq = vhalf ? 0 : cp - D / 32;  // channel k-step of the K_hat / Q' half
-    bf16x8 QRs[NS], KRs[NS];  // QRp[kq], KRp[kq], selected without dynamic indexing
-#pragma unroll
-    for (int p = 0; p < NS; ++p) { QRs[p] = QRp[0][p]; KRs[p] = KRp[0][p]; }
-#pragma unroll
-    for (int kk = 1; kk < NKD; ++kk)
-      if (kq == kk) {
-#pragma unroll
-        for (int p = 0; p < NS; ++p) { QRs[p] = QRp[kk][p]; KRs[p] = KRp[kk][p]; }
-      }
     // e^{cum_i} of this lane's channels in the K_hat / Q' half (both D1 and
     // the Q' products use it)
     float eci[8];
@@ -883,6 +875,27 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
       }
     }
     __syncthreads();
+  };
+  if constexpr (NS == 2) {
+#pragma unroll 1
+    for (int cp = 0; cp < D / 32; ++cp) pair_iter(cp, QRp[0], KRp[0]);
+#pragma unroll
+    for (int kk = 0; kk < NKD; ++kk) pair_iter(D / 32 + kk, QRp[kk], KRp[kk]);
+  } else {  // fp32 mode: unrolling the K half would spill; select at run time
+#pragma unroll 1
+    for (int cp = 0; cp < 2 * D / 32; ++cp) {
+      const int kq = cp < D / 32 ? 0 : cp - D / 32;
+      bf16x8 QRs[NS], KRs[NS];  // QRp[kq], KRp[kq], selected without dynamic indexing
+#pragma unroll
+      for (int p = 0; p < NS; ++p) { QRs[p] = QRp[0][p]; KRs[p] = KRp[0][p]; }
+#pragma unroll
+      for (int kk = 1; kk < NKD; ++kk)
+        if (kq == kk) {
+#pragma unroll
+          for (int p = 0; p < NS; ++p) { QRs[p] = QRp[kk][p]; KRs[p] = KRp[kk][p]; }
+        }
+      pair_iter(cp, QRs, KRs);
+    }
   }
 }
 
