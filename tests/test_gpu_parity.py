@@ -202,7 +202,7 @@ def gpu_packed(x, cu, chunk):
 
 
 @pytest.mark.parametrize("name,chunk", [("gdn2", 64), ("gdn2", 128), ("kda", 64), ("stress", 128),
-                                        ("tiny", 64)])
+                                        ("tiny", 64), ("gdn", 128)])
 def test_varlen_mixed_lengths(name, chunk):
     lens = [0, 1, 63, 64, 65, 200, 0, 129, 17]
     x, cu = packed_inputs(name, lens)
@@ -359,6 +359,27 @@ def test_decode_small_many_steps(d, dtype, gates):
     tol = TOL_BF16 if dtype == "bf16" else TOL_F32
     check(f"decode d{d} {dtype} {gates} o", np.stack(outs), np.stack(refs), tol)
     check(f"decode d{d} {dtype} {gates} S", S.cpu().numpy(), Sref, tol)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_scalar_decay(d):
+    """Decode with one decay and one beta per token (Gated DeltaNet)."""
+    wl = WORKLOADS["decode"].with_sizes(B=3, H=2, dk=d, dv=d, alpha="scalar", gates="kda")
+    x0 = decode_inputs(wl, 0)
+    assert x0["log_alpha"].dim() == 2
+    S = x0["S0"].clone().to(DEV)
+    Sref = x0["S0"].double().numpy()
+    outs, refs = [], []
+    for step in range(12):
+        x = decode_inputs(wl, step)
+        o = gpu_decode(S, x)
+        ro, Sref = oracle.decode_step(Sref, x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"],
+                                      gamma=x["gamma"], z=x["z"])
+        outs.append(o.float().cpu().numpy())
+        refs.append(ro)
+    torch.cuda.synchronize()
+    check(f"decode scalar decay d{d} o", np.stack(outs), np.stack(refs), TOL_BF16)
+    check(f"decode scalar decay d{d} S", S.cpu().numpy(), Sref, TOL_BF16)
 
 
 @pytest.mark.timeout(600)
