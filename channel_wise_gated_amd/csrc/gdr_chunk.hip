@@ -1247,29 +1247,34 @@ static hipError_t launch_chunk_pass(const ChunkArgs &a, size_t nch, int phases, 
   return hipGetLastError();
 }
 
+constexpr int kMaxDevices = 64;
+
 template <int C, int D, int NS, bool BF, bool OB16>
 static hipError_t launch_chunk_t(const ChunkArgs &a, int phases, hipStream_t st) {
   using Lds = IntraLds<C, D, NS>;
   static_assert(Lds::bytes <= 160 * 1024 || NS == 3, "intra-chunk LDS budget");
   if constexpr (Lds::bytes <= 160 * 1024) {
-    static std::once_flag once;
-    static hipError_t attr_err = hipSuccess;
-    std::call_once(once, [] {
-      attr_err = hipFuncSetAttribute(reinterpret_cast<const void *>(&chunk_intra_kernel<C, D, NS, BF, false>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lds::bytes);
-      if (attr_err == hipSuccess && NS == 2)
-        attr_err = hipFuncSetAttribute(reinterpret_cast<const void *>(&chunk_intra_kernel<C, D, NS, BF, NS == 2>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lds::bytes);
-    });
-    if (attr_err != hipSuccess) return attr_err;
-    static std::once_flag once2;
-    static hipError_t attr2 = hipSuccess;
-    std::call_once(once2, [] {
+    // the dynamic-LDS limits, once per device (a function attribute may be
+    // held per device)
+    static std::once_flag once[kMaxDevices];
+    static hipError_t attr_err[kMaxDevices];
+    int dev = 0;
+    hipError_t e0 = hipGetDevice(&dev);
+    if (e0 != hipSuccess) return e0;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::call_once(once[dev], [dev] {
       constexpr size_t out_lds = (size_t)(D / 16) * (D / 32) * NS * 512 * 2;
-      attr2 = hipFuncSetAttribute(reinterpret_cast<const void *>(&chunk_out_kernel<C, D, NS, OB16>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)out_lds);
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&chunk_intra_kernel<C, D, NS, BF, false>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lds::bytes);
+      if (e == hipSuccess && NS == 2)
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(&chunk_intra_kernel<C, D, NS, BF, NS == 2>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lds::bytes);
+      if (e == hipSuccess)
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(&chunk_out_kernel<C, D, NS, OB16>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)out_lds);
+      attr_err[dev] = e;
     });
-    if (attr2 != hipSuccess) return attr2;
+    if (attr_err[dev] != hipSuccess) return attr_err[dev];
     const size_t nbh = (size_t)a.B * a.H;
     if (a.ctab) {  // packed batch: one pass over the device-built chunk list
       if (phases & 1) {

@@ -643,3 +643,44 @@ def test_nan_stays_in_its_stream_and_runs_are_deterministic():
     mask = np.ones(o3.shape[:2], dtype=bool)
     mask[1, 2] = False
     assert np.array_equal(o3[mask], o1[mask]) and np.array_equal(s3[mask], s1[mask])
+
+
+def test_whole_call_and_decode_replay_from_a_hip_graph():
+    """The whole chunkwise call (long enough to run in segments) and a decode
+    step captured in one HIP graph: every replay, with eager work and
+    synchronisations between replays, equals the eager results bit for bit."""
+    wl = WORKLOADS["stress"].with_sizes(T=10000)
+    xd = make_inputs_device(wl, DEV, seed=23)
+    call = gdr.ChunkCall(xd["q"], xd["k"], xd["v"], xd["log_alpha"], xd["b"], xd["w"], xd["gamma"],
+                         xd["z"], xd["S0"], chunk=128)
+    dwl = WORKLOADS["decode"].with_sizes(B=4, H=2)
+    xdec = dev(decode_inputs(dwl, 0))
+    S_init = xdec["S0"].clone()
+    S_graph = S_init.clone()
+    o_eager, s_eager = [t.clone() for t in call()]
+    S_e = S_init.clone()
+    od_eager = gpu_decode(S_e, xdec).clone()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()  # warm-up on the capture stream
+        gpu_decode(S_graph.clone(), xdec)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        o_g, s_g = call()
+        od_g = gpu_decode(S_graph, xdec)
+    for rep in range(3):
+        call.o.zero_()
+        S_graph.copy_(S_init)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o_g, o_eager), rep
+        assert torch.equal(s_g, s_eager), rep
+        assert torch.equal(od_g, od_eager), rep
+        assert torch.equal(S_graph, S_e), rep
+        _ = (xd["q"].float() * 2).sum()  # eager work between replays
+    print("graph replays match the eager results", flush=True)
