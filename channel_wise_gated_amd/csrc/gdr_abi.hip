@@ -67,10 +67,19 @@ gdr_status chunk_plan(const gdr_desc *d, int nseq, size_t *ws) {
 // Validation and launch shared by the whole call (phases = 3), the
 // intra-chunk phase (1: reads the token inputs, writes the workspace) and the
 // scan phase (2: reads the workspace and S0, writes o and S_T).
+// Output gate of the whole call: y = RMSNorm(o) * norm_w * sigmoid(g), token-major.
+struct OutGate {
+  const void *g;
+  const float *norm_w;
+  float eps;
+  void *y;
+};
+
 gdr_status chunk_call(const gdr_desc *desc, int nseq, const int *cu, const void *q, const void *k,
                       const void *v, const float *log_alpha, const void *b, const void *w,
                       const float *gamma, const void *z, const float *S0, void *o, float *S_T,
-                      void *workspace, size_t workspace_bytes, void *stream, int phases) {
+                      void *workspace, size_t workspace_bytes, void *stream, int phases,
+                      const OutGate *og = nullptr) {
   size_t need = 0;
   gdr_status s = chunk_plan(desc, nseq, &need);
   if (s != GDR_OK) return s;
@@ -78,6 +87,12 @@ gdr_status chunk_call(const gdr_desc *desc, int nseq, const int *cu, const void 
   const long long streams = nseq > 0 ? (long long)nseq * d.H : (long long)d.B * d.H;
   if (streams == 0) return GDR_OK;
   if (nseq > 0 && (!cu || (reinterpret_cast<uintptr_t>(cu) & 3u))) return GDR_ERR_INVALID_ARG;
+  if (og) {  // gated output: y replaces o
+    if (!og->g || !og->y || !aligned16(og->g) || !aligned16(og->y)) return GDR_ERR_INVALID_ARG;
+    if (og->norm_w && !aligned16(og->norm_w)) return GDR_ERR_INVALID_ARG;
+    if (!(og->eps >= 0.f) || og->eps > 3.0e38f) return GDR_ERR_INVALID_ARG;
+    o = og->y;
+  }
   if (d.T > 0 && (phases & 1)) {
     s = check_inputs(desc, q, k, v, log_alpha, b, w, gamma, z, (phases & 2) ? o : q);
     if (s != GDR_OK) return s;
@@ -101,6 +116,10 @@ gdr_status chunk_call(const gdr_desc *desc, int nseq, const int *cu, const void 
   a.nseq = nseq;
   a.c0 = 0;  // the chunk range of each launch is set by launch_chunk
   a.ncs = 0;
+  a.og = og ? og->g : nullptr;
+  a.onw = og ? og->norm_w : nullptr;
+  a.oeps = og ? og->eps : 0.f;
+  a.y = og ? og->y : nullptr;
   if (nseq == 0) { a.ctab = nullptr; a.coff = nullptr; a.ctab_len = 0; }
   hipError_t e = gdr::launch_chunk(d, a, phases, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
@@ -124,6 +143,16 @@ gdr_status gdr_chunk_fwd(const gdr_desc *desc, const void *q, const void *k, con
                          size_t workspace_bytes, void *stream) {
   return chunk_call(desc, 0, nullptr, q, k, v, log_alpha, b, w, gamma, z, S0, o, S_T, workspace,
                     workspace_bytes, stream, 3);
+}
+
+gdr_status gdr_chunk_fwd_gated(const gdr_desc *desc, const void *q, const void *k, const void *v,
+                               const float *log_alpha, const void *b, const void *w,
+                               const float *gamma, const void *z, const float *S0, const void *g,
+                               const float *norm_weight, float eps, void *y, float *S_T,
+                               void *workspace, size_t workspace_bytes, void *stream) {
+  const OutGate og{g, norm_weight, eps, y};
+  return chunk_call(desc, 0, nullptr, q, k, v, log_alpha, b, w, gamma, z, S0, nullptr, S_T, workspace,
+                    workspace_bytes, stream, 3, &og);
 }
 
 gdr_status gdr_chunk_fwd_intra(const gdr_desc *desc, const void *q, const void *k, const void *v,

@@ -1059,7 +1059,10 @@ __global__ void __launch_bounds__(64 * (D / 16)) chunk_chain_kernel(ChunkArgs a)
 // tile w and sweeps the value slices: O = Q' S_c + O_bar.  S_c (all slices,
 // NS bf16 planes in B-fragment layout) is staged in LDS once.
 // ============================================================================
-template <int C, int D, int NS, bool OB16>
+// OG: gated output -- per token, the RMS over the dv channels of o is reduced
+// across the 16 lanes that hold the token's columns, and y = o / rms * onw *
+// sigmoid(og) is written token-major; o itself is not written.
+template <int C, int D, int NS, bool OB16, bool OG>
 __global__ void __launch_bounds__(64 * (C / 16)) chunk_out_kernel(ChunkArgs a) {
   constexpr int NRT = C / 16, NMT = D / 16, NKD = D / 32, NSL = D / 16;
   constexpr int FRAG = 64 * 8, NFR = NKD * NS;
@@ -1098,8 +1101,7 @@ __global__ void __launch_bounds__(64 * (C / 16)) chunk_out_kernel(ChunkArgs a) {
   __syncthreads();
   const int tok0 = 16 * wave + 4 * g;  // token of acc[0] within the chunk
   const size_t orow0 = rbase + tok0;
-#pragma unroll 1
-  for (int jt = 0; jt < NSL; ++jt) {
+  auto product = [&](int jt) {
     f32x4 acc = *reinterpret_cast<const f32x4 *>(Ob + ((size_t)(wave * NMT + jt) * 64 + lane) * 4);
 #pragma unroll
     for (int ks = 0; ks < NKD; ++ks) {
@@ -1107,10 +1109,50 @@ __global__ void __launch_bounds__(64 * (C / 16)) chunk_out_kernel(ChunkArgs a) {
       load_frag<NS>(sc + (jt * NFR + ks * NS) * FRAG + lane * 8, FRAG, sf);
       acc = mfma32_split<NS>(qf[ks], sf, acc);
     }
-    const int col = 16 * jt + l16;
+    return acc;
+  };
+  if constexpr (!OG) {
+#pragma unroll 1
+    for (int jt = 0; jt < NSL; ++jt) {
+      const f32x4 acc = product(jt);
+      const int col = 16 * jt + l16;
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (tok0 + r < tvalid) st1<OB16>(a.o, (orow0 + r) * D + col, acc[r]);  // no padding rows
+      for (int r = 0; r < 4; ++r)
+        if (tok0 + r < tvalid) st1<OB16>(a.o, (orow0 + r) * D + col, acc[r]);  // no padding rows
+    }
+  } else {
+    // all dv columns of this lane's 4 tokens (column 16 jt + l16)
+    f32x4 ov[NSL];
+    float ss[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int jt = 0; jt < NSL; ++jt) {
+      ov[jt] = product(jt);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ss[r] += ov[jt][r] * ov[jt][r];
+    }
+    float inv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) ss[r] += __shfl_xor(ss[r], off, kWave);  // the 16 lanes of the row
+      inv[r] = rsqrtf(ss[r] / (float)D + a.oeps);
+    }
+    const size_t T = (size_t)a.T;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (tok0 + r >= tvalid) continue;  // no padding rows
+      const size_t row = orow0 + r;      // row of [B,H,T] (head-major)
+      const size_t bh = row / T, t = row % T;
+      const size_t hh = bh % (size_t)a.H, b = bh / (size_t)a.H;
+      const size_t yrow = (b * T + t) * (size_t)a.H + hh;  // row of [B,T,H]
+#pragma unroll
+      for (int jt = 0; jt < NSL; ++jt) {
+        const int col = 16 * jt + l16;
+        const float gl = ld1<NS == 2>(a.og, row * D + col);
+        const float nw = a.onw ? a.onw[hh * D + col] : 1.f;
+        st1<OB16>(a.y, yrow * D + col, ov[jt][r] * inv[r] * nw * (1.f / (1.f + __expf(-gl))));
+      }
+    }
   }
 }
 
@@ -1243,7 +1285,10 @@ static hipError_t launch_chunk_pass(const ChunkArgs &a, size_t nch, int phases, 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nch == 0) return e;
   constexpr size_t out_lds = (size_t)NSL * (D / 32) * NS * 512 * 2;
-  hipLaunchKernelGGL((chunk_out_kernel<C, D, NS, OB16>), dim3((unsigned)nch), dim3(64 * (C / 16)), out_lds, st, a);
+  if (a.og)
+    hipLaunchKernelGGL((chunk_out_kernel<C, D, NS, OB16, true>), dim3((unsigned)nch), dim3(64 * (C / 16)), out_lds, st, a);
+  else
+    hipLaunchKernelGGL((chunk_out_kernel<C, D, NS, OB16, false>), dim3((unsigned)nch), dim3(64 * (C / 16)), out_lds, st, a);
   return hipGetLastError();
 }
 
@@ -1270,7 +1315,10 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, int phases, hipStream_t st)
         e = hipFuncSetAttribute(reinterpret_cast<const void *>(&chunk_intra_kernel<C, D, NS, BF, NS == 2>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lds::bytes);
       if (e == hipSuccess)
-        e = hipFuncSetAttribute(reinterpret_cast<const void *>(&chunk_out_kernel<C, D, NS, OB16>),
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(&chunk_out_kernel<C, D, NS, OB16, false>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)out_lds);
+      if (e == hipSuccess)
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(&chunk_out_kernel<C, D, NS, OB16, true>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)out_lds);
       attr_err[dev] = e;
     });

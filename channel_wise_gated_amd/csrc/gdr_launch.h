@@ -33,6 +33,12 @@ struct ChunkArgs {
   // stream; stream bh's chunk c sits in slot bh * ncs + (c - c0).
   int c0, ncs;
   float *Sst;  // workspace: fp32 states handed from one segment to the next
+  // Gated output (og != null): instead of o, y[b,t,h,:] = RMSNorm(o[b,h,t,:])
+  // * onw[h,:] * sigmoid(og[b,h,t,:]) in token-major [B,T,H,dv].
+  const void *og;
+  const float *onw;
+  float oeps;
+  void *y;
 };
 
 hipError_t launch_decode(const gdr_desc &d, float *S, const void *q, const void *k, const void *v,

@@ -9,6 +9,10 @@ Entry points (same names as the C ABI):
   gdr_chunk_fwd_workspace_size(desc) -> bytes
   gdr_chunk_fwd(q, k, v, log_alpha, b, w, gamma=None, z=None, S0=None, ...)
       -> (o, S_T)
+  gdr_chunk_fwd_gated(q, k, v, log_alpha, b, w, g, ...) -> (y, S_T)
+  ChunkCall(...) and its .intra() / .scan(): gdr_chunk_fwd_intra / _scan
+  gdr_chunk_fwd_varlen_workspace_size(desc, n_seqs) -> bytes
+  gdr_chunk_fwd_varlen(q, k, v, log_alpha, b, w, cu_seqlens, ...) -> (o, S_T)
   gdr_decode_step(S, q, k, v, log_alpha, b, w, gamma=None, z=None, ...) -> o
   gdr_status_string(code) -> str
 """
@@ -26,7 +30,7 @@ LIB_PATH = os.path.join(_HERE, "libgdr.so")
 GDR_OK, GDR_ERR_INVALID_ARG, GDR_ERR_UNSUPPORTED, GDR_ERR_WORKSPACE, GDR_ERR_HIP = range(5)
 GDR_BF16, GDR_F32 = 0, 1
 PER_CHANNEL, PER_TOKEN, ONES, ZEROS = 0, 1, 2, 3
-SYMBOLS = ("gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_chunk_fwd_intra",
+SYMBOLS = ("gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_chunk_fwd_gated", "gdr_chunk_fwd_intra",
            "gdr_chunk_fwd_scan", "gdr_chunk_fwd_varlen_workspace_size", "gdr_chunk_fwd_varlen",
            "gdr_decode_step", "gdr_status_string", "gdr_version")
 
@@ -65,6 +69,9 @@ def load() -> ctypes.CDLL:
     lib.gdr_chunk_fwd_workspace_size.argtypes = [dp, ctypes.POINTER(sz)]
     lib.gdr_chunk_fwd.restype = ctypes.c_int
     lib.gdr_chunk_fwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gdr_chunk_fwd_gated.restype = ctypes.c_int
+    lib.gdr_chunk_fwd_gated.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp,
+                                        vp, vp, sz, vp]
     lib.gdr_chunk_fwd_intra.restype = ctypes.c_int
     lib.gdr_chunk_fwd_intra.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gdr_chunk_fwd_scan.restype = ctypes.c_int
@@ -224,6 +231,31 @@ def gdr_chunk_fwd(q, k, v, log_alpha, b, w, gamma=None, z=None, S0=None, *, chun
     call = ChunkCall(q, k, v, log_alpha, b, w, gamma, z, S0, chunk=chunk, out_dtype=out_dtype,
                      normalize_qk=normalize_qk, scale=scale, o=o, S_T=S_T, workspace=workspace)
     return call(stream)
+
+
+def gdr_chunk_fwd_gated(q, k, v, log_alpha, b, w, g, gamma=None, z=None, S0=None, norm_weight=None,
+                        eps=1e-6, *, chunk=64, out_dtype=torch.float32, normalize_qk=True, scale=1.0,
+                        y=None, S_T=None, workspace=None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Chunkwise forward with the fused output gate; see gdr_chunk_fwd_gated in gdr.h.
+
+    Arguments as gdr_chunk_fwd, plus g [B,H,T,dv] (input dtype), norm_weight
+    [H,dv] fp32 or None, eps.  Returns (y [B,T,H,dv] out_dtype, S_T).
+    """
+    lib = load()
+    call = ChunkCall(q, k, v, log_alpha, b, w, gamma, z, S0, chunk=chunk, out_dtype=out_dtype,
+                     normalize_qk=normalize_qk, scale=scale, o=torch.empty(0, device=q.device),
+                     S_T=S_T, workspace=workspace)
+    g, norm_weight = _contig(g), _contig(norm_weight)
+    B, H, T, _ = q.shape
+    dv = v.shape[-1]
+    if y is None:
+        y = torch.empty((B, T, H, dv), dtype=out_dtype, device=q.device)
+    S0p, _, sTp = call.out_ptrs
+    rc = lib.gdr_chunk_fwd_gated(ctypes.byref(call.desc), *call.ptrs[:8], S0p, _ptr(g), _ptr(norm_weight),
+                                 float(eps), _ptr(y), sTp, *call.ws, _stream(stream))
+    if rc != GDR_OK:
+        raise GdrError(rc, "gdr_chunk_fwd_gated")
+    return y, call.S_T
 
 
 def gdr_decode_step(S, q, k, v, log_alpha, b, w, gamma=None, z=None, *, out_dtype=torch.float32,

@@ -132,6 +132,32 @@ gdr_status gdr_chunk_fwd(const gdr_desc *desc, const void *q, const void *k,
                          size_t workspace_bytes, void *stream);
 
 /*
+ * gdr_chunk_fwd with the layer's output gate fused into the output kernel
+ * (Muir reading notes, section 2.1: after a per-head RMSNorm the output gate
+ * g_t modulates every channel).  Instead of o, it writes
+ *   y[b,t,h,c] = o[b,h,t,c] / sqrt(mean_c' o[b,h,t,c']^2 + eps)
+ *                * norm_weight[h,c] * sigmoid(g[b,h,t,c])
+ * in token-major layout, ready for the output projection; o is not
+ * materialised.  The pages name neither the gate's activation nor the norm's
+ * epsilon: sigmoid (a gate in (0,1), like w) and a caller-given eps are this
+ * library's reading.
+ *
+ *   arguments as gdr_chunk_fwd, except:
+ *   g            [B,H,T,dv] in_dtype: output-gate logits
+ *   norm_weight  [H,dv] fp32 RMSNorm weight, or NULL (= 1)
+ *   eps          >= 0, finite (added to the mean square)
+ *   y            [B,T,H,dv] out_dtype (written)
+ * Validation as gdr_chunk_fwd, plus: g and y non-null and 16-byte aligned,
+ * eps finite and >= 0 (GDR_ERR_INVALID_ARG).
+ */
+gdr_status gdr_chunk_fwd_gated(const gdr_desc *desc, const void *q, const void *k,
+                               const void *v, const float *log_alpha, const void *b,
+                               const void *w, const float *gamma, const void *z,
+                               const float *S0, const void *g, const float *norm_weight,
+                               float eps, void *y, float *S_T, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/*
  * The two phases of gdr_chunk_fwd as separate calls, for callers that overlap
  * the fully parallel phase of one batch with the serial scan of another on a
  * second stream, or that time the phases.  gdr_chunk_fwd(...) gives exactly

@@ -175,3 +175,23 @@ def decode_step(S, q, k, v, log_alpha, b, w, gamma=None, z=None, scale=1.0,
 
 def max_threads() -> int:
     return _load().gdr_oracle_max_threads()
+
+
+def output_gate(o, g, norm_weight=None, eps=1e-6):
+    """The layer's output gate after the recurrence (Muir reading notes,
+    section 2.1: a per-head RMSNorm of o, after which the output gate g_t
+    modulates every channel).  The pages give neither the gate's activation
+    nor the norm's epsilon; this follows the library's reading: a sigmoid gate
+    and eps added to the mean square.
+
+    o, g: [B,H,T,dv]; norm_weight: [H,dv] or None (= 1).  Returns
+    y [B,T,H,dv] (token-major) in fp64.
+    """
+    o = _f64(o)
+    g = _f64(g)
+    mean_sq = np.mean(o * o, axis=-1, keepdims=True)
+    y = o / np.sqrt(mean_sq + eps)
+    if norm_weight is not None:
+        y = y * _f64(norm_weight)[None, :, None, :]
+    y = y / (1.0 + np.exp(-g))
+    return np.ascontiguousarray(y.transpose(0, 2, 1, 3))

@@ -115,6 +115,33 @@ def test_chunk_fwd_rejects_before_launch(ptrs, code):
     assert _call_chunk(gdr.make_desc(**GOOD), ptrs) == code
 
 
+def _call_gated(desc, ptrs, eps=1e-6, ws_bytes=1 << 30):
+    p = dict(q=16, k=32, v=48, la=64, b=80, w=96, gamma=None, z=None, S0=None, g=112, nw=None, y=128,
+             ST=144, ws=256)
+    p.update(ptrs)
+    c = lambda x: None if x is None else ctypes.c_void_p(x)
+    return gdr.load().gdr_chunk_fwd_gated(ctypes.byref(desc), c(p["q"]), c(p["k"]), c(p["v"]), c(p["la"]),
+                                          c(p["b"]), c(p["w"]), c(p["gamma"]), c(p["z"]), c(p["S0"]),
+                                          c(p["g"]), c(p["nw"]), eps, c(p["y"]), c(p["ST"]), c(p["ws"]),
+                                          ws_bytes, None)
+
+
+@pytest.mark.parametrize("ptrs,eps,code", [
+    (dict(g=None), 1e-6, gdr.GDR_ERR_INVALID_ARG),
+    (dict(y=None), 1e-6, gdr.GDR_ERR_INVALID_ARG),
+    (dict(g=120), 1e-6, gdr.GDR_ERR_INVALID_ARG),   # misaligned
+    (dict(nw=8), 1e-6, gdr.GDR_ERR_INVALID_ARG),
+    ({}, -1.0, gdr.GDR_ERR_INVALID_ARG),
+    ({}, float("nan"), gdr.GDR_ERR_INVALID_ARG),
+    ({}, float("inf"), gdr.GDR_ERR_INVALID_ARG),
+    (dict(q=None), 1e-6, gdr.GDR_ERR_INVALID_ARG),
+    (dict(ws=None), 1e-6, gdr.GDR_ERR_WORKSPACE),
+])
+def test_chunk_fwd_gated_rejects_before_launch(ptrs, eps, code):
+    _lib()
+    assert _call_gated(gdr.make_desc(**GOOD), ptrs, eps) == code
+
+
 def test_chunk_fwd_workspace_too_small():
     _lib()
     assert _call_chunk(gdr.make_desc(**GOOD), {}, ws_bytes=1024) == gdr.GDR_ERR_WORKSPACE

@@ -482,6 +482,62 @@ def test_alpha_zero_and_extreme_decay_runs(chunk):
 
 
 # ----------------------------------------------------------------------------
+# the fused output gate: y = RMSNorm(o) * weight * sigmoid(g), token-major
+# ----------------------------------------------------------------------------
+
+def gated_case(wl, seed=3):
+    x = make_inputs(wl)
+    r = np.random.default_rng(seed)
+    g = torch.from_numpy(r.standard_normal((wl.B, wl.H, wl.T, wl.dv))).to(x["v"].dtype)
+    nw = torch.from_numpy(1.0 + 0.2 * r.standard_normal((wl.H, wl.dv))).float()
+    return x, g, nw
+
+
+@pytest.mark.parametrize("name,chunk,T,d", [("gdn2", 64, 256, 128), ("stress", 128, 300, 128),
+                                            ("gdn2", 64, 77, 64), ("tiny", 64, 256, 64), ("gdn", 128, 129, 128)])
+def test_gated_output(name, chunk, T, d):
+    """The gated whole call against the oracle's recurrence followed by the
+    oracle's output gate."""
+    wl = WORKLOADS[name].with_sizes(B=2, H=2, T=T, dk=d, dv=d)
+    x, g, nw = gated_case(wl)
+    dd = dev(x)
+    y, sT = gdr.gdr_chunk_fwd_gated(dd["q"], dd["k"], dd["v"], dd["log_alpha"], dd["b"], dd["w"], g.to(DEV),
+                                    gamma=dd["gamma"], z=dd["z"], S0=dd["S0"], norm_weight=nw.to(DEV),
+                                    eps=1e-6, chunk=chunk)
+    torch.cuda.synchronize()
+    ro, rs = oracle_run(x)
+    ry = oracle.output_gate(ro, g, norm_weight=nw, eps=1e-6)
+    tol = tol_for(x)
+    check(f"gated {name} C{chunk} T{T} d{d} y", y.cpu().numpy(), ry, tol)
+    check(f"gated {name} C{chunk} T{T} d{d} S_T", sT.cpu().numpy(), rs, tol)
+
+
+def test_gated_output_bf16_and_segmented():
+    """bf16 y against the oracle's y rounded to bf16; and at a length that runs
+    in segments, the gated call equals the output gate applied (in fp64) to
+    the ungated call's o, and its final state equals the ungated one."""
+    wl = WORKLOADS["gdn2"].with_sizes(B=1, H=2, T=256)
+    x, g, nw = gated_case(wl, seed=4)
+    dd = dev(x)
+    y, _ = gdr.gdr_chunk_fwd_gated(dd["q"], dd["k"], dd["v"], dd["log_alpha"], dd["b"], dd["w"], g.to(DEV),
+                                   gamma=dd["gamma"], z=dd["z"], S0=dd["S0"], norm_weight=nw.to(DEV),
+                                   chunk=64, out_dtype=torch.bfloat16)
+    ro, _ = oracle_run(x)
+    ry = torch.from_numpy(oracle.output_gate(ro, g, norm_weight=nw)).to(torch.bfloat16).double().numpy()
+    check("gated bf16 y (vs oracle rounded to bf16)", y.float().cpu().numpy(), ry, TOL_BF16)
+    wl = WORKLOADS["stress"].with_sizes(T=10000)
+    xd = make_inputs_device(wl, DEV, seed=31)
+    gd = torch.randn((wl.B, wl.H, wl.T, wl.dv), device=DEV).to(torch.bfloat16)
+    args = (xd["q"], xd["k"], xd["v"], xd["log_alpha"], xd["b"], xd["w"])
+    o, s1 = gdr.gdr_chunk_fwd(*args, gamma=xd["gamma"], z=xd["z"], S0=xd["S0"], chunk=128)
+    y, s2 = gdr.gdr_chunk_fwd_gated(*args, gd, gamma=xd["gamma"], z=xd["z"], S0=xd["S0"], chunk=128)
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s2)
+    ry = oracle.output_gate(o.cpu(), gd.cpu(), eps=1e-6)
+    check("gated segmented y vs gate(o)", y.cpu().numpy(), ry, 1e-5)
+
+
+# ----------------------------------------------------------------------------
 # scalar decay (one log alpha per token: Gated DeltaNet, DeltaNet) -- bf16
 # inputs take the scalar-decay intra-chunk kernel
 # ----------------------------------------------------------------------------

@@ -488,3 +488,48 @@ def test_pins_reject_planted_mistakes(variant):
     ref_o, ref_s = chunk_system(*args, la, p["S0"][0, 0], 4)
     assert rel(good_o, ref_o) < 1e-11 and rel(good_s, ref_s) < 1e-11
     assert rel(bad_o, ref_o) > 1e-3
+
+
+# ----------------------------------------------------------------------------
+# the layer's output gate (Muir notes section 2.1: per-head RMSNorm of o, then
+# the output gate modulates every channel; sigmoid and eps are the readings)
+# ----------------------------------------------------------------------------
+
+def test_output_gate_unit_rms_and_scale_invariance(oracle_mod):
+    """With the gate saturated open (sigmoid -> 1), no weight and eps = 0 the
+    output has unit RMS over the channels of each (token, head), and scaling
+    o by a positive constant changes nothing."""
+    r = np.random.default_rng(5)
+    o = r.standard_normal((2, 3, 7, 16))
+    g = np.full_like(o, 60.0)
+    y = oracle_mod.output_gate(o, g, eps=0.0)
+    assert y.shape == (2, 7, 3, 16)
+    np.testing.assert_allclose(np.mean(y * y, axis=-1), 1.0, rtol=1e-12)
+    np.testing.assert_allclose(oracle_mod.output_gate(3.7 * o, g, eps=0.0), y, rtol=1e-12)
+
+
+def test_output_gate_hand_example_and_layout(oracle_mod):
+    """o = (1, -1, 1, -1) has mean square 1, so with g = 0 (sigmoid = 1/2)
+    and a weight of 2 for head 1 only, y = o / 2 for head 0 and o for head 1;
+    the (head, token) axes come out transposed."""
+    o = np.zeros((1, 2, 3, 4))
+    o[0, 0, 2] = [1.0, -1.0, 1.0, -1.0]
+    o[0, 1, 1] = [1.0, -1.0, 1.0, -1.0]
+    o[0, 0, 0] = o[0, 0, 1] = o[0, 1, 0] = o[0, 1, 2] = [2.0, 2.0, 2.0, 2.0]
+    wgt = np.ones((2, 4))
+    wgt[1] = 2.0
+    y = oracle_mod.output_gate(o, np.zeros_like(o), norm_weight=wgt, eps=0.0)
+    np.testing.assert_allclose(y[0, 2, 0], [0.5, -0.5, 0.5, -0.5], rtol=1e-15)
+    np.testing.assert_allclose(y[0, 1, 1], [1.0, -1.0, 1.0, -1.0], rtol=1e-15)
+    np.testing.assert_allclose(y[0, 0, 0], [0.5, 0.5, 0.5, 0.5], rtol=1e-15)
+    np.testing.assert_allclose(y[0, 0, 1], [1.0, 1.0, 1.0, 1.0], rtol=1e-15)
+
+
+def test_output_gate_zero_input_and_gate_values(oracle_mod):
+    """o = 0 with eps > 0 gives 0 (no division by zero); the gate factor at
+    logit x is 1 / (1 + e^-x): x = ln 3 gives 3/4."""
+    y0 = oracle_mod.output_gate(np.zeros((1, 1, 2, 8)), np.zeros((1, 1, 2, 8)), eps=1e-6)
+    assert np.all(y0 == 0.0)
+    o = np.ones((1, 1, 1, 8))
+    y = oracle_mod.output_gate(o, np.full_like(o, np.log(3.0)), eps=0.0)
+    np.testing.assert_allclose(y, 0.75, rtol=1e-14)
