@@ -1059,6 +1059,15 @@ __global__ void __launch_bounds__(64 * (D / 16)) chunk_chain_kernel(ChunkArgs a)
 // tile w and sweeps the value slices: O = Q' S_c + O_bar.  S_c (all slices,
 // NS bf16 planes in B-fragment layout) is staged in LDS once.
 // ============================================================================
+// Dynamic LDS of the output kernel: the S_c planes of all slices, and with a
+// gated output also the normalised rows [C][D + 4] fp32 (staged after the
+// planes are read).
+template <int C, int D, int NS>
+constexpr size_t out_lds_gated() {
+  constexpr size_t planes = (size_t)(D / 16) * (D / 32) * NS * 512 * 2, rows = (size_t)C * (D + 4) * 4;
+  return planes > rows ? planes : rows;
+}
+
 // OG: gated output -- per token, the RMS over the dv channels of o is reduced
 // across the 16 lanes that hold the token's columns, and y = o / rms * onw *
 // sigmoid(og) is written token-major; o itself is not written.
@@ -1137,21 +1146,37 @@ __global__ void __launch_bounds__(64 * (C / 16)) chunk_out_kernel(ChunkArgs a) {
       for (int off = 1; off < 16; off <<= 1) ss[r] += __shfl_xor(ss[r], off, kWave);  // the 16 lanes of the row
       inv[r] = rsqrtf(ss[r] / (float)D + a.oeps);
     }
-    const size_t T = (size_t)a.T;
+    // normalised rows through LDS (the S_c planes are no longer read), then
+    // each thread takes 8 consecutive columns of one token: the gate loads
+    // and the token-major stores are whole 16- or 32-byte vectors
+    __syncthreads();
+    float *ys = reinterpret_cast<float *>(smem);  // [C][D + 4] fp32
+    constexpr int YLD = D + 4;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if (tok0 + r >= tvalid) continue;  // no padding rows
-      const size_t row = orow0 + r;      // row of [B,H,T] (head-major)
+    for (int jt = 0; jt < NSL; ++jt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ys[(tok0 + r) * YLD + 16 * jt + l16] = ov[jt][r] * inv[r];
+    __syncthreads();
+    const size_t T = (size_t)a.T;
+    constexpr int PT = D / 8;  // threads per token
+    for (int idx = tid; idx < C * PT; idx += 64 * NRT) {
+      const int tk = idx / PT, c8 = (idx % PT) * 8;
+      if (tk >= tvalid) continue;  // no padding rows
+      const size_t row = rbase + tk;  // row of [B,H,T] (head-major)
       const size_t bh = row / T, t = row % T;
       const size_t hh = bh % (size_t)a.H, b = bh / (size_t)a.H;
       const size_t yrow = (b * T + t) * (size_t)a.H + hh;  // row of [B,T,H]
+      float gl[8], nw[8], yv[8];
+      ld8<NS == 2>(a.og, row * D + c8, gl);
+      if (a.onw) {
+        ld8<false>(a.onw, hh * D + c8, nw);
+      } else {
 #pragma unroll
-      for (int jt = 0; jt < NSL; ++jt) {
-        const int col = 16 * jt + l16;
-        const float gl = ld1<NS == 2>(a.og, row * D + col);
-        const float nw = a.onw ? a.onw[hh * D + col] : 1.f;
-        st1<OB16>(a.y, yrow * D + col, ov[jt][r] * inv[r] * nw * (1.f / (1.f + __expf(-gl))));
+        for (int e = 0; e < 8; ++e) nw[e] = 1.f;
       }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) yv[e] = ys[tk * YLD + c8 + e] * nw[e] * (1.f / (1.f + __expf(-gl[e])));
+      st8<OB16>(a.y, yrow * D + c8, yv);
     }
   }
 }
@@ -1285,8 +1310,10 @@ static hipError_t launch_chunk_pass(const ChunkArgs &a, size_t nch, int phases, 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nch == 0) return e;
   constexpr size_t out_lds = (size_t)NSL * (D / 32) * NS * 512 * 2;
+  constexpr size_t og_lds = out_lds_gated<C, D, NS>();
   if (a.og)
-    hipLaunchKernelGGL((chunk_out_kernel<C, D, NS, OB16, true>), dim3((unsigned)nch), dim3(64 * (C / 16)), out_lds, st, a);
+    hipLaunchKernelGGL((chunk_out_kernel<C, D, NS, OB16, true>), dim3((unsigned)nch), dim3(64 * (C / 16)), og_lds,
+                       st, a);
   else
     hipLaunchKernelGGL((chunk_out_kernel<C, D, NS, OB16, false>), dim3((unsigned)nch), dim3(64 * (C / 16)), out_lds, st, a);
   return hipGetLastError();
@@ -1319,7 +1346,7 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, int phases, hipStream_t st)
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)out_lds);
       if (e == hipSuccess)
         e = hipFuncSetAttribute(reinterpret_cast<const void *>(&chunk_out_kernel<C, D, NS, OB16, true>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)out_lds);
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)(out_lds_gated<C, D, NS>()));
       attr_err[dev] = e;
     });
     if (attr_err[dev] != hipSuccess) return attr_err[dev];

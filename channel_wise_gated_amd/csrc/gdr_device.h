@@ -82,6 +82,23 @@ __device__ __forceinline__ void ld8(const void *p, size_t i, float out[8]) {
   }
 }
 
+// Store 8 consecutive elements (i multiple of 8).
+template <bool BF16>
+__device__ __forceinline__ void st8(void *p, size_t i, const float x[8]) {
+  if constexpr (BF16) {
+    uint4 u;
+    u.x = (uint32_t)f32_to_bf16_bits(x[0]) | ((uint32_t)f32_to_bf16_bits(x[1]) << 16);
+    u.y = (uint32_t)f32_to_bf16_bits(x[2]) | ((uint32_t)f32_to_bf16_bits(x[3]) << 16);
+    u.z = (uint32_t)f32_to_bf16_bits(x[4]) | ((uint32_t)f32_to_bf16_bits(x[5]) << 16);
+    u.w = (uint32_t)f32_to_bf16_bits(x[6]) | ((uint32_t)f32_to_bf16_bits(x[7]) << 16);
+    *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(p) + i) = u;
+  } else {
+    float4 *f = reinterpret_cast<float4 *>(reinterpret_cast<float *>(p) + i);
+    f[0] = make_float4(x[0], x[1], x[2], x[3]);
+    f[1] = make_float4(x[4], x[5], x[6], x[7]);
+  }
+}
+
 template <bool BF16>
 __device__ __forceinline__ void st1(void *p, size_t i, float x) {
   if constexpr (BF16)
