@@ -125,9 +125,81 @@ gdr_status chunk_call(const gdr_desc *desc, int nseq, const int *cu, const void 
   return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }
 
+// The five-gate projection: validation, workspace size (the latent h).
+gdr_status gate_plan(const gdr_gate_desc *d, size_t *ws, int *R) {
+  if (!d) return GDR_ERR_INVALID_ARG;
+  if (d->B < 0 || d->T < 0 || d->H <= 0 || d->d_model <= 0 || d->d_model % 32) return GDR_ERR_INVALID_ARG;
+  if (!valid_dtype(d->out_dtype)) return GDR_ERR_INVALID_ARG;
+  int r = 0;
+  for (int i = 0; i < 5; ++i) {
+    if (d->rank[i] <= 0 || d->rank[i] % 32) return GDR_ERR_INVALID_ARG;
+    if (d->rank[i] > 128) return GDR_ERR_UNSUPPORTED;
+    r += d->rank[i];
+  }
+  if (d->d != 64 && d->d != 128) return GDR_ERR_UNSUPPORTED;
+  const long long N = (long long)d->B * d->T;
+  if (N > (1LL << 31) - 1 || N * (long long)(d->d_model > r ? d->d_model : r) > (1LL << 40) ||
+      N * (long long)d->H * d->d > (1LL << 40))
+    return GDR_ERR_INVALID_ARG;
+  *R = r;
+  *ws = (size_t)N * r * sizeof(float);
+  return GDR_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+gdr_status gdr_gate_proj_workspace_size(const gdr_gate_desc *desc, size_t *bytes) {
+  if (!bytes) return GDR_ERR_INVALID_ARG;
+  size_t ws = 0;
+  int R = 0;
+  gdr_status s = gate_plan(desc, &ws, &R);
+  if (s == GDR_OK) *bytes = ws;
+  return s;
+}
+
+gdr_status gdr_gate_proj(const gdr_gate_desc *desc, const void *x, const void *w_down,
+                         const void *w_up, const float *bias, float *log_alpha, void *b,
+                         void *g, void *w, void *z, void *workspace, size_t workspace_bytes,
+                         void *stream) {
+  size_t need = 0;
+  int R = 0;
+  gdr_status s = gate_plan(desc, &need, &R);
+  if (s != GDR_OK) return s;
+  const gdr_gate_desc &d = *desc;
+  if ((long long)d.B * d.T == 0) return GDR_OK;
+  if (!x || !w_down || !w_up) return GDR_ERR_INVALID_ARG;
+  const void *ptrs[] = {x, w_down, w_up, bias, log_alpha, b, g, w, z};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return GDR_ERR_INVALID_ARG;
+  if (need > 0 && (!workspace || workspace_bytes < need)) return GDR_ERR_WORKSPACE;
+  if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u)) return GDR_ERR_WORKSPACE;
+  gdr::GateArgs a;
+  a.x = static_cast<const uint16_t *>(x);
+  a.wd = static_cast<const uint16_t *>(w_down);
+  a.wu = static_cast<const uint16_t *>(w_up);
+  a.bias = bias;
+  a.hlat = static_cast<float *>(workspace);
+  void *outs[5] = {log_alpha, b, g, w, z};
+  a.N = d.B * d.T;
+  a.T = d.T;
+  a.dm = d.d_model;
+  a.H = d.H;
+  a.R = R;
+  size_t wo = 0;
+  int ro = 0;
+  for (int i = 0; i < 5; ++i) {
+    a.out[i] = outs[i];
+    a.rank[i] = d.rank[i];
+    a.roff[i] = ro;
+    a.wuoff[i] = wo;
+    ro += d.rank[i];
+    wo += (size_t)d.H * d.d * d.rank[i];
+  }
+  hipError_t e = gdr::launch_gate_proj(a, d.d, d.out_dtype == GDR_BF16, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
 
 gdr_status gdr_chunk_fwd_workspace_size(const gdr_desc *desc, size_t *bytes) {
   if (!bytes) return GDR_ERR_INVALID_ARG;

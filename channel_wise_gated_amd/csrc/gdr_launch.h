@@ -41,6 +41,21 @@ struct ChunkArgs {
   void *y;
 };
 
+// The five-gate projection: x [N, dm] bf16 (N = B*T tokens), wd [R, dm]
+// bf16, wu the gates' [H*d, rank] bf16 blocks at element offsets wuoff, bias
+// [5, H*d] fp32 or null; hlat [N, R] fp32 workspace; out[gate] (gate order f,
+// b, g, w, q) head-major [B, H, T, d] or null (not computed).
+struct GateArgs {
+  const uint16_t *x, *wd, *wu;
+  const float *bias;
+  float *hlat;
+  void *out[5];
+  int N, T, dm, H, R;
+  int rank[5], roff[5];
+  size_t wuoff[5];
+};
+hipError_t launch_gate_proj(const GateArgs &a, int d, bool out_bf16, hipStream_t st);
+
 hipError_t launch_decode(const gdr_desc &d, float *S, const void *q, const void *k, const void *v,
                          const float *la, const void *b, const void *w, const float *gamma,
                          const void *z, void *o, hipStream_t st);

@@ -32,7 +32,8 @@ GDR_BF16, GDR_F32 = 0, 1
 PER_CHANNEL, PER_TOKEN, ONES, ZEROS = 0, 1, 2, 3
 SYMBOLS = ("gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_chunk_fwd_gated", "gdr_chunk_fwd_intra",
            "gdr_chunk_fwd_scan", "gdr_chunk_fwd_varlen_workspace_size", "gdr_chunk_fwd_varlen",
-           "gdr_decode_step", "gdr_status_string", "gdr_version")
+           "gdr_decode_step", "gdr_status_string", "gdr_version", "gdr_gate_proj_workspace_size",
+           "gdr_gate_proj")
 
 
 class GdrDesc(ctypes.Structure):
@@ -42,6 +43,12 @@ class GdrDesc(ctypes.Structure):
                 ("normalize_qk", ctypes.c_int), ("scale", ctypes.c_float),
                 ("alpha_mode", ctypes.c_int), ("b_mode", ctypes.c_int),
                 ("w_mode", ctypes.c_int)]
+
+
+class GdrGateDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("T", ctypes.c_int), ("d_model", ctypes.c_int),
+                ("H", ctypes.c_int), ("d", ctypes.c_int), ("rank", ctypes.c_int * 5),
+                ("out_dtype", ctypes.c_int)]
 
 
 class GdrError(RuntimeError):
@@ -83,6 +90,11 @@ def load() -> ctypes.CDLL:
                                          vp, vp, vp, sz, vp]
     lib.gdr_decode_step.restype = ctypes.c_int
     lib.gdr_decode_step.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    gp = ctypes.POINTER(GdrGateDesc)
+    lib.gdr_gate_proj_workspace_size.restype = ctypes.c_int
+    lib.gdr_gate_proj_workspace_size.argtypes = [gp, ctypes.POINTER(sz)]
+    lib.gdr_gate_proj.restype = ctypes.c_int
+    lib.gdr_gate_proj.argtypes = [gp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gdr_status_string.restype = ctypes.c_char_p
     lib.gdr_status_string.argtypes = [ctypes.c_int]
     lib.gdr_version.restype = ctypes.c_int
@@ -256,6 +268,47 @@ def gdr_chunk_fwd_gated(q, k, v, log_alpha, b, w, g, gamma=None, z=None, S0=None
     if rc != GDR_OK:
         raise GdrError(rc, "gdr_chunk_fwd_gated")
     return y, call.S_T
+
+
+GATE_ORDER = ("f", "b", "g", "w", "q")
+
+
+def make_gate_desc(B, T, d_model, H, d, ranks, out_dtype=GDR_BF16) -> GdrGateDesc:
+    return GdrGateDesc(int(B), int(T), int(d_model), int(H), int(d), (ctypes.c_int * 5)(*map(int, ranks)),
+                       int(out_dtype))
+
+
+def gdr_gate_proj(x, w_down, w_up, bias, ranks, H, d, *, out_dtype=torch.bfloat16, gates=GATE_ORDER,
+                  workspace=None, stream=None) -> dict:
+    """The five-gate low-rank projection; see gdr_gate_proj in gdr.h.
+
+    x [B,T,d_model] bf16; w_down [R,d_model] bf16; w_up: dict gate -> [H*d, r]
+    bf16 (packed here in gate order); bias [5,H*d] fp32 or None.  Returns a
+    dict gate -> [B,H,T,d] tensor for the gates in `gates` ("f": log alpha
+    fp32; the others out_dtype).
+    """
+    lib = load()
+    x, w_down, bias = _contig(x), _contig(w_down), _contig(bias)
+    B, T, dm = x.shape
+    desc = make_gate_desc(B, T, dm, H, d, ranks, GDR_BF16 if out_dtype == torch.bfloat16 else GDR_F32)
+    wu = torch.cat([w_up[n].reshape(-1) for n in GATE_ORDER]).contiguous()
+    n = ctypes.c_size_t(0)
+    rc = lib.gdr_gate_proj_workspace_size(ctypes.byref(desc), ctypes.byref(n))
+    if rc != GDR_OK:
+        raise GdrError(rc, "gdr_gate_proj_workspace_size")
+    if workspace is None:
+        workspace = torch.empty(max(int(n.value), 1), dtype=torch.uint8, device=x.device)
+    outs = {}
+    for name in GATE_ORDER:
+        if name in gates:
+            outs[name] = torch.empty((B, H, T, d), device=x.device,
+                                     dtype=torch.float32 if name == "f" else out_dtype)
+    ptr = lambda name: _ptr(outs.get(name))
+    rc = lib.gdr_gate_proj(ctypes.byref(desc), _ptr(x), _ptr(w_down), _ptr(wu), _ptr(bias), ptr("f"), ptr("b"),
+                           ptr("g"), ptr("w"), ptr("q"), _ptr(workspace), workspace.numel(), _stream(stream))
+    if rc != GDR_OK:
+        raise GdrError(rc, "gdr_gate_proj")
+    return outs
 
 
 def gdr_decode_step(S, q, k, v, log_alpha, b, w, gamma=None, z=None, *, out_dtype=torch.float32,

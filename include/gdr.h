@@ -132,6 +132,51 @@ gdr_status gdr_chunk_fwd(const gdr_desc *desc, const void *q, const void *k,
                          size_t workspace_bytes, void *stream);
 
 /*
+ * The five gates from one shared low-rank projection of the layer input
+ * (Muir reading notes, section 2.3: a shared down-projection, then per gate
+ * an up-projection and a channel bias give the logits of the decay f, erase
+ * b, output gate g, write w and query gain q, with ranks
+ * (r_f, r_b, r_g, r_w, r_q); the main model uses (64, 64, 128, 128, 128)).
+ *   h        = x W_down^T                              [N, R], R = sum of ranks
+ *   l_gate   = h[:, ranks of the gate] W_up_gate^T + bias_gate   [N, H*d]
+ * The pages print neither the formula nor the activations; this library
+ * reads them as follows (ranges from section 2.1):
+ *   log_alpha = log sigmoid(l_f)  (alpha in (0,1); fp32)
+ *   b = 2 sigmoid(l_b) in (0,2),  w = sigmoid(l_w) in (0,1)
+ *   g = l_g  (gdr_chunk_fwd_gated applies the sigmoid)
+ *   z = l_q  (the read-out applies 2 sigmoid(z))
+ * Output channel j = h*d + c of token (b, t) is written at [b, h, t, c], the
+ * layout gdr_chunk_fwd reads (per-channel gate modes).
+ */
+typedef struct gdr_gate_desc {
+  int B, T;         /* tokens; x is [B, T, d_model]                            */
+  int d_model;      /* input width: a positive multiple of 32                  */
+  int H, d;         /* outputs [B, H, T, d]; d = 64 or 128                     */
+  int rank[5];      /* (r_f, r_b, r_g, r_w, r_q): multiples of 32, 32..128     */
+  gdr_dtype out_dtype; /* storage of b, w, g, z (log_alpha is always fp32)     */
+} gdr_gate_desc;
+
+/* Bytes of device workspace gdr_gate_proj needs (the latent h, fp32). */
+gdr_status gdr_gate_proj_workspace_size(const gdr_gate_desc *desc, size_t *bytes);
+
+/*
+ *   x          [B, T, d_model] bf16
+ *   w_down     [R, d_model] bf16 (rows in gate order f, b, g, w, q)
+ *   w_up       the gates' [H*d, r_gate] bf16 matrices, back to back in gate order
+ *   bias       [5, H*d] fp32 in gate order, or NULL (= 0)
+ *   log_alpha  [B, H, T, d] fp32;  b, g, w, z [B, H, T, d] out_dtype -- each
+ *              output may be NULL, and that gate is then not computed
+ *   workspace  >= gdr_gate_proj_workspace_size() bytes, 256-byte aligned
+ * Every pointer 16-byte aligned.  Invalid sizes, null required pointers or
+ * misalignment: GDR_ERR_INVALID_ARG; a rank above 128 or d not 64 / 128:
+ * GDR_ERR_UNSUPPORTED; all checked on the host before any launch.
+ */
+gdr_status gdr_gate_proj(const gdr_gate_desc *desc, const void *x, const void *w_down,
+                         const void *w_up, const float *bias, float *log_alpha, void *b,
+                         void *g, void *w, void *z, void *workspace, size_t workspace_bytes,
+                         void *stream);
+
+/*
  * gdr_chunk_fwd with the layer's output gate fused into the output kernel
  * (Muir reading notes, section 2.1: after a per-head RMSNorm the output gate
  * g_t modulates every channel).  Instead of o, it writes

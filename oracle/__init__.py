@@ -195,3 +195,46 @@ def output_gate(o, g, norm_weight=None, eps=1e-6):
         y = y * _f64(norm_weight)[None, :, None, :]
     y = y / (1.0 + np.exp(-g))
     return np.ascontiguousarray(y.transpose(0, 2, 1, 3))
+
+
+GATE_ORDER = ("f", "b", "g", "w", "q")
+
+
+def gate_proj(x, w_down, w_up, bias, ranks, H, d):
+    """The five gates from one shared low-rank projection (Muir reading notes,
+    section 2.3: a shared down-projection, then a per-gate up-projection and
+    channel bias give each gate's logits; ranks (r_f, r_b, r_g, r_w, r_q)).
+    The pages print neither the formula nor the activations; this follows the
+    library's reading, with the ranges section 2.1 states:
+      decay  alpha = sigmoid(l_f)   -> returned as log alpha = log sigmoid(l_f)
+      erase  b = 2 sigmoid(l_b)     in (0, 2)
+      output gate logits l_g        (the gated output applies a sigmoid)
+      write  w = sigmoid(l_w)       in (0, 1)
+      query gain logits z = l_q     (the read-out applies 2 sigmoid(z))
+
+    x: [B,T,dm]; w_down: [R,dm] with R = sum(ranks) (rows in gate order
+    f, b, g, w, q); w_up: dict gate -> [H*d, r_gate]; bias: [5, H*d] in gate
+    order.  Weights are nn.Linear-style [out, in].  Returns a dict gate ->
+    [B,H,T,d] fp64 (log alpha for "f").
+    """
+    x = _f64(x)
+    wd = _f64(w_down)
+    bias = _f64(bias)
+    B, T, _ = x.shape
+    h = x @ wd.T                       # [B,T,R]
+    out = {}
+    r0 = 0
+    for gi, name in enumerate(GATE_ORDER):
+        r = int(ranks[gi])
+        logits = h[..., r0:r0 + r] @ _f64(w_up[name]).T + bias[gi]   # [B,T,H*d]
+        r0 += r
+        if name == "f":
+            val = -np.logaddexp(0.0, -logits)        # log sigmoid
+        elif name == "b":
+            val = 2.0 / (1.0 + np.exp(-logits))
+        elif name == "w":
+            val = 1.0 / (1.0 + np.exp(-logits))
+        else:                                        # g, q: logits
+            val = logits
+        out[name] = np.ascontiguousarray(val.reshape(B, T, H, d).transpose(0, 2, 1, 3))
+    return out

@@ -209,3 +209,35 @@ def test_varlen_validation():
     assert call(None) == gdr.GDR_ERR_INVALID_ARG
     assert call(1026) == gdr.GDR_ERR_INVALID_ARG   # misaligned offsets
     assert call(1024, nseq=0) == gdr.GDR_ERR_INVALID_ARG
+
+
+GATE = dict(B=2, T=100, d_model=256, H=2, d=128, ranks=(64, 64, 128, 128, 128))
+
+
+def _gate_ws(**kw):
+    p = dict(GATE)
+    p.update(kw)
+    desc = gdr.make_gate_desc(p["B"], p["T"], p["d_model"], p["H"], p["d"], p["ranks"])
+    n = ctypes.c_size_t(0)
+    return gdr.load().gdr_gate_proj_workspace_size(ctypes.byref(desc), ctypes.byref(n)), n.value
+
+
+def test_gate_proj_workspace_and_validation():
+    _lib()
+    rc, n = _gate_ws()
+    assert rc == gdr.GDR_OK and n == 2 * 100 * 512 * 4      # the latent h, fp32
+    assert _gate_ws(d_model=100)[0] == gdr.GDR_ERR_INVALID_ARG       # not a multiple of 32
+    assert _gate_ws(ranks=(64, 64, 128, 100, 128))[0] == gdr.GDR_ERR_INVALID_ARG
+    assert _gate_ws(ranks=(64, 64, 128, 256, 128))[0] == gdr.GDR_ERR_UNSUPPORTED
+    assert _gate_ws(d=96)[0] == gdr.GDR_ERR_UNSUPPORTED
+    assert _gate_ws(H=0)[0] == gdr.GDR_ERR_INVALID_ARG
+    assert _gate_ws(T=0) == (gdr.GDR_OK, 0)
+    desc = gdr.make_gate_desc(2, 100, 256, 2, 128, (64, 64, 128, 128, 128))
+    c = lambda x: None if x is None else ctypes.c_void_p(x)
+    call = lambda x, wd, wu, ws, nb: gdr.load().gdr_gate_proj(
+        ctypes.byref(desc), c(x), c(wd), c(wu), None, c(4096), None, None, None, None, c(ws), nb, None)
+    assert call(None, 1024, 2048, 8192, 1 << 30) == gdr.GDR_ERR_INVALID_ARG   # no input
+    assert call(1032, 1024, 2048, 8192, 1 << 30) == gdr.GDR_ERR_INVALID_ARG   # misaligned
+    assert call(1024, 1288, 2048, 8192, 1 << 30) == gdr.GDR_ERR_INVALID_ARG
+    assert call(1024, 1280, 2048, None, 1 << 30) == gdr.GDR_ERR_WORKSPACE
+    assert call(1024, 1280, 2048, 8192, 1000) == gdr.GDR_ERR_WORKSPACE

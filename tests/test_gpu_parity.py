@@ -740,3 +740,75 @@ def test_whole_call_and_decode_replay_from_a_hip_graph():
         assert torch.equal(S_graph, S_e), rep
         _ = (xd["q"].float() * 2).sum()  # eager work between replays
     print("graph replays match the eager results", flush=True)
+
+
+# ----------------------------------------------------------------------------
+# the five-gate low-rank projection (x -> log alpha, b, g, w, z)
+# ----------------------------------------------------------------------------
+
+def gate_weights(dm, H, d, ranks, seed, bias=True):
+    r = np.random.default_rng(seed)
+    R = sum(ranks)
+    bf = lambda a: torch.from_numpy(a).to(torch.bfloat16)
+    wd = bf(r.standard_normal((R, dm)) / np.sqrt(dm))
+    wu = {n: bf(r.standard_normal((H * d, rk)) / np.sqrt(rk)) for n, rk in zip(gdr.GATE_ORDER, ranks)}
+    bs = torch.from_numpy(0.5 * r.standard_normal((5, H * d))).float() if bias else None
+    return wd, wu, bs
+
+
+@pytest.mark.parametrize("B,T,dm,H,d,ranks,bias", [
+    (2, 300, 256, 2, 128, (64, 64, 128, 128, 128), True),
+    (1, 77, 512, 4, 64, (32, 64, 32, 96, 128), False),
+    (1, 1, 64, 1, 128, (32, 32, 32, 32, 32), True)])
+def test_gate_proj(B, T, dm, H, d, ranks, bias):
+    r = np.random.default_rng(7)
+    x = torch.from_numpy(r.standard_normal((B, T, dm))).to(torch.bfloat16)
+    wd, wu, bs = gate_weights(dm, H, d, ranks, 8, bias)
+    out = gdr.gdr_gate_proj(x.to(DEV), wd.to(DEV), {n: t.to(DEV) for n, t in wu.items()},
+                            None if bs is None else bs.to(DEV), ranks, H, d)
+    torch.cuda.synchronize()
+    ref = oracle.gate_proj(x, wd, wu, np.zeros((5, H * d)) if bs is None else bs, ranks, H, d)
+    for n in gdr.GATE_ORDER:
+        got = out[n].float().cpu().numpy()
+        want = ref[n] if n == "f" else torch.from_numpy(ref[n]).to(torch.bfloat16).double().numpy()
+        check(f"gate proj B{B} T{T} dm{dm} H{H} d{d} {n}", got, want, TOL_BF16)
+
+
+def test_gate_proj_skips_unwanted_gates_and_fp32_outputs():
+    ranks = (64, 64, 128, 128, 128)
+    r = np.random.default_rng(9)
+    x = torch.from_numpy(r.standard_normal((1, 130, 256))).to(torch.bfloat16)
+    wd, wu, bs = gate_weights(256, 2, 128, ranks, 10)
+    out = gdr.gdr_gate_proj(x.to(DEV), wd.to(DEV), {n: t.to(DEV) for n, t in wu.items()}, bs.to(DEV), ranks,
+                            2, 128, out_dtype=torch.float32, gates=("f", "w"))
+    torch.cuda.synchronize()
+    assert set(out) == {"f", "w"}
+    ref = oracle.gate_proj(x, wd, wu, bs, ranks, 2, 128)
+    check("gate proj fp32 f", out["f"].cpu().numpy(), ref["f"], TOL_F32 * 10)
+    check("gate proj fp32 w", out["w"].cpu().numpy(), ref["w"], TOL_F32 * 10)
+
+
+def test_layer_pipeline_projection_recurrence_output_gate():
+    """x -> gate projection -> chunkwise recurrence -> gated output, against
+    the oracle's three steps on the same inputs (the GPU gates, stored bf16,
+    are what both recurrences consume)."""
+    B, T, H, d = 1, 200, 2, 128
+    dm, ranks = 256, (64, 64, 128, 128, 128)
+    r = np.random.default_rng(11)
+    x = torch.from_numpy(r.standard_normal((B, T, dm))).to(torch.bfloat16)
+    wd, wu, bs = gate_weights(dm, H, d, ranks, 12)
+    gates = gdr.gdr_gate_proj(x.to(DEV), wd.to(DEV), {n: t.to(DEV) for n, t in wu.items()}, bs.to(DEV),
+                              ranks, H, d)
+    wl = WORKLOADS["gdn2"].with_sizes(B=B, H=H, T=T)
+    xin = make_inputs(wl)
+    gamma = xin["gamma"]
+    q, k, v = (xin[n].to(DEV) for n in ("q", "k", "v"))
+    nw = torch.from_numpy(1.0 + 0.1 * r.standard_normal((H, d))).float()
+    y, sT = gdr.gdr_chunk_fwd_gated(q, k, v, gates["f"], gates["b"], gates["w"], gates["g"], gamma=gamma.to(DEV),
+                                    z=gates["q"], norm_weight=nw.to(DEV), chunk=64)
+    torch.cuda.synchronize()
+    gc = {n: t.cpu() for n, t in gates.items()}
+    ro, rs = oracle.forward(xin["q"], xin["k"], xin["v"], gc["f"], gc["b"], gc["w"], gamma=gamma, z=gc["q"])
+    ry = oracle.output_gate(ro, gc["g"], norm_weight=nw)
+    check("layer pipeline y", y.cpu().numpy(), ry, TOL_BF16)
+    check("layer pipeline S_T", sT.cpu().numpy(), rs, TOL_BF16)

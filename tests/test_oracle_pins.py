@@ -533,3 +533,83 @@ def test_output_gate_zero_input_and_gate_values(oracle_mod):
     o = np.ones((1, 1, 1, 8))
     y = oracle_mod.output_gate(o, np.full_like(o, np.log(3.0)), eps=0.0)
     np.testing.assert_allclose(y, 0.75, rtol=1e-14)
+
+
+# ----------------------------------------------------------------------------
+# the five-gate low-rank projection (Muir notes section 2.3; activations and
+# layouts are the library's reading, ranges from section 2.1)
+# ----------------------------------------------------------------------------
+
+def _gate_problem(seed, B=2, T=5, dm=12, H=2, d=3, ranks=(2, 2, 3, 3, 3)):
+    r = np.random.default_rng(seed)
+    R = sum(ranks)
+    x = r.standard_normal((B, T, dm))
+    wd = r.standard_normal((R, dm)) / np.sqrt(dm)
+    wu = {n: r.standard_normal((H * d, rk)) / np.sqrt(rk) for n, rk in zip(("f", "b", "g", "w", "q"), ranks)}
+    bias = 0.3 * r.standard_normal((5, H * d))
+    return x, wd, wu, bias, ranks, H, d
+
+
+def _logits(out):
+    """Undo each gate's activation (a different formulation from the oracle's)."""
+    return {"f": np.log(np.expm1(-out["f"])) * -1.0,        # log alpha = -softplus(-l)
+            "b": np.log(out["b"] / (2.0 - out["b"])),
+            "w": np.log(out["w"] / (1.0 - out["w"])),
+            "g": out["g"], "q": out["q"]}
+
+
+def test_gate_proj_zero_weights_give_the_bias(oracle_mod):
+    x, wd, wu, bias, ranks, H, d = _gate_problem(1)
+    out = oracle_mod.gate_proj(x, np.zeros_like(wd), wu, bias, ranks, H, d)
+    bh = bias.reshape(5, H, d)
+    np.testing.assert_allclose(out["b"][1, 1, 3], 2.0 / (1.0 + np.exp(-bh[1, 1])), rtol=1e-14)
+    np.testing.assert_allclose(out["w"][0, 0, 4], 1.0 / (1.0 + np.exp(-bh[3, 0])), rtol=1e-14)
+    np.testing.assert_allclose(out["f"][1, 0, 0], np.log(1.0 / (1.0 + np.exp(-bh[0, 0]))), rtol=1e-13)
+    np.testing.assert_allclose(out["g"][0, 1, 2], bh[2, 1], rtol=1e-15)
+    np.testing.assert_allclose(out["q"][1, 1, 1], bh[4, 1], rtol=1e-15)
+    assert np.all(out["f"] < 0) and np.all((out["b"] > 0) & (out["b"] < 2)) and np.all((out["w"] > 0) & (out["w"] < 1))
+
+
+def test_gate_proj_linear_low_rank_and_separate(oracle_mod):
+    """The logits minus the bias are linear in x, of rank at most r_gate over
+    the tokens, and each gate depends only on its own rows of the down-projection
+    and its own up-projection."""
+    x, wd, wu, bias, ranks, H, d = _gate_problem(2, B=1, T=20)
+    x2 = np.random.default_rng(9).standard_normal(x.shape)
+    l1 = _logits(oracle_mod.gate_proj(x, wd, wu, bias, ranks, H, d))
+    l2 = _logits(oracle_mod.gate_proj(x2, wd, wu, bias, ranks, H, d))
+    l12 = _logits(oracle_mod.gate_proj(x + x2, wd, wu, bias, ranks, H, d))
+    bh = bias.reshape(5, 1, H, 1, d)
+    for gi, n in enumerate(("f", "b", "g", "w", "q")):
+        lin = l1[n] + l2[n] - bh[gi]
+        np.testing.assert_allclose(l12[n], lin, rtol=1e-9, atol=1e-9)
+        tok_by_chan = (l1[n] - bh[gi])[0].transpose(1, 0, 2).reshape(x.shape[1], H * d)
+        assert np.linalg.matrix_rank(tok_by_chan, tol=1e-9) <= ranks[gi]
+    # perturb the up-projection of the write gate and the down-projection rows of
+    # the erase gate: only those gates move
+    wu2 = dict(wu)
+    wu2["w"] = wu["w"] + 0.5
+    wd2 = wd.copy()
+    wd2[ranks[0]:ranks[0] + ranks[1]] += 0.5
+    base = oracle_mod.gate_proj(x, wd, wu, bias, ranks, H, d)
+    pert = oracle_mod.gate_proj(x, wd2, wu2, bias, ranks, H, d)
+    for n in ("f", "g", "q"):
+        np.testing.assert_array_equal(base[n], pert[n])
+    assert not np.allclose(base["w"], pert["w"]) and not np.allclose(base["b"], pert["b"])
+
+
+def test_gate_proj_layout(oracle_mod):
+    """Output channel j = h * d + c of token (b, t) lands at [b, h, t, c]:
+    an up-projection that copies one rank column to a single output channel."""
+    x, wd, wu, bias, ranks, H, d = _gate_problem(3)
+    wq = np.zeros_like(wu["q"])
+    wq[1 * d + 2, 0] = 1.0                      # head 1, channel 2 <- first q rank
+    wu2 = dict(wu)
+    wu2["q"] = wq
+    out = oracle_mod.gate_proj(x, wd, wu2, np.zeros_like(bias), ranks, H, d)
+    rq0 = sum(ranks[:4])
+    expect = x @ wd[rq0]                        # [B,T]
+    np.testing.assert_allclose(out["q"][:, 1, :, 2], expect, rtol=1e-13)
+    mask = np.ones((H, d), dtype=bool)
+    mask[1, 2] = False
+    assert np.all(out["q"].transpose(0, 2, 1, 3)[:, :, mask] == 0.0)
