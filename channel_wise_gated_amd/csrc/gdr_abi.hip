@@ -138,11 +138,11 @@ gdr_status gate_plan(const gdr_gate_desc *d, size_t *ws, int *R) {
   }
   if (d->d != 64 && d->d != 128) return GDR_ERR_UNSUPPORTED;
   const long long N = (long long)d->B * d->T;
-  if (N > (1LL << 31) - 1 || N * (long long)(d->d_model > r ? d->d_model : r) > (1LL << 40) ||
+  if (N * d->H > (1LL << 31) - 1 || N * (long long)(d->d_model > r ? d->d_model : r) > (1LL << 40) ||
       N * (long long)d->H * d->d > (1LL << 40))
     return GDR_ERR_INVALID_ARG;
   *R = r;
-  *ws = (size_t)N * r * sizeof(float);
+  *ws = (size_t)N * r * sizeof(float);  // the latent h, fp32
   return GDR_OK;
 }
 

@@ -37,6 +37,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
   __bf16 b = (__bf16)x;  // round to nearest even (v_cvt_pk_bf16_f32)
   return __builtin_bit_cast(uint16_t, b);
 }
+// Two floats to two bf16 (round to nearest even, as above) in one 32-bit word,
+// x in the low half: one v_cvt_pk_bf16_f32.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float x, float y) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x, y}, bf16x2));
+}
 __device__ __forceinline__ float round_bf16(float x) {
   return bf16_bits_to_f32(f32_to_bf16_bits(x));
 }

@@ -48,7 +48,7 @@ struct ChunkArgs {
 struct GateArgs {
   const uint16_t *x, *wd, *wu;
   const float *bias;
-  float *hlat;
+  float *hlat;  // [N][R] fp32 latent
   void *out[5];
   int N, T, dm, H, R;
   int rank[5], roff[5];

@@ -278,29 +278,44 @@ def make_gate_desc(B, T, d_model, H, d, ranks, out_dtype=GDR_BF16) -> GdrGateDes
                        int(out_dtype))
 
 
+def pack_gate_up(w_up) -> torch.Tensor:
+    """The five up-projection weights (dict gate -> [H*d, r] bf16) packed one
+    after the other in gate order, as gdr_gate_proj reads them."""
+    return torch.cat([_contig(w_up[n]).reshape(-1) for n in GATE_ORDER]).contiguous()
+
+
 def gdr_gate_proj(x, w_down, w_up, bias, ranks, H, d, *, out_dtype=torch.bfloat16, gates=GATE_ORDER,
-                  workspace=None, stream=None) -> dict:
+                  outs=None, workspace=None, stream=None) -> dict:
     """The five-gate low-rank projection; see gdr_gate_proj in gdr.h.
 
     x [B,T,d_model] bf16; w_down [R,d_model] bf16; w_up: dict gate -> [H*d, r]
-    bf16 (packed here in gate order); bias [5,H*d] fp32 or None.  Returns a
-    dict gate -> [B,H,T,d] tensor for the gates in `gates` ("f": log alpha
-    fp32; the others out_dtype).
+    bf16 (packed here in gate order) or the packed tensor from pack_gate_up;
+    bias [5,H*d] fp32 or None.  Returns a dict gate -> [B,H,T,d] tensor for
+    the gates in `gates` ("f": log alpha fp32; the others out_dtype), written
+    into `outs` (same keys) when given.
     """
     lib = load()
     x, w_down, bias = _contig(x), _contig(w_down), _contig(bias)
     B, T, dm = x.shape
     desc = make_gate_desc(B, T, dm, H, d, ranks, GDR_BF16 if out_dtype == torch.bfloat16 else GDR_F32)
-    wu = torch.cat([w_up[n].reshape(-1) for n in GATE_ORDER]).contiguous()
+    wu = _contig(w_up) if isinstance(w_up, torch.Tensor) else pack_gate_up(w_up)
     n = ctypes.c_size_t(0)
     rc = lib.gdr_gate_proj_workspace_size(ctypes.byref(desc), ctypes.byref(n))
     if rc != GDR_OK:
         raise GdrError(rc, "gdr_gate_proj_workspace_size")
     if workspace is None:
         workspace = torch.empty(max(int(n.value), 1), dtype=torch.uint8, device=x.device)
-    outs = {}
+    if outs is not None:
+        gates = tuple(outs)
+        for name, t in outs.items():
+            want = torch.float32 if name == "f" else out_dtype
+            if (name not in GATE_ORDER or tuple(t.shape) != (B, H, T, d) or t.dtype != want
+                    or not t.is_contiguous() or t.device != x.device):
+                raise ValueError(f"gdr_gate_proj: output '{name}' must be a contiguous [B,H,T,d] {want} "
+                                 f"tensor on {x.device}")
+    outs = dict(outs or {})
     for name in GATE_ORDER:
-        if name in gates:
+        if name in gates and name not in outs:
             outs[name] = torch.empty((B, H, T, d), device=x.device,
                                      dtype=torch.float32 if name == "f" else out_dtype)
     ptr = lambda name: _ptr(outs.get(name))

@@ -156,7 +156,8 @@ typedef struct gdr_gate_desc {
   gdr_dtype out_dtype; /* storage of b, w, g, z (log_alpha is always fp32)     */
 } gdr_gate_desc;
 
-/* Bytes of device workspace gdr_gate_proj needs (the latent h, fp32). */
+/* Bytes of device workspace gdr_gate_proj needs: the latent h, fp32
+ * [B*T, R]. */
 gdr_status gdr_gate_proj_workspace_size(const gdr_gate_desc *desc, size_t *bytes);
 
 /*
@@ -167,8 +168,9 @@ gdr_status gdr_gate_proj_workspace_size(const gdr_gate_desc *desc, size_t *bytes
  *   log_alpha  [B, H, T, d] fp32;  b, g, w, z [B, H, T, d] out_dtype -- each
  *              output may be NULL, and that gate is then not computed
  *   workspace  >= gdr_gate_proj_workspace_size() bytes, 256-byte aligned
- * Every pointer 16-byte aligned.  Invalid sizes, null required pointers or
- * misalignment: GDR_ERR_INVALID_ARG; a rank above 128 or d not 64 / 128:
+ * Every pointer 16-byte aligned.  Invalid sizes (including B*T*H >= 2^31),
+ * null required pointers or misalignment: GDR_ERR_INVALID_ARG; a rank above
+ * 128 or d not 64 / 128:
  * GDR_ERR_UNSUPPORTED; all checked on the host before any launch.
  */
 gdr_status gdr_gate_proj(const gdr_gate_desc *desc, const void *x, const void *w_down,

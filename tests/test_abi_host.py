@@ -232,6 +232,7 @@ def test_gate_proj_workspace_and_validation():
     assert _gate_ws(d=96)[0] == gdr.GDR_ERR_UNSUPPORTED
     assert _gate_ws(H=0)[0] == gdr.GDR_ERR_INVALID_ARG
     assert _gate_ws(T=0) == (gdr.GDR_OK, 0)
+    assert _gate_ws(T=1 << 29)[0] == gdr.GDR_ERR_INVALID_ARG             # B T H >= 2^31 (row index)
     desc = gdr.make_gate_desc(2, 100, 256, 2, 128, (64, 64, 128, 128, 128))
     c = lambda x: None if x is None else ctypes.c_void_p(x)
     call = lambda x, wd, wu, ws, nb: gdr.load().gdr_gate_proj(
