@@ -4,11 +4,12 @@
 A step is one chunkwise forward (gdr_chunk_fwd: intra-chunk, chain and
 output kernels, in segments of chunks) over the long-context stress
 workload: B1 H16 T32768 dk=dv=128, bf16 inputs, fp32 output and state, chunk
-128 (default) -- inputs resident in HBM before the timed region.  The decode
-step (256 sequences x 16 heads, fp32 128 x 128 states, 1024 consecutive
-steps) and the same long-context shape with scalar gates (one decay and one
-beta per token, Gated DeltaNet) are timed in the same run and reported
-beside it.
+128 (default) -- inputs resident in HBM before the timed region.  Timed in
+the same run and reported beside it: the decode step (256 sequences x 16
+heads, fp32 128 x 128 states, 1024 consecutive steps), the same long-context
+shape with scalar gates (one decay and one beta per token, Gated DeltaNet),
+and the layer path around the recurrence (the five-gate low-rank projection,
+then the forward with the fused RMSNorm + output gate).
 
 Prints one JSON line.  Per-kernel durations come from HIP events recorded on
 the stream the kernels run on; the roofline object describes the kernel with
@@ -37,8 +38,8 @@ METRIC = "tokens/s + % bf16 MFMA peak, chunk fwd T=32K H=16 d=128; decode HBM GB
 # Valid only for the kernel sources they were taken on (digest below);
 # otherwise reported as null.
 MEASURED_TRAFFIC = {
-    "sources": "52f2f128d1e8d8f6",
-    "chunk_intra_kernel_C128": 2148668292,
+    "sources": "4b53c19c50a13701",
+    "chunk_intra_kernel_C128": 2149481371,
 }
 
 
@@ -132,6 +133,63 @@ def timed_decode(wl, steps, warmup):
     return wall, per
 
 
+def timed_layer(x, C, steps, warmup):
+    """The layer path around the recurrence at the long-context shape: the
+    five-gate projection (d_model 2048, ranks 64/64/128/128/128, 16 heads of
+    128, bf16 gates, fp32 log-decay) of a [1, 32768, 2048] bf16 input, then
+    the chunkwise forward with the fused RMSNorm + output gate on the
+    stress workload's q, k, v and those gates.  Random-init weights; the
+    decay gate's bias is +4 (alpha ~ 0.98 per token).  HIP events on the
+    stream the kernels run on, median over `steps`."""
+    import torch
+
+    from channel_wise_gated_amd import gdr
+    B, H, T, d = 1, 16, x["q"].shape[2], 128
+    dm, ranks = 2048, (64, 64, 128, 128, 128)
+    R = sum(ranks)
+    gen = torch.Generator(device="cuda").manual_seed(20251)
+    rn = lambda *s: torch.randn(*s, generator=gen, device="cuda")
+    xin = rn(B, T, dm).to(torch.bfloat16)
+    wd = (rn(R, dm) / dm ** 0.5).to(torch.bfloat16)
+    wu = gdr.pack_gate_up({n: (rn(H * d, r) / r ** 0.5).to(torch.bfloat16) for n, r in zip(gdr.GATE_ORDER, ranks)})
+    bias = 0.5 * rn(5, H * d)
+    bias[0] += 4.0
+    gates = gdr.gdr_gate_proj(xin, wd, wu, bias, ranks, H, d)
+    gws = torch.empty(B * T * R * 4, dtype=torch.uint8, device="cuda")
+    nw = 1.0 + 0.1 * rn(H, d)
+    y = torch.empty(B, T, H, d, device="cuda")
+    sT = torch.empty(B, H, d, d, device="cuda")
+    probe = gdr.ChunkCall(x["q"], x["k"], x["v"], gates["f"], gates["b"], gates["w"], x["gamma"], gates["q"],
+                          x["S0"], chunk=C)
+    cws = probe.workspace
+    proj = lambda: gdr.gdr_gate_proj(xin, wd, wu, bias, ranks, H, d, outs=gates, workspace=gws)
+    gated = lambda: gdr.gdr_chunk_fwd_gated(x["q"], x["k"], x["v"], gates["f"], gates["b"], gates["w"], gates["g"],
+                                            gamma=x["gamma"], z=gates["q"], S0=x["S0"], norm_weight=nw,
+                                            chunk=C, y=y, S_T=sT, workspace=cws)
+    for _ in range(warmup):
+        proj()
+        gated()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for e in ev:
+        e[0].record()
+        proj()
+        e[1].record()
+        gated()
+        e[2].record()
+    torch.cuda.synchronize()
+    med = lambda a: sorted(a)[len(a) // 2]
+    p_ms = med([e[0].elapsed_time(e[1]) for e in ev])
+    g_ms = med([e[1].elapsed_time(e[2]) for e in ev])
+    # algorithmic HBM bytes of the projection: x in, five gate tensors out
+    p_bytes = B * T * dm * 2 + B * T * H * d * (4 + 4 * 2)
+    return {"workload": f"layer B{B} T{T} d_model {dm} ranks {'/'.join(map(str, ranks))} H{H} d{d} chunk{C}",
+            "steps": steps, "gate_proj_ms": round(p_ms, 4), "gated_chunk_fwd_ms": round(g_ms, 4),
+            "layer_tokens_s": round(B * T / ((p_ms + g_ms) / 1e3), 1),
+            "gate_proj_hbm_gbs": round(p_bytes / (p_ms / 1e3) / 1e9, 1),
+            "gate_proj_bytes": p_bytes}
+
+
 def copy_calibration(mib):
     """A plain device-to-device copy of `mib` MiB (fp32), three times: the
     reference dispatch against which HBM byte counters are scaled."""
@@ -182,6 +240,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1024, help="0 skips the decode leg")
     ap.add_argument("--gdn-steps", type=int, default=20,
                     help="whole calls of the scalar-gate (Gated DeltaNet) leg; 0 skips it")
+    ap.add_argument("--layer-steps", type=int, default=20,
+                    help="steps of the gate projection + gated forward leg; 0 skips it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="also run a plain MIB-MiB copy (reference for HBM byte counters)")
@@ -251,6 +311,11 @@ def main():
         g_ms = 1e3 * (time.perf_counter() - t0) / gsteps
         del callg, xg
 
+    # layer: gate projection + gated chunk forward on the stress inputs
+    if args.layer_steps > 0:
+        layer = timed_layer(x, C, args.layer_steps, min(args.warmup, 5))
+        torch.cuda.empty_cache()
+
     # decode
     dwl = WORKLOADS["decode"]
     dsteps = args.decode_steps
@@ -279,6 +344,8 @@ def main():
                                    "one decay and one beta per token (b = w)",
                        "steps": gsteps, "ms_per_step": round(g_ms, 4),
                        "tokens_s": round(gwl.B * gwl.T / (g_ms / 1e3), 1)}
+    if args.layer_steps > 0:
+        line["layer"] = layer
     if dsteps > 0:
         line["decode"] = {"workload": f"decode {dwl.B} seq x H{dwl.H}, fp32 state {dwl.dk}x{dwl.dv}, "
                                       f"{dsteps} steps", "us_per_step": round(d_us, 2),
