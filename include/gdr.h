@@ -170,8 +170,8 @@ gdr_status gdr_gate_proj_workspace_size(const gdr_gate_desc *desc, size_t *bytes
  *   workspace  >= gdr_gate_proj_workspace_size() bytes, 256-byte aligned
  * Every pointer 16-byte aligned.  Invalid sizes (including B*T*H >= 2^31),
  * null required pointers or misalignment: GDR_ERR_INVALID_ARG; a rank above
- * 128 or d not 64 / 128:
- * GDR_ERR_UNSUPPORTED; all checked on the host before any launch.
+ * 128 or d not 64 / 128: GDR_ERR_UNSUPPORTED; all checked on the host before
+ * any launch.
  */
 gdr_status gdr_gate_proj(const gdr_gate_desc *desc, const void *x, const void *w_down,
                          const void *w_up, const float *bias, float *log_alpha, void *b,
