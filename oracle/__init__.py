@@ -7,7 +7,7 @@ seeded input generator (``channel_wise_gated_amd.inputs``), which holds none of
 the method's arithmetic.
 
 The arithmetic lives in ``gdr_oracle.c`` (plain C, double precision, a token
-loop per (batch, head) stream).  This wrapper only broadcasts gate arguments to
+loop per (batch, head) stream, forward and its reverse-mode backward).  This wrapper only broadcasts gate arguments to
 full per-channel fp64 arrays and marshals pointers.  The method it follows is
 stated in the C file's header: Muir reading notes (arXiv:2611.08376) section 2.1
 for the GDN-2 update and the read-out gain; the "Kimi3 = GPT2 x 22580" blog,
@@ -41,6 +41,12 @@ def _load():
     lib.gdr_oracle_prepass.restype = None
     lib.gdr_oracle_prepass.argtypes = [
         ctypes.c_int, _dp, _dp, _dp, _dp, ctypes.c_double, ctypes.c_int, _dp, _dp]
+    lib.gdr_oracle_backward.restype = ctypes.c_int
+    lib.gdr_oracle_backward.argtypes = [
+        ctypes.c_long, ctypes.c_long, ctypes.c_int, ctypes.c_int,
+        _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp,
+        ctypes.c_double, ctypes.c_int, _dp, _dp, _dp,
+        _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, ctypes.c_int]
     lib.gdr_oracle_max_threads.restype = ctypes.c_int
     lib.gdr_oracle_max_threads.argtypes = []
     _lib = lib
@@ -131,6 +137,72 @@ def forward(q, k, v, log_alpha, b, w, gamma=None, z=None, S0=None,
     if rc != 0:
         raise MemoryError("oracle could not allocate its per-stream scratch")
     return o, sT
+
+
+def _gate_grad(g, full, name):
+    """Reduce a per-channel gradient ``full`` [B, H, T, d] to the shape of the
+    gate argument ``g``: per-token gates sum over the channels, constant
+    (scalar) gates have no gradient (None)."""
+    if np.isscalar(g):
+        return None
+    shape = np.shape(g)
+    if len(shape) == 3:
+        return full.sum(axis=-1)
+    return full
+
+
+def backward(q, k, v, log_alpha, b, w, dO, gamma=None, z=None, S0=None, dS_T=None,
+             scale=1.0, normalize_qk=True, threads=None):
+    """Reverse-mode derivatives of ``forward`` in fp64 for the loss
+    <dO, o> + <dS_T, S_T> (dS_T None = 0).
+
+    Arguments as ``forward``, plus dO [B, H, T, dv] and dS_T [B, H, dk, dv].
+    Returns a dict with dq, dk, dv [like q, k, v]; dlog_alpha, db, dw shaped
+    like their gate argument (per-token gates summed over the channels; None
+    for a constant gate); dgamma [H, dk] (summed over batch and tokens; None
+    without gamma); dz [B, H, T, dk] (None without z); dS0 [B, H, dk, dv].
+    """
+    lib = _load()
+    qf, kf, vf = _f64(q), _f64(k), _f64(v)
+    B, H, T, dk = qf.shape
+    dv = vf.shape[3]
+    la = _gate(log_alpha, (B, H, T, dk), "log_alpha")
+    bb = _gate(b, (B, H, T, dk), "b")
+    ww = _gate(w, (B, H, T, dv), "w")
+    g = None
+    if gamma is not None:
+        g = _f64(gamma)
+        if g.shape != (H, dk):
+            raise ValueError("gamma must be [H, dk]")
+        g = np.ascontiguousarray(np.broadcast_to(g[None], (B, H, dk)))
+    zz = _f64(z)
+    s0 = _f64(S0)
+    do = _f64(dO)
+    if do.shape != (B, H, T, dv):
+        raise ValueError("dO must be [B, H, T, dv]")
+    dst = _f64(dS_T)
+    out = {n: np.empty((B, H, T, dk)) for n in ("dq", "dk", "dlog_alpha", "db", "dz")}
+    out["dv"] = np.empty((B, H, T, dv))
+    out["dw"] = np.empty((B, H, T, dv))
+    out["dgamma"] = np.empty((B, H, dk))
+    out["dS0"] = np.empty((B, H, dk, dv))
+    n = B * H
+    if threads is None:
+        threads = default_threads(n)
+    rc = lib.gdr_oracle_backward(n, T, dk, dv, _ptr(qf), _ptr(kf), _ptr(vf), _ptr(la), _ptr(bb), _ptr(ww),
+                                 _ptr(g), _ptr(zz), float(scale), int(bool(normalize_qk)), _ptr(s0),
+                                 _ptr(do), _ptr(dst), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                                 _ptr(out["dlog_alpha"]), _ptr(out["db"]), _ptr(out["dw"]),
+                                 _ptr(out["dgamma"]), _ptr(out["dz"]), _ptr(out["dS0"]), int(threads))
+    if rc != 0:
+        raise MemoryError("oracle could not allocate its per-stream scratch")
+    out["dlog_alpha"] = _gate_grad(log_alpha, out["dlog_alpha"], "log_alpha")
+    out["db"] = _gate_grad(b, out["db"], "b")
+    out["dw"] = _gate_grad(w, out["dw"], "w")
+    out["dgamma"] = out["dgamma"].sum(axis=0) if gamma is not None else None
+    if z is None:
+        out["dz"] = None
+    return out
 
 
 def prepass(q, k, gamma=None, z=None, scale=1.0, normalize_qk=True):

@@ -43,7 +43,10 @@
  * independent formula, brute-force products of the explicit transition
  * matrices, a dense solve of the whole-sequence triangular system, exact
  * recall, alpha -> 0 clearing, linearity, split/resume and the write/erase
- * sensitivity identity.
+ * sensitivity identity.  The backward (gdr_oracle_backward, reverse mode of
+ * the same token loop) is pinned by central differences of the forward for
+ * every input and gate mode, by split/resume across its checkpoints, and by
+ * the closed form of linear attention.
  */
 #include <math.h>
 #include <stddef.h>
@@ -167,6 +170,237 @@ int gdr_oracle_forward(long n_streams, long T, int dk, int dv,
     free(kh);
     free(vh);
     free(u);
+  }
+  return failed ? -1 : 0;
+}
+
+/* ------------------------------------------------------------------------
+ * Backward pass: reverse-mode derivatives of the recurrence above, token by
+ * token in fp64, for the loss  <dO, o> + <dS_T, S_T>  (the gradients a caller
+ * gets when dO and dS_T are the upstream gradients of o and S_T).
+ *
+ * Reverse of one token (dS = gradient of S_t, read after the write):
+ *   dS    += qt^T dO_t                 dqt  = S_t dO_t^T
+ *   du     = kn dS                     dkn  = dS u^T
+ *   dShat  = dS - k_hat^T du           dkh  = -S_hat du^T      dvh = du
+ *   dalpha_i = sum_j dShat_ij S_{t-1,ij}
+ *   dS_{t-1} = Diag(alpha) dShat
+ * then the elementwise chains: dlog_alpha = dalpha * alpha, db = dkh * kn,
+ * dkn += dkh * b, dw = dvh * v, dv = dvh * w, the read-out gain
+ * (d 2 sigma(z) / dz = 2 sigma (1 - sigma)), and SiLU + l2 normalisation
+ * (d(s / |s|) = (ds - y (y . ds)) / |s|; below the 1e-12 floor, ds / 1e-12).
+ * The states S_{t-1} are recomputed from checkpoints every 64 tokens.
+ * ------------------------------------------------------------------------ */
+
+static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+/* dy -> dx through y = SiLU(x) / max(|SiLU(x)|, 1e-12) (or y = x). */
+static void silu_l2_bwd(const double *x, int d, int normalize, const double *dy, double *dx) {
+  int j;
+  double ss = 0.0, nrm, dot = 0.0;
+  if (!normalize) {
+    for (j = 0; j < d; ++j) dx[j] = dy[j];
+    return;
+  }
+  for (j = 0; j < d; ++j) {
+    double sj = silu(x[j]);
+    ss += sj * sj;
+  }
+  nrm = sqrt(ss);
+  if (nrm > 1e-12) {
+    for (j = 0; j < d; ++j) dot += (silu(x[j]) / nrm) * dy[j];
+    for (j = 0; j < d; ++j) dx[j] = (dy[j] - (silu(x[j]) / nrm) * dot) / nrm;
+  } else {
+    for (j = 0; j < d; ++j) dx[j] = dy[j] / 1e-12;
+  }
+  for (j = 0; j < d; ++j) {
+    double sg = sigmoid(x[j]);
+    dx[j] *= sg * (1.0 + x[j] * (1.0 - sg));  /* SiLU'(x) */
+  }
+}
+
+#define GDR_ORACLE_CKPT 64
+
+/*
+ * Arguments as gdr_oracle_forward, plus
+ *   dO   [n_streams, T, dv]; dS_T [n_streams, dk, dv] or NULL (= 0)
+ * and the gradients (all written; each may be NULL if not wanted):
+ *   dq, dk_, dlog_alpha, db, dz : [n_streams, T, dk]
+ *   dv_, dw                     : [n_streams, T, dv]
+ *   dgamma                      : [n_streams, dk]   (summed over the stream's tokens)
+ *   dS0                         : [n_streams, dk, dv]
+ * Returns 0, or -1 when scratch memory cannot be allocated.
+ */
+int gdr_oracle_backward(long n_streams, long T, int dk, int dv,
+                        const double *q, const double *k, const double *v,
+                        const double *log_alpha, const double *b,
+                        const double *w, const double *gamma, const double *z,
+                        double scale, int normalize_qk, const double *S0,
+                        const double *dO, const double *dS_T,
+                        double *dq, double *dk_, double *dv_, double *dlog_alpha,
+                        double *db, double *dw, double *dgamma, double *dz,
+                        double *dS0, int n_threads) {
+  long n;
+  int failed = 0;
+  const size_t DD = (size_t)dk * dv;
+  const long nck = (T + GDR_ORACLE_CKPT - 1) / GDR_ORACLE_CKPT;
+  if (n_threads < 1) n_threads = 1;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(n_threads) reduction(|| : failed)
+  for (n = 0; n < n_streams; ++n) {
+    /* checkpoints: state before token c * CKPT; seg: states before each token
+       of one segment and after its last */
+    double *ck = (double *)malloc(sizeof(double) * DD * (size_t)(nck > 0 ? nck : 1));
+    double *seg = (double *)malloc(sizeof(double) * DD * (GDR_ORACLE_CKPT + 1));
+    double *dS = (double *)malloc(sizeof(double) * DD);
+    double *Sh = (double *)malloc(sizeof(double) * DD);
+    double *vec = (double *)malloc(sizeof(double) * (size_t)(16 * dk + 8 * dv));
+    double *gsum = (double *)calloc((size_t)dk, sizeof(double));
+    long t, c;
+    int i, j;
+    if (!ck || !seg || !dS || !Sh || !vec || !gsum) {
+      failed = 1;
+    } else {
+      double *qh = vec, *qt = vec + dk, *kn = vec + 2 * dk, *kh = vec + 3 * dk;
+      double *gain = vec + 4 * dk, *al = vec + 5 * dk, *dqt = vec + 6 * dk;
+      double *dkn = vec + 7 * dk, *dkh = vec + 8 * dk, *dal = vec + 9 * dk;
+      double *dqh = vec + 10 * dk, *tmp = vec + 11 * dk;
+      double *vh = vec + 16 * dk, *u = vh + dv, *du = vh + 2 * dv;
+      const double *gam = gamma ? gamma + (size_t)n * dk : NULL;
+      /* token t's pre-pass values (qh, qt, gain, kn, kh, vh, alpha) */
+#define GDR_TOKEN(t_)                                                         \
+  do {                                                                        \
+    size_t rk_ = ((size_t)n * T + (t_)) * dk, rv_ = ((size_t)n * T + (t_)) * dv; \
+    silu_l2(q + rk_, dk, normalize_qk, qh);                                   \
+    silu_l2(k + rk_, dk, normalize_qk, kn);                                   \
+    for (i = 0; i < dk; ++i) {                                                \
+      gain[i] = scale * (gam ? gam[i] : 1.0) * (z ? two_sigmoid(z[rk_ + i]) : 1.0); \
+      qt[i] = gain[i] * qh[i];                                                \
+      kh[i] = b[rk_ + i] * kn[i];                                             \
+      al[i] = exp(log_alpha[rk_ + i]);                                        \
+    }                                                                         \
+    for (j = 0; j < dv; ++j) vh[j] = w[rv_ + j] * v[rv_ + j];                 \
+  } while (0)
+      /* one forward token step: Snew from Sold (both [dk, dv]) */
+#define GDR_STEP(Sold, Snew)                                                  \
+  do {                                                                        \
+    for (i = 0; i < dk; ++i)                                                  \
+      for (j = 0; j < dv; ++j) Sh[(size_t)i * dv + j] = al[i] * (Sold)[(size_t)i * dv + j]; \
+    for (j = 0; j < dv; ++j) {                                                \
+      double r_ = 0.0;                                                        \
+      for (i = 0; i < dk; ++i) r_ += kh[i] * Sh[(size_t)i * dv + j];          \
+      u[j] = vh[j] - r_;                                                      \
+    }                                                                         \
+    for (i = 0; i < dk; ++i)                                                  \
+      for (j = 0; j < dv; ++j) (Snew)[(size_t)i * dv + j] = Sh[(size_t)i * dv + j] + kn[i] * u[j]; \
+  } while (0)
+      /* forward: checkpoints */
+      if (S0)
+        memcpy(seg, S0 + (size_t)n * DD, sizeof(double) * DD);
+      else
+        memset(seg, 0, sizeof(double) * DD);
+      for (t = 0; t < T; ++t) {
+        if (t % GDR_ORACLE_CKPT == 0) memcpy(ck + (size_t)(t / GDR_ORACLE_CKPT) * DD, seg, sizeof(double) * DD);
+        GDR_TOKEN(t);
+        GDR_STEP(seg, seg + DD);
+        memcpy(seg, seg + DD, sizeof(double) * DD);
+      }
+      /* backward */
+      if (dS_T)
+        memcpy(dS, dS_T + (size_t)n * DD, sizeof(double) * DD);
+      else
+        memset(dS, 0, sizeof(double) * DD);
+      for (c = nck - 1; c >= 0; --c) {
+        long t0 = c * GDR_ORACLE_CKPT, t1 = t0 + GDR_ORACLE_CKPT < T ? t0 + GDR_ORACLE_CKPT : T;
+        memcpy(seg, ck + (size_t)c * DD, sizeof(double) * DD);
+        for (t = t0; t < t1; ++t) {
+          GDR_TOKEN(t);
+          GDR_STEP(seg + (size_t)(t - t0) * DD, seg + (size_t)(t - t0 + 1) * DD);
+        }
+        for (t = t1 - 1; t >= t0; --t) {
+          const double *Sp = seg + (size_t)(t - t0) * DD;    /* S_{t-1} */
+          const double *St = Sp + DD;                        /* S_t */
+          size_t rk = ((size_t)n * T + t) * dk, rv = ((size_t)n * T + t) * dv;
+          GDR_TOKEN(t);
+          for (i = 0; i < dk; ++i)
+            for (j = 0; j < dv; ++j) Sh[(size_t)i * dv + j] = al[i] * Sp[(size_t)i * dv + j];
+          for (j = 0; j < dv; ++j) { /* u */
+            double r = 0.0;
+            for (i = 0; i < dk; ++i) r += kh[i] * Sh[(size_t)i * dv + j];
+            u[j] = vh[j] - r;
+          }
+          /* o_t = qt S_t */
+          for (i = 0; i < dk; ++i) {
+            double a = 0.0;
+            for (j = 0; j < dv; ++j) a += St[(size_t)i * dv + j] * dO[rv + j];
+            dqt[i] = a;
+            for (j = 0; j < dv; ++j) dS[(size_t)i * dv + j] += qt[i] * dO[rv + j];
+          }
+          /* S_t = S_hat + kn^T u */
+          for (j = 0; j < dv; ++j) {
+            double a = 0.0;
+            for (i = 0; i < dk; ++i) a += kn[i] * dS[(size_t)i * dv + j];
+            du[j] = a;
+          }
+          for (i = 0; i < dk; ++i) {
+            double a = 0.0;
+            for (j = 0; j < dv; ++j) a += dS[(size_t)i * dv + j] * u[j];
+            dkn[i] = a;
+          }
+          /* u = v_hat - k_hat S_hat */
+          for (i = 0; i < dk; ++i) {
+            double a = 0.0;
+            for (j = 0; j < dv; ++j) {
+              a += Sh[(size_t)i * dv + j] * du[j];
+              dS[(size_t)i * dv + j] -= kh[i] * du[j]; /* now dS_hat */
+            }
+            dkh[i] = -a;
+          }
+          /* S_hat = Diag(alpha) S_{t-1} */
+          for (i = 0; i < dk; ++i) {
+            double a = 0.0;
+            for (j = 0; j < dv; ++j) {
+              a += dS[(size_t)i * dv + j] * Sp[(size_t)i * dv + j];
+              dS[(size_t)i * dv + j] *= al[i];
+            }
+            dal[i] = a;
+          }
+          /* elementwise chains */
+          for (i = 0; i < dk; ++i) {
+            if (dlog_alpha) dlog_alpha[rk + i] = dal[i] * al[i];
+            if (db) db[rk + i] = dkh[i] * kn[i];
+            dkn[i] += dkh[i] * b[rk + i];
+            dqh[i] = dqt[i] * gain[i];
+            gsum[i] += dqt[i] * qh[i] * scale * (z ? two_sigmoid(z[rk + i]) : 1.0);
+            if (dz) {
+              double sg = sigmoid(z ? z[rk + i] : 0.0);
+              dz[rk + i] = z ? dqt[i] * qh[i] * scale * (gam ? gam[i] : 1.0) * 2.0 * sg * (1.0 - sg) : 0.0;
+            }
+          }
+          for (j = 0; j < dv; ++j) {
+            if (dw) dw[rv + j] = du[j] * v[rv + j];
+            if (dv_) dv_[rv + j] = du[j] * w[rv + j];
+          }
+          if (dq) {
+            silu_l2_bwd(q + rk, dk, normalize_qk, dqh, tmp);
+            for (i = 0; i < dk; ++i) dq[rk + i] = tmp[i];
+          }
+          if (dk_) {
+            silu_l2_bwd(k + rk, dk, normalize_qk, dkn, tmp);
+            for (i = 0; i < dk; ++i) dk_[rk + i] = tmp[i];
+          }
+        }
+      }
+      if (dS0) memcpy(dS0 + (size_t)n * DD, dS, sizeof(double) * DD);
+      if (dgamma) memcpy(dgamma + (size_t)n * dk, gsum, sizeof(double) * dk);
+#undef GDR_TOKEN
+#undef GDR_STEP
+    }
+    free(ck);
+    free(seg);
+    free(dS);
+    free(Sh);
+    free(vec);
+    free(gsum);
   }
   return failed ? -1 : 0;
 }

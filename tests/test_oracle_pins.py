@@ -613,3 +613,111 @@ def test_gate_proj_layout(oracle_mod):
     mask = np.ones((H, d), dtype=bool)
     mask[1, 2] = False
     assert np.all(out["q"].transpose(0, 2, 1, 3)[:, :, mask] == 0.0)
+
+
+# ----------------------------------------------------------------------------
+# backward (reverse-mode derivatives of the same recurrence for the loss
+# <dO, o> + <dS_T, S_T>): pinned to the forward oracle by central differences,
+# to itself across a split sequence, and to a closed form
+# ----------------------------------------------------------------------------
+
+def _bwd_problem(seed, B=1, H=2, T=9, d=4, per_token=False, gain=True):
+    r = np.random.default_rng(seed)
+    sig = lambda x: 1.0 / (1.0 + np.exp(-x))
+    gshape = (B, H, T) if per_token else (B, H, T, d)
+    p = dict(q=r.standard_normal((B, H, T, d)), k=r.standard_normal((B, H, T, d)),
+             v=r.standard_normal((B, H, T, d)), log_alpha=-0.3 * r.random(gshape),
+             b=2.0 * sig(r.standard_normal(gshape)), w=sig(r.standard_normal(gshape)),
+             S0=r.standard_normal((B, H, d, d)))
+    if gain:
+        p["gamma"] = 1.0 + 0.1 * r.standard_normal((H, d))
+        p["z"] = r.standard_normal((B, H, T, d))
+    dO = r.standard_normal((B, H, T, d))
+    dST = r.standard_normal((B, H, d, d))
+    return p, dO, dST
+
+
+def _loss(oracle_mod, p, dO, dST, **kw):
+    o, sT = oracle_mod.forward(**p, **kw)
+    return float((o * dO).sum() + (sT * dST).sum())
+
+
+def _fd_check(oracle_mod, p, dO, dST, grads, names, n_samples, seed, **kw):
+    r = np.random.default_rng(seed)
+    key = {"q": "dq", "k": "dk", "v": "dv", "log_alpha": "dlog_alpha", "b": "db", "w": "dw",
+           "z": "dz", "S0": "dS0", "gamma": "dgamma"}
+    h = 1e-6
+    for name in names:
+        arr = p[name]
+        flat = [tuple(ix) for ix in np.ndindex(arr.shape)]
+        picks = flat if len(flat) <= n_samples else [flat[i] for i in r.choice(len(flat), n_samples, replace=False)]
+        for ix in picks:
+            ap, am = arr.copy(), arr.copy()
+            ap[ix] += h
+            am[ix] -= h
+            num = (_loss(oracle_mod, {**p, name: ap}, dO, dST, **kw) -
+                   _loss(oracle_mod, {**p, name: am}, dO, dST, **kw)) / (2 * h)
+            got = grads[key[name]][ix]
+            assert abs(got - num) <= 1e-6 * (1.0 + abs(num)), (name, ix, got, num)
+
+
+ALL_INPUTS = ("q", "k", "v", "log_alpha", "b", "w", "z", "S0", "gamma")
+
+
+def test_backward_matches_central_differences(oracle_mod):
+    p, dO, dST = _bwd_problem(21)
+    g = oracle_mod.backward(**p, dO=dO, dS_T=dST)
+    _fd_check(oracle_mod, p, dO, dST, g, ALL_INPUTS, 24, 1)
+
+
+def test_backward_per_token_gates_scale_and_no_normalisation(oracle_mod):
+    p, dO, dST = _bwd_problem(22, per_token=True)
+    g = oracle_mod.backward(**p, dO=dO, dS_T=dST)
+    assert g["db"].shape == (1, 2, 9) and g["dlog_alpha"].shape == (1, 2, 9)
+    _fd_check(oracle_mod, p, dO, dST, g, ("log_alpha", "b", "w", "q", "k"), 18, 2)
+    p2, dO2, dST2 = _bwd_problem(23, gain=False)
+    g2 = oracle_mod.backward(**p2, dO=dO2, dS_T=dST2, scale=0.7, normalize_qk=False)
+    assert g2["dz"] is None and g2["dgamma"] is None
+    _fd_check(oracle_mod, p2, dO2, dST2, g2, ("q", "k", "v", "log_alpha", "S0"), 18, 3,
+              scale=0.7, normalize_qk=False)
+
+
+def test_backward_constant_gates_have_no_gradient(oracle_mod):
+    p, dO, dST = _bwd_problem(24, gain=False)
+    p.update(log_alpha=0.0, b=0.0, w=1.0)
+    g = oracle_mod.backward(**p, dO=dO, dS_T=dST)
+    assert g["dlog_alpha"] is None and g["db"] is None and g["dw"] is None
+    _fd_check(oracle_mod, p, dO, dST, g, ("q", "k", "v", "S0"), 12, 4)
+
+
+def test_backward_split_resume_across_checkpoints(oracle_mod):
+    """Gradients of a 150-token sequence (three checkpoint segments) equal the
+    backward of its last 61 tokens, from the state the first 89 leave, whose
+    dS0 is then fed as dS_T to the backward of the first 89."""
+    p, dO, dST = _bwd_problem(25, T=150, d=6)
+    full = oracle_mod.backward(**p, dO=dO, dS_T=dST)
+    cut = 89
+    head = {n: (a[:, :, :cut] if n not in ("S0", "gamma") else a) for n, a in p.items()}
+    tail = {n: (a[:, :, cut:] if n not in ("S0", "gamma") else a) for n, a in p.items()}
+    _, s_cut = oracle_mod.forward(**head)
+    tail["S0"] = s_cut
+    gt = oracle_mod.backward(**tail, dO=dO[:, :, cut:], dS_T=dST)
+    gh = oracle_mod.backward(**head, dO=dO[:, :, :cut], dS_T=gt["dS0"])
+    for n in ("dq", "dk", "dv", "dlog_alpha", "db", "dw", "dz"):
+        np.testing.assert_allclose(np.concatenate([gh[n], gt[n]], axis=2), full[n], rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(gh["dS0"], full["dS0"], rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(gh["dgamma"] + gt["dgamma"], full["dgamma"], rtol=1e-9, atol=1e-11)
+
+
+def test_backward_linear_attention_closed_form(oracle_mod):
+    """b = 0, alpha = w = 1, no normalisation: o_t = sum_{s<=t} (q_t . k_s) v_s,
+    so dv_s = sum_{t>=s} (q_t . k_s) dO_t and dq_t = sum_{s<=t} (dO_t . v_s) k_s."""
+    r = np.random.default_rng(26)
+    B, H, T, d = 1, 1, 12, 5
+    q, k, v = (r.standard_normal((B, H, T, d)) for _ in range(3))
+    dO = r.standard_normal((B, H, T, d))
+    g = oracle_mod.backward(q, k, v, 0.0, 0.0, 1.0, dO, normalize_qk=False)
+    qk = q[0, 0] @ k[0, 0].T                      # [t, s]
+    mask = np.tril(np.ones((T, T)))
+    np.testing.assert_allclose(g["dv"][0, 0], (qk * mask).T @ dO[0, 0], rtol=1e-12)
+    np.testing.assert_allclose(g["dq"][0, 0], ((dO[0, 0] @ v[0, 0].T) * mask) @ k[0, 0], rtol=1e-12)
