@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgdr.so")
-SOURCES = ["gdr_abi.hip", "gdr_decode.hip", "gdr_chunk.hip", "gdr_gate.hip"]
+SOURCES = ["gdr_abi.hip", "gdr_decode.hip", "gdr_chunk.hip", "gdr_gate.hip", "gdr_bwd.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Wno-unused-function", "-Wno-unknown-pragmas",

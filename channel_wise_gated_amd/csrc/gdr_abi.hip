@@ -116,6 +116,7 @@ gdr_status chunk_call(const gdr_desc *desc, int nseq, const int *cu, const void 
   a.nseq = nseq;
   a.c0 = 0;  // the chunk range of each launch is set by launch_chunk
   a.ncs = 0;
+  a.rev = 0;
   a.og = og ? og->g : nullptr;
   a.onw = og ? og->norm_w : nullptr;
   a.oeps = og ? og->eps : 0.f;
@@ -146,9 +147,103 @@ gdr_status gate_plan(const gdr_gate_desc *d, size_t *ws, int *R) {
   return GDR_OK;
 }
 
+// The backward: validation as the forward (its chunk size is its own, 64) and
+// the workspace (the forward's chunk maps, the reverse chain's buffers and
+// per-chunk scratch).
+gdr_status bwd_plan(const gdr_desc *d, size_t *ws) {
+  if (!d) return GDR_ERR_INVALID_ARG;
+  gdr_desc fd = *d;
+  fd.chunk = 64;
+  size_t fws = 0;
+  gdr_status s = chunk_plan(&fd, 0, &fws);
+  if (s != GDR_OK) return s;
+  const int ns = d->in_dtype == GDR_BF16 ? 2 : 3;
+  const long long nch = (long long)d->B * d->H * ((d->T + 63) / 64);
+  if (nch > (1LL << 31) - 1) return GDR_ERR_INVALID_ARG;
+  *ws = nch == 0 ? 0 : gdr::bwd_workspace(nullptr, nullptr, nullptr, d->B, d->H, d->T, d->dk, ns);
+  return GDR_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+gdr_status gdr_chunk_bwd_workspace_size(const gdr_desc *desc, size_t *bytes) {
+  if (!bytes) return GDR_ERR_INVALID_ARG;
+  size_t ws = 0;
+  gdr_status s = bwd_plan(desc, &ws);
+  if (s == GDR_OK) *bytes = ws;
+  return s;
+}
+
+gdr_status gdr_chunk_bwd(const gdr_desc *desc, const void *q, const void *k, const void *v,
+                         const float *log_alpha, const void *b, const void *w, const float *gamma,
+                         const void *z, const float *S0, const void *dO, const float *dS_T, float *dq,
+                         float *dk, float *dv, float *dlog_alpha, float *db, float *dw, float *dgamma,
+                         float *dz, float *dS0, void *workspace, size_t workspace_bytes, void *stream) {
+  size_t need = 0;
+  gdr_status s = bwd_plan(desc, &need);
+  if (s != GDR_OK) return s;
+  const gdr_desc &d = *desc;
+  if ((long long)d.B * d.H == 0) return GDR_OK;
+  if (d.T > 0) {
+    s = check_inputs(desc, q, k, v, log_alpha, b, w, gamma, z, q);
+    if (s != GDR_OK) return s;
+    if (!dO || !aligned16(dO)) return GDR_ERR_INVALID_ARG;
+  }
+  const void *outs[] = {S0, dS_T, dq, dk, dv, dlog_alpha, db, dw, dgamma, dz, dS0};
+  for (const void *p : outs)
+    if (p && !aligned16(p)) return GDR_ERR_INVALID_ARG;
+  if (need > 0 && (!workspace || workspace_bytes < need)) return GDR_ERR_WORKSPACE;
+  if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u)) return GDR_ERR_WORKSPACE;
+
+  const int ns = d.in_dtype == GDR_BF16 ? 2 : 3;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  gdr_desc fd = d;
+  fd.chunk = 64;
+  gdr::ChunkArgs f;
+  f.q = q; f.k = k; f.v = v; f.b = b; f.w = w; f.z = z;
+  f.log_alpha = log_alpha; f.gamma = gamma; f.S0 = S0;
+  f.o = nullptr; f.S_T = nullptr;
+  f.Qp = f.Mm = f.Sc = nullptr; f.Ob = f.Nn = f.Sst = nullptr;
+  f.B = d.B; f.H = d.H; f.T = d.T;
+  f.alpha_mode = d.alpha_mode; f.b_mode = d.b_mode; f.w_mode = d.w_mode;
+  f.normalize_qk = d.normalize_qk; f.scale = d.scale;
+  f.cu = nullptr; f.coff = nullptr; f.ctab = nullptr; f.nseq = 0; f.ctab_len = 0;
+  f.c0 = 0; f.ncs = 0; f.rev = 0;
+  f.og = nullptr; f.onw = nullptr; f.oeps = 0.f; f.y = nullptr;
+  gdr::BwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.b = b; a.w = w; a.z = z; a.dO = dO;
+  a.log_alpha = log_alpha; a.gamma = gamma;
+  a.B = d.B; a.H = d.H; a.T = d.T; a.NC = (d.T + 63) / 64;
+  a.alpha_mode = d.alpha_mode; a.b_mode = d.b_mode; a.w_mode = d.w_mode;
+  a.normalize_qk = d.normalize_qk; a.do_bf16 = d.out_dtype == GDR_BF16; a.scale = d.scale;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dla = dlog_alpha; a.db = db; a.dw = dw;
+  a.dz = z ? dz : nullptr;
+  a.dgamma = gamma ? dgamma : nullptr;
+  hipError_t e = hipSuccess;
+  if (a.NC > 0) {
+    gdr::bwd_workspace(&a, &f, workspace, d.B, d.H, d.T, d.dk, ns);
+    a.Qp = f.Qp; a.Mm = f.Mm; a.Sc = f.Sc;
+    // forward recompute: chunk maps and chunk-start states
+    e = gdr::launch_chunk(fd, f, 1 | 4, st);
+    if (e == hipSuccess) e = gdr::launch_bwd_prep(a, d.dk, ns, st);
+  }
+  if (e == hipSuccess) {
+    // chunk-end state gradients, last chunk to first; the final one is dS0
+    gdr::ChunkArgs r = f;
+    r.Mm = a.NC > 0 ? a.Mt : nullptr;
+    r.Nn = a.NC > 0 ? a.Gn : nullptr;
+    r.Sc = a.NC > 0 ? a.Xc : nullptr;
+    r.S0 = dS_T;
+    r.S_T = dS0;
+    r.rev = 1;
+    if (dS0 || a.NC > 0) e = gdr::launch_chunk(fd, r, 4, st);
+  }
+  if (e == hipSuccess && a.NC > 0) e = gdr::launch_bwd(a, d.dk, ns, st);
+  else if (e == hipSuccess && a.dgamma) e = gdr::launch_bwd(a, d.dk, ns, st);
+  return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
 
 gdr_status gdr_gate_proj_workspace_size(const gdr_gate_desc *desc, size_t *bytes) {
   if (!bytes) return GDR_ERR_INVALID_ARG;

@@ -1,0 +1,737 @@
+// gdr_bwd.hip -- backward pass of the chunkwise forward: reverse-mode
+// derivatives of the GDN-2 recurrence with the read-out gain (Muir reading
+// notes, arXiv:2611.08376, section 2.1), through the chunk system of section
+// 2.4.  For the loss <dO, o> + <dS_T, S_T> it returns the gradients of q, k,
+// v, the gates, gamma, z and S0.
+//
+// Chunks of C = 64 tokens.  With the chunk-start state S0, the gradient X of
+// the chunk-end state, a_t = e^{Lambda_t} (cumulative log-decay inside the
+// chunk), K_a = K_hat (.) a, Q_a = Q_tilde (.) a, K' = K (.) a_C / a and the
+// forward's T = I + L (L strictly lower), A (lower, diagonal included):
+//   U     = T^-1 (V_hat - K_a S0)              (the per-token u of the recurrence)
+//   dU~   = T^-T (A^T dO + K' X)
+//   dA    = dO U^T  (s <= t),   dL = -dU~ U^T  (s < t)
+//   dQ_a  = dO S0^T,  dK_a = -dU~ S0^T,  dK' = U X^T,  dV_hat = dU~
+// and each decayed product L_ts = sum_i k_hat_ti k_si e^{Lambda_ti - Lambda_si}
+// (A_ts likewise with q_tilde) is differentiated pair by pair.  The chunk-end
+// gradients come from a chain over chunks, last to first:
+//   X_{c-1} = M_c^T X_c + Q'_c^T dO_c
+// with M and Q' from the forward's intra-chunk kernel; it runs in the forward
+// chain kernel, with M^T and Q'^T dO in its M and N slots.
+//
+// This first version computes every per-chunk quantity in fp32 on the vector
+// ALU with exact pairwise decays (no pivots), one kernel per stage, with the
+// stages' results in per-chunk scratch of the workspace.
+#include <stdint.h>
+
+#include "gdr_device.h"
+#include "gdr_launch.h"
+
+namespace gdr {
+
+namespace {
+
+constexpr int kBC = 64;  // chunk size of the backward
+
+// Upstream gradient dO (bf16 or fp32, chosen at run time: uniform branch).
+__device__ __forceinline__ float ld_do(const void *p, size_t i, int bf) {
+  return bf ? bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(p)[i]) : reinterpret_cast<const float *>(p)[i];
+}
+
+// Element [i][j] of a D x D state stored by the chain kernel: NS bf16 planes
+// of B-fragments per 16-column slice (row i = 32 ks + 16 h + 4 g + r sits in
+// lane j % 16 + 16 g, element 4 h + r, of fragment ks * NS + p).
+template <int D, int NS>
+__device__ __forceinline__ float state_at(const uint16_t *base, int i, int j) {
+  constexpr int NFR = (D / 32) * NS, FRAG = 512;
+  const int s = j >> 4, l16 = j & 15, ks = i >> 5, h = (i >> 4) & 1, g = (i >> 2) & 3, r = i & 3;
+  const uint16_t *f = base + (size_t)s * NFR * FRAG + (size_t)(ks * NS) * FRAG + (l16 + 16 * g) * 8 + 4 * h + r;
+  float v = 0.f;
+#pragma unroll
+  for (int p = 0; p < NS; ++p) v += bf16_bits_to_f32(f[p * FRAG]);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// K1 prep: per chunk slot, M^T (plane by plane, in M's A-fragment layout) and
+// G = Q'^T dO (in N's accumulator-tile layout) for the reverse chain.
+// ---------------------------------------------------------------------------
+template <int D, int NS>
+__global__ void __launch_bounds__(256) bwd_prep_kernel(BwdArgs a) {
+  constexpr int C = kBC, NKD = D / 32, NMT = D / 16;
+  __shared__ float qs[C][D + 1];
+  __shared__ float ds[C][D + 1];
+  const size_t slot = blockIdx.x;
+  const size_t bh = slot / a.NC;
+  const int c = (int)(slot % a.NC);
+  const int tid = threadIdx.x;
+  const uint16_t *Ms = a.Mm + slot * NS * (size_t)D * D;
+  uint16_t *Mt = a.Mt + slot * NS * (size_t)D * D;
+  for (int idx = tid; idx < D * D; idx += 256) {
+    // destination: fragment (w, ks), lane (l16, g), element e holds M^T[R][Cc]
+    const int e = idx & 7, lane = (idx >> 3) & 63, f = idx >> 9;
+    const int w = f / NKD, ks = f % NKD, l16 = lane & 15, g = lane >> 4;
+    const int R = 16 * w + l16, Cc = 32 * ks + 16 * (e >> 2) + 4 * g + (e & 3);
+    // source: M[Cc][R]
+    const int rr = R & 31;
+    const int src = (((Cc >> 4) * NKD + (R >> 5)) * 64 + (Cc & 15) + 16 * ((rr >> 2) & 3)) * 8 + 4 * (rr >> 4) + (rr & 3);
+#pragma unroll
+    for (int p = 0; p < NS; ++p) Mt[(size_t)p * D * D + idx] = Ms[(size_t)p * D * D + src];
+  }
+  const uint16_t *Qs = a.Qp + slot * NS * (size_t)C * D;
+  for (int idx = tid; idx < C * D; idx += 256) {
+    const int e = idx & 7, lane = (idx >> 3) & 63, f = idx >> 9;
+    const int ti = f / NKD, ks = f % NKD;
+    const int t = 16 * ti + (lane & 15), ch = 32 * ks + 16 * (e >> 2) + 4 * (lane >> 4) + (e & 3);
+    float v = 0.f;
+#pragma unroll
+    for (int p = 0; p < NS; ++p) v += bf16_bits_to_f32(Qs[(size_t)p * C * D + idx]);
+    qs[t][ch] = v;
+  }
+  for (int idx = tid; idx < C * D; idx += 256) {
+    const int t = idx / D, j = idx % D, tt = c * C + t;
+    ds[t][j] = tt < a.T ? ld_do(a.dO, (bh * a.T + tt) * D + j, a.do_bf16) : 0.f;
+  }
+  __syncthreads();
+  constexpr int TPR = 256 / D;       // threads per row i
+  constexpr int JN = D / TPR;        // columns per thread
+  const int i = tid % D, j0 = (tid / D) * JN;
+  float acc[JN];
+#pragma unroll
+  for (int jj = 0; jj < JN; ++jj) acc[jj] = 0.f;
+  for (int t = 0; t < C; ++t) {
+    const float qv = qs[t][i];
+#pragma unroll
+    for (int jj = 0; jj < JN; ++jj) acc[jj] += qv * ds[t][j0 + jj];
+  }
+  float *G = a.Gn + slot * (size_t)D * D;
+  const int w = i >> 4, g = (i & 15) >> 2, r = i & 3;
+#pragma unroll
+  for (int jj = 0; jj < JN; ++jj) {
+    const int j = j0 + jj;
+    G[((size_t)(w * NMT + (j >> 4)) * 64 + (j & 15) + 16 * g) * 4 + r] = acc[jj];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K3 pre-pass: per chunk slot (4 waves x 16 tokens, lanes over channels), the
+// forward's per-token vectors: kn, k_hat, q_tilde, v_hat and the cumulative
+// log-decay Lambda.  Padding tokens past T are zero (identity steps).
+// ---------------------------------------------------------------------------
+template <int D, bool BF>
+__global__ void __launch_bounds__(256) bwd_prepass_kernel(BwdArgs a) {
+  constexpr int C = kBC, CPL = D / 64;  // channels per lane
+  __shared__ float la[C][D + 1];
+  const size_t slot = blockIdx.x;
+  const size_t bh = slot / a.NC;
+  const int c = (int)(slot % a.NC), h = (int)(bh % a.H);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const size_t base = slot * (size_t)C * D;
+  for (int t = wave; t < C; t += 4) {
+    const int tt = c * C + t;
+    const bool ok = tt < a.T;
+    const size_t row = bh * a.T + (ok ? tt : 0);
+    float qv[CPL], kv[CPL], sq = 0.f, sk = 0.f;
+#pragma unroll
+    for (int u = 0; u < CPL; ++u) {
+      const int ch = lane + 64 * u;
+      qv[u] = ok ? ld1<BF>(a.q, row * D + ch) : 0.f;
+      kv[u] = ok ? ld1<BF>(a.k, row * D + ch) : 0.f;
+      if (a.normalize_qk) {
+        qv[u] = silu(qv[u]);
+        kv[u] = silu(kv[u]);
+      }
+      sq += qv[u] * qv[u];
+      sk += kv[u] * kv[u];
+    }
+    float iq = 1.f, ik = 1.f;
+    if (a.normalize_qk) {
+      iq = 1.f / fmaxf(sqrtf(wave_sum(sq)), 1e-12f);
+      ik = 1.f / fmaxf(sqrtf(wave_sum(sk)), 1e-12f);
+    }
+#pragma unroll
+    for (int u = 0; u < CPL; ++u) {
+      const int ch = lane + 64 * u;
+      const float gam = a.gamma ? a.gamma[(size_t)h * D + ch] : 1.f;
+      const float dyn = (a.z && ok) ? 2.f / (1.f + expf(-ld1<BF>(a.z, row * D + ch))) : 1.f;
+      const float kn = kv[u] * ik;
+      const float bg = ok ? gate_at<BF>(a.b, a.b_mode, row, ch, D) : 0.f;
+      const float wg = ok ? gate_at<BF>(a.w, a.w_mode, row, ch, D) : 0.f;
+      const float vv = ok ? ld1<BF>(a.v, row * D + ch) : 0.f;
+      a.KN[base + t * D + ch] = ok ? kn : 0.f;
+      a.KH[base + t * D + ch] = bg * kn;
+      a.QT[base + t * D + ch] = ok ? a.scale * gam * dyn * qv[u] * iq : 0.f;
+      a.VH[base + t * D + ch] = wg * vv;
+      la[t][ch] = ok ? log_alpha_at(a.log_alpha, a.alpha_mode, row, ch, D) : 0.f;
+    }
+  }
+  __syncthreads();
+  if (tid < D) {
+    float run = 0.f;
+    for (int t = 0; t < C; ++t) {
+      run += la[t][tid];
+      a.LAM[base + t * D + tid] = run;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K4 Gram: per chunk slot, A (s <= t) and L (s < t) with exact pairwise decays
+// (e^{Lambda_t - Lambda_s} <= 1 for s <= t), then T^-1 = (I + L)^-1 column by
+// column (forward substitution).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ void __launch_bounds__(256) bwd_gram_kernel(BwdArgs a) {
+  constexpr int C = kBC, P = D + 1;
+  __shared__ float sh[4 * C * P + C * (C + 1)];
+  float *kn = sh, *kh = sh + C * P, *qt = sh + 2 * C * P, *lam = sh + 3 * C * P;
+  float *L = sh + 4 * C * P;  // [C][C + 1]
+  const size_t slot = blockIdx.x;
+  const size_t base = slot * (size_t)C * D, cbase = slot * (size_t)C * C;
+  const int tid = threadIdx.x;
+  for (int idx = tid; idx < C * D; idx += 256) {
+    const int t = idx / D, ch = idx % D;
+    kn[t * P + ch] = a.KN[base + idx];
+    kh[t * P + ch] = a.KH[base + idx];
+    qt[t * P + ch] = a.QT[base + idx];
+    lam[t * P + ch] = a.LAM[base + idx];
+  }
+  __syncthreads();
+  for (int e = tid; e < C * C; e += 256) {
+    const int t = e / C, s = e % C;
+    float av = 0.f, lv = 0.f;
+    if (s <= t) {
+      for (int ch = 0; ch < D; ++ch) {
+        const float x = __expf(lam[t * P + ch] - lam[s * P + ch]) * kn[s * P + ch];
+        av += qt[t * P + ch] * x;
+        lv += kh[t * P + ch] * x;
+      }
+    }
+    a.AM[cbase + e] = av;
+    L[t * (C + 1) + s] = s < t ? lv : 0.f;
+  }
+  __syncthreads();
+  // T^-1 column s (thread s): x_t = delta_ts - sum_{r < t} L[t][r] x_r, written
+  // into the (now free) kn region as [C][C + 1]
+  float *ti = kn;
+  if (tid < C) {
+    const int s = tid;
+    for (int t = 0; t < C; ++t) {
+      float x = t == s ? 1.f : 0.f;
+      if (t > s)
+        for (int r = s; r < t; ++r) x -= L[t * (C + 1) + r] * ti[r * (C + 1) + s];
+      ti[t * (C + 1) + s] = x;
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < C * C; e += 256) a.TI[cbase + e] = ti[(e / C) * (C + 1) + e % C];
+}
+
+// ---------------------------------------------------------------------------
+// K5: per chunk slot, U = T^-1 (V_hat - K_a S0) and dU~ = T^-T (A^T dO + K' X).
+// Thread tile: TB tokens x 4 columns.
+// ---------------------------------------------------------------------------
+template <int D, int NS>
+__global__ void __launch_bounds__(256) bwd_u_kernel(BwdArgs a) {
+  constexpr int C = kBC, JB = 4, NJB = D / JB, TB = C * D / (256 * JB);
+  __shared__ __align__(16) float big[D * D];   // S0, then X   ([i][j])
+  __shared__ __align__(16) float r1[C * D];    // K_a, R, then K'
+  __shared__ __align__(16) float r2[C * D];    // dO, then Z
+  __shared__ float tc[C * (C + 1)];            // T^-1, A, then T^-1
+  const size_t slot = blockIdx.x;
+  const size_t bh = slot / a.NC;
+  const int c = (int)(slot % a.NC);
+  const size_t base = slot * (size_t)C * D, cbase = slot * (size_t)C * C;
+  const int tid = threadIdx.x;
+  const bool act = tid < (C / TB) * NJB;
+  const int tb = tid / NJB, jb = tid % NJB, t0 = tb * TB, j0 = jb * JB;
+  const uint16_t *S0p = a.Sc + slot * NS * (size_t)D * D;
+  const uint16_t *Xp = a.Xc + slot * NS * (size_t)D * D;
+  // (a) R = V_hat - K_a S0
+  for (int idx = tid; idx < D * D; idx += 256) big[idx] = state_at<D, NS>(S0p, idx / D, idx % D);
+  for (int idx = tid; idx < C * D; idx += 256) r1[idx] = a.KH[base + idx] * __expf(a.LAM[base + idx]);
+  for (int idx = tid; idx < C * (C + 1); idx += 256) {
+    const int t = idx / (C + 1), s = idx % (C + 1);
+    tc[idx] = s < C ? a.TI[cbase + t * C + s] : 0.f;
+  }
+  __syncthreads();
+  float acc[TB][JB];
+  if (act) {
+#pragma unroll
+    for (int u = 0; u < TB; ++u)
+#pragma unroll
+      for (int v = 0; v < JB; ++v) acc[u][v] = 0.f;
+    for (int i = 0; i < D; ++i) {
+      const float4 s4 = *reinterpret_cast<const float4 *>(&big[i * D + j0]);
+#pragma unroll
+      for (int u = 0; u < TB; ++u) {
+        const float kv = r1[(t0 + u) * D + i];
+        acc[u][0] += kv * s4.x; acc[u][1] += kv * s4.y; acc[u][2] += kv * s4.z; acc[u][3] += kv * s4.w;
+      }
+    }
+  }
+  __syncthreads();
+  if (act) {
+#pragma unroll
+    for (int u = 0; u < TB; ++u)
+#pragma unroll
+      for (int v = 0; v < JB; ++v) r1[(t0 + u) * D + j0 + v] = a.VH[base + (t0 + u) * D + j0 + v] - acc[u][v];
+  }
+  __syncthreads();
+  // (b) U = T^-1 R
+  if (act) {
+#pragma unroll
+    for (int u = 0; u < TB; ++u) {
+      const int t = t0 + u;
+      float x[JB] = {0.f, 0.f, 0.f, 0.f};
+      for (int s = 0; s <= t; ++s) {
+        const float tv = tc[t * (C + 1) + s];
+        const float4 r4 = *reinterpret_cast<const float4 *>(&r1[s * D + j0]);
+        x[0] += tv * r4.x; x[1] += tv * r4.y; x[2] += tv * r4.z; x[3] += tv * r4.w;
+      }
+#pragma unroll
+      for (int v = 0; v < JB; ++v) a.U[base + t * D + j0 + v] = x[v];
+    }
+  }
+  __syncthreads();
+  // (c) Z = A^T dO + K' X
+  for (int idx = tid; idx < C * D; idx += 256) {
+    const int t = idx / D, j = idx % D, tt = c * C + t;
+    r2[idx] = tt < a.T ? ld_do(a.dO, (bh * a.T + tt) * D + j, a.do_bf16) : 0.f;
+  }
+  for (int idx = tid; idx < C * (C + 1); idx += 256) {
+    const int t = idx / (C + 1), s = idx % (C + 1);
+    tc[idx] = s < C ? a.AM[cbase + t * C + s] : 0.f;
+  }
+  for (int idx = tid; idx < D * D; idx += 256) big[idx] = state_at<D, NS>(Xp, idx / D, idx % D);
+  for (int idx = tid; idx < C * D; idx += 256) {
+    const int ch = idx % D;
+    r1[idx] = a.KN[base + idx] * __expf(a.LAM[base + (C - 1) * D + ch] - a.LAM[base + idx]);
+  }
+  __syncthreads();
+  if (act) {
+#pragma unroll
+    for (int u = 0; u < TB; ++u)
+#pragma unroll
+      for (int v = 0; v < JB; ++v) acc[u][v] = 0.f;
+    // A^T dO: Z[s][j] = sum_{t >= s} A[t][s] dO[t][j]
+    for (int t = 0; t < C; ++t) {
+      const float4 d4 = *reinterpret_cast<const float4 *>(&r2[t * D + j0]);
+#pragma unroll
+      for (int u = 0; u < TB; ++u) {
+        const float av = tc[t * (C + 1) + t0 + u];  // zero for t < s (A is lower)
+        acc[u][0] += av * d4.x; acc[u][1] += av * d4.y; acc[u][2] += av * d4.z; acc[u][3] += av * d4.w;
+      }
+    }
+    // K' X
+    for (int i = 0; i < D; ++i) {
+      const float4 x4 = *reinterpret_cast<const float4 *>(&big[i * D + j0]);
+#pragma unroll
+      for (int u = 0; u < TB; ++u) {
+        const float kv = r1[(t0 + u) * D + i];
+        acc[u][0] += kv * x4.x; acc[u][1] += kv * x4.y; acc[u][2] += kv * x4.z; acc[u][3] += kv * x4.w;
+      }
+    }
+  }
+  __syncthreads();
+  if (act) {
+#pragma unroll
+    for (int u = 0; u < TB; ++u)
+#pragma unroll
+      for (int v = 0; v < JB; ++v) r2[(t0 + u) * D + j0 + v] = acc[u][v];
+  }
+  for (int idx = tid; idx < C * (C + 1); idx += 256) {
+    const int t = idx / (C + 1), s = idx % (C + 1);
+    tc[idx] = s < C ? a.TI[cbase + t * C + s] : 0.f;
+  }
+  __syncthreads();
+  // (d) dU~ = T^-T Z: dU~[s][j] = sum_{t >= s} T^-1[t][s] Z[t][j]
+  if (act) {
+#pragma unroll
+    for (int u = 0; u < TB; ++u) {
+      const int s = t0 + u;
+      float x[JB] = {0.f, 0.f, 0.f, 0.f};
+      for (int t = s; t < C; ++t) {
+        const float tv = tc[t * (C + 1) + s];
+        const float4 z4 = *reinterpret_cast<const float4 *>(&r2[t * D + j0]);
+        x[0] += tv * z4.x; x[1] += tv * z4.y; x[2] += tv * z4.z; x[3] += tv * z4.w;
+      }
+#pragma unroll
+      for (int v = 0; v < JB; ++v) a.DU[base + s * D + j0 + v] = x[v];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K6: per chunk slot, dA = dO U^T (s <= t) and dL = -dU~ U^T (s < t).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ void __launch_bounds__(256) bwd_dmat_kernel(BwdArgs a) {
+  constexpr int C = kBC, P = D + 1;
+  __shared__ float sh[3 * C * P];
+  float *dos = sh, *dus = sh + C * P, *us = sh + 2 * C * P;
+  const size_t slot = blockIdx.x;
+  const size_t bh = slot / a.NC;
+  const int c = (int)(slot % a.NC);
+  const size_t base = slot * (size_t)C * D, cbase = slot * (size_t)C * C;
+  const int tid = threadIdx.x;
+  for (int idx = tid; idx < C * D; idx += 256) {
+    const int t = idx / D, j = idx % D, tt = c * C + t;
+    dos[t * P + j] = tt < a.T ? ld_do(a.dO, (bh * a.T + tt) * D + j, a.do_bf16) : 0.f;
+    dus[t * P + j] = a.DU[base + idx];
+    us[t * P + j] = a.U[base + idx];
+  }
+  __syncthreads();
+  for (int e = tid; e < C * C; e += 256) {
+    const int t = e / C, s = e % C;
+    float da = 0.f, dl = 0.f;
+    if (s <= t) {
+      for (int j = 0; j < D; ++j) {
+        const float uv = us[s * P + j];
+        da += dos[t * P + j] * uv;
+        dl -= dus[t * P + j] * uv;
+      }
+    }
+    a.DA[cbase + e] = da;
+    a.DL[cbase + e] = s < t ? dl : 0.f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K7: per chunk slot, dQ_a = dO S0^T, dK_a = -dU~ S0^T, dK' = U X^T.
+// Thread tile: TB tokens x 4 channels; the state is staged transposed.
+// ---------------------------------------------------------------------------
+template <int D, int NS>
+__global__ void __launch_bounds__(256) bwd_dproj_kernel(BwdArgs a) {
+  constexpr int C = kBC, IB = 4, NIB = D / IB, TB = C * D / (256 * IB);
+  __shared__ __align__(16) float st[D * D];  // [j][i]: S0 transposed, then X transposed
+  __shared__ float r1[C * D];                // dO, then U
+  __shared__ float r2[C * D];                // dU~
+  const size_t slot = blockIdx.x;
+  const size_t bh = slot / a.NC;
+  const int c = (int)(slot % a.NC);
+  const size_t base = slot * (size_t)C * D;
+  const int tid = threadIdx.x;
+  const bool act = tid < (C / TB) * NIB;
+  const int tb = tid / NIB, ib = tid % NIB, t0 = tb * TB, i0 = ib * IB;
+  const uint16_t *S0p = a.Sc + slot * NS * (size_t)D * D;
+  const uint16_t *Xp = a.Xc + slot * NS * (size_t)D * D;
+  for (int idx = tid; idx < D * D; idx += 256) {
+    const int i = idx / D, j = idx % D;
+    st[j * D + i] = state_at<D, NS>(S0p, i, j);
+  }
+  for (int idx = tid; idx < C * D; idx += 256) {
+    const int t = idx / D, j = idx % D, tt = c * C + t;
+    r1[idx] = tt < a.T ? ld_do(a.dO, (bh * a.T + tt) * D + j, a.do_bf16) : 0.f;
+    r2[idx] = a.DU[base + idx];
+  }
+  __syncthreads();
+  float aq[TB][IB], ak[TB][IB];
+  if (act) {
+#pragma unroll
+    for (int u = 0; u < TB; ++u)
+#pragma unroll
+      for (int v = 0; v < IB; ++v) aq[u][v] = ak[u][v] = 0.f;
+    for (int j = 0; j < D; ++j) {
+      const float4 s4 = *reinterpret_cast<const float4 *>(&st[j * D + i0]);
+#pragma unroll
+      for (int u = 0; u < TB; ++u) {
+        const float dv = r1[(t0 + u) * D + j], du = r2[(t0 + u) * D + j];
+        aq[u][0] += dv * s4.x; aq[u][1] += dv * s4.y; aq[u][2] += dv * s4.z; aq[u][3] += dv * s4.w;
+        ak[u][0] -= du * s4.x; ak[u][1] -= du * s4.y; ak[u][2] -= du * s4.z; ak[u][3] -= du * s4.w;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < TB; ++u)
+#pragma unroll
+      for (int v = 0; v < IB; ++v) {
+        a.DQA[base + (t0 + u) * D + i0 + v] = aq[u][v];
+        a.DKA[base + (t0 + u) * D + i0 + v] = ak[u][v];
+      }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < D * D; idx += 256) {
+    const int i = idx / D, j = idx % D;
+    st[j * D + i] = state_at<D, NS>(Xp, i, j);
+  }
+  for (int idx = tid; idx < C * D; idx += 256) r1[idx] = a.U[base + idx];
+  __syncthreads();
+  if (act) {
+#pragma unroll
+    for (int u = 0; u < TB; ++u)
+#pragma unroll
+      for (int v = 0; v < IB; ++v) aq[u][v] = 0.f;
+    for (int j = 0; j < D; ++j) {
+      const float4 x4 = *reinterpret_cast<const float4 *>(&st[j * D + i0]);
+#pragma unroll
+      for (int u = 0; u < TB; ++u) {
+        const float uv = r1[(t0 + u) * D + j];
+        aq[u][0] += uv * x4.x; aq[u][1] += uv * x4.y; aq[u][2] += uv * x4.z; aq[u][3] += uv * x4.w;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < TB; ++u)
+#pragma unroll
+      for (int v = 0; v < IB; ++v) a.DKP[base + (t0 + u) * D + i0 + v] = aq[u][v];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K8 Gram backprop: one workgroup (64 threads) per (chunk slot, 64 channels),
+// a thread per channel.  For every pair s <= t with p = e^{Lambda_t - Lambda_s}:
+//   RA_t += dA_ts k_s p,  RL_t += dL_ts k_s p            (row sums)
+//   CS_s += (dA_ts q_tilde_t + dL_ts k_hat_t) p          (column sums)
+// then, per token, the gradients of q_tilde, k_hat, k and Lambda, and the
+// reverse cumulative sum of dLambda over the chunk (= d log alpha).
+// ---------------------------------------------------------------------------
+template <int D, int NS>
+__global__ void __launch_bounds__(64) bwd_gramback_kernel(BwdArgs a) {
+  constexpr int C = kBC, CW = 64;
+  __shared__ float kn[C][CW], kh[C][CW], qt[C][CW], lam[C][CW], cs[C][CW];
+  const size_t slot = blockIdx.x / (D / CW);
+  const int cb = (int)(blockIdx.x % (D / CW)), lane = threadIdx.x, ch = cb * CW + lane;
+  const size_t base = slot * (size_t)C * D, cbase = slot * (size_t)C * C;
+  for (int t = 0; t < C; ++t) {
+    kn[t][lane] = a.KN[base + t * D + ch];
+    kh[t][lane] = a.KH[base + t * D + ch];
+    qt[t][lane] = a.QT[base + t * D + ch];
+    lam[t][lane] = a.LAM[base + t * D + ch];
+    cs[t][lane] = 0.f;
+  }
+  // (one wave: LDS written and read by the same lanes' wave, in order)
+  const float *DA = a.DA + cbase, *DL = a.DL + cbase;
+  for (int t = 0; t < C; ++t) {
+    float ra = 0.f, rl = 0.f;
+    const float lt = lam[t][lane], qv = qt[t][lane], hv = kh[t][lane];
+    for (int s = 0; s <= t; ++s) {
+      const float p = __expf(lt - lam[s][lane]);
+      const float da = DA[t * C + s], dl = DL[t * C + s];
+      const float x = kn[s][lane] * p;
+      ra += da * x;
+      rl += dl * x;
+      cs[s][lane] += (da * qv + dl * hv) * p;
+    }
+    a.DQT[base + t * D + ch] = ra;  // row sums, completed below
+    a.DKT[base + t * D + ch] = rl;
+  }
+  const float lc = lam[C - 1][lane], ac = __expf(lc);
+  float sum_kp = 0.f;
+  // pass 1: per-token gradients; dLambda into cs (column sums consumed)
+  for (int t = 0; t < C; ++t) {
+    const float at = __expf(lam[t][lane]), rat = __expf(lc - lam[t][lane]);
+    const float dqa = a.DQA[base + t * D + ch], dka = a.DKA[base + t * D + ch], dkp = a.DKP[base + t * D + ch];
+    const float ra = a.DQT[base + t * D + ch], rl = a.DKT[base + t * D + ch];
+    const float qv = qt[t][lane], hv = kh[t][lane], kv = kn[t][lane], csv = cs[t][lane];
+    a.DQT[base + t * D + ch] = at * dqa + ra;
+    a.DKT[base + t * D + ch] = at * dka + rl;
+    a.DKN[base + t * D + ch] = rat * dkp + csv;
+    cs[t][lane] = qv * at * dqa + hv * at * dka - kv * rat * dkp + qv * ra + hv * rl - kv * csv;
+    sum_kp += kv * rat * dkp;
+  }
+  // the chunk-end decay: K' and Diag(a_C) S0 in the end state
+  const uint16_t *S0p = a.Sc + slot * NS * (size_t)D * D;
+  const uint16_t *Xp = a.Xc + slot * NS * (size_t)D * D;
+  float xs = 0.f;
+  for (int j = 0; j < D; ++j) xs += state_at<D, NS>(Xp, ch, j) * state_at<D, NS>(S0p, ch, j);
+  cs[C - 1][lane] += sum_kp + ac * xs;
+  float run = 0.f;
+  for (int t = C - 1; t >= 0; --t) {
+    run += cs[t][lane];
+    a.DLA[base + t * D + ch] = run;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K9 final: per chunk slot (4 waves x 16 tokens, lanes over channels), the
+// elementwise chains to the inputs: gates, read-out gain, SiLU + l2; writes
+// the gradients of valid tokens and the chunk's gamma partial sums.
+// ---------------------------------------------------------------------------
+template <int D, bool BF>
+__global__ void __launch_bounds__(256) bwd_final_kernel(BwdArgs a) {
+  constexpr int C = kBC, CPL = D / 64;
+  __shared__ float gp[4][D];
+  const size_t slot = blockIdx.x;
+  const size_t bh = slot / a.NC;
+  const int c = (int)(slot % a.NC), h = (int)(bh % a.H);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const size_t base = slot * (size_t)C * D;
+  float gacc[CPL];
+#pragma unroll
+  for (int u = 0; u < CPL; ++u) gacc[u] = 0.f;
+  for (int t = wave; t < C; t += 4) {
+    const int tt = c * C + t;
+    if (tt >= a.T) continue;  // uniform over the wave
+    const size_t row = bh * a.T + tt;
+    float qx[CPL], kx[CPL], sq[CPL], sk[CPL], dqh[CPL], dkn[CPL];
+    float nq = 0.f, nk = 0.f;
+#pragma unroll
+    for (int u = 0; u < CPL; ++u) {
+      const int ch = lane + 64 * u;
+      qx[u] = ld1<BF>(a.q, row * D + ch);
+      kx[u] = ld1<BF>(a.k, row * D + ch);
+      sq[u] = a.normalize_qk ? silu(qx[u]) : qx[u];
+      sk[u] = a.normalize_qk ? silu(kx[u]) : kx[u];
+      nq += sq[u] * sq[u];
+      nk += sk[u] * sk[u];
+    }
+    float rq = 1.f, rk = 1.f;
+    if (a.normalize_qk) {
+      rq = fmaxf(sqrtf(wave_sum(nq)), 1e-12f);
+      rk = fmaxf(sqrtf(wave_sum(nk)), 1e-12f);
+    }
+    float dotq = 0.f, dotk = 0.f, sdb = 0.f, sdw = 0.f, sdla = 0.f;
+#pragma unroll
+    for (int u = 0; u < CPL; ++u) {
+      const int ch = lane + 64 * u;
+      const size_t ix = base + t * D + ch;
+      const float qh = sq[u] / rq, kn = sk[u] / rk;
+      const float gam = a.gamma ? a.gamma[(size_t)h * D + ch] : 1.f;
+      const float zv = a.z ? ld1<BF>(a.z, row * D + ch) : 0.f;
+      const float sg = 1.f / (1.f + expf(-zv));
+      const float dyn = a.z ? 2.f * sg : 1.f;
+      const float dqt = a.DQT[ix], dkh = a.DKT[ix], dvh = a.DU[ix];
+      const float bg = gate_at<BF>(a.b, a.b_mode, row, ch, D);
+      const float wg = gate_at<BF>(a.w, a.w_mode, row, ch, D);
+      const float vv = ld1<BF>(a.v, row * D + ch);
+      dqh[u] = dqt * a.scale * gam * dyn;
+      gacc[u] += dqt * a.scale * dyn * qh;
+      if (a.dz && a.z) a.dz[row * D + ch] = dqt * a.scale * gam * qh * 2.f * sg * (1.f - sg);
+      dkn[u] = a.DKN[ix] + dkh * bg;
+      const float db = dkh * kn, dw = dvh * vv, dla = a.DLA[ix];
+      if (a.db && a.b_mode == GDR_GATE_PER_CHANNEL) a.db[row * D + ch] = db;
+      if (a.dw && a.w_mode == GDR_GATE_PER_CHANNEL) a.dw[row * D + ch] = dw;
+      if (a.dla && a.alpha_mode == GDR_GATE_PER_CHANNEL) a.dla[row * D + ch] = dla;
+      sdb += db;
+      sdw += dw;
+      sdla += dla;
+      if (a.dv) a.dv[row * D + ch] = dvh * wg;
+      dotq += qh * dqh[u];
+      dotk += kn * dkn[u];
+    }
+    if (a.b_mode == GDR_GATE_PER_TOKEN || a.w_mode == GDR_GATE_PER_TOKEN || a.alpha_mode == GDR_GATE_PER_TOKEN) {
+      sdb = wave_sum(sdb);
+      sdw = wave_sum(sdw);
+      sdla = wave_sum(sdla);
+      if (lane == 0) {
+        if (a.db && a.b_mode == GDR_GATE_PER_TOKEN) a.db[row] = sdb;
+        if (a.dw && a.w_mode == GDR_GATE_PER_TOKEN) a.dw[row] = sdw;
+        if (a.dla && a.alpha_mode == GDR_GATE_PER_TOKEN) a.dla[row] = sdla;
+      }
+    }
+    if (a.normalize_qk) {
+      dotq = wave_sum(dotq);
+      dotk = wave_sum(dotk);
+    }
+#pragma unroll
+    for (int u = 0; u < CPL; ++u) {
+      const int ch = lane + 64 * u;
+      float gq = dqh[u], gk = dkn[u];
+      if (a.normalize_qk) {
+        // through y = s / max(|s|, 1e-12), then s = SiLU(x)
+        const float qh = sq[u] / rq, kn = sk[u] / rk;
+        gq = rq > 1e-12f ? (gq - qh * dotq) / rq : gq / 1e-12f;
+        gk = rk > 1e-12f ? (gk - kn * dotk) / rk : gk / 1e-12f;
+        const float sgq = 1.f / (1.f + expf(-qx[u])), sgk = 1.f / (1.f + expf(-kx[u]));
+        gq *= sgq * (1.f + qx[u] * (1.f - sgq));
+        gk *= sgk * (1.f + kx[u] * (1.f - sgk));
+      }
+      if (a.dq) a.dq[row * D + ch] = gq;
+      if (a.dk) a.dk[row * D + ch] = gk;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < CPL; ++u) gp[wave][lane + 64 * u] = gacc[u];
+  __syncthreads();
+  if (tid < D) a.gpart[slot * D + tid] = gp[0][tid] + gp[1][tid] + gp[2][tid] + gp[3][tid];
+}
+
+// K10: dgamma[h][c] = sum over the batch and the chunks of the partial sums.
+template <int D>
+__global__ void __launch_bounds__(256) bwd_dgamma_kernel(BwdArgs a) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= a.H * D) return;
+  const int h = idx / D, ch = idx % D;
+  float s = 0.f;
+  for (int b = 0; b < a.B; ++b)
+    for (int c = 0; c < a.NC; ++c) s += a.gpart[((size_t)(b * a.H + h) * a.NC + c) * D + ch];
+  a.dgamma[idx] = s;
+}
+
+template <int D, int NS, bool BF>
+hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
+  const unsigned nch = (unsigned)((size_t)a.B * a.H * a.NC);
+  if (nch == 0) {  // empty sequences: only dgamma (zeros)
+    if (a.dgamma && a.gamma)
+      hipLaunchKernelGGL((bwd_dgamma_kernel<D>), dim3((unsigned)((a.H * D + 255) / 256)), dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((bwd_prepass_kernel<D, BF>), dim3(nch), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((bwd_gram_kernel<D>), dim3(nch), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((bwd_u_kernel<D, NS>), dim3(nch), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((bwd_dmat_kernel<D>), dim3(nch), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((bwd_dproj_kernel<D, NS>), dim3(nch), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((bwd_gramback_kernel<D, NS>), dim3(nch * (D / 64)), dim3(64), 0, st, a);
+  hipLaunchKernelGGL((bwd_final_kernel<D, BF>), dim3(nch), dim3(256), 0, st, a);
+  if (a.dgamma && a.gamma)
+    hipLaunchKernelGGL((bwd_dgamma_kernel<D>), dim3((unsigned)((a.H * D + 255) / 256)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int D, int NS>
+hipError_t launch_bwd_prep_t(const BwdArgs &a, hipStream_t st) {
+  const unsigned nch = (unsigned)((size_t)a.B * a.H * a.NC);
+  hipLaunchKernelGGL((bwd_prep_kernel<D, NS>), dim3(nch), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t bwd_workspace(BwdArgs *a, ChunkArgs *f, void *ws, int B, int H, int T, int D, int NS) {
+  const int C = kBC;
+  const size_t nch = (size_t)B * H * ((T + C - 1) / C);
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  size_t total = al(chunk_workspace(f, ws, B, H, T, C, D, NS, 0));
+  unsigned char *base = static_cast<unsigned char *>(ws);
+  auto take = [&](size_t bytes) {
+    void *p = ws ? base + total : nullptr;
+    total += al(bytes);
+    return p;
+  };
+  void *mt = take(nch * NS * (size_t)D * D * 2), *xc = take(nch * NS * (size_t)D * D * 2);
+  void *gn = take(nch * (size_t)D * D * 4);
+  float **cd[14] = {&a->KN, &a->KH, &a->QT, &a->VH, &a->LAM, &a->U, &a->DU, &a->DQA, &a->DKA, &a->DKP,
+                    &a->DQT, &a->DKT, &a->DKN, &a->DLA};
+  float *cdp[14];
+  for (int i = 0; i < 14; ++i) cdp[i] = static_cast<float *>(take(nch * (size_t)kBC * D * 4));
+  float *ccp[4];
+  for (int i = 0; i < 4; ++i) ccp[i] = static_cast<float *>(take(nch * (size_t)kBC * kBC * 4));
+  float *gp = static_cast<float *>(take(nch * (size_t)D * 4));
+  if (a) {
+    a->Mt = static_cast<uint16_t *>(mt);
+    a->Xc = static_cast<uint16_t *>(xc);
+    a->Gn = static_cast<float *>(gn);
+    for (int i = 0; i < 14; ++i) *cd[i] = cdp[i];
+    a->AM = ccp[0];
+    a->TI = ccp[1];
+    a->DA = ccp[2];
+    a->DL = ccp[3];
+    a->gpart = gp;
+  }
+  return total;
+}
+
+hipError_t launch_bwd_prep(const BwdArgs &a, int D, int NS, hipStream_t st) {
+  if (D == 128 && NS == 2) return launch_bwd_prep_t<128, 2>(a, st);
+  if (D == 128) return launch_bwd_prep_t<128, 3>(a, st);
+  if (NS == 2) return launch_bwd_prep_t<64, 2>(a, st);
+  return launch_bwd_prep_t<64, 3>(a, st);
+}
+
+hipError_t launch_bwd(const BwdArgs &a, int D, int NS, hipStream_t st) {
+  if (D == 128 && NS == 2) return launch_bwd_t<128, 2, true>(a, st);
+  if (D == 128) return launch_bwd_t<128, 3, false>(a, st);
+  if (NS == 2) return launch_bwd_t<64, 2, true>(a, st);
+  return launch_bwd_t<64, 3, false>(a, st);
+}
+
+}  // namespace gdr

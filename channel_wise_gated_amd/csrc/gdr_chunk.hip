@@ -946,7 +946,7 @@ __global__ void __launch_bounds__(64 * (D / 16)) chunk_chain_kernel(ChunkArgs a)
     slot0 = bh * NC;
     slot_step = 1;
   }
-  auto slot = [&](int c) { return slot0 + (size_t)c * slot_step; };
+  auto slot = [&](int c) { return slot0 + (size_t)(a.rev ? NC - 1 - c : c) * slot_step; };
   const int col = 16 * slice + l16;
 
   f32x4 S = zero4();
@@ -1303,12 +1303,12 @@ static hipError_t launch_chunk_pass(const ChunkArgs &a, size_t nch, int phases, 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (!(phases & 2)) return hipSuccess;
+  if (!(phases & 6)) return hipSuccess;
   constexpr int NSL = D / 16;
   const size_t nblk = ((nbh + 7) / 8) * 8 * NSL;
   hipLaunchKernelGGL((chunk_chain_kernel<C, D, NS>), dim3((unsigned)nblk), dim3(64 * (D / 16)), 0, st, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || nch == 0) return e;
+  if (e != hipSuccess || nch == 0 || !(phases & 2)) return e;
   constexpr size_t out_lds = (size_t)NSL * (D / 32) * NS * 512 * 2;
   constexpr size_t og_lds = out_lds_gated<C, D, NS>();
   if (a.og)

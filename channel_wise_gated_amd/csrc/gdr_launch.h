@@ -33,6 +33,9 @@ struct ChunkArgs {
   // stream; stream bh's chunk c sits in slot bh * ncs + (c - c0).
   int c0, ncs;
   float *Sst;  // workspace: fp32 states handed from one segment to the next
+  // Chain only: walk each stream's chunks last to first (the backward's chain
+  // of state gradients, X <- M^T X + G, with M^T and G in the M and N slots).
+  int rev;
   // Gated output (og != null): instead of o, y[b,t,h,:] = RMSNorm(o[b,h,t,:])
   // * onw[h,:] * sigmoid(og[b,h,t,:]) in token-major [B,T,H,dv].
   const void *og;
@@ -56,10 +59,32 @@ struct GateArgs {
 };
 hipError_t launch_gate_proj(const GateArgs &a, int d, bool out_bf16, hipStream_t st);
 
+// Backward pass (gdr_bwd.hip): chunks of 64 tokens, uniform batches.
+struct BwdArgs {
+  const void *q, *k, *v, *b, *w, *z, *dO;
+  const float *log_alpha, *gamma;
+  int B, H, T, NC, alpha_mode, b_mode, w_mode, normalize_qk, do_bf16;
+  float scale;
+  const uint16_t *Qp, *Mm, *Sc;  // the forward's Q', M and chunk-start states (C = 64)
+  uint16_t *Mt, *Xc;             // M^T for the reverse chain; the chunk-end state gradients
+  float *Gn;                     // Q'^T dO for the reverse chain
+  // per-chunk scratch, [slot][64][D] fp32
+  float *KN, *KH, *QT, *VH, *LAM, *U, *DU, *DQA, *DKA, *DKP, *DQT, *DKT, *DKN, *DLA;
+  float *AM, *TI, *DA, *DL;      // [slot][64][64] fp32
+  float *gpart;                  // [slot][D] partial sums of dgamma
+  float *dq, *dk, *dv, *dla, *db, *dw, *dz, *dgamma;  // outputs (each may be null)
+};
+// Workspace of the backward: the forward's chunk workspace (C = 64; its fields
+// set in *f) followed by the backward's regions (set in *a); returns the size.
+size_t bwd_workspace(BwdArgs *a, ChunkArgs *f, void *ws, int B, int H, int T, int D, int NS);
+hipError_t launch_bwd_prep(const BwdArgs &a, int D, int NS, hipStream_t st);
+hipError_t launch_bwd(const BwdArgs &a, int D, int NS, hipStream_t st);
+
 hipError_t launch_decode(const gdr_desc &d, float *S, const void *q, const void *k, const void *v,
                          const float *la, const void *b, const void *w, const float *gamma,
                          const void *z, void *o, hipStream_t st);
-// phases: bit 0 = intra-chunk kernel, bit 1 = scan kernel
+// phases: bit 0 = intra-chunk kernel, bit 1 = scan (chain + output kernels),
+// bit 2 = chain kernel only (no output)
 hipError_t launch_chunk(const gdr_desc &d, const ChunkArgs &a, int phases, hipStream_t st);
 // Workspace of the chunkwise forward: per chunk slot the maps Q', M, O_bar,
 // N and the chunk-start state; for a packed batch (nseq > 0) the chunk list

@@ -31,6 +31,7 @@ GDR_OK, GDR_ERR_INVALID_ARG, GDR_ERR_UNSUPPORTED, GDR_ERR_WORKSPACE, GDR_ERR_HIP
 GDR_BF16, GDR_F32 = 0, 1
 PER_CHANNEL, PER_TOKEN, ONES, ZEROS = 0, 1, 2, 3
 SYMBOLS = ("gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_chunk_fwd_gated", "gdr_chunk_fwd_intra",
+           "gdr_chunk_bwd_workspace_size", "gdr_chunk_bwd",
            "gdr_chunk_fwd_scan", "gdr_chunk_fwd_varlen_workspace_size", "gdr_chunk_fwd_varlen",
            "gdr_decode_step", "gdr_status_string", "gdr_version", "gdr_gate_proj_workspace_size",
            "gdr_gate_proj")
@@ -95,6 +96,10 @@ def load() -> ctypes.CDLL:
     lib.gdr_gate_proj_workspace_size.argtypes = [gp, ctypes.POINTER(sz)]
     lib.gdr_gate_proj.restype = ctypes.c_int
     lib.gdr_gate_proj.argtypes = [gp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gdr_chunk_bwd_workspace_size.restype = ctypes.c_int
+    lib.gdr_chunk_bwd_workspace_size.argtypes = [dp, ctypes.POINTER(sz)]
+    lib.gdr_chunk_bwd.restype = ctypes.c_int
+    lib.gdr_chunk_bwd.argtypes = [dp] + [vp] * 21 + [sz, vp]
     lib.gdr_status_string.restype = ctypes.c_char_p
     lib.gdr_status_string.argtypes = [ctypes.c_int]
     lib.gdr_version.restype = ctypes.c_int
@@ -324,6 +329,58 @@ def gdr_gate_proj(x, w_down, w_up, bias, ranks, H, d, *, out_dtype=torch.bfloat1
     if rc != GDR_OK:
         raise GdrError(rc, "gdr_gate_proj")
     return outs
+
+
+def gdr_chunk_bwd(q, k, v, log_alpha, b, w, dO, gamma=None, z=None, S0=None, dS_T=None, *,
+                  normalize_qk=True, scale=1.0, workspace=None, stream=None) -> dict:
+    """Backward of gdr_chunk_fwd; see gdr_chunk_bwd in gdr.h.
+
+    Arguments as gdr_chunk_fwd, plus dO [B,H,T,dv] (its dtype is the
+    descriptor's out_dtype) and dS_T [B,H,dk,dv] fp32 or None.  Returns a dict
+    of fp32 gradients: dq, dk, dv, dS0; dlog_alpha, db, dw shaped as their
+    gate (None for a constant gate); dgamma [H,dk] (None without gamma); dz
+    (None without z).
+    """
+    lib = load()
+    q, k, v, z, gamma, S0, dO, dS_T = map(_contig, (q, k, v, z, gamma, S0, dO, dS_T))
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    if isinstance(log_alpha, (int, float)):
+        if log_alpha != 0:
+            raise ValueError("scalar log_alpha must be 0")
+        amode, la = ONES, None
+    else:
+        amode, la = _gate(_contig(log_alpha), 4, "log_alpha")
+    bmode, bt = _gate(_contig(b), 4, "b")
+    wmode, wt = _gate(_contig(w), 4, "w")
+    if tuple(dO.shape) != (B, H, T, dv):
+        raise ValueError("dO must be [B,H,T,dv]")
+    od = GDR_BF16 if dO.dtype == torch.bfloat16 else GDR_F32
+    desc = make_desc(B, H, T, dk, dv, 64, _dtype_code(q), od, int(bool(normalize_qk)), scale, amode, bmode, wmode)
+    n = ctypes.c_size_t(0)
+    rc = lib.gdr_chunk_bwd_workspace_size(ctypes.byref(desc), ctypes.byref(n))
+    if rc != GDR_OK:
+        raise GdrError(rc, "gdr_chunk_bwd_workspace_size")
+    dev = q.device
+    if workspace is None:
+        workspace = torch.empty(max(int(n.value), 1), dtype=torch.uint8, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    gshape = lambda mode, d: (B, H, T, d) if mode == PER_CHANNEL else ((B, H, T) if mode == PER_TOKEN else None)
+    out = {"dq": torch.empty(B, H, T, dk, **f32), "dk": torch.empty(B, H, T, dk, **f32),
+           "dv": torch.empty(B, H, T, dv, **f32), "dS0": torch.empty(B, H, dk, dv, **f32)}
+    for name, mode, d in (("dlog_alpha", amode, dk), ("db", bmode, dk), ("dw", wmode, dv)):
+        shp = gshape(mode, d)
+        out[name] = torch.empty(*shp, **f32) if shp else None
+    out["dgamma"] = torch.empty(H, dk, **f32) if gamma is not None else None
+    out["dz"] = torch.empty(B, H, T, dk, **f32) if z is not None else None
+    rc = lib.gdr_chunk_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(la), _ptr(bt), _ptr(wt),
+                           _ptr(gamma), _ptr(z), _ptr(S0), _ptr(dO), _ptr(dS_T), _ptr(out["dq"]),
+                           _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dlog_alpha"]), _ptr(out["db"]),
+                           _ptr(out["dw"]), _ptr(out["dgamma"]), _ptr(out["dz"]), _ptr(out["dS0"]),
+                           _ptr(workspace), workspace.numel(), _stream(stream))
+    if rc != GDR_OK:
+        raise GdrError(rc, "gdr_chunk_bwd")
+    return out
 
 
 def gdr_decode_step(S, q, k, v, log_alpha, b, w, gamma=None, z=None, *, out_dtype=torch.float32,

@@ -205,6 +205,35 @@ gdr_status gdr_chunk_fwd_gated(const gdr_desc *desc, const void *q, const void *
                                size_t workspace_bytes, void *stream);
 
 /*
+ * Backward of gdr_chunk_fwd: the gradients of the loss <dO, o> + <dS_T, S_T>
+ * with respect to every input (reverse mode of the recurrence of Muir reading
+ * notes, section 2.1, through the chunk system of section 2.4: a chain of
+ * state gradients over the chunks, last to first, X <- M^T X + Q'^T dO, then
+ * per chunk the gradients of its tokens).  It recomputes what it needs of the
+ * forward pass, in chunks of 64 tokens whatever desc->chunk says.
+ *
+ *   arguments q .. S0 and desc as gdr_chunk_fwd (uniform batches)
+ *   dO          [B,H,T,dv] in desc->out_dtype: the upstream gradient of o
+ *   dS_T        [B,H,dk,dv] fp32 or NULL (= 0): the upstream gradient of S_T
+ *   outputs, all fp32, each may be NULL (not written):
+ *     dq, dk    [B,H,T,dk];  dv [B,H,T,dv];  dz [B,H,T,dk] (only with z)
+ *     dlog_alpha, db, dw  shaped as their gate: [B,H,T,d] per channel,
+ *                         [B,H,T] per token; not written for ONES / ZEROS
+ *     dgamma    [H,dk] (only with gamma; summed over batch and tokens)
+ *     dS0       [B,H,dk,dv]
+ *   workspace   >= gdr_chunk_bwd_workspace_size() bytes, 256-byte aligned
+ * Validation as gdr_chunk_fwd, plus dO non-null and every pointer 16-byte
+ * aligned (GDR_ERR_INVALID_ARG), before any launch.
+ */
+gdr_status gdr_chunk_bwd_workspace_size(const gdr_desc *desc, size_t *bytes);
+gdr_status gdr_chunk_bwd(const gdr_desc *desc, const void *q, const void *k, const void *v,
+                         const float *log_alpha, const void *b, const void *w, const float *gamma,
+                         const void *z, const float *S0, const void *dO, const float *dS_T,
+                         float *dq, float *dk, float *dv, float *dlog_alpha, float *db, float *dw,
+                         float *dgamma, float *dz, float *dS0, void *workspace,
+                         size_t workspace_bytes, void *stream);
+
+/*
  * The two phases of gdr_chunk_fwd as separate calls, for callers that overlap
  * the fully parallel phase of one batch with the serial scan of another on a
  * second stream, or that time the phases.  gdr_chunk_fwd(...) gives exactly

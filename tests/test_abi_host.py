@@ -242,3 +242,26 @@ def test_gate_proj_workspace_and_validation():
     assert call(1024, 1288, 2048, 8192, 1 << 30) == gdr.GDR_ERR_INVALID_ARG
     assert call(1024, 1280, 2048, None, 1 << 30) == gdr.GDR_ERR_WORKSPACE
     assert call(1024, 1280, 2048, 8192, 1000) == gdr.GDR_ERR_WORKSPACE
+
+
+def test_chunk_bwd_workspace_and_validation():
+    _lib()
+    lib = gdr.load()
+    n = ctypes.c_size_t(0)
+    assert lib.gdr_chunk_bwd_workspace_size(ctypes.byref(gdr.make_desc(**GOOD)), ctypes.byref(n)) == gdr.GDR_OK
+    assert n.value > 0
+    d0 = gdr.make_desc(**dict(GOOD, T=0))
+    assert lib.gdr_chunk_bwd_workspace_size(ctypes.byref(d0), ctypes.byref(n)) == gdr.GDR_OK and n.value == 0
+    assert lib.gdr_chunk_bwd_workspace_size(ctypes.byref(gdr.make_desc(**dict(GOOD, dk=96))),
+                                            ctypes.byref(n)) == gdr.GDR_ERR_UNSUPPORTED
+    c = lambda x: None if x is None else ctypes.c_void_p(x)
+
+    def call(dO=512, q=16, ws=1 << 20, nbytes=1 << 40, dq=None):
+        p = [q, 32, 48, 64, 80, 96, None, None, None, dO, None, dq] + [None] * 8
+        return lib.gdr_chunk_bwd(ctypes.byref(gdr.make_desc(**GOOD)), *[c(x) for x in p], c(ws), nbytes, None)
+    assert call(dO=None) == gdr.GDR_ERR_INVALID_ARG
+    assert call(dO=520) == gdr.GDR_ERR_INVALID_ARG      # misaligned
+    assert call(q=None) == gdr.GDR_ERR_INVALID_ARG
+    assert call(dq=8) == gdr.GDR_ERR_INVALID_ARG
+    assert call(ws=None) == gdr.GDR_ERR_WORKSPACE
+    assert call(nbytes=1000) == gdr.GDR_ERR_WORKSPACE

@@ -812,3 +812,67 @@ def test_layer_pipeline_projection_recurrence_output_gate():
     ry = oracle.output_gate(ro, gc["g"], norm_weight=nw)
     check("layer pipeline y", y.cpu().numpy(), ry, TOL_BF16)
     check("layer pipeline S_T", sT.cpu().numpy(), rs, TOL_BF16)
+
+
+# ----------------------------------------------------------------------------
+# backward: every gradient against the oracle's reverse-mode backward
+# ----------------------------------------------------------------------------
+
+def bwd_compare(x, tag, seed=5, do_bf16=False, with_dst=True, tol=None, **kw):
+    r = np.random.default_rng(seed)
+    B, H, T, dk = x["q"].shape
+    dv = x["v"].shape[-1]
+    dO = torch.from_numpy(r.standard_normal((B, H, T, dv))).float()
+    if do_bf16:
+        dO = dO.to(torch.bfloat16)
+    dST = torch.from_numpy(0.1 * r.standard_normal((B, H, dk, dv))).float() if with_dst else None
+    d = dev(x)
+    g = gdr.gdr_chunk_bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], dO.to(DEV),
+                          gamma=d["gamma"], z=d["z"], S0=d["S0"], dS_T=None if dST is None else dST.to(DEV), **kw)
+    torch.cuda.synchronize()
+    ref = oracle.backward(x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"], dO,
+                          gamma=x["gamma"], z=x["z"], S0=x["S0"], dS_T=dST, **kw)
+    tol = tol if tol is not None else tol_for(x)
+    for key in ("dq", "dk", "dv", "dlog_alpha", "db", "dw", "dgamma", "dz", "dS0"):
+        if ref[key] is None:
+            assert g[key] is None, key
+            continue
+        check(f"bwd {tag} {key}", g[key].cpu().numpy(), ref[key], tol)
+
+
+@pytest.mark.parametrize("name,B,H,T,d", [
+    ("gdn2", 1, 2, 200, 128), ("kda", 2, 2, 130, 128), ("tiny", 1, 1, 256, 64), ("gdn", 1, 2, 192, 128),
+    ("stress", 1, 2, 150, 128), ("gdn2", 2, 1, 64, 64)])
+def test_backward_small_cases(name, B, H, T, d):
+    wl = WORKLOADS[name].with_sizes(B=B, H=H, T=T, dk=d, dv=d)
+    bwd_compare(make_inputs(wl), f"{name} B{B} H{H} T{T} d{d}")
+
+
+def test_backward_fp32_inputs_and_bf16_upstream():
+    wl = WORKLOADS["gdn2"].with_sizes(B=1, H=2, T=100, dtype="f32")
+    bwd_compare(make_inputs(wl), "f32 inputs")
+    wl2 = WORKLOADS["gdn2"].with_sizes(B=1, H=2, T=100)
+    bwd_compare(make_inputs(wl2), "bf16 dO", do_bf16=True)
+
+
+def test_backward_options_and_edges():
+    wl = WORKLOADS["gdn2"].with_sizes(B=1, H=2, T=70)
+    x = make_inputs(wl)
+    bwd_compare(x, "no dS_T", with_dst=False)
+    bwd_compare({**x, "S0": None, "gamma": None, "z": None}, "no S0, no gain")
+    # without the pre-pass the keys must have unit norm for a bounded state
+    y = dict(x)
+    y["k"] = torch.nn.functional.normalize(x["k"].float(), dim=-1).to(x["k"].dtype)
+    bwd_compare(y, "no normalisation, scale", normalize_qk=False, scale=0.5)
+    bwd_compare(make_inputs(WORKLOADS["gdn2"].with_sizes(B=1, H=2, T=1)), "T1")
+
+
+def test_backward_empty_sequence_passes_the_state_gradient():
+    wl = WORKLOADS["gdn2"].with_sizes(B=1, H=2, T=0)
+    x = dev(make_inputs(wl))
+    dST = torch.randn(1, 2, 128, 128, device=DEV)
+    g = gdr.gdr_chunk_bwd(x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"],
+                          torch.empty(1, 2, 0, 128, device=DEV), gamma=x["gamma"], z=x["z"], S0=x["S0"], dS_T=dST)
+    torch.cuda.synchronize()
+    assert torch.equal(g["dS0"], dST)
+    assert torch.count_nonzero(g["dgamma"]) == 0
