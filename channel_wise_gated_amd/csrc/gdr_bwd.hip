@@ -38,20 +38,6 @@ __device__ __forceinline__ float ld_do(const void *p, size_t i, int bf) {
   return bf ? bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(p)[i]) : reinterpret_cast<const float *>(p)[i];
 }
 
-// Element [i][j] of a D x D state stored by the chain kernel: NS bf16 planes
-// of B-fragments per 16-column slice (row i = 32 ks + 16 h + 4 g + r sits in
-// lane j % 16 + 16 g, element 4 h + r, of fragment ks * NS + p).
-template <int D, int NS>
-__device__ __forceinline__ float state_at(const uint16_t *base, int i, int j) {
-  constexpr int NFR = (D / 32) * NS, FRAG = 512;
-  const int s = j >> 4, l16 = j & 15, ks = i >> 5, h = (i >> 4) & 1, g = (i >> 2) & 3, r = i & 3;
-  const uint16_t *f = base + (size_t)s * NFR * FRAG + (size_t)(ks * NS) * FRAG + (l16 + 16 * g) * 8 + 4 * h + r;
-  float v = 0.f;
-#pragma unroll
-  for (int p = 0; p < NS; ++p) v += bf16_bits_to_f32(f[p * FRAG]);
-  return v;
-}
-
 // ---------------------------------------------------------------------------
 // K1 prep: per chunk slot, M^T (plane by plane, in M's A-fragment layout) and
 // G = Q'^T dO (in N's accumulator-tile layout) for the reverse chain.
@@ -177,43 +163,69 @@ __global__ void __launch_bounds__(256) bwd_prepass_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // K4 Gram: per chunk slot, A (s <= t) and L (s < t) with exact pairwise decays
-// (e^{Lambda_t - Lambda_s} <= 1 for s <= t), then T^-1 = (I + L)^-1 column by
-// column (forward substitution).
+// (e^{Lambda_t - Lambda_s} <= 1 for s <= t), over the lower-triangle entries
+// only (thread -> 8 or 9 of the 2080), the channels staged 32 at a time; then
+// T^-1 = (I + L)^-1 column by column (forward substitution).
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ void __launch_bounds__(256) bwd_gram_kernel(BwdArgs a) {
-  constexpr int C = kBC, P = D + 1;
-  __shared__ float sh[4 * C * P + C * (C + 1)];
-  float *kn = sh, *kh = sh + C * P, *qt = sh + 2 * C * P, *lam = sh + 3 * C * P;
-  float *L = sh + 4 * C * P;  // [C][C + 1]
+  constexpr int C = kBC, CQ = 32, P = CQ + 1, NE = C * (C + 1) / 2, EPT = (NE + 255) / 256;
+  __shared__ float kn[C * P], kh[C * P], qt[C * P], lam[C * P];
+  __shared__ float L[C * (C + 1)], ti[C * (C + 1)];
   const size_t slot = blockIdx.x;
   const size_t base = slot * (size_t)C * D, cbase = slot * (size_t)C * C;
   const int tid = threadIdx.x;
-  for (int idx = tid; idx < C * D; idx += 256) {
-    const int t = idx / D, ch = idx % D;
-    kn[t * P + ch] = a.KN[base + idx];
-    kh[t * P + ch] = a.KH[base + idx];
-    qt[t * P + ch] = a.QT[base + idx];
-    lam[t * P + ch] = a.LAM[base + idx];
+  // this thread's entries: e = tid + 256 j over the lower triangle, row-major
+  int et[EPT], es[EPT];
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int e = min(tid + 256 * j, NE - 1);
+    int t = (int)((sqrtf(8.f * e + 1.f) - 1.f) * 0.5f);
+    while (t * (t + 1) / 2 > e) --t;
+    while ((t + 1) * (t + 2) / 2 <= e) ++t;
+    et[j] = t;
+    es[j] = e - t * (t + 1) / 2;
   }
-  __syncthreads();
-  for (int e = tid; e < C * C; e += 256) {
-    const int t = e / C, s = e % C;
-    float av = 0.f, lv = 0.f;
-    if (s <= t) {
-      for (int ch = 0; ch < D; ++ch) {
-        const float x = __expf(lam[t * P + ch] - lam[s * P + ch]) * kn[s * P + ch];
-        av += qt[t * P + ch] * x;
-        lv += kh[t * P + ch] * x;
-      }
+  float av[EPT], lv[EPT];
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) av[j] = lv[j] = 0.f;
+  for (int c0 = 0; c0 < D; c0 += CQ) {
+    __syncthreads();
+    for (int idx = tid; idx < C * CQ; idx += 256) {
+      const int t = idx / CQ, c = idx % CQ;
+      const size_t gi = base + t * D + c0 + c;
+      kn[t * P + c] = a.KN[gi];
+      kh[t * P + c] = a.KH[gi];
+      qt[t * P + c] = a.QT[gi];
+      lam[t * P + c] = a.LAM[gi];
     }
-    a.AM[cbase + e] = av;
-    L[t * (C + 1) + s] = s < t ? lv : 0.f;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      const int t = et[j], s = es[j];
+      float sa = 0.f, sl = 0.f;
+#pragma unroll 8
+      for (int c = 0; c < CQ; ++c) {
+        const float x = __expf(lam[t * P + c] - lam[s * P + c]) * kn[s * P + c];
+        sa += qt[t * P + c] * x;
+        sl += kh[t * P + c] * x;
+      }
+      av[j] += sa;
+      lv[j] += sl;
+    }
+  }
+  for (int e = tid; e < C * (C + 1); e += 256) L[e] = 0.f;
+  for (int e = tid; e < C * C; e += 256) a.AM[cbase + e] = 0.f;  // upper triangle
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    if (tid + 256 * j >= NE) continue;
+    const int t = et[j], s = es[j];
+    a.AM[cbase + t * C + s] = av[j];
+    if (s < t) L[t * (C + 1) + s] = lv[j];
   }
   __syncthreads();
-  // T^-1 column s (thread s): x_t = delta_ts - sum_{r < t} L[t][r] x_r, written
-  // into the (now free) kn region as [C][C + 1]
-  float *ti = kn;
+  // T^-1 column s (thread s): x_t = delta_ts - sum_{r < t} L[t][r] x_r
   if (tid < C) {
     const int s = tid;
     for (int t = 0; t < C; ++t) {
@@ -225,6 +237,58 @@ __global__ void __launch_bounds__(256) bwd_gram_kernel(BwdArgs a) {
   }
   __syncthreads();
   for (int e = tid; e < C * C; e += 256) a.TI[cbase + e] = ti[(e / C) * (C + 1) + e % C];
+}
+
+// ---------------------------------------------------------------------------
+// K4b states: per chunk slot, S0 and X from the chain's bf16 planes into fp32
+// row-major [D][D] (through LDS: coalesced reads of the planes, coalesced row
+// writes), and the row dots sum_j X[i][j] S0[i][j].
+// ---------------------------------------------------------------------------
+template <int D, int NS>
+__global__ void __launch_bounds__(256) bwd_states_kernel(BwdArgs a) {
+  constexpr int NFR = (D / 32) * NS, FRAG = 512;
+  __shared__ __align__(16) float s0[D * D];
+  __shared__ __align__(16) float xx[D * D];
+  const size_t slot = blockIdx.x;
+  const int tid = threadIdx.x;
+  const uint16_t *S0p = a.Sc + slot * NS * (size_t)D * D;
+  const uint16_t *Xp = a.Xc + slot * NS * (size_t)D * D;
+  // one (slice, k-step, lane) entry: 8 elements of one column, rows
+  // 32 ks + 16 h + 4 g + r for e = 4 h + r
+  for (int idx = tid; idx < (D / 16) * (D / 32) * 64; idx += 256) {
+    const int lane = idx & 63, ks = (idx >> 6) % (D / 32), sl = (idx >> 6) / (D / 32);
+    const int l16 = lane & 15, g = lane >> 4, col = 16 * sl + l16;
+    const size_t off = (size_t)sl * NFR * FRAG + (size_t)(ks * NS) * FRAG + lane * 8;
+    float vs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, vx[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < NS; ++p) {
+      const bf16x8 fs = *reinterpret_cast<const bf16x8 *>(S0p + off + p * FRAG);
+      const bf16x8 fx = *reinterpret_cast<const bf16x8 *>(Xp + off + p * FRAG);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        vs[e] += (float)fs[e];
+        vx[e] += (float)fx[e];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int row = 32 * ks + 16 * (e >> 2) + 4 * g + (e & 3);
+      s0[row * D + col] = vs[e];
+      xx[row * D + col] = vx[e];
+    }
+  }
+  __syncthreads();
+  float4 *S0f = reinterpret_cast<float4 *>(a.S0f + slot * (size_t)D * D);
+  float4 *Xf = reinterpret_cast<float4 *>(a.Xf + slot * (size_t)D * D);
+  for (int idx = tid; idx < D * D / 4; idx += 256) {
+    S0f[idx] = reinterpret_cast<const float4 *>(s0)[idx];
+    Xf[idx] = reinterpret_cast<const float4 *>(xx)[idx];
+  }
+  if (tid < D) {
+    float d = 0.f;
+    for (int j = 0; j < D; ++j) d += xx[tid * D + (j + tid) % D] * s0[tid * D + (j + tid) % D];
+    a.XS[slot * D + tid] = d;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -245,10 +309,9 @@ __global__ void __launch_bounds__(256) bwd_u_kernel(BwdArgs a) {
   const int tid = threadIdx.x;
   const bool act = tid < (C / TB) * NJB;
   const int tb = tid / NJB, jb = tid % NJB, t0 = tb * TB, j0 = jb * JB;
-  const uint16_t *S0p = a.Sc + slot * NS * (size_t)D * D;
-  const uint16_t *Xp = a.Xc + slot * NS * (size_t)D * D;
   // (a) R = V_hat - K_a S0
-  for (int idx = tid; idx < D * D; idx += 256) big[idx] = state_at<D, NS>(S0p, idx / D, idx % D);
+  for (int idx = tid; idx < D * D / 4; idx += 256)
+    reinterpret_cast<float4 *>(big)[idx] = reinterpret_cast<const float4 *>(a.S0f + slot * (size_t)D * D)[idx];
   for (int idx = tid; idx < C * D; idx += 256) r1[idx] = a.KH[base + idx] * __expf(a.LAM[base + idx]);
   for (int idx = tid; idx < C * (C + 1); idx += 256) {
     const int t = idx / (C + 1), s = idx % (C + 1);
@@ -303,7 +366,8 @@ __global__ void __launch_bounds__(256) bwd_u_kernel(BwdArgs a) {
     const int t = idx / (C + 1), s = idx % (C + 1);
     tc[idx] = s < C ? a.AM[cbase + t * C + s] : 0.f;
   }
-  for (int idx = tid; idx < D * D; idx += 256) big[idx] = state_at<D, NS>(Xp, idx / D, idx % D);
+  for (int idx = tid; idx < D * D / 4; idx += 256)
+    reinterpret_cast<float4 *>(big)[idx] = reinterpret_cast<const float4 *>(a.Xf + slot * (size_t)D * D)[idx];
   for (int idx = tid; idx < C * D; idx += 256) {
     const int ch = idx % D;
     r1[idx] = a.KN[base + idx] * __expf(a.LAM[base + (C - 1) * D + ch] - a.LAM[base + idx]);
@@ -403,10 +467,10 @@ __global__ void __launch_bounds__(256) bwd_dmat_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 template <int D, int NS>
 __global__ void __launch_bounds__(256) bwd_dproj_kernel(BwdArgs a) {
-  constexpr int C = kBC, IB = 4, NIB = D / IB, TB = C * D / (256 * IB);
-  __shared__ __align__(16) float st[D * D];  // [j][i]: S0 transposed, then X transposed
-  __shared__ float r1[C * D];                // dO, then U
-  __shared__ float r2[C * D];                // dU~
+  constexpr int C = kBC, IB = 4, NIB = D / IB, TB = C * D / (256 * IB), SP = D + 1;
+  __shared__ float st[D * SP];  // [i][j] (rows padded): S0, then X
+  __shared__ float r1[C * D];   // dO, then U
+  __shared__ float r2[C * D];   // dU~
   const size_t slot = blockIdx.x;
   const size_t bh = slot / a.NC;
   const int c = (int)(slot % a.NC);
@@ -414,12 +478,8 @@ __global__ void __launch_bounds__(256) bwd_dproj_kernel(BwdArgs a) {
   const int tid = threadIdx.x;
   const bool act = tid < (C / TB) * NIB;
   const int tb = tid / NIB, ib = tid % NIB, t0 = tb * TB, i0 = ib * IB;
-  const uint16_t *S0p = a.Sc + slot * NS * (size_t)D * D;
-  const uint16_t *Xp = a.Xc + slot * NS * (size_t)D * D;
-  for (int idx = tid; idx < D * D; idx += 256) {
-    const int i = idx / D, j = idx % D;
-    st[j * D + i] = state_at<D, NS>(S0p, i, j);
-  }
+  const float *S0f = a.S0f + slot * (size_t)D * D, *Xf = a.Xf + slot * (size_t)D * D;
+  for (int idx = tid; idx < D * D; idx += 256) st[(idx / D) * SP + idx % D] = S0f[idx];
   for (int idx = tid; idx < C * D; idx += 256) {
     const int t = idx / D, j = idx % D, tt = c * C + t;
     r1[idx] = tt < a.T ? ld_do(a.dO, (bh * a.T + tt) * D + j, a.do_bf16) : 0.f;
@@ -432,13 +492,19 @@ __global__ void __launch_bounds__(256) bwd_dproj_kernel(BwdArgs a) {
     for (int u = 0; u < TB; ++u)
 #pragma unroll
       for (int v = 0; v < IB; ++v) aq[u][v] = ak[u][v] = 0.f;
+#pragma unroll 2
     for (int j = 0; j < D; ++j) {
-      const float4 s4 = *reinterpret_cast<const float4 *>(&st[j * D + i0]);
+      float sv[IB];
+#pragma unroll
+      for (int v = 0; v < IB; ++v) sv[v] = st[(i0 + v) * SP + j];
 #pragma unroll
       for (int u = 0; u < TB; ++u) {
         const float dv = r1[(t0 + u) * D + j], du = r2[(t0 + u) * D + j];
-        aq[u][0] += dv * s4.x; aq[u][1] += dv * s4.y; aq[u][2] += dv * s4.z; aq[u][3] += dv * s4.w;
-        ak[u][0] -= du * s4.x; ak[u][1] -= du * s4.y; ak[u][2] -= du * s4.z; ak[u][3] -= du * s4.w;
+#pragma unroll
+        for (int v = 0; v < IB; ++v) {
+          aq[u][v] += dv * sv[v];
+          ak[u][v] -= du * sv[v];
+        }
       }
     }
 #pragma unroll
@@ -450,10 +516,7 @@ __global__ void __launch_bounds__(256) bwd_dproj_kernel(BwdArgs a) {
       }
   }
   __syncthreads();
-  for (int idx = tid; idx < D * D; idx += 256) {
-    const int i = idx / D, j = idx % D;
-    st[j * D + i] = state_at<D, NS>(Xp, i, j);
-  }
+  for (int idx = tid; idx < D * D; idx += 256) st[(idx / D) * SP + idx % D] = Xf[idx];
   for (int idx = tid; idx < C * D; idx += 256) r1[idx] = a.U[base + idx];
   __syncthreads();
   if (act) {
@@ -461,12 +524,16 @@ __global__ void __launch_bounds__(256) bwd_dproj_kernel(BwdArgs a) {
     for (int u = 0; u < TB; ++u)
 #pragma unroll
       for (int v = 0; v < IB; ++v) aq[u][v] = 0.f;
+#pragma unroll 2
     for (int j = 0; j < D; ++j) {
-      const float4 x4 = *reinterpret_cast<const float4 *>(&st[j * D + i0]);
+      float xv[IB];
+#pragma unroll
+      for (int v = 0; v < IB; ++v) xv[v] = st[(i0 + v) * SP + j];
 #pragma unroll
       for (int u = 0; u < TB; ++u) {
         const float uv = r1[(t0 + u) * D + j];
-        aq[u][0] += uv * x4.x; aq[u][1] += uv * x4.y; aq[u][2] += uv * x4.z; aq[u][3] += uv * x4.w;
+#pragma unroll
+        for (int v = 0; v < IB; ++v) aq[u][v] += uv * xv[v];
       }
     }
 #pragma unroll
@@ -477,67 +544,87 @@ __global__ void __launch_bounds__(256) bwd_dproj_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// K8 Gram backprop: one workgroup (64 threads) per (chunk slot, 64 channels),
-// a thread per channel.  For every pair s <= t with p = e^{Lambda_t - Lambda_s}:
-//   RA_t += dA_ts k_s p,  RL_t += dL_ts k_s p            (row sums)
-//   CS_s += (dA_ts q_tilde_t + dL_ts k_hat_t) p          (column sums)
-// then, per token, the gradients of q_tilde, k_hat, k and Lambda, and the
-// reverse cumulative sum of dLambda over the chunk (= d log alpha).
+// K8 Gram backprop: one workgroup (256 threads) per (chunk slot, 32 channels):
+// thread (channel c, token group tg) owns tokens t = tg, tg + 8, ...  With
+// p = e^{Lambda_t - Lambda_s}, s <= t, two passes over the pairs:
+//   rows    RA_t = sum_s dA_ts k_s p,  RL_t = sum_s dL_ts k_s p
+//   columns CS_s = sum_t (dA_ts q_tilde_t + dL_ts k_hat_t) p
+// (each accumulated in registers for the thread's own tokens), then per token
+// the gradients of q_tilde, k_hat, k and Lambda, and the reverse cumulative
+// sum of dLambda over the chunk (= d log alpha).
 // ---------------------------------------------------------------------------
 template <int D, int NS>
-__global__ void __launch_bounds__(64) bwd_gramback_kernel(BwdArgs a) {
-  constexpr int C = kBC, CW = 64;
-  __shared__ float kn[C][CW], kh[C][CW], qt[C][CW], lam[C][CW], cs[C][CW];
+__global__ void __launch_bounds__(256) bwd_gramback_kernel(BwdArgs a) {
+  constexpr int C = kBC, CW = 32, NG = 8, TPG = C / NG;
+  __shared__ float kn[C][CW], kh[C][CW], qt[C][CW], lam[C][CW];
+  __shared__ float dA[C][C + 1], dL[C][C + 1];
+  __shared__ float dlam[C][CW];
+  __shared__ float skp_g[NG][CW];
   const size_t slot = blockIdx.x / (D / CW);
-  const int cb = (int)(blockIdx.x % (D / CW)), lane = threadIdx.x, ch = cb * CW + lane;
+  const int cb = (int)(blockIdx.x % (D / CW)), tid = threadIdx.x;
+  const int cl = tid % CW, tg = tid / CW, ch = cb * CW + cl;
   const size_t base = slot * (size_t)C * D, cbase = slot * (size_t)C * C;
-  for (int t = 0; t < C; ++t) {
-    kn[t][lane] = a.KN[base + t * D + ch];
-    kh[t][lane] = a.KH[base + t * D + ch];
-    qt[t][lane] = a.QT[base + t * D + ch];
-    lam[t][lane] = a.LAM[base + t * D + ch];
-    cs[t][lane] = 0.f;
+  for (int idx = tid; idx < C * CW; idx += 256) {
+    const int t = idx / CW, c = idx % CW;
+    const size_t gi = base + t * D + cb * CW + c;
+    kn[t][c] = a.KN[gi];
+    kh[t][c] = a.KH[gi];
+    qt[t][c] = a.QT[gi];
+    lam[t][c] = a.LAM[gi];
   }
-  // (one wave: LDS written and read by the same lanes' wave, in order)
-  const float *DA = a.DA + cbase, *DL = a.DL + cbase;
-  for (int t = 0; t < C; ++t) {
-    float ra = 0.f, rl = 0.f;
-    const float lt = lam[t][lane], qv = qt[t][lane], hv = kh[t][lane];
+  for (int idx = tid; idx < C * C; idx += 256) {
+    dA[idx / C][idx % C] = a.DA[cbase + idx];
+    dL[idx / C][idx % C] = a.DL[cbase + idx];
+  }
+  __syncthreads();
+  float ra[TPG], rl[TPG], cs[TPG];
+#pragma unroll
+  for (int u = 0; u < TPG; ++u) {
+    const int t = tg + NG * u;
+    const float lt = lam[t][cl];
+    float sa = 0.f, sl = 0.f;
+#pragma unroll 4
     for (int s = 0; s <= t; ++s) {
-      const float p = __expf(lt - lam[s][lane]);
-      const float da = DA[t * C + s], dl = DL[t * C + s];
-      const float x = kn[s][lane] * p;
-      ra += da * x;
-      rl += dl * x;
-      cs[s][lane] += (da * qv + dl * hv) * p;
+      const float x = kn[s][cl] * __expf(lt - lam[s][cl]);
+      sa += dA[t][s] * x;
+      sl += dL[t][s] * x;
     }
-    a.DQT[base + t * D + ch] = ra;  // row sums, completed below
-    a.DKT[base + t * D + ch] = rl;
+    ra[u] = sa;
+    rl[u] = sl;
+    const int sc = t;  // the column this thread owns for the same u
+    const float ls = lam[sc][cl];
+    float c2 = 0.f;
+#pragma unroll 4
+    for (int tt = sc; tt < C; ++tt)
+      c2 += (dA[tt][sc] * qt[tt][cl] + dL[tt][sc] * kh[tt][cl]) * __expf(lam[tt][cl] - ls);
+    cs[u] = c2;
   }
-  const float lc = lam[C - 1][lane], ac = __expf(lc);
-  float sum_kp = 0.f;
-  // pass 1: per-token gradients; dLambda into cs (column sums consumed)
-  for (int t = 0; t < C; ++t) {
-    const float at = __expf(lam[t][lane]), rat = __expf(lc - lam[t][lane]);
-    const float dqa = a.DQA[base + t * D + ch], dka = a.DKA[base + t * D + ch], dkp = a.DKP[base + t * D + ch];
-    const float ra = a.DQT[base + t * D + ch], rl = a.DKT[base + t * D + ch];
-    const float qv = qt[t][lane], hv = kh[t][lane], kv = kn[t][lane], csv = cs[t][lane];
-    a.DQT[base + t * D + ch] = at * dqa + ra;
-    a.DKT[base + t * D + ch] = at * dka + rl;
-    a.DKN[base + t * D + ch] = rat * dkp + csv;
-    cs[t][lane] = qv * at * dqa + hv * at * dka - kv * rat * dkp + qv * ra + hv * rl - kv * csv;
-    sum_kp += kv * rat * dkp;
+  const float lc = lam[C - 1][cl];
+  float skp = 0.f;
+#pragma unroll
+  for (int u = 0; u < TPG; ++u) {
+    const int t = tg + NG * u;
+    const size_t gi = base + t * D + ch;
+    const float at = __expf(lam[t][cl]), rat = __expf(lc - lam[t][cl]);
+    const float dqa = a.DQA[gi], dka = a.DKA[gi], dkp = a.DKP[gi];
+    const float qv = qt[t][cl], hv = kh[t][cl], kv = kn[t][cl];
+    a.DQT[gi] = at * dqa + ra[u];
+    a.DKT[gi] = at * dka + rl[u];
+    a.DKN[gi] = rat * dkp + cs[u];
+    dlam[t][cl] = qv * at * dqa + hv * at * dka - kv * rat * dkp + qv * ra[u] + hv * rl[u] - kv * cs[u];
+    skp += kv * rat * dkp;
   }
-  // the chunk-end decay: K' and Diag(a_C) S0 in the end state
-  const uint16_t *S0p = a.Sc + slot * NS * (size_t)D * D;
-  const uint16_t *Xp = a.Xc + slot * NS * (size_t)D * D;
-  float xs = 0.f;
-  for (int j = 0; j < D; ++j) xs += state_at<D, NS>(Xp, ch, j) * state_at<D, NS>(S0p, ch, j);
-  cs[C - 1][lane] += sum_kp + ac * xs;
-  float run = 0.f;
-  for (int t = C - 1; t >= 0; --t) {
-    run += cs[t][lane];
-    a.DLA[base + t * D + ch] = run;
+  skp_g[tg][cl] = skp;
+  __syncthreads();
+  if (tg == 0) {
+    // the chunk-end decay: K' and Diag(a_C) S0 in the end state
+    float run = __expf(lc) * a.XS[slot * D + ch];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) run += skp_g[g][cl];
+    for (int t = C - 1; t >= 0; --t) {
+      run += dlam[t][cl];
+      a.DLA[base + t * D + ch] = run;
+    }
   }
 }
 
@@ -667,10 +754,11 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
   }
   hipLaunchKernelGGL((bwd_prepass_kernel<D, BF>), dim3(nch), dim3(256), 0, st, a);
   hipLaunchKernelGGL((bwd_gram_kernel<D>), dim3(nch), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((bwd_states_kernel<D, NS>), dim3(nch), dim3(256), 0, st, a);
   hipLaunchKernelGGL((bwd_u_kernel<D, NS>), dim3(nch), dim3(256), 0, st, a);
   hipLaunchKernelGGL((bwd_dmat_kernel<D>), dim3(nch), dim3(256), 0, st, a);
   hipLaunchKernelGGL((bwd_dproj_kernel<D, NS>), dim3(nch), dim3(256), 0, st, a);
-  hipLaunchKernelGGL((bwd_gramback_kernel<D, NS>), dim3(nch * (D / 64)), dim3(64), 0, st, a);
+  hipLaunchKernelGGL((bwd_gramback_kernel<D, NS>), dim3(nch * (D / 32)), dim3(256), 0, st, a);
   hipLaunchKernelGGL((bwd_final_kernel<D, BF>), dim3(nch), dim3(256), 0, st, a);
   if (a.dgamma && a.gamma)
     hipLaunchKernelGGL((bwd_dgamma_kernel<D>), dim3((unsigned)((a.H * D + 255) / 256)), dim3(256), 0, st, a);
@@ -706,7 +794,13 @@ size_t bwd_workspace(BwdArgs *a, ChunkArgs *f, void *ws, int B, int H, int T, in
   float *ccp[4];
   for (int i = 0; i < 4; ++i) ccp[i] = static_cast<float *>(take(nch * (size_t)kBC * kBC * 4));
   float *gp = static_cast<float *>(take(nch * (size_t)D * 4));
+  float *s0f = static_cast<float *>(take(nch * (size_t)D * D * 4));
+  float *xf = static_cast<float *>(take(nch * (size_t)D * D * 4));
+  float *xs = static_cast<float *>(take(nch * (size_t)D * 4));
   if (a) {
+    a->S0f = s0f;
+    a->Xf = xf;
+    a->XS = xs;
     a->Mt = static_cast<uint16_t *>(mt);
     a->Xc = static_cast<uint16_t *>(xc);
     a->Gn = static_cast<float *>(gn);

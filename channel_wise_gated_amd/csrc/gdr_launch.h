@@ -72,6 +72,8 @@ struct BwdArgs {
   float *KN, *KH, *QT, *VH, *LAM, *U, *DU, *DQA, *DKA, *DKP, *DQT, *DKT, *DKN, *DLA;
   float *AM, *TI, *DA, *DL;      // [slot][64][64] fp32
   float *gpart;                  // [slot][D] partial sums of dgamma
+  float *S0f, *Xf;               // [slot][D][D] fp32 chunk-start states and chunk-end state gradients
+  float *XS;                     // [slot][D] row dots of the two
   float *dq, *dk, *dv, *dla, *db, *dw, *dz, *dgamma;  // outputs (each may be null)
 };
 // Workspace of the backward: the forward's chunk workspace (C = 64; its fields
