@@ -8,8 +8,9 @@ workload: B1 H16 T32768 dk=dv=128, bf16 inputs, fp32 output and state, chunk
 the same run and reported beside it: the decode step (256 sequences x 16
 heads, fp32 128 x 128 states, 1024 consecutive steps), the same long-context
 shape with scalar gates (one decay and one beta per token, Gated DeltaNet),
-and the layer path around the recurrence (the five-gate low-rank projection,
-then the forward with the fused RMSNorm + output gate).
+the layer path around the recurrence (the five-gate low-rank projection,
+then the forward with the fused RMSNorm + output gate), and the backward
+pass (gdr_chunk_bwd) over the long-context shape.
 
 Prints one JSON line.  Per-kernel durations come from HIP events recorded on
 the stream the kernels run on; the roofline object describes the kernel with
@@ -190,6 +191,35 @@ def timed_layer(x, C, steps, warmup):
             "gate_proj_bytes": p_bytes}
 
 
+def timed_bwd(x, steps, warmup):
+    """The backward pass over the long-context inputs (chunk 64, every
+    gradient incl. dS0 from an upstream dS_T): random fp32 dO.  HIP events on
+    the current stream, median over `steps`; gradients and workspace come
+    from torch's caching allocator (no device allocation after warm-up)."""
+    import torch
+
+    from channel_wise_gated_amd import gdr
+    B, H, T, dk = x["q"].shape
+    dv = x["v"].shape[-1]
+    gen = torch.Generator(device="cuda").manual_seed(4099)
+    dO = torch.randn(B, H, T, dv, generator=gen, device="cuda")
+    dST = 0.1 * torch.randn(B, H, dk, dv, generator=gen, device="cuda")
+    call = lambda: gdr.gdr_chunk_bwd(x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"], dO,
+                                     gamma=x["gamma"], z=x["z"], S0=x["S0"], dS_T=dST)
+    for _ in range(max(warmup, 1)):
+        call()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for e in ev:
+        e[0].record()
+        call()
+        e[1].record()
+    torch.cuda.synchronize()
+    ms = sorted(e[0].elapsed_time(e[1]) for e in ev)[steps // 2]
+    return {"workload": f"bwd B{B} H{H} T{T} dk{dk} dv{dv} chunk64, grads of q,k,v,log-decay,b,w,z,gain,S0",
+            "steps": steps, "ms_per_step": round(ms, 4), "tokens_s": round(B * T / (ms / 1e3), 1)}
+
+
 def copy_calibration(mib):
     """A plain device-to-device copy of `mib` MiB (fp32), three times: the
     reference dispatch against which HBM byte counters are scaled."""
@@ -242,6 +272,7 @@ def main():
                     help="whole calls of the scalar-gate (Gated DeltaNet) leg; 0 skips it")
     ap.add_argument("--layer-steps", type=int, default=20,
                     help="steps of the gate projection + gated forward leg; 0 skips it")
+    ap.add_argument("--bwd-steps", type=int, default=10, help="0 skips the backward leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="also run a plain MIB-MiB copy (reference for HBM byte counters)")
@@ -316,6 +347,11 @@ def main():
         layer = timed_layer(x, C, args.layer_steps, min(args.warmup, 5))
         torch.cuda.empty_cache()
 
+    # backward over the stress inputs
+    if args.bwd_steps > 0:
+        bwd = timed_bwd(x, args.bwd_steps, min(args.warmup, 3))
+        torch.cuda.empty_cache()
+
     # decode
     dwl = WORKLOADS["decode"]
     dsteps = args.decode_steps
@@ -346,6 +382,8 @@ def main():
                        "tokens_s": round(gwl.B * gwl.T / (g_ms / 1e3), 1)}
     if args.layer_steps > 0:
         line["layer"] = layer
+    if args.bwd_steps > 0:
+        line["bwd"] = bwd
     if dsteps > 0:
         line["decode"] = {"workload": f"decode {dwl.B} seq x H{dwl.H}, fp32 state {dwl.dk}x{dwl.dv}, "
                                       f"{dsteps} steps", "us_per_step": round(d_us, 2),

@@ -876,3 +876,38 @@ def test_backward_empty_sequence_passes_the_state_gradient():
     torch.cuda.synchronize()
     assert torch.equal(g["dS0"], dST)
     assert torch.count_nonzero(g["dgamma"]) == 0
+
+
+
+@pytest.mark.timeout(600)
+def test_backward_full_size_sampled():
+    """The long-context shape (B1 H16 T32768 d128, bf16) on the GPU as one
+    call; two sampled heads' gradients through the oracle."""
+    wl = WORKLOADS["stress"]
+    print(f"full-size backward B{wl.B} H{wl.H} T{wl.T}", flush=True)
+    xd = make_inputs_device(wl, DEV, seed=11)
+    g0 = torch.Generator(device=DEV).manual_seed(23)
+    dO = torch.randn(wl.B, wl.H, wl.T, wl.dv, device=DEV, generator=g0)
+    dST = 0.1 * torch.randn(wl.B, wl.H, wl.dk, wl.dv, device=DEV, generator=g0)
+    g = gdr.gdr_chunk_bwd(xd["q"], xd["k"], xd["v"], xd["log_alpha"], xd["b"], xd["w"], dO,
+                          gamma=xd["gamma"], z=xd["z"], S0=xd["S0"], dS_T=dST)
+    torch.cuda.synchronize()
+    for key in ("dq", "dk", "dv", "dlog_alpha", "dz", "dS0"):
+        assert bool(torch.isfinite(g[key]).all()), key
+    for h in (3, 14):
+        xs = {}
+        for key, val in xd.items():
+            if val is None:
+                xs[key] = None
+            elif key == "gamma":
+                xs[key] = val[h:h + 1].cpu()
+            else:
+                xs[key] = val[:, h:h + 1].cpu()
+        ref = oracle.backward(xs["q"], xs["k"], xs["v"], xs["log_alpha"], xs["b"], xs["w"],
+                              dO[:, h:h + 1].cpu(), gamma=xs["gamma"], z=xs["z"], S0=xs["S0"],
+                              dS_T=dST[:, h:h + 1].cpu())
+        for key in ("dq", "dk", "dv", "dlog_alpha", "db", "dw", "dz", "dS0", "dgamma"):
+            if ref[key] is None:
+                continue
+            got = g[key][h:h + 1] if key == "dgamma" else g[key][:, h:h + 1]
+            check(f"bwd full T{wl.T} head {h} {key}", got.cpu().numpy(), ref[key], TOL_BF16)
