@@ -292,255 +292,219 @@ __global__ void __launch_bounds__(256) bwd_states_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// K5: per chunk slot, U = T^-1 (V_hat - K_a S0) and dU~ = T^-T (A^T dO + K' X).
-// Thread tile: TB tokens x 4 columns.
+// K5: per chunk slot, the dense products of the chunk system's reverse, on the
+// fp32 matrix cores (v_mfma_f32_16x16x4_f32):
+//   R   = V_hat - K_a S0       U  = T^-1 R            dQ_a = dO S0^T
+//   dA  = dO U^T (s <= t)      Z  = A^T dO + K' X     dK'  = U X^T
+//   dU~ = T^-T Z               dL = -dU~ U^T (s < t)  dK_a = -dU~ S0^T
+// Wave w owns token rows 16w..16w+15 of every C x D result; of the C x C
+// results it owns the row tiles w (dA) and 3 - w (dL), so that the triangles
+// give every wave the same number of tiles.  In a 16x16x4 MFMA, lane
+// (l16, g) = (lane % 16, lane / 16) supplies A[l16][k] and B[k][l16] for one
+// k and receives D[4g + r][l16], r = 0..3.  A k-block of 16 takes four MFMAs,
+// lane group g supplying k = 16 kb + 4 g + e at step e, so every lane reads
+// its A values (and, for products with a transposed B, its B values) as one
+// float4.  LDS rows are padded by 4 floats: conflict-free for both access
+// patterns.
 // ---------------------------------------------------------------------------
-template <int D, int NS>
-__global__ void __launch_bounds__(256) bwd_u_kernel(BwdArgs a) {
-  constexpr int C = kBC, JB = 4, NJB = D / JB, TB = C * D / (256 * JB);
-  __shared__ __align__(16) float big[D * D];   // S0, then X   ([i][j])
-  __shared__ __align__(16) float r1[C * D];    // K_a, R, then K'
-  __shared__ __align__(16) float r2[C * D];    // dO, then Z
-  __shared__ float tc[C * (C + 1)];            // T^-1, A, then T^-1
-  const size_t slot = blockIdx.x;
-  const size_t bh = slot / a.NC;
-  const int c = (int)(slot % a.NC);
-  const size_t base = slot * (size_t)C * D, cbase = slot * (size_t)C * C;
-  const int tid = threadIdx.x;
-  const bool act = tid < (C / TB) * NJB;
-  const int tb = tid / NJB, jb = tid % NJB, t0 = tb * TB, j0 = jb * JB;
-  // (a) R = V_hat - K_a S0
-  for (int idx = tid; idx < D * D / 4; idx += 256)
-    reinterpret_cast<float4 *>(big)[idx] = reinterpret_cast<const float4 *>(a.S0f + slot * (size_t)D * D)[idx];
-  for (int idx = tid; idx < C * D; idx += 256) r1[idx] = a.KH[base + idx] * __expf(a.LAM[base + idx]);
-  for (int idx = tid; idx < C * (C + 1); idx += 256) {
-    const int t = idx / (C + 1), s = idx % (C + 1);
-    tc[idx] = s < C ? a.TI[cbase + t * C + s] : 0.f;
+__device__ __forceinline__ f32x4 mfma4(float x, float y, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(x, y, c, 0, 0, 0);
+}
+
+// four consecutive dO values (fp32 or bf16)
+__device__ __forceinline__ f32x4 ld_do4(const void *p, size_t i, int bf) {
+  if (bf) {
+    const uint2 r = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(p) + i);
+    return f32x4{__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u), __uint_as_float(r.y << 16),
+                 __uint_as_float(r.y & 0xffff0000u)};
   }
-  __syncthreads();
-  float acc[TB][JB];
-  if (act) {
+  const float4 v = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(p) + i);
+  return f32x4{v.x, v.y, v.z, v.w};
+}
+
+// acc[ct] += A B over k-blocks kb0..kb1-1; B[k][col] row-major in LDS (stride sp)
+template <int NK, int NT>
+__device__ __forceinline__ void mm_nn(f32x4 (&acc)[NT], const f32x4 (&af)[NK], const float *B, int sp, int kb0,
+                                      int kb1, int g, int l16) {
 #pragma unroll
-    for (int u = 0; u < TB; ++u)
+  for (int kb = 0; kb < NK; ++kb) {
+    if (kb < kb0 || kb >= kb1) continue;  // wave-uniform
 #pragma unroll
-      for (int v = 0; v < JB; ++v) acc[u][v] = 0.f;
-    for (int i = 0; i < D; ++i) {
-      const float4 s4 = *reinterpret_cast<const float4 *>(&big[i * D + j0]);
+    for (int e = 0; e < 4; ++e) {
+      const float *brow = B + (16 * kb + 4 * g + e) * sp + l16;
 #pragma unroll
-      for (int u = 0; u < TB; ++u) {
-        const float kv = r1[(t0 + u) * D + i];
-        acc[u][0] += kv * s4.x; acc[u][1] += kv * s4.y; acc[u][2] += kv * s4.z; acc[u][3] += kv * s4.w;
-      }
-    }
-  }
-  __syncthreads();
-  if (act) {
-#pragma unroll
-    for (int u = 0; u < TB; ++u)
-#pragma unroll
-      for (int v = 0; v < JB; ++v) r1[(t0 + u) * D + j0 + v] = a.VH[base + (t0 + u) * D + j0 + v] - acc[u][v];
-  }
-  __syncthreads();
-  // (b) U = T^-1 R
-  if (act) {
-#pragma unroll
-    for (int u = 0; u < TB; ++u) {
-      const int t = t0 + u;
-      float x[JB] = {0.f, 0.f, 0.f, 0.f};
-      for (int s = 0; s <= t; ++s) {
-        const float tv = tc[t * (C + 1) + s];
-        const float4 r4 = *reinterpret_cast<const float4 *>(&r1[s * D + j0]);
-        x[0] += tv * r4.x; x[1] += tv * r4.y; x[2] += tv * r4.z; x[3] += tv * r4.w;
-      }
-#pragma unroll
-      for (int v = 0; v < JB; ++v) a.U[base + t * D + j0 + v] = x[v];
-    }
-  }
-  __syncthreads();
-  // (c) Z = A^T dO + K' X
-  for (int idx = tid; idx < C * D; idx += 256) {
-    const int t = idx / D, j = idx % D, tt = c * C + t;
-    r2[idx] = tt < a.T ? ld_do(a.dO, (bh * a.T + tt) * D + j, a.do_bf16) : 0.f;
-  }
-  for (int idx = tid; idx < C * (C + 1); idx += 256) {
-    const int t = idx / (C + 1), s = idx % (C + 1);
-    tc[idx] = s < C ? a.AM[cbase + t * C + s] : 0.f;
-  }
-  for (int idx = tid; idx < D * D / 4; idx += 256)
-    reinterpret_cast<float4 *>(big)[idx] = reinterpret_cast<const float4 *>(a.Xf + slot * (size_t)D * D)[idx];
-  for (int idx = tid; idx < C * D; idx += 256) {
-    const int ch = idx % D;
-    r1[idx] = a.KN[base + idx] * __expf(a.LAM[base + (C - 1) * D + ch] - a.LAM[base + idx]);
-  }
-  __syncthreads();
-  if (act) {
-#pragma unroll
-    for (int u = 0; u < TB; ++u)
-#pragma unroll
-      for (int v = 0; v < JB; ++v) acc[u][v] = 0.f;
-    // A^T dO: Z[s][j] = sum_{t >= s} A[t][s] dO[t][j]
-    for (int t = 0; t < C; ++t) {
-      const float4 d4 = *reinterpret_cast<const float4 *>(&r2[t * D + j0]);
-#pragma unroll
-      for (int u = 0; u < TB; ++u) {
-        const float av = tc[t * (C + 1) + t0 + u];  // zero for t < s (A is lower)
-        acc[u][0] += av * d4.x; acc[u][1] += av * d4.y; acc[u][2] += av * d4.z; acc[u][3] += av * d4.w;
-      }
-    }
-    // K' X
-    for (int i = 0; i < D; ++i) {
-      const float4 x4 = *reinterpret_cast<const float4 *>(&big[i * D + j0]);
-#pragma unroll
-      for (int u = 0; u < TB; ++u) {
-        const float kv = r1[(t0 + u) * D + i];
-        acc[u][0] += kv * x4.x; acc[u][1] += kv * x4.y; acc[u][2] += kv * x4.z; acc[u][3] += kv * x4.w;
-      }
-    }
-  }
-  __syncthreads();
-  if (act) {
-#pragma unroll
-    for (int u = 0; u < TB; ++u)
-#pragma unroll
-      for (int v = 0; v < JB; ++v) r2[(t0 + u) * D + j0 + v] = acc[u][v];
-  }
-  for (int idx = tid; idx < C * (C + 1); idx += 256) {
-    const int t = idx / (C + 1), s = idx % (C + 1);
-    tc[idx] = s < C ? a.TI[cbase + t * C + s] : 0.f;
-  }
-  __syncthreads();
-  // (d) dU~ = T^-T Z: dU~[s][j] = sum_{t >= s} T^-1[t][s] Z[t][j]
-  if (act) {
-#pragma unroll
-    for (int u = 0; u < TB; ++u) {
-      const int s = t0 + u;
-      float x[JB] = {0.f, 0.f, 0.f, 0.f};
-      for (int t = s; t < C; ++t) {
-        const float tv = tc[t * (C + 1) + s];
-        const float4 z4 = *reinterpret_cast<const float4 *>(&r2[t * D + j0]);
-        x[0] += tv * z4.x; x[1] += tv * z4.y; x[2] += tv * z4.z; x[3] += tv * z4.w;
-      }
-#pragma unroll
-      for (int v = 0; v < JB; ++v) a.DU[base + s * D + j0 + v] = x[v];
+      for (int ct = 0; ct < NT; ++ct) acc[ct] = mfma4(af[kb][e], brow[16 * ct], acc[ct]);
     }
   }
 }
 
-// ---------------------------------------------------------------------------
-// K6: per chunk slot, dA = dO U^T (s <= t) and dL = -dU~ U^T (s < t).
-// ---------------------------------------------------------------------------
+// acc[ct] += A Y^T for column tiles ct < ct1; Y[col][k] row-major in LDS
+template <int NK, int NT>
+__device__ __forceinline__ void mm_nt(f32x4 (&acc)[NT], const f32x4 (&af)[NK], const float *Y, int sp, int ct1,
+                                      int g, int l16) {
+#pragma unroll
+  for (int kb = 0; kb < NK; ++kb)
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) {
+      if (ct >= ct1) continue;  // wave-uniform
+      const f32x4 b4 = *reinterpret_cast<const f32x4 *>(Y + (16 * ct + l16) * sp + 16 * kb + 4 * g);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[ct] = mfma4(af[kb][e], b4[e], acc[ct]);
+    }
+}
+
+template <int NT>
+__device__ __forceinline__ void zero_acc(f32x4 (&acc)[NT]) {
+#pragma unroll
+  for (int ct = 0; ct < NT; ++ct) acc[ct] = zero4();
+}
+
 template <int D>
-__global__ void __launch_bounds__(256) bwd_dmat_kernel(BwdArgs a) {
-  constexpr int C = kBC, P = D + 1;
-  __shared__ float sh[3 * C * P];
-  float *dos = sh, *dus = sh + C * P, *us = sh + 2 * C * P;
+__global__ void __launch_bounds__(256) bwd_mm_kernel(BwdArgs a) {
+  constexpr int C = kBC, SP = D + 4, NKB = D / 16, NCT = D / 16, NTC = C / 16;
+  constexpr int BBR = 2 * C > D ? 2 * C : D;
+  static_assert(NTC == 4, "four waves, one 16-token row tile each");
+  __shared__ __align__(16) float ss[D * SP];    // S0, then X, then dU~ (rows < C)
+  __shared__ __align__(16) float bb[BBR * SP];  // rows < C: R, dO, Z; rows C..2C-1: U; last: S0
+  float *bt = bb, *bu = bb + C * SP;
   const size_t slot = blockIdx.x;
   const size_t bh = slot / a.NC;
   const int c = (int)(slot % a.NC);
   const size_t base = slot * (size_t)C * D, cbase = slot * (size_t)C * C;
-  const int tid = threadIdx.x;
-  for (int idx = tid; idx < C * D; idx += 256) {
-    const int t = idx / D, j = idx % D, tt = c * C + t;
-    dos[t * P + j] = tt < a.T ? ld_do(a.dO, (bh * a.T + tt) * D + j, a.do_bf16) : 0.f;
-    dus[t * P + j] = a.DU[base + idx];
-    us[t * P + j] = a.U[base + idx];
-  }
-  __syncthreads();
-  for (int e = tid; e < C * C; e += 256) {
-    const int t = e / C, s = e % C;
-    float da = 0.f, dl = 0.f;
-    if (s <= t) {
-      for (int j = 0; j < D; ++j) {
-        const float uv = us[s * P + j];
-        da += dos[t * P + j] * uv;
-        dl -= dus[t * P + j] * uv;
-      }
-    }
-    a.DA[cbase + e] = da;
-    a.DL[cbase + e] = s < t ? dl : 0.f;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// K7: per chunk slot, dQ_a = dO S0^T, dK_a = -dU~ S0^T, dK' = U X^T.
-// Thread tile: TB tokens x 4 channels; the state is staged transposed.
-// ---------------------------------------------------------------------------
-template <int D, int NS>
-__global__ void __launch_bounds__(256) bwd_dproj_kernel(BwdArgs a) {
-  constexpr int C = kBC, IB = 4, NIB = D / IB, TB = C * D / (256 * IB), SP = D + 1;
-  __shared__ float st[D * SP];  // [i][j] (rows padded): S0, then X
-  __shared__ float r1[C * D];   // dO, then U
-  __shared__ float r2[C * D];   // dU~
-  const size_t slot = blockIdx.x;
-  const size_t bh = slot / a.NC;
-  const int c = (int)(slot % a.NC);
-  const size_t base = slot * (size_t)C * D;
-  const int tid = threadIdx.x;
-  const bool act = tid < (C / TB) * NIB;
-  const int tb = tid / NIB, ib = tid % NIB, t0 = tb * TB, i0 = ib * IB;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, g = lane >> 4;
+  const int ar = 16 * w + l16;  // the A-operand row this lane supplies
   const float *S0f = a.S0f + slot * (size_t)D * D, *Xf = a.Xf + slot * (size_t)D * D;
-  for (int idx = tid; idx < D * D; idx += 256) st[(idx / D) * SP + idx % D] = S0f[idx];
-  for (int idx = tid; idx < C * D; idx += 256) {
-    const int t = idx / D, j = idx % D, tt = c * C + t;
-    r1[idx] = tt < a.T ? ld_do(a.dO, (bh * a.T + tt) * D + j, a.do_bf16) : 0.f;
-    r2[idx] = a.DU[base + idx];
+  auto stage = [&](float *dst, const float *src) {
+    for (int idx = tid; idx < D * D / 4; idx += 256) {
+      const int i = idx / (D / 4), j4 = idx % (D / 4);
+      *reinterpret_cast<float4 *>(dst + i * SP + 4 * j4) = reinterpret_cast<const float4 *>(src)[idx];
+    }
+  };
+  // C x D result rows 16 rt + 4 g + r, columns 16 ct + l16
+  auto put_glb = [&](float *dst, const f32x4 (&acc)[NCT], int rt, float sign) {
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dst[base + (size_t)(16 * rt + 4 * g + r) * D + 16 * ct + l16] = sign * acc[ct][r];
+  };
+  auto put_lds = [&](float *dst, const f32x4 (&acc)[NCT], int rt) {
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dst[(16 * rt + 4 * g + r) * SP + 16 * ct + l16] = acc[ct][r];
+  };
+  f32x4 acc[NCT], acc2[NCT], acs[NTC];
+  f32x4 af[NKB], dof[NKB], tf[NTC];
+
+  // (1) S0 phase: R = V_hat - K_a S0 (-> LDS), dQ_a = dO S0^T
+  stage(ss, S0f);
+  const int tt = c * C + ar;
+  const size_t orow = (bh * a.T + (tt < a.T ? tt : 0)) * D;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    const size_t o = base + (size_t)ar * D + 16 * kb + 4 * g;
+    const float4 kh = *reinterpret_cast<const float4 *>(a.KH + o), la = *reinterpret_cast<const float4 *>(a.LAM + o);
+    af[kb] = f32x4{kh.x * __expf(la.x), kh.y * __expf(la.y), kh.z * __expf(la.z), kh.w * __expf(la.w)};
+    dof[kb] = tt < a.T ? ld_do4(a.dO, orow + 16 * kb + 4 * g, a.do_bf16) : zero4();
   }
   __syncthreads();
-  float aq[TB][IB], ak[TB][IB];
-  if (act) {
+  zero_acc(acc);
+  mm_nn(acc, af, ss, SP, 0, NKB, g, l16);
 #pragma unroll
-    for (int u = 0; u < TB; ++u)
+  for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-      for (int v = 0; v < IB; ++v) aq[u][v] = ak[u][v] = 0.f;
-#pragma unroll 2
-    for (int j = 0; j < D; ++j) {
-      float sv[IB];
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * w + 4 * g + r, j = 16 * ct + l16;
+      bt[t * SP + j] = a.VH[base + (size_t)t * D + j] - acc[ct][r];
+    }
+  zero_acc(acc);
+  mm_nt(acc, dof, ss, SP, NCT, g, l16);
+  put_glb(a.DQA, acc, w, 1.f);
 #pragma unroll
-      for (int v = 0; v < IB; ++v) sv[v] = st[(i0 + v) * SP + j];
+  for (int kb = 0; kb < NTC; ++kb)
+    tf[kb] = *reinterpret_cast<const f32x4 *>(a.TI + cbase + (size_t)ar * C + 16 * kb + 4 * g);
+  __syncthreads();
+
+  // (2) U = T^-1 R (T^-1 lower triangular: k-blocks up to the row tile)
+  zero_acc(acc);
+  mm_nn(acc, tf, bt, SP, 0, w + 1, g, l16);
+  put_lds(bu, acc, w);
+  __syncthreads();
+
+  // (3) X phase: dA = dO U^T, Z = A^T dO + K' X, dK' = U X^T
+  stage(ss, Xf);
+  for (int idx = tid; idx < C * D / 4; idx += 256) {
+    const int t = idx / (D / 4), j4 = idx % (D / 4), t2 = c * C + t;
+    *reinterpret_cast<f32x4 *>(bt + t * SP + 4 * j4) =
+        t2 < a.T ? ld_do4(a.dO, (bh * a.T + t2) * D + 4 * j4, a.do_bf16) : zero4();
+  }
 #pragma unroll
-      for (int u = 0; u < TB; ++u) {
-        const float dv = r1[(t0 + u) * D + j], du = r2[(t0 + u) * D + j];
+  for (int kb = 0; kb < NKB; ++kb) {
+    const size_t o = base + (size_t)ar * D + 16 * kb + 4 * g;
+    const float4 kn = *reinterpret_cast<const float4 *>(a.KN + o), la = *reinterpret_cast<const float4 *>(a.LAM + o);
+    const float4 lc = *reinterpret_cast<const float4 *>(a.LAM + base + (size_t)(C - 1) * D + 16 * kb + 4 * g);
+    af[kb] = f32x4{kn.x * __expf(lc.x - la.x), kn.y * __expf(lc.y - la.y), kn.z * __expf(lc.z - la.z),
+                   kn.w * __expf(lc.w - la.w)};
+  }
 #pragma unroll
-        for (int v = 0; v < IB; ++v) {
-          aq[u][v] += dv * sv[v];
-          ak[u][v] -= du * sv[v];
-        }
-      }
+  for (int kb = 0; kb < NTC; ++kb)  // A^T rows: A[t][ar] for t = 16 kb + 4 g + e
+#pragma unroll
+    for (int e = 0; e < 4; ++e) tf[kb][e] = a.AM[cbase + (size_t)(16 * kb + 4 * g + e) * C + ar];
+  __syncthreads();
+  zero_acc(acs);
+  mm_nt(acs, dof, bu, SP, w + 1, g, l16);
+#pragma unroll
+  for (int ct = 0; ct < NTC; ++ct)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * w + 4 * g + r, s2 = 16 * ct + l16;
+      a.DA[cbase + (size_t)t * C + s2] = s2 <= t ? acs[ct][r] : 0.f;
+    }
+  zero_acc(acc);
+  mm_nn(acc, tf, bt, SP, w, NTC, g, l16);  // A lower triangular: t >= s
+  mm_nn(acc, af, ss, SP, 0, NKB, g, l16);
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) af[kb] = *reinterpret_cast<const f32x4 *>(bu + ar * SP + 16 * kb + 4 * g);
+  zero_acc(acc2);
+  mm_nt(acc2, af, ss, SP, NCT, g, l16);
+  put_glb(a.DKP, acc2, w, 1.f);
+  __syncthreads();  // every read of dO and X is done
+  put_lds(bt, acc, w);
+#pragma unroll
+  for (int kb = 0; kb < NTC; ++kb)  // T^-T rows: T^-1[t][ar]
+#pragma unroll
+    for (int e = 0; e < 4; ++e) tf[kb][e] = a.TI[cbase + (size_t)(16 * kb + 4 * g + e) * C + ar];
+  __syncthreads();
+
+  // (4) dU~ = T^-T Z (upper triangular: k-blocks from the row tile on)
+  zero_acc(acc);
+  mm_nn(acc, tf, bt, SP, w, NTC, g, l16);
+  put_glb(a.DU, acc, w, 1.f);
+  put_lds(ss, acc, w);
+  __syncthreads();
+
+  // (5) dL = -dU~ U^T for row tile 3 - w, then dK_a = -dU~ S0^T
+  const int tw = NTC - 1 - w;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+    af[kb] = *reinterpret_cast<const f32x4 *>(ss + (16 * tw + l16) * SP + 16 * kb + 4 * g);
+  zero_acc(acs);
+  mm_nt(acs, af, bu, SP, tw + 1, g, l16);
+#pragma unroll
+  for (int ct = 0; ct < NTC; ++ct)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * tw + 4 * g + r, s2 = 16 * ct + l16;
+      a.DL[cbase + (size_t)t * C + s2] = s2 < t ? -acs[ct][r] : 0.f;
     }
 #pragma unroll
-    for (int u = 0; u < TB; ++u)
-#pragma unroll
-      for (int v = 0; v < IB; ++v) {
-        a.DQA[base + (t0 + u) * D + i0 + v] = aq[u][v];
-        a.DKA[base + (t0 + u) * D + i0 + v] = ak[u][v];
-      }
-  }
+  for (int kb = 0; kb < NKB; ++kb) af[kb] = *reinterpret_cast<const f32x4 *>(ss + ar * SP + 16 * kb + 4 * g);
+  __syncthreads();  // every read of U and Z is done
+  stage(bb, S0f);
   __syncthreads();
-  for (int idx = tid; idx < D * D; idx += 256) st[(idx / D) * SP + idx % D] = Xf[idx];
-  for (int idx = tid; idx < C * D; idx += 256) r1[idx] = a.U[base + idx];
-  __syncthreads();
-  if (act) {
-#pragma unroll
-    for (int u = 0; u < TB; ++u)
-#pragma unroll
-      for (int v = 0; v < IB; ++v) aq[u][v] = 0.f;
-#pragma unroll 2
-    for (int j = 0; j < D; ++j) {
-      float xv[IB];
-#pragma unroll
-      for (int v = 0; v < IB; ++v) xv[v] = st[(i0 + v) * SP + j];
-#pragma unroll
-      for (int u = 0; u < TB; ++u) {
-        const float uv = r1[(t0 + u) * D + j];
-#pragma unroll
-        for (int v = 0; v < IB; ++v) aq[u][v] += uv * xv[v];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < TB; ++u)
-#pragma unroll
-      for (int v = 0; v < IB; ++v) a.DKP[base + (t0 + u) * D + i0 + v] = aq[u][v];
-  }
+  zero_acc(acc);
+  mm_nt(acc, af, bb, SP, NCT, g, l16);
+  put_glb(a.DKA, acc, w, -1.f);
 }
 
 // ---------------------------------------------------------------------------
@@ -755,9 +719,7 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
   hipLaunchKernelGGL((bwd_prepass_kernel<D, BF>), dim3(nch), dim3(256), 0, st, a);
   hipLaunchKernelGGL((bwd_gram_kernel<D>), dim3(nch), dim3(256), 0, st, a);
   hipLaunchKernelGGL((bwd_states_kernel<D, NS>), dim3(nch), dim3(256), 0, st, a);
-  hipLaunchKernelGGL((bwd_u_kernel<D, NS>), dim3(nch), dim3(256), 0, st, a);
-  hipLaunchKernelGGL((bwd_dmat_kernel<D>), dim3(nch), dim3(256), 0, st, a);
-  hipLaunchKernelGGL((bwd_dproj_kernel<D, NS>), dim3(nch), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((bwd_mm_kernel<D>), dim3(nch), dim3(256), 0, st, a);
   hipLaunchKernelGGL((bwd_gramback_kernel<D, NS>), dim3(nch * (D / 32)), dim3(256), 0, st, a);
   hipLaunchKernelGGL((bwd_final_kernel<D, BF>), dim3(nch), dim3(256), 0, st, a);
   if (a.dgamma && a.gamma)
@@ -787,10 +749,10 @@ size_t bwd_workspace(BwdArgs *a, ChunkArgs *f, void *ws, int B, int H, int T, in
   };
   void *mt = take(nch * NS * (size_t)D * D * 2), *xc = take(nch * NS * (size_t)D * D * 2);
   void *gn = take(nch * (size_t)D * D * 4);
-  float **cd[14] = {&a->KN, &a->KH, &a->QT, &a->VH, &a->LAM, &a->U, &a->DU, &a->DQA, &a->DKA, &a->DKP,
+  float **cd[13] = {&a->KN, &a->KH, &a->QT, &a->VH, &a->LAM, &a->DU, &a->DQA, &a->DKA, &a->DKP,
                     &a->DQT, &a->DKT, &a->DKN, &a->DLA};
-  float *cdp[14];
-  for (int i = 0; i < 14; ++i) cdp[i] = static_cast<float *>(take(nch * (size_t)kBC * D * 4));
+  float *cdp[13];
+  for (int i = 0; i < 13; ++i) cdp[i] = static_cast<float *>(take(nch * (size_t)kBC * D * 4));
   float *ccp[4];
   for (int i = 0; i < 4; ++i) ccp[i] = static_cast<float *>(take(nch * (size_t)kBC * kBC * 4));
   float *gp = static_cast<float *>(take(nch * (size_t)D * 4));
@@ -804,7 +766,7 @@ size_t bwd_workspace(BwdArgs *a, ChunkArgs *f, void *ws, int B, int H, int T, in
     a->Mt = static_cast<uint16_t *>(mt);
     a->Xc = static_cast<uint16_t *>(xc);
     a->Gn = static_cast<float *>(gn);
-    for (int i = 0; i < 14; ++i) *cd[i] = cdp[i];
+    for (int i = 0; i < 13; ++i) *cd[i] = cdp[i];
     a->AM = ccp[0];
     a->TI = ccp[1];
     a->DA = ccp[2];

@@ -69,7 +69,7 @@ struct BwdArgs {
   uint16_t *Mt, *Xc;             // M^T for the reverse chain; the chunk-end state gradients
   float *Gn;                     // Q'^T dO for the reverse chain
   // per-chunk scratch, [slot][64][D] fp32
-  float *KN, *KH, *QT, *VH, *LAM, *U, *DU, *DQA, *DKA, *DKP, *DQT, *DKT, *DKN, *DLA;
+  float *KN, *KH, *QT, *VH, *LAM, *DU, *DQA, *DKA, *DKP, *DQT, *DKT, *DKN, *DLA;
   float *AM, *TI, *DA, *DL;      // [slot][64][64] fp32
   float *gpart;                  // [slot][D] partial sums of dgamma
   float *S0f, *Xf;               // [slot][D][D] fp32 chunk-start states and chunk-end state gradients

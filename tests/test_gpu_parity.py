@@ -865,6 +865,8 @@ def test_backward_options_and_edges():
     y["k"] = torch.nn.functional.normalize(x["k"].float(), dim=-1).to(x["k"].dtype)
     bwd_compare(y, "no normalisation, scale", normalize_qk=False, scale=0.5)
     bwd_compare(make_inputs(WORKLOADS["gdn2"].with_sizes(B=1, H=2, T=1)), "T1")
+    bwd_compare({**x, "log_alpha": 0.0, "w": 1.0}, "constant decay and write gates")
+    bwd_compare({**x, "b": 0.0}, "no erase")
 
 
 def test_backward_empty_sequence_passes_the_state_gradient():
