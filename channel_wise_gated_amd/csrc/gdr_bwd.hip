@@ -33,70 +33,108 @@ namespace {
 
 constexpr int kBC = 64;  // chunk size of the backward
 
-// Upstream gradient dO (bf16 or fp32, chosen at run time: uniform branch).
-__device__ __forceinline__ float ld_do(const void *p, size_t i, int bf) {
-  return bf ? bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(p)[i]) : reinterpret_cast<const float *>(p)[i];
-}
-
 // ---------------------------------------------------------------------------
 // K1 prep: per chunk slot, M^T (plane by plane, in M's A-fragment layout) and
-// G = Q'^T dO (in N's accumulator-tile layout) for the reverse chain.
+// G = Q'^T dO (in N's accumulator-tile layout) for the reverse chain.  Each M
+// plane goes through LDS row-major (16-byte fragment reads and writes on both
+// sides); G is computed on the fp32 matrix cores from Q' and dO in LDS, wave w
+// owning G's row tiles w * NMT/4 to (w + 1) * NMT/4 - 1 (NMT = D / 16).
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ f32x4 mfma4(float x, float y, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(x, y, c, 0, 0, 0);
+}
+
+// four consecutive dO values (fp32 or bf16)
+__device__ __forceinline__ f32x4 ld_do4(const void *p, size_t i, int bf) {
+  if (bf) {
+    const uint2 r = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(p) + i);
+    return f32x4{__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u), __uint_as_float(r.y << 16),
+                 __uint_as_float(r.y & 0xffff0000u)};
+  }
+  const float4 v = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(p) + i);
+  return f32x4{v.x, v.y, v.z, v.w};
+}
+
 template <int D, int NS>
 __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdArgs a) {
-  constexpr int C = kBC, NKD = D / 32, NMT = D / 16;
-  __shared__ float qs[C][D + 1];
-  __shared__ float ds[C][D + 1];
+  constexpr int C = kBC, NKD = D / 32, NMT = D / 16, MP = D + 8, SP = D + 4, RT = NMT / 4;
+  __shared__ __align__(16) uint16_t mp[D * MP];  // one plane of M, row-major
+  __shared__ __align__(16) float qs[C * SP];     // Q' [t][i]
+  __shared__ __align__(16) float ds[C * SP];     // dO [t][j]
   const size_t slot = blockIdx.x;
   const size_t bh = slot / a.NC;
   const int c = (int)(slot % a.NC);
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, g = lane >> 4;
+  // A-fragment entry (f, lane) of a D x D plane: 8 values of row 16 (f / NKD) + l16,
+  // columns 32 (f % NKD) + 4 g + {0..3} and + 16
   const uint16_t *Ms = a.Mm + slot * NS * (size_t)D * D;
   uint16_t *Mt = a.Mt + slot * NS * (size_t)D * D;
-  for (int idx = tid; idx < D * D; idx += 256) {
-    // destination: fragment (w, ks), lane (l16, g), element e holds M^T[R][Cc]
-    const int e = idx & 7, lane = (idx >> 3) & 63, f = idx >> 9;
-    const int w = f / NKD, ks = f % NKD, l16 = lane & 15, g = lane >> 4;
-    const int R = 16 * w + l16, Cc = 32 * ks + 16 * (e >> 2) + 4 * g + (e & 3);
-    // source: M[Cc][R]
-    const int rr = R & 31;
-    const int src = (((Cc >> 4) * NKD + (R >> 5)) * 64 + (Cc & 15) + 16 * ((rr >> 2) & 3)) * 8 + 4 * (rr >> 4) + (rr & 3);
 #pragma unroll
-    for (int p = 0; p < NS; ++p) Mt[(size_t)p * D * D + idx] = Ms[(size_t)p * D * D + src];
+  for (int p = 0; p < NS; ++p) {
+    for (int idx = tid; idx < D * D / 8; idx += 256) {
+      const int f = idx >> 6, ln = idx & 63, row = 16 * (f / NKD) + (ln & 15), col = 32 * (f % NKD) + 4 * (ln >> 4);
+      const uint4 v = reinterpret_cast<const uint4 *>(Ms + (size_t)p * D * D)[idx];
+      *reinterpret_cast<uint2 *>(mp + row * MP + col) = uint2{v.x, v.y};
+      *reinterpret_cast<uint2 *>(mp + row * MP + col + 16) = uint2{v.z, v.w};
+    }
+    __syncthreads();
+    for (int idx = tid; idx < D * D / 8; idx += 256) {
+      // M^T[R][Cc] = M[Cc][R]: R = 16 (f / NKD) + l16, Cc over the entry's 8 columns
+      const int f = idx >> 6, ln = idx & 63, R = 16 * (f / NKD) + (ln & 15), c0 = 32 * (f % NKD) + 4 * (ln >> 4);
+      uint32_t h[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) h[e] = mp[(c0 + 16 * (e >> 2) + (e & 3)) * MP + R];
+      reinterpret_cast<uint4 *>(Mt + (size_t)p * D * D)[idx] =
+          uint4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+    }
+    __syncthreads();
   }
+  // Q' (planes summed in fp32) and dO into LDS
   const uint16_t *Qs = a.Qp + slot * NS * (size_t)C * D;
-  for (int idx = tid; idx < C * D; idx += 256) {
-    const int e = idx & 7, lane = (idx >> 3) & 63, f = idx >> 9;
-    const int ti = f / NKD, ks = f % NKD;
-    const int t = 16 * ti + (lane & 15), ch = 32 * ks + 16 * (e >> 2) + 4 * (lane >> 4) + (e & 3);
-    float v = 0.f;
+  for (int idx = tid; idx < C * D / 8; idx += 256) {
+    const int f = idx >> 6, ln = idx & 63, t = 16 * (f / NKD) + (ln & 15), col = 32 * (f % NKD) + 4 * (ln >> 4);
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int p = 0; p < NS; ++p) v += bf16_bits_to_f32(Qs[(size_t)p * C * D + idx]);
-    qs[t][ch] = v;
+    for (int p = 0; p < NS; ++p) {
+      const bf16x8 q8 = reinterpret_cast<const bf16x8 *>(Qs + (size_t)p * C * D)[idx];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] += (float)q8[e];
+    }
+    *reinterpret_cast<float4 *>(qs + t * SP + col) = float4{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<float4 *>(qs + t * SP + col + 16) = float4{v[4], v[5], v[6], v[7]};
   }
-  for (int idx = tid; idx < C * D; idx += 256) {
-    const int t = idx / D, j = idx % D, tt = c * C + t;
-    ds[t][j] = tt < a.T ? ld_do(a.dO, (bh * a.T + tt) * D + j, a.do_bf16) : 0.f;
+  for (int idx = tid; idx < C * D / 4; idx += 256) {
+    const int t = idx / (D / 4), j4 = idx % (D / 4), tt = c * C + t;
+    *reinterpret_cast<f32x4 *>(ds + t * SP + 4 * j4) =
+        tt < a.T ? ld_do4(a.dO, (bh * a.T + tt) * D + 4 * j4, a.do_bf16) : zero4();
   }
   __syncthreads();
-  constexpr int TPR = 256 / D;       // threads per row i
-  constexpr int JN = D / TPR;        // columns per thread
-  const int i = tid % D, j0 = (tid / D) * JN;
-  float acc[JN];
+  // G[i][j] = sum_t Q'[t][i] dO[t][j]: lane (l16, g) supplies k = t = 16 kb + 4 g + e
+  f32x4 acc[RT][NMT];
 #pragma unroll
-  for (int jj = 0; jj < JN; ++jj) acc[jj] = 0.f;
-  for (int t = 0; t < C; ++t) {
-    const float qv = qs[t][i];
+  for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-    for (int jj = 0; jj < JN; ++jj) acc[jj] += qv * ds[t][j0 + jj];
-  }
-  float *G = a.Gn + slot * (size_t)D * D;
-  const int w = i >> 4, g = (i & 15) >> 2, r = i & 3;
+    for (int jt = 0; jt < NMT; ++jt) acc[rt][jt] = zero4();
 #pragma unroll
-  for (int jj = 0; jj < JN; ++jj) {
-    const int j = j0 + jj;
-    G[((size_t)(w * NMT + (j >> 4)) * 64 + (j & 15) + 16 * g) * 4 + r] = acc[jj];
-  }
+  for (int kb = 0; kb < C / 16; ++kb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 16 * kb + 4 * g + e;
+      float av[RT], bv[NMT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) av[rt] = qs[t * SP + 16 * (RT * w + rt) + l16];
+#pragma unroll
+      for (int jt = 0; jt < NMT; ++jt) bv[jt] = ds[t * SP + 16 * jt + l16];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int jt = 0; jt < NMT; ++jt) acc[rt][jt] = mfma4(av[rt], bv[jt], acc[rt][jt]);
+    }
+  f32x4 *G = reinterpret_cast<f32x4 *>(a.Gn + slot * (size_t)D * D);
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int jt = 0; jt < NMT; ++jt) G[((RT * w + rt) * NMT + jt) * 64 + lane] = acc[rt][jt];
 }
 
 // ---------------------------------------------------------------------------
@@ -162,81 +200,105 @@ __global__ void __launch_bounds__(256) bwd_prepass_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// K4 Gram: per chunk slot, A (s <= t) and L (s < t) with exact pairwise decays
-// (e^{Lambda_t - Lambda_s} <= 1 for s <= t), over the lower-triangle entries
-// only (thread -> 8 or 9 of the 2080), the channels staged 32 at a time; then
+// K4 Gram: per chunk slot, A (s <= t) and L (s < t), A_ts = sum_i q_tilde_ti
+// kn_si e^{Lambda_ti - Lambda_si} and L_ts likewise with k_hat, on the fp32
+// matrix cores by 16 x 16 tiles: the pair decay is split at a per-channel pivot
+// P, e^{Lambda_t - P} on the t side and e^{P - Lambda_s} on the s side.  For a
+// tile below the diagonal P is Lambda at the s-block's last token, so both
+// factors are <= 1 (a factor that underflows belongs to a product that does
+// too).  For a diagonal tile P is Lambda at the block's first token: the s-side
+// factor grows to e^{range} over the block; when the range exceeds 60 (far
+// from fp32 overflow) the tile is recomputed pair by pair.  Then
 // T^-1 = (I + L)^-1 column by column (forward substitution).
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, kWave));
+  return x;
+}
+
 template <int D>
 __global__ void __launch_bounds__(256) bwd_gram_kernel(BwdArgs a) {
-  constexpr int C = kBC, CQ = 32, P = CQ + 1, NE = C * (C + 1) / 2, EPT = (NE + 255) / 256;
-  __shared__ float kn[C * P], kh[C * P], qt[C * P], lam[C * P];
-  __shared__ float L[C * (C + 1)], ti[C * (C + 1)];
+  constexpr int C = kBC, NKB = D / 16, LP = C + 1;
+  constexpr float kMaxRange = 60.f;
+  static_assert(C == 64, "tile list for four 16-token blocks");
+  __shared__ float L[C * LP], ti[C * LP];
   const size_t slot = blockIdx.x;
   const size_t base = slot * (size_t)C * D, cbase = slot * (size_t)C * C;
-  const int tid = threadIdx.x;
-  // this thread's entries: e = tid + 256 j over the lower triangle, row-major
-  int et[EPT], es[EPT];
-#pragma unroll
-  for (int j = 0; j < EPT; ++j) {
-    const int e = min(tid + 256 * j, NE - 1);
-    int t = (int)((sqrtf(8.f * e + 1.f) - 1.f) * 0.5f);
-    while (t * (t + 1) / 2 > e) --t;
-    while ((t + 1) * (t + 2) / 2 <= e) ++t;
-    et[j] = t;
-    es[j] = e - t * (t + 1) / 2;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, g = lane >> 4;
+  for (int e = tid; e < C * C; e += 256) {
+    const int t = e / C, s2 = e % C;
+    if ((s2 >> 4) > (t >> 4)) a.AM[cbase + e] = 0.f;  // tiles above the diagonal
   }
-  float av[EPT], lv[EPT];
+  // the ten tiles (tb, sb), sb <= tb: diagonal first, wave w takes w, w + 4, w + 8
+  // nibble k of each word: tb and sb of tile k
+  constexpr unsigned long long kTb = 0x3323213210ull, kSb = 0x0102103210ull;
+  for (int k = w; k < 10; k += 4) {
+    const int tb = (int)((kTb >> (4 * k)) & 15), sb = (int)((kSb >> (4 * k)) & 15);
+    const bool diag = tb == sb;
+    const int prow = diag ? 16 * sb : 16 * sb + 15;
+    const size_t rt = base + (size_t)(16 * tb + l16) * D, rs = base + (size_t)(16 * sb + l16) * D,
+                 rp = base + (size_t)prow * D;
+    f32x4 accA = zero4(), accL = zero4();
+    float emax = 0.f;
 #pragma unroll
-  for (int j = 0; j < EPT; ++j) av[j] = lv[j] = 0.f;
-  for (int c0 = 0; c0 < D; c0 += CQ) {
-    __syncthreads();
-    for (int idx = tid; idx < C * CQ; idx += 256) {
-      const int t = idx / CQ, c = idx % CQ;
-      const size_t gi = base + t * D + c0 + c;
-      kn[t * P + c] = a.KN[gi];
-      kh[t * P + c] = a.KH[gi];
-      qt[t * P + c] = a.QT[gi];
-      lam[t * P + c] = a.LAM[gi];
-    }
-    __syncthreads();
+    for (int kb = 0; kb < NKB; ++kb) {
+      const int i0 = 16 * kb + 4 * g;
+      const float4 qt = *reinterpret_cast<const float4 *>(a.QT + rt + i0);
+      const float4 kh = *reinterpret_cast<const float4 *>(a.KH + rt + i0);
+      const float4 lt = *reinterpret_cast<const float4 *>(a.LAM + rt + i0);
+      const float4 kn = *reinterpret_cast<const float4 *>(a.KN + rs + i0);
+      const float4 ls = *reinterpret_cast<const float4 *>(a.LAM + rs + i0);
+      const float4 lp = *reinterpret_cast<const float4 *>(a.LAM + rp + i0);
+      const float q4[4] = {qt.x, qt.y, qt.z, qt.w}, h4[4] = {kh.x, kh.y, kh.z, kh.w};
+      const float t4[4] = {lt.x, lt.y, lt.z, lt.w}, n4[4] = {kn.x, kn.y, kn.z, kn.w};
+      const float s4[4] = {ls.x, ls.y, ls.z, ls.w}, p4[4] = {lp.x, lp.y, lp.z, lp.w};
 #pragma unroll
-    for (int j = 0; j < EPT; ++j) {
-      const int t = et[j], s = es[j];
-      float sa = 0.f, sl = 0.f;
-#pragma unroll 8
-      for (int c = 0; c < CQ; ++c) {
-        const float x = __expf(lam[t * P + c] - lam[s * P + c]) * kn[s * P + c];
-        sa += qt[t * P + c] * x;
-        sl += kh[t * P + c] * x;
+      for (int e = 0; e < 4; ++e) {
+        const float fa = __expf(t4[e] - p4[e]), xb = p4[e] - s4[e];
+        emax = fmaxf(emax, xb);
+        const float b = n4[e] * __expf(xb);
+        accA = mfma4(q4[e] * fa, b, accA);
+        accL = mfma4(h4[e] * fa, b, accL);
       }
-      av[j] += sa;
-      lv[j] += sl;
     }
-  }
-  for (int e = tid; e < C * (C + 1); e += 256) L[e] = 0.f;
-  for (int e = tid; e < C * C; e += 256) a.AM[cbase + e] = 0.f;  // upper triangle
-  __syncthreads();
+    if (diag && wave_max(emax) > kMaxRange) {
+      // steep decay over the block: every pair of the lane's outputs exactly
 #pragma unroll
-  for (int j = 0; j < EPT; ++j) {
-    if (tid + 256 * j >= NE) continue;
-    const int t = et[j], s = es[j];
-    a.AM[cbase + t * C + s] = av[j];
-    if (s < t) L[t * (C + 1) + s] = lv[j];
-  }
-  __syncthreads();
-  // T^-1 column s (thread s): x_t = delta_ts - sum_{r < t} L[t][r] x_r
-  if (tid < C) {
-    const int s = tid;
-    for (int t = 0; t < C; ++t) {
-      float x = t == s ? 1.f : 0.f;
-      if (t > s)
-        for (int r = s; r < t; ++r) x -= L[t * (C + 1) + r] * ti[r * (C + 1) + s];
-      ti[t * (C + 1) + s] = x;
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * tb + 4 * g + r, s2 = 16 * sb + l16;
+        float sa = 0.f, sl = 0.f;
+        if (s2 <= t)
+          for (int i = 0; i < D; ++i) {
+            const float x = a.KN[base + (size_t)s2 * D + i] *
+                            __expf(a.LAM[base + (size_t)t * D + i] - a.LAM[base + (size_t)s2 * D + i]);
+            sa += a.QT[base + (size_t)t * D + i] * x;
+            sl += a.KH[base + (size_t)t * D + i] * x;
+          }
+        accA[r] = sa;
+        accL[r] = sl;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * tb + 4 * g + r, s2 = 16 * sb + l16;
+      a.AM[cbase + (size_t)t * C + s2] = (!diag || s2 <= t) ? accA[r] : 0.f;
+      L[t * LP + s2] = (!diag || s2 < t) ? accL[r] : 0.f;
     }
   }
   __syncthreads();
-  for (int e = tid; e < C * C; e += 256) a.TI[cbase + e] = ti[(e / C) * (C + 1) + e % C];
+  // T^-1 column s (thread s): x_t = delta_ts - sum_{s <= r < t} L[t][r] x_r
+  if (tid < C) {
+    const int s2 = tid;
+    for (int t = 0; t < C; ++t) {
+      float x = t == s2 ? 1.f : 0.f;
+      if (t > s2)
+        for (int r = s2; r < t; ++r) x -= L[t * LP + r] * ti[r * LP + s2];
+      ti[t * LP + s2] = x;
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < C * C; e += 256) a.TI[cbase + e] = ti[(e / C) * LP + e % C];
 }
 
 // ---------------------------------------------------------------------------
@@ -307,21 +369,6 @@ __global__ void __launch_bounds__(256) bwd_states_kernel(BwdArgs a) {
 // float4.  LDS rows are padded by 4 floats: conflict-free for both access
 // patterns.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ f32x4 mfma4(float x, float y, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(x, y, c, 0, 0, 0);
-}
-
-// four consecutive dO values (fp32 or bf16)
-__device__ __forceinline__ f32x4 ld_do4(const void *p, size_t i, int bf) {
-  if (bf) {
-    const uint2 r = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(p) + i);
-    return f32x4{__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u), __uint_as_float(r.y << 16),
-                 __uint_as_float(r.y & 0xffff0000u)};
-  }
-  const float4 v = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(p) + i);
-  return f32x4{v.x, v.y, v.z, v.w};
-}
-
 // acc[ct] += A B over k-blocks kb0..kb1-1; B[k][col] row-major in LDS (stride sp)
 template <int NK, int NT>
 __device__ __forceinline__ void mm_nn(f32x4 (&acc)[NT], const f32x4 (&af)[NK], const float *B, int sp, int kb0,
@@ -508,86 +555,167 @@ __global__ void __launch_bounds__(256) bwd_mm_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// K8 Gram backprop: one workgroup (256 threads) per (chunk slot, 32 channels):
-// thread (channel c, token group tg) owns tokens t = tg, tg + 8, ...  With
-// p = e^{Lambda_t - Lambda_s}, s <= t, two passes over the pairs:
-//   rows    RA_t = sum_s dA_ts k_s p,  RL_t = sum_s dL_ts k_s p
-//   columns CS_s = sum_t (dA_ts q_tilde_t + dL_ts k_hat_t) p
-// (each accumulated in registers for the thread's own tokens), then per token
-// the gradients of q_tilde, k_hat, k and Lambda, and the reverse cumulative
-// sum of dLambda over the chunk (= d log alpha).
+// K8 Gram backprop: per chunk slot, on the fp32 matrix cores.  With the pair
+// decay p_ts = e^{Lambda_t - Lambda_s} (per channel), s <= t:
+//   rows    RA_t = sum_s dA_ts kn_s p_ts,   RL_t = sum_s dL_ts kn_s p_ts
+//   columns CS_s = sum_t (dA_ts q_tilde_t + dL_ts k_hat_t) p_ts
+// Wave w owns token block w (16 tokens) of RA, RL and CS: the triangles give
+// every wave five 16-token k-blocks.  Rows split the decay at Q = Lambda of
+// the block's first token, RA_t = e^{Lambda_t - Q} sum_s dA_ts kn_s e^{Q -
+// Lambda_s}; columns at R = Lambda of the block's last token, CS_s =
+// e^{R - Lambda_s} sum_t (...) e^{Lambda_t - R}.  Every factor is <= 1 except
+// over the own block, where it reaches e^{range}; past range 60 the own block
+// is summed pair by pair instead.  Column j of MFMA tile ct is channel
+// NCT j + ct, so a lane's values of one token are NCT consecutive channels.
+// Then per token the gradients of q_tilde, k_hat, kn and Lambda, and the
+// reverse cumulative sum of dLambda over the chunk (= d log alpha).
 // ---------------------------------------------------------------------------
-template <int D, int NS>
+template <int D>
 __global__ void __launch_bounds__(256) bwd_gramback_kernel(BwdArgs a) {
-  constexpr int C = kBC, CW = 32, NG = 8, TPG = C / NG;
-  __shared__ float kn[C][CW], kh[C][CW], qt[C][CW], lam[C][CW];
-  __shared__ float dA[C][C + 1], dL[C][C + 1];
-  __shared__ float dlam[C][CW];
-  __shared__ float skp_g[NG][CW];
-  const size_t slot = blockIdx.x / (D / CW);
-  const int cb = (int)(blockIdx.x % (D / CW)), tid = threadIdx.x;
-  const int cl = tid % CW, tg = tid / CW, ch = cb * CW + cl;
+  constexpr int C = kBC, NCT = D / 16, NV = NCT / 4, DP = D + 1;
+  constexpr float kMaxRange = 60.f;
+  static_assert(C == 64, "four waves, one 16-token block each");
+  __shared__ float dl[C * DP];
+  __shared__ float sk[16 * D];
+  const size_t slot = blockIdx.x;
   const size_t base = slot * (size_t)C * D, cbase = slot * (size_t)C * C;
-  for (int idx = tid; idx < C * CW; idx += 256) {
-    const int t = idx / CW, c = idx % CW;
-    const size_t gi = base + t * D + cb * CW + c;
-    kn[t][c] = a.KN[gi];
-    kh[t][c] = a.KH[gi];
-    qt[t][c] = a.QT[gi];
-    lam[t][c] = a.LAM[gi];
-  }
-  for (int idx = tid; idx < C * C; idx += 256) {
-    dA[idx / C][idx % C] = a.DA[cbase + idx];
-    dL[idx / C][idx % C] = a.DL[cbase + idx];
-  }
-  __syncthreads();
-  float ra[TPG], rl[TPG], cs[TPG];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, g = lane >> 4;
+  const int c0 = NCT * l16;  // first channel of this lane
+  auto row = [&](const float *p, int t, float (&o)[NCT]) {
 #pragma unroll
-  for (int u = 0; u < TPG; ++u) {
-    const int t = tg + NG * u;
-    const float lt = lam[t][cl];
-    float sa = 0.f, sl = 0.f;
-#pragma unroll 4
-    for (int s = 0; s <= t; ++s) {
-      const float x = kn[s][cl] * __expf(lt - lam[s][cl]);
-      sa += dA[t][s] * x;
-      sl += dL[t][s] * x;
+    for (int v = 0; v < NV; ++v) {
+      const float4 x = *reinterpret_cast<const float4 *>(p + base + (size_t)t * D + c0 + 4 * v);
+      o[4 * v] = x.x;
+      o[4 * v + 1] = x.y;
+      o[4 * v + 2] = x.z;
+      o[4 * v + 3] = x.w;
     }
-    ra[u] = sa;
-    rl[u] = sl;
-    const int sc = t;  // the column this thread owns for the same u
-    const float ls = lam[sc][cl];
-    float c2 = 0.f;
-#pragma unroll 4
-    for (int tt = sc; tt < C; ++tt)
-      c2 += (dA[tt][sc] * qt[tt][cl] + dL[tt][sc] * kh[tt][cl]) * __expf(lam[tt][cl] - ls);
-    cs[u] = c2;
-  }
-  const float lc = lam[C - 1][cl];
-  float skp = 0.f;
+  };
+  float qv[NCT], rv[NCT];
+  row(a.LAM, 16 * w, qv);
+  row(a.LAM, 16 * w + 15, rv);
+  float rng = 0.f;
 #pragma unroll
-  for (int u = 0; u < TPG; ++u) {
-    const int t = tg + NG * u;
-    const size_t gi = base + t * D + ch;
-    const float at = __expf(lam[t][cl]), rat = __expf(lc - lam[t][cl]);
-    const float dqa = a.DQA[gi], dka = a.DKA[gi], dkp = a.DKP[gi];
-    const float qv = qt[t][cl], hv = kh[t][cl], kv = kn[t][cl];
-    a.DQT[gi] = at * dqa + ra[u];
-    a.DKT[gi] = at * dka + rl[u];
-    a.DKN[gi] = rat * dkp + cs[u];
-    dlam[t][cl] = qv * at * dqa + hv * at * dka - kv * rat * dkp + qv * ra[u] + hv * rl[u] - kv * cs[u];
-    skp += kv * rat * dkp;
+  for (int ct = 0; ct < NCT; ++ct) rng = fmaxf(rng, qv[ct] - rv[ct]);
+  const bool steep = wave_max(rng) > kMaxRange;
+  const int kend = steep ? w : w + 1, kbeg = steep ? w + 1 : w;
+  f32x4 ra[NCT], rl[NCT], cs[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) ra[ct] = rl[ct] = cs[ct] = zero4();
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    if (kb < kend) {  // rows: s = 16 kb + 4 g + e
+      const float4 da4 = *reinterpret_cast<const float4 *>(a.DA + cbase + (size_t)(16 * w + l16) * C + 16 * kb + 4 * g);
+      const float4 dl4 = *reinterpret_cast<const float4 *>(a.DL + cbase + (size_t)(16 * w + l16) * C + 16 * kb + 4 * g);
+      const float av[4] = {da4.x, da4.y, da4.z, da4.w}, lv[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float kn[NCT], ls[NCT];
+        row(a.KN, 16 * kb + 4 * g + e, kn);
+        row(a.LAM, 16 * kb + 4 * g + e, ls);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          const float b = kn[ct] * __expf(qv[ct] - ls[ct]);
+          ra[ct] = mfma4(av[e], b, ra[ct]);
+          rl[ct] = mfma4(lv[e], b, rl[ct]);
+        }
+      }
+    }
+    if (kb >= kbeg) {  // columns: t = 16 kb + 4 g + e
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * kb + 4 * g + e;
+        const float dat = a.DA[cbase + (size_t)t * C + 16 * w + l16], dlt = a.DL[cbase + (size_t)t * C + 16 * w + l16];
+        float q[NCT], h[NCT], lt[NCT];
+        row(a.QT, t, q);
+        row(a.KH, t, h);
+        row(a.LAM, t, lt);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          const float f = __expf(lt[ct] - rv[ct]);
+          cs[ct] = mfma4(dat, q[ct] * f, cs[ct]);
+          cs[ct] = mfma4(dlt, h[ct] * f, cs[ct]);
+        }
+      }
+    }
   }
-  skp_g[tg][cl] = skp;
+  float lc[NCT], skp[NCT];
+  row(a.LAM, C - 1, lc);
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) skp[ct] = 0.f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int t = 16 * w + 4 * g + r;
+    float lt[NCT], q[NCT], h[NCT], kn[NCT], dqa[NCT], dka[NCT], dkp[NCT];
+    row(a.LAM, t, lt);
+    row(a.QT, t, q);
+    row(a.KH, t, h);
+    row(a.KN, t, kn);
+    row(a.DQA, t, dqa);
+    row(a.DKA, t, dka);
+    row(a.DKP, t, dkp);
+    float RA[NCT], RL[NCT], CS[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const float up = __expf(lt[ct] - qv[ct]);
+      RA[ct] = up * ra[ct][r];
+      RL[ct] = up * rl[ct][r];
+      CS[ct] = __expf(rv[ct] - lt[ct]) * cs[ct][r];
+    }
+    if (steep) {  // the own block pair by pair
+      for (int s2 = 16 * w; s2 <= t; ++s2) {
+        const float dat = a.DA[cbase + (size_t)t * C + s2], dlt = a.DL[cbase + (size_t)t * C + s2];
+        float k2[NCT], l2[NCT];
+        row(a.KN, s2, k2);
+        row(a.LAM, s2, l2);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          const float x = k2[ct] * __expf(lt[ct] - l2[ct]);
+          RA[ct] += dat * x;
+          RL[ct] += dlt * x;
+        }
+      }
+      for (int t2 = t; t2 < 16 * w + 16; ++t2) {
+        const float dat = a.DA[cbase + (size_t)t2 * C + t], dlt = a.DL[cbase + (size_t)t2 * C + t];
+        float q2[NCT], h2[NCT], l2[NCT];
+        row(a.QT, t2, q2);
+        row(a.KH, t2, h2);
+        row(a.LAM, t2, l2);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) CS[ct] += (dat * q2[ct] + dlt * h2[ct]) * __expf(l2[ct] - lt[ct]);
+      }
+    }
+    float oq[NCT], ok[NCT], on[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const float at = __expf(lt[ct]), rat = __expf(lc[ct] - lt[ct]);
+      oq[ct] = at * dqa[ct] + RA[ct];
+      ok[ct] = at * dka[ct] + RL[ct];
+      on[ct] = rat * dkp[ct] + CS[ct];
+      dl[t * DP + c0 + ct] = q[ct] * at * dqa[ct] + h[ct] * at * dka[ct] - kn[ct] * rat * dkp[ct] + q[ct] * RA[ct] +
+                             h[ct] * RL[ct] - kn[ct] * CS[ct];
+      skp[ct] += kn[ct] * rat * dkp[ct];
+    }
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const size_t o = base + (size_t)t * D + c0 + 4 * v;
+      *reinterpret_cast<float4 *>(a.DQT + o) = float4{oq[4 * v], oq[4 * v + 1], oq[4 * v + 2], oq[4 * v + 3]};
+      *reinterpret_cast<float4 *>(a.DKT + o) = float4{ok[4 * v], ok[4 * v + 1], ok[4 * v + 2], ok[4 * v + 3]};
+      *reinterpret_cast<float4 *>(a.DKN + o) = float4{on[4 * v], on[4 * v + 1], on[4 * v + 2], on[4 * v + 3]};
+    }
+  }
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) sk[(4 * w + g) * D + c0 + ct] = skp[ct];
   __syncthreads();
-  if (tg == 0) {
+  if (tid < D) {
     // the chunk-end decay: K' and Diag(a_C) S0 in the end state
-    float run = __expf(lc) * a.XS[slot * D + ch];
+    const int ch = tid;
+    float run = __expf(a.LAM[base + (size_t)(C - 1) * D + ch]) * a.XS[slot * D + ch];
 #pragma unroll
-    for (int g = 0; g < NG; ++g) run += skp_g[g][cl];
+    for (int p2 = 0; p2 < 16; ++p2) run += sk[p2 * D + ch];
     for (int t = C - 1; t >= 0; --t) {
-      run += dlam[t][cl];
-      a.DLA[base + t * D + ch] = run;
+      run += dl[t * DP + ch];
+      a.DLA[base + (size_t)t * D + ch] = run;
     }
   }
 }
@@ -720,7 +848,7 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
   hipLaunchKernelGGL((bwd_gram_kernel<D>), dim3(nch), dim3(256), 0, st, a);
   hipLaunchKernelGGL((bwd_states_kernel<D, NS>), dim3(nch), dim3(256), 0, st, a);
   hipLaunchKernelGGL((bwd_mm_kernel<D>), dim3(nch), dim3(256), 0, st, a);
-  hipLaunchKernelGGL((bwd_gramback_kernel<D, NS>), dim3(nch * (D / 32)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((bwd_gramback_kernel<D>), dim3(nch), dim3(256), 0, st, a);
   hipLaunchKernelGGL((bwd_final_kernel<D, BF>), dim3(nch), dim3(256), 0, st, a);
   if (a.dgamma && a.gamma)
     hipLaunchKernelGGL((bwd_dgamma_kernel<D>), dim3((unsigned)((a.H * D + 255) / 256)), dim3(256), 0, st, a);

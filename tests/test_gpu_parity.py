@@ -869,6 +869,21 @@ def test_backward_options_and_edges():
     bwd_compare({**x, "b": 0.0}, "no erase")
 
 
+def test_backward_extreme_and_steep_decays():
+    """log alpha = -30 at single tokens and over runs wider than a 16-token
+    block (the pair-by-pair path of the Gram kernels), and a block whose decay
+    range is just under that path's threshold (pivot factors near e^50)."""
+    wl = WORKLOADS["gdn2"].with_sizes(B=1, H=2, T=256)
+    x = make_inputs(wl)
+    la = x["log_alpha"].clone()
+    la[:, 0, 37] = -30.0
+    la[:, 0, 160:176] = -3.3
+    la[:, 1, 100:140] = -30.0
+    la[:, 1, 200:203, :64] = -30.0
+    x["log_alpha"] = la
+    bwd_compare(x, "extreme decays")
+
+
 def test_backward_empty_sequence_passes_the_state_gradient():
     wl = WORKLOADS["gdn2"].with_sizes(B=1, H=2, T=0)
     x = dev(make_inputs(wl))
