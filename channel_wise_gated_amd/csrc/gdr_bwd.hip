@@ -302,58 +302,6 @@ __global__ void __launch_bounds__(256) bwd_gram_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// K4b states: per chunk slot, S0 and X from the chain's bf16 planes into fp32
-// row-major [D][D] (through LDS: coalesced reads of the planes, coalesced row
-// writes), and the row dots sum_j X[i][j] S0[i][j].
-// ---------------------------------------------------------------------------
-template <int D, int NS>
-__global__ void __launch_bounds__(256) bwd_states_kernel(BwdArgs a) {
-  constexpr int NFR = (D / 32) * NS, FRAG = 512;
-  __shared__ __align__(16) float s0[D * D];
-  __shared__ __align__(16) float xx[D * D];
-  const size_t slot = blockIdx.x;
-  const int tid = threadIdx.x;
-  const uint16_t *S0p = a.Sc + slot * NS * (size_t)D * D;
-  const uint16_t *Xp = a.Xc + slot * NS * (size_t)D * D;
-  // one (slice, k-step, lane) entry: 8 elements of one column, rows
-  // 32 ks + 16 h + 4 g + r for e = 4 h + r
-  for (int idx = tid; idx < (D / 16) * (D / 32) * 64; idx += 256) {
-    const int lane = idx & 63, ks = (idx >> 6) % (D / 32), sl = (idx >> 6) / (D / 32);
-    const int l16 = lane & 15, g = lane >> 4, col = 16 * sl + l16;
-    const size_t off = (size_t)sl * NFR * FRAG + (size_t)(ks * NS) * FRAG + lane * 8;
-    float vs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, vx[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int p = 0; p < NS; ++p) {
-      const bf16x8 fs = *reinterpret_cast<const bf16x8 *>(S0p + off + p * FRAG);
-      const bf16x8 fx = *reinterpret_cast<const bf16x8 *>(Xp + off + p * FRAG);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        vs[e] += (float)fs[e];
-        vx[e] += (float)fx[e];
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int row = 32 * ks + 16 * (e >> 2) + 4 * g + (e & 3);
-      s0[row * D + col] = vs[e];
-      xx[row * D + col] = vx[e];
-    }
-  }
-  __syncthreads();
-  float4 *S0f = reinterpret_cast<float4 *>(a.S0f + slot * (size_t)D * D);
-  float4 *Xf = reinterpret_cast<float4 *>(a.Xf + slot * (size_t)D * D);
-  for (int idx = tid; idx < D * D / 4; idx += 256) {
-    S0f[idx] = reinterpret_cast<const float4 *>(s0)[idx];
-    Xf[idx] = reinterpret_cast<const float4 *>(xx)[idx];
-  }
-  if (tid < D) {
-    float d = 0.f;
-    for (int j = 0; j < D; ++j) d += xx[tid * D + (j + tid) % D] * s0[tid * D + (j + tid) % D];
-    a.XS[slot * D + tid] = d;
-  }
-}
-
-// ---------------------------------------------------------------------------
 // K5: per chunk slot, the dense products of the chunk system's reverse, on the
 // fp32 matrix cores (v_mfma_f32_16x16x4_f32):
 //   R   = V_hat - K_a S0       U  = T^-1 R            dQ_a = dO S0^T
@@ -406,13 +354,15 @@ __device__ __forceinline__ void zero_acc(f32x4 (&acc)[NT]) {
   for (int ct = 0; ct < NT; ++ct) acc[ct] = zero4();
 }
 
-template <int D>
+template <int D, int NS>
 __global__ void __launch_bounds__(256) bwd_mm_kernel(BwdArgs a) {
   constexpr int C = kBC, SP = D + 4, NKB = D / 16, NCT = D / 16, NTC = C / 16;
-  constexpr int BBR = 2 * C > D ? 2 * C : D;
+  constexpr int BBR = 2 * C > D ? 2 * C : D, NFR = (D / 32) * NS, FRAG = 512;
   static_assert(NTC == 4, "four waves, one 16-token row tile each");
+  static_assert(4 % (D / 32) == 0, "a thread's plane entries share their rows");
   __shared__ __align__(16) float ss[D * SP];    // S0, then X, then dU~ (rows < C)
   __shared__ __align__(16) float bb[BBR * SP];  // rows < C: R, dO, Z; rows C..2C-1: U; last: S0
+  __shared__ float xs[D];                       // row dots of X and S0
   float *bt = bb, *bu = bb + C * SP;
   const size_t slot = blockIdx.x;
   const size_t bh = slot / a.NC;
@@ -420,11 +370,43 @@ __global__ void __launch_bounds__(256) bwd_mm_kernel(BwdArgs a) {
   const size_t base = slot * (size_t)C * D, cbase = slot * (size_t)C * C;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, g = lane >> 4;
   const int ar = 16 * w + l16;  // the A-operand row this lane supplies
-  const float *S0f = a.S0f + slot * (size_t)D * D, *Xf = a.Xf + slot * (size_t)D * D;
-  auto stage = [&](float *dst, const float *src) {
-    for (int idx = tid; idx < D * D / 4; idx += 256) {
-      const int i = idx / (D / 4), j4 = idx % (D / 4);
-      *reinterpret_cast<float4 *>(dst + i * SP + 4 * j4) = reinterpret_cast<const float4 *>(src)[idx];
+  const uint16_t *S0p = a.Sc + slot * NS * (size_t)D * D, *Xp = a.Xc + slot * NS * (size_t)D * D;
+  // A state from the chains' bf16 planes (summed in fp32) into padded LDS rows.
+  // Entry (slice sl, k-step ks, lane) of a plane holds 8 values of column
+  // 16 sl + l16, rows 32 ks + 16 (e / 4) + 4 g + e % 4.  With `other` (a second
+  // state, same layout), the row dots sum_j X_ij S0_ij go to xs.
+  auto stage = [&](float *dst, const uint16_t *pl, const uint16_t *other) {
+    float dot[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    const int ks = (tid >> 6) % (D / 32);  // the same for all of this thread's entries
+    for (int idx = tid; idx < (D / 16) * (D / 32) * 64; idx += 256) {
+      const int sl = (idx >> 6) / (D / 32), col = 16 * sl + l16;
+      const size_t off = (size_t)sl * NFR * FRAG + (size_t)(ks * NS) * FRAG + lane * 8;
+      float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int p = 0; p < NS; ++p) {
+        const bf16x8 f = *reinterpret_cast<const bf16x8 *>(pl + off + p * FRAG);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] += (float)f[e];
+        if (other) {
+          const bf16x8 f2 = *reinterpret_cast<const bf16x8 *>(other + off + p * FRAG);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] += (float)f2[e];
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        dst[(32 * ks + 16 * (e >> 2) + 4 * g + (e & 3)) * SP + col] = v[e];
+        dot[e] += v[e] * o[e];
+      }
+    }
+    if (other) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float d = dot[e];
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) d += __shfl_xor(d, off, kWave);
+        if (l16 == 0) atomicAdd(&xs[32 * ks + 16 * (e >> 2) + 4 * g + (e & 3)], d);
+      }
     }
   };
   // C x D result rows 16 rt + 4 g + r, columns 16 ct + l16
@@ -444,7 +426,8 @@ __global__ void __launch_bounds__(256) bwd_mm_kernel(BwdArgs a) {
   f32x4 af[NKB], dof[NKB], tf[NTC];
 
   // (1) S0 phase: R = V_hat - K_a S0 (-> LDS), dQ_a = dO S0^T
-  stage(ss, S0f);
+  if (tid < D) xs[tid] = 0.f;
+  stage(ss, S0p, nullptr);
   const int tt = c * C + ar;
   const size_t orow = (bh * a.T + (tt < a.T ? tt : 0)) * D;
 #pragma unroll
@@ -479,7 +462,7 @@ __global__ void __launch_bounds__(256) bwd_mm_kernel(BwdArgs a) {
   __syncthreads();
 
   // (3) X phase: dA = dO U^T, Z = A^T dO + K' X, dK' = U X^T
-  stage(ss, Xf);
+  stage(ss, Xp, S0p);
   for (int idx = tid; idx < C * D / 4; idx += 256) {
     const int t = idx / (D / 4), j4 = idx % (D / 4), t2 = c * C + t;
     *reinterpret_cast<f32x4 *>(bt + t * SP + 4 * j4) =
@@ -517,6 +500,7 @@ __global__ void __launch_bounds__(256) bwd_mm_kernel(BwdArgs a) {
   put_glb(a.DKP, acc2, w, 1.f);
   __syncthreads();  // every read of dO and X is done
   put_lds(bt, acc, w);
+  if (tid < D) a.XS[slot * D + tid] = xs[tid];
 #pragma unroll
   for (int kb = 0; kb < NTC; ++kb)  // T^-T rows: T^-1[t][ar]
 #pragma unroll
@@ -547,11 +531,33 @@ __global__ void __launch_bounds__(256) bwd_mm_kernel(BwdArgs a) {
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) af[kb] = *reinterpret_cast<const f32x4 *>(ss + ar * SP + 16 * kb + 4 * g);
   __syncthreads();  // every read of U and Z is done
-  stage(bb, S0f);
+  stage(bb, S0p, nullptr);
   __syncthreads();
   zero_acc(acc);
   mm_nt(acc, af, bb, SP, NCT, g, l16);
   put_glb(a.DKA, acc, w, -1.f);
+}
+
+// sum over the 16 lanes of a lane group (lane bits 0-3)
+__device__ __forceinline__ float group16_sum(float x) {
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) x += __shfl_xor(x, off, kWave);
+  return x;
+}
+
+template <bool BF, int N>
+__device__ __forceinline__ void ldn(const void *p, size_t i, float (&o)[N]) {
+  if constexpr (N == 8)
+    ld8<BF>(p, i, o);
+  else
+    ld4<BF>(p, i, o);
+}
+
+template <int N>
+__device__ __forceinline__ void stn(float *p, const float (&x)[N]) {
+#pragma unroll
+  for (int v = 0; v < N / 4; ++v)
+    reinterpret_cast<float4 *>(p)[v] = float4{x[4 * v], x[4 * v + 1], x[4 * v + 2], x[4 * v + 3]};
 }
 
 // ---------------------------------------------------------------------------
@@ -567,17 +573,22 @@ __global__ void __launch_bounds__(256) bwd_mm_kernel(BwdArgs a) {
 // over the own block, where it reaches e^{range}; past range 60 the own block
 // is summed pair by pair instead.  Column j of MFMA tile ct is channel
 // NCT j + ct, so a lane's values of one token are NCT consecutive channels.
-// Then per token the gradients of q_tilde, k_hat, kn and Lambda, and the
-// reverse cumulative sum of dLambda over the chunk (= d log alpha).
+// Then per token the gradients of q_tilde, k_hat, kn and Lambda, their chains
+// back to the inputs (gates, read-out gain, SiLU + l2), and the reverse
+// cumulative sum of dLambda over the chunk (= d log alpha); the chunk's
+// partial sums of dgamma go to gpart.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool BF>
 __global__ void __launch_bounds__(256) bwd_gramback_kernel(BwdArgs a) {
   constexpr int C = kBC, NCT = D / 16, NV = NCT / 4, DP = D + 1;
   constexpr float kMaxRange = 60.f;
   static_assert(C == 64, "four waves, one 16-token block each");
-  __shared__ float dl[C * DP];
-  __shared__ float sk[16 * D];
+  __shared__ float dl[C * DP];  // dLambda, then d log alpha
+  __shared__ float sk[16 * D];  // per (wave, lane group): sum_t kn rat dK'
+  __shared__ float gp[16 * D];  // per (wave, lane group): partial dgamma
   const size_t slot = blockIdx.x;
+  const size_t bh = slot / a.NC;
+  const int c = (int)(slot % a.NC), hd = (int)(bh % a.H);
   const size_t base = slot * (size_t)C * D, cbase = slot * (size_t)C * C;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, g = lane >> 4;
   const int c0 = NCT * l16;  // first channel of this lane
@@ -639,10 +650,10 @@ __global__ void __launch_bounds__(256) bwd_gramback_kernel(BwdArgs a) {
       }
     }
   }
-  float lc[NCT], skp[NCT];
+  float lc[NCT], skp[NCT], gac[NCT];
   row(a.LAM, C - 1, lc);
 #pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) skp[ct] = 0.f;
+  for (int ct = 0; ct < NCT; ++ct) skp[ct] = gac[ct] = 0.f;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int t = 16 * w + 4 * g + r;
@@ -685,155 +696,154 @@ __global__ void __launch_bounds__(256) bwd_gramback_kernel(BwdArgs a) {
         for (int ct = 0; ct < NCT; ++ct) CS[ct] += (dat * q2[ct] + dlt * h2[ct]) * __expf(l2[ct] - lt[ct]);
       }
     }
-    float oq[NCT], ok[NCT], on[NCT];
+    // the chains back to the inputs (q, k through SiLU and l2, the gain,
+    // the gates); reductions over a token's channels stay in its 16 lanes
+    const int tt = c * C + t;
+    const bool live = tt < a.T;
+    const size_t grow = bh * a.T + (live ? tt : 0);
+    float qx[NCT], kx[NCT], vx[NCT], zx[NCT], bg[NCT], wg[NCT], du[NCT];
+    ldn<BF, NCT>(a.q, grow * D + c0, qx);
+    ldn<BF, NCT>(a.k, grow * D + c0, kx);
+    ldn<BF, NCT>(a.v, grow * D + c0, vx);
+    if (a.z) {
+      ldn<BF, NCT>(a.z, grow * D + c0, zx);
+    } else {
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      const float at = __expf(lt[ct]), rat = __expf(lc[ct] - lt[ct]);
-      oq[ct] = at * dqa[ct] + RA[ct];
-      ok[ct] = at * dka[ct] + RL[ct];
-      on[ct] = rat * dkp[ct] + CS[ct];
-      dl[t * DP + c0 + ct] = q[ct] * at * dqa[ct] + h[ct] * at * dka[ct] - kn[ct] * rat * dkp[ct] + q[ct] * RA[ct] +
-                             h[ct] * RL[ct] - kn[ct] * CS[ct];
-      skp[ct] += kn[ct] * rat * dkp[ct];
+      for (int ct = 0; ct < NCT; ++ct) zx[ct] = 0.f;
     }
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
-      const size_t o = base + (size_t)t * D + c0 + 4 * v;
-      *reinterpret_cast<float4 *>(a.DQT + o) = float4{oq[4 * v], oq[4 * v + 1], oq[4 * v + 2], oq[4 * v + 3]};
-      *reinterpret_cast<float4 *>(a.DKT + o) = float4{ok[4 * v], ok[4 * v + 1], ok[4 * v + 2], ok[4 * v + 3]};
-      *reinterpret_cast<float4 *>(a.DKN + o) = float4{on[4 * v], on[4 * v + 1], on[4 * v + 2], on[4 * v + 3]};
+      gate4<BF>(a.b, a.b_mode, grow, c0 + 4 * v, D, bg + 4 * v);
+      gate4<BF>(a.w, a.w_mode, grow, c0 + 4 * v, D, wg + 4 * v);
     }
-  }
+    row(a.DU, t, du);
+    float sq[NCT], sn[NCT], nq = 0.f, nk = 0.f;
 #pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) sk[(4 * w + g) * D + c0 + ct] = skp[ct];
-  __syncthreads();
-  if (tid < D) {
-    // the chunk-end decay: K' and Diag(a_C) S0 in the end state
-    const int ch = tid;
-    float run = __expf(a.LAM[base + (size_t)(C - 1) * D + ch]) * a.XS[slot * D + ch];
-#pragma unroll
-    for (int p2 = 0; p2 < 16; ++p2) run += sk[p2 * D + ch];
-    for (int t = C - 1; t >= 0; --t) {
-      run += dl[t * DP + ch];
-      a.DLA[base + (size_t)t * D + ch] = run;
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// K9 final: per chunk slot (4 waves x 16 tokens, lanes over channels), the
-// elementwise chains to the inputs: gates, read-out gain, SiLU + l2; writes
-// the gradients of valid tokens and the chunk's gamma partial sums.
-// ---------------------------------------------------------------------------
-template <int D, bool BF>
-__global__ void __launch_bounds__(256) bwd_final_kernel(BwdArgs a) {
-  constexpr int C = kBC, CPL = D / 64;
-  __shared__ float gp[4][D];
-  const size_t slot = blockIdx.x;
-  const size_t bh = slot / a.NC;
-  const int c = (int)(slot % a.NC), h = (int)(bh % a.H);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const size_t base = slot * (size_t)C * D;
-  float gacc[CPL];
-#pragma unroll
-  for (int u = 0; u < CPL; ++u) gacc[u] = 0.f;
-  for (int t = wave; t < C; t += 4) {
-    const int tt = c * C + t;
-    if (tt >= a.T) continue;  // uniform over the wave
-    const size_t row = bh * a.T + tt;
-    float qx[CPL], kx[CPL], sq[CPL], sk[CPL], dqh[CPL], dkn[CPL];
-    float nq = 0.f, nk = 0.f;
-#pragma unroll
-    for (int u = 0; u < CPL; ++u) {
-      const int ch = lane + 64 * u;
-      qx[u] = ld1<BF>(a.q, row * D + ch);
-      kx[u] = ld1<BF>(a.k, row * D + ch);
-      sq[u] = a.normalize_qk ? silu(qx[u]) : qx[u];
-      sk[u] = a.normalize_qk ? silu(kx[u]) : kx[u];
-      nq += sq[u] * sq[u];
-      nk += sk[u] * sk[u];
+    for (int ct = 0; ct < NCT; ++ct) {
+      sq[ct] = a.normalize_qk ? silu(qx[ct]) : qx[ct];
+      sn[ct] = a.normalize_qk ? silu(kx[ct]) : kx[ct];
+      nq += sq[ct] * sq[ct];
+      nk += sn[ct] * sn[ct];
     }
     float rq = 1.f, rk = 1.f;
     if (a.normalize_qk) {
-      rq = fmaxf(sqrtf(wave_sum(nq)), 1e-12f);
-      rk = fmaxf(sqrtf(wave_sum(nk)), 1e-12f);
+      rq = fmaxf(sqrtf(group16_sum(nq)), 1e-12f);
+      rk = fmaxf(sqrtf(group16_sum(nk)), 1e-12f);
     }
-    float dotq = 0.f, dotk = 0.f, sdb = 0.f, sdw = 0.f, sdla = 0.f;
+    float dqh[NCT], dkn[NCT], dzv[NCT], dbv[NCT], dwv[NCT], dvv[NCT];
+    float dotq = 0.f, dotk = 0.f, sdb = 0.f, sdw = 0.f;
 #pragma unroll
-    for (int u = 0; u < CPL; ++u) {
-      const int ch = lane + 64 * u;
-      const size_t ix = base + t * D + ch;
-      const float qh = sq[u] / rq, kn = sk[u] / rk;
-      const float gam = a.gamma ? a.gamma[(size_t)h * D + ch] : 1.f;
-      const float zv = a.z ? ld1<BF>(a.z, row * D + ch) : 0.f;
-      const float sg = 1.f / (1.f + expf(-zv));
+    for (int ct = 0; ct < NCT; ++ct) {
+      const float at = __expf(lt[ct]), rat = __expf(lc[ct] - lt[ct]);
+      const float dqt = at * dqa[ct] + RA[ct], dkh = at * dka[ct] + RL[ct], dkw = rat * dkp[ct] + CS[ct];
+      dl[t * DP + c0 + ct] = q[ct] * at * dqa[ct] + h[ct] * at * dka[ct] - kn[ct] * rat * dkp[ct] + q[ct] * RA[ct] +
+                             h[ct] * RL[ct] - kn[ct] * CS[ct];
+      skp[ct] += kn[ct] * rat * dkp[ct];
+      const float qh = sq[ct] / rq, knv = sn[ct] / rk;
+      const float gam = a.gamma ? a.gamma[(size_t)hd * D + c0 + ct] : 1.f;
+      const float sg = 1.f / (1.f + expf(-zx[ct]));
       const float dyn = a.z ? 2.f * sg : 1.f;
-      const float dqt = a.DQT[ix], dkh = a.DKT[ix], dvh = a.DU[ix];
-      const float bg = gate_at<BF>(a.b, a.b_mode, row, ch, D);
-      const float wg = gate_at<BF>(a.w, a.w_mode, row, ch, D);
-      const float vv = ld1<BF>(a.v, row * D + ch);
-      dqh[u] = dqt * a.scale * gam * dyn;
-      gacc[u] += dqt * a.scale * dyn * qh;
-      if (a.dz && a.z) a.dz[row * D + ch] = dqt * a.scale * gam * qh * 2.f * sg * (1.f - sg);
-      dkn[u] = a.DKN[ix] + dkh * bg;
-      const float db = dkh * kn, dw = dvh * vv, dla = a.DLA[ix];
-      if (a.db && a.b_mode == GDR_GATE_PER_CHANNEL) a.db[row * D + ch] = db;
-      if (a.dw && a.w_mode == GDR_GATE_PER_CHANNEL) a.dw[row * D + ch] = dw;
-      if (a.dla && a.alpha_mode == GDR_GATE_PER_CHANNEL) a.dla[row * D + ch] = dla;
-      sdb += db;
-      sdw += dw;
-      sdla += dla;
-      if (a.dv) a.dv[row * D + ch] = dvh * wg;
-      dotq += qh * dqh[u];
-      dotk += kn * dkn[u];
-    }
-    if (a.b_mode == GDR_GATE_PER_TOKEN || a.w_mode == GDR_GATE_PER_TOKEN || a.alpha_mode == GDR_GATE_PER_TOKEN) {
-      sdb = wave_sum(sdb);
-      sdw = wave_sum(sdw);
-      sdla = wave_sum(sdla);
-      if (lane == 0) {
-        if (a.db && a.b_mode == GDR_GATE_PER_TOKEN) a.db[row] = sdb;
-        if (a.dw && a.w_mode == GDR_GATE_PER_TOKEN) a.dw[row] = sdw;
-        if (a.dla && a.alpha_mode == GDR_GATE_PER_TOKEN) a.dla[row] = sdla;
-      }
+      dqh[ct] = dqt * a.scale * gam * dyn;
+      if (live) gac[ct] += dqt * a.scale * dyn * qh;
+      dzv[ct] = dqt * a.scale * gam * qh * 2.f * sg * (1.f - sg);
+      dkn[ct] = dkw + dkh * bg[ct];
+      dbv[ct] = dkh * knv;
+      dwv[ct] = du[ct] * vx[ct];
+      dvv[ct] = du[ct] * wg[ct];
+      sdb += dbv[ct];
+      sdw += dwv[ct];
+      dotq += qh * dqh[ct];
+      dotk += knv * dkn[ct];
     }
     if (a.normalize_qk) {
-      dotq = wave_sum(dotq);
-      dotk = wave_sum(dotk);
+      dotq = group16_sum(dotq);
+      dotk = group16_sum(dotk);
     }
+    if (a.b_mode == GDR_GATE_PER_TOKEN) sdb = group16_sum(sdb);
+    if (a.w_mode == GDR_GATE_PER_TOKEN) sdw = group16_sum(sdw);
+    float gq[NCT], gk[NCT];
 #pragma unroll
-    for (int u = 0; u < CPL; ++u) {
-      const int ch = lane + 64 * u;
-      float gq = dqh[u], gk = dkn[u];
+    for (int ct = 0; ct < NCT; ++ct) {
+      gq[ct] = dqh[ct];
+      gk[ct] = dkn[ct];
       if (a.normalize_qk) {
         // through y = s / max(|s|, 1e-12), then s = SiLU(x)
-        const float qh = sq[u] / rq, kn = sk[u] / rk;
-        gq = rq > 1e-12f ? (gq - qh * dotq) / rq : gq / 1e-12f;
-        gk = rk > 1e-12f ? (gk - kn * dotk) / rk : gk / 1e-12f;
-        const float sgq = 1.f / (1.f + expf(-qx[u])), sgk = 1.f / (1.f + expf(-kx[u]));
-        gq *= sgq * (1.f + qx[u] * (1.f - sgq));
-        gk *= sgk * (1.f + kx[u] * (1.f - sgk));
+        const float qh = sq[ct] / rq, knv = sn[ct] / rk;
+        gq[ct] = rq > 1e-12f ? (gq[ct] - qh * dotq) / rq : gq[ct] / 1e-12f;
+        gk[ct] = rk > 1e-12f ? (gk[ct] - knv * dotk) / rk : gk[ct] / 1e-12f;
+        const float sgq = 1.f / (1.f + expf(-qx[ct])), sgk = 1.f / (1.f + expf(-kx[ct]));
+        gq[ct] *= sgq * (1.f + qx[ct] * (1.f - sgq));
+        gk[ct] *= sgk * (1.f + kx[ct] * (1.f - sgk));
       }
-      if (a.dq) a.dq[row * D + ch] = gq;
-      if (a.dk) a.dk[row * D + ch] = gk;
+    }
+    if (live) {
+      const size_t o = grow * D + c0;
+      if (a.dq) stn<NCT>(a.dq + o, gq);
+      if (a.dk) stn<NCT>(a.dk + o, gk);
+      if (a.dv) stn<NCT>(a.dv + o, dvv);
+      if (a.dz && a.z) stn<NCT>(a.dz + o, dzv);
+      if (a.db && a.b_mode == GDR_GATE_PER_CHANNEL) stn<NCT>(a.db + o, dbv);
+      if (a.dw && a.w_mode == GDR_GATE_PER_CHANNEL) stn<NCT>(a.dw + o, dwv);
+      if (l16 == 0) {
+        if (a.db && a.b_mode == GDR_GATE_PER_TOKEN) a.db[grow] = sdb;
+        if (a.dw && a.w_mode == GDR_GATE_PER_TOKEN) a.dw[grow] = sdw;
+      }
     }
   }
 #pragma unroll
-  for (int u = 0; u < CPL; ++u) gp[wave][lane + 64 * u] = gacc[u];
+  for (int ct = 0; ct < NCT; ++ct) {
+    sk[(4 * w + g) * D + c0 + ct] = skp[ct];
+    gp[(4 * w + g) * D + c0 + ct] = gac[ct];
+  }
   __syncthreads();
-  if (tid < D) a.gpart[slot * D + tid] = gp[0][tid] + gp[1][tid] + gp[2][tid] + gp[3][tid];
+  if (tid < D) {
+    // the chunk-end decay: K' and Diag(a_C) S0 in the end state; then d log
+    // alpha = the reverse cumulative sum of dLambda over the chunk
+    const int ch = tid;
+    float run = __expf(a.LAM[base + (size_t)(C - 1) * D + ch]) * a.XS[slot * D + ch], gs = 0.f;
+#pragma unroll
+    for (int p2 = 0; p2 < 16; ++p2) {
+      run += sk[p2 * D + ch];
+      gs += gp[p2 * D + ch];
+    }
+    a.gpart[slot * D + ch] = gs;
+    const bool per_ch = a.dla && a.alpha_mode == GDR_GATE_PER_CHANNEL;
+    for (int t = C - 1; t >= 0; --t) {
+      run += dl[t * DP + ch];
+      dl[t * DP + ch] = run;
+      if (per_ch && c * C + t < a.T) a.dla[(bh * a.T + c * C + t) * D + ch] = run;
+    }
+  }
+  if (a.dla && a.alpha_mode == GDR_GATE_PER_TOKEN) {
+    __syncthreads();
+    const int t = tid >> 2, qq = tid & 3;
+    float sv = 0.f;
+    for (int j = 0; j < D / 4; ++j) sv += dl[t * DP + qq * (D / 4) + j];
+    sv += __shfl_xor(sv, 1, kWave);
+    sv += __shfl_xor(sv, 2, kWave);
+    if (qq == 0 && c * C + t < a.T) a.dla[bh * a.T + c * C + t] = sv;
+  }
 }
 
-// K10: dgamma[h][c] = sum over the batch and the chunks of the partial sums.
+// K10: dgamma[h][c] = sum over the batch and the chunks of the partial sums;
+// one workgroup per (head, 32 channels), 8 threads per channel.
 template <int D>
 __global__ void __launch_bounds__(256) bwd_dgamma_kernel(BwdArgs a) {
-  const int idx = blockIdx.x * 256 + threadIdx.x;
-  if (idx >= a.H * D) return;
-  const int h = idx / D, ch = idx % D;
+  __shared__ float part[8][32];
+  const int h = blockIdx.x / (D / 32), cl = threadIdx.x & 31, j = threadIdx.x >> 5;
+  const int ch = (blockIdx.x % (D / 32)) * 32 + cl;
   float s = 0.f;
-  for (int b = 0; b < a.B; ++b)
-    for (int c = 0; c < a.NC; ++c) s += a.gpart[((size_t)(b * a.H + h) * a.NC + c) * D + ch];
-  a.dgamma[idx] = s;
+  for (int k = j; k < a.B * a.NC; k += 8) {
+    const int b = k / a.NC, c = k % a.NC;
+    s += a.gpart[((size_t)(b * a.H + h) * a.NC + c) * D + ch];
+  }
+  part[j][cl] = s;
+  __syncthreads();
+  if (j == 0) {
+#pragma unroll
+    for (int i = 1; i < 8; ++i) s += part[i][cl];
+    a.dgamma[h * D + ch] = s;
+  }
 }
 
 template <int D, int NS, bool BF>
@@ -841,17 +851,15 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
   const unsigned nch = (unsigned)((size_t)a.B * a.H * a.NC);
   if (nch == 0) {  // empty sequences: only dgamma (zeros)
     if (a.dgamma && a.gamma)
-      hipLaunchKernelGGL((bwd_dgamma_kernel<D>), dim3((unsigned)((a.H * D + 255) / 256)), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((bwd_dgamma_kernel<D>), dim3((unsigned)(a.H * (D / 32))), dim3(256), 0, st, a);
     return hipGetLastError();
   }
   hipLaunchKernelGGL((bwd_prepass_kernel<D, BF>), dim3(nch), dim3(256), 0, st, a);
   hipLaunchKernelGGL((bwd_gram_kernel<D>), dim3(nch), dim3(256), 0, st, a);
-  hipLaunchKernelGGL((bwd_states_kernel<D, NS>), dim3(nch), dim3(256), 0, st, a);
-  hipLaunchKernelGGL((bwd_mm_kernel<D>), dim3(nch), dim3(256), 0, st, a);
-  hipLaunchKernelGGL((bwd_gramback_kernel<D>), dim3(nch), dim3(256), 0, st, a);
-  hipLaunchKernelGGL((bwd_final_kernel<D, BF>), dim3(nch), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((bwd_mm_kernel<D, NS>), dim3(nch), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((bwd_gramback_kernel<D, BF>), dim3(nch), dim3(256), 0, st, a);
   if (a.dgamma && a.gamma)
-    hipLaunchKernelGGL((bwd_dgamma_kernel<D>), dim3((unsigned)((a.H * D + 255) / 256)), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((bwd_dgamma_kernel<D>), dim3((unsigned)(a.H * (D / 32))), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -877,24 +885,19 @@ size_t bwd_workspace(BwdArgs *a, ChunkArgs *f, void *ws, int B, int H, int T, in
   };
   void *mt = take(nch * NS * (size_t)D * D * 2), *xc = take(nch * NS * (size_t)D * D * 2);
   void *gn = take(nch * (size_t)D * D * 4);
-  float **cd[13] = {&a->KN, &a->KH, &a->QT, &a->VH, &a->LAM, &a->DU, &a->DQA, &a->DKA, &a->DKP,
-                    &a->DQT, &a->DKT, &a->DKN, &a->DLA};
-  float *cdp[13];
-  for (int i = 0; i < 13; ++i) cdp[i] = static_cast<float *>(take(nch * (size_t)kBC * D * 4));
+  float **cd[9] = {&a->KN, &a->KH, &a->QT, &a->VH, &a->LAM, &a->DU, &a->DQA, &a->DKA, &a->DKP};
+  float *cdp[9];
+  for (int i = 0; i < 9; ++i) cdp[i] = static_cast<float *>(take(nch * (size_t)kBC * D * 4));
   float *ccp[4];
   for (int i = 0; i < 4; ++i) ccp[i] = static_cast<float *>(take(nch * (size_t)kBC * kBC * 4));
   float *gp = static_cast<float *>(take(nch * (size_t)D * 4));
-  float *s0f = static_cast<float *>(take(nch * (size_t)D * D * 4));
-  float *xf = static_cast<float *>(take(nch * (size_t)D * D * 4));
   float *xs = static_cast<float *>(take(nch * (size_t)D * 4));
   if (a) {
-    a->S0f = s0f;
-    a->Xf = xf;
     a->XS = xs;
     a->Mt = static_cast<uint16_t *>(mt);
     a->Xc = static_cast<uint16_t *>(xc);
     a->Gn = static_cast<float *>(gn);
-    for (int i = 0; i < 13; ++i) *cd[i] = cdp[i];
+    for (int i = 0; i < 9; ++i) *cd[i] = cdp[i];
     a->AM = ccp[0];
     a->TI = ccp[1];
     a->DA = ccp[2];

@@ -69,11 +69,10 @@ struct BwdArgs {
   uint16_t *Mt, *Xc;             // M^T for the reverse chain; the chunk-end state gradients
   float *Gn;                     // Q'^T dO for the reverse chain
   // per-chunk scratch, [slot][64][D] fp32
-  float *KN, *KH, *QT, *VH, *LAM, *DU, *DQA, *DKA, *DKP, *DQT, *DKT, *DKN, *DLA;
+  float *KN, *KH, *QT, *VH, *LAM, *DU, *DQA, *DKA, *DKP;
   float *AM, *TI, *DA, *DL;      // [slot][64][64] fp32
   float *gpart;                  // [slot][D] partial sums of dgamma
-  float *S0f, *Xf;               // [slot][D][D] fp32 chunk-start states and chunk-end state gradients
-  float *XS;                     // [slot][D] row dots of the two
+  float *XS;                     // [slot][D] row dots sum_j X_ij S0_ij of each chunk's end-state gradient and start state
   float *dq, *dk, *dv, *dla, *db, *dw, *dz, *dgamma;  // outputs (each may be null)
 };
 // Workspace of the backward: the forward's chunk workspace (C = 64; its fields
