@@ -138,29 +138,78 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// K3 pre-pass: per chunk slot (4 waves x 16 tokens, lanes over channels), the
-// forward's per-token vectors: kn, k_hat, q_tilde, v_hat and the cumulative
-// log-decay Lambda.  Padding tokens past T are zero (identity steps).
+// K3 pre-pass: per chunk slot, the forward's per-token vectors kn, k_hat,
+// q_tilde, v_hat and the cumulative log-decay Lambda.  Wave w takes tokens
+// 16w..16w+15, lane CPL = D / 64 consecutive channels; Lambda is summed along
+// the wave's tokens in registers, then offset by the earlier waves' totals.
+// Padding tokens past T are zero (identity steps).
 // ---------------------------------------------------------------------------
+template <bool BF, int N>
+__device__ __forceinline__ void ldc(const void *p, size_t i, float (&o)[N]) {
+  if constexpr (N == 2) {
+    if constexpr (BF) {
+      const uint32_t u = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint16_t *>(p) + i);
+      o[0] = __uint_as_float(u << 16);
+      o[1] = __uint_as_float(u & 0xffff0000u);
+    } else {
+      const float2 f = *reinterpret_cast<const float2 *>(reinterpret_cast<const float *>(p) + i);
+      o[0] = f.x;
+      o[1] = f.y;
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < N; ++u) o[u] = ld1<BF>(p, i + u);
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void stc(float *p, const float (&x)[N]) {
+  if constexpr (N == 2)
+    *reinterpret_cast<float2 *>(p) = float2{x[0], x[1]};
+  else
+#pragma unroll
+    for (int u = 0; u < N; ++u) p[u] = x[u];
+}
+
 template <int D, bool BF>
 __global__ void __launch_bounds__(256) bwd_prepass_kernel(BwdArgs a) {
-  constexpr int C = kBC, CPL = D / 64;  // channels per lane
-  __shared__ float la[C][D + 1];
+  constexpr int C = kBC, CPL = D / 64, TW = C / 4;
+  __shared__ float tot[4][D];
   const size_t slot = blockIdx.x;
   const size_t bh = slot / a.NC;
   const int c = (int)(slot % a.NC), h = (int)(bh % a.H);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, ch0 = CPL * lane;
   const size_t base = slot * (size_t)C * D;
-  for (int t = wave; t < C; t += 4) {
-    const int tt = c * C + t;
-    const bool ok = tt < a.T;
+  float gam[CPL], run[CPL], lam[TW][CPL];
+#pragma unroll
+  for (int u = 0; u < CPL; ++u) {
+    gam[u] = a.gamma ? a.gamma[(size_t)h * D + ch0 + u] : 1.f;
+    run[u] = 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < TW; ++j) {
+    const int t = TW * w + j, tt = c * C + t;
+    const bool ok = tt < a.T;  // uniform over the wave
     const size_t row = bh * a.T + (ok ? tt : 0);
-    float qv[CPL], kv[CPL], sq = 0.f, sk = 0.f;
+    float qv[CPL], kv[CPL], vv[CPL], zv[CPL], bg[CPL], wg[CPL], la[CPL];
+    float sq = 0.f, sk = 0.f;
+    if (ok) {
+      ldc<BF, CPL>(a.q, row * D + ch0, qv);
+      ldc<BF, CPL>(a.k, row * D + ch0, kv);
+      ldc<BF, CPL>(a.v, row * D + ch0, vv);
+#pragma unroll
+      for (int u = 0; u < CPL; ++u) {
+        zv[u] = a.z ? ld1<BF>(a.z, row * D + ch0 + u) : 0.f;
+        bg[u] = gate_at<BF>(a.b, a.b_mode, row, ch0 + u, D);
+        wg[u] = gate_at<BF>(a.w, a.w_mode, row, ch0 + u, D);
+        la[u] = log_alpha_at(a.log_alpha, a.alpha_mode, row, ch0 + u, D);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < CPL; ++u) qv[u] = kv[u] = vv[u] = zv[u] = bg[u] = wg[u] = la[u] = 0.f;
+    }
 #pragma unroll
     for (int u = 0; u < CPL; ++u) {
-      const int ch = lane + 64 * u;
-      qv[u] = ok ? ld1<BF>(a.q, row * D + ch) : 0.f;
-      kv[u] = ok ? ld1<BF>(a.k, row * D + ch) : 0.f;
       if (a.normalize_qk) {
         qv[u] = silu(qv[u]);
         kv[u] = silu(kv[u]);
@@ -173,29 +222,38 @@ __global__ void __launch_bounds__(256) bwd_prepass_kernel(BwdArgs a) {
       iq = 1.f / fmaxf(sqrtf(wave_sum(sq)), 1e-12f);
       ik = 1.f / fmaxf(sqrtf(wave_sum(sk)), 1e-12f);
     }
+    float kn[CPL], kh[CPL], qt[CPL], vh[CPL];
 #pragma unroll
     for (int u = 0; u < CPL; ++u) {
-      const int ch = lane + 64 * u;
-      const float gam = a.gamma ? a.gamma[(size_t)h * D + ch] : 1.f;
-      const float dyn = (a.z && ok) ? 2.f / (1.f + expf(-ld1<BF>(a.z, row * D + ch))) : 1.f;
-      const float kn = kv[u] * ik;
-      const float bg = ok ? gate_at<BF>(a.b, a.b_mode, row, ch, D) : 0.f;
-      const float wg = ok ? gate_at<BF>(a.w, a.w_mode, row, ch, D) : 0.f;
-      const float vv = ok ? ld1<BF>(a.v, row * D + ch) : 0.f;
-      a.KN[base + t * D + ch] = ok ? kn : 0.f;
-      a.KH[base + t * D + ch] = bg * kn;
-      a.QT[base + t * D + ch] = ok ? a.scale * gam * dyn * qv[u] * iq : 0.f;
-      a.VH[base + t * D + ch] = wg * vv;
-      la[t][ch] = ok ? log_alpha_at(a.log_alpha, a.alpha_mode, row, ch, D) : 0.f;
+      const float dyn = (a.z && ok) ? 2.f / (1.f + expf(-zv[u])) : 1.f;
+      kn[u] = kv[u] * ik;
+      kh[u] = bg[u] * kn[u];
+      qt[u] = ok ? a.scale * gam[u] * dyn * qv[u] * iq : 0.f;
+      vh[u] = wg[u] * vv[u];
+      run[u] += la[u];
+      lam[j][u] = run[u];
     }
+    const size_t o = base + (size_t)t * D + ch0;
+    stc<CPL>(a.KN + o, kn);
+    stc<CPL>(a.KH + o, kh);
+    stc<CPL>(a.QT + o, qt);
+    stc<CPL>(a.VH + o, vh);
   }
+#pragma unroll
+  for (int u = 0; u < CPL; ++u) tot[w][ch0 + u] = run[u];
   __syncthreads();
-  if (tid < D) {
-    float run = 0.f;
-    for (int t = 0; t < C; ++t) {
-      run += la[t][tid];
-      a.LAM[base + t * D + tid] = run;
-    }
+  float off[CPL];
+#pragma unroll
+  for (int u = 0; u < CPL; ++u) {
+    off[u] = 0.f;
+    for (int w2 = 0; w2 < w; ++w2) off[u] += tot[w2][ch0 + u];
+  }
+#pragma unroll
+  for (int j = 0; j < TW; ++j) {
+    float x[CPL];
+#pragma unroll
+    for (int u = 0; u < CPL; ++u) x[u] = lam[j][u] + off[u];
+    stc<CPL>(a.LAM + base + (size_t)(TW * w + j) * D + ch0, x);
   }
 }
 
