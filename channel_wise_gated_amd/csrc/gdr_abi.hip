@@ -222,23 +222,27 @@ gdr_status gdr_chunk_bwd(const gdr_desc *desc, const void *q, const void *k, con
   a.dz = z ? dz : nullptr;
   a.dgamma = gamma ? dgamma : nullptr;
   hipError_t e = hipSuccess;
+  if (a.NC > 0) gdr::bwd_workspace(&a, &f, workspace, d.B, d.H, d.T, d.dk, ns);
+  // the chain of chunk-end state gradients, last chunk to first (the final
+  // one is dS0): the forward's chain kernel with M^T and Q'^T dO
+  gdr::ChunkArgs r = f;
+  r.Mm = a.NC > 0 ? a.Mt : nullptr;
+  r.Nn = a.NC > 0 ? a.Gn : nullptr;
+  r.Sc = a.NC > 0 ? a.Xc : nullptr;
+  r.S0 = dS_T;
+  r.S_T = dS0;
+  r.rev = 1;
   if (a.NC > 0) {
-    gdr::bwd_workspace(&a, &f, workspace, d.B, d.H, d.T, d.dk, ns);
     a.Qp = f.Qp; a.Mm = f.Mm; a.Sc = f.Sc;
-    // forward recompute: chunk maps and chunk-start states
-    e = gdr::launch_chunk(fd, f, 1 | 4, st);
+    // forward recompute: the chunk maps, then M^T and Q'^T dO; then the
+    // forward chain (chunk-start states) and the reverse chain side by side
+    e = gdr::launch_chunk(fd, f, 1, st);
     if (e == hipSuccess) e = gdr::launch_bwd_prep(a, d.dk, ns, st);
-  }
-  if (e == hipSuccess) {
-    // chunk-end state gradients, last chunk to first; the final one is dS0
-    gdr::ChunkArgs r = f;
-    r.Mm = a.NC > 0 ? a.Mt : nullptr;
-    r.Nn = a.NC > 0 ? a.Gn : nullptr;
-    r.Sc = a.NC > 0 ? a.Xc : nullptr;
-    r.S0 = dS_T;
-    r.S_T = dS0;
-    r.rev = 1;
-    if (dS0 || a.NC > 0) e = gdr::launch_chunk(fd, r, 4, st);
+    f.c0 = r.c0 = 0;
+    f.ncs = r.ncs = a.NC;
+    if (e == hipSuccess) e = gdr::launch_chain_pair(fd, f, r, st);
+  } else if (dS0) {
+    e = gdr::launch_chunk(fd, r, 4, st);
   }
   if (e == hipSuccess && a.NC > 0) e = gdr::launch_bwd(a, d.dk, ns, st);
   else if (e == hipSuccess && a.dgamma) e = gdr::launch_bwd(a, d.dk, ns, st);

@@ -915,16 +915,18 @@ struct ChainBuf {
   f32x4 nn;              // accumulator tile of N
 };
 
+// S_c planes, double-buffered by chunk parity: step c reads buffer c & 1 and
+// writes buffer (c + 1) & 1, so one barrier per step suffices
+template <int D, int NS>
+using ChainLds = uint16_t[2][(D / 32) * NS * 64 * 8];
+
+// The chain of workgroup `id` of a launch over the chain `a`.
 template <int C, int D, int NS>
-__global__ void __launch_bounds__(64 * (D / 16)) chunk_chain_kernel(ChunkArgs a) {
+__device__ __forceinline__ void chain_run(const ChunkArgs &a, int id, ChainLds<D, NS> &sfr2) {
   constexpr int NMT = D / 16, NKD = D / 32, NSL = D / 16;
   constexpr int FRAG = 64 * 8, NFR = NKD * NS;
-  // S_c planes, double-buffered by chunk parity: step c reads buffer c & 1 and
-  // writes buffer (c + 1) & 1, so one barrier per step suffices
-  __shared__ __align__(16) uint16_t sfr2[2][NFR * FRAG];
 
   // all slices of one stream on the same XCD (workgroups go round-robin over 8)
-  const int id = blockIdx.x;
   const int grp = id / (8 * NSL), rem = id % (8 * NSL);
   const int slice = rem / 8;
   const size_t bh = (size_t)grp * 8 + rem % 8;
@@ -1052,6 +1054,21 @@ __global__ void __launch_bounds__(64 * (D / 16)) chunk_chain_kernel(ChunkArgs a)
 #pragma unroll
     for (int r = 0; r < 4; ++r) a.S_T[(bh * D + 16 * wave + 4 * g + r) * D + col] = S[r];
   }
+}
+
+template <int C, int D, int NS>
+__global__ void __launch_bounds__(64 * (D / 16)) chunk_chain_kernel(ChunkArgs a) {
+  __shared__ __align__(16) ChainLds<D, NS> sfr2;
+  chain_run<C, D, NS>(a, blockIdx.x, sfr2);
+}
+
+// Two independent chains in one launch: workgroups [0, na) run `a`, the rest
+// `b` (na a multiple of 8, so both keep their XCD placement).
+template <int C, int D, int NS>
+__global__ void __launch_bounds__(64 * (D / 16)) chunk_chain2_kernel(ChunkArgs a, ChunkArgs b, int na) {
+  __shared__ __align__(16) ChainLds<D, NS> sfr2;
+  const bool first = (int)blockIdx.x < na;
+  chain_run<C, D, NS>(first ? a : b, first ? (int)blockIdx.x : (int)blockIdx.x - na, sfr2);
 }
 
 // ============================================================================
@@ -1381,6 +1398,23 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, int phases, hipStream_t st)
   } else {
     return hipErrorInvalidValue;
   }
+}
+
+template <int C, int D, int NS>
+static hipError_t launch_chain_pair_t(const ChunkArgs &a, const ChunkArgs &b, hipStream_t st) {
+  constexpr int NSL = D / 16;
+  const size_t na = (((size_t)a.B * a.H + 7) / 8) * 8 * NSL, nb = (((size_t)b.B * b.H + 7) / 8) * 8 * NSL;
+  hipLaunchKernelGGL((chunk_chain2_kernel<C, D, NS>), dim3((unsigned)(na + nb)), dim3(64 * (D / 16)), 0, st, a, b,
+                     (int)na);
+  return hipGetLastError();
+}
+
+hipError_t launch_chain_pair(const gdr_desc &d, const ChunkArgs &a, const ChunkArgs &b, hipStream_t st) {
+  const bool ib = d.in_dtype == GDR_BF16;
+  if (d.chunk != 64) return hipErrorInvalidValue;
+  if (d.dk == 128) return ib ? launch_chain_pair_t<64, 128, 2>(a, b, st) : launch_chain_pair_t<64, 128, 3>(a, b, st);
+  if (d.dk == 64) return ib ? launch_chain_pair_t<64, 64, 2>(a, b, st) : launch_chain_pair_t<64, 64, 3>(a, b, st);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_chunk(const gdr_desc &d, const ChunkArgs &a, int phases, hipStream_t st) {

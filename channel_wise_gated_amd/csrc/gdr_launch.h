@@ -87,6 +87,9 @@ hipError_t launch_decode(const gdr_desc &d, float *S, const void *q, const void 
 // phases: bit 0 = intra-chunk kernel, bit 1 = scan (chain + output kernels),
 // bit 2 = chain kernel only (no output)
 hipError_t launch_chunk(const gdr_desc &d, const ChunkArgs &a, int phases, hipStream_t st);
+// Two independent chains (the chain kernel only) over uniform batches at C = 64
+// in one launch; each ChunkArgs with c0 = 0 and ncs = its chunks per stream.
+hipError_t launch_chain_pair(const gdr_desc &d, const ChunkArgs &a, const ChunkArgs &b, hipStream_t st);
 // Workspace of the chunkwise forward: per chunk slot the maps Q', M, O_bar,
 // N and the chunk-start state; for a packed batch (nseq > 0) the chunk list
 // and sequence offsets, otherwise (T > 0) the fp32 states [B,H,D,D] handed
