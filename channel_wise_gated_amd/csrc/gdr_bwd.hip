@@ -267,7 +267,8 @@ __global__ void __launch_bounds__(256) bwd_prepass_kernel(BwdArgs a) {
 // too).  For a diagonal tile P is Lambda at the block's first token: the s-side
 // factor grows to e^{range} over the block; when the range exceeds 60 (far
 // from fp32 overflow) the tile is recomputed pair by pair.  Then
-// T^-1 = (I + L)^-1 column by column (forward substitution).
+// T^-1 = (I + L)^-1 column by column (forward substitution, four lanes a
+// column).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
@@ -345,14 +346,17 @@ __global__ void __launch_bounds__(256) bwd_gram_kernel(BwdArgs a) {
     }
   }
   __syncthreads();
-  // T^-1 column s (thread s): x_t = delta_ts - sum_{s <= r < t} L[t][r] x_r
-  if (tid < C) {
-    const int s2 = tid;
+  // T^-1 column s by four adjacent lanes (each summing every fourth r):
+  // x_t = delta_ts - sum_{s <= r < t} L[t][r] x_r
+  {
+    const int s2 = tid >> 2, j = tid & 3;
     for (int t = 0; t < C; ++t) {
-      float x = t == s2 ? 1.f : 0.f;
+      float part = 0.f;
       if (t > s2)
-        for (int r = s2; r < t; ++r) x -= L[t * LP + r] * ti[r * LP + s2];
-      ti[t * LP + s2] = x;
+        for (int r = s2 + j; r < t; r += 4) part += L[t * LP + r] * ti[r * LP + s2];
+      part += __shfl_xor(part, 1, kWave);
+      part += __shfl_xor(part, 2, kWave);
+      if (j == 0) ti[t * LP + s2] = (t == s2 ? 1.f : 0.f) - part;
     }
   }
   __syncthreads();
