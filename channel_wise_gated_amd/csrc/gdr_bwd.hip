@@ -642,19 +642,43 @@ __device__ __forceinline__ void stn(float *p, const float (&x)[N]) {
 // ---------------------------------------------------------------------------
 template <int D, bool BF>
 __global__ void __launch_bounds__(256) bwd_gramback_kernel(BwdArgs a) {
-  constexpr int C = kBC, NCT = D / 16, NV = NCT / 4, DP = D + 1;
+  constexpr int C = kBC, NCT = D / 16, NV = NCT / 4, SPD = D + 4;
   constexpr float kMaxRange = 60.f;
+  constexpr int IKN = 0, ILA = 1, IQT = 2, IKH = 3;
   static_assert(C == 64, "four waves, one 16-token block each");
-  __shared__ float dl[C * DP];  // dLambda, then d log alpha
-  __shared__ float sk[16 * D];  // per (wave, lane group): sum_t kn rat dK'
-  __shared__ float gp[16 * D];  // per (wave, lane group): partial dgamma
+  // kn, Lambda, q_tilde and k_hat of the chunk, rows padded to SPD; once every
+  // wave is past its products and per-token work, the first holds dLambda
+  // (then d log alpha) and the second the per-(wave, lane group) partial sums
+  __shared__ __align__(16) float stg[4][C * SPD];
+  float *dl = stg[IKN], *sk = stg[ILA], *gp = stg[ILA] + 16 * D;
   const size_t slot = blockIdx.x;
   const size_t bh = slot / a.NC;
   const int c = (int)(slot % a.NC), hd = (int)(bh % a.H);
   const size_t base = slot * (size_t)C * D, cbase = slot * (size_t)C * C;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, g = lane >> 4;
   const int c0 = NCT * l16;  // first channel of this lane
-  auto row = [&](const float *p, int t, float (&o)[NCT]) {
+  {
+    const float *src[4] = {a.KN, a.LAM, a.QT, a.KH};
+    for (int idx = tid; idx < C * D / 4; idx += 256) {
+      const int t = idx / (D / 4), j4 = idx % (D / 4);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4 *>(stg[q] + t * SPD + 4 * j4) =
+            *reinterpret_cast<const float4 *>(src[q] + base + (size_t)t * D + 4 * j4);
+    }
+  }
+  __syncthreads();
+  auto row = [&](int q, int t, float (&o)[NCT]) {  // staged array q, token t
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const float4 x = *reinterpret_cast<const float4 *>(stg[q] + t * SPD + c0 + 4 * v);
+      o[4 * v] = x.x;
+      o[4 * v + 1] = x.y;
+      o[4 * v + 2] = x.z;
+      o[4 * v + 3] = x.w;
+    }
+  };
+  auto rowg = [&](const float *p, int t, float (&o)[NCT]) {  // [C][D] workspace array, token t
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
       const float4 x = *reinterpret_cast<const float4 *>(p + base + (size_t)t * D + c0 + 4 * v);
@@ -665,8 +689,8 @@ __global__ void __launch_bounds__(256) bwd_gramback_kernel(BwdArgs a) {
     }
   };
   float qv[NCT], rv[NCT];
-  row(a.LAM, 16 * w, qv);
-  row(a.LAM, 16 * w + 15, rv);
+  row(ILA, 16 * w, qv);
+  row(ILA, 16 * w + 15, rv);
   float rng = 0.f;
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) rng = fmaxf(rng, qv[ct] - rv[ct]);
@@ -675,7 +699,7 @@ __global__ void __launch_bounds__(256) bwd_gramback_kernel(BwdArgs a) {
   f32x4 ra[NCT], rl[NCT], cs[NCT];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) ra[ct] = rl[ct] = cs[ct] = zero4();
-#pragma unroll
+#pragma unroll 1
   for (int kb = 0; kb < 4; ++kb) {
     if (kb < kend) {  // rows: s = 16 kb + 4 g + e
       const float4 da4 = *reinterpret_cast<const float4 *>(a.DA + cbase + (size_t)(16 * w + l16) * C + 16 * kb + 4 * g);
@@ -684,8 +708,8 @@ __global__ void __launch_bounds__(256) bwd_gramback_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float kn[NCT], ls[NCT];
-        row(a.KN, 16 * kb + 4 * g + e, kn);
-        row(a.LAM, 16 * kb + 4 * g + e, ls);
+        row(IKN, 16 * kb + 4 * g + e, kn);
+        row(ILA, 16 * kb + 4 * g + e, ls);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
           const float b = kn[ct] * __expf(qv[ct] - ls[ct]);
@@ -700,9 +724,9 @@ __global__ void __launch_bounds__(256) bwd_gramback_kernel(BwdArgs a) {
         const int t = 16 * kb + 4 * g + e;
         const float dat = a.DA[cbase + (size_t)t * C + 16 * w + l16], dlt = a.DL[cbase + (size_t)t * C + 16 * w + l16];
         float q[NCT], h[NCT], lt[NCT];
-        row(a.QT, t, q);
-        row(a.KH, t, h);
-        row(a.LAM, t, lt);
+        row(IQT, t, q);
+        row(IKH, t, h);
+        row(ILA, t, lt);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
           const float f = __expf(lt[ct] - rv[ct]);
@@ -712,21 +736,21 @@ __global__ void __launch_bounds__(256) bwd_gramback_kernel(BwdArgs a) {
       }
     }
   }
-  float lc[NCT], skp[NCT], gac[NCT];
-  row(a.LAM, C - 1, lc);
+  float lc[NCT], skp[NCT], gac[NCT], dlv[4][NCT];
+  row(ILA, C - 1, lc);
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) skp[ct] = gac[ct] = 0.f;
-#pragma unroll
+#pragma unroll 1
   for (int r = 0; r < 4; ++r) {
     const int t = 16 * w + 4 * g + r;
     float lt[NCT], q[NCT], h[NCT], kn[NCT], dqa[NCT], dka[NCT], dkp[NCT];
-    row(a.LAM, t, lt);
-    row(a.QT, t, q);
-    row(a.KH, t, h);
-    row(a.KN, t, kn);
-    row(a.DQA, t, dqa);
-    row(a.DKA, t, dka);
-    row(a.DKP, t, dkp);
+    row(ILA, t, lt);
+    row(IQT, t, q);
+    row(IKH, t, h);
+    row(IKN, t, kn);
+    rowg(a.DQA, t, dqa);
+    rowg(a.DKA, t, dka);
+    rowg(a.DKP, t, dkp);
     float RA[NCT], RL[NCT], CS[NCT];
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
@@ -739,8 +763,8 @@ __global__ void __launch_bounds__(256) bwd_gramback_kernel(BwdArgs a) {
       for (int s2 = 16 * w; s2 <= t; ++s2) {
         const float dat = a.DA[cbase + (size_t)t * C + s2], dlt = a.DL[cbase + (size_t)t * C + s2];
         float k2[NCT], l2[NCT];
-        row(a.KN, s2, k2);
-        row(a.LAM, s2, l2);
+        row(IKN, s2, k2);
+        row(ILA, s2, l2);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
           const float x = k2[ct] * __expf(lt[ct] - l2[ct]);
@@ -751,9 +775,9 @@ __global__ void __launch_bounds__(256) bwd_gramback_kernel(BwdArgs a) {
       for (int t2 = t; t2 < 16 * w + 16; ++t2) {
         const float dat = a.DA[cbase + (size_t)t2 * C + t], dlt = a.DL[cbase + (size_t)t2 * C + t];
         float q2[NCT], h2[NCT], l2[NCT];
-        row(a.QT, t2, q2);
-        row(a.KH, t2, h2);
-        row(a.LAM, t2, l2);
+        row(IQT, t2, q2);
+        row(IKH, t2, h2);
+        row(ILA, t2, l2);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) CS[ct] += (dat * q2[ct] + dlt * h2[ct]) * __expf(l2[ct] - lt[ct]);
       }
@@ -778,7 +802,7 @@ __global__ void __launch_bounds__(256) bwd_gramback_kernel(BwdArgs a) {
       gate4<BF>(a.b, a.b_mode, grow, c0 + 4 * v, D, bg + 4 * v);
       gate4<BF>(a.w, a.w_mode, grow, c0 + 4 * v, D, wg + 4 * v);
     }
-    row(a.DU, t, du);
+    rowg(a.DU, t, du);
     float sq[NCT], sn[NCT], nq = 0.f, nk = 0.f;
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
@@ -798,8 +822,8 @@ __global__ void __launch_bounds__(256) bwd_gramback_kernel(BwdArgs a) {
     for (int ct = 0; ct < NCT; ++ct) {
       const float at = __expf(lt[ct]), rat = __expf(lc[ct] - lt[ct]);
       const float dqt = at * dqa[ct] + RA[ct], dkh = at * dka[ct] + RL[ct], dkw = rat * dkp[ct] + CS[ct];
-      dl[t * DP + c0 + ct] = q[ct] * at * dqa[ct] + h[ct] * at * dka[ct] - kn[ct] * rat * dkp[ct] + q[ct] * RA[ct] +
-                             h[ct] * RL[ct] - kn[ct] * CS[ct];
+      dlv[r][ct] = q[ct] * at * dqa[ct] + h[ct] * at * dka[ct] - kn[ct] * rat * dkp[ct] + q[ct] * RA[ct] +
+                   h[ct] * RL[ct] - kn[ct] * CS[ct];
       skp[ct] += kn[ct] * rat * dkp[ct];
       const float qh = sq[ct] / rq, knv = sn[ct] / rk;
       const float gam = a.gamma ? a.gamma[(size_t)hd * D + c0 + ct] : 1.f;
@@ -852,8 +876,11 @@ __global__ void __launch_bounds__(256) bwd_gramback_kernel(BwdArgs a) {
       }
     }
   }
+  __syncthreads();  // the staged arrays are read for the last time
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dl[(16 * w + 4 * g + r) * SPD + c0 + ct] = dlv[r][ct];
     sk[(4 * w + g) * D + c0 + ct] = skp[ct];
     gp[(4 * w + g) * D + c0 + ct] = gac[ct];
   }
@@ -871,8 +898,8 @@ __global__ void __launch_bounds__(256) bwd_gramback_kernel(BwdArgs a) {
     a.gpart[slot * D + ch] = gs;
     const bool per_ch = a.dla && a.alpha_mode == GDR_GATE_PER_CHANNEL;
     for (int t = C - 1; t >= 0; --t) {
-      run += dl[t * DP + ch];
-      dl[t * DP + ch] = run;
+      run += dl[t * SPD + ch];
+      dl[t * SPD + ch] = run;
       if (per_ch && c * C + t < a.T) a.dla[(bh * a.T + c * C + t) * D + ch] = run;
     }
   }
@@ -880,7 +907,7 @@ __global__ void __launch_bounds__(256) bwd_gramback_kernel(BwdArgs a) {
     __syncthreads();
     const int t = tid >> 2, qq = tid & 3;
     float sv = 0.f;
-    for (int j = 0; j < D / 4; ++j) sv += dl[t * DP + qq * (D / 4) + j];
+    for (int j = 0; j < D / 4; ++j) sv += dl[t * SPD + qq * (D / 4) + j];
     sv += __shfl_xor(sv, 1, kWave);
     sv += __shfl_xor(sv, 2, kWave);
     if (qq == 0 && c * C + t < a.T) a.dla[bh * a.T + c * C + t] = sv;
