@@ -435,33 +435,40 @@ __global__ void __launch_bounds__(256) bwd_mm_kernel(BwdArgs a) {
   const uint16_t *S0p = a.Sc + slot * NS * (size_t)D * D, *Xp = a.Xc + slot * NS * (size_t)D * D;
   // A state from the chains' bf16 planes (summed in fp32) into padded LDS rows.
   // Entry (slice sl, k-step ks, lane) of a plane holds 8 values of column
-  // 16 sl + l16, rows 32 ks + 16 (e / 4) + 4 g + e % 4.  With `other` (a second
-  // state, same layout), the row dots sum_j X_ij S0_ij go to xs.
-  auto stage = [&](float *dst, const uint16_t *pl, const uint16_t *other) {
-    float dot[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    const int ks = (tid >> 6) % (D / 32);  // the same for all of this thread's entries
-    for (int idx = tid; idx < (D / 16) * (D / 32) * 64; idx += 256) {
-      const int sl = (idx >> 6) / (D / 32), col = 16 * sl + l16;
+  // 16 sl + l16, rows 32 ks + 16 (e / 4) + 4 g + e % 4; this thread's entries
+  // are tid + 256 k (k < NE), all with the same ks.  Loads and LDS stores are
+  // separate steps so that loads can be issued a phase ahead.
+  constexpr int NE = D * D / 8 / 256;
+  static_assert(NE * 256 * 8 == D * D, "plane entries per thread");
+  const int ks = (tid >> 6) % (D / 32);
+  auto load_planes = [&](const uint16_t *pl, bf16x8 (&r)[NE][NS]) {
+#pragma unroll
+    for (int k = 0; k < NE; ++k) {
+      const int sl = ((tid + 256 * k) >> 6) / (D / 32);
       const size_t off = (size_t)sl * NFR * FRAG + (size_t)(ks * NS) * FRAG + lane * 8;
-      float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int p = 0; p < NS; ++p) {
-        const bf16x8 f = *reinterpret_cast<const bf16x8 *>(pl + off + p * FRAG);
+      for (int p = 0; p < NS; ++p) r[k][p] = *reinterpret_cast<const bf16x8 *>(pl + off + p * FRAG);
+    }
+  };
+  // with `dots`, also the row dots with the state in `o` (same layout) -> xs
+  auto store_planes = [&](float *dst, const bf16x8 (&r)[NE][NS], const bf16x8 (&o)[NE][NS], bool dots) {
+    float dot[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] += (float)f[e];
-        if (other) {
-          const bf16x8 f2 = *reinterpret_cast<const bf16x8 *>(other + off + p * FRAG);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) o[e] += (float)f2[e];
-        }
-      }
+    for (int k = 0; k < NE; ++k) {
+      const int sl = ((tid + 256 * k) >> 6) / (D / 32), col = 16 * sl + l16;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        dst[(32 * ks + 16 * (e >> 2) + 4 * g + (e & 3)) * SP + col] = v[e];
-        dot[e] += v[e] * o[e];
+        float v = 0.f, u = 0.f;
+#pragma unroll
+        for (int p = 0; p < NS; ++p) {
+          v += (float)r[k][p][e];
+          if (dots) u += (float)o[k][p][e];
+        }
+        dst[(32 * ks + 16 * (e >> 2) + 4 * g + (e & 3)) * SP + col] = v;
+        if (dots) dot[e] += v * u;
       }
     }
-    if (other) {
+    if (dots) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         float d = dot[e];
@@ -489,7 +496,9 @@ __global__ void __launch_bounds__(256) bwd_mm_kernel(BwdArgs a) {
 
   // (1) S0 phase: R = V_hat - K_a S0 (-> LDS), dQ_a = dO S0^T
   if (tid < D) xs[tid] = 0.f;
-  stage(ss, S0p, nullptr);
+  bf16x8 pa[NE][NS], pb[NE][NS];  // planes: S0 now; then X (pa) and S0 (pb) for phase 3
+  load_planes(S0p, pa);
+  store_planes(ss, pa, pa, false);
   const int tt = c * C + ar;
   const size_t orow = (bh * a.T + (tt < a.T ? tt : 0)) * D;
 #pragma unroll
@@ -499,22 +508,28 @@ __global__ void __launch_bounds__(256) bwd_mm_kernel(BwdArgs a) {
     af[kb] = f32x4{kh.x * __expf(la.x), kh.y * __expf(la.y), kh.z * __expf(la.z), kh.w * __expf(la.w)};
     dof[kb] = tt < a.T ? ld_do4(a.dO, orow + 16 * kb + 4 * g, a.do_bf16) : zero4();
   }
+  float vh[NCT][4];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) vh[ct][r] = a.VH[base + (size_t)(16 * w + 4 * g + r) * D + 16 * ct + l16];
+#pragma unroll
+  for (int kb = 0; kb < NTC; ++kb)
+    tf[kb] = *reinterpret_cast<const f32x4 *>(a.TI + cbase + (size_t)ar * C + 16 * kb + 4 * g);
+  // phase 3's states, in flight during phases 1 and 2 (issued last: the
+  // load counter completes in order)
+  load_planes(Xp, pa);
+  load_planes(S0p, pb);
   __syncthreads();
   zero_acc(acc);
   mm_nn(acc, af, ss, SP, 0, NKB, g, l16);
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 16 * w + 4 * g + r, j = 16 * ct + l16;
-      bt[t * SP + j] = a.VH[base + (size_t)t * D + j] - acc[ct][r];
-    }
+    for (int r = 0; r < 4; ++r) bt[(16 * w + 4 * g + r) * SP + 16 * ct + l16] = vh[ct][r] - acc[ct][r];
   zero_acc(acc);
   mm_nt(acc, dof, ss, SP, NCT, g, l16);
   put_glb(a.DQA, acc, w, 1.f);
-#pragma unroll
-  for (int kb = 0; kb < NTC; ++kb)
-    tf[kb] = *reinterpret_cast<const f32x4 *>(a.TI + cbase + (size_t)ar * C + 16 * kb + 4 * g);
   __syncthreads();
 
   // (2) U = T^-1 R (T^-1 lower triangular: k-blocks up to the row tile)
@@ -524,7 +539,7 @@ __global__ void __launch_bounds__(256) bwd_mm_kernel(BwdArgs a) {
   __syncthreads();
 
   // (3) X phase: dA = dO U^T, Z = A^T dO + K' X, dK' = U X^T
-  stage(ss, Xp, S0p);
+  store_planes(ss, pa, pb, true);
   for (int idx = tid; idx < C * D / 4; idx += 256) {
     const int t = idx / (D / 4), j4 = idx % (D / 4), t2 = c * C + t;
     *reinterpret_cast<f32x4 *>(bt + t * SP + 4 * j4) =
@@ -593,7 +608,7 @@ __global__ void __launch_bounds__(256) bwd_mm_kernel(BwdArgs a) {
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) af[kb] = *reinterpret_cast<const f32x4 *>(ss + ar * SP + 16 * kb + 4 * g);
   __syncthreads();  // every read of U and Z is done
-  stage(bb, S0p, nullptr);
+  store_planes(bb, pb, pb, false);
   __syncthreads();
   zero_acc(acc);
   mm_nt(acc, af, bb, SP, NCT, g, l16);
