@@ -58,9 +58,11 @@ __device__ __forceinline__ f32x4 ld_do4(const void *p, size_t i, int bf) {
 template <int D, int NS>
 __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdArgs a) {
   constexpr int C = kBC, NKD = D / 32, NMT = D / 16, MP = D + 8, SP = D + 4, RT = NMT / 4;
-  __shared__ __align__(16) uint16_t mp[D * MP];  // one plane of M, row-major
-  __shared__ __align__(16) float qs[C * SP];     // Q' [t][i]
-  __shared__ __align__(16) float ds[C * SP];     // dO [t][j]
+  static_assert(D * MP * 2 <= 2 * C * SP * 4, "an M plane fits in the Q' / dO space");
+  // first one plane of M at a time, row-major (bf16); then Q' [t][i] and dO [t][j]
+  __shared__ __align__(16) float lds[2 * C * SP];
+  uint16_t *mp = reinterpret_cast<uint16_t *>(lds);
+  float *qs = lds, *ds = lds + C * SP;
   const size_t slot = blockIdx.x;
   const size_t bh = slot / a.NC;
   const int c = (int)(slot % a.NC);
