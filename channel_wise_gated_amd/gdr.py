@@ -331,16 +331,23 @@ def gdr_gate_proj(x, w_down, w_up, bias, ranks, H, d, *, out_dtype=torch.bfloat1
     return outs
 
 
+BWD_OUTPUTS = ("dq", "dk", "dv", "dlog_alpha", "db", "dw", "dgamma", "dz", "dS0")
+
+
 def gdr_chunk_bwd(q, k, v, log_alpha, b, w, dO, gamma=None, z=None, S0=None, dS_T=None, *,
-                  normalize_qk=True, scale=1.0, workspace=None, stream=None) -> dict:
+                  normalize_qk=True, scale=1.0, workspace=None, stream=None, outputs=BWD_OUTPUTS) -> dict:
     """Backward of gdr_chunk_fwd; see gdr_chunk_bwd in gdr.h.
 
     Arguments as gdr_chunk_fwd, plus dO [B,H,T,dv] (its dtype is the
     descriptor's out_dtype) and dS_T [B,H,dk,dv] fp32 or None.  Returns a dict
     of fp32 gradients: dq, dk, dv, dS0; dlog_alpha, db, dw shaped as their
     gate (None for a constant gate); dgamma [H,dk] (None without gamma); dz
-    (None without z).
+    (None without z).  Gradients not named in `outputs` are passed as NULL
+    (not computed into memory) and returned as None.
     """
+    unknown = set(outputs) - set(BWD_OUTPUTS)
+    if unknown:
+        raise ValueError(f"unknown outputs {sorted(unknown)}")
     lib = load()
     q, k, v, z, gamma, S0, dO, dS_T = map(_contig, (q, k, v, z, gamma, S0, dO, dS_T))
     B, H, T, dk = q.shape
@@ -373,6 +380,9 @@ def gdr_chunk_bwd(q, k, v, log_alpha, b, w, dO, gamma=None, z=None, S0=None, dS_
         out[name] = torch.empty(*shp, **f32) if shp else None
     out["dgamma"] = torch.empty(H, dk, **f32) if gamma is not None else None
     out["dz"] = torch.empty(B, H, T, dk, **f32) if z is not None else None
+    for name in BWD_OUTPUTS:
+        if name not in outputs:
+            out[name] = None
     rc = lib.gdr_chunk_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(la), _ptr(bt), _ptr(wt),
                            _ptr(gamma), _ptr(z), _ptr(S0), _ptr(dO), _ptr(dS_T), _ptr(out["dq"]),
                            _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dlog_alpha"]), _ptr(out["db"]),

@@ -869,6 +869,26 @@ def test_backward_options_and_edges():
     bwd_compare({**x, "b": 0.0}, "no erase")
 
 
+def test_backward_outputs_left_out_are_not_written_and_change_nothing():
+    """Null gradient pointers: the rest is bit-identical to the full call."""
+    wl = WORKLOADS["gdn2"].with_sizes(B=1, H=2, T=150)
+    d = dev(make_inputs(wl))
+    r = np.random.default_rng(9)
+    dO = torch.from_numpy(r.standard_normal((1, 2, 150, 128))).float().to(DEV)
+    dST = torch.from_numpy(0.1 * r.standard_normal((1, 2, 128, 128))).float().to(DEV)
+    args = (d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], dO)
+    kw = dict(gamma=d["gamma"], z=d["z"], S0=d["S0"], dS_T=dST)
+    full = gdr.gdr_chunk_bwd(*args, **kw)
+    for keep in (("dq", "dS0"), ("dlog_alpha", "dgamma"), ("dk", "dv", "db", "dw", "dz"), ()):
+        part = gdr.gdr_chunk_bwd(*args, **kw, outputs=keep)
+        torch.cuda.synchronize()
+        for name in gdr.BWD_OUTPUTS:
+            if name in keep:
+                assert torch.equal(part[name], full[name]), (keep, name)
+            else:
+                assert part[name] is None
+
+
 def test_backward_extreme_and_steep_decays():
     """log alpha = -30 at single tokens and over runs wider than a 16-token
     block (the pair-by-pair path of the Gram kernels), and a block whose decay
