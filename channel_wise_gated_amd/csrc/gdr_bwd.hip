@@ -19,9 +19,14 @@
 // with M and Q' from the forward's intra-chunk kernel; it runs in the forward
 // chain kernel, with M^T and Q'^T dO in its M and N slots.
 //
-// This first version computes every per-chunk quantity in fp32 on the vector
-// ALU with exact pairwise decays (no pivots), one kernel per stage, with the
-// stages' results in per-chunk scratch of the workspace.
+// Order of a call (gdr_chunk_bwd): the forward's intra-chunk kernel
+// recomputes the chunk maps; the prep kernel forms M^T and Q'^T dO; the forward
+// chain (chunk-start states) and the reverse chain (X) run side by side in one
+// launch; then per chunk the pre-pass, the Gram kernel (A, T^-1), the dense
+// products and the Gram backprop with the chains to the inputs; last dgamma.
+// Everything is fp32 (products on the fp32 matrix cores, v_mfma_f32_16x16x4);
+// the stages hand over through per-chunk scratch of the workspace.  Pair decays
+// are split at per-block pivots, with a pair-by-pair path for steep blocks.
 #include <stdint.h>
 
 #include "gdr_device.h"
@@ -34,7 +39,7 @@ namespace {
 constexpr int kBC = 64;  // chunk size of the backward
 
 // ---------------------------------------------------------------------------
-// K1 prep: per chunk slot, M^T (plane by plane, in M's A-fragment layout) and
+// Prep: per chunk slot, M^T (plane by plane, in M's A-fragment layout) and
 // G = Q'^T dO (in N's accumulator-tile layout) for the reverse chain.  Each M
 // plane goes through LDS row-major (16-byte fragment reads and writes on both
 // sides); G is computed on the fp32 matrix cores from Q' and dO in LDS, wave w
@@ -140,7 +145,7 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// K3 pre-pass: per chunk slot, the forward's per-token vectors kn, k_hat,
+// Pre-pass: per chunk slot, the forward's per-token vectors kn, k_hat,
 // q_tilde, v_hat and the cumulative log-decay Lambda.  Wave w takes tokens
 // 16w..16w+15, lane CPL = D / 64 consecutive channels; Lambda is summed along
 // the wave's tokens in registers, then offset by the earlier waves' totals.
@@ -260,7 +265,7 @@ __global__ void __launch_bounds__(256) bwd_prepass_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// K4 Gram: per chunk slot, A (s <= t) and L (s < t), A_ts = sum_i q_tilde_ti
+// Gram: per chunk slot, A (s <= t) and L (s < t), A_ts = sum_i q_tilde_ti
 // kn_si e^{Lambda_ti - Lambda_si} and L_ts likewise with k_hat, on the fp32
 // matrix cores by 16 x 16 tiles: the pair decay is split at a per-channel pivot
 // P, e^{Lambda_t - P} on the t side and e^{P - Lambda_s} on the s side.  For a
@@ -366,7 +371,7 @@ __global__ void __launch_bounds__(256) bwd_gram_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// K5: per chunk slot, the dense products of the chunk system's reverse, on the
+// Dense products: per chunk slot, the products of the chunk system's reverse, on the
 // fp32 matrix cores (v_mfma_f32_16x16x4_f32):
 //   R   = V_hat - K_a S0       U  = T^-1 R            dQ_a = dO S0^T
 //   dA  = dO U^T (s <= t)      Z  = A^T dO + K' X     dK'  = U X^T
@@ -640,7 +645,7 @@ __device__ __forceinline__ void stn(float *p, const float (&x)[N]) {
 }
 
 // ---------------------------------------------------------------------------
-// K8 Gram backprop: per chunk slot, on the fp32 matrix cores.  With the pair
+// Gram backprop: per chunk slot, on the fp32 matrix cores.  With the pair
 // decay p_ts = e^{Lambda_t - Lambda_s} (per channel), s <= t:
 //   rows    RA_t = sum_s dA_ts kn_s p_ts,   RL_t = sum_s dL_ts kn_s p_ts
 //   columns CS_s = sum_t (dA_ts q_tilde_t + dL_ts k_hat_t) p_ts
@@ -931,7 +936,7 @@ __global__ void __launch_bounds__(256) bwd_gramback_kernel(BwdArgs a) {
   }
 }
 
-// K10: dgamma[h][c] = sum over the batch and the chunks of the partial sums;
+// dgamma[h][c] = sum over the batch and the chunks of the partial sums;
 // one workgroup per (head, 32 channels), 8 threads per channel.
 template <int D>
 __global__ void __launch_bounds__(256) bwd_dgamma_kernel(BwdArgs a) {
