@@ -216,8 +216,12 @@ def timed_bwd(x, steps, warmup):
         e[1].record()
     torch.cuda.synchronize()
     ms = sorted(e[0].elapsed_time(e[1]) for e in ev)[steps // 2]
+    # algorithmic HBM bytes: bf16 q, k, v, b, w, z and fp32 log-decay, dO in;
+    # seven fp32 gradients out (dS0 and dgamma are negligible)
+    byt = B * H * T * (6 * 2 * dk + 4 * dk + 4 * dv + 7 * 4 * dk)
     return {"workload": f"bwd B{B} H{H} T{T} dk{dk} dv{dv} chunk64, grads of q,k,v,log-decay,b,w,z,gain,S0",
-            "steps": steps, "ms_per_step": round(ms, 4), "tokens_s": round(B * T / (ms / 1e3), 1)}
+            "steps": steps, "ms_per_step": round(ms, 4), "tokens_s": round(B * T / (ms / 1e3), 1),
+            "bytes_algorithmic": byt, "hbm_gbs_algorithmic": round(byt / (ms / 1e3) / 1e9, 1)}
 
 
 def copy_calibration(mib):
