@@ -282,9 +282,9 @@ def main():
                     help="also run a plain MIB-MiB copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} requested, but this build runs on exactly one GPU "
-              "(the recurrence shards over (batch, head) streams with no communication; no "
-              "multi-GPU path is built). Run with --gpus 1.", file=sys.stderr)
+        print(f"bench.py: --gpus {args.gpus} requested, but this benchmark runs on exactly one GPU "
+              "(the recurrence shards over (batch, head) streams with no communication; the "
+              "library has no multi-GPU path). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -20,8 +20,8 @@ def oracle_mod():
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests are skipped, loudly, when no GPU is present; on a GPU machine a
-    # missing HIP library is an error raised by the binding itself.
+    # GPU tests are skipped, loudly, when no GPU is present; on a machine with
+    # a GPU a missing HIP library is an error raised by the binding itself.
     try:
         import torch
         has_gpu = torch.cuda.is_available()
