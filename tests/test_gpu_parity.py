@@ -948,3 +948,40 @@ def test_backward_full_size_sampled():
                 continue
             got = g[key][h:h + 1] if key == "dgamma" else g[key][:, h:h + 1]
             check(f"bwd full T{wl.T} head {h} {key}", got.cpu().numpy(), ref[key], TOL_BF16)
+
+
+@pytest.mark.timeout(900)
+def test_long_sequences_forward_and_backward():
+    """One sequence of half a million tokens (B1 H2 T524288, chunk 128): the
+    whole forward on the GPU, one head's outputs and final state through the
+    oracle; then the backward at T131072 the same way (64-bit offsets, chains
+    of 4096 and 2048 chunks)."""
+    wl = WORKLOADS["stress"].with_sizes(H=2, T=1 << 19)
+    print(f"long forward T{wl.T}", flush=True)
+    xd = make_inputs_device(wl, DEV, seed=31)
+    o, sT = gdr.gdr_chunk_fwd(xd["q"], xd["k"], xd["v"], xd["log_alpha"], xd["b"], xd["w"],
+                              gamma=xd["gamma"], z=xd["z"], S0=xd["S0"], chunk=128)
+    torch.cuda.synchronize()
+    h = 1
+    xs = {k: (None if v is None else (v[h:h + 1].cpu() if k == "gamma" else v[:, h:h + 1].cpu()))
+          for k, v in xd.items()}
+    ro, rs = oracle_run(xs)
+    check(f"long T{wl.T} o", o[:, h:h + 1].cpu().numpy(), ro, TOL_BF16)
+    check(f"long T{wl.T} S_T", sT[:, h:h + 1].cpu().numpy(), rs, TOL_BF16)
+    del o, sT, xd, xs, ro, rs
+    torch.cuda.empty_cache()
+    wb = WORKLOADS["stress"].with_sizes(H=2, T=1 << 17)
+    print(f"long backward T{wb.T}", flush=True)
+    xd = make_inputs_device(wb, DEV, seed=37)
+    gen = torch.Generator(device=DEV).manual_seed(41)
+    dO = torch.randn(1, 2, wb.T, wb.dv, device=DEV, generator=gen)
+    g = gdr.gdr_chunk_bwd(xd["q"], xd["k"], xd["v"], xd["log_alpha"], xd["b"], xd["w"], dO,
+                          gamma=xd["gamma"], z=xd["z"], S0=xd["S0"])
+    torch.cuda.synchronize()
+    xs = {k: (None if v is None else (v[h:h + 1].cpu() if k == "gamma" else v[:, h:h + 1].cpu()))
+          for k, v in xd.items()}
+    ref = oracle.backward(xs["q"], xs["k"], xs["v"], xs["log_alpha"], xs["b"], xs["w"], dO[:, h:h + 1].cpu(),
+                          gamma=xs["gamma"], z=xs["z"], S0=xs["S0"])
+    for key in ("dq", "dk", "dv", "dlog_alpha", "db", "dw", "dz", "dS0", "dgamma"):
+        got = g[key][h:h + 1] if key == "dgamma" else g[key][:, h:h + 1]
+        check(f"long bwd T{wb.T} {key}", got.cpu().numpy(), ref[key], TOL_BF16)
