@@ -985,3 +985,26 @@ def test_long_sequences_forward_and_backward():
     for key in ("dq", "dk", "dv", "dlog_alpha", "db", "dw", "dz", "dS0", "dgamma"):
         got = g[key][h:h + 1] if key == "dgamma" else g[key][:, h:h + 1]
         check(f"long bwd T{wb.T} {key}", got.cpu().numpy(), ref[key], TOL_BF16)
+
+
+def test_backward_nan_stays_in_its_stream():
+    """A NaN in one stream's keys poisons that stream's gradients only (and
+    dgamma of its head); the other streams' gradients equal the clean run's
+    bit for bit."""
+    wl = WORKLOADS["gdn2"].with_sizes(B=2, H=2, T=100)
+    x = make_inputs(wl)
+    r = np.random.default_rng(13)
+    dO = torch.from_numpy(r.standard_normal((2, 2, 100, 128))).float().to(DEV)
+    d = dev(x)
+    run = lambda k: gdr.gdr_chunk_bwd(d["q"], k, d["v"], d["log_alpha"], d["b"], d["w"], dO,
+                                      gamma=d["gamma"], z=d["z"], S0=d["S0"])
+    clean = run(d["k"])
+    kbad = d["k"].clone()
+    kbad[1, 0, 37, 5] = float("nan")
+    bad = run(kbad)
+    torch.cuda.synchronize()
+    for key in ("dq", "dk", "dv", "dlog_alpha", "db", "dw", "dz", "dS0"):
+        assert not bool(torch.isfinite(bad[key][1, 0]).all()), key
+        for bi, hi in ((0, 0), (0, 1), (1, 1)):
+            assert torch.equal(bad[key][bi, hi], clean[key][bi, hi]), (key, bi, hi)
+    assert torch.equal(bad["dgamma"][1], clean["dgamma"][1])
