@@ -150,42 +150,32 @@ gdr_status gate_plan(const gdr_gate_desc *d, size_t *ws, int *R) {
 // The backward: validation as the forward (its chunk size is its own, 64) and
 // the workspace (the forward's chunk maps, the reverse chain's buffers and
 // per-chunk scratch).
-gdr_status bwd_plan(const gdr_desc *d, size_t *ws) {
+gdr_status bwd_plan(const gdr_desc *d, int nseq, size_t *ws) {
   if (!d) return GDR_ERR_INVALID_ARG;
   gdr_desc fd = *d;
   fd.chunk = 64;
   size_t fws = 0;
-  gdr_status s = chunk_plan(&fd, 0, &fws);
+  gdr_status s = chunk_plan(&fd, nseq, &fws);  // also: nseq > 0 needs B = 1
   if (s != GDR_OK) return s;
   const int ns = d->in_dtype == GDR_BF16 ? 2 : 3;
-  const long long nch = (long long)d->B * d->H * ((d->T + 63) / 64);
+  const long long nch = nseq > 0 ? (long long)d->H * ((d->T + 63) / 64 + nseq)
+                                 : (long long)d->B * d->H * ((d->T + 63) / 64);
   if (nch > (1LL << 31) - 1) return GDR_ERR_INVALID_ARG;
-  *ws = nch == 0 ? 0 : gdr::bwd_workspace(nullptr, nullptr, nullptr, d->B, d->H, d->T, d->dk, ns);
+  *ws = nch == 0 ? 0 : gdr::bwd_workspace(nullptr, nullptr, nullptr, d->B, d->H, d->T, d->dk, ns, nseq);
   return GDR_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-gdr_status gdr_chunk_bwd_workspace_size(const gdr_desc *desc, size_t *bytes) {
-  if (!bytes) return GDR_ERR_INVALID_ARG;
-  size_t ws = 0;
-  gdr_status s = bwd_plan(desc, &ws);
-  if (s == GDR_OK) *bytes = ws;
-  return s;
-}
-
-gdr_status gdr_chunk_bwd(const gdr_desc *desc, const void *q, const void *k, const void *v,
-                         const float *log_alpha, const void *b, const void *w, const float *gamma,
-                         const void *z, const float *S0, const void *dO, const float *dS_T, float *dq,
-                         float *dk, float *dv, float *dlog_alpha, float *db, float *dw, float *dgamma,
-                         float *dz, float *dS0, void *workspace, size_t workspace_bytes, void *stream) {
+gdr_status bwd_call(const gdr_desc *desc, int nseq, const int *cu, const void *q, const void *k,
+                    const void *v, const float *log_alpha, const void *b, const void *w, const float *gamma,
+                    const void *z, const float *S0, const void *dO, const float *dS_T, float *dq, float *dk,
+                    float *dv, float *dlog_alpha, float *db, float *dw, float *dgamma, float *dz, float *dS0,
+                    void *workspace, size_t workspace_bytes, void *stream) {
   size_t need = 0;
-  gdr_status s = bwd_plan(desc, &need);
+  gdr_status s = bwd_plan(desc, nseq, &need);
   if (s != GDR_OK) return s;
   const gdr_desc &d = *desc;
   if ((long long)d.B * d.H == 0) return GDR_OK;
+  if (nseq > 0 && (!cu || (reinterpret_cast<uintptr_t>(cu) & 3u))) return GDR_ERR_INVALID_ARG;
   if (d.T > 0) {
     s = check_inputs(desc, q, k, v, log_alpha, b, w, gamma, z, q);
     if (s != GDR_OK) return s;
@@ -206,10 +196,11 @@ gdr_status gdr_chunk_bwd(const gdr_desc *desc, const void *q, const void *k, con
   f.log_alpha = log_alpha; f.gamma = gamma; f.S0 = S0;
   f.o = nullptr; f.S_T = nullptr;
   f.Qp = f.Mm = f.Sc = nullptr; f.Ob = f.Nn = f.Sst = nullptr;
-  f.B = d.B; f.H = d.H; f.T = d.T;
+  f.B = nseq > 0 ? nseq : d.B;  // chains: one per (sequence, head)
+  f.H = d.H; f.T = d.T;
   f.alpha_mode = d.alpha_mode; f.b_mode = d.b_mode; f.w_mode = d.w_mode;
   f.normalize_qk = d.normalize_qk; f.scale = d.scale;
-  f.cu = nullptr; f.coff = nullptr; f.ctab = nullptr; f.nseq = 0; f.ctab_len = 0;
+  f.cu = nseq > 0 ? cu : nullptr; f.coff = nullptr; f.ctab = nullptr; f.nseq = nseq; f.ctab_len = 0;
   f.c0 = 0; f.ncs = 0; f.rev = 0;
   f.og = nullptr; f.onw = nullptr; f.oeps = 0.f; f.y = nullptr;
   gdr::BwdArgs a;
@@ -221,21 +212,26 @@ gdr_status gdr_chunk_bwd(const gdr_desc *desc, const void *q, const void *k, con
   a.dq = dq; a.dk = dk; a.dv = dv; a.dla = dlog_alpha; a.db = db; a.dw = dw;
   a.dz = z ? dz : nullptr;
   a.dgamma = gamma ? dgamma : nullptr;
+  a.ctab = nullptr; a.ctab_len = 0;
+  // chunk slots: the token chunks of a uniform batch, or the (bounded) chunk
+  // list of a packed one
+  const bool chunks = nseq > 0 || a.NC > 0;
   hipError_t e = hipSuccess;
-  if (a.NC > 0) gdr::bwd_workspace(&a, &f, workspace, d.B, d.H, d.T, d.dk, ns);
+  if (chunks) gdr::bwd_workspace(&a, &f, workspace, d.B, d.H, d.T, d.dk, ns, nseq);
   // the chain of chunk-end state gradients, last chunk to first (the final
   // one is dS0): the forward's chain kernel with M^T and Q'^T dO
   gdr::ChunkArgs r = f;
-  r.Mm = a.NC > 0 ? a.Mt : nullptr;
-  r.Nn = a.NC > 0 ? a.Gn : nullptr;
-  r.Sc = a.NC > 0 ? a.Xc : nullptr;
+  r.Mm = chunks ? a.Mt : nullptr;
+  r.Nn = chunks ? a.Gn : nullptr;
+  r.Sc = chunks ? a.Xc : nullptr;
   r.S0 = dS_T;
   r.S_T = dS0;
   r.rev = 1;
-  if (a.NC > 0) {
+  if (chunks) {
     a.Qp = f.Qp; a.Mm = f.Mm; a.Sc = f.Sc;
-    // forward recompute: the chunk maps, then M^T and Q'^T dO; then the
-    // forward chain (chunk-start states) and the reverse chain side by side
+    // forward recompute: the chunk maps (a packed batch's chunk list first),
+    // then M^T and Q'^T dO; then the forward chain (chunk-start states) and
+    // the reverse chain side by side
     e = gdr::launch_chunk(fd, f, 1, st);
     if (e == hipSuccess) e = gdr::launch_bwd_prep(a, d.dk, ns, st);
     f.c0 = r.c0 = 0;
@@ -244,9 +240,48 @@ gdr_status gdr_chunk_bwd(const gdr_desc *desc, const void *q, const void *k, con
   } else if (dS0) {
     e = gdr::launch_chunk(fd, r, 4, st);
   }
-  if (e == hipSuccess && a.NC > 0) e = gdr::launch_bwd(a, d.dk, ns, st);
-  else if (e == hipSuccess && a.dgamma) e = gdr::launch_bwd(a, d.dk, ns, st);
+  if (e == hipSuccess && (chunks || a.dgamma)) e = gdr::launch_bwd(a, d.dk, ns, st);
   return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdr_status gdr_chunk_bwd_workspace_size(const gdr_desc *desc, size_t *bytes) {
+  if (!bytes) return GDR_ERR_INVALID_ARG;
+  size_t ws = 0;
+  gdr_status s = bwd_plan(desc, 0, &ws);
+  if (s == GDR_OK) *bytes = ws;
+  return s;
+}
+
+gdr_status gdr_chunk_bwd(const gdr_desc *desc, const void *q, const void *k, const void *v,
+                         const float *log_alpha, const void *b, const void *w, const float *gamma,
+                         const void *z, const float *S0, const void *dO, const float *dS_T, float *dq,
+                         float *dk, float *dv, float *dlog_alpha, float *db, float *dw, float *dgamma,
+                         float *dz, float *dS0, void *workspace, size_t workspace_bytes, void *stream) {
+  return bwd_call(desc, 0, nullptr, q, k, v, log_alpha, b, w, gamma, z, S0, dO, dS_T, dq, dk, dv, dlog_alpha,
+                  db, dw, dgamma, dz, dS0, workspace, workspace_bytes, stream);
+}
+
+gdr_status gdr_chunk_bwd_varlen_workspace_size(const gdr_desc *desc, int n_seqs, size_t *bytes) {
+  if (!bytes || n_seqs < 1) return GDR_ERR_INVALID_ARG;
+  size_t ws = 0;
+  gdr_status s = bwd_plan(desc, n_seqs, &ws);
+  if (s == GDR_OK) *bytes = ws;
+  return s;
+}
+
+gdr_status gdr_chunk_bwd_varlen(const gdr_desc *desc, int n_seqs, const int *cu_seqlens, const void *q,
+                                const void *k, const void *v, const float *log_alpha, const void *b,
+                                const void *w, const float *gamma, const void *z, const float *S0,
+                                const void *dO, const float *dS_T, float *dq, float *dk, float *dv,
+                                float *dlog_alpha, float *db, float *dw, float *dgamma, float *dz,
+                                float *dS0, void *workspace, size_t workspace_bytes, void *stream) {
+  if (n_seqs < 1) return GDR_ERR_INVALID_ARG;
+  return bwd_call(desc, n_seqs, cu_seqlens, q, k, v, log_alpha, b, w, gamma, z, S0, dO, dS_T, dq, dk, dv,
+                  dlog_alpha, db, dw, dgamma, dz, dS0, workspace, workspace_bytes, stream);
 }
 
 gdr_status gdr_gate_proj_workspace_size(const gdr_gate_desc *desc, size_t *bytes) {

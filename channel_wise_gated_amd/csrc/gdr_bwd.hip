@@ -38,6 +38,32 @@ namespace {
 
 constexpr int kBC = 64;  // chunk size of the backward
 
+// Where a chunk slot's tokens are: the token row (of the [B,H,T] or packed
+// [1,H,T] tensors) of its first token, how many of its 64 tokens are real and
+// its head.  Uniform batches: slot = stream * NC + chunk.  Packed batches:
+// slot = entry * H + head over the chunk list (entries past the end hold no
+// tokens).
+struct SlotTokens {
+  size_t row;
+  int valid, head;
+};
+__device__ __forceinline__ SlotTokens slot_tokens(const BwdArgs &a, size_t slot) {
+  SlotTokens s;
+  if (a.ctab) {
+    const int4 e = a.ctab[slot / a.H];
+    s.head = (int)(slot % a.H);
+    s.valid = e.x < 0 ? 0 : e.w;
+    s.row = (size_t)s.head * a.T + (e.x < 0 ? 0 : e.z);
+  } else {
+    const size_t bh = slot / a.NC;
+    const int c = (int)(slot % a.NC);
+    s.head = (int)(bh % a.H);
+    s.valid = min(kBC, a.T - c * kBC);
+    s.row = bh * a.T + (size_t)c * kBC;
+  }
+  return s;
+}
+
 // ---------------------------------------------------------------------------
 // Prep: per chunk slot, M^T (plane by plane, in M's A-fragment layout) and
 // G = Q'^T dO (in N's accumulator-tile layout) for the reverse chain.  Each M
@@ -69,8 +95,7 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdArgs a) {
   uint16_t *mp = reinterpret_cast<uint16_t *>(lds);
   float *qs = lds, *ds = lds + C * SP;
   const size_t slot = blockIdx.x;
-  const size_t bh = slot / a.NC;
-  const int c = (int)(slot % a.NC);
+  const SlotTokens st = slot_tokens(a, slot);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, g = lane >> 4;
   // A-fragment entry (f, lane) of a D x D plane: 8 values of row 16 (f / NKD) + l16,
   // columns 32 (f % NKD) + 4 g + {0..3} and + 16
@@ -111,9 +136,9 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdArgs a) {
     *reinterpret_cast<float4 *>(qs + t * SP + col + 16) = float4{v[4], v[5], v[6], v[7]};
   }
   for (int idx = tid; idx < C * D / 4; idx += 256) {
-    const int t = idx / (D / 4), j4 = idx % (D / 4), tt = c * C + t;
+    const int t = idx / (D / 4), j4 = idx % (D / 4);
     *reinterpret_cast<f32x4 *>(ds + t * SP + 4 * j4) =
-        tt < a.T ? ld_do4(a.dO, (bh * a.T + tt) * D + 4 * j4, a.do_bf16) : zero4();
+        t < st.valid ? ld_do4(a.dO, (st.row + t) * D + 4 * j4, a.do_bf16) : zero4();
   }
   __syncthreads();
   // G[i][j] = sum_t Q'[t][i] dO[t][j]: lane (l16, g) supplies k = t = 16 kb + 4 g + e
@@ -183,8 +208,8 @@ __global__ void __launch_bounds__(256) bwd_prepass_kernel(BwdArgs a) {
   constexpr int C = kBC, CPL = D / 64, TW = C / 4;
   __shared__ float tot[4][D];
   const size_t slot = blockIdx.x;
-  const size_t bh = slot / a.NC;
-  const int c = (int)(slot % a.NC), h = (int)(bh % a.H);
+  const SlotTokens st = slot_tokens(a, slot);
+  const int h = st.head;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, ch0 = CPL * lane;
   const size_t base = slot * (size_t)C * D;
   float gam[CPL], run[CPL], lam[TW][CPL];
@@ -195,9 +220,9 @@ __global__ void __launch_bounds__(256) bwd_prepass_kernel(BwdArgs a) {
   }
 #pragma unroll
   for (int j = 0; j < TW; ++j) {
-    const int t = TW * w + j, tt = c * C + t;
-    const bool ok = tt < a.T;  // uniform over the wave
-    const size_t row = bh * a.T + (ok ? tt : 0);
+    const int t = TW * w + j;
+    const bool ok = t < st.valid;  // uniform over the wave
+    const size_t row = st.row + (ok ? t : 0);
     float qv[CPL], kv[CPL], vv[CPL], zv[CPL], bg[CPL], wg[CPL], la[CPL];
     float sq = 0.f, sk = 0.f;
     if (ok) {
@@ -434,8 +459,7 @@ __global__ void __launch_bounds__(256) bwd_mm_kernel(BwdArgs a) {
   __shared__ float xs[D];                       // row dots of X and S0
   float *bt = bb, *bu = bb + C * SP;
   const size_t slot = blockIdx.x;
-  const size_t bh = slot / a.NC;
-  const int c = (int)(slot % a.NC);
+  const SlotTokens st = slot_tokens(a, slot);
   const size_t base = slot * (size_t)C * D, cbase = slot * (size_t)C * C;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, g = lane >> 4;
   const int ar = 16 * w + l16;  // the A-operand row this lane supplies
@@ -506,14 +530,14 @@ __global__ void __launch_bounds__(256) bwd_mm_kernel(BwdArgs a) {
   bf16x8 pa[NE][NS], pb[NE][NS];  // planes: S0 now; then X (pa) and S0 (pb) for phase 3
   load_planes(S0p, pa);
   store_planes(ss, pa, pa, false);
-  const int tt = c * C + ar;
-  const size_t orow = (bh * a.T + (tt < a.T ? tt : 0)) * D;
+  const bool arow = ar < st.valid;
+  const size_t orow = (st.row + (arow ? ar : 0)) * D;
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
     const size_t o = base + (size_t)ar * D + 16 * kb + 4 * g;
     const float4 kh = *reinterpret_cast<const float4 *>(a.KH + o), la = *reinterpret_cast<const float4 *>(a.LAM + o);
     af[kb] = f32x4{kh.x * __expf(la.x), kh.y * __expf(la.y), kh.z * __expf(la.z), kh.w * __expf(la.w)};
-    dof[kb] = tt < a.T ? ld_do4(a.dO, orow + 16 * kb + 4 * g, a.do_bf16) : zero4();
+    dof[kb] = arow ? ld_do4(a.dO, orow + 16 * kb + 4 * g, a.do_bf16) : zero4();
   }
   float vh[NCT][4];
 #pragma unroll
@@ -548,9 +572,9 @@ __global__ void __launch_bounds__(256) bwd_mm_kernel(BwdArgs a) {
   // (3) X phase: dA = dO U^T, Z = A^T dO + K' X, dK' = U X^T
   store_planes(ss, pa, pb, true);
   for (int idx = tid; idx < C * D / 4; idx += 256) {
-    const int t = idx / (D / 4), j4 = idx % (D / 4), t2 = c * C + t;
+    const int t = idx / (D / 4), j4 = idx % (D / 4);
     *reinterpret_cast<f32x4 *>(bt + t * SP + 4 * j4) =
-        t2 < a.T ? ld_do4(a.dO, (bh * a.T + t2) * D + 4 * j4, a.do_bf16) : zero4();
+        t < st.valid ? ld_do4(a.dO, (st.row + t) * D + 4 * j4, a.do_bf16) : zero4();
   }
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
@@ -674,8 +698,8 @@ __global__ void __launch_bounds__(256) bwd_gramback_kernel(BwdArgs a) {
   __shared__ __align__(16) float stg[4][C * SPD];
   float *dl = stg[IKN], *sk = stg[ILA], *gp = stg[ILA] + 16 * D;
   const size_t slot = blockIdx.x;
-  const size_t bh = slot / a.NC;
-  const int c = (int)(slot % a.NC), hd = (int)(bh % a.H);
+  const SlotTokens st = slot_tokens(a, slot);
+  const int hd = st.head;
   const size_t base = slot * (size_t)C * D, cbase = slot * (size_t)C * C;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, g = lane >> 4;
   const int c0 = NCT * l16;  // first channel of this lane
@@ -806,9 +830,8 @@ __global__ void __launch_bounds__(256) bwd_gramback_kernel(BwdArgs a) {
     }
     // the chains back to the inputs (q, k through SiLU and l2, the gain,
     // the gates); reductions over a token's channels stay in its 16 lanes
-    const int tt = c * C + t;
-    const bool live = tt < a.T;
-    const size_t grow = bh * a.T + (live ? tt : 0);
+    const bool live = t < st.valid;
+    const size_t grow = st.row + (live ? t : 0);
     float qx[NCT], kx[NCT], vx[NCT], zx[NCT], bg[NCT], wg[NCT], du[NCT];
     ldn<BF, NCT>(a.q, grow * D + c0, qx);
     ldn<BF, NCT>(a.k, grow * D + c0, kx);
@@ -922,7 +945,7 @@ __global__ void __launch_bounds__(256) bwd_gramback_kernel(BwdArgs a) {
     for (int t = C - 1; t >= 0; --t) {
       run += dl[t * SPD + ch];
       dl[t * SPD + ch] = run;
-      if (per_ch && c * C + t < a.T) a.dla[(bh * a.T + c * C + t) * D + ch] = run;
+      if (per_ch && t < st.valid) a.dla[(st.row + t) * D + ch] = run;
     }
   }
   if (a.dla && a.alpha_mode == GDR_GATE_PER_TOKEN) {
@@ -932,7 +955,7 @@ __global__ void __launch_bounds__(256) bwd_gramback_kernel(BwdArgs a) {
     for (int j = 0; j < D / 4; ++j) sv += dl[t * SPD + qq * (D / 4) + j];
     sv += __shfl_xor(sv, 1, kWave);
     sv += __shfl_xor(sv, 2, kWave);
-    if (qq == 0 && c * C + t < a.T) a.dla[bh * a.T + c * C + t] = sv;
+    if (qq == 0 && t < st.valid) a.dla[st.row + t] = sv;
   }
 }
 
@@ -944,9 +967,13 @@ __global__ void __launch_bounds__(256) bwd_dgamma_kernel(BwdArgs a) {
   const int h = blockIdx.x / (D / 32), cl = threadIdx.x & 31, j = threadIdx.x >> 5;
   const int ch = (blockIdx.x % (D / 32)) * 32 + cl;
   float s = 0.f;
-  for (int k = j; k < a.B * a.NC; k += 8) {
-    const int b = k / a.NC, c = k % a.NC;
-    s += a.gpart[((size_t)(b * a.H + h) * a.NC + c) * D + ch];
+  if (a.ctab) {  // packed batch: slots entry * H + h (entries past the end hold zeros)
+    for (int k = j; k < a.ctab_len; k += 8) s += a.gpart[((size_t)k * a.H + h) * D + ch];
+  } else {
+    for (int k = j; k < a.B * a.NC; k += 8) {
+      const int b = k / a.NC, c = k % a.NC;
+      s += a.gpart[((size_t)(b * a.H + h) * a.NC + c) * D + ch];
+    }
   }
   part[j][cl] = s;
   __syncthreads();
@@ -959,7 +986,7 @@ __global__ void __launch_bounds__(256) bwd_dgamma_kernel(BwdArgs a) {
 
 template <int D, int NS, bool BF>
 hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
-  const unsigned nch = (unsigned)((size_t)a.B * a.H * a.NC);
+  const unsigned nch = (unsigned)(a.ctab ? (size_t)a.H * a.ctab_len : (size_t)a.B * a.H * a.NC);
   if (nch == 0) {  // empty sequences: only dgamma (zeros)
     if (a.dgamma && a.gamma)
       hipLaunchKernelGGL((bwd_dgamma_kernel<D>), dim3((unsigned)(a.H * (D / 32))), dim3(256), 0, st, a);
@@ -976,18 +1003,20 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
 
 template <int D, int NS>
 hipError_t launch_bwd_prep_t(const BwdArgs &a, hipStream_t st) {
-  const unsigned nch = (unsigned)((size_t)a.B * a.H * a.NC);
+  const unsigned nch = (unsigned)(a.ctab ? (size_t)a.H * a.ctab_len : (size_t)a.B * a.H * a.NC);
   hipLaunchKernelGGL((bwd_prep_kernel<D, NS>), dim3(nch), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-size_t bwd_workspace(BwdArgs *a, ChunkArgs *f, void *ws, int B, int H, int T, int D, int NS) {
+size_t bwd_workspace(BwdArgs *a, ChunkArgs *f, void *ws, int B, int H, int T, int D, int NS, int nseq) {
   const int C = kBC;
-  const size_t nch = (size_t)B * H * ((T + C - 1) / C);
+  // chunk slots: uniform B * H * NC; packed H * (chunk-list length bound)
+  const size_t nch = nseq > 0 ? (size_t)H * ((size_t)((T + C - 1) / C) + (size_t)nseq)
+                              : (size_t)B * H * ((T + C - 1) / C);
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  size_t total = al(chunk_workspace(f, ws, B, H, T, C, D, NS, 0));
+  size_t total = al(chunk_workspace(f, ws, nseq > 0 ? 1 : B, H, T, C, D, NS, nseq));
   unsigned char *base = static_cast<unsigned char *>(ws);
   auto take = [&](size_t bytes) {
     void *p = ws ? base + total : nullptr;
@@ -1004,6 +1033,8 @@ size_t bwd_workspace(BwdArgs *a, ChunkArgs *f, void *ws, int B, int H, int T, in
   float *gp = static_cast<float *>(take(nch * (size_t)D * 4));
   float *xs = static_cast<float *>(take(nch * (size_t)D * 4));
   if (a) {
+    a->ctab = (ws && f) ? f->ctab : nullptr;
+    a->ctab_len = (ws && f) ? f->ctab_len : 0;
     a->XS = xs;
     a->Mt = static_cast<uint16_t *>(mt);
     a->Xc = static_cast<uint16_t *>(xc);

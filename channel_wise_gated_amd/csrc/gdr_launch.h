@@ -59,7 +59,7 @@ struct GateArgs {
 };
 hipError_t launch_gate_proj(const GateArgs &a, int d, bool out_bf16, hipStream_t st);
 
-// Backward pass (gdr_bwd.hip): chunks of 64 tokens, uniform batches.
+// Backward pass (gdr_bwd.hip): chunks of 64 tokens, uniform or packed batches.
 struct BwdArgs {
   const void *q, *k, *v, *b, *w, *z, *dO;
   const float *log_alpha, *gamma;
@@ -73,11 +73,13 @@ struct BwdArgs {
   float *AM, *TI, *DA, *DL;      // [slot][64][64] fp32
   float *gpart;                  // [slot][D] partial sums of dgamma
   float *XS;                     // [slot][D] row dots sum_j X_ij S0_ij of each chunk's end-state gradient and start state
+  const int4 *ctab;              // packed batch: the forward's chunk list (null for uniform batches)
+  int ctab_len;
   float *dq, *dk, *dv, *dla, *db, *dw, *dz, *dgamma;  // outputs (each may be null)
 };
 // Workspace of the backward: the forward's chunk workspace (C = 64; its fields
 // set in *f) followed by the backward's regions (set in *a); returns the size.
-size_t bwd_workspace(BwdArgs *a, ChunkArgs *f, void *ws, int B, int H, int T, int D, int NS);
+size_t bwd_workspace(BwdArgs *a, ChunkArgs *f, void *ws, int B, int H, int T, int D, int NS, int nseq);
 hipError_t launch_bwd_prep(const BwdArgs &a, int D, int NS, hipStream_t st);
 hipError_t launch_bwd(const BwdArgs &a, int D, int NS, hipStream_t st);
 

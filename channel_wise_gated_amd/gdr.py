@@ -31,7 +31,8 @@ GDR_OK, GDR_ERR_INVALID_ARG, GDR_ERR_UNSUPPORTED, GDR_ERR_WORKSPACE, GDR_ERR_HIP
 GDR_BF16, GDR_F32 = 0, 1
 PER_CHANNEL, PER_TOKEN, ONES, ZEROS = 0, 1, 2, 3
 SYMBOLS = ("gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_chunk_fwd_gated", "gdr_chunk_fwd_intra",
-           "gdr_chunk_bwd_workspace_size", "gdr_chunk_bwd",
+           "gdr_chunk_bwd_workspace_size", "gdr_chunk_bwd", "gdr_chunk_bwd_varlen_workspace_size",
+           "gdr_chunk_bwd_varlen",
            "gdr_chunk_fwd_scan", "gdr_chunk_fwd_varlen_workspace_size", "gdr_chunk_fwd_varlen",
            "gdr_decode_step", "gdr_status_string", "gdr_version", "gdr_gate_proj_workspace_size",
            "gdr_gate_proj")
@@ -100,6 +101,10 @@ def load() -> ctypes.CDLL:
     lib.gdr_chunk_bwd_workspace_size.argtypes = [dp, ctypes.POINTER(sz)]
     lib.gdr_chunk_bwd.restype = ctypes.c_int
     lib.gdr_chunk_bwd.argtypes = [dp] + [vp] * 21 + [sz, vp]
+    lib.gdr_chunk_bwd_varlen_workspace_size.restype = ctypes.c_int
+    lib.gdr_chunk_bwd_varlen_workspace_size.argtypes = [dp, ctypes.c_int, ctypes.POINTER(sz)]
+    lib.gdr_chunk_bwd_varlen.restype = ctypes.c_int
+    lib.gdr_chunk_bwd_varlen.argtypes = [dp, ctypes.c_int, vp] + [vp] * 21 + [sz, vp]
     lib.gdr_status_string.restype = ctypes.c_char_p
     lib.gdr_status_string.argtypes = [ctypes.c_int]
     lib.gdr_version.restype = ctypes.c_int
@@ -335,7 +340,8 @@ BWD_OUTPUTS = ("dq", "dk", "dv", "dlog_alpha", "db", "dw", "dgamma", "dz", "dS0"
 
 
 def gdr_chunk_bwd(q, k, v, log_alpha, b, w, dO, gamma=None, z=None, S0=None, dS_T=None, *,
-                  normalize_qk=True, scale=1.0, workspace=None, stream=None, outputs=BWD_OUTPUTS) -> dict:
+                  normalize_qk=True, scale=1.0, workspace=None, stream=None, outputs=BWD_OUTPUTS,
+                  cu_seqlens=None) -> dict:
     """Backward of gdr_chunk_fwd; see gdr_chunk_bwd in gdr.h.
 
     Arguments as gdr_chunk_fwd, plus dO [B,H,T,dv] (its dtype is the
@@ -343,7 +349,9 @@ def gdr_chunk_bwd(q, k, v, log_alpha, b, w, dO, gamma=None, z=None, S0=None, dS_
     of fp32 gradients: dq, dk, dv, dS0; dlog_alpha, db, dw shaped as their
     gate (None for a constant gate); dgamma [H,dk] (None without gamma); dz
     (None without z).  Gradients not named in `outputs` are passed as NULL
-    (not computed into memory) and returned as None.
+    (not computed into memory) and returned as None.  With `cu_seqlens` (device
+    int32 [N+1]) the tensors are a packed batch as in gdr_chunk_fwd_varlen
+    (gdr_chunk_bwd_varlen): B = 1, S0 / dS_T / dS0 are [N,H,dk,dv].
     """
     unknown = set(outputs) - set(BWD_OUTPUTS)
     if unknown:
@@ -365,7 +373,14 @@ def gdr_chunk_bwd(q, k, v, log_alpha, b, w, dO, gamma=None, z=None, S0=None, dS_
     od = GDR_BF16 if dO.dtype == torch.bfloat16 else GDR_F32
     desc = make_desc(B, H, T, dk, dv, 64, _dtype_code(q), od, int(bool(normalize_qk)), scale, amode, bmode, wmode)
     n = ctypes.c_size_t(0)
-    rc = lib.gdr_chunk_bwd_workspace_size(ctypes.byref(desc), ctypes.byref(n))
+    nseq = 0
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+            raise ValueError("cu_seqlens must be a 1-D int32 tensor of N + 1 offsets")
+        nseq = cu_seqlens.numel() - 1
+        rc = lib.gdr_chunk_bwd_varlen_workspace_size(ctypes.byref(desc), nseq, ctypes.byref(n))
+    else:
+        rc = lib.gdr_chunk_bwd_workspace_size(ctypes.byref(desc), ctypes.byref(n))
     if rc != GDR_OK:
         raise GdrError(rc, "gdr_chunk_bwd_workspace_size")
     dev = q.device
@@ -374,7 +389,7 @@ def gdr_chunk_bwd(q, k, v, log_alpha, b, w, dO, gamma=None, z=None, S0=None, dS_
     f32 = dict(dtype=torch.float32, device=dev)
     gshape = lambda mode, d: (B, H, T, d) if mode == PER_CHANNEL else ((B, H, T) if mode == PER_TOKEN else None)
     out = {"dq": torch.empty(B, H, T, dk, **f32), "dk": torch.empty(B, H, T, dk, **f32),
-           "dv": torch.empty(B, H, T, dv, **f32), "dS0": torch.empty(B, H, dk, dv, **f32)}
+           "dv": torch.empty(B, H, T, dv, **f32), "dS0": torch.empty(nseq or B, H, dk, dv, **f32)}
     for name, mode, d in (("dlog_alpha", amode, dk), ("db", bmode, dk), ("dw", wmode, dv)):
         shp = gshape(mode, d)
         out[name] = torch.empty(*shp, **f32) if shp else None
@@ -383,13 +398,16 @@ def gdr_chunk_bwd(q, k, v, log_alpha, b, w, dO, gamma=None, z=None, S0=None, dS_
     for name in BWD_OUTPUTS:
         if name not in outputs:
             out[name] = None
-    rc = lib.gdr_chunk_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(la), _ptr(bt), _ptr(wt),
-                           _ptr(gamma), _ptr(z), _ptr(S0), _ptr(dO), _ptr(dS_T), _ptr(out["dq"]),
-                           _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dlog_alpha"]), _ptr(out["db"]),
-                           _ptr(out["dw"]), _ptr(out["dgamma"]), _ptr(out["dz"]), _ptr(out["dS0"]),
-                           _ptr(workspace), workspace.numel(), _stream(stream))
+    tail = (_ptr(q), _ptr(k), _ptr(v), _ptr(la), _ptr(bt), _ptr(wt), _ptr(gamma), _ptr(z), _ptr(S0), _ptr(dO),
+            _ptr(dS_T), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dlog_alpha"]),
+            _ptr(out["db"]), _ptr(out["dw"]), _ptr(out["dgamma"]), _ptr(out["dz"]), _ptr(out["dS0"]),
+            _ptr(workspace), workspace.numel(), _stream(stream))
+    if nseq:
+        rc = lib.gdr_chunk_bwd_varlen(ctypes.byref(desc), nseq, _ptr(cu_seqlens), *tail)
+    else:
+        rc = lib.gdr_chunk_bwd(ctypes.byref(desc), *tail)
     if rc != GDR_OK:
-        raise GdrError(rc, "gdr_chunk_bwd")
+        raise GdrError(rc, "gdr_chunk_bwd_varlen" if nseq else "gdr_chunk_bwd")
     return out
 
 

@@ -234,6 +234,31 @@ gdr_status gdr_chunk_bwd(const gdr_desc *desc, const void *q, const void *k, con
                          size_t workspace_bytes, void *stream);
 
 /*
+ * Backward of gdr_chunk_fwd_varlen: the gradients of a packed batch of n_seqs
+ * sequences (each with its own S0 and S_T), the reverse of the recurrence of
+ * gdr_chunk_bwd run per sequence and head.  Layouts as gdr_chunk_fwd_varlen:
+ * desc->B must be 1 and desc->T = cu_seqlens[n_seqs]; every per-token tensor
+ * (inputs, dO and the per-token gradients) is [1,H,T,...] over the packed
+ * tokens; S0, dS_T and dS0 are [n_seqs,H,dk,dv]; dgamma [H,dk] sums over all
+ * sequences.  cu_seqlens (device, int32, n_seqs + 1 non-decreasing offsets from
+ * 0) is read on the device; sequences of length 0 pass dS_T to dS0.
+ *   workspace  >= gdr_chunk_bwd_varlen_workspace_size(desc, n_seqs) bytes,
+ *              256-byte aligned
+ * Validation as gdr_chunk_bwd, plus n_seqs >= 1, desc->B == 1 and cu_seqlens
+ * non-null and 4-byte aligned (GDR_ERR_INVALID_ARG); the offsets themselves
+ * are the caller's contract.
+ */
+gdr_status gdr_chunk_bwd_varlen_workspace_size(const gdr_desc *desc, int n_seqs, size_t *bytes);
+gdr_status gdr_chunk_bwd_varlen(const gdr_desc *desc, int n_seqs, const int *cu_seqlens,
+                                const void *q, const void *k, const void *v,
+                                const float *log_alpha, const void *b, const void *w,
+                                const float *gamma, const void *z, const float *S0,
+                                const void *dO, const float *dS_T, float *dq, float *dk,
+                                float *dv, float *dlog_alpha, float *db, float *dw,
+                                float *dgamma, float *dz, float *dS0, void *workspace,
+                                size_t workspace_bytes, void *stream);
+
+/*
  * The two phases of gdr_chunk_fwd as separate calls, for callers that overlap
  * the fully parallel phase of one batch with the serial scan of another on a
  * second stream, or that time the phases.  gdr_chunk_fwd(...) gives exactly

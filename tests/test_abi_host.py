@@ -265,3 +265,26 @@ def test_chunk_bwd_workspace_and_validation():
     assert call(dq=8) == gdr.GDR_ERR_INVALID_ARG
     assert call(ws=None) == gdr.GDR_ERR_WORKSPACE
     assert call(nbytes=1000) == gdr.GDR_ERR_WORKSPACE
+
+
+def test_chunk_bwd_varlen_workspace_and_validation():
+    _lib()
+    lib = gdr.load()
+    n = ctypes.c_size_t(0)
+    one = gdr.make_desc(**dict(GOOD, B=1))
+    assert lib.gdr_chunk_bwd_varlen_workspace_size(ctypes.byref(one), 3, ctypes.byref(n)) == gdr.GDR_OK
+    n_uniform = ctypes.c_size_t(0)
+    assert lib.gdr_chunk_bwd_workspace_size(ctypes.byref(one), ctypes.byref(n_uniform)) == gdr.GDR_OK
+    assert n.value > n_uniform.value  # room for the chunk list and one partial chunk per sequence
+    assert lib.gdr_chunk_bwd_varlen_workspace_size(ctypes.byref(one), 0, ctypes.byref(n)) == gdr.GDR_ERR_INVALID_ARG
+    two = gdr.make_desc(**dict(GOOD, B=2))
+    assert lib.gdr_chunk_bwd_varlen_workspace_size(ctypes.byref(two), 3, ctypes.byref(n)) == gdr.GDR_ERR_INVALID_ARG
+    c = lambda x: None if x is None else ctypes.c_void_p(x)
+
+    def call(nseq=3, cu=4096, desc=one):
+        p = [16, 32, 48, 64, 80, 96, None, None, None, 512, None] + [None] * 9
+        return lib.gdr_chunk_bwd_varlen(ctypes.byref(desc), nseq, c(cu), *[c(x) for x in p], c(1 << 20), 1 << 40, None)
+    assert call(nseq=0) == gdr.GDR_ERR_INVALID_ARG
+    assert call(cu=None) == gdr.GDR_ERR_INVALID_ARG
+    assert call(cu=4098) == gdr.GDR_ERR_INVALID_ARG      # misaligned offsets
+    assert call(desc=two) == gdr.GDR_ERR_INVALID_ARG     # a packed batch has B = 1

@@ -1008,3 +1008,47 @@ def test_backward_nan_stays_in_its_stream():
         for bi, hi in ((0, 0), (0, 1), (1, 1)):
             assert torch.equal(bad[key][bi, hi], clean[key][bi, hi]), (key, bi, hi)
     assert torch.equal(bad["dgamma"][1], clean["dgamma"][1])
+
+
+@pytest.mark.parametrize("name", ["gdn2", "kda", "tiny", "gdn"])
+def test_backward_varlen_mixed_lengths(name):
+    """Packed batch backward (lengths 0, 1, 63, 64, 65, 200, 0, 129, 17): each
+    sequence's gradients against the oracle's backward on its slice; dS0 per
+    sequence; dgamma summed over the sequences."""
+    lens = [0, 1, 63, 64, 65, 200, 0, 129, 17]
+    x, cu = packed_inputs(name, lens, seed_shift=3)
+    N, H, T = len(lens), x["q"].shape[1], x["q"].shape[2]
+    dk, dv = x["q"].shape[-1], x["v"].shape[-1]
+    r = np.random.default_rng(19)
+    dO = torch.from_numpy(r.standard_normal((1, H, T, dv))).float()
+    dST = torch.from_numpy(0.1 * r.standard_normal((N, H, dk, dv))).float()
+    d = dev(x)
+    g = gdr.gdr_chunk_bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], dO.to(DEV),
+                          gamma=d["gamma"], z=d["z"], S0=d["S0"], dS_T=dST.to(DEV),
+                          cu_seqlens=torch.from_numpy(cu).to(DEV))
+    torch.cuda.synchronize()
+    tol = tol_for(x)
+    per_tok = {key: [] for key in ("dq", "dk", "dv", "dlog_alpha", "db", "dw", "dz")}
+    dS0, dgam = [], 0.0
+    for n in range(N):
+        a0, b0 = int(cu[n]), int(cu[n + 1])
+        xs = {key: (val[:, :, a0:b0].contiguous() if isinstance(val, torch.Tensor) and key not in ("gamma", "S0")
+                    else val) for key, val in x.items()}
+        s0 = None if x["S0"] is None else x["S0"][n:n + 1]
+        ref = oracle.backward(xs["q"], xs["k"], xs["v"], xs["log_alpha"], xs["b"], xs["w"],
+                              dO[:, :, a0:b0].contiguous(), gamma=xs["gamma"], z=xs["z"], S0=s0,
+                              dS_T=dST[n:n + 1])
+        for key in per_tok:
+            if ref[key] is not None:
+                per_tok[key].append(ref[key])
+        dS0.append(ref["dS0"][0])
+        if ref["dgamma"] is not None:
+            dgam = dgam + ref["dgamma"]
+    for key, parts in per_tok.items():
+        if not parts:
+            assert g[key] is None, key
+            continue
+        check(f"bwd varlen {name} {key}", g[key].cpu().numpy(), np.concatenate(parts, axis=2), tol)
+    check(f"bwd varlen {name} dS0", g["dS0"].cpu().numpy(), np.stack(dS0), tol)
+    if x["gamma"] is not None:
+        check(f"bwd varlen {name} dgamma", g["dgamma"].cpu().numpy(), dgam, tol)
