@@ -269,6 +269,31 @@ def output_gate(o, g, norm_weight=None, eps=1e-6):
     return np.ascontiguousarray(y.transpose(0, 2, 1, 3))
 
 
+def output_gate_backward(o, g, dy, norm_weight=None, eps=1e-6):
+    """Reverse mode of output_gate: for the loss <dy, y>, the gradients of o,
+    g and norm_weight.  With r = (mean_c o_c^2 + eps)^(-1/2), n = o r,
+    s = sigmoid(g) and u = dy * weight * s (the gradient reaching n):
+      dg = dy * n * weight * s * (1 - s)
+      d weight[h, c] = sum over batch and tokens of dy * n * s
+      do = r * (u - n * sum_c(u_c n_c) / dv)      (through the row norm)
+    dy: [B,T,H,dv] (token-major, as y).  Returns (do, dg, d_norm_weight or
+    None) in fp64, do and dg as [B,H,T,dv].
+    """
+    o = _f64(o)
+    g = _f64(g)
+    dy = np.ascontiguousarray(_f64(dy).transpose(0, 2, 1, 3))
+    dv = o.shape[-1]
+    r = 1.0 / np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps)
+    n = o * r
+    s = 1.0 / (1.0 + np.exp(-g))
+    wgt = np.ones(o.shape[1:2] + (1, dv)) if norm_weight is None else _f64(norm_weight)[:, None, :]
+    dg = dy * n * wgt * s * (1.0 - s)
+    dw = None if norm_weight is None else np.sum(dy * n * s, axis=(0, 2))
+    u = dy * wgt * s
+    do = r * (u - n * np.sum(u * n, axis=-1, keepdims=True) / dv)
+    return do, dg, dw
+
+
 GATE_ORDER = ("f", "b", "g", "w", "q")
 
 

@@ -721,3 +721,28 @@ def test_backward_linear_attention_closed_form(oracle_mod):
     mask = np.tril(np.ones((T, T)))
     np.testing.assert_allclose(g["dv"][0, 0], (qk * mask).T @ dO[0, 0], rtol=1e-12)
     np.testing.assert_allclose(g["dq"][0, 0], ((dO[0, 0] @ v[0, 0].T) * mask) @ k[0, 0], rtol=1e-12)
+
+
+def test_output_gate_backward_matches_central_differences(oracle_mod):
+    """Every gradient of the output gate's backward against central differences
+    of output_gate (the forward), with and without a norm weight."""
+    r = np.random.default_rng(61)
+    B, H, T, dv = 2, 2, 3, 6
+    o = r.standard_normal((B, H, T, dv))
+    g = r.standard_normal((B, H, T, dv))
+    wgt = 1.0 + 0.3 * r.standard_normal((H, dv))
+    dy = r.standard_normal((B, T, H, dv))
+    eps = 1e-3
+    for w_ in (wgt, None):
+        do, dg, dw = oracle_mod.output_gate_backward(o, g, dy, norm_weight=w_, eps=eps)
+        loss = lambda o_, g_, w2: float(np.sum(dy * oracle_mod.output_gate(o_, g_, norm_weight=w2, eps=eps)))
+        h = 1e-6
+        for name, x, grad in (("o", o, do), ("g", g, dg)) + ((("w", wgt, dw),) if w_ is not None else ()):
+            for idx in [(0, 1, 2, 3), (1, 0, 0, 5), (1, 1, 1, 0)] if x.ndim == 4 else [(0, 2), (1, 5)]:
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += h
+                xm[idx] -= h
+                args_p = {"o": (xp, g, w_), "g": (o, xp, w_), "w": (o, g, xp)}[name]
+                args_m = {"o": (xm, g, w_), "g": (o, xm, w_), "w": (o, g, xm)}[name]
+                fd = (loss(*args_p) - loss(*args_m)) / (2 * h)
+                assert abs(fd - grad[idx]) <= 1e-6 * max(1.0, abs(fd)), (name, idx, fd, grad[idx])
