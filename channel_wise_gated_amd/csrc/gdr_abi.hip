@@ -244,6 +244,18 @@ gdr_status bwd_call(const gdr_desc *desc, int nseq, const int *cu, const void *q
   return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }
 
+// The output gate's backward: rows of the descriptor's streams; the weight's
+// gradient through per-block partial sums in the workspace.
+gdr_status og_bwd_plan(const gdr_desc *d, bool weight_grad, size_t *ws) {
+  gdr_status s = check_common(d, d ? d->T : 0);
+  if (s != GDR_OK) return s;
+  const long long ntb = (d->T + 63) / 64;
+  const long long blocks = (long long)d->B * d->H * ntb;
+  if (blocks > (1LL << 31) - 1) return GDR_ERR_INVALID_ARG;
+  *ws = weight_grad ? (size_t)((blocks * d->dv * 4 + 255) & ~255LL) : 0;
+  return GDR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -282,6 +294,40 @@ gdr_status gdr_chunk_bwd_varlen(const gdr_desc *desc, int n_seqs, const int *cu_
   if (n_seqs < 1) return GDR_ERR_INVALID_ARG;
   return bwd_call(desc, n_seqs, cu_seqlens, q, k, v, log_alpha, b, w, gamma, z, S0, dO, dS_T, dq, dk, dv,
                   dlog_alpha, db, dw, dgamma, dz, dS0, workspace, workspace_bytes, stream);
+}
+
+gdr_status gdr_output_gate_bwd_workspace_size(const gdr_desc *desc, int with_weight, size_t *bytes) {
+  if (!bytes) return GDR_ERR_INVALID_ARG;
+  size_t ws = 0;
+  gdr_status s = og_bwd_plan(desc, with_weight != 0, &ws);
+  if (s == GDR_OK) *bytes = ws;
+  return s;
+}
+
+gdr_status gdr_output_gate_bwd(const gdr_desc *desc, const float *o, const void *g, const float *norm_weight,
+                               float eps, const void *dy, float *d_o, float *dg, float *d_norm_weight,
+                               void *workspace, size_t workspace_bytes, void *stream) {
+  const bool wgrad = norm_weight && d_norm_weight;
+  size_t need = 0;
+  gdr_status s = og_bwd_plan(desc, wgrad, &need);
+  if (s != GDR_OK) return s;
+  const gdr_desc &d = *desc;
+  if (!(eps >= 0.f) || eps > 3.0e38f) return GDR_ERR_INVALID_ARG;
+  if ((long long)d.B * d.H == 0) return GDR_OK;
+  if (d.T > 0 && (!o || !g || !dy || !d_o)) return GDR_ERR_INVALID_ARG;
+  const void *ptrs[] = {o, g, norm_weight, dy, d_o, dg, d_norm_weight};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return GDR_ERR_INVALID_ARG;
+  if (need > 0 && (!workspace || workspace_bytes < need)) return GDR_ERR_WORKSPACE;
+  if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u)) return GDR_ERR_WORKSPACE;
+  gdr::OgBwdArgs a;
+  a.o = o; a.nw = norm_weight; a.g = g; a.dy = dy;
+  a.dO = d_o; a.dg = dg; a.dnw = wgrad ? d_norm_weight : nullptr;
+  a.part = wgrad ? static_cast<float *>(workspace) : nullptr;
+  a.B = d.B; a.H = d.H; a.T = d.T; a.ntb = (d.T + 63) / 64;
+  a.dy_bf16 = d.out_dtype == GDR_BF16; a.eps = eps;
+  hipError_t e = gdr::launch_out_gate_bwd(a, d.dv, d.in_dtype == GDR_BF16, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }
 
 gdr_status gdr_gate_proj_workspace_size(const gdr_gate_desc *desc, size_t *bytes) {

@@ -984,6 +984,89 @@ __global__ void __launch_bounds__(256) bwd_dgamma_kernel(BwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Output gate backward: y = n * weight * s with n = o r, r = (mean_c o_c^2 +
+// eps)^(-1/2), s = sigmoid(g) (the fused gate of the forward).  For the loss
+// <dy, y>: dg = dy n weight s (1 - s), do = r (u - n sum_c(u_c n_c) / dv) with
+// u = dy weight s, and per workgroup the partial sums of dy n s for the
+// weight's gradient.  One workgroup per (stream, 64 tokens); a wave per 16
+// tokens, a lane per D / 64 channels.
+// ---------------------------------------------------------------------------
+template <int D, bool BF>
+__global__ void __launch_bounds__(256) out_gate_bwd_kernel(OgBwdArgs a) {
+  constexpr int CPL = D / 64, TB = 64, TW = TB / 4;
+  __shared__ float wp[4][D];
+  const size_t bh = blockIdx.x / a.ntb;
+  const int tb = (int)(blockIdx.x % a.ntb), b = (int)(bh / a.H), h = (int)(bh % a.H);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c0 = CPL * lane;
+  float nw[CPL], acc[CPL];
+#pragma unroll
+  for (int u = 0; u < CPL; ++u) {
+    nw[u] = a.nw ? a.nw[(size_t)h * D + c0 + u] : 1.f;
+    acc[u] = 0.f;
+  }
+  for (int j = 0; j < TW; ++j) {
+    const int t = tb * TB + w * TW + j;
+    if (t >= a.T) break;  // uniform over the wave
+    const size_t row = bh * a.T + t, yrow = ((size_t)b * a.T + t) * a.H + h;
+    float o[CPL], gv[CPL], dy[CPL], ss = 0.f;
+#pragma unroll
+    for (int u = 0; u < CPL; ++u) {
+      o[u] = a.o[row * D + c0 + u];
+      gv[u] = ld1<BF>(a.g, row * D + c0 + u);
+      dy[u] = a.dy_bf16 ? ld1<true>(a.dy, yrow * D + c0 + u) : ld1<false>(a.dy, yrow * D + c0 + u);
+      ss += o[u] * o[u];
+    }
+    const float r = 1.f / sqrtf(wave_sum(ss) / D + a.eps);
+    float n[CPL], sg[CPL], uu[CPL], dot = 0.f;
+#pragma unroll
+    for (int u = 0; u < CPL; ++u) {
+      n[u] = o[u] * r;
+      sg[u] = 1.f / (1.f + expf(-gv[u]));
+      uu[u] = dy[u] * nw[u] * sg[u];
+      dot += uu[u] * n[u];
+    }
+    dot = wave_sum(dot) / D;
+#pragma unroll
+    for (int u = 0; u < CPL; ++u) {
+      a.dO[row * D + c0 + u] = r * (uu[u] - n[u] * dot);
+      if (a.dg) a.dg[row * D + c0 + u] = dy[u] * n[u] * nw[u] * sg[u] * (1.f - sg[u]);
+      acc[u] += dy[u] * n[u] * sg[u];
+    }
+  }
+  if (!a.part) return;  // uniform over the block
+#pragma unroll
+  for (int u = 0; u < CPL; ++u) wp[w][c0 + u] = acc[u];
+  __syncthreads();
+  if (tid < D)
+    a.part[(((size_t)b * a.ntb + tb) * a.H + h) * D + tid] = wp[0][tid] + wp[1][tid] + wp[2][tid] + wp[3][tid];
+}
+
+// d weight[h][c] = sum of the partials of every (batch, token block)
+template <int D>
+__global__ void __launch_bounds__(256) out_gate_dw_kernel(OgBwdArgs a) {
+  __shared__ float part[8][32];
+  const int h = blockIdx.x / (D / 32), cl = threadIdx.x & 31, j = threadIdx.x >> 5;
+  const int ch = (blockIdx.x % (D / 32)) * 32 + cl;
+  float s = 0.f;
+  for (int k = j; k < a.B * a.ntb; k += 8) s += a.part[((size_t)k * a.H + h) * D + ch];
+  part[j][cl] = s;
+  __syncthreads();
+  if (j == 0) {
+#pragma unroll
+    for (int i = 1; i < 8; ++i) s += part[i][cl];
+    a.dnw[h * D + ch] = s;
+  }
+}
+
+template <int D, bool BF>
+hipError_t launch_out_gate_bwd_t(const OgBwdArgs &a, hipStream_t st) {
+  const size_t nblk = (size_t)a.B * a.H * a.ntb;
+  if (nblk > 0) hipLaunchKernelGGL((out_gate_bwd_kernel<D, BF>), dim3((unsigned)nblk), dim3(256), 0, st, a);
+  if (a.dnw) hipLaunchKernelGGL((out_gate_dw_kernel<D>), dim3((unsigned)(a.H * (D / 32))), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 template <int D, int NS, bool BF>
 hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
   const unsigned nch = (unsigned)(a.ctab ? (size_t)a.H * a.ctab_len : (size_t)a.B * a.H * a.NC);
@@ -1054,6 +1137,11 @@ hipError_t launch_bwd_prep(const BwdArgs &a, int D, int NS, hipStream_t st) {
   if (D == 128) return launch_bwd_prep_t<128, 3>(a, st);
   if (NS == 2) return launch_bwd_prep_t<64, 2>(a, st);
   return launch_bwd_prep_t<64, 3>(a, st);
+}
+
+hipError_t launch_out_gate_bwd(const OgBwdArgs &a, int D, bool g_bf16, hipStream_t st) {
+  if (D == 128) return g_bf16 ? launch_out_gate_bwd_t<128, true>(a, st) : launch_out_gate_bwd_t<128, false>(a, st);
+  return g_bf16 ? launch_out_gate_bwd_t<64, true>(a, st) : launch_out_gate_bwd_t<64, false>(a, st);
 }
 
 hipError_t launch_bwd(const BwdArgs &a, int D, int NS, hipStream_t st) {

@@ -83,6 +83,18 @@ size_t bwd_workspace(BwdArgs *a, ChunkArgs *f, void *ws, int B, int H, int T, in
 hipError_t launch_bwd_prep(const BwdArgs &a, int D, int NS, hipStream_t st);
 hipError_t launch_bwd(const BwdArgs &a, int D, int NS, hipStream_t st);
 
+// Backward of the fused output gate (gdr_bwd.hip): rows of [B,H,T,dv] in
+// workgroups of 64 tokens; `part` holds [B][ntb][H][dv] partial sums of the
+// norm weight's gradient (null without a weight).
+struct OgBwdArgs {
+  const float *o, *nw;
+  const void *g, *dy;
+  float *dO, *dg, *dnw, *part;
+  int B, H, T, ntb, dy_bf16;
+  float eps;
+};
+hipError_t launch_out_gate_bwd(const OgBwdArgs &a, int D, bool g_bf16, hipStream_t st);
+
 hipError_t launch_decode(const gdr_desc &d, float *S, const void *q, const void *k, const void *v,
                          const float *la, const void *b, const void *w, const float *gamma,
                          const void *z, void *o, hipStream_t st);

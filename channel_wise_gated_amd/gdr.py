@@ -32,7 +32,7 @@ GDR_BF16, GDR_F32 = 0, 1
 PER_CHANNEL, PER_TOKEN, ONES, ZEROS = 0, 1, 2, 3
 SYMBOLS = ("gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_chunk_fwd_gated", "gdr_chunk_fwd_intra",
            "gdr_chunk_bwd_workspace_size", "gdr_chunk_bwd", "gdr_chunk_bwd_varlen_workspace_size",
-           "gdr_chunk_bwd_varlen",
+           "gdr_chunk_bwd_varlen", "gdr_output_gate_bwd_workspace_size", "gdr_output_gate_bwd",
            "gdr_chunk_fwd_scan", "gdr_chunk_fwd_varlen_workspace_size", "gdr_chunk_fwd_varlen",
            "gdr_decode_step", "gdr_status_string", "gdr_version", "gdr_gate_proj_workspace_size",
            "gdr_gate_proj")
@@ -105,6 +105,10 @@ def load() -> ctypes.CDLL:
     lib.gdr_chunk_bwd_varlen_workspace_size.argtypes = [dp, ctypes.c_int, ctypes.POINTER(sz)]
     lib.gdr_chunk_bwd_varlen.restype = ctypes.c_int
     lib.gdr_chunk_bwd_varlen.argtypes = [dp, ctypes.c_int, vp] + [vp] * 21 + [sz, vp]
+    lib.gdr_output_gate_bwd_workspace_size.restype = ctypes.c_int
+    lib.gdr_output_gate_bwd_workspace_size.argtypes = [dp, ctypes.c_int, ctypes.POINTER(sz)]
+    lib.gdr_output_gate_bwd.restype = ctypes.c_int
+    lib.gdr_output_gate_bwd.argtypes = [dp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp, sz, vp]
     lib.gdr_status_string.restype = ctypes.c_char_p
     lib.gdr_status_string.argtypes = [ctypes.c_int]
     lib.gdr_version.restype = ctypes.c_int
@@ -493,3 +497,35 @@ def gdr_chunk_fwd_varlen(q, k, v, log_alpha, b, w, cu_seqlens, gamma=None, z=Non
     if rc != GDR_OK:
         raise GdrError(rc, "gdr_chunk_fwd_varlen")
     return o, S_T
+
+
+def gdr_output_gate_bwd(o, g, dy, norm_weight=None, eps=1e-6, *, stream=None) -> dict:
+    """Backward of the fused output gate; see gdr_output_gate_bwd in gdr.h.
+
+    o [B,H,T,dv] fp32, g [B,H,T,dv] (bf16 or fp32), dy [B,T,H,dv] (bf16 or
+    fp32, token-major), norm_weight [H,dv] fp32 or None.  Returns fp32 d_o and
+    dg [B,H,T,dv] and d_norm_weight [H,dv] (None without a weight).
+    """
+    lib = load()
+    o, g, dy, norm_weight = map(_contig, (o, g, dy, norm_weight))
+    if o.dtype != torch.float32:
+        raise ValueError("o must be fp32")
+    B, H, T, dv = o.shape
+    if tuple(g.shape) != (B, H, T, dv) or tuple(dy.shape) != (B, T, H, dv):
+        raise ValueError("g must be [B,H,T,dv] and dy [B,T,H,dv]")
+    desc = make_desc(B, H, T, dv, dv, 64, _dtype_code(g), GDR_BF16 if dy.dtype == torch.bfloat16 else GDR_F32,
+                     1, 1.0, PER_CHANNEL, PER_CHANNEL, PER_CHANNEL)
+    f32 = dict(dtype=torch.float32, device=o.device)
+    out = {"d_o": torch.empty(B, H, T, dv, **f32), "dg": torch.empty(B, H, T, dv, **f32),
+           "d_norm_weight": torch.empty(H, dv, **f32) if norm_weight is not None else None}
+    n = ctypes.c_size_t(0)
+    rc = lib.gdr_output_gate_bwd_workspace_size(ctypes.byref(desc), int(norm_weight is not None), ctypes.byref(n))
+    if rc != GDR_OK:
+        raise GdrError(rc, "gdr_output_gate_bwd_workspace_size")
+    ws = torch.empty(max(int(n.value), 1), dtype=torch.uint8, device=o.device)
+    rc = lib.gdr_output_gate_bwd(ctypes.byref(desc), _ptr(o), _ptr(g), _ptr(norm_weight), float(eps), _ptr(dy),
+                                 _ptr(out["d_o"]), _ptr(out["dg"]), _ptr(out["d_norm_weight"]), _ptr(ws),
+                                 ws.numel(), _stream(stream))
+    if rc != GDR_OK:
+        raise GdrError(rc, "gdr_output_gate_bwd")
+    return out

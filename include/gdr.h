@@ -248,6 +248,37 @@ gdr_status gdr_chunk_bwd(const gdr_desc *desc, const void *q, const void *k, con
  * non-null and 4-byte aligned (GDR_ERR_INVALID_ARG); the offsets themselves
  * are the caller's contract.
  */
+/*
+ * Backward of the output gate of gdr_chunk_fwd_gated (Muir reading notes,
+ * section 2.1: per-head RMSNorm of o, then the output gate g per channel; the
+ * library's reading y = o / sqrt(mean_c o^2 + eps) * norm_weight *
+ * sigmoid(g)).  For the loss <dy, y> it returns the gradients of o, g and
+ * norm_weight, so that a layer's backward can run this, then gdr_chunk_bwd
+ * with d_o as its dO.
+ *
+ *   desc        B, H, T, dk = dv (64 or 128); in_dtype is g's dtype, out_dtype
+ *               dy's dtype (the rest of the descriptor is not used)
+ *   o           [B,H,T,dv] fp32: the recurrence's output (gdr_chunk_fwd's o)
+ *   g           [B,H,T,dv] in_dtype: the gate logits
+ *   norm_weight [H,dv] fp32 or NULL (= 1);  eps >= 0, finite
+ *   dy          [B,T,H,dv] out_dtype (token-major, as y)
+ *   d_o         [B,H,T,dv] fp32 (written)
+ *   dg          [B,H,T,dv] fp32 or NULL (not written)
+ *   d_norm_weight [H,dv] fp32 or NULL; written only with norm_weight (summed
+ *               over batch and tokens)
+ *   workspace   >= gdr_output_gate_bwd_workspace_size(desc, with_weight)
+ *               bytes (with_weight: norm_weight and d_norm_weight both given),
+ *               256-byte aligned; 0 bytes without the weight's gradient
+ * Errors: dimensions and dtypes as gdr_chunk_fwd; null o, g, dy or d_o (with
+ * T > 0), misaligned pointers or a bad eps: GDR_ERR_INVALID_ARG; workspace:
+ * GDR_ERR_WORKSPACE; all on the host before any launch.
+ */
+gdr_status gdr_output_gate_bwd_workspace_size(const gdr_desc *desc, int with_weight, size_t *bytes);
+gdr_status gdr_output_gate_bwd(const gdr_desc *desc, const float *o, const void *g,
+                               const float *norm_weight, float eps, const void *dy, float *d_o,
+                               float *dg, float *d_norm_weight, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
 gdr_status gdr_chunk_bwd_varlen_workspace_size(const gdr_desc *desc, int n_seqs, size_t *bytes);
 gdr_status gdr_chunk_bwd_varlen(const gdr_desc *desc, int n_seqs, const int *cu_seqlens,
                                 const void *q, const void *k, const void *v,

@@ -288,3 +288,25 @@ def test_chunk_bwd_varlen_workspace_and_validation():
     assert call(cu=None) == gdr.GDR_ERR_INVALID_ARG
     assert call(cu=4098) == gdr.GDR_ERR_INVALID_ARG      # misaligned offsets
     assert call(desc=two) == gdr.GDR_ERR_INVALID_ARG     # a packed batch has B = 1
+
+
+def test_output_gate_bwd_workspace_and_validation():
+    _lib()
+    lib = gdr.load()
+    n = ctypes.c_size_t(0)
+    desc = gdr.make_desc(**GOOD)
+    assert lib.gdr_output_gate_bwd_workspace_size(ctypes.byref(desc), 1, ctypes.byref(n)) == gdr.GDR_OK
+    assert n.value == 2 * 4 * ((256 + 63) // 64) * 128 * 4  # B H token-blocks dv fp32
+    assert lib.gdr_output_gate_bwd_workspace_size(ctypes.byref(desc), 0, ctypes.byref(n)) == gdr.GDR_OK and n.value == 0
+    c = lambda x: None if x is None else ctypes.c_void_p(x)
+
+    def call(o=16, g=32, nw=48, eps=1e-6, dy=64, d_o=80, dnw=96, ws=1 << 20, nbytes=1 << 30):
+        return lib.gdr_output_gate_bwd(ctypes.byref(desc), c(o), c(g), c(nw), eps, c(dy), c(d_o), None, c(dnw),
+                                       c(ws), nbytes, None)
+    assert call(o=None) == gdr.GDR_ERR_INVALID_ARG
+    assert call(d_o=None) == gdr.GDR_ERR_INVALID_ARG
+    assert call(dy=72) == gdr.GDR_ERR_INVALID_ARG       # misaligned
+    assert call(eps=-1.0) == gdr.GDR_ERR_INVALID_ARG
+    assert call(eps=float("nan")) == gdr.GDR_ERR_INVALID_ARG
+    assert call(ws=None) == gdr.GDR_ERR_WORKSPACE
+    assert call(nbytes=1024) == gdr.GDR_ERR_WORKSPACE

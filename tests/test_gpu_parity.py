@@ -1052,3 +1052,25 @@ def test_backward_varlen_mixed_lengths(name):
     check(f"bwd varlen {name} dS0", g["dS0"].cpu().numpy(), np.stack(dS0), tol)
     if x["gamma"] is not None:
         check(f"bwd varlen {name} dgamma", g["dgamma"].cpu().numpy(), dgam, tol)
+
+
+@pytest.mark.parametrize("d,gdt,ydt,weight", [(128, torch.bfloat16, torch.float32, True),
+                                              (128, torch.float32, torch.bfloat16, False),
+                                              (64, torch.bfloat16, torch.bfloat16, True)])
+def test_output_gate_backward(d, gdt, ydt, weight):
+    """The output gate's backward against the oracle's (ragged T, two batches)."""
+    r = np.random.default_rng(71)
+    B, H, T = 2, 3, 150
+    o = torch.from_numpy(r.standard_normal((B, H, T, d))).float()
+    g = torch.from_numpy(r.standard_normal((B, H, T, d))).to(gdt)
+    dy = torch.from_numpy(r.standard_normal((B, T, H, d))).to(ydt)
+    nw = torch.from_numpy(1.0 + 0.1 * r.standard_normal((H, d))).float() if weight else None
+    got = gdr.gdr_output_gate_bwd(o.to(DEV), g.to(DEV), dy.to(DEV), None if nw is None else nw.to(DEV), eps=1e-5)
+    torch.cuda.synchronize()
+    do, dg, dw = oracle.output_gate_backward(o, g.float(), dy.float(), norm_weight=nw, eps=1e-5)
+    check(f"out gate bwd d{d} d_o", got["d_o"].cpu().numpy(), do, TOL_F32)
+    check(f"out gate bwd d{d} dg", got["dg"].cpu().numpy(), dg, TOL_F32)
+    if weight:
+        check(f"out gate bwd d{d} d_norm_weight", got["d_norm_weight"].cpu().numpy(), dw, TOL_F32)
+    else:
+        assert got["d_norm_weight"] is None
