@@ -193,7 +193,8 @@ def timed_layer(x, C, steps, warmup):
 
 def timed_bwd(x, steps, warmup):
     """The backward pass over the long-context inputs (chunk 64, every
-    gradient incl. dS0 from an upstream dS_T): random fp32 dO.  HIP events on
+    gradient incl. dS0 from an upstream dS_T): random fp32 dO; and the output
+    gate's backward at the same shape.  HIP events on
     the current stream, median over `steps`; gradients and workspace come
     from torch's caching allocator (no device allocation after warm-up)."""
     import torch
@@ -216,12 +217,30 @@ def timed_bwd(x, steps, warmup):
         e[1].record()
     torch.cuda.synchronize()
     ms = sorted(e[0].elapsed_time(e[1]) for e in ev)[steps // 2]
+    # the output gate's backward at the same shape (o fp32, bf16 gate logits and
+    # dy, norm weight): the step before the recurrence's backward in a layer
+    o = torch.randn(B, H, T, dv, generator=gen, device="cuda")
+    gl = torch.randn(B, H, T, dv, generator=gen, device="cuda").to(torch.bfloat16)
+    dy = torch.randn(B, T, H, dv, generator=gen, device="cuda").to(torch.bfloat16)
+    nw = 1.0 + 0.1 * torch.randn(H, dv, generator=gen, device="cuda")
+    ogb = lambda: gdr.gdr_output_gate_bwd(o, gl, dy, nw, eps=1e-6)
+    ogb()
+    torch.cuda.synchronize()
+    ev2 = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for e in ev2:
+        e[0].record()
+        ogb()
+        e[1].record()
+    torch.cuda.synchronize()
+    og_ms = sorted(e[0].elapsed_time(e[1]) for e in ev2)[steps // 2]
+    og_bytes = B * H * T * dv * (4 + 2 + 2 + 4 + 4)  # o, g, dy in; do, dg out
     # algorithmic HBM bytes: bf16 q, k, v, b, w, z and fp32 log-decay, dO in;
     # seven fp32 gradients out (dS0 and dgamma are negligible)
     byt = B * H * T * (6 * 2 * dk + 4 * dk + 4 * dv + 7 * 4 * dk)
     return {"workload": f"bwd B{B} H{H} T{T} dk{dk} dv{dv} chunk64, grads of q,k,v,log-decay,b,w,z,gain,S0",
             "steps": steps, "ms_per_step": round(ms, 4), "tokens_s": round(B * T / (ms / 1e3), 1),
-            "bytes_algorithmic": byt, "hbm_gbs_algorithmic": round(byt / (ms / 1e3) / 1e9, 1)}
+            "bytes_algorithmic": byt, "hbm_gbs_algorithmic": round(byt / (ms / 1e3) / 1e9, 1),
+            "out_gate_bwd_ms": round(og_ms, 4), "out_gate_bwd_hbm_gbs": round(og_bytes / (og_ms / 1e3) / 1e9, 1)}
 
 
 def copy_calibration(mib):

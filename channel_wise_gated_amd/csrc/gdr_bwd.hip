@@ -1005,18 +1005,31 @@ __global__ void __launch_bounds__(256) out_gate_bwd_kernel(OgBwdArgs a) {
     nw[u] = a.nw ? a.nw[(size_t)h * D + c0 + u] : 1.f;
     acc[u] = 0.f;
   }
+#pragma unroll 4
   for (int j = 0; j < TW; ++j) {
     const int t = tb * TB + w * TW + j;
-    if (t >= a.T) break;  // uniform over the wave
+    if (t >= a.T) continue;  // uniform over the wave
     const size_t row = bh * a.T + t, yrow = ((size_t)b * a.T + t) * a.H + h;
     float o[CPL], gv[CPL], dy[CPL], ss = 0.f;
+    if constexpr (CPL == 2) {  // paired channels: 8- and 4-byte loads
+      const float2 o2 = *reinterpret_cast<const float2 *>(a.o + row * D + c0);
+      o[0] = o2.x;
+      o[1] = o2.y;
+      ldc<BF, 2>(a.g, row * D + c0, gv);
+      if (a.dy_bf16)
+        ldc<true, 2>(a.dy, yrow * D + c0, dy);
+      else
+        ldc<false, 2>(a.dy, yrow * D + c0, dy);
+    } else {
 #pragma unroll
-    for (int u = 0; u < CPL; ++u) {
-      o[u] = a.o[row * D + c0 + u];
-      gv[u] = ld1<BF>(a.g, row * D + c0 + u);
-      dy[u] = a.dy_bf16 ? ld1<true>(a.dy, yrow * D + c0 + u) : ld1<false>(a.dy, yrow * D + c0 + u);
-      ss += o[u] * o[u];
+      for (int u = 0; u < CPL; ++u) {
+        o[u] = a.o[row * D + c0 + u];
+        gv[u] = ld1<BF>(a.g, row * D + c0 + u);
+        dy[u] = a.dy_bf16 ? ld1<true>(a.dy, yrow * D + c0 + u) : ld1<false>(a.dy, yrow * D + c0 + u);
+      }
     }
+#pragma unroll
+    for (int u = 0; u < CPL; ++u) ss += o[u] * o[u];
     const float r = 1.f / sqrtf(wave_sum(ss) / D + a.eps);
     float n[CPL], sg[CPL], uu[CPL], dot = 0.f;
 #pragma unroll
@@ -1027,12 +1040,15 @@ __global__ void __launch_bounds__(256) out_gate_bwd_kernel(OgBwdArgs a) {
       dot += uu[u] * n[u];
     }
     dot = wave_sum(dot) / D;
+    float xo[CPL], xg[CPL];
 #pragma unroll
     for (int u = 0; u < CPL; ++u) {
-      a.dO[row * D + c0 + u] = r * (uu[u] - n[u] * dot);
-      if (a.dg) a.dg[row * D + c0 + u] = dy[u] * n[u] * nw[u] * sg[u] * (1.f - sg[u]);
+      xo[u] = r * (uu[u] - n[u] * dot);
+      xg[u] = dy[u] * n[u] * nw[u] * sg[u] * (1.f - sg[u]);
       acc[u] += dy[u] * n[u] * sg[u];
     }
+    stc<CPL>(a.dO + row * D + c0, xo);
+    if (a.dg) stc<CPL>(a.dg + row * D + c0, xg);
   }
   if (!a.part) return;  // uniform over the block
 #pragma unroll
