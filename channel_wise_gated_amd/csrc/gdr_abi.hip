@@ -73,6 +73,7 @@ struct OutGate {
   const float *norm_w;
   float eps;
   void *y;
+  float *o;  // optional: o before the norm and gate (fp32)
 };
 
 gdr_status chunk_call(const gdr_desc *desc, int nseq, const int *cu, const void *q, const void *k,
@@ -90,6 +91,7 @@ gdr_status chunk_call(const gdr_desc *desc, int nseq, const int *cu, const void 
   if (og) {  // gated output: y replaces o
     if (!og->g || !og->y || !aligned16(og->g) || !aligned16(og->y)) return GDR_ERR_INVALID_ARG;
     if (og->norm_w && !aligned16(og->norm_w)) return GDR_ERR_INVALID_ARG;
+    if (og->o && !aligned16(og->o)) return GDR_ERR_INVALID_ARG;
     if (!(og->eps >= 0.f) || og->eps > 3.0e38f) return GDR_ERR_INVALID_ARG;
     o = og->y;
   }
@@ -121,6 +123,7 @@ gdr_status chunk_call(const gdr_desc *desc, int nseq, const int *cu, const void 
   a.onw = og ? og->norm_w : nullptr;
   a.oeps = og ? og->eps : 0.f;
   a.y = og ? og->y : nullptr;
+  a.oraw = og ? og->o : nullptr;
   if (nseq == 0) { a.ctab = nullptr; a.coff = nullptr; a.ctab_len = 0; }
   hipError_t e = gdr::launch_chunk(d, a, phases, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
@@ -202,7 +205,7 @@ gdr_status bwd_call(const gdr_desc *desc, int nseq, const int *cu, const void *q
   f.normalize_qk = d.normalize_qk; f.scale = d.scale;
   f.cu = nseq > 0 ? cu : nullptr; f.coff = nullptr; f.ctab = nullptr; f.nseq = nseq; f.ctab_len = 0;
   f.c0 = 0; f.ncs = 0; f.rev = 0;
-  f.og = nullptr; f.onw = nullptr; f.oeps = 0.f; f.y = nullptr;
+  f.og = nullptr; f.onw = nullptr; f.oeps = 0.f; f.y = nullptr; f.oraw = nullptr;
   gdr::BwdArgs a;
   a.q = q; a.k = k; a.v = v; a.b = b; a.w = w; a.z = z; a.dO = dO;
   a.log_alpha = log_alpha; a.gamma = gamma;
@@ -400,9 +403,9 @@ gdr_status gdr_chunk_fwd(const gdr_desc *desc, const void *q, const void *k, con
 gdr_status gdr_chunk_fwd_gated(const gdr_desc *desc, const void *q, const void *k, const void *v,
                                const float *log_alpha, const void *b, const void *w,
                                const float *gamma, const void *z, const float *S0, const void *g,
-                               const float *norm_weight, float eps, void *y, float *S_T,
+                               const float *norm_weight, float eps, void *y, float *o, float *S_T,
                                void *workspace, size_t workspace_bytes, void *stream) {
-  const OutGate og{g, norm_weight, eps, y};
+  const OutGate og{g, norm_weight, eps, y, o};
   return chunk_call(desc, 0, nullptr, q, k, v, log_alpha, b, w, gamma, z, S0, nullptr, S_T, workspace,
                     workspace_bytes, stream, 3, &og);
 }

@@ -1155,6 +1155,11 @@ __global__ void __launch_bounds__(64 * (C / 16)) chunk_out_kernel(ChunkArgs a) {
       ov[jt] = product(jt);
 #pragma unroll
       for (int r = 0; r < 4; ++r) ss[r] += ov[jt][r] * ov[jt][r];
+      if (a.oraw) {  // o before the norm and the gate, for the gate's backward
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (tok0 + r < tvalid) a.oraw[(orow0 + r) * D + 16 * jt + l16] = ov[jt][r];
+      }
     }
     float inv[4];
 #pragma unroll

@@ -41,6 +41,7 @@ struct ChunkArgs {
   const void *og;
   const float *onw;
   float oeps;
+  float *oraw;  // gated output only: o itself as well ([B,H,T,dv] fp32), or null
   void *y;
 };
 

@@ -80,7 +80,7 @@ def load() -> ctypes.CDLL:
     lib.gdr_chunk_fwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gdr_chunk_fwd_gated.restype = ctypes.c_int
     lib.gdr_chunk_fwd_gated.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp,
-                                        vp, vp, sz, vp]
+                                        vp, vp, vp, sz, vp]
     lib.gdr_chunk_fwd_intra.restype = ctypes.c_int
     lib.gdr_chunk_fwd_intra.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gdr_chunk_fwd_scan.restype = ctypes.c_int
@@ -261,11 +261,12 @@ def gdr_chunk_fwd(q, k, v, log_alpha, b, w, gamma=None, z=None, S0=None, *, chun
 
 def gdr_chunk_fwd_gated(q, k, v, log_alpha, b, w, g, gamma=None, z=None, S0=None, norm_weight=None,
                         eps=1e-6, *, chunk=64, out_dtype=torch.float32, normalize_qk=True, scale=1.0,
-                        y=None, S_T=None, workspace=None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+                        y=None, S_T=None, workspace=None, stream=None, o=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Chunkwise forward with the fused output gate; see gdr_chunk_fwd_gated in gdr.h.
 
     Arguments as gdr_chunk_fwd, plus g [B,H,T,dv] (input dtype), norm_weight
-    [H,dv] fp32 or None, eps.  Returns (y [B,T,H,dv] out_dtype, S_T).
+    [H,dv] fp32 or None, eps.  Returns (y [B,T,H,dv] out_dtype, S_T).  With
+    `o` (an fp32 [B,H,T,dv] tensor) o itself is written there as well.
     """
     lib = load()
     call = ChunkCall(q, k, v, log_alpha, b, w, gamma, z, S0, chunk=chunk, out_dtype=out_dtype,
@@ -278,7 +279,7 @@ def gdr_chunk_fwd_gated(q, k, v, log_alpha, b, w, g, gamma=None, z=None, S0=None
         y = torch.empty((B, T, H, dv), dtype=out_dtype, device=q.device)
     S0p, _, sTp = call.out_ptrs
     rc = lib.gdr_chunk_fwd_gated(ctypes.byref(call.desc), *call.ptrs[:8], S0p, _ptr(g), _ptr(norm_weight),
-                                 float(eps), _ptr(y), sTp, *call.ws, _stream(stream))
+                                 float(eps), _ptr(y), _ptr(o), sTp, *call.ws, _stream(stream))
     if rc != GDR_OK:
         raise GdrError(rc, "gdr_chunk_fwd_gated")
     return y, call.S_T

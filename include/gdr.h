@@ -194,6 +194,8 @@ gdr_status gdr_gate_proj(const gdr_gate_desc *desc, const void *x, const void *w
  *   norm_weight  [H,dv] fp32 RMSNorm weight, or NULL (= 1)
  *   eps          >= 0, finite (added to the mean square)
  *   y            [B,T,H,dv] out_dtype (written)
+ *   o            [B,H,T,dv] fp32 or NULL: when given, o itself (before the
+ *                norm and the gate) is written too, for gdr_output_gate_bwd
  * Validation as gdr_chunk_fwd, plus: g and y non-null and 16-byte aligned,
  * eps finite and >= 0 (GDR_ERR_INVALID_ARG).
  */
@@ -201,7 +203,7 @@ gdr_status gdr_chunk_fwd_gated(const gdr_desc *desc, const void *q, const void *
                                const void *v, const float *log_alpha, const void *b,
                                const void *w, const float *gamma, const void *z,
                                const float *S0, const void *g, const float *norm_weight,
-                               float eps, void *y, float *S_T, void *workspace,
+                               float eps, void *y, float *o, float *S_T, void *workspace,
                                size_t workspace_bytes, void *stream);
 
 /*

@@ -117,12 +117,12 @@ def test_chunk_fwd_rejects_before_launch(ptrs, code):
 
 def _call_gated(desc, ptrs, eps=1e-6, ws_bytes=1 << 30):
     p = dict(q=16, k=32, v=48, la=64, b=80, w=96, gamma=None, z=None, S0=None, g=112, nw=None, y=128,
-             ST=144, ws=256)
+             o=None, ST=144, ws=256)
     p.update(ptrs)
     c = lambda x: None if x is None else ctypes.c_void_p(x)
     return gdr.load().gdr_chunk_fwd_gated(ctypes.byref(desc), c(p["q"]), c(p["k"]), c(p["v"]), c(p["la"]),
                                           c(p["b"]), c(p["w"]), c(p["gamma"]), c(p["z"]), c(p["S0"]),
-                                          c(p["g"]), c(p["nw"]), eps, c(p["y"]), c(p["ST"]), c(p["ws"]),
+                                          c(p["g"]), c(p["nw"]), eps, c(p["y"]), c(p["o"]), c(p["ST"]), c(p["ws"]),
                                           ws_bytes, None)
 
 

@@ -1074,3 +1074,36 @@ def test_output_gate_backward(d, gdt, ydt, weight):
         check(f"out gate bwd d{d} d_norm_weight", got["d_norm_weight"].cpu().numpy(), dw, TOL_F32)
     else:
         assert got["d_norm_weight"] is None
+
+
+def test_gated_forward_keeps_o_and_layer_backward_chain():
+    """The gated forward also writes o (bit-identical to the plain forward's);
+    then the layer's backward: the output gate's backward on that o, and the
+    recurrence's backward with its d_o, against the oracle's two steps."""
+    wl = WORKLOADS["gdn2"].with_sizes(B=1, H=2, T=150)
+    x = make_inputs(wl)
+    r = np.random.default_rng(83)
+    g = torch.from_numpy(r.standard_normal((1, 2, 150, 128))).to(torch.bfloat16)
+    nw = torch.from_numpy(1.0 + 0.1 * r.standard_normal((2, 128))).float()
+    dy = torch.from_numpy(r.standard_normal((1, 150, 2, 128))).float()
+    d = dev(x)
+    o_keep = torch.empty(1, 2, 150, 128, device=DEV)
+    y, sT = gdr.gdr_chunk_fwd_gated(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], g.to(DEV),
+                                    gamma=d["gamma"], z=d["z"], S0=d["S0"], norm_weight=nw.to(DEV), eps=1e-6,
+                                    chunk=64, o=o_keep)
+    o_plain, _ = gdr.gdr_chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"],
+                                   gamma=d["gamma"], z=d["z"], S0=d["S0"], chunk=64)
+    torch.cuda.synchronize()
+    assert torch.equal(o_keep, o_plain)
+    og = gdr.gdr_output_gate_bwd(o_keep, g.to(DEV), dy.to(DEV), nw.to(DEV), eps=1e-6)
+    gb = gdr.gdr_chunk_bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], og["d_o"],
+                           gamma=d["gamma"], z=d["z"], S0=d["S0"])
+    torch.cuda.synchronize()
+    ro, _ = oracle_run(x)
+    do_ref, dg_ref, dw_ref = oracle.output_gate_backward(ro, g.float(), dy, norm_weight=nw, eps=1e-6)
+    ref = oracle.backward(x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"], torch.from_numpy(do_ref),
+                          gamma=x["gamma"], z=x["z"], S0=x["S0"])
+    check("layer bwd dg", og["dg"].cpu().numpy(), dg_ref, TOL_BF16)
+    check("layer bwd d_norm_weight", og["d_norm_weight"].cpu().numpy(), dw_ref, TOL_BF16)
+    for key in ("dq", "dk", "dv", "dlog_alpha", "db", "dw", "dz", "dgamma", "dS0"):
+        check(f"layer bwd {key}", gb[key].cpu().numpy(), ref[key], TOL_BF16)
