@@ -217,8 +217,8 @@ gdr_status bwd_call(const gdr_desc *desc, int nseq, const int *cu, const void *q
   a.dgamma = gamma ? dgamma : nullptr;
   a.ctab = nullptr; a.ctab_len = 0;
   // chunk slots: the token chunks of a uniform batch, or the (bounded) chunk
-  // list of a packed one
-  const bool chunks = nseq > 0 || a.NC > 0;
+  // list of a packed one; none without tokens (then dS0 = dS_T, dgamma = 0)
+  const bool chunks = d.T > 0 && (nseq > 0 || a.NC > 0);
   hipError_t e = hipSuccess;
   if (chunks) gdr::bwd_workspace(&a, &f, workspace, d.B, d.H, d.T, d.dk, ns, nseq);
   // the chain of chunk-end state gradients, last chunk to first (the final

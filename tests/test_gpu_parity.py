@@ -1107,3 +1107,17 @@ def test_gated_forward_keeps_o_and_layer_backward_chain():
     check("layer bwd d_norm_weight", og["d_norm_weight"].cpu().numpy(), dw_ref, TOL_BF16)
     for key in ("dq", "dk", "dv", "dlog_alpha", "db", "dw", "dz", "dgamma", "dS0"):
         check(f"layer bwd {key}", gb[key].cpu().numpy(), ref[key], TOL_BF16)
+
+
+def test_backward_varlen_all_sequences_empty():
+    """A packed batch whose sequences are all empty (T = 0): dS0 = dS_T per
+    sequence, dgamma = 0, nothing else touched."""
+    x, cu = packed_inputs("gdn2", [0, 0, 0])
+    d = dev(x)
+    dST = torch.randn(3, 2, 128, 128, device=DEV)
+    g = gdr.gdr_chunk_bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"],
+                          torch.empty(1, 2, 0, 128, device=DEV), gamma=d["gamma"], z=d["z"], S0=d["S0"],
+                          dS_T=dST, cu_seqlens=torch.from_numpy(cu).to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(g["dS0"], dST)
+    assert torch.count_nonzero(g["dgamma"]) == 0
