@@ -968,8 +968,10 @@ __global__ void __launch_bounds__(256) bwd_dgamma_kernel(BwdArgs a) {
   const int ch = (blockIdx.x % (D / 32)) * 32 + cl;
   float s = 0.f;
   if (a.ctab) {  // packed batch: slots entry * H + h (entries past the end hold zeros)
+#pragma unroll 8
     for (int k = j; k < a.ctab_len; k += 8) s += a.gpart[((size_t)k * a.H + h) * D + ch];
   } else {
+#pragma unroll 8
     for (int k = j; k < a.B * a.NC; k += 8) {
       const int b = k / a.NC, c = k % a.NC;
       s += a.gpart[((size_t)(b * a.H + h) * a.NC + c) * D + ch];
@@ -1065,6 +1067,7 @@ __global__ void __launch_bounds__(256) out_gate_dw_kernel(OgBwdArgs a) {
   const int h = blockIdx.x / (D / 32), cl = threadIdx.x & 31, j = threadIdx.x >> 5;
   const int ch = (blockIdx.x % (D / 32)) * 32 + cl;
   float s = 0.f;
+#pragma unroll 8
   for (int k = j; k < a.B * a.ntb; k += 8) s += a.part[((size_t)k * a.H + h) * D + ch];
   part[j][cl] = s;
   __syncthreads();
