@@ -940,7 +940,7 @@ __device__ __forceinline__ void chain_run(const ChunkArgs &a, int id, ChainLds<D
   size_t slot0, slot_step;
   if (a.ctab) {  // packed batch: stream = sequence * H + head, slot = entry * H + head
     const int n = (int)(bh / a.H);
-    NC = (max(a.cu[n + 1] - a.cu[n], 0) + C - 1) / C;
+    NC = a.coff[n + 1] - a.coff[n];  // the sequence's entries of the chunk list
     slot0 = (size_t)a.coff[n] * a.H + bh % a.H;
     slot_step = a.H;
   } else {
@@ -1208,45 +1208,58 @@ __global__ void __launch_bounds__(64 * (C / 16)) chunk_out_kernel(ChunkArgs a) {
 // counts ceil(len_n / C) of the sequences (1024 at a time), writes the
 // offsets coff[0..nseq] and, per sequence, its entries {n, c, first packed
 // row, valid tokens}; entries past the last chunk get sequence -1.
+// The offsets are read defensively: each is clamped to [0, T] and the end of
+// a sequence to no less than its start, and no entry is written at or past
+// ctab_len (coff is capped there too), so offsets that break the documented
+// contract give wrong results but never an access outside the tensors or
+// the workspace.  Sequence n owns the coff[n + 1] - coff[n] entries from
+// coff[n] on: ceil(len_n / C) whenever the offsets are valid.
 // ============================================================================
 template <int C>
 __global__ void __launch_bounds__(1024) chunk_table_kernel(ChunkArgs a) {
-  __shared__ int wsum[16];
-  __shared__ int carry;
+  __shared__ long long wsum[16];
+  __shared__ long long carry;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const long long cap = a.ctab_len;
   if (tid == 0) carry = 0;
   __syncthreads();
   for (int base = 0; base <= a.nseq; base += 1024) {
     const int n = base + tid;
-    int len = 0, cnt = 0;
+    int len = 0, r0 = 0;
+    long long cnt = 0;
     if (n < a.nseq) {
-      len = max(a.cu[n + 1] - a.cu[n], 0);
+      r0 = min(max(a.cu[n], 0), a.T);
+      const int r1 = min(max(a.cu[n + 1], r0), a.T);
+      len = r1 - r0;
       cnt = (len + C - 1) / C;
     }
-    int x = cnt;  // inclusive scan within the wave
+    long long x = cnt;  // inclusive scan within the wave
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
-      const int y = __shfl_up(x, d, 64);
+      const long long y = __shfl_up(x, d, 64);
       if (lane >= d) x += y;
     }
     if (lane == 63) wsum[wave] = x;
     __syncthreads();
     if (tid == 0) {  // wave totals -> exclusive offsets of the waves
-      int acc = 0;
-      for (int w = 0; w < 16; ++w) { const int t = wsum[w]; wsum[w] = acc; acc += t; }
+      long long acc = 0;
+      for (int w = 0; w < 16; ++w) { const long long t = wsum[w]; wsum[w] = acc; acc += t; }
     }
     __syncthreads();
-    const int excl = carry + wsum[wave] + x - cnt;  // chunks before sequence n
-    if (n <= a.nseq) a.coff[n] = excl;
+    const long long excl = carry + wsum[wave] + x - cnt;  // chunks before sequence n
+    if (n <= a.nseq) a.coff[n] = (int)min(excl, cap);
     if (n < a.nseq) {
-      const int r0 = a.cu[n];
-      for (int c = 0; c < cnt; ++c) a.ctab[excl + c] = make_int4(n, c, r0 + c * C, min(C, len - c * C));
+      const long long stop = min(excl + cnt, cap);
+      for (long long j = excl; j < stop; ++j) {
+        const int c = (int)(j - excl);
+        a.ctab[j] = make_int4(n, c, r0 + c * C, min(C, len - c * C));
+      }
     }
     __syncthreads();
     if (tid == 1023) carry = excl + cnt;  // running total after this block of sequences
     __syncthreads();
   }
-  for (int j = carry + tid; j < a.ctab_len; j += 1024) a.ctab[j] = make_int4(-1, 0, 0, 0);
+  for (long long j = min(carry, cap) + tid; j < cap; j += 1024) a.ctab[j] = make_int4(-1, 0, 0, 0);
 }
 
 // ============================================================================

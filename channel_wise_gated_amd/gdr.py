@@ -182,6 +182,85 @@ def _contig(t):
     return t
 
 
+# ----------------------------------------------------------------- validation
+# Every tensor argument is checked before anything is launched: its shape
+# against the call's sizes, its dtype against what the kernels read it as,
+# its layout, and its device.  The C ABI checks pointers, sizes and
+# alignment, but a pointer carries neither a dtype nor an extent.
+_FLOAT = (torch.bfloat16, torch.float32)
+_F32 = (torch.float32,)
+
+
+def _req(t, name, shape, dtypes):
+    """A required tensor argument: exact shape, one of `dtypes`, contiguous."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {' or '.join(str(d) for d in dtypes)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _opt(t, name, shape, dtypes):
+    """An optional tensor argument (None passes)."""
+    return None if t is None else _req(t, name, shape, dtypes)
+
+
+def _rank(t, name, ndim):
+    if not isinstance(t, torch.Tensor) or t.dim() != ndim:
+        raise ValueError(f"{name} must be a {ndim}-d tensor")
+    return t
+
+
+def _gate_arg(g, name, full_shape, dtypes):
+    """(mode, tensor) of a gate given per channel (full_shape), per token
+    (full_shape without its last dim) or as the scalar 1 / 0 / None."""
+    mode, t = _gate(g, len(full_shape), name)
+    if t is not None:
+        _req(t, name, full_shape if mode == PER_CHANNEL else full_shape[:-1], dtypes)
+    return mode, t
+
+
+def _log_alpha_arg(la, full_shape):
+    if isinstance(la, (int, float)):
+        if la != 0:
+            raise ValueError("scalar log_alpha must be 0")
+        return ONES, None
+    if la is None:
+        raise ValueError("log_alpha must be a tensor or 0")
+    return _gate_arg(la, "log_alpha", full_shape, _F32)
+
+
+def _same_device(ref, named):
+    """Every tensor on the GPU device of `ref`."""
+    if ref.device.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU device, not {ref.device}")
+    for name, t in named.items():
+        if isinstance(t, torch.Tensor) and t.device != ref.device:
+            raise ValueError(f"{name} is on {t.device}, expected {ref.device}")
+
+
+def _workspace_arg(ws, need, device):
+    if ws is None:
+        return torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    if not isinstance(ws, torch.Tensor) or ws.dtype != torch.uint8 or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor")
+    if ws.numel() < need:
+        raise ValueError(f"workspace holds {ws.numel()} bytes, {need} needed")
+    return ws
+
+
+def _cu_seqlens_arg(cu, T):
+    if not isinstance(cu, torch.Tensor) or cu.dtype != torch.int32 or cu.dim() != 1 or cu.numel() < 2:
+        raise ValueError("cu_seqlens must be a 1-d int32 tensor of N + 1 offsets")
+    if not cu.is_contiguous():
+        raise ValueError("cu_seqlens must be contiguous")
+    return cu
+
+
 class ChunkCall:
     """Marshalled arguments of one chunkwise forward (pointers, descriptor,
     outputs and workspace), so that the call -- or either of its two phases --
@@ -189,28 +268,36 @@ class ChunkCall:
 
     def __init__(self, q, k, v, log_alpha, b, w, gamma=None, z=None, S0=None, *, chunk=64,
                  out_dtype=torch.float32, normalize_qk=True, scale=1.0, o=None, S_T=None,
-                 workspace=None):
-        q, k, v, z, gamma, S0 = map(_contig, (q, k, v, z, gamma, S0))
-        B, H, T, dk = q.shape
-        dv = v.shape[-1]
-        if isinstance(log_alpha, (int, float)):
-            if log_alpha != 0:
-                raise ValueError("scalar log_alpha must be 0")
-            amode, la = ONES, None
-        else:
-            amode, la = _gate(_contig(log_alpha), 4, "log_alpha")
-        bmode, bt = _gate(_contig(b), 4, "b")
-        wmode, wt = _gate(_contig(w), 4, "w")
+                 workspace=None, _gated=False):
+        B, H, T, dk = _rank(q, "q", 4).shape
+        dv = _rank(v, "v", 4).shape[-1]
+        dt = (_req(q, "q", (B, H, T, dk), _FLOAT).dtype,)
+        _req(k, "k", (B, H, T, dk), dt)
+        _req(v, "v", (B, H, T, dv), dt)
+        amode, la = _log_alpha_arg(log_alpha, (B, H, T, dk))
+        bmode, bt = _gate_arg(b, "b", (B, H, T, dk), dt)
+        wmode, wt = _gate_arg(w, "w", (B, H, T, dv), dt)
+        _opt(gamma, "gamma", (H, dk), _F32)
+        _opt(z, "z", (B, H, T, dk), dt)
+        _opt(S0, "S0", (B, H, dk, dv), _F32)
+        if out_dtype not in _FLOAT:
+            raise ValueError("out_dtype must be torch.bfloat16 or torch.float32")
+        if not _gated:
+            _opt(o, "o", (B, H, T, dv), (out_dtype,))
+        _opt(S_T, "S_T", (B, H, dk, dv), _F32)
         od = GDR_BF16 if out_dtype == torch.bfloat16 else GDR_F32
         self.desc = make_desc(B, H, T, dk, dv, chunk, _dtype_code(q), od, int(bool(normalize_qk)),
                               scale, amode, bmode, wmode)
+        need = gdr_chunk_fwd_workspace_size(self.desc)
+        if workspace is not None:
+            _workspace_arg(workspace, need, q.device)
+        _same_device(q, dict(k=k, v=v, log_alpha=la, b=bt, w=wt, gamma=gamma, z=z, S0=S0, o=o, S_T=S_T,
+                             workspace=workspace))
         if o is None:
             o = torch.empty((B, H, T, dv), dtype=out_dtype, device=q.device)
         if S_T is None:
             S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
-        need = gdr_chunk_fwd_workspace_size(self.desc)
-        if workspace is None:
-            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        workspace = _workspace_arg(workspace, need, q.device)
         self.o, self.S_T, self.workspace = o, S_T, workspace
         self._keep = (q, k, v, la, bt, wt, gamma, z, S0)   # keep the inputs alive
         self.ptrs = [_ptr(t) for t in self._keep]
@@ -270,11 +357,15 @@ def gdr_chunk_fwd_gated(q, k, v, log_alpha, b, w, g, gamma=None, z=None, S0=None
     """
     lib = load()
     call = ChunkCall(q, k, v, log_alpha, b, w, gamma, z, S0, chunk=chunk, out_dtype=out_dtype,
-                     normalize_qk=normalize_qk, scale=scale, o=torch.empty(0, device=q.device),
-                     S_T=S_T, workspace=workspace)
-    g, norm_weight = _contig(g), _contig(norm_weight)
+                     normalize_qk=normalize_qk, scale=scale, o=None, S_T=S_T, workspace=workspace,
+                     _gated=True)
     B, H, T, _ = q.shape
     dv = v.shape[-1]
+    _req(g, "g", (B, H, T, dv), (q.dtype,))
+    _opt(norm_weight, "norm_weight", (H, dv), _F32)
+    _opt(y, "y", (B, T, H, dv), (out_dtype,))
+    _opt(o, "o", (B, H, T, dv), _F32)
+    _same_device(q, dict(g=g, norm_weight=norm_weight, y=y, o=o))
     if y is None:
         y = torch.empty((B, T, H, dv), dtype=out_dtype, device=q.device)
     S0p, _, sTp = call.out_ptrs
@@ -310,16 +401,29 @@ def gdr_gate_proj(x, w_down, w_up, bias, ranks, H, d, *, out_dtype=torch.bfloat1
     into `outs` (same keys) when given.
     """
     lib = load()
-    x, w_down, bias = _contig(x), _contig(w_down), _contig(bias)
-    B, T, dm = x.shape
+    B, T, dm = _rank(x, "x", 3).shape
+    bf = (torch.bfloat16,)
+    _req(x, "x", (B, T, dm), bf)
+    if len(ranks) != 5:
+        raise ValueError("ranks: five gate ranks (f, b, g, w, q)")
+    R = sum(int(r) for r in ranks)
+    _req(w_down, "w_down", (R, dm), bf)
+    if isinstance(w_up, torch.Tensor):
+        wu = _req(w_up, "w_up", (H * d * R,), bf)
+    else:
+        for name, r in zip(GATE_ORDER, ranks):
+            _req(w_up.get(name), f"w_up['{name}']", (H * d, int(r)), bf)
+        wu = pack_gate_up(w_up)
+    _opt(bias, "bias", (5, H * d), _F32)
+    if out_dtype not in _FLOAT:
+        raise ValueError("out_dtype must be torch.bfloat16 or torch.float32")
+    _same_device(x, dict(w_down=w_down, w_up=wu, bias=bias, workspace=workspace))
     desc = make_gate_desc(B, T, dm, H, d, ranks, GDR_BF16 if out_dtype == torch.bfloat16 else GDR_F32)
-    wu = _contig(w_up) if isinstance(w_up, torch.Tensor) else pack_gate_up(w_up)
     n = ctypes.c_size_t(0)
     rc = lib.gdr_gate_proj_workspace_size(ctypes.byref(desc), ctypes.byref(n))
     if rc != GDR_OK:
         raise GdrError(rc, "gdr_gate_proj_workspace_size")
-    if workspace is None:
-        workspace = torch.empty(max(int(n.value), 1), dtype=torch.uint8, device=x.device)
+    workspace = _workspace_arg(workspace, int(n.value), x.device)
     if outs is not None:
         gates = tuple(outs)
         for name, t in outs.items():
@@ -362,35 +466,38 @@ def gdr_chunk_bwd(q, k, v, log_alpha, b, w, dO, gamma=None, z=None, S0=None, dS_
     if unknown:
         raise ValueError(f"unknown outputs {sorted(unknown)}")
     lib = load()
-    q, k, v, z, gamma, S0, dO, dS_T = map(_contig, (q, k, v, z, gamma, S0, dO, dS_T))
-    B, H, T, dk = q.shape
-    dv = v.shape[-1]
-    if isinstance(log_alpha, (int, float)):
-        if log_alpha != 0:
-            raise ValueError("scalar log_alpha must be 0")
-        amode, la = ONES, None
-    else:
-        amode, la = _gate(_contig(log_alpha), 4, "log_alpha")
-    bmode, bt = _gate(_contig(b), 4, "b")
-    wmode, wt = _gate(_contig(w), 4, "w")
-    if tuple(dO.shape) != (B, H, T, dv):
-        raise ValueError("dO must be [B,H,T,dv]")
+    B, H, T, dk = _rank(q, "q", 4).shape
+    dv = _rank(v, "v", 4).shape[-1]
+    dt = (_req(q, "q", (B, H, T, dk), _FLOAT).dtype,)
+    _req(k, "k", (B, H, T, dk), dt)
+    _req(v, "v", (B, H, T, dv), dt)
+    amode, la = _log_alpha_arg(log_alpha, (B, H, T, dk))
+    bmode, bt = _gate_arg(b, "b", (B, H, T, dk), dt)
+    wmode, wt = _gate_arg(w, "w", (B, H, T, dv), dt)
+    nseq = 0
+    if cu_seqlens is not None:
+        cu_seqlens = _cu_seqlens_arg(cu_seqlens, T)
+        nseq = cu_seqlens.numel() - 1
+        if B != 1:
+            raise ValueError("a packed batch (cu_seqlens) has B = 1")
+    _opt(gamma, "gamma", (H, dk), _F32)
+    _opt(z, "z", (B, H, T, dk), dt)
+    _opt(S0, "S0", (nseq or B, H, dk, dv), _F32)
+    _req(dO, "dO", (B, H, T, dv), _FLOAT)
+    _opt(dS_T, "dS_T", (nseq or B, H, dk, dv), _F32)
+    _same_device(q, dict(k=k, v=v, log_alpha=la, b=bt, w=wt, gamma=gamma, z=z, S0=S0, dO=dO, dS_T=dS_T,
+                         cu_seqlens=cu_seqlens, workspace=workspace))
     od = GDR_BF16 if dO.dtype == torch.bfloat16 else GDR_F32
     desc = make_desc(B, H, T, dk, dv, 64, _dtype_code(q), od, int(bool(normalize_qk)), scale, amode, bmode, wmode)
     n = ctypes.c_size_t(0)
-    nseq = 0
-    if cu_seqlens is not None:
-        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
-            raise ValueError("cu_seqlens must be a 1-D int32 tensor of N + 1 offsets")
-        nseq = cu_seqlens.numel() - 1
+    if nseq:
         rc = lib.gdr_chunk_bwd_varlen_workspace_size(ctypes.byref(desc), nseq, ctypes.byref(n))
     else:
         rc = lib.gdr_chunk_bwd_workspace_size(ctypes.byref(desc), ctypes.byref(n))
     if rc != GDR_OK:
         raise GdrError(rc, "gdr_chunk_bwd_workspace_size")
     dev = q.device
-    if workspace is None:
-        workspace = torch.empty(max(int(n.value), 1), dtype=torch.uint8, device=dev)
+    workspace = _workspace_arg(workspace, int(n.value), dev)
     f32 = dict(dtype=torch.float32, device=dev)
     gshape = lambda mode, d: (B, H, T, d) if mode == PER_CHANNEL else ((B, H, T) if mode == PER_TOKEN else None)
     out = {"dq": torch.empty(B, H, T, dk, **f32), "dk": torch.empty(B, H, T, dk, **f32),
@@ -424,17 +531,21 @@ def gdr_decode_step(S, q, k, v, log_alpha, b, w, gamma=None, z=None, *, out_dtyp
     channel [B,H,d], per token [B,H] or the scalars 1 / 0.
     """
     lib = load()
-    S, q, k, v, z, gamma = map(_contig, (S, q, k, v, z, gamma))
-    B, H, dk = q.shape
-    dv = v.shape[-1]
-    if isinstance(log_alpha, (int, float)):
-        if log_alpha != 0:
-            raise ValueError("scalar log_alpha must be 0")
-        amode, la = ONES, None
-    else:
-        amode, la = _gate(_contig(log_alpha), 3, "log_alpha")
-    bmode, bt = _gate(_contig(b), 3, "b")
-    wmode, wt = _gate(_contig(w), 3, "w")
+    B, H, dk = _rank(q, "q", 3).shape
+    dv = _rank(v, "v", 3).shape[-1]
+    dt = (_req(q, "q", (B, H, dk), _FLOAT).dtype,)
+    _req(k, "k", (B, H, dk), dt)
+    _req(v, "v", (B, H, dv), dt)
+    _req(S, "S", (B, H, dk, dv), _F32)
+    amode, la = _log_alpha_arg(log_alpha, (B, H, dk))
+    bmode, bt = _gate_arg(b, "b", (B, H, dk), dt)
+    wmode, wt = _gate_arg(w, "w", (B, H, dv), dt)
+    _opt(gamma, "gamma", (H, dk), _F32)
+    _opt(z, "z", (B, H, dk), dt)
+    if out_dtype not in _FLOAT:
+        raise ValueError("out_dtype must be torch.bfloat16 or torch.float32")
+    _opt(o, "o", (B, H, dv), (out_dtype,))
+    _same_device(q, dict(S=S, k=k, v=v, log_alpha=la, b=bt, w=wt, gamma=gamma, z=z, o=o))
     od = GDR_BF16 if out_dtype == torch.bfloat16 else GDR_F32
     desc = make_desc(B, H, 1, dk, dv, 64, _dtype_code(q), od, int(bool(normalize_qk)), scale,
                      amode, bmode, wmode)
@@ -467,31 +578,36 @@ def gdr_chunk_fwd_varlen(q, k, v, log_alpha, b, w, cu_seqlens, gamma=None, z=Non
     Returns (o [1,H,T,dv], S_T [N,H,dk,dv]).
     """
     lib = load()
-    q, k, v, z, gamma, S0 = map(_contig, (q, k, v, z, gamma, S0))
-    cu = _contig(cu_seqlens)
-    if cu.dtype != torch.int32 or cu.dim() != 1 or not cu.is_cuda:
-        raise ValueError("cu_seqlens must be a 1-d int32 device tensor")
+    Bq, H, T, dk = _rank(q, "q", 4).shape
+    dv = _rank(v, "v", 4).shape[-1]
+    if Bq != 1:
+        raise ValueError("a packed batch has B = 1")
+    dt = (_req(q, "q", (Bq, H, T, dk), _FLOAT).dtype,)
+    cu = _cu_seqlens_arg(cu_seqlens, T)
     n_seqs = cu.numel() - 1
-    Bq, H, T, dk = q.shape
-    dv = v.shape[-1]
-    if isinstance(log_alpha, (int, float)):
-        if log_alpha != 0:
-            raise ValueError("scalar log_alpha must be 0")
-        amode, la = ONES, None
-    else:
-        amode, la = _gate(_contig(log_alpha), 4, "log_alpha")
-    bmode, bt = _gate(_contig(b), 4, "b")
-    wmode, wt = _gate(_contig(w), 4, "w")
+    _req(k, "k", (Bq, H, T, dk), dt)
+    _req(v, "v", (Bq, H, T, dv), dt)
+    amode, la = _log_alpha_arg(log_alpha, (Bq, H, T, dk))
+    bmode, bt = _gate_arg(b, "b", (Bq, H, T, dk), dt)
+    wmode, wt = _gate_arg(w, "w", (Bq, H, T, dv), dt)
+    _opt(gamma, "gamma", (H, dk), _F32)
+    _opt(z, "z", (Bq, H, T, dk), dt)
+    _opt(S0, "S0", (n_seqs, H, dk, dv), _F32)
+    if out_dtype not in _FLOAT:
+        raise ValueError("out_dtype must be torch.bfloat16 or torch.float32")
+    _opt(o, "o", (Bq, H, T, dv), (out_dtype,))
+    _opt(S_T, "S_T", (n_seqs, H, dk, dv), _F32)
+    _same_device(q, dict(cu_seqlens=cu, k=k, v=v, log_alpha=la, b=bt, w=wt, gamma=gamma, z=z, S0=S0, o=o,
+                         S_T=S_T, workspace=workspace))
     od = GDR_BF16 if out_dtype == torch.bfloat16 else GDR_F32
     desc = make_desc(Bq, H, T, dk, dv, chunk, _dtype_code(q), od, int(bool(normalize_qk)), scale,
                      amode, bmode, wmode)
     if o is None:
         o = torch.empty((Bq, H, T, dv), dtype=out_dtype, device=q.device)
     if S_T is None:
-        S_T = torch.empty((max(n_seqs, 0), H, dk, dv), dtype=torch.float32, device=q.device)
+        S_T = torch.empty((n_seqs, H, dk, dv), dtype=torch.float32, device=q.device)
     need = gdr_chunk_fwd_varlen_workspace_size(desc, n_seqs)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    workspace = _workspace_arg(workspace, need, q.device)
     ptrs = [_ptr(t) for t in (q, k, v, la, bt, wt, gamma, z)]
     rc = lib.gdr_chunk_fwd_varlen(ctypes.byref(desc), n_seqs, _ptr(cu), *ptrs, _ptr(S0), _ptr(o),
                                   _ptr(S_T), _ptr(workspace), workspace.numel(), _stream(stream))
@@ -508,12 +624,12 @@ def gdr_output_gate_bwd(o, g, dy, norm_weight=None, eps=1e-6, *, stream=None) ->
     dg [B,H,T,dv] and d_norm_weight [H,dv] (None without a weight).
     """
     lib = load()
-    o, g, dy, norm_weight = map(_contig, (o, g, dy, norm_weight))
-    if o.dtype != torch.float32:
-        raise ValueError("o must be fp32")
-    B, H, T, dv = o.shape
-    if tuple(g.shape) != (B, H, T, dv) or tuple(dy.shape) != (B, T, H, dv):
-        raise ValueError("g must be [B,H,T,dv] and dy [B,T,H,dv]")
+    B, H, T, dv = _rank(o, "o", 4).shape
+    _req(o, "o", (B, H, T, dv), _F32)
+    _req(g, "g", (B, H, T, dv), _FLOAT)
+    _req(dy, "dy", (B, T, H, dv), _FLOAT)
+    _opt(norm_weight, "norm_weight", (H, dv), _F32)
+    _same_device(o, dict(g=g, dy=dy, norm_weight=norm_weight))
     desc = make_desc(B, H, T, dv, dv, 64, _dtype_code(g), GDR_BF16 if dy.dtype == torch.bfloat16 else GDR_F32,
                      1, 1.0, PER_CHANNEL, PER_CHANNEL, PER_CHANNEL)
     f32 = dict(dtype=torch.float32, device=o.device)

@@ -236,21 +236,6 @@ gdr_status gdr_chunk_bwd(const gdr_desc *desc, const void *q, const void *k, con
                          size_t workspace_bytes, void *stream);
 
 /*
- * Backward of gdr_chunk_fwd_varlen: the gradients of a packed batch of n_seqs
- * sequences (each with its own S0 and S_T), the reverse of the recurrence of
- * gdr_chunk_bwd run per sequence and head.  Layouts as gdr_chunk_fwd_varlen:
- * desc->B must be 1 and desc->T = cu_seqlens[n_seqs]; every per-token tensor
- * (inputs, dO and the per-token gradients) is [1,H,T,...] over the packed
- * tokens; S0, dS_T and dS0 are [n_seqs,H,dk,dv]; dgamma [H,dk] sums over all
- * sequences.  cu_seqlens (device, int32, n_seqs + 1 non-decreasing offsets from
- * 0) is read on the device; sequences of length 0 pass dS_T to dS0.
- *   workspace  >= gdr_chunk_bwd_varlen_workspace_size(desc, n_seqs) bytes,
- *              256-byte aligned
- * Validation as gdr_chunk_bwd, plus n_seqs >= 1, desc->B == 1 and cu_seqlens
- * non-null and 4-byte aligned (GDR_ERR_INVALID_ARG); the offsets themselves
- * are the caller's contract.
- */
-/*
  * Backward of the output gate of gdr_chunk_fwd_gated (Muir reading notes,
  * section 2.1: per-head RMSNorm of o, then the output gate g per channel; the
  * library's reading y = o / sqrt(mean_c o^2 + eps) * norm_weight *
@@ -281,6 +266,21 @@ gdr_status gdr_output_gate_bwd(const gdr_desc *desc, const float *o, const void 
                                float *dg, float *d_norm_weight, void *workspace,
                                size_t workspace_bytes, void *stream);
 
+/*
+ * Backward of gdr_chunk_fwd_varlen: the gradients of a packed batch of n_seqs
+ * sequences (each with its own S0 and S_T), the reverse of the recurrence of
+ * gdr_chunk_bwd run per sequence and head.  Layouts as gdr_chunk_fwd_varlen:
+ * desc->B must be 1 and desc->T = cu_seqlens[n_seqs]; every per-token tensor
+ * (inputs, dO and the per-token gradients) is [1,H,T,...] over the packed
+ * tokens; S0, dS_T and dS0 are [n_seqs,H,dk,dv]; dgamma [H,dk] sums over all
+ * sequences.  cu_seqlens (device, int32, n_seqs + 1 non-decreasing offsets from
+ * 0) is read on the device; sequences of length 0 pass dS_T to dS0.
+ *   workspace  >= gdr_chunk_bwd_varlen_workspace_size(desc, n_seqs) bytes,
+ *              256-byte aligned
+ * Validation as gdr_chunk_bwd, plus n_seqs >= 1, desc->B == 1 and cu_seqlens
+ * non-null and 4-byte aligned (GDR_ERR_INVALID_ARG); the offsets themselves
+ * are the caller's contract, read as gdr_chunk_fwd_varlen reads them.
+ */
 gdr_status gdr_chunk_bwd_varlen_workspace_size(const gdr_desc *desc, int n_seqs, size_t *bytes);
 gdr_status gdr_chunk_bwd_varlen(const gdr_desc *desc, int n_seqs, const int *cu_seqlens,
                                 const void *q, const void *k, const void *v,
@@ -326,8 +326,11 @@ gdr_status gdr_chunk_fwd_scan(const gdr_desc *desc, const float *S0, void *o, fl
  *
  *   desc->B     must be 1; desc->T = total packed tokens = cu_seqlens[n_seqs]
  *   cu_seqlens  device int32 [n_seqs + 1]: cu_seqlens[0] = 0, nondecreasing,
- *               last = desc->T (a precondition, not checked on the device);
- *               a sequence may be empty
+ *               last = desc->T; a sequence may be empty.  A precondition:
+ *               offsets that break it give undefined results, but the device
+ *               clamps every offset to [0, T] and each sequence's end to no
+ *               less than its start, and writes no chunk entry past the
+ *               workspace's list, so they cause no access out of bounds
  *   q, k, v, log_alpha, b, w, z, o   as gdr_chunk_fwd with B = 1 (packed)
  *   gamma       [H,dk] fp32 or NULL
  *   S0, S_T     [n_seqs,H,dk,dv] fp32 or NULL; S_T may alias S0

@@ -310,3 +310,50 @@ def test_output_gate_bwd_workspace_and_validation():
     assert call(eps=float("nan")) == gdr.GDR_ERR_INVALID_ARG
     assert call(ws=None) == gdr.GDR_ERR_WORKSPACE
     assert call(nbytes=1024) == gdr.GDR_ERR_WORKSPACE
+
+
+# ---------------------------------------------------------------- chunk list of a packed batch
+def chunk_table_model(cu, T, C, cap):
+    """The device chunk-list builder of a packed batch, step for step on the
+    host: offsets clamped to [0, T], a sequence's end to no less than its
+    start, entries written only below `cap` (the list's length in the
+    workspace, ceil(T / C) + n_seqs) and the offsets capped there too.
+    Returns (coff, writes) with writes = [(index, n, c, row, valid)]."""
+    nseq = len(cu) - 1
+    coff, writes, excl = [], [], 0
+    for n in range(nseq + 1):
+        cnt, r0, ln = 0, 0, 0
+        if n < nseq:
+            r0 = min(max(cu[n], 0), T)
+            r1 = min(max(cu[n + 1], r0), T)
+            ln = r1 - r0
+            cnt = (ln + C - 1) // C
+        coff.append(min(excl, cap))
+        for j in range(excl, min(excl + cnt, cap)):
+            c = j - excl
+            writes.append((j, n, c, r0 + c * C, min(C, ln - c * C)))
+        excl += cnt
+    return coff, writes
+
+
+@pytest.mark.parametrize("cu", [
+    [0, 10, 300, 300, 1000],                 # valid
+    [0, 900, 100, 1000],                     # decreasing offsets
+    [0, 5000, 1000],                         # past T
+    [-50, 40, -7, 1000],                     # negative offsets
+    [0, 1000, 0, 1000, 0, 1000, 0, 1000],    # overlapping: more chunks than the list holds
+])
+def test_chunk_table_logic_stays_in_bounds(cu):
+    T, C = 1000, 64
+    cap = (T + C - 1) // C + len(cu) - 1
+    coff, writes = chunk_table_model(cu, T, C, cap)
+    assert all(0 <= a <= b <= cap for a, b in zip(coff, coff[1:]))
+    for j, n, c, row, valid in writes:
+        assert 0 <= j < cap and 1 <= valid <= C and 0 <= row and row + valid <= T
+        assert coff[n] <= j < coff[n + 1]           # the chain walks exactly these entries
+    if cu == sorted(cu) and 0 <= cu[0] and cu[-1] <= T:
+        # valid offsets: every token is covered once, in sequence order
+        cover = sorted((row, valid) for _, _, _, row, valid in writes)
+        assert sum(v for _, v in cover) == cu[-1] - cu[0]
+        assert all(coff[n + 1] - coff[n] == -(-(cu[n + 1] - cu[n]) // C) for n in range(len(cu) - 1))
+

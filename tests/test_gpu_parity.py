@@ -630,10 +630,10 @@ def test_ill_conditioned_chunk_system(chunk, dtype):
     o, sT = gpu_chunk(x, chunk)
     ro, rs = oracle_run(x)
     print(f"cond(I+L) = {cond:.3e}", flush=True)
-    # the bf16-input bar for both modes: fp32 mode's 1e-5 is stated for
-    # well-conditioned systems (the Muir notes report ~1e-6 there)
-    check(f"ill-conditioned C{chunk} {dtype} o", o, ro, TOL_BF16)
-    check(f"ill-conditioned C{chunk} {dtype} S_T", sT, rs, TOL_BF16)
+    # each mode's own bar, whatever the conditioning
+    tol = TOL_BF16 if dtype == "bf16" else TOL_F32
+    check(f"ill-conditioned C{chunk} {dtype} o", o, ro, tol)
+    check(f"ill-conditioned C{chunk} {dtype} S_T", sT, rs, tol)
 
 
 def test_gate_modes_and_options():
@@ -662,8 +662,10 @@ def test_gate_modes_and_options():
                               scale=0.125, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     ro, rs = oracle_run(y, normalize_qk=False, scale=0.125)
-    # bf16 storage of o alone costs ~1.7e-3 relative L2; the state stays fp32
-    check("raw qk, scale, bf16 o", o.float().cpu().numpy(), ro, 3e-3)
+    # a bf16 o against the oracle's o rounded to bf16 (the rounding of the
+    # stored output is not the path's error); the state stays fp32
+    ro16 = torch.from_numpy(ro).to(torch.bfloat16).double().numpy()
+    check("raw qk, scale, bf16 o (vs oracle rounded to bf16)", o.float().cpu().numpy(), ro16, TOL_BF16)
     check("raw qk, scale S_T", sT.cpu().numpy(), rs, TOL_BF16)
 
 
