@@ -76,15 +76,20 @@ struct OutGate {
   float *o;  // optional: o before the norm and gate (fp32)
 };
 
+// seg > 0: a whole call of a uniform batch in segments of `seg` chunks per
+// stream, over a workspace laid out for that many chunks per stream.
 gdr_status chunk_call(const gdr_desc *desc, int nseq, const int *cu, const void *q, const void *k,
                       const void *v, const float *log_alpha, const void *b, const void *w,
                       const float *gamma, const void *z, const float *S0, void *o, float *S_T,
                       void *workspace, size_t workspace_bytes, void *stream, int phases,
-                      const OutGate *og = nullptr) {
+                      const OutGate *og = nullptr, int seg = 0) {
   size_t need = 0;
   gdr_status s = chunk_plan(desc, nseq, &need);
   if (s != GDR_OK) return s;
   const gdr_desc &d = *desc;
+  const int ns_ = d.in_dtype == GDR_BF16 ? 2 : 3;
+  const int t_layout = seg > 0 ? seg * d.chunk : d.T;  // tokens per stream the workspace is laid out for
+  if (seg > 0) need = gdr::chunk_workspace(nullptr, nullptr, d.B, d.H, t_layout, d.chunk, d.dk, ns_, 0);
   const long long streams = nseq > 0 ? (long long)nseq * d.H : (long long)d.B * d.H;
   if (streams == 0) return GDR_OK;
   if (nseq > 0 && (!cu || (reinterpret_cast<uintptr_t>(cu) & 3u))) return GDR_ERR_INVALID_ARG;
@@ -110,7 +115,7 @@ gdr_status chunk_call(const gdr_desc *desc, int nseq, const int *cu, const void 
   a.log_alpha = log_alpha; a.gamma = gamma; a.S0 = S0;
   a.o = o; a.S_T = S_T;
   a.Qp = a.Mm = a.Sc = nullptr; a.Ob = a.Nn = a.Sst = nullptr;
-  gdr::chunk_workspace(&a, workspace, d.B, d.H, d.T, d.chunk, d.dk, ns, nseq);
+  gdr::chunk_workspace(&a, workspace, d.B, d.H, t_layout, d.chunk, d.dk, ns, nseq);
   a.B = nseq > 0 ? nseq : d.B; a.H = d.H; a.T = d.T;
   a.alpha_mode = d.alpha_mode; a.b_mode = d.b_mode; a.w_mode = d.w_mode;
   a.normalize_qk = d.normalize_qk; a.scale = d.scale;
@@ -125,8 +130,20 @@ gdr_status chunk_call(const gdr_desc *desc, int nseq, const int *cu, const void 
   a.y = og ? og->y : nullptr;
   a.oraw = og ? og->o : nullptr;
   if (nseq == 0) { a.ctab = nullptr; a.coff = nullptr; a.ctab_len = 0; }
-  hipError_t e = gdr::launch_chunk(d, a, phases, static_cast<hipStream_t>(stream));
+  hipError_t e = gdr::launch_chunk(d, a, phases, static_cast<hipStream_t>(stream), seg);
   return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
+
+// Segment length of the allocation-free whole call: the library's regular
+// choice when its workspace fits the static scratch, else the longest that
+// fits; 0 when not even one chunk per stream fits.
+int static_segment(const gdr_desc &d) {
+  const int ns = d.in_dtype == GDR_BF16 ? 2 : 3;
+  int seg = gdr::chunk_segment(d.B, d.H, d.T, d.chunk, d.dk, ns);
+  while (seg > 0 &&
+         gdr::chunk_workspace(nullptr, nullptr, d.B, d.H, seg * d.chunk, d.chunk, d.dk, ns, 0) > gdr::kStaticScratchBytes)
+    --seg;
+  return seg;
 }
 
 // The five-gate projection: validation, workspace size (the latent h).
@@ -398,6 +415,24 @@ gdr_status gdr_chunk_fwd(const gdr_desc *desc, const void *q, const void *k, con
                          size_t workspace_bytes, void *stream) {
   return chunk_call(desc, 0, nullptr, q, k, v, log_alpha, b, w, gamma, z, S0, o, S_T, workspace,
                     workspace_bytes, stream, 3);
+}
+
+gdr_status gdr_chunk_fwd_static(const gdr_desc *desc, const void *q, const void *k, const void *v,
+                                const float *log_alpha, const void *b, const void *w, const float *gamma,
+                                const void *z, const float *S0, void *o, float *S_T, void *stream) {
+  size_t ignored = 0;
+  gdr_status s = chunk_plan(desc, 0, &ignored);
+  if (s != GDR_OK) return s;
+  if ((long long)desc->B * desc->H == 0) return GDR_OK;
+  int seg = 1;
+  if (desc->T > 0) {
+    seg = static_segment(*desc);
+    if (seg < 1) return GDR_ERR_UNSUPPORTED;  // B * H streams' segment state exceeds the static scratch
+  }
+  void *ws = nullptr;
+  if (gdr::static_scratch(&ws) != hipSuccess) return GDR_ERR_HIP;
+  return chunk_call(desc, 0, nullptr, q, k, v, log_alpha, b, w, gamma, z, S0, o, S_T, ws, gdr::kStaticScratchBytes,
+                    stream, 3, nullptr, seg);
 }
 
 gdr_status gdr_chunk_fwd_gated(const gdr_desc *desc, const void *q, const void *k, const void *v,

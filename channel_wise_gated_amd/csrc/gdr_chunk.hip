@@ -1311,6 +1311,9 @@ bool chunk_intra_fits(int C, int D, int NS) {
 // cost); NC (one segment) when the whole workspace is small enough.
 constexpr size_t kSegmentBytes = (size_t)160 << 20;
 constexpr size_t kMinSegment = 8;
+constexpr size_t seg_chunk_bytes(int C, int D, int NS) {
+  return (size_t)NS * C * D * 2 + (size_t)NS * D * D * 2 * 2 + (size_t)C * D * 4 + (size_t)D * D * 4;
+}
 static int segment_chunks(size_t nbh, int NC, size_t chunk_bytes) {
   if (nbh == 0 || NC <= 0 || nbh * (size_t)NC * chunk_bytes <= kSegmentBytes) return NC > 0 ? NC : 1;
   size_t g = 256, x = nbh % 256;
@@ -1356,8 +1359,39 @@ static hipError_t launch_chunk_pass(const ChunkArgs &a, size_t nch, int phases, 
 
 constexpr int kMaxDevices = 64;
 
+int chunk_segment(int B, int H, int T, int C, int D, int NS) {
+  const int NC = (T + C - 1) / C;
+  return segment_chunks((size_t)B * H, NC, seg_chunk_bytes(C, D, NS));
+}
+
+// Scratch of the allocation-free whole call (gdr_chunk_fwd_static): one copy
+// per GPU, held until the process ends.  Host code never passes `scratch`
+// itself to a kernel (on the host it only names the symbol): the device
+// address of the current device's copy is looked up once per device and
+// used everywhere instead.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+hipError_t static_scratch(void **ptr) {
+  static std::once_flag once[kMaxDevices];
+  static void *addr[kMaxDevices];
+  static hipError_t err[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(once[dev], [dev] {
+    void *p = nullptr;
+    err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    addr[dev] = err[dev] == hipSuccess ? p : nullptr;
+  });
+  if (err[dev] != hipSuccess) return err[dev];
+  if (!addr[dev]) return hipErrorInvalidSymbol;
+  *ptr = addr[dev];
+  return hipSuccess;
+}
+
 template <int C, int D, int NS, bool BF, bool OB16>
-static hipError_t launch_chunk_t(const ChunkArgs &a, int phases, hipStream_t st) {
+static hipError_t launch_chunk_t(const ChunkArgs &a, int phases, hipStream_t st, int seg_force) {
   using Lds = IntraLds<C, D, NS>;
   static_assert(Lds::bytes <= 160 * 1024 || NS == 3, "intra-chunk LDS budget");
   if constexpr (Lds::bytes <= 160 * 1024) {
@@ -1399,9 +1433,8 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, int phases, hipStream_t st)
     // separate intra / scan calls exchange the whole workspace and are not
     // segmented.
     const int NC = (a.T + C - 1) / C;
-    constexpr size_t chunk_bytes = (size_t)NS * C * D * 2 + (size_t)NS * D * D * 2 * 2 + (size_t)C * D * 4 +
-                                   (size_t)D * D * 4;
-    const int seg = phases == 3 ? segment_chunks(nbh, NC, chunk_bytes) : NC;
+    constexpr size_t chunk_bytes = seg_chunk_bytes(C, D, NS);
+    const int seg = seg_force > 0 ? seg_force : (phases == 3 ? segment_chunks(nbh, NC, chunk_bytes) : NC);
     const int nseg = NC > 0 ? (NC + seg - 1) / seg : 1;
     for (int sgi = 0; sgi < nseg; ++sgi) {
       ChunkArgs sa = a;
@@ -1435,11 +1468,12 @@ hipError_t launch_chain_pair(const gdr_desc &d, const ChunkArgs &a, const ChunkA
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_chunk(const gdr_desc &d, const ChunkArgs &a, int phases, hipStream_t st) {
+hipError_t launch_chunk(const gdr_desc &d, const ChunkArgs &a, int phases, hipStream_t st, int seg) {
   const bool ib = d.in_dtype == GDR_BF16, ob = d.out_dtype == GDR_BF16;
+  if (seg > 0 && (phases != 3 || a.ctab)) return hipErrorInvalidValue;
 #define GDR_CH(CC, DD, IB, OBB)                                                            \
   if (d.chunk == CC && d.dk == DD && ib == IB && ob == OBB)                                \
-    return launch_chunk_t<CC, DD, (IB ? 2 : 3), IB, OBB>(a, phases, st);
+    return launch_chunk_t<CC, DD, (IB ? 2 : 3), IB, OBB>(a, phases, st, seg);
   GDR_CH(64, 64, true, false) GDR_CH(64, 64, true, true) GDR_CH(64, 64, false, false)
   GDR_CH(64, 64, false, true) GDR_CH(64, 128, true, false) GDR_CH(64, 128, true, true)
   GDR_CH(64, 128, false, false) GDR_CH(64, 128, false, true) GDR_CH(128, 64, true, false)

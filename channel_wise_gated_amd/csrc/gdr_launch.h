@@ -100,8 +100,17 @@ hipError_t launch_decode(const gdr_desc &d, float *S, const void *q, const void 
                          const float *la, const void *b, const void *w, const float *gamma,
                          const void *z, void *o, hipStream_t st);
 // phases: bit 0 = intra-chunk kernel, bit 1 = scan (chain + output kernels),
-// bit 2 = chain kernel only (no output)
-hipError_t launch_chunk(const gdr_desc &d, const ChunkArgs &a, int phases, hipStream_t st);
+// bit 2 = chain kernel only (no output).  seg > 0 (whole calls of uniform
+// batches only): segments of exactly `seg` chunks per stream, the workspace
+// laid out for B*H*seg chunk slots (chunk_workspace with T = seg * C); 0: the
+// library's own segment choice over a workspace for every chunk.
+hipError_t launch_chunk(const gdr_desc &d, const ChunkArgs &a, int phases, hipStream_t st, int seg = 0);
+// Chunks per stream in one segment of a whole call, as the library chooses it.
+int chunk_segment(int B, int H, int T, int C, int D, int NS);
+// The static scratch of the allocation-free whole call: its size, and the
+// device address of the current device's copy (looked up once per device).
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+hipError_t static_scratch(void **ptr);
 // Two independent chains (the chain kernel only) over uniform batches at C = 64
 // in one launch; each ChunkArgs with c0 = 0 and ncs = its chunks per stream.
 hipError_t launch_chain_pair(const gdr_desc &d, const ChunkArgs &a, const ChunkArgs &b, hipStream_t st);

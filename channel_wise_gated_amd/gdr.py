@@ -11,6 +11,7 @@ Entry points (same names as the C ABI):
       -> (o, S_T)
   gdr_chunk_fwd_gated(q, k, v, log_alpha, b, w, g, ...) -> (y, S_T)
   ChunkCall(...) and its .intra() / .scan(): gdr_chunk_fwd_intra / _scan
+  ChunkCall(...).static(): gdr_chunk_fwd_static (no workspace, no allocation)
   gdr_chunk_fwd_varlen_workspace_size(desc, n_seqs) -> bytes
   gdr_chunk_fwd_varlen(q, k, v, log_alpha, b, w, cu_seqlens, ...) -> (o, S_T)
   gdr_decode_step(S, q, k, v, log_alpha, b, w, gamma=None, z=None, ...) -> o
@@ -35,7 +36,7 @@ SYMBOLS = ("gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_chunk_fwd_gated
            "gdr_chunk_bwd_varlen", "gdr_output_gate_bwd_workspace_size", "gdr_output_gate_bwd",
            "gdr_chunk_fwd_scan", "gdr_chunk_fwd_varlen_workspace_size", "gdr_chunk_fwd_varlen",
            "gdr_decode_step", "gdr_status_string", "gdr_version", "gdr_gate_proj_workspace_size",
-           "gdr_gate_proj")
+           "gdr_gate_proj", "gdr_chunk_fwd_static")
 
 
 class GdrDesc(ctypes.Structure):
@@ -81,6 +82,8 @@ def load() -> ctypes.CDLL:
     lib.gdr_chunk_fwd_gated.restype = ctypes.c_int
     lib.gdr_chunk_fwd_gated.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp,
                                         vp, vp, vp, sz, vp]
+    lib.gdr_chunk_fwd_static.restype = ctypes.c_int
+    lib.gdr_chunk_fwd_static.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.gdr_chunk_fwd_intra.restype = ctypes.c_int
     lib.gdr_chunk_fwd_intra.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gdr_chunk_fwd_scan.restype = ctypes.c_int
@@ -311,6 +314,15 @@ class ChunkCall:
                                   *self.ws, _stream(stream))
         if rc != GDR_OK:
             raise GdrError(rc, "gdr_chunk_fwd")
+        return self.o, self.S_T
+
+    def static(self, stream=None):
+        """gdr_chunk_fwd_static: the whole call with the library's static
+        scratch instead of the workspace (no device allocation)."""
+        S0p, op, sTp = self.out_ptrs
+        rc = load().gdr_chunk_fwd_static(ctypes.byref(self.desc), *self.ptrs[:8], S0p, op, sTp, _stream(stream))
+        if rc != GDR_OK:
+            raise GdrError(rc, "gdr_chunk_fwd_static")
         return self.o, self.S_T
 
     def intra(self, stream=None):

@@ -132,6 +132,29 @@ gdr_status gdr_chunk_fwd(const gdr_desc *desc, const void *q, const void *k,
                          size_t workspace_bytes, void *stream);
 
 /*
+ * gdr_chunk_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, hosts that forbid allocation.  Same
+ * arguments, results and validation as gdr_chunk_fwd on a uniform batch,
+ * without the workspace: the scratch is a static array of the library
+ * (64 MiB per GPU, held by every GPU the library runs on until the process
+ * ends), and the call allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine).  The long-context path runs in segments of chunks sized
+ * to fit that array; the results equal gdr_chunk_fwd's, bit for bit.
+ *   Limit: B * H streams' maps for one chunk each, plus their fp32 handoff
+ *   states, must fit the array (about 170 streams at dk = dv = 128 and chunk
+ *   128, 230 at chunk 64); a larger problem returns GDR_ERR_UNSUPPORTED
+ *   before any launch.
+ *   Every call on a GPU uses that GPU's one copy of the array: calls that
+ *   overlap in time on one GPU (other streams, other threads) race and give
+ *   undefined results; calls ordered on one stream are safe.  No state
+ *   carries over from one call to the next (nothing needs clearing).
+ */
+gdr_status gdr_chunk_fwd_static(const gdr_desc *desc, const void *q, const void *k,
+                                const void *v, const float *log_alpha, const void *b,
+                                const void *w, const float *gamma, const void *z,
+                                const float *S0, void *o, float *S_T, void *stream);
+
+/*
  * The five gates from one shared low-rank projection of the layer input
  * (Muir reading notes, section 2.3: a shared down-projection, then per gate
  * an up-projection and a channel bias give the logits of the decay f, erase

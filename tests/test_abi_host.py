@@ -357,3 +357,16 @@ def test_chunk_table_logic_stays_in_bounds(cu):
         assert sum(v for _, v in cover) == cu[-1] - cu[0]
         assert all(coff[n + 1] - coff[n] == -(-(cu[n + 1] - cu[n]) // C) for n in range(len(cu) - 1))
 
+
+def test_static_forward_rejects_problems_beyond_its_scratch():
+    """gdr_chunk_fwd_static returns GDR_ERR_UNSUPPORTED, before any launch,
+    when one chunk per stream of B*H streams does not fit its static scratch
+    (64 MiB); a descriptor error still comes first."""
+    lib = _lib()
+    big = gdr.make_desc(**dict(GOOD, B=64, H=16, T=4096, dk=128, dv=128, chunk=128))
+    n = [None] * 11
+    assert lib.gdr_chunk_fwd_static(ctypes.byref(big), *n, None) == gdr.GDR_ERR_UNSUPPORTED
+    bad = gdr.make_desc(**dict(GOOD, B=64, H=16, T=4096, dk=96, dv=96))
+    assert lib.gdr_chunk_fwd_static(ctypes.byref(bad), *n, None) == gdr.GDR_ERR_UNSUPPORTED
+    bad = gdr.make_desc(**dict(GOOD, chunk=32))
+    assert lib.gdr_chunk_fwd_static(ctypes.byref(bad), *n, None) == gdr.GDR_ERR_INVALID_ARG
