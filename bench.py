@@ -14,8 +14,11 @@ pass (gdr_chunk_bwd) over the long-context shape.
 
 Prints one JSON line.  Per-kernel durations come from HIP events recorded on
 the stream the kernels run on; the roofline object describes the kernel with
-the largest share of the step.  The fp64 CPU oracle is timed on a bounded
-sample of the same workload (rank 0, N = 1 only) as `cpu_baseline`.
+the largest share of the step (the intra-chunk kernel), over the launches the
+whole call makes (one per segment of chunks).  The same long-context shape at
+the other chunk size (64 when the headline uses 128) is measured beside it.
+The fp64 CPU oracle is timed on a bounded sample of the same workload (rank
+0, N = 1 only) as `cpu_baseline`.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--chunk 64|128]
 """
@@ -32,15 +35,14 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
 METRIC = "tokens/s + % bf16 MFMA peak, chunk fwd T=32K H=16 d=128; decode HBM GB/s"
-# HBM bytes per dispatch of the intra-chunk kernel launched over all 4096
-# chunks (the phase call the roofline times), from two rocprofv3 counter runs
-# (FETCH_SIZE, then WRITE_SIZE) over this benchmark, each scaled by what the
-# same counter reads for a plain 1 GiB device copy (fetch x2.0, write x1.0).
-# Valid only for the kernel sources they were taken on (digest below);
-# otherwise reported as null.
+# HBM bytes per dispatch of the intra-chunk kernel as the whole call launches
+# it (one segment of chunks; the launches the roofline times), from two
+# rocprofv3 counter runs (FETCH_SIZE, then WRITE_SIZE) over this benchmark,
+# each scaled by what the same counter reads for a plain 1 GiB device copy
+# (fetch x2.0, write x1.0).  Valid only for the sources they were taken on
+# (digest below: every source of the library); otherwise reported as null.
 MEASURED_TRAFFIC = {
-    "sources": "76e2cc6b7e60bf45",
-    "chunk_intra_kernel_C128": 2148941820,
+    "sources": "",
 }
 
 
@@ -61,19 +63,34 @@ def chunk_bytes_per_token_head(dk, dv, in_bytes=2, out_bytes=4, gain=True):
 
 
 def sources_digest():
+    """Digest of every source the library is built from (all of csrc/ and the
+    public header) and of the build flags."""
     h = hashlib.sha256()
-    for name in ("gdr_chunk.hip", "gdr_decode.hip", "gdr_device.h"):
-        with open(os.path.join(ROOT, "channel_wise_gated_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+    csrc = os.path.join(ROOT, "channel_wise_gated_amd", "csrc")
+    files = [os.path.join(csrc, n) for n in sorted(os.listdir(csrc)) if n.endswith((".hip", ".h"))]
+    files += [os.path.join(ROOT, "include", "gdr.h"), os.path.join(ROOT, "channel_wise_gated_amd", "build.py")]
+    for path in files:
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def timed_chunk(call, steps, warmup):
     """Wall time of `steps` whole calls (gdr_chunk_fwd, which runs a long
-    batch in segments of chunks), then per-kernel HIP-event times from the
-    same number of phase-call pairs (gdr_chunk_fwd_intra over every chunk in
-    one launch, gdr_chunk_fwd_scan), recorded on the stream the kernels run
-    on."""
+    batch in segments of chunks), then HIP-event times of the same number of
+    phase-call pairs over every chunk in one launch each (gdr_chunk_fwd_intra,
+    gdr_chunk_fwd_scan), recorded on the stream the kernels run on."""
     import torch
     for _ in range(warmup):
         call()
@@ -94,6 +111,112 @@ def timed_chunk(call, steps, warmup):
     intra = sorted(e[0].elapsed_time(e[1]) for e in ev)
     scan = sorted(e[1].elapsed_time(e[2]) for e in ev)
     return wall, intra, scan
+
+
+def timed_segments(x, C, steps, warmup):
+    """The kernels of a whole call, launched as gdr_chunk_fwd launches them.
+    The library reports its segment length (chunks per stream); the inputs of
+    every segment are copied to contiguous tensors of seg * C tokens, and
+    each segment's intra-chunk phase call (one launch over B * H * seg
+    chunks: the grid of the whole call's intra launches) and scan call (chain
+    and output kernels) are issued in order, the fp32 state handed from one
+    segment to the next.  HIP events on the stream the kernels run on, around
+    every launch.  Returns (seg, [intra ms per segment launch], [scan ms])."""
+    import torch
+
+    from channel_wise_gated_amd import gdr
+    B, H, T, dk = x["q"].shape
+    desc = gdr.make_desc(B, H, T, dk, x["v"].shape[-1], C)
+    seg = gdr.gdr_chunk_fwd_segment_chunks(desc)
+    L = seg * C
+    nseg = -(-T // L)
+    if nseg < 2:
+        return seg, [], []
+    calls, S = [], x["S0"]
+    ws = None
+    for s in range(nseg):
+        part = {k: (v[:, :, s * L:(s + 1) * L].contiguous() if (v is not None and v.dim() == 4 and k != "S0")
+                    else v) for k, v in x.items()}
+        c = gdr.ChunkCall(part["q"], part["k"], part["v"], part["log_alpha"], part["b"], part["w"],
+                          part["gamma"], part["z"], S, chunk=C, workspace=ws)
+        ws = c.workspace
+        calls.append(c)
+        S = c.S_T
+    for _ in range(max(1, warmup // 2)):
+        for c in calls:
+            c.intra()
+            c.scan()
+    torch.cuda.synchronize()
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in calls] for _ in range(steps)]
+    for rep in ev:
+        for c, e in zip(calls, rep):
+            e[0].record()
+            c.intra()
+            e[1].record()
+            c.scan()
+            e[2].record()
+    torch.cuda.synchronize()
+    intra = [e[0].elapsed_time(e[1]) for rep in ev for e in rep]
+    scan = [e[1].elapsed_time(e[2]) for rep in ev for e in rep]
+    del calls
+    return seg, intra, scan
+
+
+def measure_chunk(x, wl, C, steps, warmup):
+    """One forward configuration: whole-call throughput (wall clock over
+    `steps` gdr_chunk_fwd calls), algorithmic rates, and the roofline of the
+    dominant kernel over the launches the whole call runs."""
+    from channel_wise_gated_amd import gdr
+    call = gdr.ChunkCall(x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"], x["gamma"],
+                         x["z"], x["S0"], chunk=C)
+    wall, intra1, scan1 = timed_chunk(call, steps, warmup)
+    del call
+    seg, intra_s, scan_s = timed_segments(x, C, steps, warmup)
+    ms_step = 1e3 * wall / steps
+    BH = wl.B * wl.H
+    per_th = chunk_bytes_per_token_head(wl.dk, wl.dv)
+    fl = flops_per_token_head(C, wl.dk, wl.dv) * BH * wl.T
+    byt = per_th * BH * wl.T + 2 * BH * wl.dk * wl.dv * 4
+    med = lambda a: sorted(a)[len(a) // 2]
+    mean = lambda a: sum(a) / len(a)
+    in_per_th = per_th - 4 * wl.dv          # the intra-chunk kernel reads every input once
+    out = {"workload": f"stress B{wl.B} H{wl.H} T{wl.T} dk{wl.dk} dv{wl.dv} chunk{C}",
+           "steps": steps, "ms_per_step": round(ms_step, 4), "tokens_s": round(wl.B * wl.T / (ms_step / 1e3), 1),
+           "tflops_algorithmic": round(fl / (ms_step / 1e3) / 1e12, 2),
+           "mfma_frac": round(fl / (ms_step / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+           "hbm_gbs_algorithmic": round(byt / (ms_step / 1e3) / 1e9, 1),
+           "hbm_frac": round(byt / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+           "segment_chunks": seg}
+    kb1 = in_per_th * BH * wl.T
+    single = {"launch": f"one launch over all {BH * -(-wl.T // C)} chunks (gdr_chunk_fwd_intra)",
+              "avg_ms": round(mean(intra1), 4), "achieved": round(kb1 / (mean(intra1) / 1e3) / 1e9, 1),
+              "algorithmic_bytes_per_launch": kb1}
+    single["frac"] = round(single["achieved"] / HBM_PEAK_GBS, 4)
+    if intra_s:
+        ntok = seg * C
+        kb = in_per_th * BH * ntok
+        avg = mean(intra_s)
+        ach = kb / (avg / 1e3) / 1e9
+        traffic = None
+        if MEASURED_TRAFFIC["sources"] == sources_digest():
+            traffic = MEASURED_TRAFFIC.get(f"chunk_intra_kernel_C{C}_seg")
+        out["roofline"] = {
+            "bound": "hbm", "kernel": "chunk_intra_kernel", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "launch": f"one segment: {BH * seg} chunks of {C} tokens ({seg} per stream), as gdr_chunk_fwd "
+                      f"launches it; HIP events around each of the {len(intra_s) // steps} segment launches "
+                      f"of {steps} calls",
+            "algorithmic_bytes_per_launch": kb, "avg_ms": round(avg, 4)}
+        out["kernels_ms"] = {"chunk_intra_kernel": round(med(intra_s), 4), "chain_and_output": round(med(scan_s), 4),
+                             "per": f"segment launch ({BH * seg} chunks), median"}
+    else:  # the whole call runs in one pass
+        out["roofline"] = dict(bound="hbm", kernel="chunk_intra_kernel", achieved=single["achieved"],
+                               peak=HBM_PEAK_GBS, unit="GB/s", frac=single["frac"], traffic=None,
+                               launch=single["launch"], algorithmic_bytes_per_launch=kb1, avg_ms=single["avg_ms"])
+        out["kernels_ms"] = {"chunk_intra_kernel": round(med(intra1), 4), "chain_and_output": round(med(scan1), 4),
+                             "per": "whole launch, median"}
+    out["roofline_single_launch"] = single
+    return out
 
 
 def timed_decode(wl, steps, warmup):
@@ -256,32 +379,43 @@ def copy_calibration(mib):
 
 
 def cpu_baseline(x, target_s=12.0):
-    """The fp64 oracle, as it stands, on the first Ts tokens of every head."""
+    """The fp64 oracle, as it stands, on the host cores: the first Ts tokens of
+    every head, or -- when the whole sequence takes less than `target_s` --
+    the whole workload repeated until about `target_s` of CPU work."""
     import oracle
-    import numpy as np
 
     def sample(Ts):
         return {k: (v[:, :, :Ts].cpu() if (v is not None and v.dim() == 4 and k != "S0")
                     else (v.cpu() if v is not None else None)) for k, v in x.items()}
 
-    H = x["q"].shape[1]
-    threads = oracle.default_threads(H * x["q"].shape[0])
+    def run(s):
+        oracle.forward(s["q"], s["k"], s["v"], s["log_alpha"], s["b"], s["w"], gamma=s["gamma"],
+                       z=s["z"], S0=s["S0"], threads=threads)
+
+    B, H, T = x["q"].shape[:3]
+    threads = oracle.default_threads(H * B)
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        avail = os.cpu_count() or 1
     probe = 512
     s = sample(probe)
     t0 = time.perf_counter()
-    oracle.forward(s["q"], s["k"], s["v"], s["log_alpha"], s["b"], s["w"], gamma=s["gamma"],
-                   z=s["z"], S0=s["S0"], threads=threads)
+    run(s)
     rate = probe / (time.perf_counter() - t0)
-    T = x["q"].shape[2]
     Ts = int(min(T, max(probe, (rate * target_s) // 64 * 64)))
+    reps = 1 if Ts < T else max(1, int(round(target_s / (T / rate))))
     s = sample(Ts)
     t0 = time.perf_counter()
-    oracle.forward(s["q"], s["k"], s["v"], s["log_alpha"], s["b"], s["w"], gamma=s["gamma"],
-                   z=s["z"], S0=s["S0"], threads=threads)
+    for _ in range(reps):
+        run(s)
     dt = time.perf_counter() - t0
-    return {"value": round(Ts * x["q"].shape[0] / dt, 1), "unit": "tokens/s", "cores": threads,
-            "kind": "oracle", "seconds": round(dt, 2),
-            "sample": f"first {Ts} of {T} tokens, all {H} heads, fp64 token recurrence"}
+    what = f"first {Ts} of {T} tokens" if Ts < T else f"all {T} tokens, {reps} runs"
+    return {"value": round(reps * Ts * B / dt, 1), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle", "seconds": round(dt, 2), "cpu_model": cpu_model(),
+            "cores_available": avail, "threads_used": threads,
+            "sample": f"{what}, all {H} heads (one thread per stream, at most one per core), "
+                      f"fp64 token recurrence"}
 
 
 def main():
@@ -290,6 +424,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--chunk", type=int, default=128, choices=(64, 128))
+    ap.add_argument("--no-both-chunks", dest="both_chunks", action="store_false",
+                    help="skip the leg at the other chunk size (64 when --chunk 128)")
     ap.add_argument("--decode-steps", type=int, default=1024, help="0 skips the decode leg")
     ap.add_argument("--gdn-steps", type=int, default=20,
                     help="whole calls of the scalar-gate (Gated DeltaNet) leg; 0 skips it")
@@ -318,35 +454,11 @@ def main():
     wl = WORKLOADS["stress"]
     C = args.chunk
     x = make_inputs_device(wl, "cuda")
-    call = gdr.ChunkCall(x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"], x["gamma"],
-                         x["z"], x["S0"], chunk=C)
-    wall, intra, scan = timed_chunk(call, args.steps, args.warmup)
-    ms_step = 1e3 * wall / args.steps
-    med = lambda a: a[len(a) // 2]
-    intra_ms, scan_ms = med(intra), med(scan)
-    BH = wl.B * wl.H
-    toks = wl.B * wl.T
-    tok_s = toks / (ms_step / 1e3)
-    fl = flops_per_token_head(C, wl.dk, wl.dv) * BH * wl.T
-    tflops = fl / (ms_step / 1e3) / 1e12
-    byt = chunk_bytes_per_token_head(wl.dk, wl.dv) * BH * wl.T + 2 * BH * wl.dk * wl.dv * 4
-    gbs = byt / (ms_step / 1e3) / 1e9
-
-    # roofline of the kernel with the largest share of the step
-    in_bytes = (chunk_bytes_per_token_head(wl.dk, wl.dv) - 4 * wl.dv) * BH * wl.T
-    out_bytes = 4 * wl.dv * BH * wl.T + 2 * BH * wl.dk * wl.dv * 4
-    if intra_ms >= scan_ms:
-        kname, kms, kbytes = "chunk_intra_kernel", intra_ms, in_bytes
-    else:
-        kname, kms, kbytes = "chunk_scan_kernel", scan_ms, out_bytes
-    achieved = kbytes / (kms / 1e3) / 1e9
-    traffic = None
-    if MEASURED_TRAFFIC["sources"] == sources_digest():
-        traffic = MEASURED_TRAFFIC.get(f"{kname}_C{C}")
-    roof = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "algorithmic_bytes_per_launch": kbytes, "avg_ms": round(sum(intra if kname.endswith(
-                "intra_kernel") else scan) / args.steps, 4)}
+    main_leg = measure_chunk(x, wl, C, args.steps, args.warmup)
+    other_c = 64 if C == 128 else 128
+    other_leg = measure_chunk(x, wl, other_c, args.steps, args.warmup) if args.both_chunks else None
+    ms_step = main_leg["ms_per_step"]
+    tok_s = wl.B * wl.T / (ms_step / 1e3)
 
     # scalar-gate leg: the same shape with one decay and one beta per token
     gsteps = args.gdn_steps
@@ -389,15 +501,19 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"stress B{wl.B} H{wl.H} T{wl.T} dk{wl.dk} dv{wl.dv} chunk{C}",
+        "config": {"workload": main_leg["workload"],
                    "inputs": "bf16 q,k,v,b,w,z; fp32 log-decay, gain, state and o",
                    "arith": "bf16 hi/lo-split MFMA, fp32 accumulate and state"},
-        "tflops_algorithmic": round(tflops, 2), "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4),
-        "hbm_gbs_algorithmic": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-        "kernels_ms": {"chunk_intra_kernel": round(intra_ms, 4), "chunk_scan_kernel": round(scan_ms, 4),
-                       "from": "phase calls over all chunks in one launch each (median of steps)"},
-        "roofline": roof,
+        "tflops_algorithmic": main_leg["tflops_algorithmic"], "mfma_frac": main_leg["mfma_frac"],
+        "mfma_target_frac": 0.40,
+        "hbm_gbs_algorithmic": main_leg["hbm_gbs_algorithmic"], "hbm_frac": main_leg["hbm_frac"],
+        "segment_chunks": main_leg["segment_chunks"],
+        "kernels_ms": main_leg["kernels_ms"],
+        "roofline": main_leg["roofline"],
+        "roofline_single_launch": main_leg["roofline_single_launch"],
     }
+    if other_leg is not None:
+        line[f"chunk{other_c}"] = other_leg
     if gsteps > 0:
         line["gdn"] = {"workload": f"gdn B{gwl.B} H{gwl.H} T{gwl.T} dk{gwl.dk} dv{gwl.dv} chunk{C}, "
                                    "one decay and one beta per token (b = w)",

@@ -459,6 +459,16 @@ gdr_status gdr_chunk_fwd_scan(const gdr_desc *desc, const float *S0, void *o, fl
                     nullptr, S0, o, S_T, const_cast<void *>(workspace), workspace_bytes, stream, 2);
 }
 
+gdr_status gdr_chunk_fwd_segment_chunks(const gdr_desc *desc, int *chunks) {
+  if (!chunks) return GDR_ERR_INVALID_ARG;
+  size_t ws = 0;
+  gdr_status s = chunk_plan(desc, 0, &ws);
+  if (s != GDR_OK) return s;
+  const int ns = desc->in_dtype == GDR_BF16 ? 2 : 3;
+  *chunks = desc->T > 0 ? gdr::chunk_segment(desc->B, desc->H, desc->T, desc->chunk, desc->dk, ns) : 0;
+  return GDR_OK;
+}
+
 gdr_status gdr_chunk_fwd_varlen_workspace_size(const gdr_desc *desc, int n_seqs, size_t *bytes) {
   if (!bytes || n_seqs < 1) return GDR_ERR_INVALID_ARG;
   size_t ws = 0;

@@ -7,6 +7,7 @@ raises.
 
 Entry points (same names as the C ABI):
   gdr_chunk_fwd_workspace_size(desc) -> bytes
+  gdr_chunk_fwd_segment_chunks(desc) -> chunks per stream in one segment
   gdr_chunk_fwd(q, k, v, log_alpha, b, w, gamma=None, z=None, S0=None, ...)
       -> (o, S_T)
   gdr_chunk_fwd_gated(q, k, v, log_alpha, b, w, g, ...) -> (y, S_T)
@@ -36,7 +37,7 @@ SYMBOLS = ("gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_chunk_fwd_gated
            "gdr_chunk_bwd_varlen", "gdr_output_gate_bwd_workspace_size", "gdr_output_gate_bwd",
            "gdr_chunk_fwd_scan", "gdr_chunk_fwd_varlen_workspace_size", "gdr_chunk_fwd_varlen",
            "gdr_decode_step", "gdr_status_string", "gdr_version", "gdr_gate_proj_workspace_size",
-           "gdr_gate_proj", "gdr_chunk_fwd_static")
+           "gdr_gate_proj", "gdr_chunk_fwd_static", "gdr_chunk_fwd_segment_chunks")
 
 
 class GdrDesc(ctypes.Structure):
@@ -82,6 +83,8 @@ def load() -> ctypes.CDLL:
     lib.gdr_chunk_fwd_gated.restype = ctypes.c_int
     lib.gdr_chunk_fwd_gated.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp,
                                         vp, vp, vp, sz, vp]
+    lib.gdr_chunk_fwd_segment_chunks.restype = ctypes.c_int
+    lib.gdr_chunk_fwd_segment_chunks.argtypes = [dp, ctypes.POINTER(ctypes.c_int)]
     lib.gdr_chunk_fwd_static.restype = ctypes.c_int
     lib.gdr_chunk_fwd_static.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.gdr_chunk_fwd_intra.restype = ctypes.c_int
@@ -137,6 +140,15 @@ def gdr_chunk_fwd_workspace_size(desc: GdrDesc) -> int:
     rc = load().gdr_chunk_fwd_workspace_size(ctypes.byref(desc), ctypes.byref(n))
     if rc != GDR_OK:
         raise GdrError(rc, "gdr_chunk_fwd_workspace_size")
+    return int(n.value)
+
+
+def gdr_chunk_fwd_segment_chunks(desc: GdrDesc) -> int:
+    """Chunks per stream in one segment of gdr_chunk_fwd (see gdr.h)."""
+    n = ctypes.c_int(0)
+    rc = load().gdr_chunk_fwd_segment_chunks(ctypes.byref(desc), ctypes.byref(n))
+    if rc != GDR_OK:
+        raise GdrError(rc, "gdr_chunk_fwd_segment_chunks")
     return int(n.value)
 
 

@@ -132,6 +132,19 @@ gdr_status gdr_chunk_fwd(const gdr_desc *desc, const void *q, const void *k,
                          size_t workspace_bytes, void *stream);
 
 /*
+ * Chunks per (batch, head) stream in one segment of gdr_chunk_fwd on a
+ * uniform batch: the whole call runs the intra-chunk, chain and output
+ * kernels over that many chunks of every stream at a time (each launch of
+ * the intra-chunk and output kernels covers B * H * chunks chunks), handing
+ * the fp32 state from one segment to the next, so that the chunk maps the
+ * kernels exchange stay in the GPU's last-level cache (Muir notes section 2.4
+ * computes the same chunk maps; the segmenting is this library's).  Equal to
+ * ceil(T / chunk) when the call runs in one pass.  Validation as
+ * gdr_chunk_fwd_workspace_size; written to *chunks (0 when T = 0).
+ */
+gdr_status gdr_chunk_fwd_segment_chunks(const gdr_desc *desc, int *chunks);
+
+/*
  * gdr_chunk_fwd for callers that cannot allocate device memory: code under
  * HIP graph capture, tight serving loops, hosts that forbid allocation.  Same
  * arguments, results and validation as gdr_chunk_fwd on a uniform batch,

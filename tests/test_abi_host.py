@@ -370,3 +370,18 @@ def test_static_forward_rejects_problems_beyond_its_scratch():
     assert lib.gdr_chunk_fwd_static(ctypes.byref(bad), *n, None) == gdr.GDR_ERR_UNSUPPORTED
     bad = gdr.make_desc(**dict(GOOD, chunk=32))
     assert lib.gdr_chunk_fwd_static(ctypes.byref(bad), *n, None) == gdr.GDR_ERR_INVALID_ARG
+
+
+def test_segment_chunks_query():
+    """Segment length of the whole call: one pass for a small problem, whole
+    rounds of the 256 compute units (and at least 8 chunks) for the
+    long-context shape, 0 without tokens; validation as the workspace query."""
+    _lib()
+    small = gdr.make_desc(**GOOD)
+    assert gdr.gdr_chunk_fwd_segment_chunks(small) == 256 // 64
+    stress = gdr.make_desc(B=1, H=16, T=32768, dk=128, dv=128, chunk=128)
+    seg = gdr.gdr_chunk_fwd_segment_chunks(stress)
+    assert 8 <= seg < 256 and (16 * seg) % 256 == 0
+    assert gdr.gdr_chunk_fwd_segment_chunks(gdr.make_desc(**dict(GOOD, T=0))) == 0
+    with pytest.raises(gdr.GdrError):
+        gdr.gdr_chunk_fwd_segment_chunks(gdr.make_desc(**dict(GOOD, chunk=32)))
