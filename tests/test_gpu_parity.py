@@ -255,6 +255,29 @@ def test_segmented_call_matches_the_phase_calls(chunk):
     assert torch.equal(s1, s2)
 
 
+def test_long_call_d64_matches_the_phase_calls_and_the_oracle():
+    """The long whole call at d = 64, chunk 64 (16 streams x 256 chunks, run
+    in segments): bit-identical to the phase calls, and within the bar of the
+    oracle on two sampled streams."""
+    wl = WORKLOADS["stress"].with_sizes(T=16384, dk=64, dv=64)
+    xd = make_inputs_device(wl, DEV, seed=23)
+    args = (xd["q"], xd["k"], xd["v"], xd["log_alpha"], xd["b"], xd["w"], xd["gamma"], xd["z"], xd["S0"])
+    whole = gdr.ChunkCall(*args, chunk=64)
+    phased = gdr.ChunkCall(*args, chunk=64)
+    o1, s1 = whole()
+    phased.intra()
+    o2, s2 = phased.scan()
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    bi = torch.tensor([0, 0], device=DEV)
+    hi = torch.tensor([3, 14], device=DEV)
+    xs = {key: (None if val is None else (val[hi].cpu() if key == "gamma" else val[bi, hi][None].cpu()))
+          for key, val in xd.items()}
+    ro, rs = oracle_run(xs)
+    check("long d64 o sampled", o1[bi, hi][None].float().cpu().numpy(), ro, TOL_BF16)
+    check("long d64 S_T sampled", s1[bi, hi][None].cpu().numpy(), rs, TOL_BF16)
+
+
 # ----------------------------------------------------------------------------
 # the workloads at full size: GPU on everything, oracle on sampled streams
 # ----------------------------------------------------------------------------
