@@ -797,80 +797,65 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
       }
     }
     __syncthreads();
-    // D3: products with R (the chunk map)
-    if (vhalf) {
-      if (wave < NMT) {  // N = K'^T U_bar
+    // D3: products with R (the chunk map).  Every wave multiplies the same
+    // staged fragments of R into its tile of N or M (channel tile `wave`)
+    // and of O_bar or Q' (token block i): each fragment is read from LDS once
+    // for both.
+    const bool mw = wave < NMT;
+    f32x4 accC[2] = {zero4(), zero4()}, accT[2] = {zero4(), zero4()};  // channel-tile, token-block products
 #pragma unroll
-        for (int ctl = 0; ctl < 2; ++ctl) {
-          f32x4 acc = zero4();
+    for (int ctl = 0; ctl < 2; ++ctl)
 #pragma unroll
-          for (int ks = 0; ks < NKC; ++ks) {
-            bf16x8 zb[NS];
-            load_frag<NS>(rst + ((ks * 2 + ctl) * NS) * FRAG + lane * 8, FRAG, zb);
-            acc = mfma32_split<NS>(wf[ks], zb, acc);
-          }
-          const int jt = 2 * cp + ctl;
-          *reinterpret_cast<f32x4 *>(Nn + ((size_t)(wave * NMT + jt) * 64 + lane) * 4) = acc;
+      for (int ks = 0; ks < NKC; ++ks) {
+        const bool tw = rowwave && 2 * ks <= i;
+        if (!mw && !tw) continue;
+        bf16x8 zb[NS];
+        load_frag<NS>(rst + ((ks * 2 + ctl) * NS) * FRAG + lane * 8, FRAG, zb);
+        if (vhalf) {
+          if (mw) accC[ctl] = mfma32_split<NS>(wf[ks], zb, accC[ctl]);  // N = K'^T U_bar
+          if (tw) accT[ctl] = mfma32_split<NS>(pf[ks], zb, accT[ctl]);  // O_bar = A U_bar
+        } else {
+          if (mw) accC[ctl] = mfma32_split<NS>(zb, wf[ks], accC[ctl]);  // (K'^T Y)^T = Y^T K'
+          if (tw) accT[ctl] = mfma32_split<NS>(zb, pf[ks], accT[ctl]);  // (A Y)^T = Y^T A^T
         }
       }
-      if (rowwave) {  // O_bar = A U_bar
+    if (vhalf) {
+      if (mw) {
 #pragma unroll
-        for (int ctl = 0; ctl < 2; ++ctl) {
-          f32x4 acc = zero4();
+        for (int ctl = 0; ctl < 2; ++ctl)
+          *reinterpret_cast<f32x4 *>(Nn + ((size_t)(wave * NMT + 2 * cp + ctl) * 64 + lane) * 4) = accC[ctl];
+      }
+      if (rowwave) {
 #pragma unroll
-          for (int ks = 0; ks < NKC; ++ks) {
-            if (2 * ks > i) continue;
-            bf16x8 zb[NS];
-            load_frag<NS>(rst + ((ks * 2 + ctl) * NS) * FRAG + lane * 8, FRAG, zb);
-            acc = mfma32_split<NS>(pf[ks], zb, acc);
-          }
-          const int jt = 2 * cp + ctl;
-          *reinterpret_cast<f32x4 *>(Ob + ((size_t)(i * NMT + jt) * 64 + lane) * 4) = acc;
-        }
+        for (int ctl = 0; ctl < 2; ++ctl)
+          *reinterpret_cast<f32x4 *>(Ob + ((size_t)(i * NMT + 2 * cp + ctl) * 64 + lane) * 4) = accT[ctl];
       }
     } else {
       const int ksy = cp - D / 32;  // k-step of the state-row index covered by this pair
-      if (wave < NMT) {             // M = Diag(e^Lambda_C) - K'^T Y, as (K'^T Y)^T = Y^T K'
+      if (mw) {                     // M = Diag(e^Lambda_C) - K'^T Y
         const int c = 16 * wave + l16;
         float mv[8];
 #pragma unroll
-        for (int ctl = 0; ctl < 2; ++ctl) {
-          f32x4 acc = zero4();
-#pragma unroll
-          for (int ks = 0; ks < NKC; ++ks) {
-            bf16x8 zb[NS];
-            load_frag<NS>(rst + ((ks * 2 + ctl) * NS) * FRAG + lane * 8, FRAG, zb);
-            acc = mfma32_split<NS>(zb, wf[ks], acc);
-          }
+        for (int ctl = 0; ctl < 2; ++ctl)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int cpr = 32 * ksy + 16 * ctl + 4 * g + r;
-            mv[4 * ctl + r] = (cpr == c ? gdiag : 0.f) - acc[r];
+            mv[4 * ctl + r] = (cpr == c ? gdiag : 0.f) - accC[ctl][r];
           }
-        }
         store8_planes<NS>(Mm + ((size_t)(wave * NKD + ksy) * 64 + lane) * 8, (size_t)D * D, mv);
       }
-      if (rowwave) {  // Q' = Qt e^Lambda - A Y, as (A Y)^T = Y^T A^T
+      if (rowwave) {  // Q' = Qt e^Lambda - A Y
         float qv8[8];
 #pragma unroll
-        for (int ctl = 0; ctl < 2; ++ctl) {
-          f32x4 acc = zero4();
-#pragma unroll
-          for (int ks = 0; ks < NKC; ++ks) {
-            if (2 * ks > i) continue;
-            bf16x8 zb[NS];
-            load_frag<NS>(rst + ((ks * 2 + ctl) * NS) * FRAG + lane * 8, FRAG, zb);
-            acc = mfma32_split<NS>(zb, pf[ks], acc);
-          }
+        for (int ctl = 0; ctl < 2; ++ctl)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int e = 4 * ctl + r;  // channel tp_chan(ksy, g, e)
             float qr = 0.f;
 #pragma unroll
             for (int p = 0; p < NS; ++p) qr += (float)QRs[p][e];
-            qv8[e] = qr * eci[e] - acc[r];
+            qv8[e] = qr * eci[e] - accT[ctl][r];
           }
-        }
         store8_planes<NS>(Qp + ((size_t)(i * NKD + ksy) * 64 + lane) * 8, (size_t)C * D, qv8);
       }
     }

@@ -25,18 +25,21 @@ namespace {
 constexpr int kGates = 5;
 
 // ---------------------------------------------------------------------------
-// down: workgroup tile 128 tokens x 256 latent columns, 8 waves as 4 token
-// groups x 2 latent halves (wave tile: 32 tokens x 128 latent, 2 x 8 MFMA
-// tiles).  k-steps of 32: both operand tiles of a step are staged in LDS
-// (double-buffered, rows padded to 40 elements so that the 16 rows of a
-// fragment read fall in distinct banks).  The x tile of step k + 4 (streamed
+// down: workgroup tile 256 tokens x 256 latent columns, 8 waves as 4 token
+// groups x 2 latent halves (wave tile: 64 tokens x 128 latent, 4 x 8 MFMA
+// tiles: 12 fragment reads from LDS per 32 products).  k-steps of 32: both
+// operand tiles of a step are staged in LDS (double-buffered, rows padded to
+// 40 elements so that the 16 rows of a fragment read fall in distinct
+// banks); 80 KB, one workgroup per CU.  The x tile of step k + 4 (streamed
 // from HBM) and the Wd tile of step k + 2 (L2-resident) are fetched into
 // registers at the start of step k, so enough bytes are in flight to cover
 // the memory latency; step k commits the tiles of step k + 1 after its
 // products.  The loop runs four steps per iteration with the register slots
 // named, so no register copy waits for a load in flight.
 // ---------------------------------------------------------------------------
-constexpr int kDnTok = 128, kDnLat = 256, kDnK = 32, kDnRow = kDnK + 8;
+constexpr int kDnTok = 256, kDnLat = 256, kDnK = 32, kDnRow = kDnK + 8;
+constexpr int kDnWaveTok = 64, kDnWaveLat = 128;  // wave tile
+constexpr int kDnMT = kDnWaveTok / 16, kDnNT = kDnWaveLat / 16;
 
 __global__ void __launch_bounds__(512) gate_down_kernel(GateArgs a) {
   __shared__ __align__(16) uint16_t xs[2][kDnTok * kDnRow];  // [buffer][token][k]
@@ -46,49 +49,54 @@ __global__ void __launch_bounds__(512) gate_down_kernel(GateArgs a) {
   const int l16 = lane & 15, g = lane >> 4;
   const int wt = wave & 3, wl = wave >> 2;  // token group, latent half
   const int n0 = blockIdx.x * kDnTok, c0 = blockIdx.y * kDnLat;
-  // staging: thread -> row tid / 4 (x: one token row; W: two latent rows,
-  // tid / 4 and 128 + tid / 4), 8 k values (tid % 4) * 8; rows past N or R
-  // read the last row and are never stored
+  // staging: thread -> rows tid / 4 and 128 + tid / 4 of each tile, 8 k
+  // values (tid % 4) * 8; rows past N or R read the last row and are never
+  // stored
   const int sr = tid >> 2, sk = (tid & 3) * 8;
-  const uint16_t *xsrc = a.x + (size_t)min(n0 + sr, a.N - 1) * a.dm + sk;
+  const uint16_t *xsrc0 = a.x + (size_t)min(n0 + sr, a.N - 1) * a.dm + sk;
+  const uint16_t *xsrc1 = a.x + (size_t)min(n0 + 128 + sr, a.N - 1) * a.dm + sk;
   const uint16_t *wsrc0 = a.wd + (size_t)min(c0 + sr, a.R - 1) * a.dm + sk;
   const uint16_t *wsrc1 = a.wd + (size_t)min(c0 + 128 + sr, a.R - 1) * a.dm + sk;
   const int so = sr * kDnRow + sk;
   const int nk = a.dm / kDnK;  // d_model is a multiple of 32
-  struct WPair {
+  struct Pair {
     u32x4 r0, r1;
   };
   // steps past the last are clamped to it (re-loads, no branch around a load)
-  auto ldx = [&](int ks) { return *reinterpret_cast<const u32x4 *>(xsrc + min(ks, nk - 1) * kDnK); };
-  auto ldw = [&](int ks) {
+  auto ld2 = [&](const uint16_t *p0, const uint16_t *p1, int ks) {
     const int k = min(ks, nk - 1) * kDnK;
-    return WPair{*reinterpret_cast<const u32x4 *>(wsrc0 + k), *reinterpret_cast<const u32x4 *>(wsrc1 + k)};
+    return Pair{*reinterpret_cast<const u32x4 *>(p0 + k), *reinterpret_cast<const u32x4 *>(p1 + k)};
   };
-  auto commit = [&](int buf, const u32x4 &rx, const WPair &rw) {
-    *reinterpret_cast<u32x4 *>(&xs[buf][so]) = rx;
+  auto ldx = [&](int ks) { return ld2(xsrc0, xsrc1, ks); };
+  auto ldw = [&](int ks) { return ld2(wsrc0, wsrc1, ks); };
+  auto commit = [&](int buf, const Pair &rx, const Pair &rw) {
+    *reinterpret_cast<u32x4 *>(&xs[buf][so]) = rx.r0;
+    *reinterpret_cast<u32x4 *>(&xs[buf][so + 128 * kDnRow]) = rx.r1;
     *reinterpret_cast<u32x4 *>(&ws[buf][so]) = rw.r0;
     *reinterpret_cast<u32x4 *>(&ws[buf][so + 128 * kDnRow]) = rw.r1;
   };
-  f32x4 acc[2][8];
+  f32x4 acc[kDnMT][kDnNT];
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt)
+  for (int tt = 0; tt < kDnMT; ++tt)
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct) acc[tt][ct] = zero4();
+    for (int ct = 0; ct < kDnNT; ++ct) acc[tt][ct] = zero4();
   auto products = [&](int buf) {
-    const uint16_t *xc = &xs[buf][(wt * 32 + l16) * kDnRow + 8 * g];
-    const uint16_t *wc = &ws[buf][(wl * 128 + l16) * kDnRow + 8 * g];
-    const bf16x8 xb0 = *reinterpret_cast<const bf16x8 *>(xc);
-    const bf16x8 xb1 = *reinterpret_cast<const bf16x8 *>(xc + 16 * kDnRow);
+    const uint16_t *xc = &xs[buf][(wt * kDnWaveTok + l16) * kDnRow + 8 * g];
+    const uint16_t *wc = &ws[buf][(wl * kDnWaveLat + l16) * kDnRow + 8 * g];
+    bf16x8 xb[kDnMT];
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct) {
+    for (int tt = 0; tt < kDnMT; ++tt) xb[tt] = *reinterpret_cast<const bf16x8 *>(xc + 16 * tt * kDnRow);
+#pragma unroll
+    for (int ct = 0; ct < kDnNT; ++ct) {
       const bf16x8 wa = *reinterpret_cast<const bf16x8 *>(wc + 16 * ct * kDnRow);
-      acc[0][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, xb0, acc[0][ct], 0, 0, 0);
-      acc[1][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, xb1, acc[1][ct], 0, 0, 0);
+#pragma unroll
+      for (int tt = 0; tt < kDnMT; ++tt)
+        acc[tt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, xb[tt], acc[tt][ct], 0, 0, 0);
     }
   };
   // step ks: fetch x(ks + 4) into the slot x(ks) left, Wd(ks + 2) into the
   // slot Wd(ks) left; products of step ks; commit x(ks + 1), Wd(ks + 1)
-  auto step = [&](int ks, u32x4 &x_ld, const u32x4 &x_cm, WPair &w_ld, const WPair &w_cm) {
+  auto step = [&](int ks, Pair &x_ld, const Pair &x_cm, Pair &w_ld, const Pair &w_cm) {
     x_ld = ldx(ks + 4);
     w_ld = ldw(ks + 2);
     asm volatile("" ::: "memory");
@@ -100,8 +108,8 @@ __global__ void __launch_bounds__(512) gate_down_kernel(GateArgs a) {
     commit((ks + 1) & 1, x_cm, w_cm);
     __syncthreads();
   };
-  u32x4 x0 = ldx(0), x1 = ldx(1), x2 = ldx(2), x3 = ldx(3);
-  WPair w0 = ldw(0), w1 = ldw(1);
+  Pair x0 = ldx(0), x1 = ldx(1), x2 = ldx(2), x3 = ldx(3);
+  Pair w0 = ldw(0), w1 = ldw(1);
   commit(0, x0, w0);
   __syncthreads();
 #pragma unroll 1
@@ -113,13 +121,13 @@ __global__ void __launch_bounds__(512) gate_down_kernel(GateArgs a) {
   }
   // accumulator: lane (token l16 of tile tt, latent columns 16 ct + 4g .. +3)
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    const int n = n0 + wt * 32 + 16 * tt + l16;
+  for (int tt = 0; tt < kDnMT; ++tt) {
+    const int n = n0 + wt * kDnWaveTok + 16 * tt + l16;
     if (n >= a.N) continue;
-    float *dst = a.hlat + (size_t)n * a.R + c0 + wl * 128 + 4 * g;
+    float *dst = a.hlat + (size_t)n * a.R + c0 + wl * kDnWaveLat + 4 * g;
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct)
-      if (c0 + wl * 128 + 16 * ct + 4 * g < a.R) *reinterpret_cast<f32x4 *>(dst + 16 * ct) = acc[tt][ct];
+    for (int ct = 0; ct < kDnNT; ++ct)
+      if (c0 + wl * kDnWaveLat + 16 * ct + 4 * g < a.R) *reinterpret_cast<f32x4 *>(dst + 16 * ct) = acc[tt][ct];
   }
 }
 
