@@ -502,6 +502,36 @@ gdr_status gdr_decode_step(const gdr_desc *desc, float *S, const void *q, const 
   return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }
 
+gdr_status gdr_check_inputs(const gdr_desc *desc, const void *q, const void *k, const void *v,
+                            const float *log_alpha, const void *b, const void *w, const float *gamma,
+                            const void *z, unsigned long long *counts, void *stream) {
+  gdr_status s = check_common(desc, desc ? desc->T : 0);
+  if (s != GDR_OK) return s;
+  if (!counts || reinterpret_cast<uintptr_t>(counts) % 8) return GDR_ERR_INVALID_ARG;
+  const gdr_desc &d = *desc;
+  const unsigned long long rows = (unsigned long long)d.B * d.H * d.T;
+  if (rows > 0) {
+    s = check_inputs(desc, q, k, v, log_alpha, b, w, gamma, z, q);  // no output: q stands in for o
+    if (s != GDR_OK) return s;
+  }
+  const int bf = d.in_dtype == GDR_BF16;
+  auto gate_n = [&](gdr_gate_mode m, int dim) {
+    return m == GDR_GATE_PER_CHANNEL ? rows * dim : m == GDR_GATE_PER_TOKEN ? rows : 0ull;
+  };
+  auto gate_p = [&](gdr_gate_mode m, const void *p) { return needs_ptr(m) && rows > 0 ? p : nullptr; };
+  const gdr::CheckTensor t[gdr::kCheckCounts] = {
+      {rows > 0 ? q : nullptr, rows * d.dk, bf, 0},
+      {rows > 0 ? k : nullptr, rows * d.dk, bf, 0},
+      {rows > 0 ? v : nullptr, rows * d.dv, bf, 0},
+      {gate_p(d.alpha_mode, log_alpha), gate_n(d.alpha_mode, d.dk), 0, 1},
+      {gate_p(d.b_mode, b), gate_n(d.b_mode, d.dk), bf, 0},
+      {gate_p(d.w_mode, w), gate_n(d.w_mode, d.dv), bf, 0},
+      {rows > 0 ? z : nullptr, rows * d.dk, bf, 0},
+      {gamma, (unsigned long long)d.H * d.dk, 0, 0}};
+  hipError_t e = gdr::launch_check(t, counts, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
+
 const char *gdr_status_string(gdr_status status) {
   switch (status) {
     case GDR_OK: return "GDR_OK";

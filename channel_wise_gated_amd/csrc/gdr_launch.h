@@ -96,6 +96,18 @@ struct OgBwdArgs {
 };
 hipError_t launch_out_gate_bwd(const OgBwdArgs &a, int D, bool g_bf16, hipStream_t st);
 
+// The opt-in precondition check (gdr_check.hip): per tensor its pointer (null:
+// not checked), element count, storage (bf16 or fp32) and whether the
+// log-decay range applies; counts[i] gets the number of elements of tensor i
+// that break the preconditions (zeroed first, on the stream).
+struct CheckTensor {
+  const void *p;
+  unsigned long long n;
+  int bf16, range;
+};
+constexpr int kCheckCounts = 8;
+hipError_t launch_check(const CheckTensor (&t)[kCheckCounts], unsigned long long *counts, hipStream_t st);
+
 hipError_t launch_decode(const gdr_desc &d, float *S, const void *q, const void *k, const void *v,
                          const float *la, const void *b, const void *w, const float *gamma,
                          const void *z, void *o, hipStream_t st);

@@ -37,7 +37,9 @@ SYMBOLS = ("gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_chunk_fwd_gated
            "gdr_chunk_bwd_varlen", "gdr_output_gate_bwd_workspace_size", "gdr_output_gate_bwd",
            "gdr_chunk_fwd_scan", "gdr_chunk_fwd_varlen_workspace_size", "gdr_chunk_fwd_varlen",
            "gdr_decode_step", "gdr_status_string", "gdr_version", "gdr_gate_proj_workspace_size",
-           "gdr_gate_proj", "gdr_chunk_fwd_static", "gdr_chunk_fwd_segment_chunks")
+           "gdr_gate_proj", "gdr_chunk_fwd_static", "gdr_chunk_fwd_segment_chunks", "gdr_check_inputs")
+# counters of gdr_check_inputs, in order
+CHECK_NAMES = ("q", "k", "v", "log_alpha", "b", "w", "z", "gamma")
 
 
 class GdrDesc(ctypes.Structure):
@@ -115,6 +117,8 @@ def load() -> ctypes.CDLL:
     lib.gdr_output_gate_bwd_workspace_size.argtypes = [dp, ctypes.c_int, ctypes.POINTER(sz)]
     lib.gdr_output_gate_bwd.restype = ctypes.c_int
     lib.gdr_output_gate_bwd.argtypes = [dp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp, sz, vp]
+    lib.gdr_check_inputs.restype = ctypes.c_int
+    lib.gdr_check_inputs.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.gdr_status_string.restype = ctypes.c_char_p
     lib.gdr_status_string.argtypes = [ctypes.c_int]
     lib.gdr_version.restype = ctypes.c_int
@@ -580,6 +584,36 @@ def gdr_decode_step(S, q, k, v, log_alpha, b, w, gamma=None, z=None, *, out_dtyp
     if rc != GDR_OK:
         raise GdrError(rc, "gdr_decode_step")
     return o
+
+
+def gdr_check_inputs(q, k, v, log_alpha, b, w, gamma=None, z=None, *, counts=None, stream=None) -> torch.Tensor:
+    """The opt-in precondition check: per input tensor, the number of its
+    elements that are NaN or +-inf (and for log_alpha also > 0 or < -30), as
+    a device int64 tensor of 8 counts in the order of CHECK_NAMES, written on
+    the stream.  Arguments as gdr_chunk_fwd ([B,H,T,d] head-major; gates per
+    channel, per token or the scalars 1 / 0); `counts` may be given (int64,
+    8 elements, on the inputs' device)."""
+    lib = load()
+    B, H, T, dk = _rank(q, "q", 4).shape
+    dv = _rank(v, "v", 4).shape[-1]
+    dt = (_req(q, "q", (B, H, T, dk), _FLOAT).dtype,)
+    _req(k, "k", (B, H, T, dk), dt)
+    _req(v, "v", (B, H, T, dv), dt)
+    amode, la = _log_alpha_arg(log_alpha, (B, H, T, dk))
+    bmode, bt = _gate_arg(b, "b", (B, H, T, dk), dt)
+    wmode, wt = _gate_arg(w, "w", (B, H, T, dv), dt)
+    _opt(gamma, "gamma", (H, dk), _F32)
+    _opt(z, "z", (B, H, T, dk), dt)
+    _opt(counts, "counts", (len(CHECK_NAMES),), (torch.int64,))
+    _same_device(q, dict(k=k, v=v, log_alpha=la, b=bt, w=wt, gamma=gamma, z=z, counts=counts))
+    desc = make_desc(B, H, T, dk, dv, 64, _dtype_code(q), GDR_F32, 1, 1.0, amode, bmode, wmode)
+    if counts is None:
+        counts = torch.empty(len(CHECK_NAMES), dtype=torch.int64, device=q.device)
+    rc = lib.gdr_check_inputs(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(la), _ptr(bt), _ptr(wt),
+                              _ptr(gamma), _ptr(z), _ptr(counts), _stream(stream))
+    if rc != GDR_OK:
+        raise GdrError(rc, "gdr_check_inputs")
+    return counts
 
 
 def gdr_chunk_fwd_varlen_workspace_size(desc: GdrDesc, n_seqs: int) -> int:

@@ -50,8 +50,10 @@
  *     (three-term bf16 splits on the matrix cores, relative error ~1e-6);
  *     bf16 inputs select two-term splits (~1e-5).  State, log-decay and all
  *     accumulation are fp32 in both.
- *   - The library keeps no mutable global state: concurrent calls from
- *     several threads or streams are safe.
+ *   - The library keeps no mutable global state, so concurrent calls from
+ *     several threads or streams are safe; the one exception is
+ *     gdr_chunk_fwd_static, whose scratch array is shared by every call on
+ *     a GPU.
  */
 #ifndef GDR_H
 #define GDR_H
@@ -399,6 +401,41 @@ gdr_status gdr_decode_step(const gdr_desc *desc, float *S, const void *q,
                            const void *k, const void *v, const float *log_alpha,
                            const void *b, const void *w, const float *gamma,
                            const void *z, void *o, void *stream);
+
+/*
+ * Opt-in precondition check of the token inputs of a call with this
+ * descriptor (gdr_chunk_fwd's layout; for decode pass T = 1).  The update
+ * above decays the state by alpha_t = exp(log_alpha_t) in (0, 1] and the
+ * chunk kernels' pivoted decay factors are sized for log_alpha >= -30; no
+ * entry point looks for a violation on its hot path.  This call counts, on
+ * the device, the elements that break the preconditions:
+ *
+ *   counts[GDR_CHECK_Q], [_K], [_V], [_B], [_W], [_Z], [_GAMMA]: NaN or +-inf
+ *   counts[GDR_CHECK_LOG_ALPHA]: NaN, +-inf, > 0 or < -30
+ *
+ * Tensors follow desc (in_dtype, gate modes; a gate in mode ONES or ZEROS,
+ * a NULL z or gamma is not read and counts 0).  counts: device memory, 8-byte
+ * aligned, GDR_CHECK_COUNT unsigned 64-bit counters, zeroed and then written
+ * on `stream` (read them once the stream's work is done).  Errors: as
+ * gdr_chunk_fwd's validation (GDR_ERR_INVALID_ARG for a null desc or
+ * counts, a null required input or a misaligned pointer), checked on the
+ * host before any launch; GDR_ERR_HIP on a launch failure.
+ */
+enum {
+  GDR_CHECK_Q = 0,
+  GDR_CHECK_K = 1,
+  GDR_CHECK_V = 2,
+  GDR_CHECK_LOG_ALPHA = 3,
+  GDR_CHECK_B = 4,
+  GDR_CHECK_W = 5,
+  GDR_CHECK_Z = 6,
+  GDR_CHECK_GAMMA = 7,
+  GDR_CHECK_COUNT = 8
+};
+gdr_status gdr_check_inputs(const gdr_desc *desc, const void *q, const void *k,
+                            const void *v, const float *log_alpha, const void *b,
+                            const void *w, const float *gamma, const void *z,
+                            unsigned long long *counts, void *stream);
 
 /* Static, human-readable name of a status code. */
 const char *gdr_status_string(gdr_status status);
