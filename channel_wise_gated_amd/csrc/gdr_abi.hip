@@ -252,7 +252,9 @@ gdr_status bwd_call(const gdr_desc *desc, int nseq, const int *cu, const void *q
     // forward recompute: the chunk maps (a packed batch's chunk list first),
     // then M^T and Q'^T dO; then the forward chain (chunk-start states) and
     // the reverse chain side by side
-    e = gdr::launch_chunk(fd, f, 1, st);
+    gdr::ChunkArgs fi = f;
+    fi.Ob = nullptr;  // the backward needs no O_bar: the intra kernel skips it
+    e = gdr::launch_chunk(fd, fi, 1, st);
     if (e == hipSuccess) e = gdr::launch_bwd_prep(a, d.dk, ns, st);
     f.c0 = r.c0 = 0;
     f.ncs = r.ncs = a.NC;

@@ -807,7 +807,7 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
     for (int ctl = 0; ctl < 2; ++ctl)
 #pragma unroll
       for (int ks = 0; ks < NKC; ++ks) {
-        const bool tw = rowwave && 2 * ks <= i;
+        const bool tw = rowwave && 2 * ks <= i && (!vhalf || a.Ob);  // O_bar only when it is stored
         if (!mw && !tw) continue;
         bf16x8 zb[NS];
         load_frag<NS>(rst + ((ks * 2 + ctl) * NS) * FRAG + lane * 8, FRAG, zb);
@@ -825,7 +825,7 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
         for (int ctl = 0; ctl < 2; ++ctl)
           *reinterpret_cast<f32x4 *>(Nn + ((size_t)(wave * NMT + 2 * cp + ctl) * 64 + lane) * 4) = accC[ctl];
       }
-      if (rowwave) {
+      if (rowwave && a.Ob) {
 #pragma unroll
         for (int ctl = 0; ctl < 2; ++ctl)
           *reinterpret_cast<f32x4 *>(Ob + ((size_t)(i * NMT + 2 * cp + ctl) * 64 + lane) * 4) = accT[ctl];
