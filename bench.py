@@ -40,9 +40,12 @@ METRIC = "tokens/s + % bf16 MFMA peak, chunk fwd T=32K H=16 d=128; decode HBM GB
 # rocprofv3 counter runs (FETCH_SIZE, then WRITE_SIZE) over this benchmark,
 # each scaled by what the same counter reads for a plain 1 GiB device copy
 # (fetch x2.0, write x1.0).  Valid only for the sources they were taken on
-# (digest below: every source of the library); otherwise reported as null.
+# (digest below: the kernel's sources, the ABI and the build flags);
+# otherwise reported as null.
 MEASURED_TRAFFIC = {
-    "sources": "",
+    "sources": "60284a3dc2848df2",
+    "chunk_intra_kernel_C128_seg": 269406106,   # 512 chunks of 128 tokens per launch
+    "chunk_intra_kernel_C64_seg": 168498043,    # 512 chunks of 64 tokens per launch
 }
 
 
@@ -63,11 +66,12 @@ def chunk_bytes_per_token_head(dk, dv, in_bytes=2, out_bytes=4, gain=True):
 
 
 def sources_digest():
-    """Digest of every source the library is built from (all of csrc/ and the
-    public header) and of the build flags."""
+    """Digest of every source the measured intra-chunk kernel and its launch
+    are built from: the kernel's translation unit and the headers it
+    includes, the C ABI that sets its arguments, and the build flags."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "channel_wise_gated_amd", "csrc")
-    files = [os.path.join(csrc, n) for n in sorted(os.listdir(csrc)) if n.endswith((".hip", ".h"))]
+    files = [os.path.join(csrc, n) for n in ("gdr_chunk.hip", "gdr_abi.hip", "gdr_device.h", "gdr_launch.h")]
     files += [os.path.join(ROOT, "include", "gdr.h"), os.path.join(ROOT, "channel_wise_gated_amd", "build.py")]
     for path in files:
         with open(path, "rb") as f:
