@@ -950,9 +950,6 @@ __device__ __forceinline__ void chain_run(const ChunkArgs &a, int id, ChainLds<D
   // buffer loads: the chunk base goes in scalar registers and the lane
   // offsets never change, so no address register is rewritten while a load
   // into another buffer is still in flight (that would cost a wait)
-  // buffer loads: the chunk base goes in scalar registers and the lane
-  // offsets never change, so no address register is rewritten while a load
-  // into another buffer is still in flight (that would cost a wait)
   auto load = [&](int c, ChainBuf<D, NS> &bf) {
     c = c < NC ? c : NC - 1;  // clamped instead of skipped: no conditional load
     const size_t ch = slot(c);
