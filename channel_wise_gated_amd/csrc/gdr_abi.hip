@@ -110,7 +110,7 @@ gdr_status chunk_call(const gdr_desc *desc, int nseq, const int *cu, const void 
   if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u)) return GDR_ERR_WORKSPACE;
 
   const int ns = d.in_dtype == GDR_BF16 ? 2 : 3;
-  gdr::ChunkArgs a;
+  gdr::ChunkArgs a{};  // every field not set below is null / zero
   a.q = q; a.k = k; a.v = v; a.b = b; a.w = w; a.z = z;
   a.log_alpha = log_alpha; a.gamma = gamma; a.S0 = S0;
   a.o = o; a.S_T = S_T;
@@ -211,7 +211,7 @@ gdr_status bwd_call(const gdr_desc *desc, int nseq, const int *cu, const void *q
   const hipStream_t st = static_cast<hipStream_t>(stream);
   gdr_desc fd = d;
   fd.chunk = 64;
-  gdr::ChunkArgs f;
+  gdr::ChunkArgs f{};  // every field not set below is null / zero
   f.q = q; f.k = k; f.v = v; f.b = b; f.w = w; f.z = z;
   f.log_alpha = log_alpha; f.gamma = gamma; f.S0 = S0;
   f.o = nullptr; f.S_T = nullptr;
@@ -252,8 +252,11 @@ gdr_status bwd_call(const gdr_desc *desc, int nseq, const int *cu, const void *q
     // forward recompute: the chunk maps (a packed batch's chunk list first),
     // then M^T and Q'^T dO; then the forward chain (chunk-start states) and
     // the reverse chain side by side
+    // the backward needs no O_bar (the intra kernel skips it) but the
+    // per-token vectors, which the same kernel writes beside the maps
     gdr::ChunkArgs fi = f;
-    fi.Ob = nullptr;  // the backward needs no O_bar: the intra kernel skips it
+    fi.Ob = nullptr;
+    fi.pp_kn = a.KN; fi.pp_kh = a.KH; fi.pp_qt = a.QT; fi.pp_vh = a.VH; fi.pp_lam = a.LAM;
     e = gdr::launch_chunk(fd, fi, 1, st);
     if (e == hipSuccess) e = gdr::launch_bwd_prep(a, d.dk, ns, st);
     f.c0 = r.c0 = 0;

@@ -20,9 +20,11 @@
 // chain kernel, with M^T and Q'^T dO in its M and N slots.
 //
 // Order of a call (gdr_chunk_bwd): the forward's intra-chunk kernel
-// recomputes the chunk maps; the prep kernel forms M^T and Q'^T dO; the forward
-// chain (chunk-start states) and the reverse chain (X) run side by side in one
-// launch; then per chunk the pre-pass, the Gram kernel (A, T^-1), the dense
+// recomputes the chunk maps and, beside them, writes the per-token vectors
+// kn, k_hat, q_tilde, v_hat and the in-chunk cumulative log decay Lambda
+// (its pre-pass already forms them); the prep kernel forms M^T and Q'^T dO;
+// the forward chain (chunk-start states) and the reverse chain (X) run side
+// by side in one launch; then per chunk the Gram kernel (A, T^-1), the dense
 // products and the Gram backprop with the chains to the inputs; last dgamma.
 // Everything is fp32 (products on the fp32 matrix cores, v_mfma_f32_16x16x4);
 // the stages hand over through per-chunk scratch of the workspace.  Pair decays
@@ -169,13 +171,15 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdArgs a) {
     for (int jt = 0; jt < NMT; ++jt) G[((RT * w + rt) * NMT + jt) * 64 + lane] = acc[rt][jt];
 }
 
-// ---------------------------------------------------------------------------
-// Pre-pass: per chunk slot, the forward's per-token vectors kn, k_hat,
-// q_tilde, v_hat and the cumulative log-decay Lambda.  Wave w takes tokens
-// 16w..16w+15, lane CPL = D / 64 consecutive channels; Lambda is summed along
-// the wave's tokens in registers, then offset by the earlier waves' totals.
-// Padding tokens past T are zero (identity steps).
-// ---------------------------------------------------------------------------
+template <int N>
+__device__ __forceinline__ void stc(float *p, const float (&x)[N]) {
+  if constexpr (N == 2)
+    *reinterpret_cast<float2 *>(p) = float2{x[0], x[1]};
+  else
+#pragma unroll
+    for (int u = 0; u < N; ++u) p[u] = x[u];
+}
+
 template <bool BF, int N>
 __device__ __forceinline__ void ldc(const void *p, size_t i, float (&o)[N]) {
   if constexpr (N == 2) {
@@ -191,101 +195,6 @@ __device__ __forceinline__ void ldc(const void *p, size_t i, float (&o)[N]) {
   } else {
 #pragma unroll
     for (int u = 0; u < N; ++u) o[u] = ld1<BF>(p, i + u);
-  }
-}
-
-template <int N>
-__device__ __forceinline__ void stc(float *p, const float (&x)[N]) {
-  if constexpr (N == 2)
-    *reinterpret_cast<float2 *>(p) = float2{x[0], x[1]};
-  else
-#pragma unroll
-    for (int u = 0; u < N; ++u) p[u] = x[u];
-}
-
-template <int D, bool BF>
-__global__ void __launch_bounds__(256) bwd_prepass_kernel(BwdArgs a) {
-  constexpr int C = kBC, CPL = D / 64, TW = C / 4;
-  __shared__ float tot[4][D];
-  const size_t slot = blockIdx.x;
-  const SlotTokens st = slot_tokens(a, slot);
-  const int h = st.head;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, ch0 = CPL * lane;
-  const size_t base = slot * (size_t)C * D;
-  float gam[CPL], run[CPL], lam[TW][CPL];
-#pragma unroll
-  for (int u = 0; u < CPL; ++u) {
-    gam[u] = a.gamma ? a.gamma[(size_t)h * D + ch0 + u] : 1.f;
-    run[u] = 0.f;
-  }
-#pragma unroll
-  for (int j = 0; j < TW; ++j) {
-    const int t = TW * w + j;
-    const bool ok = t < st.valid;  // uniform over the wave
-    const size_t row = st.row + (ok ? t : 0);
-    float qv[CPL], kv[CPL], vv[CPL], zv[CPL], bg[CPL], wg[CPL], la[CPL];
-    float sq = 0.f, sk = 0.f;
-    if (ok) {
-      ldc<BF, CPL>(a.q, row * D + ch0, qv);
-      ldc<BF, CPL>(a.k, row * D + ch0, kv);
-      ldc<BF, CPL>(a.v, row * D + ch0, vv);
-#pragma unroll
-      for (int u = 0; u < CPL; ++u) {
-        zv[u] = a.z ? ld1<BF>(a.z, row * D + ch0 + u) : 0.f;
-        bg[u] = gate_at<BF>(a.b, a.b_mode, row, ch0 + u, D);
-        wg[u] = gate_at<BF>(a.w, a.w_mode, row, ch0 + u, D);
-        la[u] = log_alpha_at(a.log_alpha, a.alpha_mode, row, ch0 + u, D);
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < CPL; ++u) qv[u] = kv[u] = vv[u] = zv[u] = bg[u] = wg[u] = la[u] = 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < CPL; ++u) {
-      if (a.normalize_qk) {
-        qv[u] = silu(qv[u]);
-        kv[u] = silu(kv[u]);
-      }
-      sq += qv[u] * qv[u];
-      sk += kv[u] * kv[u];
-    }
-    float iq = 1.f, ik = 1.f;
-    if (a.normalize_qk) {
-      iq = 1.f / fmaxf(sqrtf(wave_sum(sq)), 1e-12f);
-      ik = 1.f / fmaxf(sqrtf(wave_sum(sk)), 1e-12f);
-    }
-    float kn[CPL], kh[CPL], qt[CPL], vh[CPL];
-#pragma unroll
-    for (int u = 0; u < CPL; ++u) {
-      const float dyn = (a.z && ok) ? 2.f / (1.f + expf(-zv[u])) : 1.f;
-      kn[u] = kv[u] * ik;
-      kh[u] = bg[u] * kn[u];
-      qt[u] = ok ? a.scale * gam[u] * dyn * qv[u] * iq : 0.f;
-      vh[u] = wg[u] * vv[u];
-      run[u] += la[u];
-      lam[j][u] = run[u];
-    }
-    const size_t o = base + (size_t)t * D + ch0;
-    stc<CPL>(a.KN + o, kn);
-    stc<CPL>(a.KH + o, kh);
-    stc<CPL>(a.QT + o, qt);
-    stc<CPL>(a.VH + o, vh);
-  }
-#pragma unroll
-  for (int u = 0; u < CPL; ++u) tot[w][ch0 + u] = run[u];
-  __syncthreads();
-  float off[CPL];
-#pragma unroll
-  for (int u = 0; u < CPL; ++u) {
-    off[u] = 0.f;
-    for (int w2 = 0; w2 < w; ++w2) off[u] += tot[w2][ch0 + u];
-  }
-#pragma unroll
-  for (int j = 0; j < TW; ++j) {
-    float x[CPL];
-#pragma unroll
-    for (int u = 0; u < CPL; ++u) x[u] = lam[j][u] + off[u];
-    stc<CPL>(a.LAM + base + (size_t)(TW * w + j) * D + ch0, x);
   }
 }
 
@@ -1094,7 +1003,6 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
       hipLaunchKernelGGL((bwd_dgamma_kernel<D>), dim3((unsigned)(a.H * (D / 32))), dim3(256), 0, st, a);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((bwd_prepass_kernel<D, BF>), dim3(nch), dim3(256), 0, st, a);
   hipLaunchKernelGGL((bwd_gram_kernel<D>), dim3(nch), dim3(256), 0, st, a);
   hipLaunchKernelGGL((bwd_mm_kernel<D, NS>), dim3(nch), dim3(256), 0, st, a);
   hipLaunchKernelGGL((bwd_gramback_kernel<D, BF>), dim3(nch), dim3(256), 0, st, a);

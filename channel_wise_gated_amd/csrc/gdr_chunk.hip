@@ -166,7 +166,10 @@ __device__ __forceinline__ int tp_chan(int ks, int g, int e) { return 32 * ks + 
 // block pair, which leaves the channel dimension of the Gram products free of
 // per-pair factors: kn * Cf is split into bf16 planes once, in the pre-pass,
 // and the pair factor D_ij scales the accumulated tile.
-template <int C, int D, int NS, bool BF, bool SA>
+// PP: also write the per-token vectors the backward reads (kn, k_hat, q_tilde,
+// v_hat and the in-chunk cumulative log decay; zero on padding rows) to the
+// pp arrays, [slot][C][D] fp32 each.
+template <int C, int D, int NS, bool BF, bool SA, bool PP = false>
 __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
   static_assert(!SA || NS == 2, "the scalar-decay kernel keeps kn * Cf as two bf16 planes in the kn * Cf region");
   using Lds = IntraLds<C, D, NS>;
@@ -197,7 +200,17 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
   size_t row0;  // first token row
   if (a.ctab) {  // packed batch: slot = entry * H + head
     const int4 e = a.ctab[ch / a.H];
-    if (e.x < 0) return;  // past the last chunk (the grid is an upper bound)
+    if (e.x < 0) {  // past the last chunk (the grid is an upper bound)
+      if constexpr (PP) {  // the backward still reads the slot: zeros
+        float *pp[5] = {a.pp_kn, a.pp_kh, a.pp_qt, a.pp_vh, a.pp_lam};
+        const size_t o = ch * (size_t)C * D;
+#pragma unroll
+        for (int q = 0; q < 5; ++q)
+          for (int x = threadIdx.x; x < C * D / 4; x += blockDim.x)
+            reinterpret_cast<float4 *>(pp[q] + o)[x] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      return;
+    }
     h = (int)(ch % a.H);
     row0 = (size_t)h * a.T + e.z;
     tvalid = e.w;
@@ -222,6 +235,15 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
   const bool tok_ok = t < tvalid;
   const size_t rowt = row0 + min(t, tvalid - 1);  // row the lane's inputs are read from
   auto rowc = [&](int tt) { return row0 + min(tt, tvalid - 1); };
+
+  // PP: the lane's 8 values of k-step ks (channels tp_chan(ks, g, 0..7): two
+  // runs of 4) into row t of a [slot][C][D] array
+  auto pp_store = [&](float *arr, int ks, const float x[8]) {
+    float *r = arr + (ch * (size_t)C + t) * D + 32 * ks + 4 * g;
+    *reinterpret_cast<float4 *>(r) = make_float4(x[0], x[1], x[2], x[3]);
+    *reinterpret_cast<float4 *>(r + 16) = make_float4(x[4], x[5], x[6], x[7]);
+  };
+  float pp_lam[PP ? NKD : 1][8];  // PP: the in-block decay prefix, kept for Lambda
 
   // ----------------------------------------------------------- A: pre-pass
   // QRp / KRp: NS bf16 planes of qt * R and k_hat * R, R = exp(P_t), P the
@@ -339,6 +361,21 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
         KR[e] = bbv[e] * kn * R;
         KC[e] = kn * Cf;
       }
+      if constexpr (PP) {
+        float kn8[8], kh8[8], qt8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float kn = tok_ok ? kv[ks][e] * nk : 0.f;
+          kn8[e] = kn;
+          kh8[e] = bbv[e] * kn;
+          qt8[e] = tok_ok ? fq[e] * qv[ks][e] * nq : 0.f;
+          if constexpr (SA) pp_lam[ks][e] = P1;
+          else pp_lam[ks][e] = lv[ks][e];
+        }
+        pp_store(a.pp_kn, ks, kn8);
+        pp_store(a.pp_kh, ks, kh8);
+        pp_store(a.pp_qt, ks, qt8);
+      }
       if (l16 == 15) {  // channels tp_chan(ks, g, 0..3) and (ks, g, 4..7) are two runs of 4
         float *cb = cum + (i + 1) * D + 32 * ks + 4 * g;
         *reinterpret_cast<float4 *>(cb) = make_float4(tot[0], tot[1], tot[2], tot[3]);
@@ -373,6 +410,24 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
     }
   }
   __syncthreads();
+
+  if constexpr (PP) {  // Lambda_t = block-start cumulative log decay + in-block prefix
+    if (rowwave) {
+#pragma unroll
+      for (int ks = 0; ks < NKD; ++ks) {
+        float x[8];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const float4 f = *reinterpret_cast<const float4 *>(cum + i * D + 32 * ks + 16 * hh + 4 * g);
+          x[4 * hh] = f.x + pp_lam[ks][4 * hh];
+          x[4 * hh + 1] = f.y + pp_lam[ks][4 * hh + 1];
+          x[4 * hh + 2] = f.z + pp_lam[ks][4 * hh + 2];
+          x[4 * hh + 3] = f.w + pp_lam[ks][4 * hh + 3];
+        }
+        pp_store(a.pp_lam, ks, x);
+      }
+    }
+  }
 
   // pair decay factors D_ij[c] = exp(cum_i - cum_{j+1}) for j <= i, one
   // exponential per (pair, channel), kept in the (still unused) staging area
@@ -727,6 +782,7 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
       float4 *dst = reinterpret_cast<float4 *>(vhat + ((i * NKD + ks) * 64 + lane) * 8);
       dst[0] = make_float4(x[0], x[1], x[2], x[3]);
       dst[1] = make_float4(x[4], x[5], x[6], x[7]);
+      if constexpr (PP) pp_store(a.pp_vh, ks, x);
     }
   }
 
@@ -1314,12 +1370,24 @@ static hipError_t launch_chunk_pass(const ChunkArgs &a, size_t nch, int phases, 
   using Lds = IntraLds<C, D, NS>;
   const size_t nbh = (size_t)a.B * a.H;
   if (nch > 0 && (phases & 1)) {
-    if (NS == 2 && a.alpha_mode != GDR_GATE_PER_CHANNEL)  // scalar decay
-      hipLaunchKernelGGL((chunk_intra_kernel<C, D, NS, BF, NS == 2>), dim3((unsigned)nch), dim3(64 * Lds::WAVES),
-                         Lds::bytes, st, a);
-    else
-      hipLaunchKernelGGL((chunk_intra_kernel<C, D, NS, BF, false>), dim3((unsigned)nch), dim3(64 * Lds::WAVES),
-                         Lds::bytes, st, a);
+    const bool sa = NS == 2 && a.alpha_mode != GDR_GATE_PER_CHANNEL;  // scalar decay
+    const dim3 grid((unsigned)nch), block(64 * Lds::WAVES);
+    bool pp = false;
+    if constexpr (C == 64) {
+      if (a.pp_kn) {  // the backward's recompute: the per-token vectors as well
+        pp = true;
+        if (sa)
+          hipLaunchKernelGGL((chunk_intra_kernel<C, D, NS, BF, NS == 2, true>), grid, block, Lds::bytes, st, a);
+        else
+          hipLaunchKernelGGL((chunk_intra_kernel<C, D, NS, BF, false, true>), grid, block, Lds::bytes, st, a);
+      }
+    }
+    if (!pp) {
+      if (sa)
+        hipLaunchKernelGGL((chunk_intra_kernel<C, D, NS, BF, NS == 2>), grid, block, Lds::bytes, st, a);
+      else
+        hipLaunchKernelGGL((chunk_intra_kernel<C, D, NS, BF, false>), grid, block, Lds::bytes, st, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1392,6 +1460,14 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, int phases, hipStream_t st,
       if (e == hipSuccess && NS == 2)
         e = hipFuncSetAttribute(reinterpret_cast<const void *>(&chunk_intra_kernel<C, D, NS, BF, NS == 2>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lds::bytes);
+      if constexpr (C == 64) {
+        if (e == hipSuccess)
+          e = hipFuncSetAttribute(reinterpret_cast<const void *>(&chunk_intra_kernel<C, D, NS, BF, false, true>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lds::bytes);
+        if (e == hipSuccess && NS == 2)
+          e = hipFuncSetAttribute(reinterpret_cast<const void *>(&chunk_intra_kernel<C, D, NS, BF, NS == 2, true>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lds::bytes);
+      }
       if (e == hipSuccess)
         e = hipFuncSetAttribute(reinterpret_cast<const void *>(&chunk_out_kernel<C, D, NS, OB16, false>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)out_lds);

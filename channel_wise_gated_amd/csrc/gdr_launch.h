@@ -44,6 +44,10 @@ struct ChunkArgs {
   float oeps;
   float *oraw;  // gated output only: o itself as well ([B,H,T,dv] fp32), or null
   void *y;
+  // Intra-chunk kernel at C = 64 for the backward (all null otherwise): the
+  // per-token vectors kn, k_hat, q_tilde, v_hat and the in-chunk cumulative
+  // log decay, [slot][C][D] fp32 each, zero on padding rows.
+  float *pp_kn, *pp_kh, *pp_qt, *pp_vh, *pp_lam;
 };
 
 // The five-gate projection: x [N, dm] bf16 (N = B*T tokens), wd [R, dm]
