@@ -770,6 +770,9 @@ __global__ void __launch_bounds__(256) bwd_gramback_kernel(BwdArgs a) {
       rq = fmaxf(sqrtf(group16_sum(nq)), 1e-12f);
       rk = fmaxf(sqrtf(group16_sum(nk)), 1e-12f);
     }
+    // hardware reciprocals (1 ulp) and exponentials: the per-channel chains
+    // below take no IEEE division
+    const float irq = fast_rcp(rq), irk = fast_rcp(rk);
     float dqh[NCT], dkn[NCT], dzv[NCT], dbv[NCT], dwv[NCT], dvv[NCT];
     float dotq = 0.f, dotk = 0.f, sdb = 0.f, sdw = 0.f;
 #pragma unroll
@@ -779,9 +782,9 @@ __global__ void __launch_bounds__(256) bwd_gramback_kernel(BwdArgs a) {
       dlv[r][ct] = q[ct] * at * dqa[ct] + h[ct] * at * dka[ct] - kn[ct] * rat * dkp[ct] + q[ct] * RA[ct] +
                    h[ct] * RL[ct] - kn[ct] * CS[ct];
       skp[ct] += kn[ct] * rat * dkp[ct];
-      const float qh = sq[ct] / rq, knv = sn[ct] / rk;
+      const float qh = sq[ct] * irq, knv = sn[ct] * irk;
       const float gam = a.gamma ? a.gamma[(size_t)hd * D + c0 + ct] : 1.f;
-      const float sg = 1.f / (1.f + expf(-zx[ct]));
+      const float sg = fast_rcp(1.f + __expf(-zx[ct]));
       const float dyn = a.z ? 2.f * sg : 1.f;
       dqh[ct] = dqt * a.scale * gam * dyn;
       if (live) gac[ct] += dqt * a.scale * dyn * qh;
@@ -808,10 +811,11 @@ __global__ void __launch_bounds__(256) bwd_gramback_kernel(BwdArgs a) {
       gk[ct] = dkn[ct];
       if (a.normalize_qk) {
         // through y = s / max(|s|, 1e-12), then s = SiLU(x)
-        const float qh = sq[ct] / rq, knv = sn[ct] / rk;
-        gq[ct] = rq > 1e-12f ? (gq[ct] - qh * dotq) / rq : gq[ct] / 1e-12f;
-        gk[ct] = rk > 1e-12f ? (gk[ct] - knv * dotk) / rk : gk[ct] / 1e-12f;
-        const float sgq = 1.f / (1.f + expf(-qx[ct])), sgk = 1.f / (1.f + expf(-kx[ct]));
+        // (at the 1e-12 floor the norm is a constant: only the 1 / 1e-12 scale)
+        const float qh = sq[ct] * irq, knv = sn[ct] * irk;
+        gq[ct] = (rq > 1e-12f ? gq[ct] - qh * dotq : gq[ct]) * irq;
+        gk[ct] = (rk > 1e-12f ? gk[ct] - knv * dotk : gk[ct]) * irk;
+        const float sgq = fast_rcp(1.f + __expf(-qx[ct])), sgk = fast_rcp(1.f + __expf(-kx[ct]));
         gq[ct] *= sgq * (1.f + qx[ct] * (1.f - sgq));
         gk[ct] *= sgk * (1.f + kx[ct] * (1.f - sgk));
       }
