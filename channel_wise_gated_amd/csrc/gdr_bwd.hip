@@ -695,17 +695,34 @@ __global__ void __launch_bounds__(256) bwd_gramback_kernel(BwdArgs a) {
   row(ILA, C - 1, lc);
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) skp[ct] = gac[ct] = 0.f;
+  // the per-token rows of the dense products' gradients, one token ahead:
+  // token r + 1's loads are in flight during token r's work
+  struct TokRows {
+    float dqa[NCT], dka[NCT], dkp[NCT], du[NCT];
+  };
+  auto load_rows = [&](int r, TokRows &R) {
+    const int t = 16 * w + 4 * g + r;
+    rowg(a.DQA, t, R.dqa);
+    rowg(a.DKA, t, R.dka);
+    rowg(a.DKP, t, R.dkp);
+    rowg(a.DU, t, R.du);
+  };
+  TokRows cur;
+  load_rows(0, cur);
 #pragma unroll 1
   for (int r = 0; r < 4; ++r) {
     const int t = 16 * w + 4 * g + r;
-    float lt[NCT], q[NCT], h[NCT], kn[NCT], dqa[NCT], dka[NCT], dkp[NCT];
+    TokRows nxt;
+    load_rows(r < 3 ? r + 1 : 3, nxt);  // the last token re-reads its own rows
+    const float(&dqa)[NCT] = cur.dqa;
+    const float(&dka)[NCT] = cur.dka;
+    const float(&dkp)[NCT] = cur.dkp;
+    const float(&du)[NCT] = cur.du;
+    float lt[NCT], q[NCT], h[NCT], kn[NCT];
     row(ILA, t, lt);
     row(IQT, t, q);
     row(IKH, t, h);
     row(IKN, t, kn);
-    rowg(a.DQA, t, dqa);
-    rowg(a.DKA, t, dka);
-    rowg(a.DKP, t, dkp);
     float RA[NCT], RL[NCT], CS[NCT];
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
@@ -741,7 +758,7 @@ __global__ void __launch_bounds__(256) bwd_gramback_kernel(BwdArgs a) {
     // the gates); reductions over a token's channels stay in its 16 lanes
     const bool live = t < st.valid;
     const size_t grow = st.row + (live ? t : 0);
-    float qx[NCT], kx[NCT], vx[NCT], zx[NCT], bg[NCT], wg[NCT], du[NCT];
+    float qx[NCT], kx[NCT], vx[NCT], zx[NCT], bg[NCT], wg[NCT];
     ldn<BF, NCT>(a.q, grow * D + c0, qx);
     ldn<BF, NCT>(a.k, grow * D + c0, kx);
     ldn<BF, NCT>(a.v, grow * D + c0, vx);
@@ -756,7 +773,6 @@ __global__ void __launch_bounds__(256) bwd_gramback_kernel(BwdArgs a) {
       gate4<BF>(a.b, a.b_mode, grow, c0 + 4 * v, D, bg + 4 * v);
       gate4<BF>(a.w, a.w_mode, grow, c0 + 4 * v, D, wg + 4 * v);
     }
-    rowg(a.DU, t, du);
     float sq[NCT], sn[NCT], nq = 0.f, nk = 0.f;
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
@@ -833,6 +849,7 @@ __global__ void __launch_bounds__(256) bwd_gramback_kernel(BwdArgs a) {
         if (a.dw && a.w_mode == GDR_GATE_PER_TOKEN) a.dw[grow] = sdw;
       }
     }
+    cur = nxt;
   }
   __syncthreads();  // the staged arrays are read for the last time
 #pragma unroll
