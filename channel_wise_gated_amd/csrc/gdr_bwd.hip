@@ -709,11 +709,45 @@ __global__ void __launch_bounds__(256) bwd_gramback_kernel(BwdArgs a) {
   };
   TokRows cur;
   load_rows(0, cur);
+  // bf16 inputs: the token's raw q, k, v, z and per-channel b, w (NCT bf16
+  // each, as 32-bit pairs), also one token ahead
+  constexpr int NP = BF ? NCT / 2 : 1;
+  struct TokRaw {
+    uint32_t q[NP], k[NP], v[NP], z[NP], b[NP], w[NP];
+  };
+  auto load_raw = [&](int r, TokRaw &R) {
+    if constexpr (BF) {
+      const int t = 16 * w + 4 * g + r;
+      const size_t o = (st.row + (t < st.valid ? t : 0)) * D + c0;
+      auto ld = [&](const void *p, uint32_t(&x)[NP]) {
+        const uint32_t *src = reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(p) + o);
+#pragma unroll
+        for (int i = 0; i < NP; ++i) x[i] = src[i];
+      };
+      ld(a.q, R.q);
+      ld(a.k, R.k);
+      ld(a.v, R.v);
+      if (a.z) ld(a.z, R.z);
+      if (a.b_mode == GDR_GATE_PER_CHANNEL) ld(a.b, R.b);
+      if (a.w_mode == GDR_GATE_PER_CHANNEL) ld(a.w, R.w);
+    }
+  };
+  auto unpack = [](const uint32_t(&x)[NP], float(&o)[NCT]) {
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      o[2 * i] = __uint_as_float(x[i] << 16);
+      o[2 * i + 1] = __uint_as_float(x[i] & 0xffff0000u);
+    }
+  };
+  TokRaw craw;
+  load_raw(0, craw);
 #pragma unroll 1
   for (int r = 0; r < 4; ++r) {
     const int t = 16 * w + 4 * g + r;
     TokRows nxt;
+    TokRaw nraw;
     load_rows(r < 3 ? r + 1 : 3, nxt);  // the last token re-reads its own rows
+    load_raw(r < 3 ? r + 1 : 3, nraw);
     const float(&dqa)[NCT] = cur.dqa;
     const float(&dka)[NCT] = cur.dka;
     const float(&dkp)[NCT] = cur.dkp;
@@ -759,19 +793,33 @@ __global__ void __launch_bounds__(256) bwd_gramback_kernel(BwdArgs a) {
     const bool live = t < st.valid;
     const size_t grow = st.row + (live ? t : 0);
     float qx[NCT], kx[NCT], vx[NCT], zx[NCT], bg[NCT], wg[NCT];
-    ldn<BF, NCT>(a.q, grow * D + c0, qx);
-    ldn<BF, NCT>(a.k, grow * D + c0, kx);
-    ldn<BF, NCT>(a.v, grow * D + c0, vx);
+    if constexpr (BF) {
+      unpack(craw.q, qx);
+      unpack(craw.k, kx);
+      unpack(craw.v, vx);
+    } else {
+      ldn<BF, NCT>(a.q, grow * D + c0, qx);
+      ldn<BF, NCT>(a.k, grow * D + c0, kx);
+      ldn<BF, NCT>(a.v, grow * D + c0, vx);
+    }
     if (a.z) {
-      ldn<BF, NCT>(a.z, grow * D + c0, zx);
+      if constexpr (BF) unpack(craw.z, zx);
+      else ldn<BF, NCT>(a.z, grow * D + c0, zx);
     } else {
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) zx[ct] = 0.f;
     }
+    if (BF && a.b_mode == GDR_GATE_PER_CHANNEL) {
+      if constexpr (BF) unpack(craw.b, bg);
+    } else {
 #pragma unroll
-    for (int v = 0; v < NV; ++v) {
-      gate4<BF>(a.b, a.b_mode, grow, c0 + 4 * v, D, bg + 4 * v);
-      gate4<BF>(a.w, a.w_mode, grow, c0 + 4 * v, D, wg + 4 * v);
+      for (int v = 0; v < NV; ++v) gate4<BF>(a.b, a.b_mode, grow, c0 + 4 * v, D, bg + 4 * v);
+    }
+    if (BF && a.w_mode == GDR_GATE_PER_CHANNEL) {
+      if constexpr (BF) unpack(craw.w, wg);
+    } else {
+#pragma unroll
+      for (int v = 0; v < NV; ++v) gate4<BF>(a.w, a.w_mode, grow, c0 + 4 * v, D, wg + 4 * v);
     }
     float sq[NCT], sn[NCT], nq = 0.f, nk = 0.f;
 #pragma unroll
@@ -850,6 +898,7 @@ __global__ void __launch_bounds__(256) bwd_gramback_kernel(BwdArgs a) {
       }
     }
     cur = nxt;
+    craw = nraw;
   }
   __syncthreads();  // the staged arrays are read for the last time
 #pragma unroll
@@ -872,10 +921,19 @@ __global__ void __launch_bounds__(256) bwd_gramback_kernel(BwdArgs a) {
     }
     a.gpart[slot * D + ch] = gs;
     const bool per_ch = a.dla && a.alpha_mode == GDR_GATE_PER_CHANNEL;
+    // the channel's C values read at once, summed in registers
+    float dv[C];
+#pragma unroll
+    for (int t = 0; t < C; ++t) dv[t] = dl[t * SPD + ch];
+#pragma unroll
     for (int t = C - 1; t >= 0; --t) {
-      run += dl[t * SPD + ch];
-      dl[t * SPD + ch] = run;
-      if (per_ch && t < st.valid) a.dla[(st.row + t) * D + ch] = run;
+      run += dv[t];
+      dv[t] = run;
+    }
+#pragma unroll
+    for (int t = 0; t < C; ++t) {
+      dl[t * SPD + ch] = dv[t];
+      if (per_ch && t < st.valid) a.dla[(st.row + t) * D + ch] = dv[t];
     }
   }
   if (a.dla && a.alpha_mode == GDR_GATE_PER_TOKEN) {
