@@ -253,10 +253,12 @@ gdr_status bwd_call(const gdr_desc *desc, int nseq, const int *cu, const void *q
     // then M^T and Q'^T dO; then the forward chain (chunk-start states) and
     // the reverse chain side by side
     // the backward needs no O_bar (the intra kernel skips it) but the
-    // per-token vectors, which the same kernel writes beside the maps
+    // per-token vectors and the chunk system's A and T^-1, which the same
+    // kernel writes beside the maps
     gdr::ChunkArgs fi = f;
     fi.Ob = nullptr;
     fi.pp_kn = a.KN; fi.pp_kh = a.KH; fi.pp_qt = a.QT; fi.pp_vh = a.VH; fi.pp_lam = a.LAM;
+    fi.pp_am = a.AM; fi.pp_ti = a.TI;
     e = gdr::launch_chunk(fd, fi, 1, st);
     if (e == hipSuccess) e = gdr::launch_bwd_prep(a, d.dk, ns, st);
     f.c0 = r.c0 = 0;

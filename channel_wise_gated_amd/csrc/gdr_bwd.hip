@@ -22,10 +22,11 @@
 // Order of a call (gdr_chunk_bwd): the forward's intra-chunk kernel
 // recomputes the chunk maps and, beside them, writes the per-token vectors
 // kn, k_hat, q_tilde, v_hat and the in-chunk cumulative log decay Lambda
-// (its pre-pass already forms them); the prep kernel forms M^T and Q'^T dO;
+// (its pre-pass already forms them) and the chunk system's A and T^-1 (its
+// Gram and solve phases form them); the prep kernel forms M^T and Q'^T dO;
 // the forward chain (chunk-start states) and the reverse chain (X) run side
-// by side in one launch; then per chunk the Gram kernel (A, T^-1), the dense
-// products and the Gram backprop with the chains to the inputs; last dgamma.
+// by side in one launch; then per chunk the dense products and the Gram
+// backprop with the chains to the inputs; last dgamma.
 // Everything is fp32 (products on the fp32 matrix cores, v_mfma_f32_16x16x4);
 // the stages hand over through per-chunk scratch of the workspace.  Pair decays
 // are split at per-block pivots, with a pair-by-pair path for steep blocks.
@@ -171,6 +172,12 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdArgs a) {
     for (int jt = 0; jt < NMT; ++jt) G[((RT * w + rt) * NMT + jt) * 64 + lane] = acc[rt][jt];
 }
 
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, kWave));
+  return x;
+}
+
 template <int N>
 __device__ __forceinline__ void stc(float *p, const float (&x)[N]) {
   if constexpr (N == 2)
@@ -198,111 +205,6 @@ __device__ __forceinline__ void ldc(const void *p, size_t i, float (&o)[N]) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// Gram: per chunk slot, A (s <= t) and L (s < t), A_ts = sum_i q_tilde_ti
-// kn_si e^{Lambda_ti - Lambda_si} and L_ts likewise with k_hat, on the fp32
-// matrix cores by 16 x 16 tiles: the pair decay is split at a per-channel pivot
-// P, e^{Lambda_t - P} on the t side and e^{P - Lambda_s} on the s side.  For a
-// tile below the diagonal P is Lambda at the s-block's last token, so both
-// factors are <= 1 (a factor that underflows belongs to a product that does
-// too).  For a diagonal tile P is Lambda at the block's first token: the s-side
-// factor grows to e^{range} over the block; when the range exceeds 60 (far
-// from fp32 overflow) the tile is recomputed pair by pair.  Then
-// T^-1 = (I + L)^-1 column by column (forward substitution, four lanes a
-// column).
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, kWave));
-  return x;
-}
-
-template <int D>
-__global__ void __launch_bounds__(256) bwd_gram_kernel(BwdArgs a) {
-  constexpr int C = kBC, NKB = D / 16, LP = C + 1;
-  constexpr float kMaxRange = 60.f;
-  static_assert(C == 64, "tile list for four 16-token blocks");
-  __shared__ float L[C * LP], ti[C * LP];
-  const size_t slot = blockIdx.x;
-  const size_t base = slot * (size_t)C * D, cbase = slot * (size_t)C * C;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, g = lane >> 4;
-  for (int e = tid; e < C * C; e += 256) {
-    const int t = e / C, s2 = e % C;
-    if ((s2 >> 4) > (t >> 4)) a.AM[cbase + e] = 0.f;  // tiles above the diagonal
-  }
-  // the ten tiles (tb, sb), sb <= tb: diagonal first, wave w takes w, w + 4, w + 8
-  // nibble k of each word: tb and sb of tile k
-  constexpr unsigned long long kTb = 0x3323213210ull, kSb = 0x0102103210ull;
-  for (int k = w; k < 10; k += 4) {
-    const int tb = (int)((kTb >> (4 * k)) & 15), sb = (int)((kSb >> (4 * k)) & 15);
-    const bool diag = tb == sb;
-    const int prow = diag ? 16 * sb : 16 * sb + 15;
-    const size_t rt = base + (size_t)(16 * tb + l16) * D, rs = base + (size_t)(16 * sb + l16) * D,
-                 rp = base + (size_t)prow * D;
-    f32x4 accA = zero4(), accL = zero4();
-    float emax = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      const int i0 = 16 * kb + 4 * g;
-      const float4 qt = *reinterpret_cast<const float4 *>(a.QT + rt + i0);
-      const float4 kh = *reinterpret_cast<const float4 *>(a.KH + rt + i0);
-      const float4 lt = *reinterpret_cast<const float4 *>(a.LAM + rt + i0);
-      const float4 kn = *reinterpret_cast<const float4 *>(a.KN + rs + i0);
-      const float4 ls = *reinterpret_cast<const float4 *>(a.LAM + rs + i0);
-      const float4 lp = *reinterpret_cast<const float4 *>(a.LAM + rp + i0);
-      const float q4[4] = {qt.x, qt.y, qt.z, qt.w}, h4[4] = {kh.x, kh.y, kh.z, kh.w};
-      const float t4[4] = {lt.x, lt.y, lt.z, lt.w}, n4[4] = {kn.x, kn.y, kn.z, kn.w};
-      const float s4[4] = {ls.x, ls.y, ls.z, ls.w}, p4[4] = {lp.x, lp.y, lp.z, lp.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float fa = __expf(t4[e] - p4[e]), xb = p4[e] - s4[e];
-        emax = fmaxf(emax, xb);
-        const float b = n4[e] * __expf(xb);
-        accA = mfma4(q4[e] * fa, b, accA);
-        accL = mfma4(h4[e] * fa, b, accL);
-      }
-    }
-    if (diag && wave_max(emax) > kMaxRange) {
-      // steep decay over the block: every pair of the lane's outputs exactly
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * tb + 4 * g + r, s2 = 16 * sb + l16;
-        float sa = 0.f, sl = 0.f;
-        if (s2 <= t)
-          for (int i = 0; i < D; ++i) {
-            const float x = a.KN[base + (size_t)s2 * D + i] *
-                            __expf(a.LAM[base + (size_t)t * D + i] - a.LAM[base + (size_t)s2 * D + i]);
-            sa += a.QT[base + (size_t)t * D + i] * x;
-            sl += a.KH[base + (size_t)t * D + i] * x;
-          }
-        accA[r] = sa;
-        accL[r] = sl;
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 16 * tb + 4 * g + r, s2 = 16 * sb + l16;
-      a.AM[cbase + (size_t)t * C + s2] = (!diag || s2 <= t) ? accA[r] : 0.f;
-      L[t * LP + s2] = (!diag || s2 < t) ? accL[r] : 0.f;
-    }
-  }
-  __syncthreads();
-  // T^-1 column s by four adjacent lanes (each summing every fourth r):
-  // x_t = delta_ts - sum_{s <= r < t} L[t][r] x_r
-  {
-    const int s2 = tid >> 2, j = tid & 3;
-    for (int t = 0; t < C; ++t) {
-      float part = 0.f;
-      if (t > s2)
-        for (int r = s2 + j; r < t; r += 4) part += L[t * LP + r] * ti[r * LP + s2];
-      part += __shfl_xor(part, 1, kWave);
-      part += __shfl_xor(part, 2, kWave);
-      if (j == 0) ti[t * LP + s2] = (t == s2 ? 1.f : 0.f) - part;
-    }
-  }
-  __syncthreads();
-  for (int e = tid; e < C * C; e += 256) a.TI[cbase + e] = ti[(e / C) * LP + e % C];
-}
 
 // ---------------------------------------------------------------------------
 // Dense products: per chunk slot, the products of the chunk system's reverse, on the
@@ -1082,7 +984,6 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
       hipLaunchKernelGGL((bwd_dgamma_kernel<D>), dim3((unsigned)(a.H * (D / 32))), dim3(256), 0, st, a);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((bwd_gram_kernel<D>), dim3(nch), dim3(256), 0, st, a);
   hipLaunchKernelGGL((bwd_mm_kernel<D, NS>), dim3(nch), dim3(256), 0, st, a);
   hipLaunchKernelGGL((bwd_gramback_kernel<D, BF>), dim3(nch), dim3(256), 0, st, a);
   if (a.dgamma && a.gamma)

@@ -166,9 +166,10 @@ __device__ __forceinline__ int tp_chan(int ks, int g, int e) { return 32 * ks + 
 // block pair, which leaves the channel dimension of the Gram products free of
 // per-pair factors: kn * Cf is split into bf16 planes once, in the pre-pass,
 // and the pair factor D_ij scales the accumulated tile.
-// PP: also write the per-token vectors the backward reads (kn, k_hat, q_tilde,
-// v_hat and the in-chunk cumulative log decay; zero on padding rows) to the
-// pp arrays, [slot][C][D] fp32 each.
+// PP: also write what the backward reads of the chunk: the per-token vectors
+// kn, k_hat, q_tilde, v_hat and the in-chunk cumulative log decay ([slot][C][D]
+// fp32 each, zero on padding rows), and the chunk system's A and T^-1
+// ([slot][C][C] fp32 each).
 template <int C, int D, int NS, bool BF, bool SA, bool PP = false>
 __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
   static_assert(!SA || NS == 2, "the scalar-decay kernel keeps kn * Cf as two bf16 planes in the kn * Cf region");
@@ -202,12 +203,13 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
     const int4 e = a.ctab[ch / a.H];
     if (e.x < 0) {  // past the last chunk (the grid is an upper bound)
       if constexpr (PP) {  // the backward still reads the slot: zeros
-        float *pp[5] = {a.pp_kn, a.pp_kh, a.pp_qt, a.pp_vh, a.pp_lam};
-        const size_t o = ch * (size_t)C * D;
+        float *pp[7] = {a.pp_kn, a.pp_kh, a.pp_qt, a.pp_vh, a.pp_lam, a.pp_am, a.pp_ti};
 #pragma unroll
-        for (int q = 0; q < 5; ++q)
-          for (int x = threadIdx.x; x < C * D / 4; x += blockDim.x)
-            reinterpret_cast<float4 *>(pp[q] + o)[x] = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int q = 0; q < 7; ++q) {
+          const int n4 = q < 5 ? C * D / 4 : C * C / 4;
+          float4 *dst = reinterpret_cast<float4 *>(pp[q] + ch * (size_t)n4 * 4);
+          for (int x = threadIdx.x; x < n4; x += blockDim.x) dst[x] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
       }
       return;
     }
@@ -561,6 +563,14 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
           if (s2 > t) accA[r] = 0.f;
         }
       }
+      if constexpr (PP) {  // A[t][s] (s = 16 j + 4 g + r), zero on padding rows and columns
+        float4 av;
+        av.x = tok_ok && 16 * j + 4 * g < tvalid ? accA[0] : 0.f;
+        av.y = tok_ok && 16 * j + 4 * g + 1 < tvalid ? accA[1] : 0.f;
+        av.z = tok_ok && 16 * j + 4 * g + 2 < tvalid ? accA[2] : 0.f;
+        av.w = tok_ok && 16 * j + 4 * g + 3 < tvalid ? accA[3] : 0.f;
+        *reinterpret_cast<float4 *>(a.pp_am + (ch * (size_t)C + t) * C + 16 * j + 4 * g) = av;
+      }
       if (j == i || !LPRE) {  // diagonal tile: fp32, row-major [t][s], for the leaf inverse
         *reinterpret_cast<float4 *>(Lt + tidx(i, j) * TILE_SZ + l16 * TILE_LD + 4 * g) =
             make_float4(accL[0], accL[1], accL[2], accL[3]);
@@ -585,6 +595,11 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
 #pragma unroll
               for (int p = 0; p < NS; ++p) afr[kk][p][4 * hf + r] = __builtin_bit_cast(__bf16, hp[r][p]);
           }
+    }
+    if constexpr (PP) {  // A's tiles above the diagonal
+      for (int j = i + 1; j < NB; ++j)
+        *reinterpret_cast<float4 *>(a.pp_am + (ch * (size_t)C + t) * C + 16 * j + 4 * g) =
+            make_float4(0.f, 0.f, 0.f, 0.f);
     }
   }
   __syncthreads();
@@ -676,6 +691,13 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
         for (int r = 0; r < 4; ++r) Xc[ii][r] = -Xn[r];
         const float xv[4] = {Xc[ii][0], Xc[ii][1], Xc[ii][2], Xc[ii][3]};
         Xs[ii] = split4<NS>(xv);
+      }
+      if constexpr (PP) {  // column block q of T^-1: tile (ii, q) holds rows 4g..4g+3, column l16
+#pragma unroll
+        for (int ii = 0; ii < NB; ++ii)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            a.pp_ti[(ch * (size_t)C + 16 * ii + 4 * g + r) * C + 16 * q + l16] = ii >= q ? Xc[ii][r] : 0.f;
       }
     }
     __syncthreads();  // every L and X tile has been read before the fragments overwrite them

@@ -48,6 +48,9 @@ struct ChunkArgs {
   // per-token vectors kn, k_hat, q_tilde, v_hat and the in-chunk cumulative
   // log decay, [slot][C][D] fp32 each, zero on padding rows.
   float *pp_kn, *pp_kh, *pp_qt, *pp_vh, *pp_lam;
+  // ... and the chunk system's A (diagonal included) and T^-1, [slot][C][C]
+  // fp32 each, zero above the diagonal and on padding rows and columns of A.
+  float *pp_am, *pp_ti;
 };
 
 // The five-gate projection: x [N, dm] bf16 (N = B*T tokens), wd [R, dm]
