@@ -556,11 +556,25 @@ __global__ void __launch_bounds__(256) bwd_gramback_kernel(BwdArgs a) {
   f32x4 ra[NCT], rl[NCT], cs[NCT];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) ra[ct] = rl[ct] = cs[ct] = zero4();
-#pragma unroll 1
+  // every dA / dL value the loops below read, loaded at once (rows: this
+  // lane's t = 16 w + l16, s over the k-block; columns: s = 16 w + l16, t
+  // over the k-block)
+  float4 rda[4], rdl[4];
+  float cda[4][4], cdl[4][4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    rda[kb] = *reinterpret_cast<const float4 *>(a.DA + cbase + (size_t)(16 * w + l16) * C + 16 * kb + 4 * g);
+    rdl[kb] = *reinterpret_cast<const float4 *>(a.DL + cbase + (size_t)(16 * w + l16) * C + 16 * kb + 4 * g);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      cda[kb][e] = a.DA[cbase + (size_t)(16 * kb + 4 * g + e) * C + 16 * w + l16];
+      cdl[kb][e] = a.DL[cbase + (size_t)(16 * kb + 4 * g + e) * C + 16 * w + l16];
+    }
+  }
+#pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     if (kb < kend) {  // rows: s = 16 kb + 4 g + e
-      const float4 da4 = *reinterpret_cast<const float4 *>(a.DA + cbase + (size_t)(16 * w + l16) * C + 16 * kb + 4 * g);
-      const float4 dl4 = *reinterpret_cast<const float4 *>(a.DL + cbase + (size_t)(16 * w + l16) * C + 16 * kb + 4 * g);
+      const float4 da4 = rda[kb], dl4 = rdl[kb];
       const float av[4] = {da4.x, da4.y, da4.z, da4.w}, lv[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -579,7 +593,7 @@ __global__ void __launch_bounds__(256) bwd_gramback_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = 16 * kb + 4 * g + e;
-        const float dat = a.DA[cbase + (size_t)t * C + 16 * w + l16], dlt = a.DL[cbase + (size_t)t * C + 16 * w + l16];
+        const float dat = cda[kb][e], dlt = cdl[kb][e];
         float q[NCT], h[NCT], lt[NCT];
         row(IQT, t, q);
         row(IKH, t, h);
