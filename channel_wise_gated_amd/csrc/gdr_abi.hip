@@ -521,6 +521,7 @@ gdr_status gdr_check_inputs(const gdr_desc *desc, const void *q, const void *k, 
     s = check_inputs(desc, q, k, v, log_alpha, b, w, gamma, z, q);  // no output: q stands in for o
     if (s != GDR_OK) return s;
   }
+  if (gamma && !aligned16(gamma)) return GDR_ERR_INVALID_ARG;  // read even without tokens
   const int bf = d.in_dtype == GDR_BF16;
   auto gate_n = [&](gdr_gate_mode m, int dim) {
     return m == GDR_GATE_PER_CHANNEL ? rows * dim : m == GDR_GATE_PER_TOKEN ? rows : 0ull;

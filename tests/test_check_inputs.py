@@ -38,6 +38,7 @@ def test_check_rejects_before_launch():
     assert _raw(d, k=40) == gdr.GDR_ERR_INVALID_ARG                # misaligned input
     assert _raw(d, la=None) == gdr.GDR_ERR_INVALID_ARG             # per-channel alpha needs a pointer
     assert _raw(d, z=24) == gdr.GDR_ERR_INVALID_ARG
+    assert _raw(gdr.make_desc(B=0, H=3, T=100, dk=64, dv=64), gamma=40) == gdr.GDR_ERR_INVALID_ARG
     assert _raw(gdr.make_desc(B=2, H=3, T=100, dk=80, dv=80)) == gdr.GDR_ERR_UNSUPPORTED
     assert _raw(gdr.make_desc(B=2, H=3, T=100, dk=64, dv=64, alpha_mode=gdr.ZEROS)) == gdr.GDR_ERR_INVALID_ARG
 
