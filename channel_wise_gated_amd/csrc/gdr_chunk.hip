@@ -1204,7 +1204,7 @@ __global__ void __launch_bounds__(64 * (C / 16)) chunk_out_kernel(ChunkArgs a) {
       const int col = 16 * jt + l16;
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        if (tok0 + r < tvalid) st1<OB16>(a.o, (orow0 + r) * D + col, acc[r]);  // no padding rows
+        if (tok0 + r < tvalid) st1_stream<OB16>(a.o, (orow0 + r) * D + col, acc[r]);  // no padding rows
     }
   } else {
     // all dv columns of this lane's 4 tokens (column 16 jt + l16)

@@ -106,6 +106,16 @@ __device__ __forceinline__ void st8(void *p, size_t i, const float x[8]) {
   }
 }
 
+// Streaming stores of outputs the kernel never reads back (nontemporal: no
+// reuse expected in the caches).
+template <bool BF16>
+__device__ __forceinline__ void st1_stream(void *p, size_t i, float x) {
+  if constexpr (BF16)
+    __builtin_nontemporal_store(f32_to_bf16_bits(x), reinterpret_cast<uint16_t *>(p) + i);
+  else
+    __builtin_nontemporal_store(x, reinterpret_cast<float *>(p) + i);
+}
+
 template <bool BF16>
 __device__ __forceinline__ void st1(void *p, size_t i, float x) {
   if constexpr (BF16)
