@@ -472,11 +472,13 @@ __device__ __forceinline__ void ldn(const void *p, size_t i, float (&o)[N]) {
     ld4<BF>(p, i, o);
 }
 
+// The final gradients: written once and not read back here, so stored
+// nontemporally (past the caches).
 template <int N>
 __device__ __forceinline__ void stn(float *p, const float (&x)[N]) {
 #pragma unroll
   for (int v = 0; v < N / 4; ++v)
-    reinterpret_cast<float4 *>(p)[v] = float4{x[4 * v], x[4 * v + 1], x[4 * v + 2], x[4 * v + 3]};
+    __builtin_nontemporal_store(f32x4{x[4 * v], x[4 * v + 1], x[4 * v + 2], x[4 * v + 3]}, reinterpret_cast<f32x4 *>(p) + v);
 }
 
 // ---------------------------------------------------------------------------
