@@ -249,8 +249,8 @@ gdr_status bwd_call(const gdr_desc *desc, int nseq, const int *cu, const void *q
   r.rev = 1;
   if (chunks) {
     a.Qp = f.Qp; a.Mm = f.Mm; a.Sc = f.Sc;
-    // forward recompute: the chunk maps (a packed batch's chunk list first),
-    // then M^T and Q'^T dO; then the forward chain (chunk-start states) and
+    // forward recompute: the chunk maps and M^T (a packed batch's chunk list
+    // first), then Q'^T dO; then the forward chain (chunk-start states) and
     // the reverse chain side by side
     // the backward needs no O_bar (the intra kernel skips it) but the
     // per-token vectors and the chunk system's A and T^-1, which the same
@@ -258,7 +258,7 @@ gdr_status bwd_call(const gdr_desc *desc, int nseq, const int *cu, const void *q
     gdr::ChunkArgs fi = f;
     fi.Ob = nullptr;
     fi.pp_kn = a.KN; fi.pp_kh = a.KH; fi.pp_qt = a.QT; fi.pp_vh = a.VH; fi.pp_lam = a.LAM;
-    fi.pp_am = a.AM; fi.pp_ti = a.TI;
+    fi.pp_am = a.AM; fi.pp_ti = a.TI; fi.pp_mt = a.Mt;
     e = gdr::launch_chunk(fd, fi, 1, st);
     if (e == hipSuccess) e = gdr::launch_bwd_prep(a, d.dk, ns, st);
     f.c0 = r.c0 = 0;

@@ -68,11 +68,10 @@ __device__ __forceinline__ SlotTokens slot_tokens(const BwdArgs &a, size_t slot)
 }
 
 // ---------------------------------------------------------------------------
-// Prep: per chunk slot, M^T (plane by plane, in M's A-fragment layout) and
-// G = Q'^T dO (in N's accumulator-tile layout) for the reverse chain.  Each M
-// plane goes through LDS row-major (16-byte fragment reads and writes on both
-// sides); G is computed on the fp32 matrix cores from Q' and dO in LDS, wave w
-// owning G's row tiles w * NMT/4 to (w + 1) * NMT/4 - 1 (NMT = D / 16).
+// Prep: per chunk slot, G = Q'^T dO (in N's accumulator-tile layout) for the
+// reverse chain (M^T comes from the recompute), on the fp32 matrix cores from
+// Q' and dO in LDS, wave w owning G's row tiles w * NMT/4 to (w + 1) * NMT/4 - 1
+// (NMT = D / 16).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ f32x4 mfma4(float x, float y, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(x, y, c, 0, 0, 0);
@@ -91,39 +90,13 @@ __device__ __forceinline__ f32x4 ld_do4(const void *p, size_t i, int bf) {
 
 template <int D, int NS>
 __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdArgs a) {
-  constexpr int C = kBC, NKD = D / 32, NMT = D / 16, MP = D + 8, SP = D + 4, RT = NMT / 4;
-  static_assert(D * MP * 2 <= 2 * C * SP * 4, "an M plane fits in the Q' / dO space");
-  // first one plane of M at a time, row-major (bf16); then Q' [t][i] and dO [t][j]
+  constexpr int C = kBC, NKD = D / 32, NMT = D / 16, SP = D + 4, RT = NMT / 4;
+  // Q' [t][i] and dO [t][j]
   __shared__ __align__(16) float lds[2 * C * SP];
-  uint16_t *mp = reinterpret_cast<uint16_t *>(lds);
   float *qs = lds, *ds = lds + C * SP;
   const size_t slot = blockIdx.x;
   const SlotTokens st = slot_tokens(a, slot);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, g = lane >> 4;
-  // A-fragment entry (f, lane) of a D x D plane: 8 values of row 16 (f / NKD) + l16,
-  // columns 32 (f % NKD) + 4 g + {0..3} and + 16
-  const uint16_t *Ms = a.Mm + slot * NS * (size_t)D * D;
-  uint16_t *Mt = a.Mt + slot * NS * (size_t)D * D;
-#pragma unroll
-  for (int p = 0; p < NS; ++p) {
-    for (int idx = tid; idx < D * D / 8; idx += 256) {
-      const int f = idx >> 6, ln = idx & 63, row = 16 * (f / NKD) + (ln & 15), col = 32 * (f % NKD) + 4 * (ln >> 4);
-      const uint4 v = reinterpret_cast<const uint4 *>(Ms + (size_t)p * D * D)[idx];
-      *reinterpret_cast<uint2 *>(mp + row * MP + col) = uint2{v.x, v.y};
-      *reinterpret_cast<uint2 *>(mp + row * MP + col + 16) = uint2{v.z, v.w};
-    }
-    __syncthreads();
-    for (int idx = tid; idx < D * D / 8; idx += 256) {
-      // M^T[R][Cc] = M[Cc][R]: R = 16 (f / NKD) + l16, Cc over the entry's 8 columns
-      const int f = idx >> 6, ln = idx & 63, R = 16 * (f / NKD) + (ln & 15), c0 = 32 * (f % NKD) + 4 * (ln >> 4);
-      uint32_t h[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) h[e] = mp[(c0 + 16 * (e >> 2) + (e & 3)) * MP + R];
-      reinterpret_cast<uint4 *>(Mt + (size_t)p * D * D)[idx] =
-          uint4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
-    }
-    __syncthreads();
-  }
   // Q' (planes summed in fp32) and dO into LDS
   const uint16_t *Qs = a.Qp + slot * NS * (size_t)C * D;
   for (int idx = tid; idx < C * D / 8; idx += 256) {

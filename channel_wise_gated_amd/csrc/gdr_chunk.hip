@@ -168,8 +168,9 @@ __device__ __forceinline__ int tp_chan(int ks, int g, int e) { return 32 * ks + 
 // and the pair factor D_ij scales the accumulated tile.
 // PP: also write what the backward reads of the chunk: the per-token vectors
 // kn, k_hat, q_tilde, v_hat and the in-chunk cumulative log decay ([slot][C][D]
-// fp32 each, zero on padding rows), and the chunk system's A and T^-1
-// ([slot][C][C] fp32 each).
+// fp32 each, zero on padding rows), the chunk system's A and T^-1
+// ([slot][C][C] fp32 each), and M^T in M's A-fragment plane layout (for the
+// reverse chain of state gradients).
 template <int C, int D, int NS, bool BF, bool SA, bool PP = false>
 __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
   static_assert(!SA || NS == 2, "the scalar-decay kernel keeps kn * Cf as two bf16 planes in the kn * Cf region");
@@ -881,6 +882,7 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
     // for both.
     const bool mw = wave < NMT;
     f32x4 accC[2] = {zero4(), zero4()}, accT[2] = {zero4(), zero4()};  // channel-tile, token-block products
+    f32x4 accMt[PP ? 2 : 1] = {};  // PP, K half: K'^T Y itself (M^T up to the diagonal)
 #pragma unroll
     for (int ctl = 0; ctl < 2; ++ctl)
 #pragma unroll
@@ -895,6 +897,8 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
         } else {
           if (mw) accC[ctl] = mfma32_split<NS>(zb, wf[ks], accC[ctl]);  // (K'^T Y)^T = Y^T K'
           if (tw) accT[ctl] = mfma32_split<NS>(zb, pf[ks], accT[ctl]);  // (A Y)^T = Y^T A^T
+          if constexpr (PP)
+            if (mw) accMt[ctl] = mfma32_split<NS>(wf[ks], zb, accMt[ctl]);
         }
       }
     if (vhalf) {
@@ -921,6 +925,22 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
             mv[4 * ctl + r] = (cpr == c ? gdiag : 0.f) - accC[ctl][r];
           }
         store8_planes<NS>(Mm + ((size_t)(wave * NKD + ksy) * 64 + lane) * 8, (size_t)D * D, mv);
+        if constexpr (PP) {
+          // M^T[j][c] for j = 32 ksy + 16 ctl + l16 (its A-fragment row) and
+          // c = 16 wave + 4 g + r: half of the fragment entry of row tile
+          // 2 ksy + ctl and k-step wave / 2 (the diagonal, j = c, falls on the
+          // lanes whose own channel 16 wave + l16 is j)
+#pragma unroll
+          for (int ctl = 0; ctl < 2; ++ctl) {
+            float x[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              x[r] = (2 * ksy + ctl == wave && l16 == 4 * g + r ? gdiag : 0.f) - accMt[ctl][r];
+            store4_planes<NS>(a.pp_mt + chq * (size_t)D * D +
+                                  ((size_t)((2 * ksy + ctl) * NKD + wave / 2) * 64 + lane) * 8 + 4 * (wave % 2),
+                              (size_t)D * D, x);
+          }
+        }
       }
       if (rowwave) {  // Q' = Qt e^Lambda - A Y
         float qv8[8];

@@ -49,8 +49,11 @@ struct ChunkArgs {
   // log decay, [slot][C][D] fp32 each, zero on padding rows.
   float *pp_kn, *pp_kh, *pp_qt, *pp_vh, *pp_lam;
   // ... and the chunk system's A (diagonal included) and T^-1, [slot][C][C]
-  // fp32 each, zero above the diagonal and on padding rows and columns of A.
+  // fp32 each, zero above the diagonal and on padding rows and columns of A;
+  // and M^T as NS bf16 planes in M's A-fragment layout ([slot][NS][D][D]; not
+  // written for an empty slot of a packed batch).
   float *pp_am, *pp_ti;
+  uint16_t *pp_mt;
 };
 
 // The five-gate projection: x [N, dm] bf16 (N = B*T tokens), wd [R, dm]
