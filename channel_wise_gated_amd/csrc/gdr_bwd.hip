@@ -185,9 +185,12 @@ __device__ __forceinline__ void ldc(const void *p, size_t i, float (&o)[N]) {
 //   R   = V_hat - K_a S0       U  = T^-1 R            dQ_a = dO S0^T
 //   dA  = dO U^T (s <= t)      Z  = A^T dO + K' X     dK'  = U X^T
 //   dU~ = T^-T Z               dL = -dU~ U^T (s < t)  dK_a = -dU~ S0^T
-// Wave w owns token rows 16w..16w+15 of every C x D result; of the C x C
-// results it owns the row tiles w (dA) and 3 - w (dL), so that the triangles
-// give every wave the same number of tiles.  In a 16x16x4 MFMA, lane
+// Eight waves: the pair 2p, 2p + 1 owns token row tile rt (p = 0, 1, 2, 3 ->
+// rt = 0, 1, 3, 2, so that each SIMD, which holds waves w and w + 4, gets the
+// row tiles {0, 3} or {1, 2} and the triangles give every SIMD the same
+// work); wave 2p + hc computes column half hc of every C x D result of its
+// row tile.  Of the C x C results the pair owns row tiles rt (dA) and 3 - rt
+// (dL), the two waves taking alternate column tiles.  In a 16x16x4 MFMA, lane
 // (l16, g) = (lane % 16, lane / 16) supplies A[l16][k] and B[k][l16] for one
 // k and receives D[4g + r][l16], r = 0..3.  A k-block of 16 takes four MFMAs,
 // lane group g supplying k = 16 kb + 4 g + e at step e, so every lane reads
@@ -195,34 +198,51 @@ __device__ __forceinline__ void ldc(const void *p, size_t i, float (&o)[N]) {
 // float4.  LDS rows are padded by 4 floats: conflict-free for both access
 // patterns.
 // ---------------------------------------------------------------------------
-// acc[ct] += A B over k-blocks kb0..kb1-1; B[k][col] row-major in LDS (stride sp)
+// acc[ct] += A B over k-blocks kb0..kb1-1 for column tiles ct0 + ct; B[k][col]
+// row-major in LDS (stride sp)
 template <int NK, int NT>
 __device__ __forceinline__ void mm_nn(f32x4 (&acc)[NT], const f32x4 (&af)[NK], const float *B, int sp, int kb0,
-                                      int kb1, int g, int l16) {
+                                      int kb1, int g, int l16, int ct0) {
 #pragma unroll
   for (int kb = 0; kb < NK; ++kb) {
     if (kb < kb0 || kb >= kb1) continue;  // wave-uniform
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float *brow = B + (16 * kb + 4 * g + e) * sp + l16;
+      const float *brow = B + (16 * kb + 4 * g + e) * sp + 16 * ct0 + l16;
 #pragma unroll
       for (int ct = 0; ct < NT; ++ct) acc[ct] = mfma4(af[kb][e], brow[16 * ct], acc[ct]);
     }
   }
 }
 
-// acc[ct] += A Y^T for column tiles ct < ct1; Y[col][k] row-major in LDS
+// acc[ct] += A Y^T for column tiles ct0 + ct; Y[col][k] row-major in LDS
 template <int NK, int NT>
-__device__ __forceinline__ void mm_nt(f32x4 (&acc)[NT], const f32x4 (&af)[NK], const float *Y, int sp, int ct1,
-                                      int g, int l16) {
+__device__ __forceinline__ void mm_nt(f32x4 (&acc)[NT], const f32x4 (&af)[NK], const float *Y, int sp, int g,
+                                      int l16, int ct0) {
 #pragma unroll
   for (int kb = 0; kb < NK; ++kb)
 #pragma unroll
     for (int ct = 0; ct < NT; ++ct) {
-      if (ct >= ct1) continue;  // wave-uniform
-      const f32x4 b4 = *reinterpret_cast<const f32x4 *>(Y + (16 * ct + l16) * sp + 16 * kb + 4 * g);
+      const f32x4 b4 = *reinterpret_cast<const f32x4 *>(Y + (16 * (ct0 + ct) + l16) * sp + 16 * kb + 4 * g);
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[ct] = mfma4(af[kb][e], b4[e], acc[ct]);
+    }
+}
+
+// C x C row tile against U^T: acc[j] += A U^T for column tiles ct = hc + 2 j
+// with ct <= ctmax; U[s][k] row-major in LDS
+template <int NK>
+__device__ __forceinline__ void mm_nt_alt(f32x4 (&acc)[2], const f32x4 (&af)[NK], const float *U, int sp, int hc,
+                                          int ctmax, int g, int l16) {
+#pragma unroll
+  for (int kb = 0; kb < NK; ++kb)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int ct = hc + 2 * j;
+      if (ct > ctmax) continue;  // wave-uniform
+      const f32x4 b4 = *reinterpret_cast<const f32x4 *>(U + (16 * ct + l16) * sp + 16 * kb + 4 * g);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[j] = mfma4(af[kb][e], b4[e], acc[j]);
     }
 }
 
@@ -233,11 +253,11 @@ __device__ __forceinline__ void zero_acc(f32x4 (&acc)[NT]) {
 }
 
 template <int D, int NS>
-__global__ void __launch_bounds__(256) bwd_mm_kernel(BwdArgs a) {
-  constexpr int C = kBC, SP = D + 4, NKB = D / 16, NCT = D / 16, NTC = C / 16;
+__global__ void __launch_bounds__(512) bwd_mm_kernel(BwdArgs a) {
+  constexpr int C = kBC, SP = D + 4, NKB = D / 16, NCT = D / 16, NCH = NCT / 2, NTC = C / 16;
   constexpr int BBR = 2 * C > D ? 2 * C : D, NFR = (D / 32) * NS, FRAG = 512;
-  static_assert(NTC == 4, "four waves, one 16-token row tile each");
-  static_assert(4 % (D / 32) == 0, "a thread's plane entries share their rows");
+  static_assert(NTC == 4, "four 16-token row tiles, two waves each");
+  static_assert(8 % (D / 32) == 0, "a thread's plane entries share their k-step");
   __shared__ __align__(16) float ss[D * SP];    // S0, then X, then dU~ (rows < C)
   __shared__ __align__(16) float bb[BBR * SP];  // rows < C: R, dO, Z; rows C..2C-1: U; last: S0
   __shared__ float xs[D];                       // row dots of X and S0
@@ -246,20 +266,21 @@ __global__ void __launch_bounds__(256) bwd_mm_kernel(BwdArgs a) {
   const SlotTokens st = slot_tokens(a, slot);
   const size_t base = slot * (size_t)C * D, cbase = slot * (size_t)C * C;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, g = lane >> 4;
-  const int ar = 16 * w + l16;  // the A-operand row this lane supplies
+  const int pr = w >> 1, rt = pr < 2 ? pr : 5 - pr, hc = w & 1, ct0 = NCH * hc;
+  const int ar = 16 * rt + l16;  // the A-operand row this lane supplies
   const uint16_t *S0p = a.Sc + slot * NS * (size_t)D * D, *Xp = a.Xc + slot * NS * (size_t)D * D;
   // A state from the chains' bf16 planes (summed in fp32) into padded LDS rows.
   // Entry (slice sl, k-step ks, lane) of a plane holds 8 values of column
   // 16 sl + l16, rows 32 ks + 16 (e / 4) + 4 g + e % 4; this thread's entries
-  // are tid + 256 k (k < NE), all with the same ks.  Loads and LDS stores are
+  // are tid + 512 k (k < NE), all with the same ks.  Loads and LDS stores are
   // separate steps so that loads can be issued a phase ahead.
-  constexpr int NE = D * D / 8 / 256;
-  static_assert(NE * 256 * 8 == D * D, "plane entries per thread");
-  const int ks = (tid >> 6) % (D / 32);
+  constexpr int NE = D * D / 8 / 512;
+  static_assert(NE * 512 * 8 == D * D, "plane entries per thread");
+  const int ks = w % (D / 32);
   auto load_planes = [&](const uint16_t *pl, bf16x8 (&r)[NE][NS]) {
 #pragma unroll
     for (int k = 0; k < NE; ++k) {
-      const int sl = ((tid + 256 * k) >> 6) / (D / 32);
+      const int sl = (w + 8 * k) / (D / 32);
       const size_t off = (size_t)sl * NFR * FRAG + (size_t)(ks * NS) * FRAG + lane * 8;
 #pragma unroll
       for (int p = 0; p < NS; ++p) r[k][p] = *reinterpret_cast<const bf16x8 *>(pl + off + p * FRAG);
@@ -270,7 +291,7 @@ __global__ void __launch_bounds__(256) bwd_mm_kernel(BwdArgs a) {
     float dot[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < NE; ++k) {
-      const int sl = ((tid + 256 * k) >> 6) / (D / 32), col = 16 * sl + l16;
+      const int sl = (w + 8 * k) / (D / 32), col = 16 * sl + l16;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         float v = 0.f, u = 0.f;
@@ -293,20 +314,32 @@ __global__ void __launch_bounds__(256) bwd_mm_kernel(BwdArgs a) {
       }
     }
   };
-  // C x D result rows 16 rt + 4 g + r, columns 16 ct + l16
-  auto put_glb = [&](float *dst, const f32x4 (&acc)[NCT], int rt, float sign) {
+  // this wave's part of a C x D result: rows 16 rt + 4 g + r, columns 16 (ct0 + ct) + l16
+  auto put_glb = [&](float *dst, const f32x4 (&acc)[NCH], float sign) {
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
+    for (int ct = 0; ct < NCH; ++ct)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dst[base + (size_t)(16 * rt + 4 * g + r) * D + 16 * ct + l16] = sign * acc[ct][r];
+      for (int r = 0; r < 4; ++r)
+        dst[base + (size_t)(16 * rt + 4 * g + r) * D + 16 * (ct0 + ct) + l16] = sign * acc[ct][r];
   };
-  auto put_lds = [&](float *dst, const f32x4 (&acc)[NCT], int rt) {
+  auto put_lds = [&](float *dst, const f32x4 (&acc)[NCH]) {
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
+    for (int ct = 0; ct < NCH; ++ct)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dst[(16 * rt + 4 * g + r) * SP + 16 * ct + l16] = acc[ct][r];
+      for (int r = 0; r < 4; ++r) dst[(16 * rt + 4 * g + r) * SP + 16 * (ct0 + ct) + l16] = acc[ct][r];
   };
-  f32x4 acc[NCT], acc2[NCT], acs[NTC];
+  // this wave's column tiles ct = hc + 2 j of C x C row tile `row` (zero
+  // where s > t, or s >= t when strict)
+  auto put_cc = [&](float *dst, const f32x4 (&acc)[2], int row, float sign, bool strict) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * row + 4 * g + r, s2 = 16 * (hc + 2 * j) + l16;
+        dst[cbase + (size_t)t * C + s2] = (strict ? s2 < t : s2 <= t) ? sign * acc[j][r] : 0.f;
+      }
+  };
+  f32x4 acc[NCH], acc2[NCH], acs[2];
   f32x4 af[NKB], dof[NKB], tf[NTC];
 
   // (1) S0 phase: R = V_hat - K_a S0 (-> LDS), dQ_a = dO S0^T
@@ -323,39 +356,39 @@ __global__ void __launch_bounds__(256) bwd_mm_kernel(BwdArgs a) {
     af[kb] = f32x4{kh.x * __expf(la.x), kh.y * __expf(la.y), kh.z * __expf(la.z), kh.w * __expf(la.w)};
     dof[kb] = arow ? ld_do4(a.dO, orow + 16 * kb + 4 * g, a.do_bf16) : zero4();
   }
-  float vh[NCT][4];
+  float vh[NCH][4];
 #pragma unroll
-  for (int ct = 0; ct < NCT; ++ct)
+  for (int ct = 0; ct < NCH; ++ct)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) vh[ct][r] = a.VH[base + (size_t)(16 * w + 4 * g + r) * D + 16 * ct + l16];
+    for (int r = 0; r < 4; ++r) vh[ct][r] = a.VH[base + (size_t)(16 * rt + 4 * g + r) * D + 16 * (ct0 + ct) + l16];
 #pragma unroll
   for (int kb = 0; kb < NTC; ++kb)
     tf[kb] = *reinterpret_cast<const f32x4 *>(a.TI + cbase + (size_t)ar * C + 16 * kb + 4 * g);
-  // phase 3's states, in flight during phases 1 and 2 (issued last: the
-  // load counter completes in order)
-  load_planes(Xp, pa);
-  load_planes(S0p, pb);
   __syncthreads();
   zero_acc(acc);
-  mm_nn(acc, af, ss, SP, 0, NKB, g, l16);
+  mm_nn(acc, af, ss, SP, 0, NKB, g, l16, ct0);
 #pragma unroll
-  for (int ct = 0; ct < NCT; ++ct)
+  for (int ct = 0; ct < NCH; ++ct)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) bt[(16 * w + 4 * g + r) * SP + 16 * ct + l16] = vh[ct][r] - acc[ct][r];
+    for (int r = 0; r < 4; ++r) bt[(16 * rt + 4 * g + r) * SP + 16 * (ct0 + ct) + l16] = vh[ct][r] - acc[ct][r];
   zero_acc(acc);
-  mm_nt(acc, dof, ss, SP, NCT, g, l16);
-  put_glb(a.DQA, acc, w, 1.f);
+  mm_nt(acc, dof, ss, SP, g, l16, ct0);
+  put_glb(a.DQA, acc, 1.f);
+  // phase 3's states, in flight during phase 2 (issued after phase 1's
+  // products, whose registers they would otherwise share)
+  load_planes(Xp, pa);
+  load_planes(S0p, pb);
   __syncthreads();
 
   // (2) U = T^-1 R (T^-1 lower triangular: k-blocks up to the row tile)
   zero_acc(acc);
-  mm_nn(acc, tf, bt, SP, 0, w + 1, g, l16);
-  put_lds(bu, acc, w);
+  mm_nn(acc, tf, bt, SP, 0, rt + 1, g, l16, ct0);
+  put_lds(bu, acc);
   __syncthreads();
 
   // (3) X phase: dA = dO U^T, Z = A^T dO + K' X, dK' = U X^T
   store_planes(ss, pa, pb, true);
-  for (int idx = tid; idx < C * D / 4; idx += 256) {
+  for (int idx = tid; idx < C * D / 4; idx += 512) {
     const int t = idx / (D / 4), j4 = idx % (D / 4);
     *reinterpret_cast<f32x4 *>(bt + t * SP + 4 * j4) =
         t < st.valid ? ld_do4(a.dO, (st.row + t) * D + 4 * j4, a.do_bf16) : zero4();
@@ -373,25 +406,22 @@ __global__ void __launch_bounds__(256) bwd_mm_kernel(BwdArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) tf[kb][e] = a.AM[cbase + (size_t)(16 * kb + 4 * g + e) * C + ar];
   __syncthreads();
+  // dO's row ar again, from its LDS copy (not kept in registers since phase 1)
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) dof[kb] = *reinterpret_cast<const f32x4 *>(bt + ar * SP + 16 * kb + 4 * g);
   zero_acc(acs);
-  mm_nt(acs, dof, bu, SP, w + 1, g, l16);
-#pragma unroll
-  for (int ct = 0; ct < NTC; ++ct)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 16 * w + 4 * g + r, s2 = 16 * ct + l16;
-      a.DA[cbase + (size_t)t * C + s2] = s2 <= t ? acs[ct][r] : 0.f;
-    }
+  mm_nt_alt(acs, dof, bu, SP, hc, rt, g, l16);
+  put_cc(a.DA, acs, rt, 1.f, false);
   zero_acc(acc);
-  mm_nn(acc, tf, bt, SP, w, NTC, g, l16);  // A lower triangular: t >= s
-  mm_nn(acc, af, ss, SP, 0, NKB, g, l16);
+  mm_nn(acc, tf, bt, SP, rt, NTC, g, l16, ct0);  // A lower triangular: t >= s
+  mm_nn(acc, af, ss, SP, 0, NKB, g, l16, ct0);
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) af[kb] = *reinterpret_cast<const f32x4 *>(bu + ar * SP + 16 * kb + 4 * g);
   zero_acc(acc2);
-  mm_nt(acc2, af, ss, SP, NCT, g, l16);
-  put_glb(a.DKP, acc2, w, 1.f);
+  mm_nt(acc2, af, ss, SP, g, l16, ct0);
+  put_glb(a.DKP, acc2, 1.f);
   __syncthreads();  // every read of dO and X is done
-  put_lds(bt, acc, w);
+  put_lds(bt, acc);
   if (tid < D) a.XS[slot * D + tid] = xs[tid];
 #pragma unroll
   for (int kb = 0; kb < NTC; ++kb)  // T^-T rows: T^-1[t][ar]
@@ -401,33 +431,27 @@ __global__ void __launch_bounds__(256) bwd_mm_kernel(BwdArgs a) {
 
   // (4) dU~ = T^-T Z (upper triangular: k-blocks from the row tile on)
   zero_acc(acc);
-  mm_nn(acc, tf, bt, SP, w, NTC, g, l16);
-  put_glb(a.DU, acc, w, 1.f);
-  put_lds(ss, acc, w);
+  mm_nn(acc, tf, bt, SP, rt, NTC, g, l16, ct0);
+  put_glb(a.DU, acc, 1.f);
+  put_lds(ss, acc);
   __syncthreads();
 
-  // (5) dL = -dU~ U^T for row tile 3 - w, then dK_a = -dU~ S0^T
-  const int tw = NTC - 1 - w;
+  // (5) dL = -dU~ U^T for row tile 3 - rt, then dK_a = -dU~ S0^T
+  const int tw = NTC - 1 - rt;
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
     af[kb] = *reinterpret_cast<const f32x4 *>(ss + (16 * tw + l16) * SP + 16 * kb + 4 * g);
   zero_acc(acs);
-  mm_nt(acs, af, bu, SP, tw + 1, g, l16);
-#pragma unroll
-  for (int ct = 0; ct < NTC; ++ct)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 16 * tw + 4 * g + r, s2 = 16 * ct + l16;
-      a.DL[cbase + (size_t)t * C + s2] = s2 < t ? -acs[ct][r] : 0.f;
-    }
+  mm_nt_alt(acs, af, bu, SP, hc, tw, g, l16);
+  put_cc(a.DL, acs, tw, -1.f, true);
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) af[kb] = *reinterpret_cast<const f32x4 *>(ss + ar * SP + 16 * kb + 4 * g);
   __syncthreads();  // every read of U and Z is done
   store_planes(bb, pb, pb, false);
   __syncthreads();
   zero_acc(acc);
-  mm_nt(acc, af, bb, SP, NCT, g, l16);
-  put_glb(a.DKA, acc, w, -1.f);
+  mm_nt(acc, af, bb, SP, g, l16, ct0);
+  put_glb(a.DKA, acc, -1.f);
 }
 
 // sum over the 16 lanes of a lane group (lane bits 0-3)
@@ -973,7 +997,7 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
       hipLaunchKernelGGL((bwd_dgamma_kernel<D>), dim3((unsigned)(a.H * (D / 32))), dim3(256), 0, st, a);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((bwd_mm_kernel<D, NS>), dim3(nch), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((bwd_mm_kernel<D, NS>), dim3(nch), dim3(512), 0, st, a);
   hipLaunchKernelGGL((bwd_gramback_kernel<D, BF>), dim3(nch), dim3(256), 0, st, a);
   if (a.dgamma && a.gamma)
     hipLaunchKernelGGL((bwd_dgamma_kernel<D>), dim3((unsigned)(a.H * (D / 32))), dim3(256), 0, st, a);
