@@ -44,8 +44,8 @@ METRIC = "tokens/s + % bf16 MFMA peak, chunk fwd T=32K H=16 d=128; decode HBM GB
 # otherwise reported as null.
 MEASURED_TRAFFIC = {
     "sources": "949cd32d739628ad",
-    "chunk_intra_kernel_C128_seg": 269376636,   # 512 chunks of 128 tokens per launch
-    "chunk_intra_kernel_C64_seg": 168506101,    # 512 chunks of 64 tokens per launch
+    "chunk_intra_kernel_C128_seg": 269442261,   # 512 chunks of 128 tokens per launch
+    "chunk_intra_kernel_C64_seg": 168475136,    # 512 chunks of 64 tokens per launch
 }
 
 
