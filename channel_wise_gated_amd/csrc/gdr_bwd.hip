@@ -259,7 +259,7 @@ __global__ void __launch_bounds__(512) bwd_mm_kernel(BwdArgs a) {
   static_assert(NTC == 4, "four 16-token row tiles, two waves each");
   static_assert(8 % (D / 32) == 0, "a thread's plane entries share their k-step");
   __shared__ __align__(16) float ss[D * SP];    // S0, then X, then dU~ (rows < C)
-  __shared__ __align__(16) float bb[BBR * SP];  // rows < C: R, dO, Z; rows C..2C-1: U; last: S0
+  __shared__ __align__(16) float bb[BBR * SP];  // rows < C: R, then U; rows C..2C-1: dO, then Z; last: S0
   __shared__ float xs[D];                       // row dots of X and S0
   float *bt = bb, *bu = bb + C * SP;
   const size_t slot = blockIdx.x;
@@ -342,19 +342,22 @@ __global__ void __launch_bounds__(512) bwd_mm_kernel(BwdArgs a) {
   f32x4 acc[NCH], acc2[NCH], acs[2];
   f32x4 af[NKB], dof[NKB], tf[NTC];
 
-  // (1) S0 phase: R = V_hat - K_a S0 (-> LDS), dQ_a = dO S0^T
+  // (1) S0 phase: R = V_hat - K_a S0 (-> LDS), dQ_a = dO S0^T; dO staged
+  // once, for this phase and the third
   if (tid < D) xs[tid] = 0.f;
-  bf16x8 pa[NE][NS], pb[NE][NS];  // planes: S0 now; then X (pa) and S0 (pb) for phase 3
-  load_planes(S0p, pa);
-  store_planes(ss, pa, pa, false);
-  const bool arow = ar < st.valid;
-  const size_t orow = (st.row + (arow ? ar : 0)) * D;
+  bf16x8 pa[NE][NS], pb[NE][NS];  // planes: S0 (pb, kept for phases 3 and 5); X (pa)
+  load_planes(S0p, pb);
+  store_planes(ss, pb, pb, false);
+  for (int idx = tid; idx < C * D / 4; idx += 512) {
+    const int t = idx / (D / 4), j4 = idx % (D / 4);
+    *reinterpret_cast<f32x4 *>(bu + t * SP + 4 * j4) =
+        t < st.valid ? ld_do4(a.dO, (st.row + t) * D + 4 * j4, a.do_bf16) : zero4();
+  }
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
     const size_t o = base + (size_t)ar * D + 16 * kb + 4 * g;
     const float4 kh = *reinterpret_cast<const float4 *>(a.KH + o), la = *reinterpret_cast<const float4 *>(a.LAM + o);
     af[kb] = f32x4{kh.x * __expf(la.x), kh.y * __expf(la.y), kh.z * __expf(la.z), kh.w * __expf(la.w)};
-    dof[kb] = arow ? ld_do4(a.dO, orow + 16 * kb + 4 * g, a.do_bf16) : zero4();
   }
   float vh[NCH][4];
 #pragma unroll
@@ -371,28 +374,25 @@ __global__ void __launch_bounds__(512) bwd_mm_kernel(BwdArgs a) {
   for (int ct = 0; ct < NCH; ++ct)
 #pragma unroll
     for (int r = 0; r < 4; ++r) bt[(16 * rt + 4 * g + r) * SP + 16 * (ct0 + ct) + l16] = vh[ct][r] - acc[ct][r];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) dof[kb] = *reinterpret_cast<const f32x4 *>(bu + ar * SP + 16 * kb + 4 * g);
   zero_acc(acc);
   mm_nt(acc, dof, ss, SP, g, l16, ct0);
   put_glb(a.DQA, acc, 1.f);
-  // phase 3's states, in flight during phase 2 (issued after phase 1's
-  // products, whose registers they would otherwise share)
+  // phase 3's state, in flight during phase 2 (issued after phase 1's
+  // products, whose registers it would otherwise share)
   load_planes(Xp, pa);
-  load_planes(S0p, pb);
   __syncthreads();
 
-  // (2) U = T^-1 R (T^-1 lower triangular: k-blocks up to the row tile)
+  // (2) U = T^-1 R (T^-1 lower triangular: k-blocks up to the row tile),
+  // written over R once every wave has read R
   zero_acc(acc);
   mm_nn(acc, tf, bt, SP, 0, rt + 1, g, l16, ct0);
-  put_lds(bu, acc);
   __syncthreads();
+  put_lds(bt, acc);
 
   // (3) X phase: dA = dO U^T, Z = A^T dO + K' X, dK' = U X^T
   store_planes(ss, pa, pb, true);
-  for (int idx = tid; idx < C * D / 4; idx += 512) {
-    const int t = idx / (D / 4), j4 = idx % (D / 4);
-    *reinterpret_cast<f32x4 *>(bt + t * SP + 4 * j4) =
-        t < st.valid ? ld_do4(a.dO, (st.row + t) * D + 4 * j4, a.do_bf16) : zero4();
-  }
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
     const size_t o = base + (size_t)ar * D + 16 * kb + 4 * g;
@@ -406,22 +406,21 @@ __global__ void __launch_bounds__(512) bwd_mm_kernel(BwdArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) tf[kb][e] = a.AM[cbase + (size_t)(16 * kb + 4 * g + e) * C + ar];
   __syncthreads();
-  // dO's row ar again, from its LDS copy (not kept in registers since phase 1)
 #pragma unroll
-  for (int kb = 0; kb < NKB; ++kb) dof[kb] = *reinterpret_cast<const f32x4 *>(bt + ar * SP + 16 * kb + 4 * g);
+  for (int kb = 0; kb < NKB; ++kb) dof[kb] = *reinterpret_cast<const f32x4 *>(bu + ar * SP + 16 * kb + 4 * g);
   zero_acc(acs);
-  mm_nt_alt(acs, dof, bu, SP, hc, rt, g, l16);
+  mm_nt_alt(acs, dof, bt, SP, hc, rt, g, l16);
   put_cc(a.DA, acs, rt, 1.f, false);
   zero_acc(acc);
-  mm_nn(acc, tf, bt, SP, rt, NTC, g, l16, ct0);  // A lower triangular: t >= s
+  mm_nn(acc, tf, bu, SP, rt, NTC, g, l16, ct0);  // A lower triangular: t >= s
   mm_nn(acc, af, ss, SP, 0, NKB, g, l16, ct0);
 #pragma unroll
-  for (int kb = 0; kb < NKB; ++kb) af[kb] = *reinterpret_cast<const f32x4 *>(bu + ar * SP + 16 * kb + 4 * g);
+  for (int kb = 0; kb < NKB; ++kb) af[kb] = *reinterpret_cast<const f32x4 *>(bt + ar * SP + 16 * kb + 4 * g);
   zero_acc(acc2);
   mm_nt(acc2, af, ss, SP, g, l16, ct0);
   put_glb(a.DKP, acc2, 1.f);
   __syncthreads();  // every read of dO and X is done
-  put_lds(bt, acc);
+  put_lds(bu, acc);
   if (tid < D) a.XS[slot * D + tid] = xs[tid];
 #pragma unroll
   for (int kb = 0; kb < NTC; ++kb)  // T^-T rows: T^-1[t][ar]
@@ -431,7 +430,7 @@ __global__ void __launch_bounds__(512) bwd_mm_kernel(BwdArgs a) {
 
   // (4) dU~ = T^-T Z (upper triangular: k-blocks from the row tile on)
   zero_acc(acc);
-  mm_nn(acc, tf, bt, SP, rt, NTC, g, l16, ct0);
+  mm_nn(acc, tf, bu, SP, rt, NTC, g, l16, ct0);
   put_glb(a.DU, acc, 1.f);
   put_lds(ss, acc);
   __syncthreads();
@@ -442,7 +441,7 @@ __global__ void __launch_bounds__(512) bwd_mm_kernel(BwdArgs a) {
   for (int kb = 0; kb < NKB; ++kb)
     af[kb] = *reinterpret_cast<const f32x4 *>(ss + (16 * tw + l16) * SP + 16 * kb + 4 * g);
   zero_acc(acs);
-  mm_nt_alt(acs, af, bu, SP, hc, tw, g, l16);
+  mm_nt_alt(acs, af, bt, SP, hc, tw, g, l16);
   put_cc(a.DL, acs, tw, -1.f, true);
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) af[kb] = *reinterpret_cast<const f32x4 *>(ss + ar * SP + 16 * kb + 4 * g);
