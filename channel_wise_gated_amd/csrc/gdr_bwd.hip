@@ -22,8 +22,9 @@
 // Order of a call (gdr_chunk_bwd): the forward's intra-chunk kernel
 // recomputes the chunk maps and, beside them, writes the per-token vectors
 // kn, k_hat, q_tilde, v_hat and the in-chunk cumulative log decay Lambda
-// (its pre-pass already forms them) and the chunk system's A and T^-1 (its
-// Gram and solve phases form them); the prep kernel forms M^T and Q'^T dO;
+// (its pre-pass already forms them), the chunk system's A and T^-1 (its
+// Gram and solve phases form them) and M^T (its column loop); the prep
+// kernel forms Q'^T dO;
 // the forward chain (chunk-start states) and the reverse chain (X) run side
 // by side in one launch; then per chunk the dense products and the Gram
 // backprop with the chains to the inputs; last dgamma.
