@@ -12,7 +12,9 @@
 // Weights use the [out, in] row-major convention, so every MFMA operand
 // fragment is 16 contiguous bytes of one row.  Both kernels put the weight
 // rows in the MFMA's A operand and the tokens in its B operand: a lane's
-// accumulator then holds four consecutive output columns of one token.
+// accumulator then holds four output columns of one token (the up kernel
+// orders its weight rows so that two tiles give a lane eight consecutive
+// columns).
 #include <stdint.h>
 
 #include "gdr_device.h"
@@ -213,23 +215,32 @@ __device__ __forceinline__ void gate_up_heads(const GateArgs &a, int gate, OT *o
     if (tid < D / 4) *reinterpret_cast<f32x4 *>(bl + buf * D + 4 * tid) = pb;
   };
   // epilogue: bias and activation, stored straight from the accumulator
-  // layout (lane: token l16, channels 16 ct + 4g .. +3: 16 or 8 contiguous
-  // bytes; the four lanes of a token cover 64 or 32 contiguous bytes)
+  // layout (lane: token l16; tiles 2j, 2j + 1 hold its channels 32 j + 8 g ..
+  // + 7: one 16-byte store in bf16, two in fp32; the four lanes of a token
+  // cover 64 or 128 contiguous bytes)
   auto epilogue = [&](const f32x4 (&acc)[NCT], const float *bb, int hh, auto act) {
-    OT *orow = out + ((size_t)rb + (size_t)hh * a.T) * D + 4 * g;
+    OT *orow = out + ((size_t)rb + (size_t)hh * a.T) * D + 8 * g;
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      const f32x4 bv = *reinterpret_cast<const f32x4 *>(bb + 16 * ct + 4 * g);
-      const float y0 = act(acc[ct][0] + bv[0]), y1 = act(acc[ct][1] + bv[1]);
-      const float y2 = act(acc[ct][2] + bv[2]), y3 = act(acc[ct][3] + bv[3]);
+    for (int j = 0; j < NCT / 2; ++j) {
+      const f32x4 b0 = *reinterpret_cast<const f32x4 *>(bb + 32 * j + 8 * g);
+      const f32x4 b1 = *reinterpret_cast<const f32x4 *>(bb + 32 * j + 8 * g + 4);
+      float y[8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        y[r] = act(acc[2 * j][r] + b0[r]);
+        y[4 + r] = act(acc[2 * j + 1][r] + b1[r]);
+      }
       if (live) {
         if constexpr (F32) {
-          *reinterpret_cast<f32x4 *>(orow + 16 * ct) = f32x4{y0, y1, y2, y3};
+          *reinterpret_cast<f32x4 *>(orow + 32 * j) = f32x4{y[0], y[1], y[2], y[3]};
+          *reinterpret_cast<f32x4 *>(orow + 32 * j + 4) = f32x4{y[4], y[5], y[6], y[7]};
         } else {
-          uint2 pk;
-          pk.x = pack_bf16x2(y0, y1);
-          pk.y = pack_bf16x2(y2, y3);
-          *reinterpret_cast<uint2 *>(orow + 16 * ct) = pk;
+          uint4 pk;
+          pk.x = pack_bf16x2(y[0], y[1]);
+          pk.y = pack_bf16x2(y[2], y[3]);
+          pk.z = pack_bf16x2(y[4], y[5]);
+          pk.w = pack_bf16x2(y[6], y[7]);
+          *reinterpret_cast<uint4 *>(orow + 32 * j) = pk;
         }
       }
     }
@@ -248,12 +259,14 @@ __device__ __forceinline__ void gate_up_heads(const GateArgs &a, int gate, OT *o
     f32x4 acc[NCT];
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) acc[ct] = zero4();
-    const uint16_t *wc = wl + cur * WBUF + l16 * WROW + 8 * g;
+    // tile ct, row i holds channel 32 (ct / 2) + 8 (i / 4) + 4 (ct % 2) + i % 4, so
+    // that a lane's accumulators of tiles 2j, 2j + 1 are 8 consecutive channels
+    const uint16_t *wc = wl + cur * WBUF + (8 * (l16 >> 2) + (l16 & 3)) * WROW + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < NK; ++ks) {
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
-        const bf16x8 wb = *reinterpret_cast<const bf16x8 *>(wc + 16 * ct * WROW + 32 * ks);
+        const bf16x8 wb = *reinterpret_cast<const bf16x8 *>(wc + (32 * (ct >> 1) + 4 * (ct & 1)) * WROW + 32 * ks);
         acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb, hf[ks][1], acc[ct], 0, 0, 0);
         acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb, hf[ks][0], acc[ct], 0, 0, 0);
       }
