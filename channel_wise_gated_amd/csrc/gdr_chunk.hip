@@ -893,7 +893,7 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
         load_frag<NS>(rst + ((ks * 2 + ctl) * NS) * FRAG + lane * 8, FRAG, zb);
         if (vhalf) {
           if (mw) accC[ctl] = mfma32_split<NS>(wf[ks], zb, accC[ctl]);  // N = K'^T U_bar
-          if (tw) accT[ctl] = mfma32_split<NS>(pf[ks], zb, accT[ctl]);  // O_bar = A U_bar
+          if (tw) accT[ctl] = mfma32_split<NS>(zb, pf[ks], accT[ctl]);  // O_bar^T = U_bar^T A^T
         } else {
           if (mw) accC[ctl] = mfma32_split<NS>(zb, wf[ks], accC[ctl]);  // (K'^T Y)^T = Y^T K'
           if (tw) accT[ctl] = mfma32_split<NS>(zb, pf[ks], accT[ctl]);  // (A Y)^T = Y^T A^T
@@ -1153,8 +1153,12 @@ __global__ void __launch_bounds__(64 * (D / 16)) chunk_chain2_kernel(ChunkArgs a
 
 // ============================================================================
 // Kernel 3 (output): one workgroup per (stream, chunk); wave w owns output row
-// tile w and sweeps the value slices: O = Q' S_c + O_bar.  S_c (all slices,
-// NS bf16 planes in B-fragment layout) is staged in LDS once.
+// tile w and sweeps the value slices: O = Q' S_c + O_bar, formed transposed
+// (O^T = S_c^T Q'^T: the S_c fragments in the A operand, Q''s in the B
+// operand, O_bar stored transposed by the intra-chunk kernel) so that a lane
+// holds 4 consecutive value channels of one token and stores them as one
+// vector.  S_c (all slices, NS bf16 planes in B-fragment layout, which is the
+// A-fragment layout of S_c^T) is staged in LDS once.
 // ============================================================================
 // Dynamic LDS of the output kernel: the S_c planes of all slices, and with a
 // gated output also the normalised rows [C][D + 4] fp32 (staged after the
@@ -1166,7 +1170,7 @@ constexpr size_t out_lds_gated() {
 }
 
 // OG: gated output -- per token, the RMS over the dv channels of o is reduced
-// across the 16 lanes that hold the token's columns, and y = o / rms * onw *
+// across the 4 lanes that hold the token's columns, and y = o / rms * onw *
 // sigmoid(og) is written token-major; o itself is not written.
 template <int C, int D, int NS, bool OB16, bool OG>
 __global__ void __launch_bounds__(64 * (C / 16)) chunk_out_kernel(ChunkArgs a) {
@@ -1205,15 +1209,17 @@ __global__ void __launch_bounds__(64 * (C / 16)) chunk_out_kernel(ChunkArgs a) {
       qf[ks][p] = *reinterpret_cast<const bf16x8 *>(Qp + (size_t)p * C * D + ((wave * NKD + ks) * 64 + lane) * 8);
   const float *Ob = a.Ob + ch * (size_t)C * D;
   __syncthreads();
-  const int tok0 = 16 * wave + 4 * g;  // token of acc[0] within the chunk
-  const size_t orow0 = rbase + tok0;
+  const int tok = 16 * wave + l16;  // this lane's token within the chunk
+  const bool live = tok < tvalid;   // padding rows are never stored
+  const size_t orow = rbase + tok;
+  // lane (l16, g): token tok, value channels 16 jt + 4 g .. + 3
   auto product = [&](int jt) {
     f32x4 acc = *reinterpret_cast<const f32x4 *>(Ob + ((size_t)(wave * NMT + jt) * 64 + lane) * 4);
 #pragma unroll
     for (int ks = 0; ks < NKD; ++ks) {
       bf16x8 sf[NS];
       load_frag<NS>(sc + (jt * NFR + ks * NS) * FRAG + lane * 8, FRAG, sf);
-      acc = mfma32_split<NS>(qf[ks], sf, acc);
+      acc = mfma32_split<NS>(sf, qf[ks], acc);
     }
     return acc;
   };
@@ -1221,33 +1227,23 @@ __global__ void __launch_bounds__(64 * (C / 16)) chunk_out_kernel(ChunkArgs a) {
 #pragma unroll 1
     for (int jt = 0; jt < NSL; ++jt) {
       const f32x4 acc = product(jt);
-      const int col = 16 * jt + l16;
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (tok0 + r < tvalid) st1_stream<OB16>(a.o, (orow0 + r) * D + col, acc[r]);  // no padding rows
+      if (live) st4_stream<OB16>(a.o, orow * D + 16 * jt + 4 * g, acc);
     }
   } else {
-    // all dv columns of this lane's 4 tokens (column 16 jt + l16)
+    // this lane's 4 value channels of every slice
     f32x4 ov[NSL];
-    float ss[4] = {0.f, 0.f, 0.f, 0.f};
+    float ss = 0.f;
 #pragma unroll
     for (int jt = 0; jt < NSL; ++jt) {
       ov[jt] = product(jt);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) ss[r] += ov[jt][r] * ov[jt][r];
-      if (a.oraw) {  // o before the norm and the gate, for the gate's backward
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (tok0 + r < tvalid) a.oraw[(orow0 + r) * D + 16 * jt + l16] = ov[jt][r];
-      }
+      for (int r = 0; r < 4; ++r) ss += ov[jt][r] * ov[jt][r];
+      if (a.oraw && live)  // o before the norm and the gate, for the gate's backward
+        *reinterpret_cast<f32x4 *>(a.oraw + orow * D + 16 * jt + 4 * g) = ov[jt];
     }
-    float inv[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-#pragma unroll
-      for (int off = 1; off < 16; off <<= 1) ss[r] += __shfl_xor(ss[r], off, kWave);  // the 16 lanes of the row
-      inv[r] = rsqrtf(ss[r] / (float)D + a.oeps);
-    }
+    ss += __shfl_xor(ss, 16, kWave);  // the 4 lanes of the token
+    ss += __shfl_xor(ss, 32, kWave);
+    const float inv = rsqrtf(ss / (float)D + a.oeps);
     // normalised rows through LDS (the S_c planes are no longer read), then
     // each thread takes 8 consecutive columns of one token: the gate loads
     // and the token-major stores are whole 16- or 32-byte vectors
@@ -1255,9 +1251,7 @@ __global__ void __launch_bounds__(64 * (C / 16)) chunk_out_kernel(ChunkArgs a) {
     float *ys = reinterpret_cast<float *>(smem);  // [C][D + 4] fp32
     constexpr int YLD = D + 4;
 #pragma unroll
-    for (int jt = 0; jt < NSL; ++jt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) ys[(tok0 + r) * YLD + 16 * jt + l16] = ov[jt][r] * inv[r];
+    for (int jt = 0; jt < NSL; ++jt) *reinterpret_cast<f32x4 *>(ys + tok * YLD + 16 * jt + 4 * g) = ov[jt] * inv;
     __syncthreads();
     const size_t T = (size_t)a.T;
     constexpr int PT = D / 8;  // threads per token

@@ -116,6 +116,17 @@ __device__ __forceinline__ void st1_stream(void *p, size_t i, float x) {
     __builtin_nontemporal_store(x, reinterpret_cast<float *>(p) + i);
 }
 
+// ... and of 4 consecutive elements (i multiple of 4; 8- or 16-byte aligned).
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+template <bool BF16>
+__device__ __forceinline__ void st4_stream(void *p, size_t i, f32x4 x) {
+  if constexpr (BF16)
+    __builtin_nontemporal_store(u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])},
+                                reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(p) + i));
+  else
+    __builtin_nontemporal_store(x, reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p) + i));
+}
+
 template <bool BF16>
 __device__ __forceinline__ void st1(void *p, size_t i, float x) {
   if constexpr (BF16)

@@ -16,7 +16,7 @@ struct ChunkArgs {
   void *o;
   float *S_T;
   uint16_t *Qp, *Mm;  // workspace: A-fragment planes of Q' and M
-  float *Ob, *Nn;     // workspace: accumulator tiles of O_bar and N (intra-chunk
+  float *Ob, *Nn;     // workspace: accumulator tiles of O_bar^T and N (intra-chunk
                       // kernel alone: Ob null skips O_bar, which only the output kernel reads)
   uint16_t *Sc;       // workspace: chunk-start states as B-fragment planes
   int B, H, T, alpha_mode, b_mode, w_mode, normalize_qk;
