@@ -192,10 +192,13 @@ __device__ __forceinline__ void ldc(const void *p, size_t i, float (&o)[N]) {
 // work); wave 2p + hc computes column half hc of every C x D result of its
 // row tile.  Of the C x C results the pair owns row tiles rt (dA) and 3 - rt
 // (dL), the two waves taking alternate column tiles.  In a 16x16x4 MFMA, lane
-// (l16, g) = (lane % 16, lane / 16) supplies A[l16][k] and B[k][l16] for one
-// k and receives D[4g + r][l16], r = 0..3.  A k-block of 16 takes four MFMAs,
-// lane group g supplying k = 16 kb + 4 g + e at step e, so every lane reads
-// its A values (and, for products with a transposed B, its B values) as one
+// (l16, g) = (lane % 16, lane / 16) supplies X[l16][k] and Y[k][l16] for one
+// k and receives (XY)[4g + r][l16], r = 0..3.  The products here pass B's
+// values as X and A's as Y, so the instruction forms the transposed tile and
+// lane (l16, g) receives C[l16][4g + r] of C = AB: four consecutive columns
+// of one row, stored as one vector.  A k-block of 16 takes four MFMAs, lane
+// group g supplying k = 16 kb + 4 g + e at step e, so every lane reads its A
+// values (and, for products with a transposed B, its B values) as one
 // float4.  LDS rows are padded by 4 floats: conflict-free for both access
 // patterns.
 // ---------------------------------------------------------------------------
@@ -211,7 +214,7 @@ __device__ __forceinline__ void mm_nn(f32x4 (&acc)[NT], const f32x4 (&af)[NK], c
     for (int e = 0; e < 4; ++e) {
       const float *brow = B + (16 * kb + 4 * g + e) * sp + 16 * ct0 + l16;
 #pragma unroll
-      for (int ct = 0; ct < NT; ++ct) acc[ct] = mfma4(af[kb][e], brow[16 * ct], acc[ct]);
+      for (int ct = 0; ct < NT; ++ct) acc[ct] = mfma4(brow[16 * ct], af[kb][e], acc[ct]);
     }
   }
 }
@@ -226,7 +229,7 @@ __device__ __forceinline__ void mm_nt(f32x4 (&acc)[NT], const f32x4 (&af)[NK], c
     for (int ct = 0; ct < NT; ++ct) {
       const f32x4 b4 = *reinterpret_cast<const f32x4 *>(Y + (16 * (ct0 + ct) + l16) * sp + 16 * kb + 4 * g);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[ct] = mfma4(af[kb][e], b4[e], acc[ct]);
+      for (int e = 0; e < 4; ++e) acc[ct] = mfma4(b4[e], af[kb][e], acc[ct]);
     }
 }
 
@@ -243,7 +246,7 @@ __device__ __forceinline__ void mm_nt_alt(f32x4 (&acc)[2], const f32x4 (&af)[NK]
       if (ct > ctmax) continue;  // wave-uniform
       const f32x4 b4 = *reinterpret_cast<const f32x4 *>(U + (16 * ct + l16) * sp + 16 * kb + 4 * g);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[j] = mfma4(af[kb][e], b4[e], acc[j]);
+      for (int e = 0; e < 4; ++e) acc[j] = mfma4(b4[e], af[kb][e], acc[j]);
     }
 }
 
@@ -315,30 +318,30 @@ __global__ void __launch_bounds__(512) bwd_mm_kernel(BwdArgs a) {
       }
     }
   };
-  // this wave's part of a C x D result: rows 16 rt + 4 g + r, columns 16 (ct0 + ct) + l16
+  // this wave's part of a C x D result: row 16 rt + l16, columns
+  // 16 (ct0 + ct) + 4 g .. + 3 (one vector per tile)
   auto put_glb = [&](float *dst, const f32x4 (&acc)[NCH], float sign) {
 #pragma unroll
     for (int ct = 0; ct < NCH; ++ct)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        dst[base + (size_t)(16 * rt + 4 * g + r) * D + 16 * (ct0 + ct) + l16] = sign * acc[ct][r];
+      *reinterpret_cast<f32x4 *>(dst + base + (size_t)ar * D + 16 * (ct0 + ct) + 4 * g) = sign * acc[ct];
   };
   auto put_lds = [&](float *dst, const f32x4 (&acc)[NCH]) {
 #pragma unroll
-    for (int ct = 0; ct < NCH; ++ct)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) dst[(16 * rt + 4 * g + r) * SP + 16 * (ct0 + ct) + l16] = acc[ct][r];
+    for (int ct = 0; ct < NCH; ++ct) *reinterpret_cast<f32x4 *>(dst + ar * SP + 16 * (ct0 + ct) + 4 * g) = acc[ct];
   };
-  // this wave's column tiles ct = hc + 2 j of C x C row tile `row` (zero
-  // where s > t, or s >= t when strict)
+  // this wave's column tiles ct = hc + 2 j of C x C row tile `row`: row
+  // 16 row + l16, columns 16 ct + 4 g .. + 3 (zero where s > t, or s >= t
+  // when strict)
   auto put_cc = [&](float *dst, const f32x4 (&acc)[2], int row, float sign, bool strict) {
+    const int t = 16 * row + l16;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 2; ++j) {
+      const int s0 = 16 * (hc + 2 * j) + 4 * g;
+      f32x4 v;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * row + 4 * g + r, s2 = 16 * (hc + 2 * j) + l16;
-        dst[cbase + (size_t)t * C + s2] = (strict ? s2 < t : s2 <= t) ? sign * acc[j][r] : 0.f;
-      }
+      for (int r = 0; r < 4; ++r) v[r] = (strict ? s0 + r < t : s0 + r <= t) ? sign * acc[j][r] : 0.f;
+      *reinterpret_cast<f32x4 *>(dst + cbase + (size_t)t * C + s0) = v;
+    }
   };
   f32x4 acc[NCH], acc2[NCH], acs[2];
   f32x4 af[NKB], dof[NKB], tf[NTC];
@@ -360,11 +363,10 @@ __global__ void __launch_bounds__(512) bwd_mm_kernel(BwdArgs a) {
     const float4 kh = *reinterpret_cast<const float4 *>(a.KH + o), la = *reinterpret_cast<const float4 *>(a.LAM + o);
     af[kb] = f32x4{kh.x * __expf(la.x), kh.y * __expf(la.y), kh.z * __expf(la.z), kh.w * __expf(la.w)};
   }
-  float vh[NCH][4];
+  f32x4 vh[NCH];
 #pragma unroll
   for (int ct = 0; ct < NCH; ++ct)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) vh[ct][r] = a.VH[base + (size_t)(16 * rt + 4 * g + r) * D + 16 * (ct0 + ct) + l16];
+    vh[ct] = *reinterpret_cast<const f32x4 *>(a.VH + base + (size_t)ar * D + 16 * (ct0 + ct) + 4 * g);
 #pragma unroll
   for (int kb = 0; kb < NTC; ++kb)
     tf[kb] = *reinterpret_cast<const f32x4 *>(a.TI + cbase + (size_t)ar * C + 16 * kb + 4 * g);
@@ -372,9 +374,7 @@ __global__ void __launch_bounds__(512) bwd_mm_kernel(BwdArgs a) {
   zero_acc(acc);
   mm_nn(acc, af, ss, SP, 0, NKB, g, l16, ct0);
 #pragma unroll
-  for (int ct = 0; ct < NCH; ++ct)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) bt[(16 * rt + 4 * g + r) * SP + 16 * (ct0 + ct) + l16] = vh[ct][r] - acc[ct][r];
+  for (int ct = 0; ct < NCH; ++ct) *reinterpret_cast<f32x4 *>(bt + ar * SP + 16 * (ct0 + ct) + 4 * g) = vh[ct] - acc[ct];
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) dof[kb] = *reinterpret_cast<const f32x4 *>(bu + ar * SP + 16 * kb + 4 * g);
   zero_acc(acc);
