@@ -43,9 +43,9 @@ METRIC = "tokens/s + % bf16 MFMA peak, chunk fwd T=32K H=16 d=128; decode HBM GB
 # (digest below: the kernel's sources, the ABI and the build flags);
 # otherwise reported as null.
 MEASURED_TRAFFIC = {
-    "sources": "949cd32d739628ad",
-    "chunk_intra_kernel_C128_seg": 269442261,   # 512 chunks of 128 tokens per launch
-    "chunk_intra_kernel_C64_seg": 168475136,    # 512 chunks of 64 tokens per launch
+    "sources": "070100487ff0aef5",
+    "chunk_intra_kernel_C128_seg": 269419924,   # 512 chunks of 128 tokens per launch
+    "chunk_intra_kernel_C64_seg": 168478480,    # 512 chunks of 64 tokens per launch
 }
 
 
