@@ -99,23 +99,36 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdArgs a) {
   const SlotTokens st = slot_tokens(a, slot);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, g = lane >> 4;
   // Q' (planes summed in fp32) and dO into LDS
+  // every load of the staging in flight before the first LDS store
   const uint16_t *Qs = a.Qp + slot * NS * (size_t)C * D;
-  for (int idx = tid; idx < C * D / 8; idx += 256) {
-    const int f = idx >> 6, ln = idx & 63, t = 16 * (f / NKD) + (ln & 15), col = 32 * (f % NKD) + 4 * (ln >> 4);
+  constexpr int NQ = C * D / 8 / 256, ND = C * D / 4 / 256;
+  bf16x8 qv[NQ][NS];
+  f32x4 dv[ND];
+#pragma unroll
+  for (int it = 0; it < NQ; ++it)
+#pragma unroll
+    for (int p = 0; p < NS; ++p) qv[it][p] = reinterpret_cast<const bf16x8 *>(Qs + (size_t)p * C * D)[tid + 256 * it];
+#pragma unroll
+  for (int it = 0; it < ND; ++it) {
+    const int idx = tid + 256 * it, t = idx / (D / 4), j4 = idx % (D / 4);
+    dv[it] = t < st.valid ? ld_do4(a.dO, (st.row + t) * D + 4 * j4, a.do_bf16) : zero4();
+  }
+#pragma unroll
+  for (int it = 0; it < NQ; ++it) {
+    const int idx = tid + 256 * it, f = idx >> 6, ln = idx & 63, t = 16 * (f / NKD) + (ln & 15),
+              col = 32 * (f % NKD) + 4 * (ln >> 4);
     float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int p = 0; p < NS; ++p) {
-      const bf16x8 q8 = reinterpret_cast<const bf16x8 *>(Qs + (size_t)p * C * D)[idx];
+    for (int p = 0; p < NS; ++p)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] += (float)q8[e];
-    }
+      for (int e = 0; e < 8; ++e) v[e] += (float)qv[it][p][e];
     *reinterpret_cast<float4 *>(qs + t * SP + col) = float4{v[0], v[1], v[2], v[3]};
     *reinterpret_cast<float4 *>(qs + t * SP + col + 16) = float4{v[4], v[5], v[6], v[7]};
   }
-  for (int idx = tid; idx < C * D / 4; idx += 256) {
-    const int t = idx / (D / 4), j4 = idx % (D / 4);
-    *reinterpret_cast<f32x4 *>(ds + t * SP + 4 * j4) =
-        t < st.valid ? ld_do4(a.dO, (st.row + t) * D + 4 * j4, a.do_bf16) : zero4();
+#pragma unroll
+  for (int it = 0; it < ND; ++it) {
+    const int idx = tid + 256 * it, t = idx / (D / 4), j4 = idx % (D / 4);
+    *reinterpret_cast<f32x4 *>(ds + t * SP + 4 * j4) = dv[it];
   }
   __syncthreads();
   // G[i][j] = sum_t Q'[t][i] dO[t][j]: lane (l16, g) supplies k = t = 16 kb + 4 g + e
@@ -352,10 +365,19 @@ __global__ void __launch_bounds__(512) bwd_mm_kernel(BwdArgs a) {
   bf16x8 pa[NE][NS], pb[NE][NS];  // planes: S0 (pb, kept for phases 3 and 5); X (pa)
   load_planes(S0p, pb);
   store_planes(ss, pb, pb, false);
-  for (int idx = tid; idx < C * D / 4; idx += 512) {
-    const int t = idx / (D / 4), j4 = idx % (D / 4);
-    *reinterpret_cast<f32x4 *>(bu + t * SP + 4 * j4) =
-        t < st.valid ? ld_do4(a.dO, (st.row + t) * D + 4 * j4, a.do_bf16) : zero4();
+  {  // every load in flight before the first LDS store
+    constexpr int NIT = C * D / 4 / 512;
+    f32x4 dv[NIT];
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int idx = tid + 512 * it, t = idx / (D / 4), j4 = idx % (D / 4);
+      dv[it] = t < st.valid ? ld_do4(a.dO, (st.row + t) * D + 4 * j4, a.do_bf16) : zero4();
+    }
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int idx = tid + 512 * it, t = idx / (D / 4), j4 = idx % (D / 4);
+      *reinterpret_cast<f32x4 *>(bu + t * SP + 4 * j4) = dv[it];
+    }
   }
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
@@ -513,14 +535,21 @@ __global__ void __launch_bounds__(256) bwd_gramback_kernel(BwdArgs a) {
   const size_t base = slot * (size_t)C * D, cbase = slot * (size_t)C * C;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, g = lane >> 4;
   const int c0 = NCT * l16;  // first channel of this lane
-  {
+  {  // every load of the staging in flight before the first LDS store
     const float *src[4] = {a.KN, a.LAM, a.QT, a.KH};
-    for (int idx = tid; idx < C * D / 4; idx += 256) {
-      const int t = idx / (D / 4), j4 = idx % (D / 4);
+    constexpr int NIT = C * D / 4 / 256;
+    float4 sv[NIT][4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<float4 *>(stg[q] + t * SPD + 4 * j4) =
-            *reinterpret_cast<const float4 *>(src[q] + base + (size_t)t * D + 4 * j4);
+    for (int it = 0; it < NIT; ++it) {
+      const int idx = tid + 256 * it, t = idx / (D / 4), j4 = idx % (D / 4);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sv[it][q] = *reinterpret_cast<const float4 *>(src[q] + base + (size_t)t * D + 4 * j4);
+    }
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int idx = tid + 256 * it, t = idx / (D / 4), j4 = idx % (D / 4);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) *reinterpret_cast<float4 *>(stg[q] + t * SPD + 4 * j4) = sv[it][q];
     }
   }
   __syncthreads();

@@ -1197,9 +1197,15 @@ __global__ void __launch_bounds__(64 * (C / 16)) chunk_out_kernel(ChunkArgs a) {
   }
 
   const uint16_t *Scg = a.Sc + ch * (size_t)NS * D * D;
-  constexpr int NV = NSL * NFR * FRAG / 8;  // 16-byte vectors
-  for (int v = tid; v < NV; v += 64 * NRT)
-    *reinterpret_cast<uint4 *>(sc + v * 8) = *reinterpret_cast<const uint4 *>(Scg + v * 8);
+  // all of a thread's 16-byte vectors loaded before any is stored, so their
+  // loads are in flight together
+  constexpr int NV = NSL * NFR * FRAG / 8, NVT = NV / (64 * NRT);
+  static_assert(NVT * 64 * NRT == NV, "whole vectors per thread");
+  u32x4 scv[NVT];  // a vector type: an array of structs would stay in scratch
+#pragma unroll
+  for (int v = 0; v < NVT; ++v) scv[v] = *reinterpret_cast<const u32x4 *>(Scg + (tid + v * 64 * NRT) * 8);
+#pragma unroll
+  for (int v = 0; v < NVT; ++v) *reinterpret_cast<u32x4 *>(sc + (tid + v * 64 * NRT) * 8) = scv[v];
   const uint16_t *Qp = a.Qp + ch * NS * (size_t)C * D;
   bf16x8 qf[NKD][NS];
 #pragma unroll
