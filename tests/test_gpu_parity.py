@@ -535,6 +535,22 @@ def test_gated_output(name, chunk, T, d):
     check(f"gated {name} C{chunk} T{T} d{d} S_T", sT.cpu().numpy(), rs, tol)
 
 
+def test_gated_output_fp32_inputs_d128():
+    """fp32 inputs at d = 128 (three bf16 planes per operand) through the
+    gated whole call, against the oracle's recurrence and output gate."""
+    wl = WORKLOADS["gdn2"].with_sizes(B=1, H=2, T=130, dtype="f32")
+    x, g, nw = gated_case(wl, seed=5)
+    dd = dev(x)
+    y, sT = gdr.gdr_chunk_fwd_gated(dd["q"], dd["k"], dd["v"], dd["log_alpha"], dd["b"], dd["w"], g.to(DEV),
+                                    gamma=dd["gamma"], z=dd["z"], S0=dd["S0"], norm_weight=nw.to(DEV),
+                                    eps=1e-6, chunk=64)
+    torch.cuda.synchronize()
+    ro, rs = oracle_run(x)
+    ry = oracle.output_gate(ro, g, norm_weight=nw, eps=1e-6)
+    check("gated f32 d128 y", y.cpu().numpy(), ry, TOL_F32)
+    check("gated f32 d128 S_T", sT.cpu().numpy(), rs, TOL_F32)
+
+
 def test_gated_output_bf16_and_segmented():
     """bf16 y against the oracle's y rounded to bf16; and at a length that runs
     in segments, the gated call equals the output gate applied (in fp64) to
