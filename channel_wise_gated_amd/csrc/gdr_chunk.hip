@@ -311,8 +311,11 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
       x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xF, 0xF, false));
       return x;
     };
-    // block total (lane 15 of the row), broadcast by a bit-mode swizzle: lane -> (lane & 16) | 15
-    auto row_total = [](float x) { return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x1F0)); };
+    // block total (lane 15 of the row), broadcast within each row of 16 lanes
+    // by a DPP row broadcast (no trip through the LDS unit)
+    auto row_total = [](float x) {
+      return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x15F, 0xF, 0xF, false));
+    };
     float P1 = 0.f, tot1 = 0.f, R1 = 1.f, Cf1 = 1.f;  // scalar decay: per token
     if constexpr (SA) {
       P1 = row_scan(la1);
