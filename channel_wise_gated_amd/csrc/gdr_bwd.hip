@@ -655,26 +655,36 @@ __global__ void __launch_bounds__(256) bwd_gramback_kernel(BwdArgs a) {
   load_rows(0, cur);
   // bf16 inputs: the token's raw q, k, v, z and per-channel b, w (NCT bf16
   // each, as 32-bit pairs), also one token ahead
+  // (and the per-token gate values of b and w in that mode, for any input
+  // type).  Every load is unconditional -- an absent tensor reads q instead --
+  // because a branch around a load makes the compiler wait at the join for
+  // every load in flight, the next token's included.
   constexpr int NP = BF ? NCT / 2 : 1;
   struct TokRaw {
     uint32_t q[NP], k[NP], v[NP], z[NP], b[NP], w[NP];
+    float bt, wt;
   };
+  const bool bch = a.b_mode == GDR_GATE_PER_CHANNEL, wch = a.w_mode == GDR_GATE_PER_CHANNEL;
+  const bool btk = a.b_mode == GDR_GATE_PER_TOKEN, wtk = a.w_mode == GDR_GATE_PER_TOKEN;
   auto load_raw = [&](int r, TokRaw &R) {
+    const int t = 16 * w + 4 * g + r;
+    const size_t row = st.row + (t < st.valid ? t : 0);
     if constexpr (BF) {
-      const int t = 16 * w + 4 * g + r;
-      const size_t o = (st.row + (t < st.valid ? t : 0)) * D + c0;
-      auto ld = [&](const void *p, uint32_t(&x)[NP]) {
-        const uint32_t *src = reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(p) + o);
+      const size_t o = row * D + c0;
+      auto ld = [&](const void *p, bool use, uint32_t(&x)[NP]) {
+        const uint32_t *src = reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(use ? p : a.q) + o);
 #pragma unroll
         for (int i = 0; i < NP; ++i) x[i] = src[i];
       };
-      ld(a.q, R.q);
-      ld(a.k, R.k);
-      ld(a.v, R.v);
-      if (a.z) ld(a.z, R.z);
-      if (a.b_mode == GDR_GATE_PER_CHANNEL) ld(a.b, R.b);
-      if (a.w_mode == GDR_GATE_PER_CHANNEL) ld(a.w, R.w);
+      ld(a.q, true, R.q);
+      ld(a.k, true, R.k);
+      ld(a.v, true, R.v);
+      ld(a.z, a.z != nullptr, R.z);
+      ld(a.b, bch, R.b);
+      ld(a.w, wch, R.w);
     }
+    R.bt = ld1<BF>(btk ? a.b : a.q, btk ? row : 0);
+    R.wt = ld1<BF>(wtk ? a.w : a.q, wtk ? row : 0);
   };
   auto unpack = [](const uint32_t(&x)[NP], float(&o)[NCT]) {
 #pragma unroll
@@ -685,6 +695,10 @@ __global__ void __launch_bounds__(256) bwd_gramback_kernel(BwdArgs a) {
   };
   TokRaw craw;
   load_raw(0, craw);
+  // the read-out gain of this lane's channels (loaded once, not per token)
+  float gamv[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) gamv[ct] = a.gamma ? a.gamma[(size_t)hd * D + c0 + ct] : 1.f;
 #pragma unroll 1
   for (int r = 0; r < 4; ++r) {
     const int t = 16 * w + 4 * g + r;
@@ -753,17 +767,29 @@ __global__ void __launch_bounds__(256) bwd_gramback_kernel(BwdArgs a) {
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) zx[ct] = 0.f;
     }
-    if (BF && a.b_mode == GDR_GATE_PER_CHANNEL) {
-      if constexpr (BF) unpack(craw.b, bg);
-    } else {
+    if (bch) {
+      if constexpr (BF) {
+        unpack(craw.b, bg);
+      } else {
 #pragma unroll
-      for (int v = 0; v < NV; ++v) gate4<BF>(a.b, a.b_mode, grow, c0 + 4 * v, D, bg + 4 * v);
+        for (int v = 0; v < NV; ++v) ld4<BF>(a.b, grow * D + c0 + 4 * v, bg + 4 * v);
+      }
+    } else {
+      const float bv = btk ? craw.bt : (a.b_mode == GDR_GATE_ONES ? 1.f : 0.f);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) bg[ct] = bv;
     }
-    if (BF && a.w_mode == GDR_GATE_PER_CHANNEL) {
-      if constexpr (BF) unpack(craw.w, wg);
-    } else {
+    if (wch) {
+      if constexpr (BF) {
+        unpack(craw.w, wg);
+      } else {
 #pragma unroll
-      for (int v = 0; v < NV; ++v) gate4<BF>(a.w, a.w_mode, grow, c0 + 4 * v, D, wg + 4 * v);
+        for (int v = 0; v < NV; ++v) ld4<BF>(a.w, grow * D + c0 + 4 * v, wg + 4 * v);
+      }
+    } else {
+      const float wv = wtk ? craw.wt : (a.w_mode == GDR_GATE_ONES ? 1.f : 0.f);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) wg[ct] = wv;
     }
     float sq[NCT], sn[NCT], nq = 0.f, nk = 0.f;
 #pragma unroll
@@ -791,7 +817,7 @@ __global__ void __launch_bounds__(256) bwd_gramback_kernel(BwdArgs a) {
                    h[ct] * RL[ct] - kn[ct] * CS[ct];
       skp[ct] += kn[ct] * rat * dkp[ct];
       const float qh = sq[ct] * irq, knv = sn[ct] * irk;
-      const float gam = a.gamma ? a.gamma[(size_t)hd * D + c0 + ct] : 1.f;
+      const float gam = gamv[ct];
       const float sg = fast_rcp(1.f + __expf(-zx[ct]));
       const float dyn = a.z ? 2.f * sg : 1.f;
       dqh[ct] = dqt * a.scale * gam * dyn;
