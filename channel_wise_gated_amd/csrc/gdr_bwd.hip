@@ -78,18 +78,30 @@ __device__ __forceinline__ f32x4 mfma4(float x, float y, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(x, y, c, 0, 0, 0);
 }
 
-// four consecutive dO values (fp32 or bf16)
-__device__ __forceinline__ f32x4 ld_do4(const void *p, size_t i, int bf) {
-  if (bf) {
+// four consecutive dO values (bf16 or fp32: a template argument, so that
+// the loads of a staging loop have no branch between them, which would make
+// the compiler wait for each before issuing the next)
+template <bool DOBF>
+__device__ __forceinline__ f32x4 ld_do4(const void *p, size_t i) {
+  if constexpr (DOBF) {
     const uint2 r = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(p) + i);
     return f32x4{__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u), __uint_as_float(r.y << 16),
                  __uint_as_float(r.y & 0xffff0000u)};
+  } else {
+    const float4 v = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(p) + i);
+    return f32x4{v.x, v.y, v.z, v.w};
   }
-  const float4 v = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(p) + i);
-  return f32x4{v.x, v.y, v.z, v.w};
 }
 
-template <int D, int NS>
+// Row t of a slot's dO (rows past the slot's tokens read its last real row,
+// or row 0 of an empty slot, and are zeroed after the load).
+template <bool DOBF, int D>
+__device__ __forceinline__ f32x4 ld_do_row(const void *dO, size_t row0, int valid, int t, int c) {
+  const f32x4 v = ld_do4<DOBF>(dO, (row0 + (size_t)min(t, max(valid - 1, 0))) * D + c);
+  return t < valid ? v : zero4();
+}
+
+template <int D, int NS, bool DOBF>
 __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdArgs a) {
   constexpr int C = kBC, NKD = D / 32, NMT = D / 16, SP = D + 4, RT = NMT / 4;
   // Q' [t][i] and dO [t][j]
@@ -111,7 +123,7 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdArgs a) {
 #pragma unroll
   for (int it = 0; it < ND; ++it) {
     const int idx = tid + 256 * it, t = idx / (D / 4), j4 = idx % (D / 4);
-    dv[it] = t < st.valid ? ld_do4(a.dO, (st.row + t) * D + 4 * j4, a.do_bf16) : zero4();
+    dv[it] = ld_do_row<DOBF, D>(a.dO, st.row, st.valid, t, 4 * j4);
   }
 #pragma unroll
   for (int it = 0; it < NQ; ++it) {
@@ -269,7 +281,7 @@ __device__ __forceinline__ void zero_acc(f32x4 (&acc)[NT]) {
   for (int ct = 0; ct < NT; ++ct) acc[ct] = zero4();
 }
 
-template <int D, int NS>
+template <int D, int NS, bool DOBF>
 __global__ void __launch_bounds__(512) bwd_mm_kernel(BwdArgs a) {
   constexpr int C = kBC, SP = D + 4, NKB = D / 16, NCT = D / 16, NCH = NCT / 2, NTC = C / 16;
   constexpr int BBR = 2 * C > D ? 2 * C : D, NFR = (D / 32) * NS, FRAG = 512;
@@ -371,7 +383,7 @@ __global__ void __launch_bounds__(512) bwd_mm_kernel(BwdArgs a) {
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
       const int idx = tid + 512 * it, t = idx / (D / 4), j4 = idx % (D / 4);
-      dv[it] = t < st.valid ? ld_do4(a.dO, (st.row + t) * D + 4 * j4, a.do_bf16) : zero4();
+      dv[it] = ld_do_row<DOBF, D>(a.dO, st.row, st.valid, t, 4 * j4);
     }
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
@@ -1052,7 +1064,10 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
       hipLaunchKernelGGL((bwd_dgamma_kernel<D>), dim3((unsigned)(a.H * (D / 32))), dim3(256), 0, st, a);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((bwd_mm_kernel<D, NS>), dim3(nch), dim3(512), 0, st, a);
+  if (a.do_bf16)
+    hipLaunchKernelGGL((bwd_mm_kernel<D, NS, true>), dim3(nch), dim3(512), 0, st, a);
+  else
+    hipLaunchKernelGGL((bwd_mm_kernel<D, NS, false>), dim3(nch), dim3(512), 0, st, a);
   hipLaunchKernelGGL((bwd_gramback_kernel<D, BF>), dim3(nch), dim3(256), 0, st, a);
   if (a.dgamma && a.gamma)
     hipLaunchKernelGGL((bwd_dgamma_kernel<D>), dim3((unsigned)(a.H * (D / 32))), dim3(256), 0, st, a);
@@ -1062,7 +1077,10 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
 template <int D, int NS>
 hipError_t launch_bwd_prep_t(const BwdArgs &a, hipStream_t st) {
   const unsigned nch = (unsigned)(a.ctab ? (size_t)a.H * a.ctab_len : (size_t)a.B * a.H * a.NC);
-  hipLaunchKernelGGL((bwd_prep_kernel<D, NS>), dim3(nch), dim3(256), 0, st, a);
+  if (a.do_bf16)
+    hipLaunchKernelGGL((bwd_prep_kernel<D, NS, true>), dim3(nch), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((bwd_prep_kernel<D, NS, false>), dim3(nch), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
