@@ -1217,6 +1217,13 @@ __global__ void __launch_bounds__(64 * (C / 16)) chunk_out_kernel(ChunkArgs a) {
     for (int p = 0; p < NS; ++p)
       qf[ks][p] = *reinterpret_cast<const bf16x8 *>(Qp + (size_t)p * C * D + ((wave * NKD + ks) * 64 + lane) * 8);
   const float *Ob = a.Ob + ch * (size_t)C * D;
+  // gated output: all of the wave's O_bar tiles loaded with the other loads
+  // (its products come before any store, so they are waited for once)
+  f32x4 obg[OG ? NSL : 1];
+  if constexpr (OG) {
+#pragma unroll
+    for (int jt = 0; jt < NSL; ++jt) obg[jt] = *reinterpret_cast<const f32x4 *>(Ob + ((size_t)(wave * NMT + jt) * 64 + lane) * 4);
+  }
   __syncthreads();
   const int tok = 16 * wave + l16;  // this lane's token within the chunk
   const bool live = tok < tvalid;   // padding rows are never stored
@@ -1241,10 +1248,19 @@ __global__ void __launch_bounds__(64 * (C / 16)) chunk_out_kernel(ChunkArgs a) {
   } else {
     // this lane's 4 value channels of every slice
     f32x4 ov[NSL];
+#pragma unroll
+    for (int jt = 0; jt < NSL; ++jt) ov[jt] = obg[jt];
+#pragma unroll
+    for (int jt = 0; jt < NSL; ++jt)
+#pragma unroll
+      for (int ks = 0; ks < NKD; ++ks) {
+        bf16x8 sf[NS];
+        load_frag<NS>(sc + (jt * NFR + ks * NS) * FRAG + lane * 8, FRAG, sf);
+        ov[jt] = mfma32_split<NS>(sf, qf[ks], ov[jt]);
+      }
     float ss = 0.f;
 #pragma unroll
     for (int jt = 0; jt < NSL; ++jt) {
-      ov[jt] = product(jt);
 #pragma unroll
       for (int r = 0; r < 4; ++r) ss += ov[jt][r] * ov[jt][r];
       if (a.oraw && live)  // o before the norm and the gate, for the gate's backward
