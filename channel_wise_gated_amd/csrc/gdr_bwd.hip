@@ -426,8 +426,12 @@ __global__ void __launch_bounds__(512) bwd_mm_kernel(BwdArgs a) {
   __syncthreads();
   put_lds(bt, acc);
 
-  // (3) X phase: dA = dO U^T, Z = A^T dO + K' X, dK' = U X^T
-  store_planes(ss, pa, pb, true);
+  // (3) X phase: dA = dO U^T, Z = A^T dO + K' X, dK' = U X^T; this phase's
+  // rows of A^T, kn and Lambda are loaded before the state is staged
+#pragma unroll
+  for (int kb = 0; kb < NTC; ++kb)  // A^T rows: A[t][ar] for t = 16 kb + 4 g + e
+#pragma unroll
+    for (int e = 0; e < 4; ++e) tf[kb][e] = a.AM[cbase + (size_t)(16 * kb + 4 * g + e) * C + ar];
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
     const size_t o = base + (size_t)ar * D + 16 * kb + 4 * g;
@@ -436,10 +440,7 @@ __global__ void __launch_bounds__(512) bwd_mm_kernel(BwdArgs a) {
     af[kb] = f32x4{kn.x * __expf(lc.x - la.x), kn.y * __expf(lc.y - la.y), kn.z * __expf(lc.z - la.z),
                    kn.w * __expf(lc.w - la.w)};
   }
-#pragma unroll
-  for (int kb = 0; kb < NTC; ++kb)  // A^T rows: A[t][ar] for t = 16 kb + 4 g + e
-#pragma unroll
-    for (int e = 0; e < 4; ++e) tf[kb][e] = a.AM[cbase + (size_t)(16 * kb + 4 * g + e) * C + ar];
+  store_planes(ss, pa, pb, true);
   __syncthreads();
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) dof[kb] = *reinterpret_cast<const f32x4 *>(bu + ar * SP + 16 * kb + 4 * g);
@@ -448,6 +449,10 @@ __global__ void __launch_bounds__(512) bwd_mm_kernel(BwdArgs a) {
   put_cc(a.DA, acs, rt, 1.f, false);
   zero_acc(acc);
   mm_nn(acc, tf, bu, SP, rt, NTC, g, l16, ct0);  // A lower triangular: t >= s
+#pragma unroll
+  for (int kb = 0; kb < NTC; ++kb)  // phase 4's T^-T rows: T^-1[t][ar], in flight meanwhile
+#pragma unroll
+    for (int e = 0; e < 4; ++e) tf[kb][e] = a.TI[cbase + (size_t)(16 * kb + 4 * g + e) * C + ar];
   mm_nn(acc, af, ss, SP, 0, NKB, g, l16, ct0);
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) af[kb] = *reinterpret_cast<const f32x4 *>(bt + ar * SP + 16 * kb + 4 * g);
@@ -457,10 +462,6 @@ __global__ void __launch_bounds__(512) bwd_mm_kernel(BwdArgs a) {
   __syncthreads();  // every read of dO and X is done
   put_lds(bu, acc);
   if (tid < D) a.XS[slot * D + tid] = xs[tid];
-#pragma unroll
-  for (int kb = 0; kb < NTC; ++kb)  // T^-T rows: T^-1[t][ar]
-#pragma unroll
-    for (int e = 0; e < 4; ++e) tf[kb][e] = a.TI[cbase + (size_t)(16 * kb + 4 * g + e) * C + ar];
   __syncthreads();
 
   // (4) dU~ = T^-T Z (upper triangular: k-blocks from the row tile on)
