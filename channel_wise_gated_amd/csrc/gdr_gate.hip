@@ -262,15 +262,29 @@ __device__ __forceinline__ void gate_up_heads(const GateArgs &a, int gate, OT *o
     // tile ct, row i holds channel 32 (ct / 2) + 8 (i / 4) + 4 (ct % 2) + i % 4, so
     // that a lane's accumulators of tiles 2j, 2j + 1 are 8 consecutive channels
     const uint16_t *wc = wl + cur * WBUF + (8 * (l16 >> 2) + (l16 & 3)) * WROW + 8 * g;
+    // per k-step and pair of tiles: the pair's weight fragments read first,
+    // then its lo products and its hi products, so that an LDS read and the
+    // previous product on the same accumulator overlap other products (pairs
+    // keep the kernel within 128 registers; groups of 4 spilled)
+    constexpr int TG = 2;
+    static_assert(NCT % TG == 0, "whole pairs of tiles");
 #pragma unroll
-    for (int ks = 0; ks < NK; ++ks) {
+    for (int ks = 0; ks < NK; ++ks)
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        const bf16x8 wb = *reinterpret_cast<const bf16x8 *>(wc + (32 * (ct >> 1) + 4 * (ct & 1)) * WROW + 32 * ks);
-        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb, hf[ks][1], acc[ct], 0, 0, 0);
-        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb, hf[ks][0], acc[ct], 0, 0, 0);
+      for (int c0 = 0; c0 < NCT; c0 += TG) {
+        bf16x8 wb[TG];
+#pragma unroll
+        for (int u = 0; u < TG; ++u) {
+          const int ct = c0 + u;
+          wb[u] = *reinterpret_cast<const bf16x8 *>(wc + (32 * (ct >> 1) + 4 * (ct & 1)) * WROW + 32 * ks);
+        }
+#pragma unroll
+        for (int u = 0; u < TG; ++u)
+          acc[c0 + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb[u], hf[ks][1], acc[c0 + u], 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < TG; ++u)
+          acc[c0 + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb[u], hf[ks][0], acc[c0 + u], 0, 0, 0);
       }
-    }
     // buffer cur ^ 1 was last read in head hh - 1, which every wave finished
     // before the barrier that ended it
     asm volatile("" ::: "memory");
