@@ -886,24 +886,26 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
     const bool mw = wave < NMT;
     f32x4 accC[2] = {zero4(), zero4()}, accT[2] = {zero4(), zero4()};  // channel-tile, token-block products
     f32x4 accMt[PP ? 2 : 1] = {};  // PP, K half: K'^T Y itself (M^T up to the diagonal)
+    // both column tiles of a k-step together: their fragments read at once
+    // and their two accumulators' products interleaved (each accumulator
+    // still sums the k-steps in order)
 #pragma unroll
-    for (int ctl = 0; ctl < 2; ++ctl)
-#pragma unroll
-      for (int ks = 0; ks < NKC; ++ks) {
-        const bool tw = rowwave && 2 * ks <= i && (!vhalf || a.Ob);  // O_bar only when it is stored
-        if (!mw && !tw) continue;
-        bf16x8 zb[NS];
-        load_frag<NS>(rst + ((ks * 2 + ctl) * NS) * FRAG + lane * 8, FRAG, zb);
-        if (vhalf) {
-          if (mw) accC[ctl] = mfma32_split<NS>(wf[ks], zb, accC[ctl]);  // N = K'^T U_bar
-          if (tw) accT[ctl] = mfma32_split<NS>(zb, pf[ks], accT[ctl]);  // O_bar^T = U_bar^T A^T
-        } else {
-          if (mw) accC[ctl] = mfma32_split<NS>(zb, wf[ks], accC[ctl]);  // (K'^T Y)^T = Y^T K'
-          if (tw) accT[ctl] = mfma32_split<NS>(zb, pf[ks], accT[ctl]);  // (A Y)^T = Y^T A^T
-          if constexpr (PP)
-            if (mw) accMt[ctl] = mfma32_split<NS>(wf[ks], zb, accMt[ctl]);
-        }
+    for (int ks = 0; ks < NKC; ++ks) {
+      const bool tw = rowwave && 2 * ks <= i && (!vhalf || a.Ob);  // O_bar only when it is stored
+      if (!mw && !tw) continue;
+      bf16x8 z0[NS], z1[NS];
+      load_frag<NS>(rst + ((ks * 2) * NS) * FRAG + lane * 8, FRAG, z0);
+      load_frag<NS>(rst + ((ks * 2 + 1) * NS) * FRAG + lane * 8, FRAG, z1);
+      if (vhalf) {
+        if (mw) mfma32_split2<NS>(wf[ks], z0, accC[0], wf[ks], z1, accC[1]);  // N = K'^T U_bar
+        if (tw) mfma32_split2<NS>(z0, pf[ks], accT[0], z1, pf[ks], accT[1]);  // O_bar^T = U_bar^T A^T
+      } else {
+        if (mw) mfma32_split2<NS>(z0, wf[ks], accC[0], z1, wf[ks], accC[1]);  // (K'^T Y)^T = Y^T K'
+        if (tw) mfma32_split2<NS>(z0, pf[ks], accT[0], z1, pf[ks], accT[1]);  // (A Y)^T = Y^T A^T
+        if constexpr (PP)
+          if (mw) mfma32_split2<NS>(wf[ks], z0, accMt[0], wf[ks], z1, accMt[1]);
       }
+    }
     if (vhalf) {
       if (mw) {
 #pragma unroll

@@ -186,6 +186,21 @@ __device__ __forceinline__ f32x4 mfma32_split(const bf16x8 a[NS], const bf16x8 b
   return c;
 }
 
+// Two independent split products, c0 += a0 b0 and c1 += a1 b1, each in the
+// order of mfma32_split (so bit-identical to two such calls), issued
+// alternately so that neither waits for its own previous product.
+template <int NS>
+__device__ __forceinline__ void mfma32_split2(const bf16x8 a0[NS], const bf16x8 b0[NS], f32x4 &c0,
+                                              const bf16x8 a1[NS], const bf16x8 b1[NS], f32x4 &c1) {
+#pragma unroll
+  for (int s = NS - 1; s >= 0; --s)
+#pragma unroll
+    for (int pa = 0; pa <= s; ++pa) {
+      c0 = mfma32(a0[pa], b0[s - pa], c0);
+      c1 = mfma32(a1[pa], b1[s - pa], c1);
+    }
+}
+
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 // ---------------------------------------------------------------- gates
