@@ -887,15 +887,22 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
     f32x4 accC[2] = {zero4(), zero4()}, accT[2] = {zero4(), zero4()};  // channel-tile, token-block products
     f32x4 accMt[PP ? 2 : 1] = {};  // PP, K half: K'^T Y itself (M^T up to the diagonal)
     // both column tiles of a k-step together: their fragments read at once
-    // and their two accumulators' products interleaved (each accumulator
-    // still sums the k-steps in order)
+    // (one k-step ahead) and their two accumulators' products interleaved
+    // (each accumulator still sums the k-steps in order)
+    bf16x8 n0[NS], n1[NS];
+    load_frag<NS>(rst + 0 * NS * FRAG + lane * 8, FRAG, n0);
+    load_frag<NS>(rst + 1 * NS * FRAG + lane * 8, FRAG, n1);
 #pragma unroll
     for (int ks = 0; ks < NKC; ++ks) {
+      bf16x8 z0[NS], z1[NS];
+#pragma unroll
+      for (int p = 0; p < NS; ++p) { z0[p] = n0[p]; z1[p] = n1[p]; }
+      if (ks + 1 < NKC) {
+        load_frag<NS>(rst + ((ks * 2 + 2) * NS) * FRAG + lane * 8, FRAG, n0);
+        load_frag<NS>(rst + ((ks * 2 + 3) * NS) * FRAG + lane * 8, FRAG, n1);
+      }
       const bool tw = rowwave && 2 * ks <= i && (!vhalf || a.Ob);  // O_bar only when it is stored
       if (!mw && !tw) continue;
-      bf16x8 z0[NS], z1[NS];
-      load_frag<NS>(rst + ((ks * 2) * NS) * FRAG + lane * 8, FRAG, z0);
-      load_frag<NS>(rst + ((ks * 2 + 1) * NS) * FRAG + lane * 8, FRAG, z1);
       if (vhalf) {
         if (mw) mfma32_split2<NS>(wf[ks], z0, accC[0], wf[ks], z1, accC[1]);  // N = K'^T U_bar
         if (tw) mfma32_split2<NS>(z0, pf[ks], accT[0], z1, pf[ks], accT[1]);  // O_bar^T = U_bar^T A^T
