@@ -248,7 +248,7 @@ gdr_status bwd_call(const gdr_desc *desc, int nseq, const int *cu, const void *q
   r.S_T = dS0;
   r.rev = 1;
   if (chunks) {
-    a.Qp = f.Qp; a.Mm = f.Mm; a.Sc = f.Sc;
+    a.Mm = f.Mm; a.Sc = f.Sc;
     // forward recompute: the chunk maps and M^T (a packed batch's chunk list
     // first), then Q'^T dO; then the forward chain (chunk-start states) and
     // the reverse chain side by side
@@ -259,8 +259,8 @@ gdr_status bwd_call(const gdr_desc *desc, int nseq, const int *cu, const void *q
     fi.Ob = nullptr;
     fi.pp_kn = a.KN; fi.pp_kh = a.KH; fi.pp_qt = a.QT; fi.pp_vh = a.VH; fi.pp_lam = a.LAM;
     fi.pp_am = a.AM; fi.pp_ti = a.TI; fi.pp_mt = a.Mt;
+    fi.pp_do = dO; fi.pp_do_bf16 = a.do_bf16; fi.pp_g = a.Gn;
     e = gdr::launch_chunk(fd, fi, 1, st);
-    if (e == hipSuccess) e = gdr::launch_bwd_prep(a, d.dk, ns, st);
     f.c0 = r.c0 = 0;
     f.ncs = r.ncs = a.NC;
     if (e == hipSuccess) e = gdr::launch_chain_pair(fd, f, r, st);

@@ -23,8 +23,8 @@
 // recomputes the chunk maps and, beside them, writes the per-token vectors
 // kn, k_hat, q_tilde, v_hat and the in-chunk cumulative log decay Lambda
 // (its pre-pass already forms them), the chunk system's A and T^-1 (its
-// Gram and solve phases form them) and M^T (its column loop); the prep
-// kernel forms Q'^T dO;
+// Gram and solve phases form them), and M^T and Q'^T dO (its column loop,
+// from dO staged in LDS; Q' itself is not written);
 // the forward chain (chunk-start states) and the reverse chain (X) run side
 // by side in one launch; then per chunk the dense products and the Gram
 // backprop with the chains to the inputs; last dgamma.
@@ -68,12 +68,7 @@ __device__ __forceinline__ SlotTokens slot_tokens(const BwdArgs &a, size_t slot)
   return s;
 }
 
-// ---------------------------------------------------------------------------
-// Prep: per chunk slot, G = Q'^T dO (in N's accumulator-tile layout) for the
-// reverse chain (M^T comes from the recompute), on the fp32 matrix cores from
-// Q' and dO in LDS, wave w owning G's row tiles w * NMT/4 to (w + 1) * NMT/4 - 1
-// (NMT = D / 16).
-// ---------------------------------------------------------------------------
+// One fp32 MFMA 16x16x4 (the dense products and the Gram backprop).
 __device__ __forceinline__ f32x4 mfma4(float x, float y, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(x, y, c, 0, 0, 0);
 }
@@ -99,76 +94,6 @@ template <bool DOBF, int D>
 __device__ __forceinline__ f32x4 ld_do_row(const void *dO, size_t row0, int valid, int t, int c) {
   const f32x4 v = ld_do4<DOBF>(dO, (row0 + (size_t)min(t, max(valid - 1, 0))) * D + c);
   return t < valid ? v : zero4();
-}
-
-template <int D, int NS, bool DOBF>
-__global__ void __launch_bounds__(256) bwd_prep_kernel(BwdArgs a) {
-  constexpr int C = kBC, NKD = D / 32, NMT = D / 16, SP = D + 4, RT = NMT / 4;
-  // Q' [t][i] and dO [t][j]
-  __shared__ __align__(16) float lds[2 * C * SP];
-  float *qs = lds, *ds = lds + C * SP;
-  const size_t slot = blockIdx.x;
-  const SlotTokens st = slot_tokens(a, slot);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, g = lane >> 4;
-  // Q' (planes summed in fp32) and dO into LDS
-  // every load of the staging in flight before the first LDS store
-  const uint16_t *Qs = a.Qp + slot * NS * (size_t)C * D;
-  constexpr int NQ = C * D / 8 / 256, ND = C * D / 4 / 256;
-  bf16x8 qv[NQ][NS];
-  f32x4 dv[ND];
-#pragma unroll
-  for (int it = 0; it < NQ; ++it)
-#pragma unroll
-    for (int p = 0; p < NS; ++p) qv[it][p] = reinterpret_cast<const bf16x8 *>(Qs + (size_t)p * C * D)[tid + 256 * it];
-#pragma unroll
-  for (int it = 0; it < ND; ++it) {
-    const int idx = tid + 256 * it, t = idx / (D / 4), j4 = idx % (D / 4);
-    dv[it] = ld_do_row<DOBF, D>(a.dO, st.row, st.valid, t, 4 * j4);
-  }
-#pragma unroll
-  for (int it = 0; it < NQ; ++it) {
-    const int idx = tid + 256 * it, f = idx >> 6, ln = idx & 63, t = 16 * (f / NKD) + (ln & 15),
-              col = 32 * (f % NKD) + 4 * (ln >> 4);
-    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int p = 0; p < NS; ++p)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] += (float)qv[it][p][e];
-    *reinterpret_cast<float4 *>(qs + t * SP + col) = float4{v[0], v[1], v[2], v[3]};
-    *reinterpret_cast<float4 *>(qs + t * SP + col + 16) = float4{v[4], v[5], v[6], v[7]};
-  }
-#pragma unroll
-  for (int it = 0; it < ND; ++it) {
-    const int idx = tid + 256 * it, t = idx / (D / 4), j4 = idx % (D / 4);
-    *reinterpret_cast<f32x4 *>(ds + t * SP + 4 * j4) = dv[it];
-  }
-  __syncthreads();
-  // G[i][j] = sum_t Q'[t][i] dO[t][j]: lane (l16, g) supplies k = t = 16 kb + 4 g + e
-  f32x4 acc[RT][NMT];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-    for (int jt = 0; jt < NMT; ++jt) acc[rt][jt] = zero4();
-#pragma unroll
-  for (int kb = 0; kb < C / 16; ++kb)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int t = 16 * kb + 4 * g + e;
-      float av[RT], bv[NMT];
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) av[rt] = qs[t * SP + 16 * (RT * w + rt) + l16];
-#pragma unroll
-      for (int jt = 0; jt < NMT; ++jt) bv[jt] = ds[t * SP + 16 * jt + l16];
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int jt = 0; jt < NMT; ++jt) acc[rt][jt] = mfma4(av[rt], bv[jt], acc[rt][jt]);
-    }
-  f32x4 *G = reinterpret_cast<f32x4 *>(a.Gn + slot * (size_t)D * D);
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-    for (int jt = 0; jt < NMT; ++jt) G[((RT * w + rt) * NMT + jt) * 64 + lane] = acc[rt][jt];
 }
 
 __device__ __forceinline__ float wave_max(float x) {
@@ -1075,16 +1000,6 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int D, int NS>
-hipError_t launch_bwd_prep_t(const BwdArgs &a, hipStream_t st) {
-  const unsigned nch = (unsigned)(a.ctab ? (size_t)a.H * a.ctab_len : (size_t)a.B * a.H * a.NC);
-  if (a.do_bf16)
-    hipLaunchKernelGGL((bwd_prep_kernel<D, NS, true>), dim3(nch), dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL((bwd_prep_kernel<D, NS, false>), dim3(nch), dim3(256), 0, st, a);
-  return hipGetLastError();
-}
-
 }  // namespace
 
 size_t bwd_workspace(BwdArgs *a, ChunkArgs *f, void *ws, int B, int H, int T, int D, int NS, int nseq) {
@@ -1124,13 +1039,6 @@ size_t bwd_workspace(BwdArgs *a, ChunkArgs *f, void *ws, int B, int H, int T, in
     a->gpart = gp;
   }
   return total;
-}
-
-hipError_t launch_bwd_prep(const BwdArgs &a, int D, int NS, hipStream_t st) {
-  if (D == 128 && NS == 2) return launch_bwd_prep_t<128, 2>(a, st);
-  if (D == 128) return launch_bwd_prep_t<128, 3>(a, st);
-  if (NS == 2) return launch_bwd_prep_t<64, 2>(a, st);
-  return launch_bwd_prep_t<64, 3>(a, st);
 }
 
 hipError_t launch_out_gate_bwd(const OgBwdArgs &a, int D, bool g_bf16, hipStream_t st) {

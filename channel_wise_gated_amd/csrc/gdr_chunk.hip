@@ -149,6 +149,12 @@ struct IntraLds {
   // same layout), loaded during the pre-pass.
   static constexpr size_t bytes = sizeof(float) * ((size_t)STG + STG_SZ) + sizeof(int) * NB;
   static constexpr int WAVES = NB > D / 16 ? NB : D / 16;
+  // The backward's recompute (PP) also forms G = Q'^T dO: dO of the chunk
+  // [C][D + 4] and one column pair's Q' [C][36] in fp32, after the rest.
+  static constexpr int DOS_LD = D + 4, QS_LD = 36;
+  static constexpr int DOS = (int)((bytes + 15) / 16 * 4);  // float offset, 16-byte aligned
+  static constexpr int QS = DOS + C * DOS_LD;
+  static constexpr size_t pp_bytes = sizeof(float) * ((size_t)QS + C * QS_LD);
 };
 
 // Channel held by (lane group g, k-step ks, element e) in tile-pair order.
@@ -169,9 +175,11 @@ __device__ __forceinline__ int tp_chan(int ks, int g, int e) { return 32 * ks + 
 // PP: also write what the backward reads of the chunk: the per-token vectors
 // kn, k_hat, q_tilde, v_hat and the in-chunk cumulative log decay ([slot][C][D]
 // fp32 each, zero on padding rows), the chunk system's A and T^-1
-// ([slot][C][C] fp32 each), and M^T in M's A-fragment plane layout (for the
-// reverse chain of state gradients).
-template <int C, int D, int NS, bool BF, bool SA, bool PP = false>
+// ([slot][C][C] fp32 each), M^T in M's A-fragment plane layout and G =
+// Q'^T dO in N's accumulator-tile layout (for the reverse chain of state
+// gradients, X <- M^T X + G); Q' itself is not written.
+// DOBF (PP only): dO is bf16 (else fp32).
+template <int C, int D, int NS, bool BF, bool SA, bool PP = false, bool DOBF = false>
 __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
   static_assert(!SA || NS == 2, "the scalar-decay kernel keeps kn * Cf as two bf16 planes in the kn * Cf region");
   using Lds = IntraLds<C, D, NS>;
@@ -204,10 +212,10 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
     const int4 e = a.ctab[ch / a.H];
     if (e.x < 0) {  // past the last chunk (the grid is an upper bound)
       if constexpr (PP) {  // the backward still reads the slot: zeros
-        float *pp[7] = {a.pp_kn, a.pp_kh, a.pp_qt, a.pp_vh, a.pp_lam, a.pp_am, a.pp_ti};
+        float *pp[8] = {a.pp_kn, a.pp_kh, a.pp_qt, a.pp_vh, a.pp_lam, a.pp_am, a.pp_ti, a.pp_g};
 #pragma unroll
-        for (int q = 0; q < 7; ++q) {
-          const int n4 = q < 5 ? C * D / 4 : C * C / 4;
+        for (int q = 0; q < 8; ++q) {
+          const int n4 = q < 5 ? C * D / 4 : (q < 7 ? C * C / 4 : D * D / 4);
           float4 *dst = reinterpret_cast<float4 *>(pp[q] + ch * (size_t)n4 * 4);
           for (int x = threadIdx.x; x < n4; x += blockDim.x) dst[x] = make_float4(0.f, 0.f, 0.f, 0.f);
         }
@@ -724,6 +732,24 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
   }
 
   // -------------------------------------------------- D: the chunk map
+  // PP: dO of the chunk, loaded here (in flight while W and P are formed)
+  // and staged in LDS before the column loop; rows past the chunk's tokens
+  // read its last real row and are zeroed
+  constexpr int NDO = PP ? C * D / 4 / (64 * Lds::WAVES) : 1;
+  static_assert(!PP || NDO * 4 * 64 * Lds::WAVES == C * D, "whole float4s of dO per thread");
+  using DoRaw = std::conditional_t<DOBF, uint2, float4>;
+  DoRaw dor[NDO];
+  if constexpr (PP) {
+#pragma unroll
+    for (int it = 0; it < NDO; ++it) {
+      const int idx = tid + 64 * Lds::WAVES * it, tt = idx / (D / 4), j4 = idx % (D / 4);
+      const size_t off = rowc(tt) * D + 4 * j4;
+      if constexpr (DOBF)
+        dor[it] = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(a.pp_do) + off);
+      else
+        dor[it] = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.pp_do) + off);
+    }
+  }
   // With W = K'^T T^-1 (D x C) and P = A T^-1 (C x C, lower triangular):
   //   N = W V_hat,  M = Diag(e^Lambda_C) - W K_hat e^Lambda,
   //   O_bar = P V_hat,  Q' = Qt e^Lambda - P K_hat e^Lambda,
@@ -795,6 +821,21 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
   // every wave has read kcf: the region now takes v_hat = w * v (fp32, kcf
   // layout), read back by the same wave in the first half of the loop below
   __syncthreads();
+  if constexpr (PP) {  // dO -> [C][D + 4] fp32 (read after the first half's barriers)
+    float *dos = sm + Lds::DOS;
+#pragma unroll
+    for (int it = 0; it < NDO; ++it) {
+      const int idx = tid + 64 * Lds::WAVES * it, tt = idx / (D / 4), j4 = idx % (D / 4);
+      float4 v;
+      if constexpr (DOBF)
+        v = make_float4(__uint_as_float(dor[it].x << 16), __uint_as_float(dor[it].x & 0xffff0000u),
+                        __uint_as_float(dor[it].y << 16), __uint_as_float(dor[it].y & 0xffff0000u));
+      else
+        v = dor[it];
+      if (tt >= tvalid) v = make_float4(0.f, 0.f, 0.f, 0.f);
+      *reinterpret_cast<float4 *>(dos + tt * Lds::DOS_LD + 4 * j4) = v;
+    }
+  }
   float *vhat = sm + Lds::KCF;
   if (rowwave) {
     const float wconst = gate_const(a.w_mode);
@@ -966,10 +1007,41 @@ __global__ void __launch_bounds__(512) chunk_intra_kernel(ChunkArgs a) {
             for (int p = 0; p < NS; ++p) qr += (float)QRs[p][e];
             qv8[e] = qr * eci[e] - accT[ctl][r];
           }
-        store8_planes<NS>(Qp + ((size_t)(i * NKD + ksy) * 64 + lane) * 8, (size_t)C * D, qv8);
+        if constexpr (PP) {  // this pair's 32 channels of Q' for G (row t, channel 16 ctl + 4 g + r)
+          float *qs = sm + Lds::QS + t * Lds::QS_LD + 4 * g;
+          *reinterpret_cast<float4 *>(qs) = make_float4(qv8[0], qv8[1], qv8[2], qv8[3]);
+          *reinterpret_cast<float4 *>(qs + 16) = make_float4(qv8[4], qv8[5], qv8[6], qv8[7]);
+        } else {
+          store8_planes<NS>(Qp + ((size_t)(i * NKD + ksy) * 64 + lane) * 8, (size_t)C * D, qv8);
+        }
       }
     }
     __syncthreads();
+    if constexpr (PP) {
+      // G rows of this pair's 32 channels (state-row tiles 2 ksy, 2 ksy + 1)
+      // = Q'[:, channels]^T dO on the fp32 matrix cores, k = token; wave w
+      // takes row tile 2 ksy + (w & 1) and value tiles 2 (w >> 1), + 1.  The
+      // next pair writes Q' only after its own first barrier.
+      if (!vhalf) {
+        static_assert(NMT == Lds::WAVES, "two G tiles per wave");
+        const float *qs = sm + Lds::QS, *dos = sm + Lds::DOS;
+        const int rl = wave & 1, jt0 = 2 * (wave >> 1);
+        f32x4 g0 = zero4(), g1 = zero4();
+#pragma unroll
+        for (int kb = 0; kb < C / 4; ++kb) {
+          const int tt = 4 * kb + g;
+          const float av = qs[tt * Lds::QS_LD + 16 * rl + l16];
+          const float b0 = dos[tt * Lds::DOS_LD + 16 * jt0 + l16];
+          const float b1 = dos[tt * Lds::DOS_LD + 16 * (jt0 + 1) + l16];
+          g0 = __builtin_amdgcn_mfma_f32_16x16x4f32(av, b0, g0, 0, 0, 0);
+          g1 = __builtin_amdgcn_mfma_f32_16x16x4f32(av, b1, g1, 0, 0, 0);
+        }
+        const int rt = 2 * (cp - D / 32) + rl;
+        float *G = a.pp_g + ch * (size_t)D * D;
+        *reinterpret_cast<f32x4 *>(G + ((size_t)(rt * NMT + jt0) * 64 + lane) * 4) = g0;
+        *reinterpret_cast<f32x4 *>(G + ((size_t)(rt * NMT + jt0 + 1) * 64 + lane) * 4) = g1;
+      }
+    }
   };
   if constexpr (NS == 2) {
 #pragma unroll 1
@@ -1444,12 +1516,19 @@ static hipError_t launch_chunk_pass(const ChunkArgs &a, size_t nch, int phases, 
     const dim3 grid((unsigned)nch), block(64 * Lds::WAVES);
     bool pp = false;
     if constexpr (C == 64) {
-      if (a.pp_kn) {  // the backward's recompute: the per-token vectors as well
+      if (a.pp_kn) {  // the backward's recompute: the per-token vectors and G as well
         pp = true;
-        if (sa)
-          hipLaunchKernelGGL((chunk_intra_kernel<C, D, NS, BF, NS == 2, true>), grid, block, Lds::bytes, st, a);
-        else
-          hipLaunchKernelGGL((chunk_intra_kernel<C, D, NS, BF, false, true>), grid, block, Lds::bytes, st, a);
+        if (a.pp_do_bf16) {
+          if (sa)
+            hipLaunchKernelGGL((chunk_intra_kernel<C, D, NS, BF, NS == 2, true, true>), grid, block, Lds::pp_bytes, st, a);
+          else
+            hipLaunchKernelGGL((chunk_intra_kernel<C, D, NS, BF, false, true, true>), grid, block, Lds::pp_bytes, st, a);
+        } else {
+          if (sa)
+            hipLaunchKernelGGL((chunk_intra_kernel<C, D, NS, BF, NS == 2, true>), grid, block, Lds::pp_bytes, st, a);
+          else
+            hipLaunchKernelGGL((chunk_intra_kernel<C, D, NS, BF, false, true>), grid, block, Lds::pp_bytes, st, a);
+        }
       }
     }
     if (!pp) {
@@ -1531,12 +1610,13 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, int phases, hipStream_t st,
         e = hipFuncSetAttribute(reinterpret_cast<const void *>(&chunk_intra_kernel<C, D, NS, BF, NS == 2>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lds::bytes);
       if constexpr (C == 64) {
-        if (e == hipSuccess)
-          e = hipFuncSetAttribute(reinterpret_cast<const void *>(&chunk_intra_kernel<C, D, NS, BF, false, true>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lds::bytes);
-        if (e == hipSuccess && NS == 2)
-          e = hipFuncSetAttribute(reinterpret_cast<const void *>(&chunk_intra_kernel<C, D, NS, BF, NS == 2, true>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lds::bytes);
+        static_assert(Lds::pp_bytes <= 160 * 1024, "the recompute's LDS budget");
+        const void *pk[4] = {reinterpret_cast<const void *>(&chunk_intra_kernel<C, D, NS, BF, false, true>),
+                             reinterpret_cast<const void *>(&chunk_intra_kernel<C, D, NS, BF, false, true, true>),
+                             reinterpret_cast<const void *>(&chunk_intra_kernel<C, D, NS, BF, NS == 2, true>),
+                             reinterpret_cast<const void *>(&chunk_intra_kernel<C, D, NS, BF, NS == 2, true, true>)};
+        for (int q = 0; q < (NS == 2 ? 4 : 2) && e == hipSuccess; ++q)
+          e = hipFuncSetAttribute(pk[q], hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lds::pp_bytes);
       }
       if (e == hipSuccess)
         e = hipFuncSetAttribute(reinterpret_cast<const void *>(&chunk_out_kernel<C, D, NS, OB16, false>),

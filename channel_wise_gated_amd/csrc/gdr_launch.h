@@ -54,6 +54,12 @@ struct ChunkArgs {
   // written for an empty slot of a packed batch).
   float *pp_am, *pp_ti;
   uint16_t *pp_mt;
+  // ... and G = Q'^T dO for the reverse chain, in N's accumulator-tile layout
+  // ([slot][D][D] fp32), from dO ([B,H,T,dv] rows as q's, bf16 when
+  // pp_do_bf16, else fp32); Q' itself is then not written.
+  const void *pp_do;
+  int pp_do_bf16;
+  float *pp_g;
 };
 
 // The five-gate projection: x [N, dm] bf16 (N = B*T tokens), wd [R, dm]
@@ -77,7 +83,7 @@ struct BwdArgs {
   const float *log_alpha, *gamma;
   int B, H, T, NC, alpha_mode, b_mode, w_mode, normalize_qk, do_bf16;
   float scale;
-  const uint16_t *Qp, *Mm, *Sc;  // the forward's Q', M and chunk-start states (C = 64)
+  const uint16_t *Mm, *Sc;       // the forward's M and chunk-start states (C = 64)
   uint16_t *Mt, *Xc;             // M^T for the reverse chain; the chunk-end state gradients
   float *Gn;                     // Q'^T dO for the reverse chain
   // per-chunk scratch, [slot][64][D] fp32
@@ -92,7 +98,6 @@ struct BwdArgs {
 // Workspace of the backward: the forward's chunk workspace (C = 64; its fields
 // set in *f) followed by the backward's regions (set in *a); returns the size.
 size_t bwd_workspace(BwdArgs *a, ChunkArgs *f, void *ws, int B, int H, int T, int D, int NS, int nseq);
-hipError_t launch_bwd_prep(const BwdArgs &a, int D, int NS, hipStream_t st);
 hipError_t launch_bwd(const BwdArgs &a, int D, int NS, hipStream_t st);
 
 // Backward of the fused output gate (gdr_bwd.hip): rows of [B,H,T,dv] in
