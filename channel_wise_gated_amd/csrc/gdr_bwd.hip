@@ -1008,34 +1008,63 @@ size_t bwd_workspace(BwdArgs *a, ChunkArgs *f, void *ws, int B, int H, int T, in
   const size_t nch = nseq > 0 ? (size_t)H * ((size_t)((T + C - 1) / C) + (size_t)nseq)
                               : (size_t)B * H * ((T + C - 1) / C);
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  size_t total = al(chunk_workspace(f, ws, nseq > 0 ? 1 : B, H, T, C, D, NS, nseq));
+  // the forward's chunk workspace first (its fields set in *f; with no
+  // workspace, in a scratch copy: only the size counts then)
+  ChunkArgs scratch_args{};
+  const ChunkArgs &fl = f ? *f : scratch_args;
+  size_t total = al(chunk_workspace(f ? f : &scratch_args, ws, nseq > 0 ? 1 : B, H, T, C, D, NS, nseq));
   unsigned char *base = static_cast<unsigned char *>(ws);
   auto take = [&](size_t bytes) {
     void *p = ws ? base + total : nullptr;
     total += al(bytes);
     return p;
   };
+  // Regions the backward's later arrays can share: the forward workspace's Q'
+  // and O_bar slots, which the recompute does not write (it forms G instead
+  // of Q' and skips O_bar); its M and N slots and the backward's M^T and G,
+  // all dead once the two chains have run.
+  struct Region {
+    unsigned char *p;
+    size_t cap, used;
+  };
+  auto region = [&](void *p, size_t cap) { return Region{ws ? static_cast<unsigned char *>(p) : nullptr, cap, 0}; };
+  Region never[2] = {region(fl.Qp, nch * NS * (size_t)C * D * 2), region(fl.Ob, nch * (size_t)C * D * 4)};
   void *mt = take(nch * NS * (size_t)D * D * 2), *xc = take(nch * NS * (size_t)D * D * 2);
   void *gn = take(nch * (size_t)D * D * 4);
-  float **cd[9] = {&a->KN, &a->KH, &a->QT, &a->VH, &a->LAM, &a->DU, &a->DQA, &a->DKA, &a->DKP};
-  float *cdp[9];
-  for (int i = 0; i < 9; ++i) cdp[i] = static_cast<float *>(take(nch * (size_t)kBC * D * 4));
-  float *ccp[4];
-  for (int i = 0; i < 4; ++i) ccp[i] = static_cast<float *>(take(nch * (size_t)kBC * kBC * 4));
+  Region after_chains[4] = {region(fl.Mm, nch * NS * (size_t)D * D * 2), region(fl.Nn, nch * (size_t)D * D * 4),
+                            region(mt, nch * NS * (size_t)D * D * 2), region(gn, nch * (size_t)D * D * 4)};
+  // in the first region with room left, else in fresh workspace
+  auto place = [&](Region *rs, int n, size_t bytes) -> float * {
+    for (int r = 0; r < n; ++r)
+      if (rs[r].cap - rs[r].used >= bytes) {
+        void *p = rs[r].p ? rs[r].p + rs[r].used : nullptr;
+        rs[r].used += al(bytes);
+        return static_cast<float *>(p);
+      }
+    return static_cast<float *>(take(bytes));
+  };
+  const size_t vec = nch * (size_t)C * D * 4, sq = nch * (size_t)C * C * 4;
+  // written by the recompute, read by the per-chunk kernels
+  float *vecs[5];
+  for (int i = 0; i < 5; ++i) vecs[i] = static_cast<float *>(take(vec));  // kn, k_hat, q_tilde, v_hat, Lambda
+  float *am = place(never, 2, sq), *ti = place(never, 2, sq);
+  // written by the dense products, read by the Gram backprop (after the chains)
+  float *res[4];
+  for (int i = 0; i < 4; ++i) res[i] = place(after_chains, 4, vec);  // dU~, dQ_a, dK_a, dK'
+  float *da = place(after_chains, 4, sq), *dl = place(after_chains, 4, sq);
   float *gp = static_cast<float *>(take(nch * (size_t)D * 4));
   float *xs = static_cast<float *>(take(nch * (size_t)D * 4));
   if (a) {
-    a->ctab = (ws && f) ? f->ctab : nullptr;
-    a->ctab_len = (ws && f) ? f->ctab_len : 0;
+    a->ctab = ws ? fl.ctab : nullptr;
+    a->ctab_len = ws ? fl.ctab_len : 0;
     a->XS = xs;
     a->Mt = static_cast<uint16_t *>(mt);
     a->Xc = static_cast<uint16_t *>(xc);
     a->Gn = static_cast<float *>(gn);
-    for (int i = 0; i < 9; ++i) *cd[i] = cdp[i];
-    a->AM = ccp[0];
-    a->TI = ccp[1];
-    a->DA = ccp[2];
-    a->DL = ccp[3];
+    a->KN = vecs[0]; a->KH = vecs[1]; a->QT = vecs[2]; a->VH = vecs[3]; a->LAM = vecs[4];
+    a->AM = am; a->TI = ti;
+    a->DU = res[0]; a->DQA = res[1]; a->DKA = res[2]; a->DKP = res[3];
+    a->DA = da; a->DL = dl;
     a->gpart = gp;
   }
   return total;
