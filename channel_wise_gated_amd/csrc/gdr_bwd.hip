@@ -214,7 +214,7 @@ __global__ void __launch_bounds__(512) bwd_mm_kernel(BwdArgs a) {
   static_assert(8 % (D / 32) == 0, "a thread's plane entries share their k-step");
   __shared__ __align__(16) float ss[D * SP];    // S0, then X, then dU~ (rows < C)
   __shared__ __align__(16) float bb[BBR * SP];  // rows < C: R, then U; rows C..2C-1: dO, then Z; last: S0
-  __shared__ float xs[D];                       // row dots of X and S0
+  __shared__ float xsp[8][32];                  // row dots of X and S0, one part per wave
   float *bt = bb, *bu = bb + C * SP;
   const size_t slot = blockIdx.x;
   const SlotTokens st = slot_tokens(a, slot);
@@ -240,7 +240,8 @@ __global__ void __launch_bounds__(512) bwd_mm_kernel(BwdArgs a) {
       for (int p = 0; p < NS; ++p) r[k][p] = *reinterpret_cast<const bf16x8 *>(pl + off + p * FRAG);
     }
   };
-  // with `dots`, also the row dots with the state in `o` (same layout) -> xs
+  // with `dots`, also this wave's part of the row dots with the state in `o`
+  // (same layout) -> xsp[w]: rows 32 ks + the entry's index there
   auto store_planes = [&](float *dst, const bf16x8 (&r)[NE][NS], const bf16x8 (&o)[NE][NS], bool dots) {
     float dot[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -264,7 +265,7 @@ __global__ void __launch_bounds__(512) bwd_mm_kernel(BwdArgs a) {
         float d = dot[e];
 #pragma unroll
         for (int off = 1; off < 16; off <<= 1) d += __shfl_xor(d, off, kWave);
-        if (l16 == 0) atomicAdd(&xs[32 * ks + 16 * (e >> 2) + 4 * g + (e & 3)], d);
+        if (l16 == 0) xsp[w][16 * (e >> 2) + 4 * g + (e & 3)] = d;
       }
     }
   };
@@ -298,7 +299,6 @@ __global__ void __launch_bounds__(512) bwd_mm_kernel(BwdArgs a) {
 
   // (1) S0 phase: R = V_hat - K_a S0 (-> LDS), dQ_a = dO S0^T; dO staged
   // once, for this phase and the third
-  if (tid < D) xs[tid] = 0.f;
   bf16x8 pa[NE][NS], pb[NE][NS];  // planes: S0 (pb, kept for phases 3 and 5); X (pa)
   load_planes(S0p, pb);
   store_planes(ss, pb, pb, false);
@@ -386,7 +386,11 @@ __global__ void __launch_bounds__(512) bwd_mm_kernel(BwdArgs a) {
   put_glb(a.DKP, acc2, 1.f);
   __syncthreads();  // every read of dO and X is done
   put_lds(bu, acc);
-  if (tid < D) a.XS[slot * D + tid] = xs[tid];
+  if (tid < D) {  // the waves' parts summed in a fixed order: results do not depend on timing
+    float sum = 0.f;
+    for (int ww = tid / 32; ww < 8; ww += D / 32) sum += xsp[ww][tid % 32];
+    a.XS[slot * D + tid] = sum;
+  }
   __syncthreads();
 
   // (4) dU~ = T^-T Z (upper triangular: k-blocks from the row tile on)

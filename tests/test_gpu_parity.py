@@ -6,6 +6,8 @@ run the oracle on everything; the workloads at their full sizes run the GPU on
 everything, in the launch configuration the benchmark times, and the oracle on
 sampled (batch, head) streams.
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -887,6 +889,57 @@ def bwd_compare(x, tag, seed=5, do_bf16=False, with_dst=True, tol=None, **kw):
 def test_backward_small_cases(name, B, H, T, d):
     wl = WORKLOADS[name].with_sizes(B=B, H=H, T=T, dk=d, dv=d)
     bwd_compare(make_inputs(wl), f"{name} B{B} H{H} T{T} d{d}")
+
+
+@pytest.mark.parametrize("name,T,d,dtype,do_bf16,packed", [
+    ("gdn2", 200, 128, "bf16", False, False), ("gdn2", 100, 64, "f32", False, False),
+    ("kda", 130, 128, "bf16", True, False), ("gdn2", 0, 128, "bf16", False, True)])
+def test_backward_workspace_contents_do_not_matter(name, T, d, dtype, do_bf16, packed):
+    """The backward's workspace arrays share memory where their lifetimes do
+    not overlap, so every value a kernel reads must have been written earlier
+    in the same call: a workspace filled with NaN gives gradients bit-identical
+    to a zero-filled one (which also needs every reduction in the backward to
+    run in a fixed order)."""
+    r = np.random.default_rng(29)
+    if packed:
+        x, cu = packed_inputs(name, [0, 65, 1, 130, 17], seed_shift=5)
+        cuj = torch.from_numpy(cu).to(DEV)
+        nseq = len(cu) - 1
+    else:
+        x, cuj, nseq = make_inputs(WORKLOADS[name].with_sizes(B=1, H=2, T=T, dk=d, dv=d, dtype=dtype)), None, None
+    B, H, TT, dk = x["q"].shape
+    dv = x["v"].shape[-1]
+    dO = torch.from_numpy(r.standard_normal((B, H, TT, dv))).float()
+    if do_bf16:
+        dO = dO.to(torch.bfloat16)
+    nS = nseq if packed else B
+    dST = torch.from_numpy(0.1 * r.standard_normal((nS, H, dk, dv))).float().to(DEV)
+    dd = dev(x)
+    lib = gdr.load()
+    amode, _ = gdr._log_alpha_arg(dd["log_alpha"], (B, H, TT, dk))
+    bmode, _ = gdr._gate_arg(dd["b"], "b", (B, H, TT, dk), (dd["q"].dtype,))
+    wmode, _ = gdr._gate_arg(dd["w"], "w", (B, H, TT, dv), (dd["q"].dtype,))
+    desc = gdr.make_desc(B, H, TT, dk, dv, 64, gdr._dtype_code(dd["q"]),
+                         gdr.GDR_BF16 if do_bf16 else gdr.GDR_F32, 1, 1.0, amode, bmode, wmode)
+    n = ctypes.c_size_t(0)
+    if packed:
+        assert lib.gdr_chunk_bwd_varlen_workspace_size(ctypes.byref(desc), nseq, ctypes.byref(n)) == gdr.GDR_OK
+    else:
+        assert lib.gdr_chunk_bwd_workspace_size(ctypes.byref(desc), ctypes.byref(n)) == gdr.GDR_OK
+    print(f"workspace poisoning: {name} T{TT} d{d} {dtype} dO bf16 {do_bf16} packed {packed}, {n.value} B", flush=True)
+    outs = []
+    for fill in (0, 0xFF):  # all-ones bytes are NaN in fp32 and in bf16
+        ws = torch.full((n.value,), fill, dtype=torch.uint8, device=DEV)
+        g = gdr.gdr_chunk_bwd(dd["q"], dd["k"], dd["v"], dd["log_alpha"], dd["b"], dd["w"], dO.to(DEV),
+                              gamma=dd["gamma"], z=dd["z"], S0=dd["S0"], dS_T=dST, workspace=ws,
+                              cu_seqlens=cuj)
+        torch.cuda.synchronize()
+        outs.append(g)
+    for key, val in outs[0].items():
+        if val is None:
+            continue
+        assert bool(torch.isfinite(val).all()), key
+        assert torch.equal(val, outs[1][key]), key
 
 
 def test_backward_fp32_inputs_and_bf16_upstream():
