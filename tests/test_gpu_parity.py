@@ -891,6 +891,16 @@ def test_backward_small_cases(name, B, H, T, d):
     bwd_compare(make_inputs(wl), f"{name} B{B} H{H} T{T} d{d}")
 
 
+@pytest.mark.parametrize("chunk,dtype,d", [(64, "bf16", 128), (128, "bf16", 128), (64, "f32", 64)])
+def test_forward_is_bit_reproducible(chunk, dtype, d):
+    """Two calls on the same inputs give bit-identical o and S_T: no result
+    depends on the order in which workgroups or waves finish."""
+    x = make_inputs(WORKLOADS["gdn2"].with_sizes(B=2, H=2, T=700, dk=d, dv=d, dtype=dtype))
+    print(f"forward reproducibility: C{chunk} {dtype} d{d}", flush=True)
+    runs = [gpu_chunk(x, chunk) for _ in range(2)]
+    assert np.array_equal(runs[0][0], runs[1][0]) and np.array_equal(runs[0][1], runs[1][1])
+
+
 @pytest.mark.parametrize("name,T,d,dtype,do_bf16,packed", [
     ("gdn2", 200, 128, "bf16", False, False), ("gdn2", 100, 64, "f32", False, False),
     ("kda", 130, 128, "bf16", True, False), ("gdn2", 0, 128, "bf16", False, True)])
